@@ -1,0 +1,435 @@
+// Host side of libhws: the C ABI declared in include/hws.h.
+//
+// Validation runs before any HIP call, so every error status can be produced
+// without a GPU.  Device work is only kernel launches on the caller's stream;
+// nothing here allocates device memory or synchronises (except
+// hws_profile_read, which waits for its own timing events).
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "hws.h"
+#include "hws_internal.h"
+
+using namespace hws;
+
+namespace {
+
+constexpr int NUM_STAGES = 4;
+const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge"};
+
+struct EvPair {
+  hipEvent_t a, b;
+  int stage;
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace regions of one decode call.
+struct Layout {
+  size_t scores, agg, spart, sel, apart_ml, apart_o, qrot, total;
+  int n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
+};
+
+}  // namespace
+
+struct hws_ctx {
+  hws_config cfg;
+  int G = 1;
+  uint8_t kinds[MAX_KV] = {};
+  int nR = 0, nL = 0;
+  signed char ret_slot[MAX_KV];
+  signed char ret_head[MAX_KV];
+  signed char loc_head[MAX_KV];
+  bool appended = false, bound = false;
+  hws_buffers buf{};
+  std::string err;
+  bool prof = false;
+  std::vector<EvPair> recorded;
+  std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+hws_status fail(hws_ctx* ctx, hws_status st, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+hws_status fail(hws_ctx* ctx, hws_status st, const char* fmt, ...) {
+  if (ctx != nullptr) {
+    char msg[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, sizeof(msg), fmt, ap);
+    va_end(ap);
+    ctx->err = msg;
+  }
+  return st;
+}
+
+hws_status hip_fail(hws_ctx* ctx, hipError_t e, const char* what) {
+  return fail(ctx, HWS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void rebuild_slots(hws_ctx* c) {
+  c->nR = c->nL = 0;
+  for (int h = 0; h < MAX_KV; ++h) { c->ret_slot[h] = -1; c->ret_head[h] = -1; c->loc_head[h] = -1; }
+  for (int h = 0; h < c->cfg.num_kv_heads; ++h) {
+    if (c->kinds[h] == HWS_HEAD_RETRIEVAL) {
+      c->ret_slot[h] = (signed char)c->nR;
+      c->ret_head[c->nR++] = (signed char)h;
+    } else {
+      c->loc_head[c->nL++] = (signed char)h;
+    }
+  }
+}
+
+int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope) {
+  Layout L{};
+  const int G = c->G;
+  L.n_score_chunks = cdiv(Nmax, SCORE_CHUNK);
+  L.n_sel_chunks = cdiv(Nmax, SEL_CHUNK);
+  // Retrieval attention chunk: longer contexts get longer chunks so that the
+  // split partials stay small next to the gathered rows.
+  L.att_chunk_R = Nmax >= 65536 ? 4096 : (Nmax >= 16384 ? 2048 : 1024);
+  L.ncR = cdiv(Nmax, L.att_chunk_R);
+  const long long local_rows = std::min<long long>(Nmax, (long long)c->cfg.n_sink + c->cfg.window);
+  L.ncL = std::max(1, cdiv(local_rows, LOCAL_CHUNK));
+  L.max_splits = std::max(c->nR > 0 ? L.ncR : 1, c->nL > 0 ? L.ncL : 1);
+  const size_t nRb = (size_t)B * c->nR;
+  size_t off = 0;
+  L.scores = off;   off = align_up(off + nRb * Nmax * G * sizeof(float));
+  L.agg = off;      off = align_up(off + nRb * Nmax * sizeof(float));
+  L.spart = off;    off = align_up(off + nRb * L.n_score_chunks * G * sizeof(float2));
+  L.sel = off;      off = align_up(off + nRb * sizeof(SelState));
+  const size_t nsp = (size_t)B * c->cfg.num_kv_heads * L.max_splits * G;
+  L.apart_ml = off; off = align_up(off + nsp * sizeof(float2));
+  L.apart_o = off;  off = align_up(off + nsp * D * sizeof(float));
+  L.qrot = off;     off = align_up(off + (rope ? (size_t)B * c->cfg.num_q_heads * D * sizeof(float) : 0));
+  L.total = off;
+  return L;
+}
+
+bool finite_f(float x) { return std::isfinite(x); }
+
+hws_status check_ctx(hws_ctx* ctx) {
+  return ctx == nullptr ? HWS_ERR_INVALID_ARG : HWS_OK;
+}
+
+void record(hws_ctx* ctx, hipStream_t s, int stage, bool begin, hipEvent_t* open) {
+  if (!ctx->prof) return;
+  hipEvent_t e;
+  if (ctx->pool.empty()) {
+    if (hipEventCreate(&e) != hipSuccess) return;
+  } else {
+    e = ctx->pool.back();
+    ctx->pool.pop_back();
+  }
+  hipEventRecord(e, s);
+  if (begin) {
+    *open = e;
+  } else {
+    ctx->recorded.push_back(EvPair{*open, e, stage});
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hws_abi_version(void) { return HWS_ABI_VERSION; }
+
+const char* hws_status_string(hws_status s) {
+  switch (s) {
+    case HWS_OK: return "ok";
+    case HWS_ERR_INVALID_ARG: return "invalid argument";
+    case HWS_ERR_STATE: return "call out of order";
+    case HWS_ERR_CAPACITY: return "capacity exceeded";
+    case HWS_ERR_WORKSPACE: return "workspace too small";
+    case HWS_ERR_UNSUPPORTED: return "unsupported shape";
+    case HWS_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* hws_last_error(const hws_ctx* ctx) { return ctx == nullptr ? "" : ctx->err.c_str(); }
+
+hws_status hws_create(const hws_config* cfg, hws_ctx** out) {
+  if (cfg == nullptr || out == nullptr) return HWS_ERR_INVALID_ARG;
+  *out = nullptr;
+  const hws_config& c = *cfg;
+  if (c.num_q_heads < 1 || c.num_kv_heads < 1 || c.num_q_heads % c.num_kv_heads != 0) return HWS_ERR_INVALID_ARG;
+  const int G = c.num_q_heads / c.num_kv_heads;
+  if (c.num_kv_heads > MAX_KV || (G != 1 && G != 2 && G != 4 && G != 8)) return HWS_ERR_UNSUPPORTED;
+  if (c.head_dim != D || c.index_dim != R || c.block_size != BS) return HWS_ERR_UNSUPPORTED;
+  if (c.num_blocks < 1 || c.max_blocks_per_seq < 1 || c.max_blocks_per_seq > (1 << 26)) return HWS_ERR_INVALID_ARG;
+  if (c.kv_dtype != HWS_KV_BF16 && c.kv_dtype != HWS_KV_FP8_E4M3) return HWS_ERR_INVALID_ARG;
+  if (c.n_sink < 0 || c.window < 0 || (long long)c.n_sink + c.window < 1) return HWS_ERR_INVALID_ARG;
+  if (!finite_f(c.attn_scale) || !(c.attn_scale > 0.f) || !finite_f(c.index_scale) ||
+      !finite_f(c.rope_theta) || c.rope_theta < 0.f)
+    return HWS_ERR_INVALID_ARG;
+  hws_ctx* ctx = new (std::nothrow) hws_ctx();
+  if (ctx == nullptr) return HWS_ERR_INVALID_ARG;
+  ctx->cfg = c;
+  ctx->G = G;
+  rebuild_slots(ctx);
+  *out = ctx;
+  return HWS_OK;
+}
+
+hws_status hws_destroy(hws_ctx* ctx) {
+  if (ctx == nullptr) return HWS_OK;
+  for (auto& p : ctx->recorded) { hipEventDestroy(p.a); hipEventDestroy(p.b); }
+  for (auto e : ctx->pool) hipEventDestroy(e);
+  delete ctx;
+  return HWS_OK;
+}
+
+hws_status hws_set_head_kinds(hws_ctx* ctx, const uint8_t* kinds) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (kinds == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "kinds is NULL");
+  if (ctx->appended) return fail(ctx, HWS_ERR_STATE, "head kinds are fixed after the first append");
+  for (int h = 0; h < ctx->cfg.num_kv_heads; ++h)
+    if (kinds[h] != HWS_HEAD_LOCAL && kinds[h] != HWS_HEAD_RETRIEVAL)
+      return fail(ctx, HWS_ERR_INVALID_ARG, "kinds[%d] = %d is not a head kind", h, (int)kinds[h]);
+  std::memcpy(ctx->kinds, kinds, (size_t)ctx->cfg.num_kv_heads);
+  rebuild_slots(ctx);
+  return HWS_OK;
+}
+
+hws_status hws_classify_by_scores(hws_ctx* ctx, const float* q_head_scores, int32_t n_retrieval_kv,
+                                  int32_t lower_is_retrieval) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (q_head_scores == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "scores is NULL");
+  const int Hkv = ctx->cfg.num_kv_heads, G = ctx->G;
+  if (n_retrieval_kv < 0 || n_retrieval_kv > Hkv)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "n_retrieval_kv = %d outside [0, %d]", n_retrieval_kv, Hkv);
+  if (ctx->appended) return fail(ctx, HWS_ERR_STATE, "head kinds are fixed after the first append");
+  std::vector<double> pooled(Hkv);
+  for (int h = 0; h < Hkv; ++h) {
+    double s = 0.0;
+    for (int g = 0; g < G; ++g) {
+      const float v = q_head_scores[h * G + g];
+      if (!finite_f(v)) return fail(ctx, HWS_ERR_INVALID_ARG, "score of query head %d is not finite", h * G + g);
+      s += v;
+    }
+    pooled[h] = s / G;                       // mean pooling over the GQA group
+  }
+  std::vector<int> order(Hkv);
+  for (int h = 0; h < Hkv; ++h) order[h] = h;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return lower_is_retrieval ? pooled[a] < pooled[b] : pooled[a] > pooled[b];
+  });
+  uint8_t kinds[MAX_KV] = {};
+  for (int i = 0; i < n_retrieval_kv; ++i) kinds[order[i]] = HWS_HEAD_RETRIEVAL;
+  std::memcpy(ctx->kinds, kinds, (size_t)Hkv);
+  rebuild_slots(ctx);
+  return HWS_OK;
+}
+
+hws_status hws_get_head_kinds(const hws_ctx* ctx, uint8_t* kinds) {
+  if (ctx == nullptr || kinds == nullptr) return HWS_ERR_INVALID_ARG;
+  std::memcpy(kinds, ctx->kinds, (size_t)ctx->cfg.num_kv_heads);
+  return HWS_OK;
+}
+
+hws_status hws_bind(hws_ctx* ctx, const hws_buffers* buf) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (buf == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "buffers is NULL");
+  if (buf->k_pool == nullptr || buf->v_pool == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "k_pool / v_pool is NULL");
+  if (ctx->cfg.kv_dtype == HWS_KV_FP8_E4M3 && buf->kv_scales == nullptr)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "fp8 cache needs kv_scales");
+  ctx->buf = *buf;
+  ctx->bound = true;
+  return HWS_OK;
+}
+
+hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq_len, int32_t score_mode,
+                              size_t* bytes) {
+  if (ctx == nullptr || bytes == nullptr) return HWS_ERR_INVALID_ARG;
+  if (batch < 1 || max_seq_len < 1) return HWS_ERR_INVALID_ARG;
+  if (score_mode != HWS_SCORE_INDEX && score_mode != HWS_SCORE_FULL) return HWS_ERR_INVALID_ARG;
+  if ((long long)max_seq_len > (long long)ctx->cfg.max_blocks_per_seq * BS) return HWS_ERR_CAPACITY;
+  *bytes = make_layout(ctx, batch, max_seq_len, ctx->cfg.rope_theta > 0.f).total;
+  return HWS_OK;
+}
+
+hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t* block_tables,
+                      const int32_t* start_pos, const void* k, const void* v, void* stream) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, HWS_ERR_STATE, "append before bind");
+  if (n_seq < 1 || n_tok < 1) return fail(ctx, HWS_ERR_INVALID_ARG, "n_seq = %d, n_tok = %d", n_seq, n_tok);
+  if (block_tables == nullptr || start_pos == nullptr || k == nullptr || v == nullptr)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "null device pointer");
+  if ((long long)n_tok > (long long)ctx->cfg.max_blocks_per_seq * BS)
+    return fail(ctx, HWS_ERR_CAPACITY, "n_tok = %d exceeds the block table", n_tok);
+  if (ctx->nR > 0 && (ctx->buf.index_pool == nullptr || ctx->buf.proj == nullptr))
+    return fail(ctx, HWS_ERR_INVALID_ARG, "retrieval heads need index_pool and proj");
+  AppendParams p{};
+  p.n_seq = n_seq;
+  p.n_tok = n_tok;
+  p.Hkv = ctx->cfg.num_kv_heads;
+  p.nR = ctx->nR;
+  p.max_blocks = ctx->cfg.max_blocks_per_seq;
+  p.num_blocks = ctx->cfg.num_blocks;
+  p.rope_theta = ctx->cfg.rope_theta;
+  p.block_tables = block_tables;
+  p.start_pos = start_pos;
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.k_pool = ctx->buf.k_pool;
+  p.v_pool = ctx->buf.v_pool;
+  p.kv_scales = ctx->buf.kv_scales;
+  p.index_pool = ctx->buf.index_pool;
+  p.proj = ctx->buf.proj;
+  std::memcpy(p.ret_slot, ctx->ret_slot, sizeof(p.ret_slot));
+  ctx->appended = true;
+  const hipError_t e = launch_append(p, ctx->cfg.kv_dtype == HWS_KV_FP8_E4M3, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(ctx, e, "append launch");
+  return HWS_OK;
+}
+
+hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (a == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "args is NULL");
+  if (!ctx->bound) return fail(ctx, HWS_ERR_STATE, "decode before bind");
+  const hws_config& c = ctx->cfg;
+  if (a->batch < 1 || a->max_seq_len < 1)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "batch = %d, max_seq_len = %d", a->batch, a->max_seq_len);
+  if ((long long)a->max_seq_len > (long long)c.max_blocks_per_seq * BS)
+    return fail(ctx, HWS_ERR_CAPACITY, "max_seq_len = %d exceeds %d pages of 16", a->max_seq_len, c.max_blocks_per_seq);
+  if (a->select_mode != HWS_SELECT_TOP_P && a->select_mode != HWS_SELECT_TOP_K)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "select_mode = %d", a->select_mode);
+  if (a->score_mode != HWS_SCORE_INDEX && a->score_mode != HWS_SCORE_FULL)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "score_mode = %d", a->score_mode);
+  if (a->q == nullptr || a->block_tables == nullptr || a->seq_lens == nullptr || a->out == nullptr)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "null device pointer (q, block_tables, seq_lens or out)");
+  if (ctx->nR > 0) {
+    if (a->select_mode == HWS_SELECT_TOP_P && a->top_p == nullptr)
+      return fail(ctx, HWS_ERR_INVALID_ARG, "top-p selection needs top_p");
+    if (a->select_mode == HWS_SELECT_TOP_K && a->top_k == nullptr)
+      return fail(ctx, HWS_ERR_INVALID_ARG, "top-k selection needs top_k");
+    if (a->score_mode == HWS_SCORE_INDEX && (ctx->buf.index_pool == nullptr || ctx->buf.proj == nullptr))
+      return fail(ctx, HWS_ERR_INVALID_ARG, "index scoring needs index_pool and proj");
+  }
+  if (a->sel_idx != nullptr && a->sel_cap < 1) return fail(ctx, HWS_ERR_INVALID_ARG, "sel_cap = %d", a->sel_cap);
+  const bool rope = c.rope_theta > 0.f;
+  const Layout L = make_layout(ctx, a->batch, a->max_seq_len, rope);
+  if (a->workspace == nullptr || a->workspace_bytes < L.total)
+    return fail(ctx, HWS_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, L.total);
+
+  char* ws = static_cast<char*>(a->workspace);
+  DecodeParams p{};
+  p.B = a->batch;
+  p.Hq = c.num_q_heads;
+  p.Hkv = c.num_kv_heads;
+  p.G = ctx->G;
+  p.nR = ctx->nR;
+  p.nL = ctx->nL;
+  p.Nmax = a->max_seq_len;
+  p.max_blocks = c.max_blocks_per_seq;
+  p.num_blocks = c.num_blocks;
+  p.select_mode = a->select_mode;
+  p.score_mode = a->score_mode;
+  p.n_sink = c.n_sink;
+  p.window = c.window;
+  p.attn_scale = c.attn_scale;
+  p.index_scale = c.index_scale;
+  p.rope_theta = c.rope_theta;
+  p.c2_attn = (float)((double)c.attn_scale * 1.4426950408889634);
+  p.c2_score = a->score_mode == HWS_SCORE_FULL ? p.c2_attn : (float)((double)c.index_scale * 1.4426950408889634);
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.block_tables = a->block_tables;
+  p.seq_lens = a->seq_lens;
+  p.top_p = a->top_p;
+  p.top_k = a->top_k;
+  p.k_pool = ctx->buf.k_pool;
+  p.v_pool = ctx->buf.v_pool;
+  p.kv_scales = c.kv_dtype == HWS_KV_FP8_E4M3 ? ctx->buf.kv_scales : nullptr;
+  p.index_pool = ctx->buf.index_pool;
+  p.proj = ctx->buf.proj;
+  p.scores = a->scores != nullptr ? a->scores : reinterpret_cast<float*>(ws + L.scores);
+  p.agg = reinterpret_cast<float*>(ws + L.agg);
+  p.spart = reinterpret_cast<float2*>(ws + L.spart);
+  p.sel = reinterpret_cast<SelState*>(ws + L.sel);
+  p.apart_ml = reinterpret_cast<float2*>(ws + L.apart_ml);
+  p.apart_o = reinterpret_cast<float*>(ws + L.apart_o);
+  p.qrot = rope ? reinterpret_cast<float*>(ws + L.qrot) : nullptr;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.sel_counts = a->sel_counts;
+  p.sel_idx = a->sel_idx;
+  p.sel_cap = a->sel_cap;
+  p.n_score_chunks = L.n_score_chunks;
+  p.n_sel_chunks = L.n_sel_chunks;
+  p.ncR = L.ncR;
+  p.ncL = L.ncL;
+  p.att_chunk_R = L.att_chunk_R;
+  p.max_splits = L.max_splits;
+  std::memcpy(p.ret_slot, ctx->ret_slot, sizeof(p.ret_slot));
+  std::memcpy(p.ret_head, ctx->ret_head, sizeof(p.ret_head));
+  std::memcpy(p.loc_head, ctx->loc_head, sizeof(p.loc_head));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  hipEvent_t open = nullptr;
+  if (rope && (e = launch_prep_q(p, s)) != hipSuccess) return hip_fail(ctx, e, "prep_q launch");
+  if (ctx->nR > 0) {
+    record(ctx, s, 0, true, &open);
+    if ((e = launch_score(p, s)) != hipSuccess) return hip_fail(ctx, e, "score launch");
+    record(ctx, s, 0, false, &open);
+    record(ctx, s, 1, true, &open);
+    for (int pass = 1; pass <= 3; ++pass)
+      if ((e = launch_select(p, s, pass)) != hipSuccess) return hip_fail(ctx, e, "select launch");
+    if (a->select_mode == HWS_SELECT_TOP_K && (e = launch_select(p, s, 4)) != hipSuccess)
+      return hip_fail(ctx, e, "tie launch");
+    record(ctx, s, 1, false, &open);
+  }
+  record(ctx, s, 2, true, &open);
+  if ((e = launch_attend(p, s)) != hipSuccess) return hip_fail(ctx, e, "attend launch");
+  record(ctx, s, 2, false, &open);
+  record(ctx, s, 3, true, &open);
+  if ((e = launch_merge(p, s)) != hipSuccess) return hip_fail(ctx, e, "merge launch");
+  record(ctx, s, 3, false, &open);
+  if (ctx->nR > 0 && a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess)
+    return hip_fail(ctx, e, "emit launch");
+  return HWS_OK;
+}
+
+hws_status hws_profile_enable(hws_ctx* ctx, int32_t enable) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  ctx->prof = enable != 0;
+  return HWS_OK;
+}
+
+hws_status hws_profile_read(hws_ctx* ctx, double* ms, int32_t* calls, int32_t n) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (n < 0 || (n > 0 && (ms == nullptr || calls == nullptr))) return fail(ctx, HWS_ERR_INVALID_ARG, "bad output arrays");
+  for (int i = 0; i < n; ++i) { ms[i] = 0.0; calls[i] = 0; }
+  hws_status st = HWS_OK;
+  for (auto& pr : ctx->recorded) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(pr.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, pr.a, pr.b);
+    if (e != hipSuccess) {
+      st = hip_fail(ctx, e, "profile read");
+    } else if (pr.stage < n) {
+      ms[pr.stage] += t;
+      calls[pr.stage] += 1;
+    }
+    ctx->pool.push_back(pr.a);
+    ctx->pool.push_back(pr.b);
+  }
+  ctx->recorded.clear();
+  return st;
+}
+
+const char* hws_profile_stage_name(int32_t i) {
+  return (i >= 0 && i < NUM_STAGES) ? STAGE_NAMES[i] : "";
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Device helpers for the gfx950 kernels (wave64).
+#pragma once
+
+#include "hws_internal.h"
+
+namespace hws {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp64 -> bf16 bits with a single rounding (nearest even) from the double.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  // bf16 keeps 7 explicit mantissa bits; a double has 52 -> drop 45 bits.
+  u += ((1ull << 44) - 1ull) + ((u >> 45) & 1ull);
+  u &= ~((1ull << 45) - 1ull);
+  float f = (float)__longlong_as_double((long long)u);   // exact: value is bf16-representable
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// OCP e4m3fn encode of an fp32 value: saturate to +-448, round to nearest
+// even, sign copied from the input.
+__device__ __forceinline__ uint8_t e4m3_encode(float y) {
+  uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  float a = fminf(fabsf(y), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8 (8 = smallest normal)
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);        // round mantissa to 3 bits
+    uint32_t e = (u >> 23) - 127u + 7u;
+    uint32_t m = (u >> 20) & 7u;
+    code = (e << 3) | m;
+  }
+  return (uint8_t)(sign | code);
+}
+
+// Combine two (max, sum) pairs of a log2-sum-exp2.
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+  float mn = fmaxf(m, m2);
+  if (mn == NEG_INF) { m = mn; s = 0.f; return; }
+  s = s * fast_exp2(m - mn) + s2 * fast_exp2(m2 - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ unsigned long long load_u64_coherent(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned int load_u32_coherent(const unsigned int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace hws

@@ -1,0 +1,112 @@
+// Internal definitions shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hws {
+
+constexpr int D = 128;            // head dim
+constexpr int R = 16;             // index dim
+constexpr int BS = 16;            // tokens per page
+constexpr int MAX_KV = 64;        // KV heads per layer
+constexpr int MAX_G = 8;          // query heads per KV head
+
+constexpr int SCORE_CHUNK = 1024; // tokens per scoring workgroup (4 waves x 256)
+constexpr int SEL_CHUNK = 16384;  // tokens per selection workgroup (256 thr x 64)
+constexpr int HIST_BINS = 4096;   // pass 1 bins: bits 30..19 of the fp32 pattern
+constexpr int LOCAL_CHUNK = 256;  // rows per local-head attention workgroup
+
+// Bit split of the non-negative fp32 aggregate a_i (bit 31 is always 0):
+// pass 1 bins bits 30..19 (12 bits), pass 2 bits 18..9 (10), pass 3 bits 8..0 (9).
+constexpr int P1_SHIFT = 19, P2_SHIFT = 9;
+constexpr int P2_BINS = 1024, P3_BINS = 512;
+
+constexpr uint32_t SEL_FINISHED = 1u;   // tstar / icut are final
+constexpr uint32_t SEL_TIE = 2u;        // top-k: ties at tstar exceed the quota
+
+// Fixed-point mass: round(a * 2^40) as uint64.  Integer bins make the
+// threshold independent of the order in which workgroups add their counts.
+constexpr float MASS_SCALE = 1099511627776.0f;   // 2^40
+
+// Selection state of one (sequence, retrieval head).  Zeroed by the scoring
+// kernel of each decode call; histograms are cleared by the last workgroup
+// of each pass for the next one.
+struct alignas(256) SelState {
+  unsigned long long mass[HIST_BINS];
+  unsigned int cnt[HIST_BINS];
+  unsigned int done;        // arrivals in the current pass
+  unsigned int flags;       // SEL_*
+  unsigned int prefix;      // known high bits of the threshold pattern
+  unsigned int tstar;       // threshold pattern (valid once FINISHED)
+  unsigned long long mass_above;  // mass strictly above the candidate bin range
+  unsigned int cnt_above;   // count strictly above the candidate bin range
+  unsigned int icut;        // ties at tstar kept while position <= icut
+  unsigned int nsel;        // |S|
+  unsigned int quota;       // top-k: ties still to keep
+  float lse2[MAX_G];        // per query head log2-sum-exp2 of the logits
+};
+constexpr int SELSTATE_WORDS = (int)(sizeof(SelState) / 4);
+
+// Everything a decode kernel needs, passed by value.
+struct DecodeParams {
+  int B, Hq, Hkv, G, nR, nL, Nmax, max_blocks, num_blocks;
+  int select_mode, score_mode;
+  int n_sink, window;
+  float attn_scale, index_scale, rope_theta;
+  float c2_attn;    // attn_scale * log2(e)
+  float c2_score;   // scale of raw scores to log2 logits (index or attention)
+  const uint16_t* q;            // [B][Hq][D] bf16
+  const int* block_tables;      // [B][max_blocks]
+  const int* seq_lens;          // [B]
+  const float* top_p;           // [B]
+  const int* top_k;             // [B]
+  const void* k_pool;
+  const void* v_pool;
+  const float* kv_scales;
+  const float* index_pool;
+  const float* proj;
+  float* scores;                // [B][nR][Nmax][G]
+  float* agg;                   // [B][nR][Nmax]
+  float2* spart;                // [B][nR][n_score_chunks][G]  (max, sum) in log2 units
+  SelState* sel;                // [B][nR]
+  float2* apart_ml;             // [B][Hkv][max_splits][G]  (max, sum)
+  float* apart_o;               // [B][Hkv][max_splits][G][D]
+  float* qrot;                  // [B][Hq][D] fp32 rotated queries (RoPE on) or null
+  float* out;
+  float* lse;
+  int* sel_counts;
+  int* sel_idx;
+  int sel_cap;
+  int n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
+  signed char ret_slot[MAX_KV];
+  signed char ret_head[MAX_KV];
+  signed char loc_head[MAX_KV];
+};
+
+struct AppendParams {
+  int n_seq, n_tok, Hkv, nR, max_blocks, num_blocks;
+  float rope_theta;
+  const int* block_tables;
+  const int* start_pos;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* k_pool;
+  void* v_pool;
+  float* kv_scales;
+  float* index_pool;
+  const float* proj;
+  signed char ret_slot[MAX_KV];
+};
+
+// Kernel launchers (one translation unit each); return the launch status.
+hipError_t launch_prep_q(const DecodeParams& p, hipStream_t s);
+hipError_t launch_score(const DecodeParams& p, hipStream_t s);
+hipError_t launch_select(const DecodeParams& p, hipStream_t s, int pass);
+hipError_t launch_attend(const DecodeParams& p, hipStream_t s);
+hipError_t launch_merge(const DecodeParams& p, hipStream_t s);
+hipError_t launch_emit(const DecodeParams& p, hipStream_t s);
+hipError_t launch_append(const AppendParams& p, int kv_fp8, hipStream_t s);
+
+}  // namespace hws

@@ -1,0 +1,299 @@
+// Scoring scans of retrieval heads: one pass over every cached token.
+//
+// INDEX mode ([RTPurbo] "Full attention returns in force ...", Methodology §2:
+// a 16-dim projection of the pre-RoPE query and key estimates relevance):
+// s_{g,i} = (P_h q_g) . k~_i with k~_i = P_h k_i stored in the index pool,
+// 64 bytes per token and head, streamed with one 16-byte load per lane.
+//
+// FULL mode ([ICS] "Inference-time context sparsity: illusion or
+// opportunity?", §2 "Oracle Top-K"): s_{g,i} = q_g . k_i over all 128 dims,
+// reading every K row once.  The G x 16-token x 128 tile is a dense bf16
+// contraction, done with v_mfma_f32_16x16x32_bf16.
+//
+// Both write the raw scores to [B][nR][Nmax][G] and, per workgroup chunk,
+// the (max, sum) of 2^(c2 * s) for each query head, so that the selection
+// pass can form the per-head log-sum-exp without another scan.
+#include "hws_device.h"
+
+namespace hws {
+
+// Zero this chunk's share of the (b, hr) selection state.
+__device__ __forceinline__ void zero_state_share(SelState* st, int c, int nchunks) {
+  unsigned int* w = reinterpret_cast<unsigned int*>(st);
+  for (int i = c * 256 + (int)threadIdx.x; i < SELSTATE_WORDS; i += nchunks * 256) w[i] = 0u;
+}
+
+// Reduce (max, sum) over lanes sharing the same (lane & (span-1)) pattern.
+__device__ __forceinline__ void wave_lse_reduce(float& m, float& s, int from_mask, int to_mask) {
+  for (int off = from_mask; off <= to_mask; off <<= 1) {
+    float m2 = __shfl_xor(m, off);
+    float s2 = __shfl_xor(s, off);
+    lse_combine(m, s, m2, s2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// INDEX mode
+// Lane l of a wave holds token slot l/4 of a page and index dims 4*(l%4)..+3.
+// After a 2-step butterfly over the 4 lanes of a token, lane l keeps the
+// score of query head g = l%4 (+4 for G = 8).
+// ---------------------------------------------------------------------------
+template <int G>
+__global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
+  constexpr int NOWN = (G + 3) / 4;       // scores owned per lane per token
+  const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
+  const int N = min(p.seq_lens[b], p.Nmax);
+  const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;
+  SelState* st = p.sel + (size_t)b * p.nR + hr;
+  if (c >= nchunks) return;
+  zero_state_share(st, c, nchunks);
+
+  const int h = p.ret_head[hr];
+  __shared__ float qt_s[G][R];
+  __shared__ float red_m[4][G], red_s[4][G];
+  if (tid < G * R) {
+    const int g = tid / R, j = tid % R;
+    const float* prow = p.proj + ((size_t)h * R + j) * D;
+    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(p.q + ((size_t)b * p.Hq + h * G + g) * D);
+    float acc = 0.f;
+    for (int e = 0; e < D / 2; ++e) {
+      const uint32_t w = qrow[e];
+      acc = fmaf(prow[2 * e], bf16_lo(w), acc);
+      acc = fmaf(prow[2 * e + 1], bf16_hi(w), acc);
+    }
+    qt_s[g][j] = acc;
+  }
+  __syncthreads();
+
+  const int sub = lane & 3;
+  float qv[G][4];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qv[g][j] = qt_s[g][sub * 4 + j];
+
+  const int tok0 = c * SCORE_CHUNK + wave * 256;
+  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
+  float4 kv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = tok0 + i * BS;
+    kv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < N) {
+      const int blk = bt[t >> 4];
+      if ((unsigned)blk < (unsigned)p.num_blocks) {
+        const float4* src = reinterpret_cast<const float4*>(
+            p.index_pool + ((size_t)blk * p.nR + hr) * (BS * R));
+        kv[i] = src[lane];
+      }
+    }
+  }
+
+  float* out = p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G;
+  float m[NOWN], s[NOWN];
+#pragma unroll
+  for (int k = 0; k < NOWN; ++k) { m[k] = NEG_INF; s[k] = 0.f; }
+  const float c2 = p.c2_score;
+
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = tok0 + i * BS + (lane >> 2);
+    float part[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float a = qv[g][0] * kv[i].x;
+      a = fmaf(qv[g][1], kv[i].y, a);
+      a = fmaf(qv[g][2], kv[i].z, a);
+      a = fmaf(qv[g][3], kv[i].w, a);
+      a += __shfl_xor(a, 1);
+      a += __shfl_xor(a, 2);
+      part[g] = a;
+    }
+#pragma unroll
+    for (int k = 0; k < NOWN; ++k) {
+      const int g = sub + 4 * k;
+      float v = part[0];
+#pragma unroll
+      for (int gg = 1; gg < G; ++gg) v = (g == gg) ? part[gg] : v;
+      if (t < N && g < G) {
+        out[(size_t)t * G + g] = v;
+        const float x = v * c2;
+        const float mn = fmaxf(m[k], x);
+        s[k] = s[k] * fast_exp2(m[k] - mn) + fast_exp2(x - mn);
+        m[k] = mn;
+      }
+    }
+  }
+  // lanes with equal (lane & 3) hold the same query heads: reduce over bits 2..5
+#pragma unroll
+  for (int k = 0; k < NOWN; ++k) {
+    wave_lse_reduce(m[k], s[k], 4, 32);
+    const int g = sub + 4 * k;
+    if (lane < 4 && g < G) { red_m[wave][g] = m[k]; red_s[wave][g] = s[k]; }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mm = red_m[0][tid], ss = red_s[0][tid];
+    for (int w = 1; w < 4; ++w) lse_combine(mm, ss, red_m[w][tid], red_s[w][tid]);
+    p.spart[((size_t)(b * p.nR + hr) * p.n_score_chunks + c) * G + tid] = make_float2(mm, ss);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FULL mode (MFMA).  A = query tile: row g < G holds q_g (bf16); with RoPE on
+// rows G..2G-1 hold the bf16 residual q_g - bf16(q_g) of the rotated fp32
+// query, so hi + lo carries ~16 mantissa bits.  B = 32 dims x 16 tokens of
+// one page.  Lane l supplies row/column l%16 and the 8 consecutive
+// contraction elements 8*(l/16)..+7 of each 32-wide step; both operands use
+// the same dim for the same (lane, element), so the product sums over all
+// 128 dims.  C[row][col] sits in lane col + 16*(row/4), element row%4.
+// ---------------------------------------------------------------------------
+template <int G, bool SPLITQ>
+__global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
+  const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
+  const int N = min(p.seq_lens[b], p.Nmax);
+  const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;
+  SelState* st = p.sel + (size_t)b * p.nR + hr;
+  if (c >= nchunks) return;
+  zero_state_share(st, c, nchunks);
+
+  const int h = p.ret_head[hr];
+  const int row = lane & 15, quad = lane >> 4;
+  __shared__ float red_m[4][MAX_G], red_s[4][MAX_G];
+
+  // A operand (query tile), 4 contraction steps of 32 dims.
+  bf16x8 afrag[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = 32 * s + 8 * quad + j;
+      float v = 0.f;
+      if (SPLITQ) {
+        const int g = row < G ? row : row - G;
+        if (row < 2 * G) {
+          const float x = p.qrot[((size_t)b * p.Hq + h * G + g) * D + d];
+          const float hi = bf16_to_f32(f32_to_bf16_rne(x));
+          v = row < G ? hi : (x - hi);
+        }
+      } else if (row < G) {
+        v = bf16_to_f32(p.q[((size_t)b * p.Hq + h * G + row) * D + d]);
+      }
+      afrag[s][j] = (__bf16)v;
+    }
+  }
+
+  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
+  float* out = p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G;
+  const float c2 = p.c2_score;
+  float m[4], sm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = NEG_INF; sm[i] = 0.f; }
+
+  const int page0 = c * (SCORE_CHUNK / BS) + wave * 16;   // 16 pages per wave
+  constexpr int U = 4;                                     // pages in flight
+#pragma unroll 1
+  for (int i0 = 0; i0 < 16; i0 += U) {
+    bf16x8 bfrag[U][4];
+    int tpage[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pg = page0 + i0 + u;
+      tpage[u] = pg * BS;
+      int blk = -1;
+      if (tpage[u] < N) blk = bt[pg];
+      if ((unsigned)blk < (unsigned)p.num_blocks) {
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(
+            kpool + (((size_t)blk * p.Hkv + h) * BS + row) * D + 8 * quad);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag[u][s] = src[4 * s];
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag[u][s] = (bf16x8)(__bf16)0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (tpage[u] >= N) continue;                         // wave-uniform
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s], bfrag[u][s], acc, 0, 0, 0);
+      // Fold the lo rows onto the hi rows and keep the G scores of token `row`.
+      float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+      if (SPLITQ) {
+        if (G == 1) { v[0] += v[1]; }
+        else if (G == 2) { v[0] += v[2]; v[1] += v[3]; }
+        else {
+          const int off = 16 * (G / 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += __shfl_down(v[i], off);
+        }
+      }
+      // Lanes holding query heads: quad < G/4 (G >= 4) or quad 0 (G < 4).
+      const bool owner = (G >= 4) ? (quad < G / 4) : (quad == 0);
+      const int t = tpage[u] + row;
+      if (owner && t < N) {
+        float* dst = out + (size_t)t * G + ((G >= 4) ? 4 * quad : 0);
+        if (G >= 4) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if (G == 2) {
+          *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+        } else {
+          dst[0] = v[0];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < G) {
+            const float x = v[i] * c2;
+            const float mn = fmaxf(m[i], x);
+            sm[i] = sm[i] * fast_exp2(m[i] - mn) + fast_exp2(x - mn);
+            m[i] = mn;
+          }
+        }
+      }
+    }
+  }
+  // reduce over the 16 lanes of each quad (token columns)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wave_lse_reduce(m[i], sm[i], 1, 8);
+    const int g = ((G >= 4) ? 4 * quad : 0) + i;
+    const bool owner = (G >= 4) ? (quad < G / 4) : (quad == 0);
+    if (row == 0 && owner && i < G && g < G) { red_m[wave][g] = m[i]; red_s[wave][g] = sm[i]; }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mm = red_m[0][tid], ss = red_s[0][tid];
+    for (int w = 1; w < 4; ++w) lse_combine(mm, ss, red_m[w][tid], red_s[w][tid]);
+    p.spart[((size_t)(b * p.nR + hr) * p.n_score_chunks + c) * G + tid] = make_float2(mm, ss);
+  }
+}
+
+template <int G>
+static hipError_t launch_score_g(const DecodeParams& p, hipStream_t st) {
+  dim3 grid(p.n_score_chunks, p.nR, p.B);
+  if (p.score_mode == 0) {
+    hipLaunchKernelGGL(score_index_kernel<G>, grid, dim3(256), 0, st, p);
+  } else if (p.qrot != nullptr) {
+    hipLaunchKernelGGL((score_full_kernel<G, true>), grid, dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((score_full_kernel<G, false>), grid, dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const DecodeParams& p, hipStream_t st) {
+  switch (p.G) {
+    case 1: return launch_score_g<1>(p, st);
+    case 2: return launch_score_g<2>(p, st);
+    case 4: return launch_score_g<4>(p, st);
+    case 8: return launch_score_g<8>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hws

@@ -1,0 +1,227 @@
+"""ctypes binding of libhws (include/hws.h): same call names, marshalling only.
+
+Tensors are torch tensors used as device memory: the binding passes
+``data_ptr()`` and the current HIP stream handle and does no compute.  The
+library is loaded on first use; if ``libhws.so`` is missing or cannot be
+loaded, every call raises ``HwsError`` (there is no fallback path).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhws.so")
+_lib = None
+
+# status codes and enums (include/hws.h)
+HWS_OK = 0
+HWS_ERR_INVALID_ARG = -1
+HWS_ERR_STATE = -2
+HWS_ERR_CAPACITY = -3
+HWS_ERR_WORKSPACE = -4
+HWS_ERR_UNSUPPORTED = -5
+HWS_ERR_HIP = -6
+HWS_KV_BF16, HWS_KV_FP8_E4M3 = 0, 1
+HWS_HEAD_LOCAL, HWS_HEAD_RETRIEVAL = 0, 1
+HWS_SELECT_TOP_P, HWS_SELECT_TOP_K = 0, 1
+HWS_SCORE_INDEX, HWS_SCORE_FULL = 0, 1
+
+EXPORTED = (
+    "hws_abi_version", "hws_status_string", "hws_last_error", "hws_create", "hws_destroy",
+    "hws_set_head_kinds", "hws_classify_by_scores", "hws_get_head_kinds", "hws_bind",
+    "hws_workspace_size", "hws_append", "hws_decode", "hws_profile_enable",
+    "hws_profile_read", "hws_profile_stage_name",
+)
+
+
+class HwsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_q_heads", "num_kv_heads", "head_dim", "index_dim", "block_size", "num_blocks",
+        "max_blocks_per_seq", "kv_dtype", "n_sink", "window")] + [
+        ("attn_scale", ctypes.c_float), ("index_scale", ctypes.c_float),
+        ("rope_theta", ctypes.c_float)]
+
+
+class Buffers(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("kv_scales", ctypes.c_void_p), ("index_pool", ctypes.c_void_p),
+                ("proj", ctypes.c_void_p)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("select_mode", ctypes.c_int32), ("score_mode", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
+                ("top_k", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("sel_counts", ctypes.c_void_p), ("sel_idx", ctypes.c_void_p),
+                ("sel_cap", ctypes.c_int32), ("scores", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhws.so (once).  Raises HwsError if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise HwsError(HWS_ERR_STATE, f"{_LIB_PATH} is not built; run "
+                       "`python -m head_wise_sparse_02_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
+    sig = {
+        "hws_abi_version": (i32, []),
+        "hws_status_string": (ctypes.c_char_p, [i32]),
+        "hws_last_error": (ctypes.c_char_p, [vp]),
+        "hws_create": (i32, [P(Config), P(vp)]),
+        "hws_destroy": (i32, [vp]),
+        "hws_set_head_kinds": (i32, [vp, P(ctypes.c_uint8)]),
+        "hws_classify_by_scores": (i32, [vp, P(ctypes.c_float), i32, i32]),
+        "hws_get_head_kinds": (i32, [vp, P(ctypes.c_uint8)]),
+        "hws_bind": (i32, [vp, P(Buffers)]),
+        "hws_workspace_size": (i32, [vp, i32, i32, i32, P(ctypes.c_size_t)]),
+        "hws_append": (i32, [vp, i32, i32, vp, vp, vp, vp, vp]),
+        "hws_decode": (i32, [vp, P(DecodeArgs), vp]),
+        "hws_profile_enable": (i32, [vp, i32]),
+        "hws_profile_read": (i32, [vp, P(ctypes.c_double), P(i32), i32]),
+        "hws_profile_stage_name": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def status_string(st: int) -> str:
+    return lib().hws_status_string(st).decode()
+
+
+class Context:
+    """One attention layer: owns an hws_ctx (host object)."""
+
+    def __init__(self, *, num_q_heads: int, num_kv_heads: int, num_blocks: int,
+                 max_blocks_per_seq: int, n_sink: int, window: int, attn_scale: float,
+                 index_scale: float = 1.0, rope_theta: float = 0.0, kv_dtype: int = HWS_KV_BF16,
+                 head_dim: int = 128, index_dim: int = 16, block_size: int = 16):
+        self._L = lib()
+        self.cfg = Config(num_q_heads, num_kv_heads, head_dim, index_dim, block_size, num_blocks,
+                          max_blocks_per_seq, kv_dtype, n_sink, window, attn_scale, index_scale,
+                          rope_theta)
+        h = ctypes.c_void_p()
+        st = self._L.hws_create(ctypes.byref(self.cfg), ctypes.byref(h))
+        if st != HWS_OK:
+            raise HwsError(st, f"hws_create: {status_string(st)}")
+        self.handle = h
+
+    # -- lifecycle ---------------------------------------------------------
+    def close(self):
+        if getattr(self, "handle", None):
+            self._L.hws_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, st: int, what: str):
+        if st != HWS_OK:
+            msg = self._L.hws_last_error(self.handle).decode()
+            raise HwsError(st, f"{what}: {status_string(st)}: {msg}")
+
+    # -- head kinds ----------------------------------------------------------
+    def set_head_kinds(self, kinds):
+        arr = (ctypes.c_uint8 * len(kinds))(*[int(k) for k in kinds])
+        self._check(self._L.hws_set_head_kinds(self.handle, arr), "hws_set_head_kinds")
+
+    def classify_by_scores(self, q_head_scores, n_retrieval_kv: int, lower_is_retrieval: bool):
+        arr = (ctypes.c_float * len(q_head_scores))(*[float(x) for x in q_head_scores])
+        self._check(self._L.hws_classify_by_scores(self.handle, arr, int(n_retrieval_kv),
+                                                   int(bool(lower_is_retrieval))),
+                    "hws_classify_by_scores")
+
+    def head_kinds(self) -> list:
+        arr = (ctypes.c_uint8 * self.cfg.num_kv_heads)()
+        self._check(self._L.hws_get_head_kinds(self.handle, arr), "hws_get_head_kinds")
+        return list(arr)
+
+    # -- memory --------------------------------------------------------------
+    def bind(self, k_pool, v_pool, kv_scales=None, index_pool=None, proj=None):
+        self._buf = Buffers(_ptr(k_pool), _ptr(v_pool), _ptr(kv_scales), _ptr(index_pool), _ptr(proj))
+        self._check(self._L.hws_bind(self.handle, ctypes.byref(self._buf)), "hws_bind")
+
+    def workspace_size(self, batch: int, max_seq_len: int, score_mode: int) -> int:
+        n = ctypes.c_size_t()
+        self._check(self._L.hws_workspace_size(self.handle, batch, max_seq_len, score_mode,
+                                               ctypes.byref(n)), "hws_workspace_size")
+        return n.value
+
+    # -- device work -----------------------------------------------------------
+    def append(self, block_tables, start_pos, k, v, stream=None):
+        """k, v: [n_seq, n_tok, Hkv, 128] bf16 device tensors."""
+        n_seq, n_tok = int(k.shape[0]), int(k.shape[1])
+        self._check(self._L.hws_append(self.handle, n_seq, n_tok, _ptr(block_tables), _ptr(start_pos),
+                                       _ptr(k), _ptr(v), _stream(stream)), "hws_append")
+
+    def decode(self, *, q, block_tables, seq_lens, max_seq_len: int, select_mode: int,
+               score_mode: int, out, workspace, top_p=None, top_k=None, lse=None,
+               sel_counts=None, sel_idx=None, scores=None, stream=None):
+        a = DecodeArgs()
+        a.batch = int(q.shape[0]) if q is not None else 0
+        a.max_seq_len = int(max_seq_len)
+        a.select_mode, a.score_mode = int(select_mode), int(score_mode)
+        a.q, a.block_tables, a.seq_lens = _ptr(q), _ptr(block_tables), _ptr(seq_lens)
+        a.top_p, a.top_k = _ptr(top_p), _ptr(top_k)
+        a.out, a.lse, a.sel_counts = _ptr(out), _ptr(lse), _ptr(sel_counts)
+        a.sel_idx = _ptr(sel_idx)
+        a.sel_cap = int(sel_idx.shape[-1]) if sel_idx is not None else 0
+        a.scores = _ptr(scores)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+        self._check(self._L.hws_decode(self.handle, ctypes.byref(a), _stream(stream)), "hws_decode")
+
+    # -- timing ------------------------------------------------------------------
+    def profile_enable(self, enable: bool = True):
+        self._check(self._L.hws_profile_enable(self.handle, int(enable)), "hws_profile_enable")
+
+    def profile_read(self) -> dict:
+        n = 8
+        ms = (ctypes.c_double * n)()
+        calls = (ctypes.c_int32 * n)()
+        self._check(self._L.hws_profile_read(self.handle, ms, calls, n), "hws_profile_read")
+        out = {}
+        for i in range(n):
+            name = self._L.hws_profile_stage_name(i).decode()
+            if name:
+                out[name] = (ms[i], calls[i])
+        return out

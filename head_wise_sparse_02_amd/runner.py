@@ -1,0 +1,118 @@
+"""Set up a paged cache for a workload and drive append + decode through libhws.
+
+Torch supplies device memory and the stream; every step of the path runs in
+the library's kernels.  Inputs come from ``workloads`` (seeded, bf16-exact).
+The cache is filled the way a decode loop fills it: one bulk append of the
+first N-1 tokens of each sequence, then a single-token append of the current
+token, then the decode step.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import hws
+from .workloads import Workload
+
+KIND_CODE = {"local": hws.HWS_HEAD_LOCAL, "retrieval": hws.HWS_HEAD_RETRIEVAL}
+
+
+def append_segments(n: int) -> list:
+    """The append calls that fill a sequence of length n: [(start, count)]."""
+    return [(0, n - 1), (n - 1, 1)] if n > 1 else [(0, 1)]
+
+
+class DecodeSetup:
+    def __init__(self, wl: Workload, device: str = "cuda", spare_pages: int = 2,
+                 keep_host: bool = False, sequences=None):
+        self.wl = wl
+        self.dev = torch.device(device)
+        B, Hkv, Hq, d = wl.B, wl.Hkv, wl.Hq, wl.d
+        self.Nmax = int(max(wl.seq_lens))
+        self.max_blocks = (self.Nmax + 15) // 16 + spare_pages
+        pages = [(n + 15) // 16 + spare_pages for n in wl.seq_lens]
+        self.num_blocks = int(sum(pages))
+        self.fp8 = wl.kv_dtype == "fp8"
+        self.ctx = hws.Context(
+            num_q_heads=Hq, num_kv_heads=Hkv, num_blocks=self.num_blocks,
+            max_blocks_per_seq=self.max_blocks, n_sink=max(wl.n_sink, 0),
+            window=max(wl.window, 1 if wl.n_sink == 0 else 0),
+            attn_scale=wl.attn_scale, index_scale=wl.index_scale, rope_theta=wl.rope_theta,
+            kv_dtype=hws.HWS_KV_FP8_E4M3 if self.fp8 else hws.HWS_KV_BF16)
+        self.ctx.set_head_kinds([KIND_CODE[k] for k in wl.head_kinds])
+        self.nR = len(wl.retrieval_heads)
+
+        # pools and a seeded random page assignment (pages are not contiguous)
+        kv_dt = torch.uint8 if self.fp8 else torch.bfloat16
+        self.k_pool = torch.zeros((self.num_blocks, Hkv, 16, d), dtype=kv_dt, device=self.dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.kv_scales = (torch.ones((self.num_blocks, Hkv, 2), dtype=torch.float32, device=self.dev)
+                          if self.fp8 else None)
+        self.index_pool = (torch.zeros((self.num_blocks, max(self.nR, 1), 16, 16), dtype=torch.float32,
+                                       device=self.dev) if self.nR else None)
+        self.proj_host = wl.projections()
+        self.proj = torch.from_numpy(self.proj_host).to(self.dev)
+        rng = np.random.default_rng(np.random.SeedSequence([wl.cfg, wl.seed, 3000]))
+        perm = rng.permutation(self.num_blocks).astype(np.int32)
+        bt = np.full((B, self.max_blocks), -1, dtype=np.int32)
+        off = 0
+        for b in range(B):
+            bt[b, :pages[b]] = perm[off:off + pages[b]]
+            off += pages[b]
+        self.block_tables_host = bt
+        self.block_tables = torch.from_numpy(bt).to(self.dev)
+        self.seq_lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=self.dev)
+        self.ctx.bind(self.k_pool, self.v_pool, self.kv_scales, self.index_pool,
+                      self.proj if self.nR else None)
+
+        # fill the cache, sequence by sequence
+        self.q_host = np.zeros((B, Hq, d), dtype=np.float32)
+        self.host = [] if keep_host else None
+        for b in range(B):
+            seq = wl.sequence(b) if sequences is None else sequences[b]
+            self.q_host[b] = seq.q
+            if keep_host:
+                self.host.append(seq)
+            k = torch.from_numpy(seq.k).to(torch.bfloat16).to(self.dev)[None]
+            v = torch.from_numpy(seq.v).to(torch.bfloat16).to(self.dev)[None]
+            for start, cnt in append_segments(wl.seq_lens[b]):
+                sp = torch.tensor([start], dtype=torch.int32, device=self.dev)
+                self.ctx.append(self.block_tables[b:b + 1], sp, k[:, start:start + cnt].contiguous(),
+                                v[:, start:start + cnt].contiguous())
+            del k, v
+        torch.cuda.synchronize(self.dev)
+        self.q = torch.from_numpy(self.q_host).to(torch.bfloat16).to(self.dev)
+        self.top_p = torch.from_numpy(np.asarray(wl.top_p, np.float32)).to(self.dev)
+        self.top_k = torch.from_numpy(np.asarray(wl.top_k, np.int32)).to(self.dev)
+        self.select_mode = hws.HWS_SELECT_TOP_P if wl.select_mode == "top_p" else hws.HWS_SELECT_TOP_K
+        self.score_mode = hws.HWS_SCORE_INDEX if wl.score_mode == "index" else hws.HWS_SCORE_FULL
+        ws = self.ctx.workspace_size(B, self.Nmax, self.score_mode)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=self.dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=self.dev)
+        self.sel_counts = torch.empty((B, Hkv), dtype=torch.int32, device=self.dev)
+
+    def decode(self, *, debug: bool = False, sel_cap: int | None = None, stream=None):
+        """Run one decode step.  With debug=True also return the raw scores and
+        the ascending selected positions (host numpy arrays)."""
+        B, G = self.wl.B, self.wl.G
+        scores = sel_idx = None
+        if debug and self.nR:
+            scores = torch.empty((B, self.nR, self.Nmax, G), dtype=torch.float32, device=self.dev)
+            cap = sel_cap or self.Nmax
+            sel_idx = torch.full((B, self.nR, cap), -1, dtype=torch.int32, device=self.dev)
+        self.ctx.decode(q=self.q, block_tables=self.block_tables, seq_lens=self.seq_lens,
+                        max_seq_len=self.Nmax, select_mode=self.select_mode,
+                        score_mode=self.score_mode, out=self.out, workspace=self.workspace,
+                        top_p=self.top_p, top_k=self.top_k, lse=self.lse,
+                        sel_counts=self.sel_counts, sel_idx=sel_idx, scores=scores, stream=stream)
+        if not debug:
+            return None
+        torch.cuda.synchronize(self.dev)
+        res = {"out": self.out.cpu().numpy(), "lse": self.lse.cpu().numpy(),
+               "sel_counts": self.sel_counts.cpu().numpy()}
+        if scores is not None:
+            res["scores"] = scores.cpu().numpy()
+            res["sel_idx"] = sel_idx.cpu().numpy()
+        return res

@@ -1,0 +1,212 @@
+/*
+ * hws.h — C ABI of libhws: head-wise sparse decode attention on AMD MI355X (gfx950).
+ *
+ * One context serves one attention layer.  Attention heads are split into
+ * retrieval heads and local heads:
+ *   - a retrieval KV head scores every cached token through a 16-dim pre-RoPE
+ *     key index (or, in FULL mode, through the full-dim keys), keeps a dynamic
+ *     top-p or fixed top-k token set and attends over only those rows;
+ *   - a local KV head attends to its attention-sink tokens plus a sliding window.
+ *
+ * Sources (gist.science summary pages; titles as shown on the pages, the first
+ * translated from Arabic):
+ *   [RTPurbo] "Full attention returns in force: converting full attention to
+ *             sparse attention within hundreds of training steps" (arXiv 2605.16928)
+ *   [ICS]     "Inference-time context sparsity: illusion or opportunity?" (arXiv 2605.24168)
+ *   [NHA]     "Native Hybrid Attention for Efficient Sequence Modeling" (arXiv 2510.07019)
+ *   [AoH]     "Autonomy-of-Heads: Data-Free Sparse Attention from Frozen Query-Key
+ *             Geometry" (arXiv 2608.06849)
+ *
+ * Conventions that hold for every call:
+ *   - Return codes only (hws_status); nothing throws or aborts across the ABI.
+ *     hws_last_error(ctx) holds a message for the last failing call on ctx.
+ *   - Every argument is validated on the host before any HIP call, so all
+ *     validation errors are reported without touching a GPU.
+ *   - All device memory is caller-owned and passed as raw device pointers; the
+ *     library never allocates device memory.  Host arrays and structs are
+ *     copied before the call returns.
+ *   - Device work is enqueued on the caller's stream (a hipStream_t passed as
+ *     void*, NULL = the default stream) and is asynchronous: device buffers
+ *     must stay valid until the stream has finished.  No call synchronises.
+ *   - A launch failure returns HWS_ERR_HIP with the HIP error text; a fault
+ *     inside a kernel surfaces at the caller's next synchronisation.
+ *   - A context is not thread-safe: use one context per stream.
+ *
+ * Supported shapes: head_dim 128, index_dim 16, block_size 16, GQA group
+ * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}, num_kv_heads <= 64.
+ * Other values give HWS_ERR_UNSUPPORTED.
+ */
+#ifndef HWS_H
+#define HWS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HWS_ABI_VERSION 1
+
+typedef int32_t hws_status;
+enum {
+  HWS_OK = 0,
+  HWS_ERR_INVALID_ARG = -1, /* null pointer, out-of-range value             */
+  HWS_ERR_STATE = -2,       /* call out of order (e.g. decode before bind)    */
+  HWS_ERR_CAPACITY = -3,    /* sequence longer than the block table allows    */
+  HWS_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required     */
+  HWS_ERR_UNSUPPORTED = -5, /* shape outside the supported set                */
+  HWS_ERR_HIP = -6          /* a HIP launch or runtime call failed            */
+};
+
+/* KV storage type.  FP8 is OCP e4m3fn with one fp32 scale per
+ * (block, KV head, K|V); see hws_append for how scales are set. */
+enum { HWS_KV_BF16 = 0, HWS_KV_FP8_E4M3 = 1 };
+
+/* Head kinds ([RTPurbo] Methodology §1: retrieval heads vs local heads). */
+enum { HWS_HEAD_LOCAL = 0, HWS_HEAD_RETRIEVAL = 1 };
+
+/* Selection rule of retrieval heads ([RTPurbo] Methodology §3). */
+enum { HWS_SELECT_TOP_P = 0, HWS_SELECT_TOP_K = 1 };
+
+/* Selection score: INDEX = 16-dim pre-RoPE index ([RTPurbo] Methodology §2);
+ * FULL = full-dim q.k, i.e. exact "oracle top-k" ([ICS] §2). */
+enum { HWS_SCORE_INDEX = 0, HWS_SCORE_FULL = 1 };
+
+typedef struct hws_ctx hws_ctx; /* opaque host object, owned by the library */
+
+typedef struct {
+  int32_t num_q_heads;        /* Hq                                          */
+  int32_t num_kv_heads;       /* Hkv; query head g uses KV head g / (Hq/Hkv) */
+  int32_t head_dim;           /* d, must be 128                              */
+  int32_t index_dim;          /* r, must be 16                               */
+  int32_t block_size;         /* tokens per KV page, must be 16              */
+  int32_t num_blocks;         /* pages in the pools                          */
+  int32_t max_blocks_per_seq; /* row length of every block table             */
+  int32_t kv_dtype;           /* HWS_KV_*                                    */
+  int32_t n_sink;             /* local heads: sink tokens 0..n_sink-1        */
+  int32_t window;             /* local heads: last `window` tokens           */
+  float attn_scale;           /* softmax scale of attention, e.g. 1/sqrt(d)  */
+  float index_scale;          /* logit = index_scale * (P q).(P k)           */
+  float rope_theta;           /* > 0: rotate-half RoPE with this base; 0: off */
+} hws_config;
+
+/* Caller-owned device buffers.  Layouts (row-major):
+ *   k_pool, v_pool: [num_blocks][Hkv][16][128] bf16, or e4m3 bytes for FP8;
+ *                   K rows are stored after RoPE (when rope_theta > 0).
+ *   kv_scales:      [num_blocks][Hkv][2] fp32 (K scale, V scale); FP8 only.
+ *   index_pool:     [num_blocks][n_retrieval][16][16] fp32, the projected
+ *                   pre-RoPE keys of retrieval heads in KV-head order; may be
+ *                   NULL when no head is a retrieval head.
+ *   proj:           [Hkv][16][128] fp32 index projections (rows of local
+ *                   heads are ignored); may be NULL when no head is retrieval. */
+typedef struct {
+  void* k_pool;
+  void* v_pool;
+  float* kv_scales;
+  float* index_pool;
+  const float* proj;
+} hws_buffers;
+
+/* One decode step for a batch.  Device pointers unless noted. */
+typedef struct {
+  int32_t batch;             /* B >= 1 (host)                                 */
+  int32_t max_seq_len;       /* host upper bound of seq_lens (sizes grids)    */
+  int32_t select_mode;       /* HWS_SELECT_*                                  */
+  int32_t score_mode;        /* HWS_SCORE_*                                   */
+  const void* q;             /* [B][Hq][128] bf16, pre-RoPE queries           */
+  const int32_t* block_tables; /* [B][max_blocks_per_seq] page ids            */
+  const int32_t* seq_lens;   /* [B] context lengths incl. the current token   */
+  const float* top_p;        /* [B] (TOP_P); p >= 1 keeps every token         */
+  const int32_t* top_k;      /* [B] (TOP_K); k >= N keeps every token         */
+  float* out;                /* [B][Hq][128] fp32 attention output            */
+  float* lse;                /* [B][Hq] natural-log LSE over the set, or NULL */
+  int32_t* sel_counts;       /* [B][Hkv] |S| per head, or NULL                */
+  int32_t* sel_idx;          /* [B][n_retrieval][sel_cap] ascending, or NULL  */
+  int32_t sel_cap;           /* row length of sel_idx (host)                  */
+  float* scores;             /* [B][n_retrieval][max_seq_len][G] raw scores
+                                (P q).(P k) or q.k, or NULL (then kept in the
+                                workspace)                                    */
+  void* workspace;           /* hws_workspace_size() bytes                    */
+  size_t workspace_bytes;
+} hws_decode_args;
+
+/* ABI version of the loaded library (HWS_ABI_VERSION). */
+int32_t hws_abi_version(void);
+
+/* Static text for a status code. */
+const char* hws_status_string(hws_status s);
+
+/* Message of the last failing call on ctx ("" if none; ctx may be NULL). */
+const char* hws_last_error(const hws_ctx* ctx);
+
+/* Create a context from cfg (copied).  All heads start as local heads. */
+hws_status hws_create(const hws_config* cfg, hws_ctx** out);
+
+/* Destroy a context (NULL is accepted).  Device buffers are not touched. */
+hws_status hws_destroy(hws_ctx* ctx);
+
+/* Set the head kinds: kinds[Hkv] (host) of HWS_HEAD_*.  Must precede the
+ * first hws_append, because only retrieval heads keep an index
+ * ([RTPurbo] Methodology §1: heads are split offline into H_ret and H_loc). */
+hws_status hws_set_head_kinds(hws_ctx* ctx, const uint8_t* kinds);
+
+/* Classify heads from per-query-head scores (host, [Hq]): scores are
+ * mean-pooled over each GQA group ([AoH] Methodology §4) and the
+ * n_retrieval_kv groups ranked first become retrieval heads.  With
+ * lower_is_retrieval = 1 the lowest scores win (effective rank, [AoH]
+ * Methodology §4); with 0 the highest win (needle calibration, [RTPurbo]
+ * Methodology §1).  Equal scores go to the lower head index.  Same ordering
+ * rule as hws_set_head_kinds. */
+hws_status hws_classify_by_scores(hws_ctx* ctx, const float* q_head_scores,
+                                  int32_t n_retrieval_kv, int32_t lower_is_retrieval);
+
+/* Copy the current head kinds into kinds[Hkv] (host). */
+hws_status hws_get_head_kinds(const hws_ctx* ctx, uint8_t* kinds);
+
+/* Bind the caller's pools (pointers copied; memory stays caller-owned). */
+hws_status hws_bind(hws_ctx* ctx, const hws_buffers* buf);
+
+/* Workspace bytes that hws_decode needs for this batch and length bound. */
+hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq_len,
+                              int32_t score_mode, size_t* bytes);
+
+/* Append n_tok tokens to each of n_seq sequences: token t of sequence s goes to
+ * position start_pos[s] + t, i.e. slot pos % 16 of page
+ * block_tables[s][pos / 16].  k, v: [n_seq][n_tok][Hkv][128] bf16, pre-RoPE.
+ * For each retrieval head the projected key P_h k (fp32, before RoPE) goes to
+ * the index pool ([RTPurbo] Methodology §2).  With RoPE on, K is rotated at its
+ * position and rounded to bf16 before it is stored.  FP8: when a call writes
+ * slot 0 of a page, that page's scale becomes amax/448 over the rows this call
+ * writes into it (1.0 if all zero); later appends into the open page keep the
+ * scale and saturate at +-448.  The KV cache grows by one row per token
+ * ([AoH] Problem statement).  block_tables and start_pos are device arrays;
+ * max_blocks_per_seq (from the config) is the row stride of block_tables. */
+hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t* block_tables,
+                      const int32_t* start_pos, const void* k, const void* v, void* stream);
+
+/* One decode step ([RTPurbo] Methodology §1: retrieval heads switch to dynamic
+ * sparse selection during decoding, local heads use sinks plus a window).
+ * Retrieval head h with query heads g: logits l_{g,i} = index_scale (P q_g).(P k_i)
+ * (INDEX) or attn_scale q_g.k_i (FULL, rotated vectors); a_i = mean_g
+ * softmax_i(l_g); S = top-p set (smallest descending prefix with mass >= p,
+ * all ties at the threshold kept) or top-k set (ties at the k-th value by
+ * lowest position).  Local head: S = {0..n_sink-1} U {N-window..N-1}.  Then
+ * out_g = sum_{i in S} softmax_S(attn_scale q_g.k_i) v_i. */
+hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
+
+/* Optional per-stage timing with HIP events on the decode stream.
+ * hws_profile_enable(ctx, 1) starts recording one event pair per stage per
+ * decode call; hws_profile_read(ctx, ms, calls, n) waits for the recorded
+ * events, writes the summed milliseconds of stage i to ms[i] and the number
+ * of timed calls to calls[i] for i < n, then clears the record.  The stage
+ * names come from hws_profile_stage_name(i) ("" past the last stage). */
+hws_status hws_profile_enable(hws_ctx* ctx, int32_t enable);
+hws_status hws_profile_read(hws_ctx* ctx, double* ms, int32_t* calls, int32_t n);
+const char* hws_profile_stage_name(int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HWS_H */

@@ -1,0 +1,185 @@
+"""C-ABI host tests: library loads, exports every declared symbol, and every
+validation error is reported before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from head_wise_sparse_02_amd import hws
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "hws.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(hws_\w+)\s*\(", text, re.M)))
+
+
+def _cfg(**kw):
+    base = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, index_dim=16, block_size=16,
+                num_blocks=64, max_blocks_per_seq=32, kv_dtype=0, n_sink=4, window=256,
+                attn_scale=0.0883883, index_scale=0.7071, rope_theta=0.0)
+    base.update(kw)
+    return hws.Config(*[base[n] for n, _ in hws.Config._fields_])
+
+
+def _create(**kw):
+    L = hws.lib()
+    h = ctypes.c_void_p()
+    st = L.hws_create(ctypes.byref(_cfg(**kw)), ctypes.byref(h))
+    return st, h
+
+
+def test_library_exports_every_declared_symbol():
+    L = hws.lib()
+    decl = _declared()
+    assert len(decl) >= 15
+    for name in decl:
+        assert hasattr(L, name), name
+    assert sorted(hws.EXPORTED) == decl
+    assert L.hws_abi_version() == 1
+    assert L.hws_status_string(hws.HWS_ERR_WORKSPACE) == b"workspace too small"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), hws.HWS_ERR_UNSUPPORTED),
+    (dict(index_dim=32), hws.HWS_ERR_UNSUPPORTED),
+    (dict(block_size=32), hws.HWS_ERR_UNSUPPORTED),
+    (dict(num_q_heads=6, num_kv_heads=2), hws.HWS_ERR_UNSUPPORTED),     # G = 3
+    (dict(num_q_heads=7, num_kv_heads=2), hws.HWS_ERR_INVALID_ARG),
+    (dict(num_q_heads=128, num_kv_heads=128), hws.HWS_ERR_UNSUPPORTED),  # > 64 KV heads
+    (dict(n_sink=0, window=0), hws.HWS_ERR_INVALID_ARG),
+    (dict(window=-1), hws.HWS_ERR_INVALID_ARG),
+    (dict(attn_scale=0.0), hws.HWS_ERR_INVALID_ARG),
+    (dict(attn_scale=float("nan")), hws.HWS_ERR_INVALID_ARG),
+    (dict(rope_theta=-1.0), hws.HWS_ERR_INVALID_ARG),
+    (dict(kv_dtype=2), hws.HWS_ERR_INVALID_ARG),
+    (dict(num_blocks=0), hws.HWS_ERR_INVALID_ARG),
+])
+def test_create_rejects(kw, status):
+    st, h = _create(**kw)
+    assert st == status and not h.value
+
+
+def test_create_null_arguments():
+    L = hws.lib()
+    h = ctypes.c_void_p()
+    assert L.hws_create(None, ctypes.byref(h)) == hws.HWS_ERR_INVALID_ARG
+    assert L.hws_create(ctypes.byref(_cfg()), None) == hws.HWS_ERR_INVALID_ARG
+    assert L.hws_destroy(None) == hws.HWS_OK
+
+
+def _ctx(**kw):
+    return hws.Context(num_q_heads=kw.get("hq", 8), num_kv_heads=kw.get("hkv", 2), num_blocks=64,
+                       max_blocks_per_seq=32, n_sink=4, window=256, attn_scale=0.088,
+                       index_scale=0.707, kv_dtype=kw.get("kv", 0))
+
+
+def test_head_kinds_and_classification():
+    c = _ctx(hq=32, hkv=8)
+    assert c.head_kinds() == [0] * 8
+    with pytest.raises(hws.HwsError) as e:
+        c.set_head_kinds([0, 1, 2, 0, 0, 0, 0, 0])
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG
+    c.set_head_kinds([1, 0, 0, 1, 0, 0, 0, 0])
+    assert c.head_kinds() == [1, 0, 0, 1, 0, 0, 0, 0]
+    # mean pooling over each group of 4 query heads, then ranking
+    s = [0.0] * 32
+    for g in range(4):
+        s[4 * 5 + g] = 1.0               # group 5 mean 1.0
+        s[4 * 2 + g] = 3.0 if g == 0 else 0.0   # group 2 mean 0.75 (one large head)
+    s[4 * 7] = 4.0                        # group 7 mean 1.0 as well: tie with 5 -> lower index wins
+    c.classify_by_scores(s, 2, lower_is_retrieval=False)
+    assert c.head_kinds() == [0, 0, 0, 0, 0, 1, 0, 1]
+    c.classify_by_scores(s, 1, lower_is_retrieval=False)
+    assert c.head_kinds() == [0, 0, 0, 0, 0, 1, 0, 0]
+    # effective-rank rule: lowest scores become retrieval heads
+    er = [float(10 - h) for h in range(8) for _ in range(4)]
+    c.classify_by_scores(er, 3, lower_is_retrieval=True)
+    assert c.head_kinds() == [0, 0, 0, 0, 0, 1, 1, 1]
+    with pytest.raises(hws.HwsError):
+        c.classify_by_scores(er, 9, lower_is_retrieval=True)
+    with pytest.raises(hws.HwsError):
+        c.classify_by_scores([float("inf")] * 32, 1, lower_is_retrieval=True)
+
+
+def test_bind_and_state_errors():
+    c = _ctx()
+    with pytest.raises(hws.HwsError) as e:
+        c.append(block_tables=8, start_pos=8, k=_FakeT(), v=_FakeT(), stream=0)
+    assert e.value.status == hws.HWS_ERR_STATE
+    with pytest.raises(hws.HwsError) as e:
+        c.bind(0, 16)
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG
+    c8 = _ctx(kv=1)
+    with pytest.raises(hws.HwsError) as e:
+        c8.bind(16, 16)                  # fp8 without scales
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG
+
+
+class _FakeT:
+    """Stand-in for a tensor: only shapes and addresses are read on the host."""
+    def __init__(self, shape=(1, 1, 2, 128), nbytes=1 << 20):
+        self.shape = shape
+        self._n = nbytes
+
+    def data_ptr(self):
+        return 4096
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+
+def _decode(c, **kw):
+    args = dict(q=_FakeT((1, 8, 128)), block_tables=_FakeT(), seq_lens=_FakeT(), max_seq_len=100,
+                select_mode=0, score_mode=0, out=_FakeT(), workspace=_FakeT(nbytes=1 << 30),
+                top_p=_FakeT(), stream=0)
+    args.update(kw)
+    c.decode(**args)
+
+
+def test_decode_validation_without_gpu():
+    c = _ctx()
+    with pytest.raises(hws.HwsError) as e:
+        _decode(c)
+    assert e.value.status == hws.HWS_ERR_STATE          # before bind
+    c.set_head_kinds([1, 0])
+    c.bind(4096, 4096, None, 4096, 4096)
+    cases = [
+        (dict(max_seq_len=32 * 16 + 1), hws.HWS_ERR_CAPACITY),
+        (dict(max_seq_len=0), hws.HWS_ERR_INVALID_ARG),
+        (dict(select_mode=2), hws.HWS_ERR_INVALID_ARG),
+        (dict(score_mode=5), hws.HWS_ERR_INVALID_ARG),
+        (dict(q=None), hws.HWS_ERR_INVALID_ARG),
+        (dict(top_p=None), hws.HWS_ERR_INVALID_ARG),
+        (dict(select_mode=1), hws.HWS_ERR_INVALID_ARG),  # top-k without top_k
+        (dict(sel_idx=_FakeT((1, 1, 0))), hws.HWS_ERR_INVALID_ARG),
+        (dict(workspace=_FakeT(nbytes=100)), hws.HWS_ERR_WORKSPACE),
+        (dict(workspace=None), hws.HWS_ERR_WORKSPACE),
+    ]
+    for kw, status in cases:
+        with pytest.raises(hws.HwsError) as e:
+            _decode(c, **kw)
+        assert e.value.status == status, (kw, e.value)
+        assert hws.lib().hws_last_error(c.handle)
+
+
+def test_workspace_size_rules():
+    c = _ctx()
+    c.set_head_kinds([1, 0])
+    n1 = c.workspace_size(1, 500, 0)
+    n2 = c.workspace_size(2, 500, 0)
+    assert 0 < n1 < n2 and n1 % 256 == 0
+    with pytest.raises(hws.HwsError) as e:
+        c.workspace_size(1, 32 * 16 + 1, 0)
+    assert e.value.status == hws.HWS_ERR_CAPACITY
+    with pytest.raises(hws.HwsError):
+        c.workspace_size(0, 10, 0)
+    # scores region: 4 bytes x G per token per retrieval head at least
+    assert n1 >= 500 * 4 * 4 + 500 * 4
