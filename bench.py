@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark one head-wise sparse decode step on one MI355X.
+
+Default workload: oracle top-k decode at 50x sparsity, B=4, 32 query / 8 KV
+heads, head_dim 128, 131072-token context, bf16 paged KV, every head scoring
+all tokens with full-dim q.k and keeping the exact top 2 % (k = 2621).  A
+"step" is one ``hws_decode`` call: score, select, gather-attend, merge for
+the whole batch.  Inputs (K/V pages, queries, block tables) are resident in
+HBM before the timed region starts.
+
+Prints one JSON line.  ``value`` is decode tokens/s for one attention layer
+(B tokens per step).  ``roofline`` describes the kernel that moves the most
+algorithmic bytes, timed with HIP events on the decode stream over the timed
+region.  ``cpu_baseline`` is the float64 CPU oracle timed on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_GBS = 8000.0          # MI355X HBM3E peak
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+STAGE_KERNEL = {"score": {"index": "score_index_kernel", "full": "score_full_kernel"},
+                "attend": {"index": "attend_kernel", "full": "attend_kernel"}}
+STAGE_SOURCE = {"score": "k_score.hip", "attend": "k_attend.hip"}
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = 128K headline)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cold-iters", type=int, default=20,
+                    help="extra steps each preceded by a 1 GiB cache flush (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
+    return ap.parse_args(argv)
+
+
+# ---------------------------------------------------------------------------
+# byte model: only the bytes the method has to move
+# ---------------------------------------------------------------------------
+
+def algorithmic_bytes(wl, sel_counts) -> dict:
+    """Required HBM bytes of one decode step, by stage.
+
+    score : every token of every retrieval head once: the 16-dim fp32 index
+            (64 B) or, with full-dim scores, the K row (256 B bf16 / 128 B fp8);
+    attend: K and V rows of every selected token (V only with full-dim
+            scores, whose logits are already known) and of the local heads'
+            sinks + window; fp8 adds 8 B of scales per page and head touched;
+    io    : queries (bf16) and outputs (fp32).
+    Scratch (scores, aggregates, histograms, partials) and block-table reads
+    are not counted.
+    """
+    row = 128 if wl.kv_dtype == "fp8" else 256
+    score = attend = 0
+    for b, n in enumerate(wl.seq_lens):
+        for h, kind in enumerate(wl.head_kinds):
+            cnt = int(sel_counts[b, h])
+            if kind == "retrieval":
+                score += n * (row if wl.score_mode == "full" else 64)
+                attend += cnt * (row if wl.score_mode == "full" else 2 * row)
+            else:
+                attend += cnt * 2 * row
+            if wl.kv_dtype == "fp8":
+                attend += 8 * ((cnt + 15) // 16)
+    io = wl.B * wl.Hq * wl.d * (2 + 4)
+    return {"score": score, "attend": attend, "io": io, "total": score + attend + io}
+
+
+def _read_traffic(stage: str, kernel: str, workload: str):
+    """HBM traffic per launch from the committed counter summary, or None if it
+    is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```json\s*(\{.*?\})\s*```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    src = os.path.join(ROOT, "head_wise_sparse_02_amd", "csrc", STAGE_SOURCE[stage])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+def calibrate_copy():
+    import torch
+    n = 1 << 28                                  # 2^28 fp32 = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise copy", "read_bytes": 4 * n, "write_bytes": 4 * n,
+                      "dispatches": 3}), flush=True)
+
+
+def cpu_baseline(wl, setup, reps: int) -> dict:
+    """Time the float64 oracle on the host for the whole decode step."""
+    import numpy as np
+    import oracle as O
+    from head_wise_sparse_02_amd.runner import append_segments
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    times = []
+    for _ in range(max(1, reps)):
+        t0 = time.perf_counter()
+        for b in range(wl.B):
+            seq = setup.host[b]
+            n = wl.seq_lens[b]
+            O.decode_sequence_ref(
+                seq.q, seq.k, seq.v, head_kinds=wl.head_kinds, proj=setup.proj_host,
+                score_mode=wl.score_mode, select_mode=wl.select_mode, top_p=float(wl.top_p[b]),
+                top_k=int(wl.top_k[b]), n_sink=wl.n_sink, window=wl.window,
+                attn_scale=wl.attn_scale, index_scale=wl.index_scale, rope_theta=wl.rope_theta,
+                kv_fp8=wl.kv_dtype == "fp8", segments=append_segments(n))
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": wl.B / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"whole decode step (all {wl.B} sequences x {wl.Hkv} KV heads), "
+                      f"median of {len(times)} runs, {t:.2f} s per step"}
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the decode path "
+              "has no multi-GPU mode in this build.", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+
+    import numpy as np
+    import torch
+    from head_wise_sparse_02_amd import workloads as W
+    from head_wise_sparse_02_amd.runner import DecodeSetup
+
+    wl = W.make_workload(args.config, seed=args.seed)
+    want_cpu = not args.no_cpu_baseline
+    print(f"[bench] building workload {args.config}: {W.CONFIG_NAMES[args.config]}",
+          file=sys.stderr, flush=True)
+    setup = DecodeSetup(wl, keep_host=want_cpu)
+    print("[bench] cache filled; warming up", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        setup.decode()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` decode calls, stage events recorded on the stream
+    ctx = setup.ctx
+    ctx.profile_enable(True)
+    ctx.profile_read()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        setup.decode()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    prof = ctx.profile_read()
+    ctx.profile_enable(False)
+    ms_per_step = total_ms / args.steps
+
+    sel_counts = setup.sel_counts.cpu().numpy()
+    by = algorithmic_bytes(wl, sel_counts)
+    stages = {}
+    for name, (ms, calls) in prof.items():
+        if calls:
+            us = 1000.0 * ms / calls
+            b = by.get(name, 0)
+            stages[name] = {"us": round(us, 2), "bytes": b,
+                            "GBps": round(b / (us * 1e3), 1) if b else None}
+    dom = max(("score", "attend"), key=lambda s: by[s])
+    dom_us = stages[dom]["us"]
+    achieved = by[dom] / (dom_us * 1e3)
+    traffic = _read_traffic(dom, STAGE_KERNEL[dom][wl.score_mode], wl.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
+                "kernel": STAGE_KERNEL[dom][wl.score_mode], "bytes_per_launch": by[dom],
+                "avg_launch_us": dom_us}
+
+    cold = None
+    if args.cold_iters > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        times = []
+        for i in range(args.cold_iters):
+            flush.fill_(float(i))
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            setup.decode()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b_))
+        times.sort()
+        cold = {"p10_ms": round(times[len(times) // 10], 4), "p50_ms": round(statistics.median(times), 4),
+                "p90_ms": round(times[(9 * len(times)) // 10], 4)}
+        del flush
+
+    cpu = cpu_baseline(wl, setup, args.cpu_reps) if want_cpu else None
+
+    step_gbs = by["total"] / (ms_per_step * 1e6)
+    value = wl.B * args.steps / (total_ms / 1000.0)
+    line = {
+        "metric": "sparse decode-attn tokens/s & achieved HBM GB/s (% of peak) at 128K ctx, 1 GPU",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.kv_dtype == "bf16" else "fp8",
+        "data": "synthetic (seeded; shapes and structure of the workload, no dataset or weights)",
+        "config": {"workload": wl.name, "description": W.CONFIG_NAMES[wl.cfg], "batch": wl.B,
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
+                   "context": int(max(wl.seq_lens)), "score_mode": wl.score_mode,
+                   "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype},
+        "step_bytes": by["total"], "step_GBps": round(step_gbs, 1),
+        "step_frac_of_peak": round(step_gbs / PEAK_GBS, 4),
+        "selected_per_head_mean": round(float(sel_counts[:, [h for h in wl.retrieval_heads]].mean()), 1)
+        if wl.retrieval_heads else None,
+        "stages": stages, "cold_cache_step": cold,
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
