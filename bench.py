@@ -168,10 +168,8 @@ def main(argv=None) -> int:
         setup.decode()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` decode calls, stage events recorded on the stream
+    # timed region: exactly `steps` decode calls, nothing else in the stream
     ctx = setup.ctx
-    ctx.profile_enable(True)
-    ctx.profile_read()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -181,9 +179,19 @@ def main(argv=None) -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+
+    # per-kernel durations: the same `steps` decode calls again, each stage's
+    # first/last dispatch carrying HIP timing events on the decode stream (the
+    # events add bubbles between dispatches, so this loop is not the one timed
+    # for `value`)
+    ctx.profile_enable(True)
+    ctx.profile_read()
+    for _ in range(args.steps):
+        setup.decode()
+    torch.cuda.synchronize()
     prof = ctx.profile_read()
     ctx.profile_enable(False)
-    ms_per_step = total_ms / args.steps
 
     sel_counts = setup.sel_counts.cpu().numpy()
     by = algorithmic_bytes(wl, sel_counts)

@@ -33,7 +33,8 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace regions of one decode call.
 struct Layout {
   size_t scores, agg, spart, sel, apart_ml, apart_o, qrot, total;
-  int n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
+  int Nagg;
+  int score_chunk, n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
 };
 
 }  // namespace
@@ -88,10 +89,12 @@ void rebuild_slots(hws_ctx* c) {
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope) {
+Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode) {
   Layout L{};
   const int G = c->G;
-  L.n_score_chunks = cdiv(Nmax, SCORE_CHUNK);
+  // The G=4 full-dim scan (bf16 queries, RoPE off) uses longer chunks.
+  L.score_chunk = (score_mode == HWS_SCORE_FULL && G == 4 && !rope) ? G4_SCORE_CHUNK : SCORE_CHUNK;
+  L.n_score_chunks = cdiv(Nmax, L.score_chunk);
   L.n_sel_chunks = cdiv(Nmax, SEL_CHUNK);
   // Retrieval attention chunk: longer contexts get longer chunks so that the
   // split partials stay small next to the gathered rows.
@@ -103,7 +106,8 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope) {
   const size_t nRb = (size_t)B * c->nR;
   size_t off = 0;
   L.scores = off;   off = align_up(off + nRb * Nmax * G * sizeof(float));
-  L.agg = off;      off = align_up(off + nRb * Nmax * sizeof(float));
+  L.Nagg = (Nmax + 63) & ~63;
+  L.agg = off;      off = align_up(off + nRb * L.Nagg * sizeof(float));
   L.spart = off;    off = align_up(off + nRb * L.n_score_chunks * G * sizeof(float2));
   L.sel = off;      off = align_up(off + nRb * sizeof(SelState));
   const size_t nsp = (size_t)B * c->cfg.num_kv_heads * L.max_splits * G;
@@ -120,21 +124,35 @@ hws_status check_ctx(hws_ctx* ctx) {
   return ctx == nullptr ? HWS_ERR_INVALID_ARG : HWS_OK;
 }
 
-void record(hws_ctx* ctx, hipStream_t s, int stage, bool begin, hipEvent_t* open) {
-  if (!ctx->prof) return;
-  hipEvent_t e;
+// Timing events of one stage (both null when profiling is off).  The events
+// are taken by the first / last dispatch of the stage itself.
+struct StageEv {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+hipEvent_t pool_event(hws_ctx* ctx) {
+  hipEvent_t e = nullptr;
   if (ctx->pool.empty()) {
-    if (hipEventCreate(&e) != hipSuccess) return;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
   } else {
     e = ctx->pool.back();
     ctx->pool.pop_back();
   }
-  hipEventRecord(e, s);
-  if (begin) {
-    *open = e;
-  } else {
-    ctx->recorded.push_back(EvPair{*open, e, stage});
+  return e;
+}
+
+StageEv stage_events(hws_ctx* ctx, int stage) {
+  StageEv ev;
+  if (!ctx->prof) return ev;
+  ev.start = pool_event(ctx);
+  ev.stop = pool_event(ctx);
+  if (ev.start == nullptr || ev.stop == nullptr) {
+    if (ev.start) ctx->pool.push_back(ev.start);
+    if (ev.stop) ctx->pool.push_back(ev.stop);
+    return StageEv{};
   }
+  ctx->recorded.push_back(EvPair{ev.start, ev.stop, stage});
+  return ev;
 }
 
 }  // namespace
@@ -254,7 +272,7 @@ hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq
   if (batch < 1 || max_seq_len < 1) return HWS_ERR_INVALID_ARG;
   if (score_mode != HWS_SCORE_INDEX && score_mode != HWS_SCORE_FULL) return HWS_ERR_INVALID_ARG;
   if ((long long)max_seq_len > (long long)ctx->cfg.max_blocks_per_seq * BS) return HWS_ERR_CAPACITY;
-  *bytes = make_layout(ctx, batch, max_seq_len, ctx->cfg.rope_theta > 0.f).total;
+  *bytes = make_layout(ctx, batch, max_seq_len, ctx->cfg.rope_theta > 0.f, score_mode).total;
   return HWS_OK;
 }
 
@@ -317,8 +335,10 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
       return fail(ctx, HWS_ERR_INVALID_ARG, "index scoring needs index_pool and proj");
   }
   if (a->sel_idx != nullptr && a->sel_cap < 1) return fail(ctx, HWS_ERR_INVALID_ARG, "sel_cap = %d", a->sel_cap);
+  if (ctx->nR > 0 && a->score_mode == HWS_SCORE_FULL && c.kv_dtype != HWS_KV_BF16)
+    return fail(ctx, HWS_ERR_UNSUPPORTED, "full-dim scoring needs a bf16 cache");
   const bool rope = c.rope_theta > 0.f;
-  const Layout L = make_layout(ctx, a->batch, a->max_seq_len, rope);
+  const Layout L = make_layout(ctx, a->batch, a->max_seq_len, rope, a->score_mode);
   if (a->workspace == nullptr || a->workspace_bytes < L.total)
     return fail(ctx, HWS_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, L.total);
 
@@ -331,6 +351,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.nR = ctx->nR;
   p.nL = ctx->nL;
   p.Nmax = a->max_seq_len;
+  p.Nagg = L.Nagg;
   p.max_blocks = c.max_blocks_per_seq;
   p.num_blocks = c.num_blocks;
   p.select_mode = a->select_mode;
@@ -364,6 +385,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.sel_counts = a->sel_counts;
   p.sel_idx = a->sel_idx;
   p.sel_cap = a->sel_cap;
+  p.score_chunk = L.score_chunk;
   p.n_score_chunks = L.n_score_chunks;
   p.n_sel_chunks = L.n_sel_chunks;
   p.ncR = L.ncR;
@@ -376,25 +398,20 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  hipEvent_t open = nullptr;
   if (rope && (e = launch_prep_q(p, s)) != hipSuccess) return hip_fail(ctx, e, "prep_q launch");
   if (ctx->nR > 0) {
-    record(ctx, s, 0, true, &open);
-    if ((e = launch_score(p, s)) != hipSuccess) return hip_fail(ctx, e, "score launch");
-    record(ctx, s, 0, false, &open);
-    record(ctx, s, 1, true, &open);
-    for (int pass = 1; pass <= 3; ++pass)
-      if ((e = launch_select(p, s, pass)) != hipSuccess) return hip_fail(ctx, e, "select launch");
-    if (a->select_mode == HWS_SELECT_TOP_K && (e = launch_select(p, s, 4)) != hipSuccess)
-      return hip_fail(ctx, e, "tie launch");
-    record(ctx, s, 1, false, &open);
+    const StageEv es = stage_events(ctx, 0);
+    if ((e = launch_score(p, s, es.start, es.stop)) != hipSuccess) return hip_fail(ctx, e, "score launch");
+    const StageEv ev = stage_events(ctx, 1);
+    for (int pass = 1; pass <= 3; ++pass) {
+      if ((e = launch_select(p, s, pass, pass == 1 ? ev.start : nullptr, pass == 3 ? ev.stop : nullptr)) != hipSuccess)
+        return hip_fail(ctx, e, "select launch");
+    }
   }
-  record(ctx, s, 2, true, &open);
-  if ((e = launch_attend(p, s)) != hipSuccess) return hip_fail(ctx, e, "attend launch");
-  record(ctx, s, 2, false, &open);
-  record(ctx, s, 3, true, &open);
-  if ((e = launch_merge(p, s)) != hipSuccess) return hip_fail(ctx, e, "merge launch");
-  record(ctx, s, 3, false, &open);
+  const StageEv ea = stage_events(ctx, 2);
+  if ((e = launch_attend(p, s, ea.start, ea.stop)) != hipSuccess) return hip_fail(ctx, e, "attend launch");
+  const StageEv em = stage_events(ctx, 3);
+  if ((e = launch_merge(p, s, em.start, em.stop)) != hipSuccess) return hip_fail(ctx, e, "merge launch");
   if (ctx->nR > 0 && a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess)
     return hip_fail(ctx, e, "emit launch");
   return HWS_OK;

@@ -8,6 +8,19 @@ namespace hws {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// K pages are stored blocked by 32 dims: element (row r, dim d) of a page
+// (16 rows x 128 dims) sits at ((d / 32) * 16 + r) * 32 + d % 32.  One
+// 32-dim block of all 16 rows is then one contiguous 1 KiB (bf16) run, which
+// is exactly one MFMA B-operand load of a wave, and a single row is still
+// four whole 64-byte pieces.  V pages stay row-major.
+__device__ __forceinline__ int kpage_off(int r, int d) { return (((d >> 5) << 4) + r) * 32 + (d & 31); }
+
+// 16-byte load that does not allocate in the caches (data streamed once).
+__device__ __forceinline__ u32x4 load_nt16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -68,6 +81,23 @@ __device__ __forceinline__ unsigned long long load_u64_coherent(const unsigned l
 __device__ __forceinline__ unsigned int load_u32_coherent(const unsigned int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+__device__ __forceinline__ float load_f32_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_f32_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Cross-workgroup hand-off without a device-wide fence.  A device-scope
+// fence on this chip writes back and invalidates the whole L2 of the XCD,
+// serialised across workgroups, so the hand-offs here use only data that is
+// coherent at device scope by construction (device-scope atomics and
+// agent-scope atomic stores/loads, which bypass the non-coherent cache
+// levels).  The writer waits for its outstanding memory operations to be
+// acknowledged before it bumps the arrival counter; the reader reads the
+// data with agent-scope atomic loads after it has seen the counter.
+__device__ __forceinline__ void wait_memory_ops() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

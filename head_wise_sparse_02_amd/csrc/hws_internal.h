@@ -1,6 +1,7 @@
 // Internal definitions shared by the host library and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -14,7 +15,10 @@ constexpr int MAX_KV = 64;        // KV heads per layer
 constexpr int MAX_G = 8;          // query heads per KV head
 
 constexpr int SCORE_CHUNK = 1024; // tokens per scoring workgroup (4 waves x 256)
-constexpr int SEL_CHUNK = 16384;  // tokens per selection workgroup (256 thr x 64)
+constexpr int G4_SCORE_CHUNK = 4096;  // tokens per workgroup of the G=4 full-dim scan
+constexpr int SEL_THREADS = 1024; // threads per selection workgroup
+constexpr int SEL_PER_THREAD = 16;
+constexpr int SEL_CHUNK = SEL_THREADS * SEL_PER_THREAD;   // 16384 tokens
 constexpr int HIST_BINS = 4096;   // pass 1 bins: bits 30..19 of the fp32 pattern
 constexpr int LOCAL_CHUNK = 256;  // rows per local-head attention workgroup
 
@@ -23,8 +27,8 @@ constexpr int LOCAL_CHUNK = 256;  // rows per local-head attention workgroup
 constexpr int P1_SHIFT = 19, P2_SHIFT = 9;
 constexpr int P2_BINS = 1024, P3_BINS = 512;
 
-constexpr uint32_t SEL_FINISHED = 1u;   // tstar / icut are final
-constexpr uint32_t SEL_TIE = 2u;        // top-k: ties at tstar exceed the quota
+constexpr uint32_t SEL_FINISHED = 1u;   // tstar is final
+constexpr uint32_t SEL_TIE = 2u;        // top-k: keep only the `quota` lowest-position ties
 
 // Fixed-point mass: round(a * 2^40) as uint64.  Integer bins make the
 // threshold independent of the order in which workgroups add their counts.
@@ -42,9 +46,8 @@ struct alignas(256) SelState {
   unsigned int tstar;       // threshold pattern (valid once FINISHED)
   unsigned long long mass_above;  // mass strictly above the candidate bin range
   unsigned int cnt_above;   // count strictly above the candidate bin range
-  unsigned int icut;        // ties at tstar kept while position <= icut
-  unsigned int nsel;        // |S|
-  unsigned int quota;       // top-k: ties still to keep
+  unsigned int nsel;        // |S| (top-p: summed by the attention kernel)
+  unsigned int quota;       // top-k with SEL_TIE: ties at tstar to keep
   float lse2[MAX_G];        // per query head log2-sum-exp2 of the logits
 };
 constexpr int SELSTATE_WORDS = (int)(sizeof(SelState) / 4);
@@ -52,6 +55,7 @@ constexpr int SELSTATE_WORDS = (int)(sizeof(SelState) / 4);
 // Everything a decode kernel needs, passed by value.
 struct DecodeParams {
   int B, Hq, Hkv, G, nR, nL, Nmax, max_blocks, num_blocks;
+  int Nagg;                     // row stride of agg (Nmax rounded up to 64)
   int select_mode, score_mode;
   int n_sink, window;
   float attn_scale, index_scale, rope_theta;
@@ -68,7 +72,7 @@ struct DecodeParams {
   const float* index_pool;
   const float* proj;
   float* scores;                // [B][nR][Nmax][G]
-  float* agg;                   // [B][nR][Nmax]
+  float* agg;                   // [B][nR][Nagg]
   float2* spart;                // [B][nR][n_score_chunks][G]  (max, sum) in log2 units
   SelState* sel;                // [B][nR]
   float2* apart_ml;             // [B][Hkv][max_splits][G]  (max, sum)
@@ -79,6 +83,7 @@ struct DecodeParams {
   int* sel_counts;
   int* sel_idx;
   int sel_cap;
+  int score_chunk;              // tokens per scoring workgroup
   int n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
   signed char ret_slot[MAX_KV];
   signed char ret_head[MAX_KV];
@@ -100,12 +105,26 @@ struct AppendParams {
   signed char ret_slot[MAX_KV];
 };
 
+// Launch a kernel; with timing events the start/stop timestamps are taken
+// by the dispatch packet itself (no extra barrier packets in the stream).
+template <typename K, typename... A>
+inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0,
+                                hipEvent_t e1, A... args) {
+  if (e0 != nullptr || e1 != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+  return hipGetLastError();
+}
+
 // Kernel launchers (one translation unit each); return the launch status.
+// e0 / e1: optional timing events recorded at the start / end of the launch.
 hipError_t launch_prep_q(const DecodeParams& p, hipStream_t s);
-hipError_t launch_score(const DecodeParams& p, hipStream_t s);
-hipError_t launch_select(const DecodeParams& p, hipStream_t s, int pass);
-hipError_t launch_attend(const DecodeParams& p, hipStream_t s);
-hipError_t launch_merge(const DecodeParams& p, hipStream_t s);
+hipError_t launch_score(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_select(const DecodeParams& p, hipStream_t s, int pass, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_attend(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_emit(const DecodeParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, int kv_fp8, hipStream_t s);
 

@@ -73,12 +73,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
 
   const size_t row0 = ((size_t)phys * p.Hkv + h) * BS + slot0;
+  const size_t page0 = ((size_t)phys * p.Hkv + h) * BS * D;      // K page (blocked layout)
   if (!FP8) {
     uint16_t* kp = reinterpret_cast<uint16_t*>(p.k_pool);
     uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool);
     for (int e = tid; e < nrows * D; e += 256) {
       const int r = e / D, d = e % D;
-      kp[(row0 + r) * D + d] = f32_to_bf16_rne(ks[r][d]);
+      kp[page0 + kpage_off(slot0 + r, d)] = f32_to_bf16_rne(ks[r][d]);
       vp[(row0 + r) * D + d] = f32_to_bf16_rne(vs[r][d]);
     }
   } else {
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     uint8_t* vp = reinterpret_cast<uint8_t*>(p.v_pool);
     for (int e = tid; e < nrows * D; e += 256) {
       const int r = e / D, d = e % D;
-      kp[(row0 + r) * D + d] = e4m3_encode(ks[r][d] / kscale);
+      kp[page0 + kpage_off(slot0 + r, d)] = e4m3_encode(ks[r][d] / kscale);
       vp[(row0 + r) * D + d] = e4m3_encode(vs[r][d] / vscale);
     }
   }

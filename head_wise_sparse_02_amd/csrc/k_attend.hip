@@ -1,33 +1,37 @@
-// Split-K decode attention over a token set, and the log-sum-exp merge.
+// Split-K decode attention over a token set, and the log-sum-exp merge of the
+// splits.
 //
 // Retrieval heads ([ICS] "Inference-time context sparsity: illusion or
 // opportunity?", §3c: sparse decode reads only the selected rows, O(k d)
 // instead of O(N d)): a workgroup owns a chunk of positions, keeps the tokens
 // of the chunk that pass the threshold found by the selection passes
-// (a_i > t*, or a_i == t* and position <= icut), and gathers their K/V rows
-// through the block table.  In FULL score mode the attention logits are the
-// stored full-dim scores, so only V rows are read.
+// (a_i > t*, or a_i == t* -- for top-k only the lowest-position ties up to the
+// budget), and gathers their K/V rows through the block table.  In FULL score
+// mode the attention logits are the stored full-dim scores, so only V rows
+// are read.
 //
 // Local heads ([RTPurbo] "Full attention returns in force ...", Methodology §1;
 // [AoH] "Autonomy-of-Heads ...", Methodology §4): the rows are the sinks
 // 0..n_sink-1 followed by the window N-w..N-1 (a position in both once),
 // split into chunks of LOCAL_CHUNK rows.
 //
-// Each workgroup emits (max, sum, unnormalised output) per query head in
-// log2 units; merge_kernel combines the splits.
+// Each workgroup produces (max, sum, unnormalised output) per query head in
+// log2 units; merge_kernel combines them.
 #include "hws_device.h"
 
 namespace hws {
 
 constexpr int ATT_ROWS_MAX = 4096;   // largest retrieval chunk (LDS row list)
-constexpr int RB = 4;                // rows per 16-lane processor per batch
 
-__device__ __forceinline__ unsigned int block_rank(bool f, unsigned int* tmp) {
+// Exclusive scan of a per-thread count over a 256-thread block; total in tmp[4].
+__device__ __forceinline__ unsigned int block_excl_scan256(unsigned int v, unsigned int* tmp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const unsigned long long bal = __ballot(f);
-  const unsigned int below = __builtin_amdgcn_mbcnt_hi((unsigned int)(bal >> 32),
-                                 __builtin_amdgcn_mbcnt_lo((unsigned int)bal, 0u));
-  if (lane == 0) tmp[wave] = (unsigned int)__popcll(bal);
+  unsigned int inc = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned int t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) tmp[wave] = inc;
   __syncthreads();
   unsigned int off = 0;
   for (int w = 0; w < wave; ++w) off += tmp[w];
@@ -35,10 +39,10 @@ __device__ __forceinline__ unsigned int block_rank(bool f, unsigned int* tmp) {
   __syncthreads();
   if (tid == 0) tmp[4] = tot;
   __syncthreads();
-  return off + below;
+  return off + inc - v;
 }
 
-// Load 8 consecutive elements of a K or V row as fp32 (bf16 or e4m3 codes).
+// Load 8 consecutive elements of a V row as fp32 (bf16 or e4m3 codes).
 template <bool FP8>
 __device__ __forceinline__ void load_row8(const void* pool, size_t row_off, int sub, float* x) {
   if (!FP8) {
@@ -57,8 +61,42 @@ __device__ __forceinline__ void load_row8(const void* pool, size_t row_off, int 
   }
 }
 
-template <int G, bool FP8, bool FULL, bool ROPE>
+// 8 consecutive dims 8*sub..8*sub+7 of row r of a K page (blocked layout).
+template <bool FP8>
+__device__ __forceinline__ void load_krow8(const void* pool, size_t page, int r, int sub, float* x) {
+  const size_t off = page * (BS * D) + (size_t)(((sub >> 2) << 4) + r) * 32 + 8 * (sub & 3);
+  if (!FP8) {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(pool) + off);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(pool) + off);
+    f32x2 t;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false); x[0] = t.x; x[1] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);  x[2] = t.x; x[3] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false); x[4] = t.x; x[5] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);  x[6] = t.x; x[7] = t.y;
+  }
+}
+
+// Ties at t* in positions [0, lo) of one (b, retrieval head).  Only reached
+// for top-k when the ties at the threshold exceed the budget.
+__device__ unsigned int ties_before(const float* agg, int lo, unsigned int tstar, unsigned int* tmp) {
+  unsigned int cnt = 0;
+  for (int i = threadIdx.x; i < lo; i += 256) cnt += (__float_as_uint(agg[i]) == tstar) ? 1u : 0u;
+  block_excl_scan256(cnt, tmp);
+  const unsigned int tot = tmp[4];
+  __syncthreads();
+  return tot;
+}
+
+// MODE 0: rows need K (index scoring or local heads); MODE 1: FULL scoring and
+// retrieval heads only (logits from the stored scores, V rows only);
+// MODE 2: FULL scoring with local heads present (both paths).
+template <int G, bool FP8, int MODE, bool ROPE>
 __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
+  constexpr bool NEED_K = MODE != 1;
+  constexpr int RB = (MODE == 1 || G <= 4) ? 8 : 2;   // rows per 16-lane processor per batch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int proc = tid >> 4, sub = tid & 15;     // 16 row processors of 16 lanes
   const int w = blockIdx.x;
@@ -79,66 +117,109 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   }
   const bool is_ret = hr >= 0;
   const int N = min(p.seq_lens[b], p.Nmax);
+  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
 
-  __shared__ int rows_s[ATT_ROWS_MAX];
+  __shared__ unsigned short rows_s[ATT_ROWS_MAX];   // retrieval: offset in the chunk
+  __shared__ int pages_s[LOCAL_CHUNK];              // retrieval: chunk pages; local: row pages
+  __shared__ int ltok_s[LOCAL_CHUNK];               // local: row tokens
   __shared__ unsigned int tmp[8];
   __shared__ float wm[4][MAX_G], wl[4][MAX_G];
   __shared__ float wo[4][MAX_G][D];
 
-  int nrows = 0;
+  int nrows = 0, lo = 0;
   if (is_ret) {
-    const int lo = split * p.att_chunk_R;
-    const int hi = min(N, lo + p.att_chunk_R);
+    const int chunk = p.att_chunk_R;
+    const int per = chunk / 256;                 // 4, 8 or 16 positions per thread
+    lo = split * chunk;
+    const int hi = min(N, lo + chunk);
     if (lo < hi) {
       const SelState* st = p.sel + (size_t)b * p.nR + hr;
-      const unsigned int tstar = st->tstar, icut = st->icut;
-      const float* agg = p.agg + (size_t)(b * p.nR + hr) * p.Nmax;
-      for (int base = lo; base < hi; base += 256) {
-        const int i = base + tid;
-        bool f = false;
-        if (i < hi) {
-          const unsigned int bits = __float_as_uint(agg[i]);
-          f = bits > tstar || (bits == tstar && (unsigned int)i <= icut);
+      const unsigned int tstar = st->tstar, flags = st->flags;
+      const float* agg = p.agg + (size_t)(b * p.nR + hr) * p.Nagg;
+      const int i0 = lo + tid * per;
+      float av[16];
+      if (i0 + per <= hi) {
+        for (int j = 0; j < per; j += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(agg + i0 + j);
+          av[j] = v.x; av[j + 1] = v.y; av[j + 2] = v.z; av[j + 3] = v.w;
         }
-        const unsigned int rank = block_rank(f, tmp);
-        if (f) rows_s[nrows + rank] = i;
-        nrows += (int)tmp[4];
-        __syncthreads();
+      } else {
+        for (int j = 0; j < per; ++j) av[j] = (i0 + j < hi) ? agg[i0 + j] : -1.0f;
       }
+      const int npg = (hi - lo + BS - 1) / BS;
+      if (tid < npg) pages_s[tid] = bt[(lo >> 4) + tid];
+      unsigned int gt_mask = 0, eq_mask = 0;
+      for (int j = 0; j < per; ++j) {
+        const unsigned int bits = __float_as_uint(av[j]);
+        if (i0 + j < hi) {
+          if (bits > tstar) gt_mask |= 1u << j;
+          else if (bits == tstar) eq_mask |= 1u << j;
+        }
+      }
+      if (flags & SEL_TIE) {
+        // keep a tie only while its position-ordered rank stays below the quota
+        const unsigned int before = ties_before(agg, lo, tstar, tmp);
+        const unsigned int quota = st->quota;
+        const unsigned int myrank = block_excl_scan256((unsigned int)__popc(eq_mask), tmp) + before;
+        unsigned int r = myrank, keep = 0;
+        for (int j = 0; j < per; ++j)
+          if (eq_mask & (1u << j)) { if (r < quota) keep |= 1u << j; ++r; }
+        eq_mask = keep;
+      }
+      const unsigned int mask = gt_mask | eq_mask;
+      const unsigned int off = block_excl_scan256((unsigned int)__popc(mask), tmp);
+      nrows = (int)tmp[4];
+      if (p.select_mode == 0 && tid == 0 && nrows > 0)        // top-p: |S| summed over chunks
+        atomicAdd(&p.sel[(size_t)b * p.nR + hr].nsel, (unsigned int)nrows);
+      unsigned int k = off;
+      for (int j = 0; j < per; ++j)
+        if (mask & (1u << j)) rows_s[k++] = (unsigned short)(i0 + j - lo);
+      __syncthreads();
     }
-  } else {
+  } else if (MODE != 1) {
     const int L1 = min(p.n_sink, N);
     const int start2 = max(L1, N - p.window);
     const int L = L1 + (N - start2);
-    const int lo = split * LOCAL_CHUNK;
-    const int hi = min(L, lo + LOCAL_CHUNK);
-    for (int r = lo + tid; r < hi; r += 256) rows_s[r - lo] = r < L1 ? r : start2 + (r - L1);
-    nrows = max(0, hi - lo);
+    const int llo = split * LOCAL_CHUNK;
+    const int hi = min(L, llo + LOCAL_CHUNK);
+    const int r = llo + tid;
+    if (r < hi) {
+      const int tok = r < L1 ? r : start2 + (r - L1);
+      ltok_s[tid] = tok;
+      pages_s[tid] = bt[tok >> 4];
+    }
+    nrows = max(0, hi - llo);
     __syncthreads();
   }
 
   float2* ml = p.apart_ml + ((size_t)(b * p.Hkv + h) * p.max_splits + split) * G;
+  float* po = p.apart_o + (((size_t)(b * p.Hkv + h) * p.max_splits + split) * G) * D;
   if (nrows == 0) {
     if (tid < G) ml[tid] = make_float2(NEG_INF, 0.f);
     return;
   }
-
-  const bool use_scores = FULL && is_ret;
+  const bool use_scores = MODE != 0 && is_ret;
   // queries of the group, pre-scaled to log2 units: dims 8*sub..8*sub+7
-  float qf[G][8];
-  if (!use_scores) {
+  float qf[NEED_K ? G : 1][8];
+  if (NEED_K && !use_scores) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < (NEED_K ? G : 1); ++g) {
       const size_t qo = ((size_t)b * p.Hq + h * G + g) * D + 8 * sub;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = ROPE ? p.qrot[qo + j] : bf16_to_f32(p.q[qo + j]);
-        qf[g][j] = x * p.c2_attn;
+      if (ROPE) {
+        const float4 a = *reinterpret_cast<const float4*>(p.qrot + qo);
+        const float4 c = *reinterpret_cast<const float4*>(p.qrot + qo + 4);
+        qf[g][0] = a.x; qf[g][1] = a.y; qf[g][2] = a.z; qf[g][3] = a.w;
+        qf[g][4] = c.x; qf[g][5] = c.y; qf[g][6] = c.z; qf[g][7] = c.w;
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(p.q + qo);
+        qf[g][0] = bf16_lo(u.x); qf[g][1] = bf16_hi(u.x); qf[g][2] = bf16_lo(u.y); qf[g][3] = bf16_hi(u.y);
+        qf[g][4] = bf16_lo(u.z); qf[g][5] = bf16_hi(u.z); qf[g][6] = bf16_lo(u.w); qf[g][7] = bf16_hi(u.w);
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[g][j] *= p.c2_attn;
     }
   }
 
-  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
   const float* sc = use_scores ? p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G : nullptr;
   float m[G], l[G], o[G][8];
 #pragma unroll
@@ -156,14 +237,24 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     for (int u = 0; u < RB; ++u) {
       const int r = r0 + u;
       const bool valid = r < nrows;
-      const int i = valid ? rows_s[r] : 0;
-      const int pg = bt[i >> 4];
+      int i = 0, pg = 0;
+      if (valid) {
+        if (is_ret) {
+          const int off = rows_s[r];
+          i = lo + off;
+          pg = pages_s[off >> 4];
+        } else {
+          i = ltok_s[r];
+          pg = pages_s[r];
+        }
+      }
       const bool ok = valid && (unsigned)pg < (unsigned)p.num_blocks;
       const size_t row_off = ((size_t)(ok ? pg : 0) * p.Hkv + h) * BS + (i & 15);
       float ks = 1.f, vs = 1.f;
       if (FP8 && ok) {
-        ks = p.kv_scales[((size_t)pg * p.Hkv + h) * 2 + 0];
-        vs = p.kv_scales[((size_t)pg * p.Hkv + h) * 2 + 1];
+        const float2 s2 = *reinterpret_cast<const float2*>(p.kv_scales + ((size_t)pg * p.Hkv + h) * 2);
+        ks = s2.x;
+        vs = s2.y;
       }
       if (ok) {
         load_row8<FP8>(p.v_pool, row_off, sub, vv[u]);
@@ -176,21 +267,33 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
         for (int j = 0; j < 8; ++j) vv[u][j] *= vs;
       }
       if (use_scores) {
+        if (G >= 4) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) z[u][g] = ok ? sc[(size_t)i * G + g] * p.c2_score : NEG_INF;
-      } else {
+          for (int q4 = 0; q4 < G / 4; ++q4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (ok) v = *reinterpret_cast<const float4*>(sc + (size_t)i * G + 4 * q4);
+            z[u][4 * q4 + 0] = ok ? v.x * p.c2_score : NEG_INF;
+            z[u][4 * q4 + 1] = ok ? v.y * p.c2_score : NEG_INF;
+            z[u][4 * q4 + 2] = ok ? v.z * p.c2_score : NEG_INF;
+            z[u][4 * q4 + 3] = ok ? v.w * p.c2_score : NEG_INF;
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) z[u][g] = ok ? sc[(size_t)i * G + g] * p.c2_score : NEG_INF;
+        }
+      } else if (NEED_K) {
         float kx[8];
         if (ok) {
-          load_row8<FP8>(p.k_pool, row_off, sub, kx);
+          load_krow8<FP8>(p.k_pool, (size_t)pg * p.Hkv + h, i & 15, sub, kx);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) kx[j] = 0.f;
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          float a = qf[g][0] * kx[0];
+          float a = qf[NEED_K ? g : 0][0] * kx[0];
 #pragma unroll
-          for (int j = 1; j < 8; ++j) a = fmaf(qf[g][j], kx[j], a);
+          for (int j = 1; j < 8; ++j) a = fmaf(qf[NEED_K ? g : 0][j], kx[j], a);
           a += __shfl_xor(a, 1);
           a += __shfl_xor(a, 2);
           a += __shfl_xor(a, 4);
@@ -249,7 +352,6 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
-  float* po = p.apart_o + (((size_t)(b * p.Hkv + h) * p.max_splits + split) * G) * D;
   for (int e = tid; e < G * D; e += 256) {
     const int g = e / D, d = e % D;
     float mm = NEG_INF;
@@ -266,35 +368,50 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   }
 }
 
-// out_g = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);  lse = (M + log2 L) ln 2
-__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int G = p.G;
+// out_g = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);  lse = (M + log2 L) ln 2.
+// One workgroup per (sequence, KV head, query head), one thread per dim; the
+// partials of up to 32 splits are loaded at once and folded in online.
+template <int G>
+__global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
+  constexpr int SB = 32;
+  const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int hr = p.ret_slot[h];
   const int nspl = hr >= 0 ? p.ncR : p.ncL;
   const int N = min(p.seq_lens[b], p.Nmax);
-  const float2* ml = p.apart_ml + (size_t)(b * p.Hkv + h) * p.max_splits * G;
-  const float* po = p.apart_o + (size_t)(b * p.Hkv + h) * p.max_splits * G * D;
-  for (int e = tid; e < G * D; e += 256) {
-    const int g = e / D, d = e % D;
-    float M = NEG_INF;
-    for (int s = 0; s < nspl; ++s) {
-      const float2 v = ml[s * G + g];
-      if (v.y > 0.f) M = fmaxf(M, v.x);
+  const size_t base = (size_t)(b * p.Hkv + h) * p.max_splits * G + g;
+  const float2* ml = p.apart_ml + base;                 // split s at ml[s * G]
+  const float* po = p.apart_o + base * D + d;           // split s at po[s * G * D]
+  float M = NEG_INF, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < nspl; s0 += SB) {
+    float2 v[SB];
+    float ov[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const bool in = s0 + u < nspl;
+      v[u] = in ? ml[(size_t)(s0 + u) * G] : make_float2(NEG_INF, 0.f);
+      ov[u] = in ? po[(size_t)(s0 + u) * G * D] : 0.f;
     }
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < nspl; ++s) {
-      const float2 v = ml[s * G + g];
-      if (v.y > 0.f) {
-        const float wgt = fast_exp2(v.x - M);
-        L += v.y * wgt;
-        O += po[((size_t)s * G + g) * D + d] * wgt;
+    float mt = M;
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+      if (v[u].y > 0.f) mt = fmaxf(mt, v[u].x);
+    if (mt == NEG_INF) continue;
+    const float cf = fast_exp2(M - mt);                 // 0 while nothing was folded in
+    L *= cf;
+    O *= cf;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      if (v[u].y > 0.f) {                               // empty splits left no output
+        const float w = fast_exp2(v[u].x - mt);
+        L = fmaf(v[u].y, w, L);
+        O = fmaf(ov[u], w, O);
       }
     }
-    p.out[((size_t)b * p.Hq + h * G + g) * D + d] = L > 0.f ? O / L : 0.f;
-    if (d == 0 && p.lse != nullptr) p.lse[(size_t)b * p.Hq + h * G + g] = (M + log2f(L)) * LN2;
+    M = mt;
   }
-  if (tid == 0 && p.sel_counts != nullptr) {
+  p.out[((size_t)b * p.Hq + h * G + g) * D + d] = L > 0.f ? O / L : 0.f;
+  if (d == 0 && p.lse != nullptr) p.lse[(size_t)b * p.Hq + h * G + g] = (M + log2f(L)) * LN2;
+  if (g == 0 && d == 0 && p.sel_counts != nullptr) {
     int cnt;
     if (hr >= 0) {
       cnt = (int)p.sel[(size_t)b * p.nR + hr].nsel;
@@ -323,36 +440,44 @@ __global__ __launch_bounds__(64) void prep_q_kernel(DecodeParams p) {
 }
 
 template <int G, bool FP8>
-static hipError_t launch_attend_g(const DecodeParams& p, hipStream_t s) {
+static hipError_t launch_attend_g(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int nwg = p.B * (p.nR * p.ncR + p.nL * p.ncL);
-  if (nwg == 0) return hipSuccess;
   const bool full = p.score_mode == 1, rope = p.qrot != nullptr;
-  if (full && rope) hipLaunchKernelGGL((attend_kernel<G, FP8, true, true>), dim3(nwg), dim3(256), 0, s, p);
-  else if (full) hipLaunchKernelGGL((attend_kernel<G, FP8, true, false>), dim3(nwg), dim3(256), 0, s, p);
-  else if (rope) hipLaunchKernelGGL((attend_kernel<G, FP8, false, true>), dim3(nwg), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((attend_kernel<G, FP8, false, false>), dim3(nwg), dim3(256), 0, s, p);
-  return hipGetLastError();
+  const dim3 grid(nwg), blk(256);
+  if (!full) {
+    if (rope) return launch_kernel(attend_kernel<G, FP8, 0, true>, grid, blk, s, e0, e1, p);
+    return launch_kernel(attend_kernel<G, FP8, 0, false>, grid, blk, s, e0, e1, p);
+  }
+  if (p.nL == 0) return launch_kernel(attend_kernel<G, FP8, 1, false>, grid, blk, s, e0, e1, p);
+  if (rope) return launch_kernel(attend_kernel<G, FP8, 2, true>, grid, blk, s, e0, e1, p);
+  return launch_kernel(attend_kernel<G, FP8, 2, false>, grid, blk, s, e0, e1, p);
 }
 
 template <int G>
-static hipError_t launch_attend_fp(const DecodeParams& p, hipStream_t s, bool fp8) {
-  return fp8 ? launch_attend_g<G, true>(p, s) : launch_attend_g<G, false>(p, s);
+static hipError_t launch_attend_fp(const DecodeParams& p, hipStream_t s, bool fp8, hipEvent_t e0, hipEvent_t e1) {
+  return fp8 ? launch_attend_g<G, true>(p, s, e0, e1) : launch_attend_g<G, false>(p, s, e0, e1);
 }
 
-hipError_t launch_attend(const DecodeParams& p, hipStream_t s) {
+hipError_t launch_attend(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const bool fp8 = p.kv_scales != nullptr;
   switch (p.G) {
-    case 1: return launch_attend_fp<1>(p, s, fp8);
-    case 2: return launch_attend_fp<2>(p, s, fp8);
-    case 4: return launch_attend_fp<4>(p, s, fp8);
-    case 8: return launch_attend_fp<8>(p, s, fp8);
+    case 1: return launch_attend_fp<1>(p, s, fp8, e0, e1);
+    case 2: return launch_attend_fp<2>(p, s, fp8, e0, e1);
+    case 4: return launch_attend_fp<4>(p, s, fp8, e0, e1);
+    case 8: return launch_attend_fp<8>(p, s, fp8, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(p.Hkv, p.B), dim3(256), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 grid(p.G, p.Hkv, p.B), blk(D);
+  switch (p.G) {
+    case 1: return launch_kernel(merge_kernel<1>, grid, blk, s, e0, e1, p);
+    case 2: return launch_kernel(merge_kernel<2>, grid, blk, s, e0, e1, p);
+    case 4: return launch_kernel(merge_kernel<4>, grid, blk, s, e0, e1, p);
+    case 8: return launch_kernel(merge_kernel<8>, grid, blk, s, e0, e1, p);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prep_q(const DecodeParams& p, hipStream_t s) {

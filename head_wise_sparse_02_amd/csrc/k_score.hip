@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
   const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int N = min(p.seq_lens[b], p.Nmax);
-  const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;
+  const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;  // == p.score_chunk here
   SelState* st = p.sel + (size_t)b * p.nR + hr;
   if (c >= nchunks) return;
   zero_state_share(st, c, nchunks);
@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
       if ((unsigned)blk < (unsigned)p.num_blocks) {
         const float4* src = reinterpret_cast<const float4*>(
             p.index_pool + ((size_t)blk * p.nR + hr) * (BS * R));
-        kv[i] = src[lane];
+        const u32x4 w = load_nt16(src + lane);
+        kv[i] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
       }
     }
   }
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
 // FULL mode (MFMA).  A = query tile: row g < G holds q_g (bf16); with RoPE on
 // rows G..2G-1 hold the bf16 residual q_g - bf16(q_g) of the rotated fp32
 // query, so hi + lo carries ~16 mantissa bits.  B = 32 dims x 16 tokens of
-// one page.  Lane l supplies row/column l%16 and the 8 consecutive
+// one page, read from the dim-blocked K page as one contiguous 1 KiB run per
+// step with non-temporal loads.  Lane l supplies row/column l%16 and the 8 consecutive
 // contraction elements 8*(l/16)..+7 of each 32-wide step; both operands use
 // the same dim for the same (lane, element), so the product sums over all
 // 128 dims.  C[row][col] sits in lane col + 16*(row/4), element row%4.
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int N = min(p.seq_lens[b], p.Nmax);
-  const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;
+  const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;  // == p.score_chunk here
   SelState* st = p.sel + (size_t)b * p.nR + hr;
   if (c >= nchunks) return;
   zero_state_share(st, c, nchunks);
@@ -206,10 +208,10 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
       int blk = -1;
       if (tpage[u] < N) blk = bt[pg];
       if ((unsigned)blk < (unsigned)p.num_blocks) {
-        const bf16x8* src = reinterpret_cast<const bf16x8*>(
-            kpool + (((size_t)blk * p.Hkv + h) * BS + row) * D + 8 * quad);
+        // blocked page: step s of all 16 rows is one contiguous 1 KiB run
+        const uint16_t* src = kpool + ((size_t)blk * p.Hkv + h) * (BS * D) + row * 32 + 8 * quad;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag[u][s] = src[4 * s];
+        for (int s = 0; s < 4; ++s) bfrag[u][s] = __builtin_bit_cast(bf16x8, load_nt16(src + 512 * s));
       } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s) bfrag[u][s] = (bf16x8)(__bf16)0.f;
@@ -273,25 +275,124 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   }
 }
 
-template <int G>
-static hipError_t launch_score_g(const DecodeParams& p, hipStream_t st) {
-  dim3 grid(p.n_score_chunks, p.nR, p.B);
-  if (p.score_mode == 0) {
-    hipLaunchKernelGGL(score_index_kernel<G>, grid, dim3(256), 0, st, p);
-  } else if (p.qrot != nullptr) {
-    hipLaunchKernelGGL((score_full_kernel<G, true>), grid, dim3(256), 0, st, p);
-  } else {
-    hipLaunchKernelGGL((score_full_kernel<G, false>), grid, dim3(256), 0, st, p);
+// FULL mode, G = 4 query heads per KV head, unrotated (exact bf16) queries.
+// The query tile is replicated into all four 4-row groups of the 16-row A
+// operand, and four pages are multiplied into four accumulators, so lane l
+// (quad u = l/16) keeps accumulator u: the 4 scores of token l%16 of page u.
+// Every lane then owns one token, and a wave's 64 tokens x 4 scores are one
+// contiguous 1 KiB block.  The blocks are staged in LDS and the workgroup
+// writes its CH x 16 bytes of scores in one burst after its last page:
+// interleaving small writes with the K stream costs read bandwidth.
+template <int CH>
+__global__ __launch_bounds__(256) void score_full_g4_kernel(DecodeParams p) {
+  constexpr int G = 4;
+  constexpr int PW = CH / BS / 4;                          // pages per wave
+  const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
+  const int N = min(p.seq_lens[b], p.Nmax);
+  const int nchunks = (N + CH - 1) / CH;
+  SelState* st = p.sel + (size_t)b * p.nR + hr;
+  if (c >= nchunks) return;
+  zero_state_share(st, c, nchunks);
+
+  const int h = p.ret_head[hr];
+  const int row = lane & 15, quad = lane >> 4;
+  __shared__ float red_m[4][G], red_s[4][G];
+  __shared__ f32x4 stage[CH];                              // this chunk's scores
+
+  bf16x8 afrag[4];
+  {
+    const uint16_t* qg = p.q + ((size_t)b * p.Hq + h * G + (row & 3)) * D + 8 * quad;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) afrag[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qg + 32 * s));
   }
-  return hipGetLastError();
+
+  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
+  const float c2 = p.c2_score;
+  float m[4], sm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = NEG_INF; sm[i] = 0.f; }
+
+  const int page0 = c * (CH / BS) + wave * PW;
+#pragma unroll 1
+  for (int i0 = 0; i0 < PW; i0 += 4) {
+    const int pgb = page0 + i0;
+    if (pgb * BS >= N) break;                              // wave-uniform
+    bf16x8 bfrag[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int blk = -1;
+      if ((pgb + u) * BS < N) blk = bt[pgb + u];
+      if ((unsigned)blk < (unsigned)p.num_blocks) {
+        // dim-blocked page: step s of all 16 rows is one contiguous 1 KiB run
+        const uint16_t* src = kpool + ((size_t)blk * p.Hkv + h) * (BS * D) + row * 32 + 8 * quad;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag[u][s] = __builtin_bit_cast(bf16x8, load_nt16(src + 512 * s));
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag[u][s] = (bf16x8)(__bf16)0.f;
+      }
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s], bfrag[u][s], acc[u], 0, 0, 0);
+    }
+    f32x4 v = acc[0];
+    v = quad == 1 ? acc[1] : v;
+    v = quad == 2 ? acc[2] : v;
+    v = quad == 3 ? acc[3] : v;
+    stage[(wave * PW + i0) * BS + lane] = v;
+    const int t = pgb * BS + lane;                         // token of this lane
+    if (t < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = v[i] * c2;
+        const float mn = fmaxf(m[i], x);
+        sm[i] = sm[i] * fast_exp2(m[i] - mn) + fast_exp2(x - mn);
+        m[i] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wave_lse_reduce(m[i], sm[i], 1, 32);
+    if (lane == 0) { red_m[wave][i] = m[i]; red_s[wave][i] = sm[i]; }
+  }
+  __syncthreads();
+  float* out = p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G;
+  const int t0 = c * CH;
+#pragma unroll
+  for (int k = 0; k < CH / 256; ++k) {
+    const int e = k * 256 + tid;
+    if (t0 + e < N) __builtin_nontemporal_store(stage[e], reinterpret_cast<f32x4*>(out + (size_t)(t0 + e) * G));
+  }
+  if (tid < G) {
+    float mm = red_m[0][tid], ss = red_s[0][tid];
+    for (int w = 1; w < 4; ++w) lse_combine(mm, ss, red_m[w][tid], red_s[w][tid]);
+    p.spart[((size_t)(b * p.nR + hr) * p.n_score_chunks + c) * G + tid] = make_float2(mm, ss);
+  }
 }
 
-hipError_t launch_score(const DecodeParams& p, hipStream_t st) {
+template <int G>
+static hipError_t launch_score_g(const DecodeParams& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 grid(p.n_score_chunks, p.nR, p.B), blk(256);
+  if (p.score_mode == 0) return launch_kernel(score_index_kernel<G>, grid, blk, st, e0, e1, p);
+  if (p.qrot != nullptr) return launch_kernel(score_full_kernel<G, true>, grid, blk, st, e0, e1, p);
+  if (G == 4) return launch_kernel(score_full_g4_kernel<G4_SCORE_CHUNK>, grid, blk, st, e0, e1, p);
+  return launch_kernel(score_full_kernel<G, false>, grid, blk, st, e0, e1, p);
+}
+
+hipError_t launch_score(const DecodeParams& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (p.G) {
-    case 1: return launch_score_g<1>(p, st);
-    case 2: return launch_score_g<2>(p, st);
-    case 4: return launch_score_g<4>(p, st);
-    case 8: return launch_score_g<8>(p, st);
+    case 1: return launch_score_g<1>(p, st, e0, e1);
+    case 2: return launch_score_g<2>(p, st, e0, e1);
+    case 4: return launch_score_g<4>(p, st, e0, e1);
+    case 8: return launch_score_g<8>(p, st, e0, e1);
   }
   return hipErrorInvalidValue;
 }

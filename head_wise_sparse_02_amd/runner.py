@@ -45,8 +45,9 @@ class DecodeSetup:
 
         # pools and a seeded random page assignment (pages are not contiguous)
         kv_dt = torch.uint8 if self.fp8 else torch.bfloat16
-        self.k_pool = torch.zeros((self.num_blocks, Hkv, 16, d), dtype=kv_dt, device=self.dev)
-        self.v_pool = torch.zeros_like(self.k_pool)
+        # K pages are dim-blocked [4][16][32]; V pages are row-major [16][128]
+        self.k_pool = torch.zeros((self.num_blocks, Hkv, 4, 16, 32), dtype=kv_dt, device=self.dev)
+        self.v_pool = torch.zeros((self.num_blocks, Hkv, 16, d), dtype=kv_dt, device=self.dev)
         self.kv_scales = (torch.ones((self.num_blocks, Hkv, 2), dtype=torch.float32, device=self.dev)
                           if self.fp8 else None)
         self.index_pool = (torch.zeros((self.num_blocks, max(self.nR, 1), 16, 16), dtype=torch.float32,

@@ -92,8 +92,11 @@ typedef struct {
 } hws_config;
 
 /* Caller-owned device buffers.  Layouts (row-major):
- *   k_pool, v_pool: [num_blocks][Hkv][16][128] bf16, or e4m3 bytes for FP8;
- *                   K rows are stored after RoPE (when rope_theta > 0).
+ *   k_pool:         [num_blocks][Hkv][4][16][32] bf16 (or e4m3 bytes for FP8):
+ *                   each 16-token page is stored in four 32-dim blocks, i.e.
+ *                   element (slot r, dim d) of a page is at ((d/32)*16 + r)*32
+ *                   + d%32; K is stored after RoPE (when rope_theta > 0).
+ *   v_pool:         [num_blocks][Hkv][16][128] bf16 or e4m3 bytes, row-major.
  *   kv_scales:      [num_blocks][Hkv][2] fp32 (K scale, V scale); FP8 only.
  *   index_pool:     [num_blocks][n_retrieval][16][16] fp32, the projected
  *                   pre-RoPE keys of retrieval heads in KV-head order; may be
@@ -194,6 +197,7 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
  * lowest position).  Local head: S = {0..n_sink-1} U {N-window..N-1}.  Then
  * out_g = sum_{i in S} softmax_S(attn_scale q_g.k_i) v_i. */
 hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
+/* (FULL scoring requires a bf16 cache: HWS_ERR_UNSUPPORTED otherwise.) */
 
 /* Optional per-stage timing with HIP events on the decode stream.
  * hws_profile_enable(ctx, 1) starts recording one event pair per stage per

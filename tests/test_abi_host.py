@@ -170,6 +170,15 @@ def test_decode_validation_without_gpu():
         assert hws.lib().hws_last_error(c.handle)
 
 
+def test_full_scores_need_bf16_cache():
+    c = _ctx(kv=1)
+    c.set_head_kinds([1, 0])
+    c.bind(4096, 4096, 4096, 4096, 4096)
+    with pytest.raises(hws.HwsError) as e:
+        _decode(c, score_mode=1)
+    assert e.value.status == hws.HWS_ERR_UNSUPPORTED
+
+
 def test_workspace_size_rules():
     c = _ctx()
     c.set_head_kinds([1, 0])
