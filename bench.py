@@ -42,6 +42,9 @@ def parse_args(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cold-iters", type=int, default=20,
                     help="extra steps each preceded by a 1 GiB cache flush (0 = skip)")
+    ap.add_argument("--launch", choices=["auto", "multi", "cooperative"], default="auto",
+                    help="auto: one launch after scoring (grid sized to the device); cooperative: the "
+                         "same as a cooperative launch; multi: a kernel per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -155,6 +158,7 @@ def main(argv=None) -> int:
 
     import numpy as np
     import torch
+    from head_wise_sparse_02_amd import hws
     from head_wise_sparse_02_amd import workloads as W
     from head_wise_sparse_02_amd.runner import DecodeSetup
 
@@ -163,6 +167,8 @@ def main(argv=None) -> int:
     print(f"[bench] building workload {args.config}: {W.CONFIG_NAMES[args.config]}",
           file=sys.stderr, flush=True)
     setup = DecodeSetup(wl, keep_host=want_cpu)
+    setup.ctx.set_launch_mode({"auto": hws.HWS_LAUNCH_AUTO, "multi": hws.HWS_LAUNCH_MULTI,
+                               "cooperative": hws.HWS_LAUNCH_COOPERATIVE}[args.launch])
     print("[bench] cache filled; warming up", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         setup.decode()
@@ -199,7 +205,7 @@ def main(argv=None) -> int:
     for name, (ms, calls) in prof.items():
         if calls:
             us = 1000.0 * ms / calls
-            b = by.get(name, 0)
+            b = by["attend"] + by["io"] if name == "tail" else by.get(name, 0)
             stages[name] = {"us": round(us, 2), "bytes": b,
                             "GBps": round(b / (us * 1e3), 1) if b else None}
     dom = max(("score", "attend"), key=lambda s: by[s])
@@ -241,7 +247,7 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "description": W.CONFIG_NAMES[wl.cfg], "batch": wl.B,
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
                    "context": int(max(wl.seq_lens)), "score_mode": wl.score_mode,
-                   "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype},
+                   "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype, "launch": args.launch},
         "step_bytes": by["total"], "step_GBps": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_GBS, 4),
         "selected_per_head_mean": round(float(sel_counts[:, [h for h in wl.retrieval_heads]].mean()), 1)

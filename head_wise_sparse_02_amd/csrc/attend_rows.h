@@ -1,0 +1,201 @@
+// Gathered decode attention of one 16-lane row processor, shared by the
+// per-stage attention kernel and the single-launch tail.
+//
+// [ICS] "Inference-time context sparsity: illusion or opportunity?", §3c:
+// sparse decode reads only the rows of the selected tokens.  A processor
+// walks its rows RB at a time; lane `sub` holds dims 8*sub..8*sub+7.  All
+// loads of a batch are issued before any is used: rows past the end (or on
+// an out-of-range page) load row 0 of page 0 and are masked afterwards, so
+// no load sits behind a per-lane branch (which would make the compiler wait
+// for each one in turn).  The softmax runs online in log2 units.
+#pragma once
+
+#include "hws_device.h"
+
+namespace hws {
+
+// Rows per processor per batch: all loads of a batch are in flight at once.
+template <int G, int MODE>
+struct AttRB {
+  // MODE 1 reads V rows and stored scores; the others also read K rows.
+  static constexpr int value = MODE == 1 ? 8 : (G <= 2 ? 8 : (G == 4 ? 4 : 2));
+};
+
+// Row r of the list: retrieval rows are offsets (from lo) in `rows`, whose
+// page is pages[offset / 16]; local rows are tokens ltok[r] on page lpg[r].
+// MODE 0: logits q.k from K rows; MODE 1: retrieval heads only, logits from
+// the stored full-dim scores; MODE 2: both (scores for retrieval heads).
+template <int G, bool FP8, int MODE>
+__device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, int h, int hr, int lo, int nrows,
+                                                int r_begin, int r_step, int sub, const unsigned short* rows,
+                                                const int* pages, const int* ltok, const int* lpg, float (&m)[G],
+                                                float (&l)[G], float (&o)[G][8]) {
+  constexpr bool NEED_K = MODE != 1;
+  constexpr int RB = AttRB<G, MODE>::value;
+  const bool is_ret = hr >= 0;
+  const bool use_scores = MODE != 0 && is_ret;
+
+  // queries of the group, pre-scaled to log2 units: dims 8*sub..8*sub+7
+  float qf[NEED_K ? G : 1][8];
+  if (NEED_K && !use_scores) {
+#pragma unroll
+    for (int g = 0; g < (NEED_K ? G : 1); ++g) {
+      const size_t qo = ((size_t)b * p.Hq + h * G + g) * D + 8 * sub;
+      if (p.qrot != nullptr) {
+        const float4 a = *reinterpret_cast<const float4*>(p.qrot + qo);
+        const float4 c = *reinterpret_cast<const float4*>(p.qrot + qo + 4);
+        qf[g][0] = a.x; qf[g][1] = a.y; qf[g][2] = a.z; qf[g][3] = a.w;
+        qf[g][4] = c.x; qf[g][5] = c.y; qf[g][6] = c.z; qf[g][7] = c.w;
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(p.q + qo);
+        qf[g][0] = bf16_lo(u.x); qf[g][1] = bf16_hi(u.x); qf[g][2] = bf16_lo(u.y); qf[g][3] = bf16_hi(u.y);
+        qf[g][4] = bf16_lo(u.z); qf[g][5] = bf16_hi(u.z); qf[g][6] = bf16_lo(u.w); qf[g][7] = bf16_hi(u.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[g][j] *= p.c2_attn;
+    }
+  }
+  const float* sc = use_scores ? p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G : nullptr;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = NEG_INF;
+    l[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+  }
+
+  for (int r0 = r_begin; r0 < nrows; r0 += r_step) {
+    int ii[RB], pg[RB];
+    bool ok[RB];
+    if (is_ret) {
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int off = rows[min(r0 + u, nrows - 1)];
+        ii[u] = lo + off;
+        pg[u] = pages[off >> 4];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int rc = min(r0 + u, nrows - 1);
+        ii[u] = ltok[rc];
+        pg[u] = lpg[rc];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      ok[u] = r0 + u < nrows && (unsigned)pg[u] < (unsigned)p.num_blocks;
+      if (!ok[u]) { pg[u] = 0; ii[u] = 0; }
+    }
+
+    // every load of the batch
+    float vv[RB][8];
+    float z[RB][G];
+    float kx[NEED_K ? RB : 1][8];
+    float ks[RB], vs[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      load_row8<FP8>(p.v_pool, ((size_t)pg[u] * p.Hkv + h) * BS + (ii[u] & 15), sub, vv[u]);
+    if (FP8) {
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const float2 s2 = *reinterpret_cast<const float2*>(p.kv_scales + ((size_t)pg[u] * p.Hkv + h) * 2);
+        ks[u] = s2.x;
+        vs[u] = s2.y;
+      }
+    }
+    if (use_scores) {
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        if (G >= 4) {
+#pragma unroll
+          for (int q4 = 0; q4 < G / 4; ++q4) {
+            const float4 v = *reinterpret_cast<const float4*>(sc + (size_t)ii[u] * G + 4 * q4);
+            z[u][4 * q4 + 0] = v.x; z[u][4 * q4 + 1] = v.y; z[u][4 * q4 + 2] = v.z; z[u][4 * q4 + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) z[u][g] = sc[(size_t)ii[u] * G + g];
+        }
+      }
+    } else if (NEED_K) {
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+        load_krow8<FP8>(p.k_pool, (size_t)pg[u] * p.Hkv + h, ii[u] & 15, sub, kx[NEED_K ? u : 0]);
+    }
+
+    // logits (log2 units), masked rows at -inf
+    if (use_scores) {
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) z[u][g] = ok[u] ? z[u][g] * p.c2_score : NEG_INF;
+    } else if (NEED_K) {
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float a = qf[NEED_K ? g : 0][0] * kx[NEED_K ? u : 0][0];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) a = fmaf(qf[NEED_K ? g : 0][j], kx[NEED_K ? u : 0][j], a);
+          a += __shfl_xor(a, 1);
+          a += __shfl_xor(a, 2);
+          a += __shfl_xor(a, 4);
+          a += __shfl_xor(a, 8);
+          z[u][g] = ok[u] ? (FP8 ? a * ks[u] : a) : NEG_INF;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vv[u][j] = ok[u] ? (FP8 ? vv[u][j] * vs[u] : vv[u][j]) : 0.f;
+    }
+
+    // one rescale per batch
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mn = m[g];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) mn = fmaxf(mn, z[u][g]);
+      if (mn == NEG_INF) continue;                   // uniform over the processor
+      const float cf = fast_exp2(m[g] - mn);
+      l[g] *= cf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[g][j] *= cf;
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const float pz = fast_exp2(z[u][g] - mn);
+        l[g] += pz;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pz, vv[u][j], o[g][j]);
+      }
+      m[g] = mn;
+    }
+  }
+}
+
+// Combine the 4 processors of a wave (lanes sub, sub+16, sub+32, sub+48).
+template <int G>
+__device__ __forceinline__ void combine_wave_procs(float (&m)[G], float (&l)[G], float (&o)[G][8]) {
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m2 = __shfl_xor(m[g], off);
+      const float l2 = __shfl_xor(l[g], off);
+      const float mn = fmaxf(m[g], m2);
+      const float c1 = (mn == NEG_INF) ? 0.f : fast_exp2(m[g] - mn);
+      const float c2 = (mn == NEG_INF) ? 0.f : fast_exp2(m2 - mn);
+      l[g] = l[g] * c1 + l2 * c2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float o2 = __shfl_xor(o[g][j], off);
+        o[g][j] = o[g][j] * c1 + o2 * c2;
+      }
+      m[g] = mn;
+    }
+  }
+}
+
+}  // namespace hws

@@ -20,8 +20,8 @@ using namespace hws;
 
 namespace {
 
-constexpr int NUM_STAGES = 4;
-const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge"};
+constexpr int NUM_STAGES = 5;
+const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge", "tail"};
 
 struct EvPair {
   hipEvent_t a, b;
@@ -32,9 +32,10 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace regions of one decode call.
 struct Layout {
-  size_t scores, agg, spart, sel, apart_ml, apart_o, qrot, total;
+  size_t scores, agg, spart, sel, apart_ml, apart_o, qrot, tail_sync, tail_ties, total;
   int Nagg;
   int score_chunk, n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
+  int tail_tph, tail_ntiles;
 };
 
 }  // namespace
@@ -50,6 +51,7 @@ struct hws_ctx {
   bool appended = false, bound = false;
   hws_buffers buf{};
   std::string err;
+  int launch_mode = HWS_LAUNCH_AUTO;
   bool prof = false;
   std::vector<EvPair> recorded;
   std::vector<hipEvent_t> pool;
@@ -114,6 +116,11 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode)
   L.apart_ml = off; off = align_up(off + nsp * sizeof(float2));
   L.apart_o = off;  off = align_up(off + nsp * D * sizeof(float));
   L.qrot = off;     off = align_up(off + (rope ? (size_t)B * c->cfg.num_q_heads * D * sizeof(float) : 0));
+  // single-launch tail: tiles of TAIL_TILE positions per retrieval head
+  L.tail_tph = cdiv(Nmax, TAIL_TILE);
+  L.tail_ntiles = (int)(nRb * L.tail_tph);
+  L.tail_sync = off; off = align_up(off + (1 + (size_t)B * c->cfg.num_kv_heads) * sizeof(unsigned int));
+  L.tail_ties = off; off = align_up(off + (size_t)L.tail_ntiles * sizeof(unsigned int));
   L.total = off;
   return L;
 }
@@ -392,6 +399,10 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.ncL = L.ncL;
   p.att_chunk_R = L.att_chunk_R;
   p.max_splits = L.max_splits;
+  p.tail_tph = L.tail_tph;
+  p.tail_ntiles = L.tail_ntiles;
+  p.tail_sync = reinterpret_cast<unsigned int*>(ws + L.tail_sync);
+  p.tail_ties = reinterpret_cast<unsigned int*>(ws + L.tail_ties);
   std::memcpy(p.ret_slot, ctx->ret_slot, sizeof(p.ret_slot));
   std::memcpy(p.ret_head, ctx->ret_head, sizeof(p.ret_head));
   std::memcpy(p.loc_head, ctx->loc_head, sizeof(p.loc_head));
@@ -399,6 +410,21 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (rope && (e = launch_prep_q(p, s)) != hipSuccess) return hip_fail(ctx, e, "prep_q launch");
+  // Selection + attention + merge in one cooperative launch when every tile
+  // fits the co-resident grid; otherwise one kernel per stage.
+  const int nwg = (ctx->nR > 0 && ctx->launch_mode != HWS_LAUNCH_MULTI) ? tail_grid(p, ctx->launch_mode == HWS_LAUNCH_COOPERATIVE) : 0;
+  const bool tail = nwg > 0 && (long long)L.tail_ntiles <= (long long)TAIL_MAXT * nwg;
+  if (tail) {
+    const StageEv es = stage_events(ctx, 0);
+    if ((e = launch_score(p, s, es.start, es.stop)) != hipSuccess) return hip_fail(ctx, e, "score launch");
+    const StageEv et = stage_events(ctx, 4);
+    if (et.start != nullptr && (e = hipEventRecord(et.start, s)) != hipSuccess) return hip_fail(ctx, e, "event record");
+    if ((e = launch_tail(p, nwg, ctx->launch_mode == HWS_LAUNCH_COOPERATIVE, s)) != hipSuccess)
+      return hip_fail(ctx, e, "tail launch");
+    if (et.stop != nullptr && (e = hipEventRecord(et.stop, s)) != hipSuccess) return hip_fail(ctx, e, "event record");
+    if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
+    return HWS_OK;
+  }
   if (ctx->nR > 0) {
     const StageEv es = stage_events(ctx, 0);
     if ((e = launch_score(p, s, es.start, es.stop)) != hipSuccess) return hip_fail(ctx, e, "score launch");
@@ -414,6 +440,14 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   if ((e = launch_merge(p, s, em.start, em.stop)) != hipSuccess) return hip_fail(ctx, e, "merge launch");
   if (ctx->nR > 0 && a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess)
     return hip_fail(ctx, e, "emit launch");
+  return HWS_OK;
+}
+
+hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (mode != HWS_LAUNCH_AUTO && mode != HWS_LAUNCH_MULTI && mode != HWS_LAUNCH_COOPERATIVE)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "launch mode = %d", mode);
+  ctx->launch_mode = mode;
   return HWS_OK;
 }
 

@@ -101,4 +101,41 @@ __device__ __forceinline__ void wait_memory_ops() { __builtin_amdgcn_s_waitcnt(0
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Load 8 consecutive elements of a V row as fp32 (bf16 or e4m3 codes).
+template <bool FP8>
+__device__ __forceinline__ void load_row8(const void* pool, size_t row_off, int sub, float* x) {
+  if (!FP8) {
+    const uint4 w = *reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(pool) + row_off * D + 8 * sub);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(
+        reinterpret_cast<const uint8_t*>(pool) + row_off * D + 8 * sub);
+    f32x2 t;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false); x[0] = t.x; x[1] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);  x[2] = t.x; x[3] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false); x[4] = t.x; x[5] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);  x[6] = t.x; x[7] = t.y;
+  }
+}
+
+// 8 consecutive dims 8*sub..8*sub+7 of row r of a K page (blocked layout).
+template <bool FP8>
+__device__ __forceinline__ void load_krow8(const void* pool, size_t page, int r, int sub, float* x) {
+  const size_t off = page * (BS * D) + (size_t)(((sub >> 2) << 4) + r) * 32 + 8 * (sub & 3);
+  if (!FP8) {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(pool) + off);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(pool) + off);
+    f32x2 t;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false); x[0] = t.x; x[1] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);  x[2] = t.x; x[3] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false); x[4] = t.x; x[5] = t.y;
+    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);  x[6] = t.x; x[7] = t.y;
+  }
+}
+
 }  // namespace hws

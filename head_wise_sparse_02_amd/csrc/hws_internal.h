@@ -22,6 +22,12 @@ constexpr int SEL_CHUNK = SEL_THREADS * SEL_PER_THREAD;   // 16384 tokens
 constexpr int HIST_BINS = 4096;   // pass 1 bins: bits 30..19 of the fp32 pattern
 constexpr int LOCAL_CHUNK = 256;  // rows per local-head attention workgroup
 
+// Single-launch tail (selection + attention + merge in one cooperative launch)
+constexpr int TAIL_THREADS = 512;
+constexpr int TAIL_TPT = 32;                             // tokens per thread per tile
+constexpr int TAIL_TILE = TAIL_THREADS * TAIL_TPT;       // 16384 tokens
+constexpr int TAIL_MAXT = 2;                             // tiles a workgroup keeps in registers
+
 // Bit split of the non-negative fp32 aggregate a_i (bit 31 is always 0):
 // pass 1 bins bits 30..19 (12 bits), pass 2 bits 18..9 (10), pass 3 bits 8..0 (9).
 constexpr int P1_SHIFT = 19, P2_SHIFT = 9;
@@ -49,6 +55,13 @@ struct alignas(256) SelState {
   unsigned int nsel;        // |S| (top-p: summed by the attention kernel)
   unsigned int quota;       // top-k with SEL_TIE: ties at tstar to keep
   float lse2[MAX_G];        // per query head log2-sum-exp2 of the logits
+  // Single-launch tail: every radix pass has its own bins (top-p: fixed-point
+  // mass, top-k: counts; pass 1 uses `mass` above), and the tiles of the
+  // head count their arrivals here.
+  unsigned int arrive;      // tiles done with a radix pass (monotonic over passes)
+  unsigned int tie_arrive;  // tiles that published their tie count
+  unsigned long long mass2[P2_BINS];
+  unsigned long long mass3[P3_BINS];
 };
 constexpr int SELSTATE_WORDS = (int)(sizeof(SelState) / 4);
 
@@ -84,6 +97,9 @@ struct DecodeParams {
   int* sel_idx;
   int sel_cap;
   int score_chunk;              // tokens per scoring workgroup
+  int tail_tph, tail_ntiles;    // tail: tiles per retrieval head, total tiles
+  unsigned int* tail_sync;      // [0] error word, [1 + b*Hkv + h] split arrivals (zeroed by the scan)
+  unsigned int* tail_ties;      // [tail_ntiles] ties at t* per tile
   int n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
   signed char ret_slot[MAX_KV];
   signed char ret_head[MAX_KV];
@@ -126,6 +142,12 @@ hipError_t launch_select(const DecodeParams& p, hipStream_t s, int pass, hipEven
 hipError_t launch_attend(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_emit(const DecodeParams& p, hipStream_t s);
+// Single launch for select + attend + merge.  tail_grid() is the number of
+// workgroups of the instantiation `p` needs that the device holds at once (0
+// if there is no such instantiation, or `cooperative` and the device has no
+// cooperative launches).
+int tail_grid(const DecodeParams& p, bool cooperative);
+hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, int kv_fp8, hipStream_t s);
 
 }  // namespace hws

@@ -17,7 +17,7 @@
 //
 // Each workgroup produces (max, sum, unnormalised output) per query head in
 // log2 units; merge_kernel combines them.
-#include "hws_device.h"
+#include "attend_rows.h"
 
 namespace hws {
 
@@ -42,43 +42,6 @@ __device__ __forceinline__ unsigned int block_excl_scan256(unsigned int v, unsig
   return off + inc - v;
 }
 
-// Load 8 consecutive elements of a V row as fp32 (bf16 or e4m3 codes).
-template <bool FP8>
-__device__ __forceinline__ void load_row8(const void* pool, size_t row_off, int sub, float* x) {
-  if (!FP8) {
-    const uint4 w = *reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(pool) + row_off * D + 8 * sub);
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(
-        reinterpret_cast<const uint8_t*>(pool) + row_off * D + 8 * sub);
-    f32x2 t;
-    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false); x[0] = t.x; x[1] = t.y;
-    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);  x[2] = t.x; x[3] = t.y;
-    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false); x[4] = t.x; x[5] = t.y;
-    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);  x[6] = t.x; x[7] = t.y;
-  }
-}
-
-// 8 consecutive dims 8*sub..8*sub+7 of row r of a K page (blocked layout).
-template <bool FP8>
-__device__ __forceinline__ void load_krow8(const void* pool, size_t page, int r, int sub, float* x) {
-  const size_t off = page * (BS * D) + (size_t)(((sub >> 2) << 4) + r) * 32 + 8 * (sub & 3);
-  if (!FP8) {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(pool) + off);
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(pool) + off);
-    f32x2 t;
-    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false); x[0] = t.x; x[1] = t.y;
-    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);  x[2] = t.x; x[3] = t.y;
-    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false); x[4] = t.x; x[5] = t.y;
-    t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);  x[6] = t.x; x[7] = t.y;
-  }
-}
-
 // Ties at t* in positions [0, lo) of one (b, retrieval head).  Only reached
 // for top-k when the ties at the threshold exceed the budget.
 __device__ unsigned int ties_before(const float* agg, int lo, unsigned int tstar, unsigned int* tmp) {
@@ -93,10 +56,8 @@ __device__ unsigned int ties_before(const float* agg, int lo, unsigned int tstar
 // MODE 0: rows need K (index scoring or local heads); MODE 1: FULL scoring and
 // retrieval heads only (logits from the stored scores, V rows only);
 // MODE 2: FULL scoring with local heads present (both paths).
-template <int G, bool FP8, int MODE, bool ROPE>
+template <int G, bool FP8, int MODE>
 __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
-  constexpr bool NEED_K = MODE != 1;
-  constexpr int RB = (MODE == 1 || G <= 4) ? 8 : 2;   // rows per 16-lane processor per batch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int proc = tid >> 4, sub = tid & 15;     // 16 row processors of 16 lanes
   const int w = blockIdx.x;
@@ -198,151 +159,11 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     if (tid < G) ml[tid] = make_float2(NEG_INF, 0.f);
     return;
   }
-  const bool use_scores = MODE != 0 && is_ret;
-  // queries of the group, pre-scaled to log2 units: dims 8*sub..8*sub+7
-  float qf[NEED_K ? G : 1][8];
-  if (NEED_K && !use_scores) {
-#pragma unroll
-    for (int g = 0; g < (NEED_K ? G : 1); ++g) {
-      const size_t qo = ((size_t)b * p.Hq + h * G + g) * D + 8 * sub;
-      if (ROPE) {
-        const float4 a = *reinterpret_cast<const float4*>(p.qrot + qo);
-        const float4 c = *reinterpret_cast<const float4*>(p.qrot + qo + 4);
-        qf[g][0] = a.x; qf[g][1] = a.y; qf[g][2] = a.z; qf[g][3] = a.w;
-        qf[g][4] = c.x; qf[g][5] = c.y; qf[g][6] = c.z; qf[g][7] = c.w;
-      } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(p.q + qo);
-        qf[g][0] = bf16_lo(u.x); qf[g][1] = bf16_hi(u.x); qf[g][2] = bf16_lo(u.y); qf[g][3] = bf16_hi(u.y);
-        qf[g][4] = bf16_lo(u.z); qf[g][5] = bf16_hi(u.z); qf[g][6] = bf16_lo(u.w); qf[g][7] = bf16_hi(u.w);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qf[g][j] *= p.c2_attn;
-    }
-  }
-
-  const float* sc = use_scores ? p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G : nullptr;
   float m[G], l[G], o[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = NEG_INF;
-    l[g] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
-  }
-
-  for (int r0 = proc * RB; r0 < nrows; r0 += 16 * RB) {
-    float z[RB][G];
-    float vv[RB][8];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int r = r0 + u;
-      const bool valid = r < nrows;
-      int i = 0, pg = 0;
-      if (valid) {
-        if (is_ret) {
-          const int off = rows_s[r];
-          i = lo + off;
-          pg = pages_s[off >> 4];
-        } else {
-          i = ltok_s[r];
-          pg = pages_s[r];
-        }
-      }
-      const bool ok = valid && (unsigned)pg < (unsigned)p.num_blocks;
-      const size_t row_off = ((size_t)(ok ? pg : 0) * p.Hkv + h) * BS + (i & 15);
-      float ks = 1.f, vs = 1.f;
-      if (FP8 && ok) {
-        const float2 s2 = *reinterpret_cast<const float2*>(p.kv_scales + ((size_t)pg * p.Hkv + h) * 2);
-        ks = s2.x;
-        vs = s2.y;
-      }
-      if (ok) {
-        load_row8<FP8>(p.v_pool, row_off, sub, vv[u]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vv[u][j] = 0.f;
-      }
-      if (FP8) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vv[u][j] *= vs;
-      }
-      if (use_scores) {
-        if (G >= 4) {
-#pragma unroll
-          for (int q4 = 0; q4 < G / 4; ++q4) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (ok) v = *reinterpret_cast<const float4*>(sc + (size_t)i * G + 4 * q4);
-            z[u][4 * q4 + 0] = ok ? v.x * p.c2_score : NEG_INF;
-            z[u][4 * q4 + 1] = ok ? v.y * p.c2_score : NEG_INF;
-            z[u][4 * q4 + 2] = ok ? v.z * p.c2_score : NEG_INF;
-            z[u][4 * q4 + 3] = ok ? v.w * p.c2_score : NEG_INF;
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < G; ++g) z[u][g] = ok ? sc[(size_t)i * G + g] * p.c2_score : NEG_INF;
-        }
-      } else if (NEED_K) {
-        float kx[8];
-        if (ok) {
-          load_krow8<FP8>(p.k_pool, (size_t)pg * p.Hkv + h, i & 15, sub, kx);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) kx[j] = 0.f;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float a = qf[NEED_K ? g : 0][0] * kx[0];
-#pragma unroll
-          for (int j = 1; j < 8; ++j) a = fmaf(qf[NEED_K ? g : 0][j], kx[j], a);
-          a += __shfl_xor(a, 1);
-          a += __shfl_xor(a, 2);
-          a += __shfl_xor(a, 4);
-          a += __shfl_xor(a, 8);
-          z[u][g] = ok ? a * ks : NEG_INF;
-        }
-      }
-    }
-    // one rescale per batch of RB rows
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mn = m[g];
-#pragma unroll
-      for (int u = 0; u < RB; ++u) mn = fmaxf(mn, z[u][g]);
-      if (mn == NEG_INF) continue;                   // uniform over the processor
-      const float cf = fast_exp2(m[g] - mn);
-      l[g] *= cf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[g][j] *= cf;
-#pragma unroll
-      for (int u = 0; u < RB; ++u) {
-        const float pz = fast_exp2(z[u][g] - mn);
-        l[g] += pz;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pz, vv[u][j], o[g][j]);
-      }
-      m[g] = mn;
-    }
-  }
-
-  // combine the 4 processors of each wave (lanes sub, sub+16, sub+32, sub+48)
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m2 = __shfl_xor(m[g], off);
-      const float l2 = __shfl_xor(l[g], off);
-      const float mn = fmaxf(m[g], m2);
-      const float c1 = (mn == NEG_INF) ? 0.f : fast_exp2(m[g] - mn);
-      const float c2 = (mn == NEG_INF) ? 0.f : fast_exp2(m2 - mn);
-      l[g] = l[g] * c1 + l2 * c2;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float o2 = __shfl_xor(o[g][j], off);
-        o[g][j] = o[g][j] * c1 + o2 * c2;
-      }
-      m[g] = mn;
-    }
-  }
+  constexpr int RB = AttRB<G, MODE>::value;
+  accumulate_rows<G, FP8, MODE>(p, b, h, hr, lo, nrows, proc * RB, 16 * RB, sub, rows_s, pages_s, ltok_s,
+                                pages_s, m, l, o);
+  combine_wave_procs<G>(m, l, o);
   if (lane < 16) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -442,15 +263,10 @@ __global__ __launch_bounds__(64) void prep_q_kernel(DecodeParams p) {
 template <int G, bool FP8>
 static hipError_t launch_attend_g(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int nwg = p.B * (p.nR * p.ncR + p.nL * p.ncL);
-  const bool full = p.score_mode == 1, rope = p.qrot != nullptr;
   const dim3 grid(nwg), blk(256);
-  if (!full) {
-    if (rope) return launch_kernel(attend_kernel<G, FP8, 0, true>, grid, blk, s, e0, e1, p);
-    return launch_kernel(attend_kernel<G, FP8, 0, false>, grid, blk, s, e0, e1, p);
-  }
-  if (p.nL == 0) return launch_kernel(attend_kernel<G, FP8, 1, false>, grid, blk, s, e0, e1, p);
-  if (rope) return launch_kernel(attend_kernel<G, FP8, 2, true>, grid, blk, s, e0, e1, p);
-  return launch_kernel(attend_kernel<G, FP8, 2, false>, grid, blk, s, e0, e1, p);
+  if (p.score_mode != 1) return launch_kernel(attend_kernel<G, FP8, 0>, grid, blk, s, e0, e1, p);
+  if (p.nL == 0) return launch_kernel(attend_kernel<G, FP8, 1>, grid, blk, s, e0, e1, p);
+  return launch_kernel(attend_kernel<G, FP8, 2>, grid, blk, s, e0, e1, p);
 }
 
 template <int G>

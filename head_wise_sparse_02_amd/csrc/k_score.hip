@@ -18,9 +18,18 @@
 namespace hws {
 
 // Zero this chunk's share of the (b, hr) selection state.
-__device__ __forceinline__ void zero_state_share(SelState* st, int c, int nchunks) {
+__device__ __forceinline__ void zero_state_share(const DecodeParams& p, SelState* st, int b, int hr, int c,
+                                                 int nchunks) {
+  // the chunks that exist share the work; chunk 0 also runs for an empty sequence
+  const int nz = nchunks > 0 ? nchunks : 1;
+  if (c >= nz) return;
   unsigned int* w = reinterpret_cast<unsigned int*>(st);
-  for (int i = c * 256 + (int)threadIdx.x; i < SELSTATE_WORDS; i += nchunks * 256) w[i] = 0u;
+  for (int i = c * 256 + (int)threadIdx.x; i < SELSTATE_WORDS; i += nz * 256) w[i] = 0u;
+  // split arrival counters of the single-launch tail (and its error word)
+  if (p.tail_sync != nullptr && c == 0 && hr == 0) {
+    for (int h = threadIdx.x; h < p.Hkv; h += 256) p.tail_sync[1 + b * p.Hkv + h] = 0u;
+    if (b == 0 && threadIdx.x == 0) p.tail_sync[0] = 0u;
+  }
 }
 
 // Reduce (max, sum) over lanes sharing the same (lane & (span-1)) pattern.
@@ -46,8 +55,8 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
   const int N = min(p.seq_lens[b], p.Nmax);
   const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;  // == p.score_chunk here
   SelState* st = p.sel + (size_t)b * p.nR + hr;
+  zero_state_share(p, st, b, hr, c, nchunks);
   if (c >= nchunks) return;
-  zero_state_share(st, c, nchunks);
 
   const int h = p.ret_head[hr];
   __shared__ float qt_s[G][R];
@@ -158,8 +167,8 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   const int N = min(p.seq_lens[b], p.Nmax);
   const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;  // == p.score_chunk here
   SelState* st = p.sel + (size_t)b * p.nR + hr;
+  zero_state_share(p, st, b, hr, c, nchunks);
   if (c >= nchunks) return;
-  zero_state_share(st, c, nchunks);
 
   const int h = p.ret_head[hr];
   const int row = lane & 15, quad = lane >> 4;
@@ -292,8 +301,8 @@ __global__ __launch_bounds__(256) void score_full_g4_kernel(DecodeParams p) {
   const int N = min(p.seq_lens[b], p.Nmax);
   const int nchunks = (N + CH - 1) / CH;
   SelState* st = p.sel + (size_t)b * p.nR + hr;
+  zero_state_share(p, st, b, hr, c, nchunks);
   if (c >= nchunks) return;
-  zero_state_share(st, c, nchunks);
 
   const int h = p.ret_head[hr];
   const int row = lane & 15, quad = lane >> 4;

@@ -1,0 +1,740 @@
+// Selection, gathered attention and merge of one decode step in a single
+// launch of co-resident workgroups.
+//
+// The steps are those of the multi-kernel path (k_select.hip, k_attend.hip):
+// [RTPurbo] "Full attention returns in force ...", Methodology §3 (top-p mass
+// / top-k budget over the GQA-aggregated softmax) and §5 (histogram
+// threshold instead of a sort); [ICS] "Inference-time context sparsity:
+// illusion or opportunity?", §3c (attention reads only the selected rows);
+// [RTPurbo] Methodology §1 and [AoH] "Autonomy-of-Heads ...", Methodology §4
+// (local heads: sinks + window).  What changes is how the work is laid out:
+//
+// * A retrieval head's positions are cut into tiles of TAIL_TILE tokens; a
+//   workgroup owns up to TAIL_MAXT tiles and keeps their aggregates a_i in
+//   registers through all three radix passes, so the raw scores are read
+//   once and a_i is never written out (except for the optional index list).
+// * Between passes only the tiles of the same head wait for each other: each
+//   tile flushes its LDS histogram into the head's global bins, bumps the
+//   head's arrival counter, then spins until all tiles of the head arrived
+//   and scans the merged bins itself.  Nothing waits on another head.  The
+//   grid is sized to what the device holds at once (compute units times
+//   occupancy), so every workgroup that is waited for is resident; the
+//   cooperative form of the launch has the runtime guarantee it.
+// * A tile then compacts its kept positions in position order and attends
+//   over them; local-head chunks go to the workgroups without tiles first.
+// * The last split of a (sequence, KV head) to finish merges all its splits.
+//
+// Hand-offs use only device-coherent accesses (atomics, agent-scope atomic
+// loads/stores) after waiting for the writer's memory operations to be
+// acknowledged; no device-wide fence is issued.  Every wait is bounded: on a
+// timeout the error word is set, the kernel runs to its end and the outputs
+// of the step are NaN.
+#include <mutex>
+#include <vector>
+
+#include "attend_rows.h"
+
+namespace hws {
+
+namespace {
+
+constexpr int TT = TAIL_THREADS;              // 512 threads
+constexpr int TW = TT / 64;                   // 8 waves
+constexpr int TPT = TAIL_TPT;                 // tokens per thread per tile
+constexpr int MAXT = TAIL_MAXT;
+constexpr int NPROC = TT / 16;                // 16-lane row processors
+constexpr unsigned int SPIN_LIMIT = 1u << 20; // polls (~1 us each): a wait gives up after ~1 s
+
+struct TailLds {
+  union {
+    unsigned long long hist[HIST_BINS];       // radix bins (pass 1 is the largest)
+    unsigned short rows[TAIL_TILE];           // kept offsets of the tile, position order
+    float wo[TW][MAX_G][D];                   // per-wave partial outputs
+  } u;
+  int pages[MAXT][TAIL_TILE / BS];            // block-table entries of the tiles
+  int ltok[LOCAL_CHUNK], lpg[LOCAL_CHUNK];    // local chunk: tokens and pages
+  unsigned int cnt[TPT * TW];                 // per (u, wave) counts for ordered compaction
+  float lse[MAXT][MAX_G];
+  float wm[TW][MAX_G], wl[TW][MAX_G];
+  unsigned long long wsum[TW];
+  unsigned long long above;
+  unsigned int tmp[TW + 1];
+  int bin;
+  int flag;
+};
+
+__device__ __forceinline__ unsigned long long mass_fixed(float a) {
+  return __float2ull_rn(a * MASS_SCALE);
+}
+
+__device__ __forceinline__ unsigned int lane_rank(unsigned long long bal) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned int)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned int)bal, 0u));
+}
+
+// Thread 0 polls `ctr` until it reaches `target`.  Returns false (and sets
+// the error word) if the limit passes or another workgroup already failed.
+__device__ __forceinline__ bool spin_until(const unsigned int* ctr, unsigned int target, unsigned int* err) {
+  unsigned int it = 0;
+  while (load_u32_coherent(ctr) < target) {
+    ++it;
+    if ((it & 255u) == 0u && (it >= SPIN_LIMIT || load_u32_coherent(err) != 0u)) {
+      atomicOr(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// Everyone waits for thread 0's spin.
+__device__ __forceinline__ void block_wait(TailLds& S, const unsigned int* ctr, unsigned int target, unsigned int* err) {
+  __syncthreads();
+  if (threadIdx.x == 0) spin_until(ctr, target, err);
+  __syncthreads();
+}
+
+// In-place exclusive scan of S.cnt (TPT * TW entries, (u, wave) order);
+// returns the total.  Entry order is position order inside the tile.
+__device__ __forceinline__ unsigned int scan_cnt(TailLds& S) {
+  constexpr int NE = TPT * TW;                // 256
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned int v = 0, inc = 0;
+  if (tid < NE) {
+    v = S.cnt[tid];
+    inc = v;
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned int t = __shfl_up(inc, off);
+      if (lane >= off) inc += t;
+    }
+    if (lane == 63) S.tmp[wave] = inc;
+  }
+  __syncthreads();
+  if (tid < NE) {
+    unsigned int off = 0;
+    for (int w2 = 0; w2 < wave; ++w2) off += S.tmp[w2];
+    S.cnt[tid] = off + inc - v;
+  }
+  unsigned int tot = 0;
+  for (int w2 = 0; w2 < NE / 64; ++w2) tot += S.tmp[w2];
+  __syncthreads();
+  return tot;
+}
+
+// Count the flagged tokens per (u, wave) in S.cnt (not yet scanned).
+__device__ __forceinline__ void count_flags(TailLds& S, unsigned int mask) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const unsigned long long bal = __ballot((mask >> u) & 1u);
+    if (lane == 0) S.cnt[u * TW + wave] = (unsigned int)__popcll(bal);
+  }
+}
+
+// Scan `nbins` LDS bins from the top down, starting from `above`; the bin
+// where the cumulative sum first reaches `target` (-1 if it never does) and
+// the sum strictly above it.
+__device__ __forceinline__ void scan_top(TailLds& S, int nbins, unsigned long long above, unsigned long long target,
+                         int& out_bin, unsigned long long& out_above) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = nbins / TT;                 // 8, 2 or 1
+  const int top = nbins - 1 - tid * per;
+  unsigned long long m = 0ull;
+  for (int k = 0; k < per; ++k) m += S.u.hist[top - k];
+  unsigned long long inc = m;
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) S.wsum[wave] = inc;
+  if (tid == 0) S.bin = -1;
+  __syncthreads();
+  unsigned long long cm = above + inc - m;
+  for (int w2 = 0; w2 < wave; ++w2) cm += S.wsum[w2];
+  for (int k = 0; k < per; ++k) {
+    const unsigned long long nm = cm + S.u.hist[top - k];
+    if (cm < target && nm >= target) {        // one bin at most: the sum is monotone
+      S.bin = top - k;
+      S.above = cm;
+    }
+    cm = nm;
+  }
+  __syncthreads();
+  out_bin = S.bin;
+  out_above = S.above;
+  __syncthreads();
+}
+
+struct Tile {
+  int t, b, hr, j, N, lo, hi;   // t < 0: no tile in this slot
+};
+
+// Per-tile selection state (uniform over the workgroup).
+struct TileSel {
+  bool done;                    // threshold known
+  unsigned int key;             // bits of the threshold fixed so far
+  unsigned long long above;     // mass / count strictly above the candidate range
+  unsigned int tstar;
+  bool tie;                     // top-k: keep only `quota` lowest-position ties
+  unsigned int quota;
+};
+
+// One radix pass over the workgroup's tiles: LDS histogram of the candidate
+// tokens, flush into the head's bins, arrive, wait for the head, scan.
+template <int PASS>
+__device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, const Tile (&tl)[MAXT],
+                           const float (&av)[MAXT][TPT], TileSel (&ts)[MAXT], bool bymass,
+                           unsigned int* err) {
+  constexpr int NB = PASS == 1 ? HIST_BINS : (PASS == 2 ? P2_BINS : P3_BINS);
+  constexpr int SHIFT = PASS == 1 ? P1_SHIFT : (PASS == 2 ? P2_SHIFT : 0);
+  constexpr int KEY_SHIFT = PASS == 1 ? 31 : (PASS == 2 ? P1_SHIFT : P2_SHIFT);
+  const int tid = threadIdx.x;
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < MAXT; ++k) {
+    if (tl[k].t < 0 || ts[k].done) continue;                 // uniform
+    any = true;
+    SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
+    unsigned long long* gh = PASS == 1 ? st->mass : (PASS == 2 ? st->mass2 : st->mass3);
+    for (int i = tid; i < NB; i += TT) S.u.hist[i] = 0ull;
+    __syncthreads();
+    const unsigned int key = ts[k].key;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const unsigned int bits = __float_as_uint(av[k][u]);   // sign bit: no token
+      if ((bits >> KEY_SHIFT) == key) {
+        const unsigned int bin = (bits >> SHIFT) & (NB - 1);
+        atomicAdd(&S.u.hist[bin], bymass ? mass_fixed(av[k][u]) : 1ull);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < NB; i += TT) {
+      const unsigned long long v = S.u.hist[i];
+      if (v != 0ull) atomicAdd(&gh[i], v);
+    }
+    __syncthreads();
+  }
+  if (!any) return;
+  wait_memory_ops();
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k)
+      if (tl[k].t >= 0 && !ts[k].done) atomicAdd(&p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].arrive, 1u);
+  }
+#pragma unroll
+  for (int k = 0; k < MAXT; ++k) {
+    if (tl[k].t < 0 || ts[k].done) continue;
+    SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
+    const unsigned long long* gh = PASS == 1 ? st->mass : (PASS == 2 ? st->mass2 : st->mass3);
+    block_wait(S, &st->arrive, (unsigned int)(PASS * p.tail_tph), err);
+    unsigned long long v[NB / TT];
+#pragma unroll
+    for (int e = 0; e < NB / TT; ++e) v[e] = load_u64_coherent(&gh[tid + e * TT]);
+#pragma unroll
+    for (int e = 0; e < NB / TT; ++e) S.u.hist[tid + e * TT] = v[e];
+    __syncthreads();
+    unsigned long long target;
+    if (bymass) {
+      const float pp = p.top_p[tl[k].b];
+      const unsigned long long tg = pp > 0.f ? (unsigned long long)((double)pp * 1099511627776.0) : 0ull;
+      target = tg > 0ull ? tg : 1ull;          // p <= 0: the largest value alone
+    } else {
+      target = (unsigned long long)max(p.top_k[tl[k].b], 1);
+    }
+    int bin;
+    unsigned long long above;
+    scan_top(S, NB, ts[k].above, target, bin, above);
+    if (bin < 0) {                             // rounding left the total short: keep all
+      ts[k].done = true;
+      ts[k].tstar = 0u;
+    } else if (PASS < 3) {
+      ts[k].key = PASS == 1 ? (unsigned int)bin : ((ts[k].key << 10) | (unsigned int)bin);
+      ts[k].above = above;
+    } else {
+      ts[k].done = true;
+      ts[k].tstar = (ts[k].key << 9) | (unsigned int)bin;
+      if (!bymass) {
+        const unsigned long long eq = S.u.hist[bin];
+        if (above + eq > target) {
+          ts[k].tie = true;
+          ts[k].quota = (unsigned int)(target - above);
+        }
+      }
+    }
+    __syncthreads();                           // hist is reused by the next tile
+  }
+}
+
+// Attention of one workgroup over `nrows` rows of KV head h, then the split
+// partial (max, sum, unnormalised output) in log2 units, coherent stores.
+template <int G, bool FP8, int MODE>
+__device__ __forceinline__ void attend_rows(const DecodeParams& p, TailLds& S, int b, int h, int hr, int split, int lo,
+                            int nrows, const int* pages) {
+  constexpr int RB = AttRB<G, MODE>::value;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int proc = tid >> 4, sub = tid & 15;
+  const size_t pbase = (size_t)(b * p.Hkv + h) * p.max_splits + split;
+  float* ml = reinterpret_cast<float*>(p.apart_ml) + pbase * G * 2;   // (max, sum) pairs
+  float* po = p.apart_o + pbase * G * D;
+  float m[G], l[G], o[G][8];
+  accumulate_rows<G, FP8, MODE>(p, b, h, hr, lo, nrows, proc * RB, NPROC * RB, sub, S.u.rows, pages, S.ltok,
+                                S.lpg, m, l, o);
+  combine_wave_procs<G>(m, l, o);
+  __syncthreads();                               // rows / pages no longer read; wo aliases rows
+  if (lane < 16) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (lane == 0) { S.wm[wave][g] = m[g]; S.wl[wave][g] = l[g]; }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) S.u.wo[wave][g][8 * sub + j] = o[g][j];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += TT) {
+    const int g = e / D, d = e % D;
+    float mm = NEG_INF;
+    for (int k = 0; k < TW; ++k) mm = fmaxf(mm, S.wm[k][g]);
+    float ll = 0.f, oo = 0.f;
+    for (int k = 0; k < TW; ++k) {
+      if (S.wm[k][g] == NEG_INF) continue;
+      const float cf = fast_exp2(S.wm[k][g] - mm);
+      ll += S.wl[k][g] * cf;
+      oo += S.u.wo[k][g][d] * cf;
+    }
+    store_f32_coherent(po + (size_t)g * D + d, oo);
+    if (d == 0) {
+      store_f32_coherent(ml + 2 * g, mm);
+      store_f32_coherent(ml + 2 * g + 1, ll);
+    }
+  }
+}
+
+// A split with no rows.
+template <int G>
+__device__ __forceinline__ void empty_split(const DecodeParams& p, int b, int h, int split) {
+  float* ml = reinterpret_cast<float*>(p.apart_ml) + ((size_t)(b * p.Hkv + h) * p.max_splits + split) * G * 2;
+  if (threadIdx.x < G) {
+    store_f32_coherent(ml + 2 * threadIdx.x, NEG_INF);
+    store_f32_coherent(ml + 2 * threadIdx.x + 1, 0.f);
+  }
+}
+
+// Count this split as done; the last split of (b, h) merges all of them.
+//   out_g = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);  lse = (M + log2 L) ln 2.
+template <int G>
+__device__ __forceinline__ void finish_split(const DecodeParams& p, TailLds& S, int b, int h, int hr) {
+  const int tid = threadIdx.x;
+  const int nspl = hr >= 0 ? p.tail_tph : p.ncL;
+  wait_memory_ops();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned int prev = atomicAdd(&p.tail_sync[1 + b * p.Hkv + h], 1u);
+    S.flag = prev == (unsigned int)(nspl - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = S.flag != 0;
+  __syncthreads();
+  if (!last) return;
+
+  const bool bad = load_u32_coherent(&p.tail_sync[0]) != 0u;
+  const size_t base = (size_t)(b * p.Hkv + h) * p.max_splits;
+  const float* mlf = reinterpret_cast<const float*>(p.apart_ml);
+  const int N = min(p.seq_lens[b], p.Nmax);
+  for (int e = tid; e < G * D; e += TT) {
+    const int g = e / D, d = e % D;
+    float M = NEG_INF, L = 0.f, O = 0.f;
+    constexpr int SB = 8;
+    for (int s0 = 0; s0 < nspl; s0 += SB) {
+      float mv[SB], lv[SB], ov[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const bool in = s0 + u < nspl;
+        const size_t sp = base + s0 + u;
+        mv[u] = in ? load_f32_coherent(mlf + (sp * G + g) * 2) : NEG_INF;
+        lv[u] = in ? load_f32_coherent(mlf + (sp * G + g) * 2 + 1) : 0.f;
+        ov[u] = in ? load_f32_coherent(p.apart_o + (sp * G + g) * D + d) : 0.f;
+      }
+      float mt = M;
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+        if (lv[u] > 0.f) mt = fmaxf(mt, mv[u]);
+      if (mt == NEG_INF) continue;
+      const float cf = fast_exp2(M - mt);
+      L *= cf;
+      O *= cf;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        if (lv[u] > 0.f) {
+          const float wgt = fast_exp2(mv[u] - mt);
+          L = fmaf(lv[u], wgt, L);
+          O = fmaf(ov[u], wgt, O);
+        }
+      }
+      M = mt;
+    }
+    const float nan = __builtin_nanf("");
+    p.out[((size_t)b * p.Hq + h * G + g) * D + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
+    if (d == 0 && p.lse != nullptr) p.lse[(size_t)b * p.Hq + h * G + g] = bad ? nan : (M + log2f(L)) * LN2;
+  }
+  if (tid == 0 && p.sel_counts != nullptr) {
+    int cnt;
+    if (hr >= 0) {
+      cnt = (int)load_u32_coherent(&p.sel[(size_t)b * p.nR + hr].nsel);
+    } else {
+      const int L1 = min(p.n_sink, N);
+      cnt = L1 + (N - max(L1, N - p.window));
+    }
+    p.sel_counts[(size_t)b * p.Hkv + h] = cnt;
+  }
+}
+
+// Rows of one local-head chunk of LOCAL_CHUNK rows (sinks first, then the
+// window) into S.ltok / S.lpg; returns the row count.
+__device__ __forceinline__ int local_rows(const DecodeParams& p, TailLds& S, int item, int& b, int& h, int& c) {
+  c = item % p.ncL;
+  const int t = item / p.ncL;
+  b = t / p.nL;
+  h = p.loc_head[t % p.nL];
+  const int N = min(p.seq_lens[b], p.Nmax);
+  const int L1 = min(p.n_sink, N);
+  const int start2 = max(L1, N - p.window);
+  const int L = L1 + (N - start2);
+  const int llo = c * LOCAL_CHUNK;
+  const int nrows = max(0, min(L, llo + LOCAL_CHUNK) - llo);
+  const int tid = threadIdx.x;
+  if (tid < nrows) {
+    const int r = llo + tid;
+    const int tok = r < L1 ? r : start2 + (r - L1);
+    S.ltok[tid] = tok;
+    S.lpg[tid] = p.block_tables[(size_t)b * p.max_blocks + (tok >> 4)];
+  }
+  return nrows;
+}
+
+// Selection for the tiles of workgroup blockIdx.x (tile t = blockIdx.x + k *
+// gridDim.x): a_i of every token, the three radix passes, top-k ties.  Leaves
+// the tiles in tl, their kept-token masks in keepm and the block-table
+// entries in S.pages.
+template <int G>
+__device__ __forceinline__ void select_tiles(const DecodeParams& p, TailLds& S, Tile (&tl)[MAXT], unsigned int (&keepm)[MAXT],
+                             int& my_tiles, unsigned int* err) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int w = blockIdx.x, nwg = gridDim.x;
+  const bool bymass = p.select_mode == 0;
+  TileSel ts[MAXT];
+  float av[MAXT][TPT];
+#pragma unroll
+  for (int k = 0; k < MAXT; ++k) {
+    const int t = w + k * nwg;
+    ts[k] = TileSel{false, 0u, 0ull, 0u, false, 0u};
+    if (t >= p.tail_ntiles) {
+      tl[k] = Tile{-1, 0, 0, 0, 0, 0, 0};
+      continue;
+    }
+    const int head = t / p.tail_tph;
+    tl[k].t = t;
+    tl[k].j = t % p.tail_tph;
+    tl[k].b = head / p.nR;
+    tl[k].hr = head % p.nR;
+    tl[k].N = min(p.seq_lens[tl[k].b], p.Nmax);
+    tl[k].lo = tl[k].j * TAIL_TILE;
+    tl[k].hi = min(tl[k].N, tl[k].lo + TAIL_TILE);
+  }
+
+  // ---- a_i = mean_g 2^(x_gi - LSE2_g) for the tokens of each tile ----
+#pragma unroll
+  for (int k = 0; k < MAXT; ++k) {
+    if (tl[k].t < 0) {
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) av[k][u] = -1.0f;
+      continue;
+    }
+    const int b = tl[k].b, hr = tl[k].hr, N = tl[k].N, lo = tl[k].lo, hi = tl[k].hi;
+    const size_t row = (size_t)(b * p.nR + hr);
+    const int* bt = p.block_tables + (size_t)b * p.max_blocks;
+    const int npg = hi > lo ? (hi - lo + BS - 1) / BS : 0;
+    for (int e = tid; e < npg; e += TT) S.pages[k][e] = bt[(lo >> 4) + e];
+    const int nsc = (N + p.score_chunk - 1) / p.score_chunk;
+    if (wave < G) {
+      const float2* sp = p.spart + row * p.n_score_chunks * G + wave;
+      float m = NEG_INF, s = 0.f;
+      for (int j0 = lane; j0 < nsc; j0 += 256) {
+        float2 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int jj = j0 + 64 * u;
+          v[u] = jj < nsc ? sp[(size_t)jj * G] : make_float2(NEG_INF, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lse_combine(m, s, v[u].x, v[u].y);
+      }
+      for (int off = 1; off < 64; off <<= 1) {
+        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+        lse_combine(m, s, m2, s2);
+      }
+      if (lane == 0) S.lse[k][wave] = m + log2f(s);
+    }
+    __syncthreads();
+    if (tl[k].j == 0 && tid < G) p.sel[row].lse2[tid] = S.lse[k][tid];
+    float lse[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) lse[g] = S.lse[k][g];
+    const float c2 = p.c2_score;
+    const float invG = 1.0f / (float)G;
+    const float* sc = p.scores + row * p.Nmax * G;
+    float* agg = p.sel_idx != nullptr ? p.agg + row * p.Nagg : nullptr;
+    // loads of UB tokens in flight at once; positions past the end re-read
+    // the last token and are masked, so no load sits behind a per-lane branch
+    constexpr int UB = G <= 2 ? 32 : (G == 4 ? 16 : 8);
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) av[k][u] = -1.0f;
+    if (hi > lo) {
+#pragma unroll
+      for (int u0 = 0; u0 < TPT; u0 += UB) {
+        float x[UB][G];
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          const int i = min(lo + (u0 + u) * TT + tid, hi - 1);
+          if (G >= 4) {
+#pragma unroll
+            for (int q4 = 0; q4 < G / 4; ++q4) {
+              const float4 v = *reinterpret_cast<const float4*>(sc + (size_t)i * G + 4 * q4);
+              x[u][4 * q4 + 0] = v.x; x[u][4 * q4 + 1] = v.y; x[u][4 * q4 + 2] = v.z; x[u][4 * q4 + 3] = v.w;
+            }
+          } else if (G == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(sc + (size_t)i * G);
+            x[u][0] = v.x; x[u][G - 1] = v.y;
+          } else {
+            x[u][0] = sc[i];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          const int i = lo + (u0 + u) * TT + tid;
+          float a = 0.f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) a += fast_exp2(x[u][g] * c2 - lse[g]);
+          a *= invG;
+          if (i < hi) {
+            av[k][u0 + u] = a;
+            if (agg != nullptr) agg[i] = a;
+          }
+        }
+      }
+    }
+    // the whole sequence kept: no threshold to find
+    if (N == 0 || (bymass ? !(p.top_p[tl[k].b] < 1.0f) : max(p.top_k[tl[k].b], 1) >= N)) {
+      ts[k].done = true;
+      ts[k].tstar = 0u;
+    }
+  }
+
+  // ---- three radix passes; the tiles of a head wait only for each other ----
+  radix_pass<1>(p, S, tl, av, ts, bymass, err);
+  radix_pass<2>(p, S, tl, av, ts, bymass, err);
+  radix_pass<3>(p, S, tl, av, ts, bymass, err);
+
+  // ---- top-k ties at t*: every tile publishes its count, then each tile
+  // sums the counts of the earlier tiles of its head.  Publishing for all
+  // tiles before waiting keeps the hand-off free of cycles. ----
+  unsigned int before[MAXT];
+  bool any_tie = false;
+#pragma unroll
+  for (int k = 0; k < MAXT; ++k) {
+    before[k] = 0u;
+    if (tl[k].t < 0 || !ts[k].tie) continue;
+    any_tie = true;
+    unsigned int c = 0u;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) c += __float_as_uint(av[k][u]) == ts[k].tstar ? 1u : 0u;
+    for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off);
+    __syncthreads();
+    if (lane == 0) S.tmp[wave] = c;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned int tot = 0u;
+      for (int w2 = 0; w2 < TW; ++w2) tot += S.tmp[w2];
+      __hip_atomic_store(&p.tail_ties[tl[k].t], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (any_tie) {
+    wait_memory_ops();
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+      for (int k = 0; k < MAXT; ++k)
+        if (tl[k].t >= 0 && ts[k].tie) atomicAdd(&p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].tie_arrive, 1u);
+    }
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k) {
+      if (tl[k].t < 0 || !ts[k].tie) continue;
+      block_wait(S, &p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].tie_arrive, (unsigned int)p.tail_tph, err);
+      if (tid == 0) {
+        unsigned int sum = 0u;
+        const int t0 = tl[k].t - tl[k].j;
+        for (int jj = 0; jj < tl[k].j; ++jj) sum += load_u32_coherent(&p.tail_ties[t0 + jj]);
+        S.tmp[TW] = sum;
+      }
+      __syncthreads();
+      before[k] = S.tmp[TW];
+      __syncthreads();
+    }
+  }
+
+  // ---- kept tokens: a_i > t*, and for top-k the ties at t* that rank below
+  // the quota in position order ----
+#pragma unroll
+  for (int k = 0; k < MAXT; ++k) {
+    keepm[k] = 0u;
+    if (tl[k].t < 0) continue;
+    ++my_tiles;
+    SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
+    const unsigned int tstar = ts[k].tstar;
+    if (tl[k].j == 0 && tid == 0) {
+      st->tstar = tstar;
+      st->quota = ts[k].quota;
+      st->flags = SEL_FINISHED | (ts[k].tie ? SEL_TIE : 0u);
+    }
+    unsigned int gt = 0u, eq = 0u;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const unsigned int bits = __float_as_uint(av[k][u]);
+      if (!(bits >> 31)) {
+        if (bits > tstar) gt |= 1u << u;
+        else if (bits == tstar) eq |= 1u << u;
+      }
+    }
+    if (ts[k].tie) {
+      __syncthreads();
+      count_flags(S, eq);
+      __syncthreads();
+      scan_cnt(S);
+      unsigned int kept = 0u;
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const unsigned long long bal = __ballot((eq >> u) & 1u);
+        const unsigned int rank = before[k] + S.cnt[u * TW + wave] + lane_rank(bal);
+        if (((eq >> u) & 1u) && rank < ts[k].quota) kept |= 1u << u;
+      }
+      eq = kept;
+      __syncthreads();
+    }
+    keepm[k] = gt | eq;
+  }
+}
+
+template <int G, bool FP8, int MODE>
+__global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
+  static_assert(MAXT == 2, "the work loop picks tile slots 0 / 1");
+  __shared__ TailLds S;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int w = blockIdx.x, nwg = gridDim.x;
+  unsigned int* err = p.tail_sync;
+
+  // Local-head chunks: item i goes to workgroup (ntiles + i) mod nwg, so the
+  // workgroups without a tile take the first ones and start on them at once.
+  const int nitems = (MODE == 1) ? 0 : p.B * p.nL * p.ncL;
+  const int first_item = ((w - p.tail_ntiles) % nwg + nwg) % nwg;
+  const int my_items = first_item < nitems ? (nitems - first_item + nwg - 1) / nwg : 0;
+  int my_tiles = 0;
+  unsigned int keepm[MAXT];                     // kept tokens of each tile, bit u = slot u
+  Tile tl[MAXT];
+  if (w < p.tail_ntiles) select_tiles<G>(p, S, tl, keepm, my_tiles, err);
+
+  // ---- work list: this workgroup's tiles, then its local-head chunks ----
+  for (int wi = 0; wi < my_tiles + my_items; ++wi) {
+    int b, h, hr, split, lo = 0, nrows;
+    const int* pages = nullptr;
+    __syncthreads();                            // LDS of the previous item is free
+    if (wi < my_tiles) {
+      const Tile t = wi == 0 ? tl[0] : tl[MAXT - 1];
+      const unsigned int keep = wi == 0 ? keepm[0] : keepm[MAXT - 1];
+      b = t.b;
+      hr = t.hr;
+      h = p.ret_head[hr];
+      split = t.j;
+      lo = t.lo;
+      pages = S.pages[wi == 0 ? 0 : MAXT - 1];
+      count_flags(S, keep);
+      __syncthreads();
+      nrows = (int)scan_cnt(S);
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const unsigned long long bal = __ballot((keep >> u) & 1u);
+        if ((keep >> u) & 1u) S.u.rows[S.cnt[u * TW + wave] + lane_rank(bal)] = (unsigned short)(u * TT + tid);
+      }
+      if (tid == 0 && nrows > 0) atomicAdd(&p.sel[(size_t)b * p.nR + hr].nsel, (unsigned int)nrows);
+    } else {
+      hr = -1;
+      if constexpr (MODE != 1) nrows = local_rows(p, S, first_item + (wi - my_tiles) * nwg, b, h, split);
+      else { b = h = split = 0; nrows = 0; }     // no local heads in this mode
+    }
+    __syncthreads();
+    if (nrows > 0) attend_rows<G, FP8, MODE>(p, S, b, h, hr, split, lo, nrows, pages);
+    else empty_split<G>(p, b, h, split);
+    finish_split<G>(p, S, b, h, hr);
+  }
+}
+
+template <int G, bool FP8, int MODE>
+struct TailKernel {
+  static void* fn() { return reinterpret_cast<void*>(&tail_kernel<G, FP8, MODE>); }
+};
+
+template <int G>
+void* pick_mode(const DecodeParams& p) {
+  const bool fp8 = p.kv_scales != nullptr;
+  if (p.score_mode != 1) return fp8 ? TailKernel<G, true, 0>::fn() : TailKernel<G, false, 0>::fn();
+  if (fp8) return nullptr;                       // full-dim scores need a bf16 cache
+  return p.nL == 0 ? TailKernel<G, false, 1>::fn() : TailKernel<G, false, 2>::fn();
+}
+
+void* pick_kernel(const DecodeParams& p) {
+  switch (p.G) {
+    case 1: return pick_mode<1>(p);
+    case 2: return pick_mode<2>(p);
+    case 4: return pick_mode<4>(p);
+    case 8: return pick_mode<8>(p);
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+int tail_grid(const DecodeParams& p, bool cooperative) {
+  void* fn = pick_kernel(p);
+  if (fn == nullptr) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  // (kernel, device) -> workgroups resident at once, computed once
+  struct Entry { void* fn; int dev; int nwg; int coop; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const Entry* hit = nullptr;
+  for (const Entry& e : cache)
+    if (e.fn == fn && e.dev == dev) hit = &e;
+  if (hit == nullptr) {
+    int ncu = 0, occ = 0, coop = 0;
+    int nwg = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(fn), TT, 0) == hipSuccess)
+      nwg = ncu * occ;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
+    cache.push_back(Entry{fn, dev, nwg, coop});
+    hit = &cache.back();
+  }
+  return (cooperative && hit->coop == 0) ? 0 : hit->nwg;
+}
+
+hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s) {
+  void* fn = pick_kernel(p);
+  if (fn == nullptr || nwg < 1) return hipErrorInvalidValue;
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  if (cooperative)
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(TT), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(TT), args, 0, s);
+}
+
+}  // namespace hws

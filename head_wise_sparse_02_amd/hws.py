@@ -26,12 +26,13 @@ HWS_KV_BF16, HWS_KV_FP8_E4M3 = 0, 1
 HWS_HEAD_LOCAL, HWS_HEAD_RETRIEVAL = 0, 1
 HWS_SELECT_TOP_P, HWS_SELECT_TOP_K = 0, 1
 HWS_SCORE_INDEX, HWS_SCORE_FULL = 0, 1
+HWS_LAUNCH_AUTO, HWS_LAUNCH_MULTI, HWS_LAUNCH_COOPERATIVE = 0, 1, 2
 
 EXPORTED = (
     "hws_abi_version", "hws_status_string", "hws_last_error", "hws_create", "hws_destroy",
     "hws_set_head_kinds", "hws_classify_by_scores", "hws_get_head_kinds", "hws_bind",
     "hws_workspace_size", "hws_append", "hws_decode", "hws_profile_enable",
-    "hws_profile_read", "hws_profile_stage_name",
+    "hws_profile_read", "hws_profile_stage_name", "hws_set_launch_mode",
 )
 
 
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
         "hws_append": (i32, [vp, i32, i32, vp, vp, vp, vp, vp]),
         "hws_decode": (i32, [vp, P(DecodeArgs), vp]),
         "hws_profile_enable": (i32, [vp, i32]),
+        "hws_set_launch_mode": (i32, [vp, i32]),
         "hws_profile_read": (i32, [vp, P(ctypes.c_double), P(i32), i32]),
         "hws_profile_stage_name": (ctypes.c_char_p, [i32]),
     }
@@ -211,6 +213,12 @@ class Context:
         self._check(self._L.hws_decode(self.handle, ctypes.byref(a), _stream(stream)), "hws_decode")
 
     # -- timing ------------------------------------------------------------------
+    def set_launch_mode(self, mode: int):
+        """HWS_LAUNCH_AUTO (one launch after scoring, grid sized to the
+        device), HWS_LAUNCH_COOPERATIVE (the same as a cooperative launch) or
+        HWS_LAUNCH_MULTI (one kernel per stage)."""
+        self._check(self._L.hws_set_launch_mode(self.handle, int(mode)), "hws_set_launch_mode")
+
     def profile_enable(self, enable: bool = True):
         self._check(self._L.hws_profile_enable(self.handle, int(enable)), "hws_profile_enable")
 

@@ -72,6 +72,7 @@ enum { HWS_SELECT_TOP_P = 0, HWS_SELECT_TOP_K = 1 };
 /* Selection score: INDEX = 16-dim pre-RoPE index ([RTPurbo] Methodology §2);
  * FULL = full-dim q.k, i.e. exact "oracle top-k" ([ICS] §2). */
 enum { HWS_SCORE_INDEX = 0, HWS_SCORE_FULL = 1 };
+enum { HWS_LAUNCH_AUTO = 0, HWS_LAUNCH_MULTI = 1, HWS_LAUNCH_COOPERATIVE = 2 };
 
 typedef struct hws_ctx hws_ctx; /* opaque host object, owned by the library */
 
@@ -199,12 +200,35 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
 hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
 /* (FULL scoring requires a bf16 cache: HWS_ERR_UNSUPPORTED otherwise.) */
 
+/* Launch shape of hws_decode.
+ *  HWS_LAUNCH_AUTO (the default): after the scoring scan, selection,
+ *    attention and merge run as ONE launch whose workgroups hand results to
+ *    each other through device memory and wait for each other, with the grid
+ *    sized to what the device holds at once (compute units x occupancy).  It
+ *    is an ordinary dispatch: it relies on this process having the device's
+ *    compute units (no CU masking); a kernel running concurrently on another
+ *    stream only delays it.  Every wait is bounded: a launch that cannot make
+ *    progress ends after about a second per wait with NaN outputs.
+ *  HWS_LAUNCH_COOPERATIVE: the same single launch as a cooperative launch,
+ *    so the runtime guarantees that all its workgroups are resident (costs a
+ *    few tens of microseconds of launch latency per call).
+ *  HWS_LAUNCH_MULTI: one kernel per stage, no waits between workgroups.
+ * The single launch is used when the device supports it and every retrieval
+ * tile (16384 positions of one sequence and head) fits the grid at two tiles
+ * per workgroup; otherwise the decode falls back to HWS_LAUNCH_MULTI.  All
+ * shapes select the same token sets; outputs differ only by the fp32 rounding
+ * order of the attention splits.  Returns HWS_ERR_INVALID_ARG for an unknown
+ * mode. */
+hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode);
+
 /* Optional per-stage timing with HIP events on the decode stream.
  * hws_profile_enable(ctx, 1) starts recording one event pair per stage per
  * decode call; hws_profile_read(ctx, ms, calls, n) waits for the recorded
  * events, writes the summed milliseconds of stage i to ms[i] and the number
  * of timed calls to calls[i] for i < n, then clears the record.  The stage
- * names come from hws_profile_stage_name(i) ("" past the last stage). */
+ * names come from hws_profile_stage_name(i) ("" past the last stage):
+ * score, select, attend, merge, and tail (the single launch that replaces
+ * select, attend and merge). */
 hws_status hws_profile_enable(hws_ctx* ctx, int32_t enable);
 hws_status hws_profile_read(hws_ctx* ctx, double* ms, int32_t* calls, int32_t n);
 const char* hws_profile_stage_name(int32_t i);

@@ -120,6 +120,19 @@ def test_bind_and_state_errors():
     assert e.value.status == hws.HWS_ERR_INVALID_ARG
 
 
+def test_launch_mode_values():
+    c = _ctx()
+    c.set_launch_mode(hws.HWS_LAUNCH_MULTI)
+    c.set_launch_mode(hws.HWS_LAUNCH_COOPERATIVE)
+    c.set_launch_mode(hws.HWS_LAUNCH_AUTO)
+    for bad in (-1, 3, 99):
+        with pytest.raises(hws.HwsError) as e:
+            c.set_launch_mode(bad)
+        assert e.value.status == hws.HWS_ERR_INVALID_ARG
+    assert hws.lib().hws_profile_stage_name(4) == b"tail"
+    assert hws.lib().hws_profile_stage_name(5) == b""
+
+
 class _FakeT:
     """Stand-in for a tensor: only shapes and addresses are read on the host."""
     def __init__(self, shape=(1, 1, 2, 128), nbytes=1 << 20):

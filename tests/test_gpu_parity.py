@@ -9,24 +9,30 @@ import pytest
 import torch
 
 import oracle as O
+from head_wise_sparse_02_amd import hws
 from head_wise_sparse_02_amd import workloads as W
 from head_wise_sparse_02_amd.runner import DecodeSetup, append_segments
 from gpu_check import check_decode
 
 pytestmark = pytest.mark.gpu
 
+AUTO, MULTI, COOP = hws.HWS_LAUNCH_AUTO, hws.HWS_LAUNCH_MULTI, hws.HWS_LAUNCH_COOPERATIVE
+BOTH = pytest.mark.parametrize("launch", [AUTO, MULTI], ids=["single", "multi"])
 
-def _run(wl, pairs=None, sequences=None, verbose=True, **kw):
+
+def _run(wl, pairs=None, sequences=None, verbose=True, launch=AUTO, **kw):
     print(f"\n[case] {wl.name} cfg={wl.cfg} B={wl.B} N={wl.seq_lens[:4]} G={wl.G} "
-          f"{wl.score_mode}/{wl.select_mode} kv={wl.kv_dtype} rope={wl.rope_theta}", flush=True)
+          f"{wl.score_mode}/{wl.select_mode} kv={wl.kv_dtype} rope={wl.rope_theta} launch={launch}", flush=True)
     st = DecodeSetup(wl, keep_host=True, sequences=sequences)
+    st.ctx.set_launch_mode(launch)
     res = st.decode(debug=True)
     reps = check_decode(st, res, pairs=pairs, verbose=verbose, **kw)
     return st, res, reps
 
 
-def test_tiny_workload_full_parity():
-    st, res, reps = _run(W.make_workload(1))
+@BOTH
+def test_tiny_workload_full_parity(launch):
+    st, res, reps = _run(W.make_workload(1), launch=launch)
     r0 = [r for r in reps if r["kind"] == "retrieval"][0]
     seq = st.host[0]
     sel = res["sel_idx"][0, 0][:res["sel_counts"][0, 0]]
@@ -39,25 +45,29 @@ def test_group_sizes(hq, hkv):
     _run(W.make_workload(1, n=3000, Hq=hq, Hkv=hkv))
 
 
-@pytest.mark.parametrize("n", [1, 2, 15, 17, 255, 1023, 1025, 16385, 20001])
-def test_ragged_lengths(n):
-    _run(W.make_workload(1, n=n, extra={"needle_range": (0, None)}))
+@BOTH
+@pytest.mark.parametrize("n", [1, 2, 15, 17, 255, 1023, 1025, 16385, 20001, 32769])
+def test_ragged_lengths(n, launch):
+    _run(W.make_workload(1, n=n, extra={"needle_range": (0, None)}), launch=launch)
 
 
-def test_full_scores_top_k():
+@BOTH
+def test_full_scores_top_k(launch):
     wl = W.make_workload(3, n=5000, batch=2)
-    _, res, reps = _run(wl)
+    _, res, reps = _run(wl, launch=launch)
     assert all(r["n_gpu"] == int(0.02 * 5000) for r in reps)
 
 
-def test_full_scores_top_p_and_index_top_k():
-    _run(W.make_workload(1, n=4100, score_mode="full"))
+@BOTH
+def test_full_scores_top_p_and_index_top_k(launch):
+    _run(W.make_workload(1, n=4100, score_mode="full"), launch=launch)
     _run(W.make_workload(2, n=3000, batch=2, select_mode="top_k",
-                         top_k=np.array([37, 1], np.int32)))
+                         top_k=np.array([37, 1], np.int32)), launch=launch)
 
 
+@BOTH
 @pytest.mark.parametrize("mode", ["top_p_one", "top_k_all", "window_all", "tiny_p"])
-def test_reductions_to_dense_and_degenerate(mode):
+def test_reductions_to_dense_and_degenerate(mode, launch):
     n = 777
     if mode == "top_p_one":
         wl = W.make_workload(1, n=n, top_p=np.array([1.0], np.float32))
@@ -67,7 +77,7 @@ def test_reductions_to_dense_and_degenerate(mode):
         wl = W.make_workload(1, n=n, window=4096, n_sink=8)
     else:
         wl = W.make_workload(1, n=n, top_p=np.array([1e-7], np.float32))
-    st, res, _ = _run(wl)
+    st, res, _ = _run(wl, launch=launch)
     if mode in ("top_p_one", "top_k_all"):
         assert res["sel_counts"][0, 0] == n
     if mode == "window_all":
@@ -76,19 +86,20 @@ def test_reductions_to_dense_and_degenerate(mode):
         assert res["sel_counts"][0, 0] == 1
 
 
-def test_exact_ties_top_k_lowest_positions():
+@BOTH
+def test_exact_ties_top_k_lowest_positions(launch):
     """All keys of the retrieval head equal: every a_i ties, so top-k keeps
     positions 0..k-1; top-p keeps every token (ties at the threshold)."""
     n = 40000
     seq = W.make_workload(1, n=n).sequence(0)
     seq.k[:, 0, :] = seq.k[0, 0, :]
-    for k in (1234, 20000):            # inside the first attention chunk / across chunks
+    for k in (1234, 20000, 39000):     # inside the first chunk / tile, across them
         wl = W.make_workload(1, n=n, select_mode="top_k", top_k=np.array([k], np.int32))
-        _, res, _ = _run(wl, sequences=[seq])
+        _, res, _ = _run(wl, sequences=[seq], launch=launch)
         assert res["sel_counts"][0, 0] == k
         np.testing.assert_array_equal(res["sel_idx"][0, 0, :k], np.arange(k))
     wl2 = W.make_workload(1, n=n)
-    _, res2, _ = _run(wl2, sequences=[seq])
+    _, res2, _ = _run(wl2, sequences=[seq], launch=launch)
     assert res2["sel_counts"][0, 0] == n
 
 
@@ -107,14 +118,47 @@ def test_long_256k_sampled():
     print("config 4 retrieval |S| =", res["sel_counts"][0, 0], flush=True)
 
 
-def test_ragged_fp8_mix_reduced():
-    wl = W.make_workload(5, n=12000, batch=12)
-    _run(wl, verbose=False)
+@BOTH
+def test_ragged_fp8_mix_reduced(launch):
+    wl = W.make_workload(5, n=40000, batch=12)
+    _run(wl, verbose=False, launch=launch)
 
 
+@BOTH
 @pytest.mark.parametrize("score_mode", ["index", "full"])
-def test_rope_on(score_mode):
-    _run(W.make_workload(1, n=3000, rope_theta=10000.0, score_mode=score_mode))
+def test_rope_on(score_mode, launch):
+    _run(W.make_workload(1, n=3000, rope_theta=10000.0, score_mode=score_mode), launch=launch)
+
+
+@pytest.mark.parametrize("cfg,kw", [(3, dict(n=40000, batch=4)), (2, dict(n=33000, batch=3)),
+                                    (5, dict(n=30000, batch=8))])
+def test_single_launch_matches_multi(cfg, kw):
+    """Same token sets from both launch shapes; outputs equal up to the fp32
+    rounding order of the attention splits.  The single launch is the one
+    that ran (its profile stage is recorded)."""
+    wl = W.make_workload(cfg, **kw)
+    st = DecodeSetup(wl)
+    st.ctx.profile_enable(True)
+    st.ctx.set_launch_mode(AUTO)
+    a = st.decode(debug=True)
+    prof = st.ctx.profile_read()
+    assert prof["tail"][1] == 1 and prof["select"][1] == 0, prof
+    st.ctx.set_launch_mode(MULTI)
+    m = st.decode(debug=True)
+    prof = st.ctx.profile_read()
+    assert prof["tail"][1] == 0 and prof["select"][1] == 1, prof
+    st.ctx.set_launch_mode(COOP)
+    c = st.decode(debug=True)
+    prof = st.ctx.profile_read()
+    assert prof["tail"][1] == 1 and prof["select"][1] == 0, prof
+    st.ctx.profile_enable(False)
+    for key in ("out", "lse", "sel_counts", "sel_idx", "scores"):   # same kernel, same grid
+        np.testing.assert_array_equal(a[key], c[key])
+    np.testing.assert_array_equal(a["sel_counts"], m["sel_counts"])
+    np.testing.assert_array_equal(a["sel_idx"], m["sel_idx"])
+    np.testing.assert_array_equal(a["scores"], m["scores"])
+    np.testing.assert_allclose(a["out"], m["out"], rtol=0, atol=2e-5)
+    np.testing.assert_allclose(a["lse"], m["lse"], rtol=0, atol=2e-5)
 
 
 def test_fp8_codes_and_scales_bit_exact():
