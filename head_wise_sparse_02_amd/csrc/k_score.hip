@@ -292,10 +292,11 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
 // contiguous 1 KiB block.  The blocks are staged in LDS and the workgroup
 // writes its CH x 16 bytes of scores in one burst after its last page:
 // interleaving small writes with the K stream costs read bandwidth.
-template <int CH>
+template <int CH, int GP, bool PF>
 __global__ __launch_bounds__(256) void score_full_g4_kernel(DecodeParams p) {
   constexpr int G = 4;
   constexpr int PW = CH / BS / 4;                          // pages per wave
+  static_assert(PW <= 64 && PW % GP == 0, "one page id per lane, whole groups");
   const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int N = min(p.seq_lens[b], p.Nmax);
@@ -323,48 +324,73 @@ __global__ __launch_bounds__(256) void score_full_g4_kernel(DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { m[i] = NEG_INF; sm[i] = 0.f; }
 
+  // page ids of this wave's pages, one per lane; read back wave-uniform with
+  // readlane so that page addresses are scalar and no load waits on another
   const int page0 = c * (CH / BS) + wave * PW;
-#pragma unroll 1
-  for (int i0 = 0; i0 < PW; i0 += 4) {
-    const int pgb = page0 + i0;
-    if (pgb * BS >= N) break;                              // wave-uniform
-    bf16x8 bfrag[4][4];
+  const int my_blk = (lane < PW && (page0 + lane) * BS < N) ? bt[page0 + lane] : -1;
+  const int npages = min(PW, max(0, (N - page0 * BS + BS - 1) / BS));
+  const size_t page_stride = (size_t)p.Hkv * (BS * D);
+  const uint16_t* kbase = kpool + (size_t)h * (BS * D) + (size_t)row * 32 + 8 * quad;
+
+  // GP pages per step; invalid pages read page 0 and are zeroed after the MFMA
+  bf16x8 cur[GP][4], nxt[GP][4];
+  unsigned vcur = 0u, vnxt = 0u;
+  auto load_group = [&](int pg, bf16x8 (&f)[GP][4], unsigned& valid) {
+    valid = 0u;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int blk = -1;
-      if ((pgb + u) * BS < N) blk = bt[pgb + u];
-      if ((unsigned)blk < (unsigned)p.num_blocks) {
-        // dim-blocked page: step s of all 16 rows is one contiguous 1 KiB run
-        const uint16_t* src = kpool + ((size_t)blk * p.Hkv + h) * (BS * D) + row * 32 + 8 * quad;
+    for (int u = 0; u < GP; ++u) {
+      const int blk = __builtin_amdgcn_readlane(my_blk, pg + u);
+      const bool ok = (unsigned)blk < (unsigned)p.num_blocks;
+      valid |= ok ? (1u << u) : 0u;
+      const uint16_t* src = kbase + (size_t)(ok ? blk : 0) * page_stride;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag[u][s] = __builtin_bit_cast(bf16x8, load_nt16(src + 512 * s));
-      } else {
+      for (int s2 = 0; s2 < 4; ++s2) f[u][s2] = __builtin_bit_cast(bf16x8, load_nt16(src + 512 * s2));
+    }
+  };
+  if (PF && npages > 0) load_group(0, cur, vcur);
+  for (int pg = 0; pg < npages; pg += GP) {
+    if (!PF) load_group(pg, cur, vcur);
+    else if (pg + GP < npages) load_group(pg + GP, nxt, vnxt);
+    // 4 pages per MFMA group: lane quad u keeps page u's accumulator
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag[u][s] = (bf16x8)(__bf16)0.f;
+    for (int u0 = 0; u0 < GP; u0 += 4) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (u0 + u < GP) {
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s2], cur[u0 + u < GP ? u0 + u : 0][s2], acc[u], 0, 0, 0);
+          if (!((vcur >> (u0 + u)) & 1u)) acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      // GP < 4: quads beyond GP hold no page this step
+      const int npg_here = GP < 4 ? GP : 4;
+      if (quad < npg_here) {
+        f32x4 v = acc[0];
+        v = quad == 1 ? acc[1] : v;
+        v = quad == 2 ? acc[2] : v;
+        v = quad == 3 ? acc[3] : v;
+        stage[(wave * PW + pg + u0) * BS + lane] = v;
+        const int t = (page0 + pg + u0) * BS + lane;     // token of this lane
+        if (t < N) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = v[i] * c2;
+            const float mn = fmaxf(m[i], x);
+            sm[i] = sm[i] * fast_exp2(m[i] - mn) + fast_exp2(x - mn);
+            m[i] = mn;
+          }
+        }
       }
     }
-    f32x4 acc[4];
+    if (PF) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < GP; ++u)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s], bfrag[u][s], acc[u], 0, 0, 0);
-    }
-    f32x4 v = acc[0];
-    v = quad == 1 ? acc[1] : v;
-    v = quad == 2 ? acc[2] : v;
-    v = quad == 3 ? acc[3] : v;
-    stage[(wave * PW + i0) * BS + lane] = v;
-    const int t = pgb * BS + lane;                         // token of this lane
-    if (t < N) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = v[i] * c2;
-        const float mn = fmaxf(m[i], x);
-        sm[i] = sm[i] * fast_exp2(m[i] - mn) + fast_exp2(x - mn);
-        m[i] = mn;
-      }
+        for (int s2 = 0; s2 < 4; ++s2) cur[u][s2] = nxt[u][s2];
+      vcur = vnxt;
     }
   }
 #pragma unroll
@@ -387,12 +413,15 @@ __global__ __launch_bounds__(256) void score_full_g4_kernel(DecodeParams p) {
   }
 }
 
+constexpr int G4_GP = 1;          // pages per load step of the G=4 scan
+constexpr bool G4_PF = true;      // issue the next step's loads before this step's MFMAs
+
 template <int G>
 static hipError_t launch_score_g(const DecodeParams& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.n_score_chunks, p.nR, p.B), blk(256);
   if (p.score_mode == 0) return launch_kernel(score_index_kernel<G>, grid, blk, st, e0, e1, p);
   if (p.qrot != nullptr) return launch_kernel(score_full_kernel<G, true>, grid, blk, st, e0, e1, p);
-  if (G == 4) return launch_kernel(score_full_g4_kernel<G4_SCORE_CHUNK>, grid, blk, st, e0, e1, p);
+  if (G == 4) return launch_kernel(score_full_g4_kernel<G4_SCORE_CHUNK, G4_GP, G4_PF>, grid, blk, st, e0, e1, p);
   return launch_kernel(score_full_kernel<G, false>, grid, blk, st, e0, e1, p);
 }
 
