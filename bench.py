@@ -28,9 +28,26 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_GBS = 8000.0          # MI355X HBM3E peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-STAGE_KERNEL = {"score": {"index": "score_index_kernel", "full": "score_full_kernel"},
-                "attend": {"index": "attend_kernel", "full": "attend_kernel"}}
-STAGE_SOURCE = {"score": "k_score.hip", "attend": "k_attend.hip"}
+STAGE_SOURCE = {"score": "k_score.hip", "attend": "k_attend.hip", "tail": "k_tail.hip", "fused": "k_tail.hip"}
+
+
+def stage_kernel(stage: str, wl) -> str:
+    """Name of the kernel that a profiled stage times (as rocprofv3 lists it)."""
+    if stage == "score":
+        if wl.score_mode == "index":
+            return "score_index_kernel"
+        return "score_full_g4_kernel" if (wl.G == 4 and not wl.rope_theta) else "score_full_kernel"
+    return {"attend": "attend_kernel", "tail": "tail_kernel", "fused": "fused_g4_kernel"}.get(stage, stage)
+
+
+def stage_bytes(stage: str, by: dict) -> int:
+    """Algorithmic bytes a stage moves: the fused launch moves all of them, the
+    tail launch the attention's and the step's inputs/outputs."""
+    if stage == "fused":
+        return by["total"]
+    if stage == "tail":
+        return by["attend"] + by["io"]
+    return by.get(stage, 0)
 
 
 def parse_args(argv=None):
@@ -95,11 +112,18 @@ def _read_traffic(stage: str, kernel: str, workload: str):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    src = os.path.join(ROOT, "head_wise_sparse_02_amd", "csrc", STAGE_SOURCE[stage])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != kernel_source_sha(stage):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def kernel_source_sha(stage: str) -> str:
+    """sha256 over the stage's kernel source and the device headers it includes."""
+    csrc = os.path.join(ROOT, "head_wise_sparse_02_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (STAGE_SOURCE[stage], "attend_rows.h", "hws_device.h", "hws_internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
 
 
 # ---------------------------------------------------------------------------
@@ -205,16 +229,18 @@ def main(argv=None) -> int:
     for name, (ms, calls) in prof.items():
         if calls:
             us = 1000.0 * ms / calls
-            b = by["attend"] + by["io"] if name == "tail" else by.get(name, 0)
-            stages[name] = {"us": round(us, 2), "bytes": b,
+            b = stage_bytes(name, by)
+            stages[name] = {"us": round(us, 2), "bytes": b, "kernel": stage_kernel(name, wl),
                             "GBps": round(b / (us * 1e3), 1) if b else None}
-    dom = max(("score", "attend"), key=lambda s: by[s])
+    # the kernel that moves the most algorithmic bytes
+    dom = max(stages, key=lambda n: stages[n]["bytes"])
     dom_us = stages[dom]["us"]
-    achieved = by[dom] / (dom_us * 1e3)
-    traffic = _read_traffic(dom, STAGE_KERNEL[dom][wl.score_mode], wl.name)
+    dom_bytes = stages[dom]["bytes"]
+    achieved = dom_bytes / (dom_us * 1e3)
+    traffic = _read_traffic(dom, stage_kernel(dom, wl), wl.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                "kernel": STAGE_KERNEL[dom][wl.score_mode], "bytes_per_launch": by[dom],
+                "kernel": stage_kernel(dom, wl), "bytes_per_launch": dom_bytes,
                 "avg_launch_us": dom_us}
 
     cold = None

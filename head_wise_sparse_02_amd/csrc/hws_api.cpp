@@ -20,8 +20,8 @@ using namespace hws;
 
 namespace {
 
-constexpr int NUM_STAGES = 5;
-const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge", "tail"};
+constexpr int NUM_STAGES = 6;
+const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge", "tail", "fused"};
 
 struct EvPair {
   hipEvent_t a, b;
@@ -381,6 +381,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.index_pool = ctx->buf.index_pool;
   p.proj = ctx->buf.proj;
   p.scores = a->scores != nullptr ? a->scores : reinterpret_cast<float*>(ws + L.scores);
+  p.scores_out = a->scores != nullptr ? 1 : 0;
   p.agg = reinterpret_cast<float*>(ws + L.agg);
   p.spart = reinterpret_cast<float2*>(ws + L.spart);
   p.sel = reinterpret_cast<SelState*>(ws + L.sel);
@@ -410,18 +411,26 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (rope && (e = launch_prep_q(p, s)) != hipSuccess) return hip_fail(ctx, e, "prep_q launch");
-  // Selection + attention + merge in one cooperative launch when every tile
-  // fits the co-resident grid; otherwise one kernel per stage.
-  const int nwg = (ctx->nR > 0 && ctx->launch_mode != HWS_LAUNCH_MULTI) ? tail_grid(p, ctx->launch_mode == HWS_LAUNCH_COOPERATIVE) : 0;
+  // Single launch after the scoring scan (or with the scan inside, one tile
+  // per workgroup, for full-dim G = 4 scoring) when every tile fits the
+  // grid the device holds at once; otherwise one kernel per stage.
+  const bool coop = ctx->launch_mode == HWS_LAUNCH_COOPERATIVE;
+  const bool single = ctx->nR > 0 && ctx->launch_mode != HWS_LAUNCH_MULTI;
+  const int nwf = single ? fused_grid(p, coop) : 0;
+  if (nwf > 0 && L.tail_ntiles <= nwf) {
+    p.n_score_chunks = L.tail_tph;                 // one (max, sum) partial per tile
+    const StageEv ef = stage_events(ctx, 5);
+    if ((e = launch_fused(p, nwf, coop, s, ef.start, ef.stop)) != hipSuccess) return hip_fail(ctx, e, "fused launch");
+    if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
+    return HWS_OK;
+  }
+  const int nwg = single ? tail_grid(p, coop) : 0;
   const bool tail = nwg > 0 && (long long)L.tail_ntiles <= (long long)TAIL_MAXT * nwg;
   if (tail) {
     const StageEv es = stage_events(ctx, 0);
     if ((e = launch_score(p, s, es.start, es.stop)) != hipSuccess) return hip_fail(ctx, e, "score launch");
     const StageEv et = stage_events(ctx, 4);
-    if (et.start != nullptr && (e = hipEventRecord(et.start, s)) != hipSuccess) return hip_fail(ctx, e, "event record");
-    if ((e = launch_tail(p, nwg, ctx->launch_mode == HWS_LAUNCH_COOPERATIVE, s)) != hipSuccess)
-      return hip_fail(ctx, e, "tail launch");
-    if (et.stop != nullptr && (e = hipEventRecord(et.stop, s)) != hipSuccess) return hip_fail(ctx, e, "event record");
+    if ((e = launch_tail(p, nwg, coop, s, et.start, et.stop)) != hipSuccess) return hip_fail(ctx, e, "tail launch");
     if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
     return HWS_OK;
   }

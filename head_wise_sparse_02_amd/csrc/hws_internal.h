@@ -85,6 +85,7 @@ struct DecodeParams {
   const float* index_pool;
   const float* proj;
   float* scores;                // [B][nR][Nmax][G]
+  int scores_out;               // the caller asked for every score (else only kept ones may be written)
   float* agg;                   // [B][nR][Nagg]
   float2* spart;                // [B][nR][n_score_chunks][G]  (max, sum) in log2 units
   SelState* sel;                // [B][nR]
@@ -147,7 +148,13 @@ hipError_t launch_emit(const DecodeParams& p, hipStream_t s);
 // if there is no such instantiation, or `cooperative` and the device has no
 // cooperative launches).
 int tail_grid(const DecodeParams& p, bool cooperative);
-hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s);
+hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
+                       hipEvent_t e1);
+// The same with the scoring scan inside (full-dim scores, G = 4, bf16, no
+// RoPE: 0 workgroups otherwise); launch_fused also resets the selection state.
+int fused_grid(const DecodeParams& p, bool cooperative);
+hipError_t launch_fused(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
+                        hipEvent_t e1);
 hipError_t launch_append(const AppendParams& p, int kv_fp8, hipStream_t s);
 
 }  // namespace hws

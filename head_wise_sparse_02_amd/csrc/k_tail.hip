@@ -93,8 +93,8 @@ __device__ __forceinline__ void block_wait(TailLds& S, const unsigned int* ctr, 
   __syncthreads();
 }
 
-// In-place exclusive scan of S.cnt (TPT * TW entries, (u, wave) order);
-// returns the total.  Entry order is position order inside the tile.
+// In-place exclusive scan of S.cnt (TPT * TW entries in position order);
+// returns the total.
 __device__ __forceinline__ unsigned int scan_cnt(TailLds& S) {
   constexpr int NE = TPT * TW;                // 256
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,13 +120,23 @@ __device__ __forceinline__ unsigned int scan_cnt(TailLds& S) {
   return tot;
 }
 
+// Token slot u of a thread: position u*TT + tid of the tile (slot-major, the
+// tail's layout) or wave*TPT*64 + u*64 + lane (wave-major, the fused scan's:
+// a wave owns 2048 consecutive positions).  cnt_idx orders the per-(u, wave)
+// counts by position.
+template <bool WM>
+__device__ __forceinline__ int cnt_idx(int u, int wave) { return WM ? wave * TPT + u : u * TW + wave; }
+template <bool WM>
+__device__ __forceinline__ int slot_pos(int u, int tid) { return WM ? (tid >> 6) * (TPT * 64) + u * 64 + (tid & 63) : u * TT + tid; }
+
 // Count the flagged tokens per (u, wave) in S.cnt (not yet scanned).
+template <bool WM>
 __device__ __forceinline__ void count_flags(TailLds& S, unsigned int mask) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int u = 0; u < TPT; ++u) {
     const unsigned long long bal = __ballot((mask >> u) & 1u);
-    if (lane == 0) S.cnt[u * TW + wave] = (unsigned int)__popcll(bal);
+    if (lane == 0) S.cnt[cnt_idx<WM>(u, wave)] = (unsigned int)__popcll(bal);
   }
 }
 
@@ -180,17 +190,19 @@ struct TileSel {
 
 // One radix pass over the workgroup's tiles: LDS histogram of the candidate
 // tokens, flush into the head's bins, arrive, wait for the head, scan.
-template <int PASS>
-__device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, const Tile (&tl)[MAXT],
-                           const float (&av)[MAXT][TPT], TileSel (&ts)[MAXT], bool bymass,
-                           unsigned int* err) {
+// The head's arrival counter is at `base` + (PASS - 1) * tiles per head
+// before the pass.
+template <int PASS, int NT>
+__device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, const Tile (&tl)[NT],
+                                           const float (&av)[NT][TPT], TileSel (&ts)[NT], bool bymass,
+                                           unsigned int* err, unsigned int base) {
   constexpr int NB = PASS == 1 ? HIST_BINS : (PASS == 2 ? P2_BINS : P3_BINS);
   constexpr int SHIFT = PASS == 1 ? P1_SHIFT : (PASS == 2 ? P2_SHIFT : 0);
   constexpr int KEY_SHIFT = PASS == 1 ? 31 : (PASS == 2 ? P1_SHIFT : P2_SHIFT);
   const int tid = threadIdx.x;
   bool any = false;
 #pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
+  for (int k = 0; k < NT; ++k) {
     if (tl[k].t < 0 || ts[k].done) continue;                 // uniform
     any = true;
     SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
@@ -218,15 +230,15 @@ __device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, co
   __syncthreads();
   if (tid == 0) {
 #pragma unroll
-    for (int k = 0; k < MAXT; ++k)
+    for (int k = 0; k < NT; ++k)
       if (tl[k].t >= 0 && !ts[k].done) atomicAdd(&p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].arrive, 1u);
   }
 #pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
+  for (int k = 0; k < NT; ++k) {
     if (tl[k].t < 0 || ts[k].done) continue;
     SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
     const unsigned long long* gh = PASS == 1 ? st->mass : (PASS == 2 ? st->mass2 : st->mass3);
-    block_wait(S, &st->arrive, (unsigned int)(PASS * p.tail_tph), err);
+    block_wait(S, &st->arrive, base + (unsigned int)(PASS * p.tail_tph), err);
     unsigned long long v[NB / TT];
 #pragma unroll
     for (int e = 0; e < NB / TT; ++e) v[e] = load_u64_coherent(&gh[tid + e * TT]);
@@ -411,6 +423,116 @@ __device__ __forceinline__ int local_rows(const DecodeParams& p, TailLds& S, int
   return nrows;
 }
 
+// Top-k ties at t*, then the kept-token masks: a_i > t*, and for top-k the
+// ties at t* that rank below the quota in position order.  Every tile of a
+// tie head publishes its tie count first and only then waits for the counts
+// of the head's other tiles, so the hand-off has no cycles.
+template <int NT, bool WM>
+__device__ __forceinline__ void tie_keep(const DecodeParams& p, TailLds& S, const Tile (&tl)[NT],
+                                         const float (&av)[NT][TPT], const TileSel (&ts)[NT],
+                                         unsigned int (&keepm)[NT], unsigned int* err) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned int before[NT];
+  bool any_tie = false;
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    before[k] = 0u;
+    if (tl[k].t < 0 || !ts[k].tie) continue;
+    any_tie = true;
+    unsigned int c = 0u;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) c += __float_as_uint(av[k][u]) == ts[k].tstar ? 1u : 0u;
+    for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off);
+    __syncthreads();
+    if (lane == 0) S.tmp[wave] = c;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned int tot = 0u;
+      for (int w2 = 0; w2 < TW; ++w2) tot += S.tmp[w2];
+      __hip_atomic_store(&p.tail_ties[tl[k].t], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (any_tie) {
+    wait_memory_ops();
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+      for (int k = 0; k < NT; ++k)
+        if (tl[k].t >= 0 && ts[k].tie) atomicAdd(&p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].tie_arrive, 1u);
+    }
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      if (tl[k].t < 0 || !ts[k].tie) continue;
+      block_wait(S, &p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].tie_arrive, (unsigned int)p.tail_tph, err);
+      if (tid == 0) {
+        unsigned int sum = 0u;
+        const int t0 = tl[k].t - tl[k].j;
+        for (int jj = 0; jj < tl[k].j; ++jj) sum += load_u32_coherent(&p.tail_ties[t0 + jj]);
+        S.tmp[TW] = sum;
+      }
+      __syncthreads();
+      before[k] = S.tmp[TW];
+      __syncthreads();
+    }
+  }
+
+  // ---- kept tokens: a_i > t*, and for top-k the ties at t* that rank below
+  // the quota in position order ----
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    keepm[k] = 0u;
+    if (tl[k].t < 0) continue;
+    SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
+    const unsigned int tstar = ts[k].tstar;
+    if (tl[k].j == 0 && tid == 0) {
+      st->tstar = tstar;
+      st->quota = ts[k].quota;
+      st->flags = SEL_FINISHED | (ts[k].tie ? SEL_TIE : 0u);
+    }
+    unsigned int gt = 0u, eq = 0u;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const unsigned int bits = __float_as_uint(av[k][u]);
+      if (!(bits >> 31)) {
+        if (bits > tstar) gt |= 1u << u;
+        else if (bits == tstar) eq |= 1u << u;
+      }
+    }
+    if (ts[k].tie) {
+      __syncthreads();
+      count_flags<WM>(S, eq);
+      __syncthreads();
+      scan_cnt(S);
+      unsigned int kept = 0u;
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const unsigned long long bal = __ballot((eq >> u) & 1u);
+        const unsigned int rank = before[k] + S.cnt[cnt_idx<WM>(u, wave)] + lane_rank(bal);
+        if (((eq >> u) & 1u) && rank < ts[k].quota) kept |= 1u << u;
+      }
+      eq = kept;
+      __syncthreads();
+    }
+    keepm[k] = gt | eq;
+  }
+}
+
+// Kept positions of a tile (bit u of `keep` = slot u of this thread) into
+// S.u.rows in position order; returns their number.
+template <bool WM>
+__device__ __forceinline__ int compact_rows(TailLds& S, unsigned int keep) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  count_flags<WM>(S, keep);
+  __syncthreads();
+  const int nrows = (int)scan_cnt(S);
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const unsigned long long bal = __ballot((keep >> u) & 1u);
+    if ((keep >> u) & 1u) S.u.rows[S.cnt[cnt_idx<WM>(u, wave)] + lane_rank(bal)] = (unsigned short)slot_pos<WM>(u, tid);
+  }
+  return nrows;
+}
+
 // Selection for the tiles of workgroup blockIdx.x (tile t = blockIdx.x + k *
 // gridDim.x): a_i of every token, the three radix passes, top-k ties.  Leaves
 // the tiles in tl, their kept-token masks in keepm and the block-table
@@ -530,97 +652,12 @@ __device__ __forceinline__ void select_tiles(const DecodeParams& p, TailLds& S, 
   }
 
   // ---- three radix passes; the tiles of a head wait only for each other ----
-  radix_pass<1>(p, S, tl, av, ts, bymass, err);
-  radix_pass<2>(p, S, tl, av, ts, bymass, err);
-  radix_pass<3>(p, S, tl, av, ts, bymass, err);
-
-  // ---- top-k ties at t*: every tile publishes its count, then each tile
-  // sums the counts of the earlier tiles of its head.  Publishing for all
-  // tiles before waiting keeps the hand-off free of cycles. ----
-  unsigned int before[MAXT];
-  bool any_tie = false;
+  radix_pass<1, MAXT>(p, S, tl, av, ts, bymass, err, 0u);
+  radix_pass<2, MAXT>(p, S, tl, av, ts, bymass, err, 0u);
+  radix_pass<3, MAXT>(p, S, tl, av, ts, bymass, err, 0u);
+  tie_keep<MAXT, false>(p, S, tl, av, ts, keepm, err);
 #pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
-    before[k] = 0u;
-    if (tl[k].t < 0 || !ts[k].tie) continue;
-    any_tie = true;
-    unsigned int c = 0u;
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) c += __float_as_uint(av[k][u]) == ts[k].tstar ? 1u : 0u;
-    for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off);
-    __syncthreads();
-    if (lane == 0) S.tmp[wave] = c;
-    __syncthreads();
-    if (tid == 0) {
-      unsigned int tot = 0u;
-      for (int w2 = 0; w2 < TW; ++w2) tot += S.tmp[w2];
-      __hip_atomic_store(&p.tail_ties[tl[k].t], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  if (any_tie) {
-    wait_memory_ops();
-    __syncthreads();
-    if (tid == 0) {
-#pragma unroll
-      for (int k = 0; k < MAXT; ++k)
-        if (tl[k].t >= 0 && ts[k].tie) atomicAdd(&p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].tie_arrive, 1u);
-    }
-#pragma unroll
-    for (int k = 0; k < MAXT; ++k) {
-      if (tl[k].t < 0 || !ts[k].tie) continue;
-      block_wait(S, &p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].tie_arrive, (unsigned int)p.tail_tph, err);
-      if (tid == 0) {
-        unsigned int sum = 0u;
-        const int t0 = tl[k].t - tl[k].j;
-        for (int jj = 0; jj < tl[k].j; ++jj) sum += load_u32_coherent(&p.tail_ties[t0 + jj]);
-        S.tmp[TW] = sum;
-      }
-      __syncthreads();
-      before[k] = S.tmp[TW];
-      __syncthreads();
-    }
-  }
-
-  // ---- kept tokens: a_i > t*, and for top-k the ties at t* that rank below
-  // the quota in position order ----
-#pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
-    keepm[k] = 0u;
-    if (tl[k].t < 0) continue;
-    ++my_tiles;
-    SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
-    const unsigned int tstar = ts[k].tstar;
-    if (tl[k].j == 0 && tid == 0) {
-      st->tstar = tstar;
-      st->quota = ts[k].quota;
-      st->flags = SEL_FINISHED | (ts[k].tie ? SEL_TIE : 0u);
-    }
-    unsigned int gt = 0u, eq = 0u;
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const unsigned int bits = __float_as_uint(av[k][u]);
-      if (!(bits >> 31)) {
-        if (bits > tstar) gt |= 1u << u;
-        else if (bits == tstar) eq |= 1u << u;
-      }
-    }
-    if (ts[k].tie) {
-      __syncthreads();
-      count_flags(S, eq);
-      __syncthreads();
-      scan_cnt(S);
-      unsigned int kept = 0u;
-#pragma unroll
-      for (int u = 0; u < TPT; ++u) {
-        const unsigned long long bal = __ballot((eq >> u) & 1u);
-        const unsigned int rank = before[k] + S.cnt[u * TW + wave] + lane_rank(bal);
-        if (((eq >> u) & 1u) && rank < ts[k].quota) kept |= 1u << u;
-      }
-      eq = kept;
-      __syncthreads();
-    }
-    keepm[k] = gt | eq;
-  }
+  for (int k = 0; k < MAXT; ++k) my_tiles += tl[k].t >= 0 ? 1 : 0;
 }
 
 template <int G, bool FP8, int MODE>
@@ -655,14 +692,7 @@ __global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
       split = t.j;
       lo = t.lo;
       pages = S.pages[wi == 0 ? 0 : MAXT - 1];
-      count_flags(S, keep);
-      __syncthreads();
-      nrows = (int)scan_cnt(S);
-#pragma unroll
-      for (int u = 0; u < TPT; ++u) {
-        const unsigned long long bal = __ballot((keep >> u) & 1u);
-        if ((keep >> u) & 1u) S.u.rows[S.cnt[u * TW + wave] + lane_rank(bal)] = (unsigned short)(u * TT + tid);
-      }
+      nrows = compact_rows<false>(S, keep);
       if (tid == 0 && nrows > 0) atomicAdd(&p.sel[(size_t)b * p.nR + hr].nsel, (unsigned int)nrows);
     } else {
       hr = -1;
@@ -674,6 +704,230 @@ __global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
     else empty_split<G>(p, b, h, split);
     finish_split<G>(p, S, b, h, hr);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode: full-dim scores, G = 4, bf16 cache, unrotated queries.  The
+// scoring scan runs inside the same launch, one tile per workgroup, and the
+// tile's 16384 x 4 scores stay in registers: wave w scans pages
+// w*128 .. w*128+127 of the tile, four at a time (the MFMA layout of the
+// scoring kernel: lane quad u takes page u, so each lane owns one token of
+// every 4-page group, 32 tokens in all).  The log-sum-exp of every query
+// head is exchanged between the tiles of the head like a radix pass; then
+// a_i, the passes, the compaction and the attention follow as in the tail.
+// Only the kept tokens' scores are written out (the attention reads its
+// logits from there), unless all scores were asked for.
+// ---------------------------------------------------------------------------
+constexpr int FPW = TAIL_TILE / BS / TW;     // pages per wave: 128
+static_assert(FPW == 4 * TPT, "a lane owns one token of every 4-page group");
+
+template <int MODE>
+__device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, unsigned int* err) {
+  constexpr int G = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, quad = lane >> 4;
+  const bool bymass = p.select_mode == 0;
+  Tile tl[1];
+  TileSel ts[1];
+  {
+    const int t = blockIdx.x, head = t / p.tail_tph;
+    tl[0].t = t;
+    tl[0].j = t % p.tail_tph;
+    tl[0].b = head / p.nR;
+    tl[0].hr = head % p.nR;
+    tl[0].N = min(p.seq_lens[tl[0].b], p.Nmax);
+    tl[0].lo = tl[0].j * TAIL_TILE;
+    tl[0].hi = min(tl[0].N, tl[0].lo + TAIL_TILE);
+    ts[0] = TileSel{false, 0u, 0ull, 0u, false, 0u};
+  }
+  const int b = tl[0].b, hr = tl[0].hr, j = tl[0].j, N = tl[0].N, lo = tl[0].lo, hi = tl[0].hi;
+  const int h = p.ret_head[hr];
+  const size_t hrow = (size_t)(b * p.nR + hr);
+  SelState* st = p.sel + hrow;
+
+  // ---- scoring scan: x[u] = the 4 raw scores q_g . k of this lane's token u ----
+  bf16x8 afrag[4];
+  {
+    const uint16_t* qg = p.q + ((size_t)b * p.Hq + h * G + (row & 3)) * D + 8 * quad;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) afrag[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qg + 32 * s2));
+  }
+  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
+  const int page0 = (lo >> 4) + wave * FPW;                // sequence page of this wave's first page
+  const int blkA = (page0 + lane) * BS < N ? bt[page0 + lane] : -1;
+  const int blkB = (page0 + 64 + lane) * BS < N ? bt[page0 + 64 + lane] : -1;
+  S.pages[0][wave * FPW + lane] = blkA;
+  S.pages[0][wave * FPW + 64 + lane] = blkB;
+  const int ngroups = min(TPT, max(0, (N - page0 * BS + 4 * BS - 1) / (4 * BS)));
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k_pool) + (size_t)h * (BS * D) + (size_t)row * 32 + 8 * quad;
+  const size_t page_stride = (size_t)p.Hkv * (BS * D);
+  const float c2 = p.c2_score;
+  float x[TPT][G];
+  float m[G], sm[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { m[g] = NEG_INF; sm[g] = 0.f; }
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) x[u][g] = 0.f;
+    if (u < ngroups) {                                     // wave-uniform
+      bf16x8 f[4][4];
+      unsigned valid = 0u;
+#pragma unroll
+      for (int pg = 0; pg < 4; ++pg) {
+        const int idx = 4 * u + pg;
+        const int blk = __builtin_amdgcn_readlane(idx < 64 ? blkA : blkB, idx & 63);
+        const bool ok = (unsigned)blk < (unsigned)p.num_blocks;
+        valid |= ok ? (1u << pg) : 0u;
+        const uint16_t* src = kbase + (size_t)(ok ? blk : 0) * page_stride;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) f[pg][s2] = __builtin_bit_cast(bf16x8, load_nt16(src + 512 * s2));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc[4];
+#pragma unroll
+      for (int pg = 0; pg < 4; ++pg) {
+        acc[pg] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          acc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s2], f[pg][s2], acc[pg], 0, 0, 0);
+        if (!((valid >> pg) & 1u)) acc[pg] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+      f32x4 v = acc[0];
+      v = quad == 1 ? acc[1] : v;
+      v = quad == 2 ? acc[2] : v;
+      v = quad == 3 ? acc[3] : v;
+#pragma unroll
+      for (int g = 0; g < G; ++g) x[u][g] = v[g];
+      if (lo + wave * (TPT * 64) + u * 64 + lane < hi) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float z = v[g] * c2;
+          const float mn = fmaxf(m[g], z);
+          sm[g] = sm[g] * fast_exp2(m[g] - mn) + fast_exp2(z - mn);
+          m[g] = mn;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- log-sum-exp of the head: this tile's partial, exchanged between tiles ----
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    for (int off = 1; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m[g], off), s2 = __shfl_xor(sm[g], off);
+      lse_combine(m[g], sm[g], m2, s2);
+    }
+    if (lane == 0) { S.wm[wave][g] = m[g]; S.wl[wave][g] = sm[g]; }
+  }
+  __syncthreads();
+  float* spf = reinterpret_cast<float*>(p.spart) + hrow * p.n_score_chunks * G * 2;   // [tile][g] (max, sum)
+  if (tid < G) {
+    float mm = S.wm[0][tid], ss = S.wl[0][tid];
+    for (int w2 = 1; w2 < TW; ++w2) lse_combine(mm, ss, S.wm[w2][tid], S.wl[w2][tid]);
+    store_f32_coherent(spf + ((size_t)j * G + tid) * 2, mm);
+    store_f32_coherent(spf + ((size_t)j * G + tid) * 2 + 1, ss);
+  }
+  wait_memory_ops();
+  __syncthreads();
+  if (tid == 0) atomicAdd(&st->arrive, 1u);
+  block_wait(S, &st->arrive, (unsigned int)p.tail_tph, err);
+  if (wave < G) {
+    float mm = NEG_INF, ss = 0.f;
+    for (int jj = lane; jj < p.tail_tph; jj += 64)
+      lse_combine(mm, ss, load_f32_coherent(spf + ((size_t)jj * G + wave) * 2),
+                  load_f32_coherent(spf + ((size_t)jj * G + wave) * 2 + 1));
+    for (int off = 1; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(mm, off), s2 = __shfl_xor(ss, off);
+      lse_combine(mm, ss, m2, s2);
+    }
+    if (lane == 0) S.lse[0][wave] = mm + log2f(ss);
+  }
+  __syncthreads();
+  float lse[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) lse[g] = S.lse[0][g];
+  if (j == 0 && tid < G) st->lse2[tid] = S.lse[0][tid];
+
+  // ---- a_i = mean_g 2^(x_gi - LSE2_g) ----
+  float av[1][TPT];
+  float* agg = p.sel_idx != nullptr ? p.agg + hrow * p.Nagg : nullptr;
+  float* sc = p.scores + hrow * p.Nmax * G;
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const int i = lo + wave * (TPT * 64) + u * 64 + lane;
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) a += fast_exp2(x[u][g] * c2 - lse[g]);
+    a *= 0.25f;
+    av[0][u] = i < hi ? a : -1.0f;
+    if (i < hi) {
+      if (agg != nullptr) agg[i] = a;
+      if (p.scores_out) *reinterpret_cast<f32x4*>(sc + (size_t)i * G) = (f32x4){x[u][0], x[u][1], x[u][2], x[u][3]};
+    }
+  }
+  if (N == 0 || (bymass ? !(p.top_p[b] < 1.0f) : max(p.top_k[b], 1) >= N)) {
+    ts[0].done = true;                           // the whole sequence kept
+    ts[0].tstar = 0u;
+  }
+
+  // ---- radix passes (the arrival counter already holds the exchange) ----
+  const unsigned int base = (unsigned int)p.tail_tph;
+  radix_pass<1, 1>(p, S, tl, av, ts, bymass, err, base);
+  radix_pass<2, 1>(p, S, tl, av, ts, bymass, err, base);
+  radix_pass<3, 1>(p, S, tl, av, ts, bymass, err, base);
+  unsigned int keepm[1];
+  tie_keep<1, true>(p, S, tl, av, ts, keepm, err);
+  const unsigned int keep = keepm[0];
+
+  // ---- kept tokens' scores out (the attention's logits), then compaction ----
+  if (!p.scores_out) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u)
+      if ((keep >> u) & 1u) {
+        const int i = lo + wave * (TPT * 64) + u * 64 + lane;
+        *reinterpret_cast<f32x4*>(sc + (size_t)i * G) = (f32x4){x[u][0], x[u][1], x[u][2], x[u][3]};
+      }
+  }
+  wait_memory_ops();
+  __syncthreads();
+  const int nrows = compact_rows<true>(S, keep);
+  if (tid == 0 && nrows > 0) atomicAdd(&st->nsel, (unsigned int)nrows);
+  __syncthreads();
+  if (nrows > 0) attend_rows<G, false, MODE>(p, S, b, h, hr, j, lo, nrows, S.pages[0]);
+  else empty_split<G>(p, b, h, j);
+  finish_split<G>(p, S, b, h, hr);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
+  __shared__ TailLds S;
+  const int w = blockIdx.x, nwg = gridDim.x;
+  unsigned int* err = p.tail_sync;
+  if (w < p.tail_ntiles) fused_tile<MODE>(p, S, err);
+  if constexpr (MODE != 1) {
+    // local-head chunks: item i goes to workgroup (ntiles + i) mod nwg
+    const int nitems = p.B * p.nL * p.ncL;
+    const int first_item = ((w - p.tail_ntiles) % nwg + nwg) % nwg;
+    for (int it = first_item; it < nitems; it += nwg) {
+      int b, h, c;
+      __syncthreads();
+      const int nrows = local_rows(p, S, it, b, h, c);
+      __syncthreads();
+      if (nrows > 0) attend_rows<4, false, MODE>(p, S, b, h, -1, c, 0, nrows, nullptr);
+      else empty_split<4>(p, b, h, c);
+      finish_split<4>(p, S, b, h, -1);
+    }
+  }
+}
+
+// Selection state and split counters back to zero before a fused launch.
+__global__ __launch_bounds__(256) void reset_state_kernel(DecodeParams p) {
+  unsigned int* w = reinterpret_cast<unsigned int*>(p.sel + blockIdx.x);
+  for (int i = threadIdx.x; i < SELSTATE_WORDS; i += 256) w[i] = 0u;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < 1 + p.B * p.Hkv; i += 256) p.tail_sync[i] = 0u;
 }
 
 template <int G, bool FP8, int MODE>
@@ -727,14 +981,68 @@ int tail_grid(const DecodeParams& p, bool cooperative) {
   return (cooperative && hit->coop == 0) ? 0 : hit->nwg;
 }
 
-hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s) {
-  void* fn = pick_kernel(p);
-  if (fn == nullptr || nwg < 1) return hipErrorInvalidValue;
+void* pick_fused(const DecodeParams& p) {
+  if (p.G != 4 || p.score_mode != 1 || p.kv_scales != nullptr || p.qrot != nullptr) return nullptr;
+  return p.nL == 0 ? reinterpret_cast<void*>(&fused_g4_kernel<1>) : reinterpret_cast<void*>(&fused_g4_kernel<2>);
+}
+
+int fused_grid(const DecodeParams& p, bool cooperative) {
+  void* fn = pick_fused(p);
+  if (fn == nullptr) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  struct Entry { void* fn; int dev; int nwg; int coop; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const Entry* hit = nullptr;
+  for (const Entry& e : cache)
+    if (e.fn == fn && e.dev == dev) hit = &e;
+  if (hit == nullptr) {
+    int ncu = 0, occ = 0, coop = 0;
+    int nwg = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(fn), TT, 0) == hipSuccess)
+      nwg = ncu * occ;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
+    cache.push_back(Entry{fn, dev, nwg, coop});
+    hit = &cache.back();
+  }
+  return (cooperative && hit->coop == 0) ? 0 : hit->nwg;
+}
+
+// Launch `fn` on nwg workgroups; e0 / e1 (optional) time the dispatch itself.
+hipError_t launch_single(void* fn, const DecodeParams& p, int nwg, bool cooperative, hipStream_t s,
+                         hipEvent_t e0, hipEvent_t e1) {
   DecodeParams arg = p;
   void* args[] = {&arg};
-  if (cooperative)
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(TT), args, 0, s);
+  hipError_t e;
+  if (cooperative) {
+    if (e0 != nullptr && (e = hipEventRecord(e0, s)) != hipSuccess) return e;
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(TT), args, 0, s);
+    if (e == hipSuccess && e1 != nullptr) e = hipEventRecord(e1, s);
+    return e;
+  }
+  if (e0 != nullptr || e1 != nullptr)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(TT), args, 0, s, e0, e1, 0);
   return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(nwg), dim3(TT), args, 0, s);
+}
+
+hipError_t launch_fused(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
+                        hipEvent_t e1) {
+  void* fn = pick_fused(p);
+  if (fn == nullptr || nwg < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reset_state_kernel, dim3(p.B * p.nR), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_single(fn, p, nwg, cooperative, s, e0, e1);
+}
+
+hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
+                       hipEvent_t e1) {
+  void* fn = pick_kernel(p);
+  if (fn == nullptr || nwg < 1) return hipErrorInvalidValue;
+  return launch_single(fn, p, nwg, cooperative, s, e0, e1);
 }
 
 }  // namespace hws

@@ -227,8 +227,9 @@ hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode);
  * events, writes the summed milliseconds of stage i to ms[i] and the number
  * of timed calls to calls[i] for i < n, then clears the record.  The stage
  * names come from hws_profile_stage_name(i) ("" past the last stage):
- * score, select, attend, merge, and tail (the single launch that replaces
- * select, attend and merge). */
+ * score, select, attend, merge, tail (the single launch that replaces
+ * select, attend and merge) and fused (the single launch that also does the
+ * scoring scan). */
 hws_status hws_profile_enable(hws_ctx* ctx, int32_t enable);
 hws_status hws_profile_read(hws_ctx* ctx, double* ms, int32_t* calls, int32_t n);
 const char* hws_profile_stage_name(int32_t i);

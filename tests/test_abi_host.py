@@ -130,7 +130,8 @@ def test_launch_mode_values():
             c.set_launch_mode(bad)
         assert e.value.status == hws.HWS_ERR_INVALID_ARG
     assert hws.lib().hws_profile_stage_name(4) == b"tail"
-    assert hws.lib().hws_profile_stage_name(5) == b""
+    assert hws.lib().hws_profile_stage_name(5) == b"fused"
+    assert hws.lib().hws_profile_stage_name(6) == b""
 
 
 class _FakeT:

@@ -138,11 +138,12 @@ def test_single_launch_matches_multi(cfg, kw):
     that ran (its profile stage is recorded)."""
     wl = W.make_workload(cfg, **kw)
     st = DecodeSetup(wl)
+    single = "fused" if (wl.score_mode == "full" and wl.G == 4 and not wl.rope_theta) else "tail"
     st.ctx.profile_enable(True)
     st.ctx.set_launch_mode(AUTO)
     a = st.decode(debug=True)
     prof = st.ctx.profile_read()
-    assert prof["tail"][1] == 1 and prof["select"][1] == 0, prof
+    assert prof[single][1] == 1 and prof["select"][1] == 0, prof
     st.ctx.set_launch_mode(MULTI)
     m = st.decode(debug=True)
     prof = st.ctx.profile_read()
@@ -150,7 +151,7 @@ def test_single_launch_matches_multi(cfg, kw):
     st.ctx.set_launch_mode(COOP)
     c = st.decode(debug=True)
     prof = st.ctx.profile_read()
-    assert prof["tail"][1] == 1 and prof["select"][1] == 0, prof
+    assert prof[single][1] == 1 and prof["select"][1] == 0, prof
     st.ctx.profile_enable(False)
     for key in ("out", "lse", "sel_counts", "sel_idx", "scores"):   # same kernel, same grid
         np.testing.assert_array_equal(a[key], c[key])
@@ -211,3 +212,54 @@ def test_repeat_is_bitwise_deterministic():
     st.decode(debug=False)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(st.out.cpu().numpy(), first["out"])
+
+
+# -- single launch with the scoring scan inside (full-dim scores, G = 4) ------
+
+@pytest.mark.parametrize("n", [1, 17, 1000, 4097, 16384, 16385, 40000])
+def test_fused_ragged_lengths(n):
+    """Tiles past the end, partial pages and partial tiles; with a local head
+    (config 1 shape) the local chunks run in the same launch."""
+    _run(W.make_workload(1, n=n, score_mode="full", extra={"needle_range": (0, None)}))
+
+
+def test_fused_top_k_batch_and_ties():
+    _run(W.make_workload(3, n=33000, batch=3))
+    n = 40000
+    seq = W.make_workload(1, n=n).sequence(0)
+    seq.k[:, 0, :] = seq.k[0, 0, :]                  # every logit of head 0 equal
+    for k in (1234, 20000, 39000):
+        wl = W.make_workload(1, n=n, score_mode="full", select_mode="top_k", top_k=np.array([k], np.int32))
+        _, res, _ = _run(wl, sequences=[seq])
+        assert res["sel_counts"][0, 0] == k
+        np.testing.assert_array_equal(res["sel_idx"][0, 0, :k], np.arange(k))
+
+
+@pytest.mark.parametrize("mode", ["top_p_one", "top_k_all", "tiny_p"])
+def test_fused_degenerate(mode):
+    n = 5000
+    if mode == "top_p_one":
+        wl = W.make_workload(1, n=n, score_mode="full", top_p=np.array([1.0], np.float32))
+    elif mode == "top_k_all":
+        wl = W.make_workload(1, n=n, score_mode="full", select_mode="top_k", top_k=np.array([9000], np.int32))
+    else:
+        wl = W.make_workload(1, n=n, score_mode="full", top_p=np.array([1e-7], np.float32))
+    _, res, _ = _run(wl)
+    assert res["sel_counts"][0, 0] == (1 if mode == "tiny_p" else n)
+
+
+def test_fused_timed_path_matches_debug_path():
+    """Without debug outputs the fused launch writes only the kept tokens'
+    scores; the results are bitwise those of the debug run."""
+    wl = W.make_workload(3, n=50000, batch=2)
+    st = DecodeSetup(wl)
+    st.ctx.profile_enable(True)
+    full = st.decode(debug=True)
+    st.decode(debug=False)
+    torch.cuda.synchronize()
+    prof = st.ctx.profile_read()
+    st.ctx.profile_enable(False)
+    assert prof["fused"][1] == 2, prof
+    np.testing.assert_array_equal(st.out.cpu().numpy(), full["out"])
+    np.testing.assert_array_equal(st.lse.cpu().numpy(), full["lse"])
+    np.testing.assert_array_equal(st.sel_counts.cpu().numpy(), full["sel_counts"])
