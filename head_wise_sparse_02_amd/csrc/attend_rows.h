@@ -25,14 +25,18 @@ struct AttRB {
 // page is pages[offset / 16]; local rows are tokens ltok[r] on page lpg[r].
 // MODE 0: logits q.k from K rows; MODE 1: retrieval heads only, logits from
 // the stored full-dim scores; MODE 2: both (scores for retrieval heads).
-template <int G, bool FP8, int MODE>
+// RET: the rows are known to be a retrieval head's (no K path compiled in).
+// lds_logits (full-dim scores only): the scores of row r at lds_logits[r*G];
+// null reads them from the scores buffer at the row's position.
+template <int G, bool FP8, int MODE, int RB, bool RET = false>
 __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, int h, int hr, int lo, int nrows,
                                                 int r_begin, int r_step, int sub, const unsigned short* rows,
-                                                const int* pages, const int* ltok, const int* lpg, float (&m)[G],
-                                                float (&l)[G], float (&o)[G][8]) {
-  constexpr bool NEED_K = MODE != 1;
-  constexpr int RB = AttRB<G, MODE>::value;
-  const bool is_ret = hr >= 0;
+                                                const int* pages, const int* ltok, const int* lpg,
+                                                const float* lds_logits, float (&m)[G], float (&l)[G],
+                                                float (&o)[G][8]) {
+  static_assert(!RET || MODE != 0, "retrieval rows read K only in index mode");
+  constexpr bool NEED_K = MODE != 1 && !RET;
+  const bool is_ret = RET || hr >= 0;
   const bool use_scores = MODE != 0 && is_ret;
 
   // queries of the group, pre-scaled to log2 units: dims 8*sub..8*sub+7
@@ -104,7 +108,14 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
         vs[u] = s2.y;
       }
     }
-    if (use_scores) {
+    if (use_scores && lds_logits != nullptr) {
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int rc = min(r0 + u, nrows - 1);
+#pragma unroll
+        for (int g = 0; g < G; ++g) z[u][g] = lds_logits[(size_t)rc * G + g];
+      }
+    } else if (use_scores) {
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         if (G >= 4) {

@@ -186,7 +186,22 @@ struct TileSel {
   unsigned int tstar;
   bool tie;                     // top-k: keep only `quota` lowest-position ties
   unsigned int quota;
+  unsigned long long target;    // mass (fixed point) or count the threshold must reach
 };
+
+// The threshold's target for sequence b, and whether the whole sequence of N
+// tokens is kept (p >= 1 or k >= N).
+__device__ __forceinline__ unsigned long long sel_target(const DecodeParams& p, int b, int N, bool& all) {
+  if (p.select_mode == 0) {
+    const float pp = p.top_p[b];
+    all = N == 0 || !(pp < 1.0f);
+    const unsigned long long tg = pp > 0.f ? (unsigned long long)((double)pp * 1099511627776.0) : 0ull;
+    return tg > 0ull ? tg : 1ull;              // p <= 0: the largest value alone
+  }
+  const int k = max(p.top_k[b], 1);
+  all = k >= N;
+  return (unsigned long long)k;
+}
 
 // One radix pass over the workgroup's tiles: LDS histogram of the candidate
 // tokens, flush into the head's bins, arrive, wait for the head, scan.
@@ -245,14 +260,7 @@ __device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, co
 #pragma unroll
     for (int e = 0; e < NB / TT; ++e) S.u.hist[tid + e * TT] = v[e];
     __syncthreads();
-    unsigned long long target;
-    if (bymass) {
-      const float pp = p.top_p[tl[k].b];
-      const unsigned long long tg = pp > 0.f ? (unsigned long long)((double)pp * 1099511627776.0) : 0ull;
-      target = tg > 0ull ? tg : 1ull;          // p <= 0: the largest value alone
-    } else {
-      target = (unsigned long long)max(p.top_k[tl[k].b], 1);
-    }
+    const unsigned long long target = ts[k].target;
     int bin;
     unsigned long long above;
     scan_top(S, NB, ts[k].above, target, bin, above);
@@ -279,18 +287,17 @@ __device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, co
 
 // Attention of one workgroup over `nrows` rows of KV head h, then the split
 // partial (max, sum, unnormalised output) in log2 units, coherent stores.
-template <int G, bool FP8, int MODE>
+template <int G, bool FP8, int MODE, int RB = AttRB<G, MODE>::value, bool RET = false>
 __device__ __forceinline__ void attend_rows(const DecodeParams& p, TailLds& S, int b, int h, int hr, int split, int lo,
-                            int nrows, const int* pages) {
-  constexpr int RB = AttRB<G, MODE>::value;
+                                            int nrows, const int* pages, const float* lds_logits = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int proc = tid >> 4, sub = tid & 15;
   const size_t pbase = (size_t)(b * p.Hkv + h) * p.max_splits + split;
   float* ml = reinterpret_cast<float*>(p.apart_ml) + pbase * G * 2;   // (max, sum) pairs
   float* po = p.apart_o + pbase * G * D;
   float m[G], l[G], o[G][8];
-  accumulate_rows<G, FP8, MODE>(p, b, h, hr, lo, nrows, proc * RB, NPROC * RB, sub, S.u.rows, pages, S.ltok,
-                                S.lpg, m, l, o);
+  accumulate_rows<G, FP8, MODE, RB, RET>(p, b, h, hr, lo, nrows, proc * RB, NPROC * RB, sub, S.u.rows, pages,
+                                         S.ltok, S.lpg, lds_logits, m, l, o);
   combine_wave_procs<G>(m, l, o);
   __syncthreads();                               // rows / pages no longer read; wo aliases rows
   if (lane < 16) {
@@ -548,7 +555,7 @@ __device__ __forceinline__ void select_tiles(const DecodeParams& p, TailLds& S, 
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) {
     const int t = w + k * nwg;
-    ts[k] = TileSel{false, 0u, 0ull, 0u, false, 0u};
+    ts[k] = TileSel{false, 0u, 0ull, 0u, false, 0u, 0ull};
     if (t >= p.tail_ntiles) {
       tl[k] = Tile{-1, 0, 0, 0, 0, 0, 0};
       continue;
@@ -645,7 +652,9 @@ __device__ __forceinline__ void select_tiles(const DecodeParams& p, TailLds& S, 
       }
     }
     // the whole sequence kept: no threshold to find
-    if (N == 0 || (bymass ? !(p.top_p[tl[k].b] < 1.0f) : max(p.top_k[tl[k].b], 1) >= N)) {
+    bool all;
+    ts[k].target = sel_target(p, tl[k].b, N, all);
+    if (all) {
       ts[k].done = true;
       ts[k].tstar = 0u;
     }
@@ -721,8 +730,11 @@ __global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
 constexpr int FPW = TAIL_TILE / BS / TW;     // pages per wave: 128
 static_assert(FPW == 4 * TPT, "a lane owns one token of every 4-page group");
 
+constexpr int FUSED_LOGITS = 2048;          // kept rows whose logits stay in LDS
+constexpr int FUSED_RB = 12;                 // rows per processor per gather batch
+
 template <int MODE>
-__device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, unsigned int* err) {
+__device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f32x4* logits, unsigned int* err) {
   constexpr int G = 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, quad = lane >> 4;
@@ -738,7 +750,10 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, un
     tl[0].N = min(p.seq_lens[tl[0].b], p.Nmax);
     tl[0].lo = tl[0].j * TAIL_TILE;
     tl[0].hi = min(tl[0].N, tl[0].lo + TAIL_TILE);
-    ts[0] = TileSel{false, 0u, 0ull, 0u, false, 0u};
+    ts[0] = TileSel{false, 0u, 0ull, 0u, false, 0u, 0ull};
+    bool all;
+    ts[0].target = sel_target(p, tl[0].b, tl[0].N, all);
+    ts[0].done = all;                           // the whole sequence kept: no threshold to find
   }
   const int b = tl[0].b, hr = tl[0].hr, j = tl[0].j, N = tl[0].N, lo = tl[0].lo, hi = tl[0].hi;
   const int h = p.ret_head[hr];
@@ -822,6 +837,16 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, un
     if (lane == 0) { S.wm[wave][g] = m[g]; S.wl[wave][g] = sm[g]; }
   }
   __syncthreads();
+  // this tile's share of the head's radix bins back to zero (device-coherent
+  // stores, acknowledged before the arrival that every flush waits for)
+  {
+    constexpr int NBIN = HIST_BINS + P2_BINS + P3_BINS;
+    for (int e = j * TT + tid; e < NBIN; e += p.tail_tph * TT) {
+      unsigned long long* bin = e < HIST_BINS ? &st->mass[e]
+                              : (e < HIST_BINS + P2_BINS ? &st->mass2[e - HIST_BINS] : &st->mass3[e - HIST_BINS - P2_BINS]);
+      __hip_atomic_store(bin, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   float* spf = reinterpret_cast<float*>(p.spart) + hrow * p.n_score_chunks * G * 2;   // [tile][g] (max, sum)
   if (tid < G) {
     float mm = S.wm[0][tid], ss = S.wl[0][tid];
@@ -867,10 +892,6 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, un
       if (p.scores_out) *reinterpret_cast<f32x4*>(sc + (size_t)i * G) = (f32x4){x[u][0], x[u][1], x[u][2], x[u][3]};
     }
   }
-  if (N == 0 || (bymass ? !(p.top_p[b] < 1.0f) : max(p.top_k[b], 1) >= N)) {
-    ts[0].done = true;                           // the whole sequence kept
-    ts[0].tstar = 0u;
-  }
 
   // ---- radix passes (the arrival counter already holds the exchange) ----
   const unsigned int base = (unsigned int)p.tail_tph;
@@ -881,31 +902,42 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, un
   tie_keep<1, true>(p, S, tl, av, ts, keepm, err);
   const unsigned int keep = keepm[0];
 
-  // ---- kept tokens' scores out (the attention's logits), then compaction ----
-  if (!p.scores_out) {
-#pragma unroll
-    for (int u = 0; u < TPT; ++u)
-      if ((keep >> u) & 1u) {
-        const int i = lo + wave * (TPT * 64) + u * 64 + lane;
-        *reinterpret_cast<f32x4*>(sc + (size_t)i * G) = (f32x4){x[u][0], x[u][1], x[u][2], x[u][3]};
-      }
-  }
-  wait_memory_ops();
+  // ---- ordered compaction; the kept tokens' scores (the attention's logits)
+  // go to LDS next to the row list, or to the scores buffer if too many ----
+  count_flags<true>(S, keep);
   __syncthreads();
-  const int nrows = compact_rows<true>(S, keep);
+  const int nrows = (int)scan_cnt(S);
+  const bool lds = nrows <= FUSED_LOGITS;
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const unsigned long long bal = __ballot((keep >> u) & 1u);
+    if ((keep >> u) & 1u) {
+      const int slot = S.cnt[cnt_idx<true>(u, wave)] + lane_rank(bal);
+      const int off = slot_pos<true>(u, tid);
+      S.u.rows[slot] = (unsigned short)off;
+      const f32x4 v = (f32x4){x[u][0], x[u][1], x[u][2], x[u][3]};
+      if (lds) logits[slot] = v;
+      else if (!p.scores_out) *reinterpret_cast<f32x4*>(sc + (size_t)(lo + off) * G) = v;
+    }
+  }
+  if (!lds) wait_memory_ops();
   if (tid == 0 && nrows > 0) atomicAdd(&st->nsel, (unsigned int)nrows);
   __syncthreads();
-  if (nrows > 0) attend_rows<G, false, MODE>(p, S, b, h, hr, j, lo, nrows, S.pages[0]);
-  else empty_split<G>(p, b, h, j);
+  if (nrows > 0)
+    attend_rows<G, false, MODE, FUSED_RB, true>(p, S, b, h, hr, j, lo, nrows, S.pages[0],
+                                                lds ? reinterpret_cast<const float*>(logits) : nullptr);
+  else
+    empty_split<G>(p, b, h, j);
   finish_split<G>(p, S, b, h, hr);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
   __shared__ TailLds S;
+  __shared__ f32x4 logits[FUSED_LOGITS];
   const int w = blockIdx.x, nwg = gridDim.x;
   unsigned int* err = p.tail_sync;
-  if (w < p.tail_ntiles) fused_tile<MODE>(p, S, err);
+  if (w < p.tail_ntiles) fused_tile<MODE>(p, S, logits, err);
   if constexpr (MODE != 1) {
     // local-head chunks: item i goes to workgroup (ntiles + i) mod nwg
     const int nitems = p.B * p.nL * p.ncL;
@@ -922,12 +954,16 @@ __global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
   }
 }
 
-// Selection state and split counters back to zero before a fused launch.
+// Counters back to zero before a fused launch (the radix bins are cleared by
+// the tiles themselves before their first hand-off).
 __global__ __launch_bounds__(256) void reset_state_kernel(DecodeParams p) {
-  unsigned int* w = reinterpret_cast<unsigned int*>(p.sel + blockIdx.x);
-  for (int i = threadIdx.x; i < SELSTATE_WORDS; i += 256) w[i] = 0u;
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < 1 + p.B * p.Hkv; i += 256) p.tail_sync[i] = 0u;
+  for (int i = threadIdx.x; i < p.B * p.nR; i += 256) {
+    SelState* st = p.sel + i;
+    st->arrive = 0u;
+    st->tie_arrive = 0u;
+    st->nsel = 0u;
+  }
+  for (int i = threadIdx.x; i < 1 + p.B * p.Hkv; i += 256) p.tail_sync[i] = 0u;
 }
 
 template <int G, bool FP8, int MODE>
@@ -1032,7 +1068,7 @@ hipError_t launch_fused(const DecodeParams& p, int nwg, bool cooperative, hipStr
                         hipEvent_t e1) {
   void* fn = pick_fused(p);
   if (fn == nullptr || nwg < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(reset_state_kernel, dim3(p.B * p.nR), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(reset_state_kernel, dim3(1), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_single(fn, p, nwg, cooperative, s, e0, e1);
