@@ -59,9 +59,10 @@ def parse_args(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cold-iters", type=int, default=20,
                     help="extra steps each preceded by a 1 GiB cache flush (0 = skip)")
-    ap.add_argument("--launch", choices=["auto", "multi", "cooperative"], default="auto",
-                    help="auto: one launch after scoring (grid sized to the device); cooperative: the "
-                         "same as a cooperative launch; multi: a kernel per stage")
+    ap.add_argument("--launch", choices=["auto", "single", "multi", "cooperative"], default="auto",
+                    help="auto: the library's default; single: one launch after (or with) the scoring "
+                         "scan, grid sized to the device; cooperative: the same as a cooperative launch; "
+                         "multi: a kernel per stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -192,6 +193,7 @@ def main(argv=None) -> int:
           file=sys.stderr, flush=True)
     setup = DecodeSetup(wl, keep_host=want_cpu)
     setup.ctx.set_launch_mode({"auto": hws.HWS_LAUNCH_AUTO, "multi": hws.HWS_LAUNCH_MULTI,
+                               "single": hws.HWS_LAUNCH_SINGLE,
                                "cooperative": hws.HWS_LAUNCH_COOPERATIVE}[args.launch])
     print("[bench] cache filled; warming up", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -416,6 +416,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   // grid the device holds at once; otherwise one kernel per stage.
   const bool coop = ctx->launch_mode == HWS_LAUNCH_COOPERATIVE;
   const bool single = ctx->nR > 0 && ctx->launch_mode != HWS_LAUNCH_MULTI;
+  const bool tail_ok = ctx->launch_mode == HWS_LAUNCH_SINGLE || coop;   // AUTO: fused launch only
   const int nwf = single ? fused_grid(p, coop) : 0;
   if (nwf > 0 && L.tail_ntiles <= nwf) {
     p.n_score_chunks = L.tail_tph;                 // one (max, sum) partial per tile
@@ -424,7 +425,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
     if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
     return HWS_OK;
   }
-  const int nwg = single ? tail_grid(p, coop) : 0;
+  const int nwg = (single && tail_ok) ? tail_grid(p, coop) : 0;
   const bool tail = nwg > 0 && (long long)L.tail_ntiles <= (long long)TAIL_MAXT * nwg;
   if (tail) {
     const StageEv es = stage_events(ctx, 0);
@@ -454,7 +455,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
 
 hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode) {
   if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
-  if (mode != HWS_LAUNCH_AUTO && mode != HWS_LAUNCH_MULTI && mode != HWS_LAUNCH_COOPERATIVE)
+  if (mode != HWS_LAUNCH_AUTO && mode != HWS_LAUNCH_MULTI && mode != HWS_LAUNCH_COOPERATIVE &&
+      mode != HWS_LAUNCH_SINGLE)
     return fail(ctx, HWS_ERR_INVALID_ARG, "launch mode = %d", mode);
   ctx->launch_mode = mode;
   return HWS_OK;

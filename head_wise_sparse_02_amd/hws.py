@@ -26,7 +26,7 @@ HWS_KV_BF16, HWS_KV_FP8_E4M3 = 0, 1
 HWS_HEAD_LOCAL, HWS_HEAD_RETRIEVAL = 0, 1
 HWS_SELECT_TOP_P, HWS_SELECT_TOP_K = 0, 1
 HWS_SCORE_INDEX, HWS_SCORE_FULL = 0, 1
-HWS_LAUNCH_AUTO, HWS_LAUNCH_MULTI, HWS_LAUNCH_COOPERATIVE = 0, 1, 2
+HWS_LAUNCH_AUTO, HWS_LAUNCH_MULTI, HWS_LAUNCH_COOPERATIVE, HWS_LAUNCH_SINGLE = 0, 1, 2, 3
 
 EXPORTED = (
     "hws_abi_version", "hws_status_string", "hws_last_error", "hws_create", "hws_destroy",
@@ -214,9 +214,10 @@ class Context:
 
     # -- timing ------------------------------------------------------------------
     def set_launch_mode(self, mode: int):
-        """HWS_LAUNCH_AUTO (one launch after scoring, grid sized to the
-        device), HWS_LAUNCH_COOPERATIVE (the same as a cooperative launch) or
-        HWS_LAUNCH_MULTI (one kernel per stage)."""
+        """HWS_LAUNCH_AUTO (default), HWS_LAUNCH_SINGLE (one launch after or
+        with the scoring scan, grid sized to the device), HWS_LAUNCH_COOPERATIVE
+        (the same as a cooperative launch) or HWS_LAUNCH_MULTI (one kernel per
+        stage)."""
         self._check(self._L.hws_set_launch_mode(self.handle, int(mode)), "hws_set_launch_mode")
 
     def profile_enable(self, enable: bool = True):

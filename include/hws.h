@@ -72,7 +72,7 @@ enum { HWS_SELECT_TOP_P = 0, HWS_SELECT_TOP_K = 1 };
 /* Selection score: INDEX = 16-dim pre-RoPE index ([RTPurbo] Methodology §2);
  * FULL = full-dim q.k, i.e. exact "oracle top-k" ([ICS] §2). */
 enum { HWS_SCORE_INDEX = 0, HWS_SCORE_FULL = 1 };
-enum { HWS_LAUNCH_AUTO = 0, HWS_LAUNCH_MULTI = 1, HWS_LAUNCH_COOPERATIVE = 2 };
+enum { HWS_LAUNCH_AUTO = 0, HWS_LAUNCH_MULTI = 1, HWS_LAUNCH_COOPERATIVE = 2, HWS_LAUNCH_SINGLE = 3 };
 
 typedef struct hws_ctx hws_ctx; /* opaque host object, owned by the library */
 
@@ -201,24 +201,32 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
 /* (FULL scoring requires a bf16 cache: HWS_ERR_UNSUPPORTED otherwise.) */
 
 /* Launch shape of hws_decode.
- *  HWS_LAUNCH_AUTO (the default): after the scoring scan, selection,
- *    attention and merge run as ONE launch whose workgroups hand results to
- *    each other through device memory and wait for each other, with the grid
- *    sized to what the device holds at once (compute units x occupancy).  It
- *    is an ordinary dispatch: it relies on this process having the device's
- *    compute units (no CU masking); a kernel running concurrently on another
- *    stream only delays it.  Every wait is bounded: a launch that cannot make
- *    progress ends after about a second per wait with NaN outputs.
- *  HWS_LAUNCH_COOPERATIVE: the same single launch as a cooperative launch,
- *    so the runtime guarantees that all its workgroups are resident (costs a
- *    few tens of microseconds of launch latency per call).
- *  HWS_LAUNCH_MULTI: one kernel per stage, no waits between workgroups.
- * The single launch is used when the device supports it and every retrieval
- * tile (16384 positions of one sequence and head) fits the grid at two tiles
- * per workgroup; otherwise the decode falls back to HWS_LAUNCH_MULTI.  All
- * shapes select the same token sets; outputs differ only by the fp32 rounding
- * order of the attention splits.  Returns HWS_ERR_INVALID_ARG for an unknown
- * mode. */
+ *  HWS_LAUNCH_MULTI: one kernel per stage (score, select passes, attend,
+ *    merge); no workgroup waits for another.
+ *  HWS_LAUNCH_SINGLE: everything after the scoring scan runs as ONE launch
+ *    whose workgroups hand results to each other through device memory and
+ *    wait for each other (bounded spins); for full-dim scores with G = 4, a
+ *    bf16 cache and RoPE off, the scan itself runs inside it too, one
+ *    16384-position tile per workgroup with the tile's scores in registers.
+ *    The grid is sized to what the device holds at once (compute units x
+ *    occupancy) and launched as an ordinary dispatch: it relies on this
+ *    process having the device's compute units (no CU masking); a kernel
+ *    running concurrently on another stream only delays it.  A launch that
+ *    cannot make progress ends after about a second per wait with NaN
+ *    outputs.  Used when the device supports it and the tiles fit the grid
+ *    (one tile per workgroup with the scan inside, else two); otherwise the
+ *    decode runs as HWS_LAUNCH_MULTI.
+ *  HWS_LAUNCH_COOPERATIVE: HWS_LAUNCH_SINGLE as a cooperative launch, so the
+ *    runtime guarantees that all workgroups are resident (costs a few tens of
+ *    microseconds of launch latency per call).
+ *  HWS_LAUNCH_AUTO (the default): HWS_LAUNCH_SINGLE where the scan runs
+ *    inside the launch (it is then faster), else HWS_LAUNCH_MULTI.  The
+ *    single launch without the scan gathers each tile's kept rows in one
+ *    workgroup, which loses to the per-stage kernels when many rows are kept
+ *    or many local-head chunks run beside it.
+ * All shapes select the same token sets; outputs differ only by the fp32
+ * rounding order of the attention splits.  Returns HWS_ERR_INVALID_ARG for an
+ * unknown mode. */
 hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode);
 
 /* Optional per-stage timing with HIP events on the decode stream.

@@ -124,8 +124,9 @@ def test_launch_mode_values():
     c = _ctx()
     c.set_launch_mode(hws.HWS_LAUNCH_MULTI)
     c.set_launch_mode(hws.HWS_LAUNCH_COOPERATIVE)
+    c.set_launch_mode(hws.HWS_LAUNCH_SINGLE)
     c.set_launch_mode(hws.HWS_LAUNCH_AUTO)
-    for bad in (-1, 3, 99):
+    for bad in (-1, 4, 99):
         with pytest.raises(hws.HwsError) as e:
             c.set_launch_mode(bad)
         assert e.value.status == hws.HWS_ERR_INVALID_ARG

@@ -16,8 +16,9 @@ from gpu_check import check_decode
 
 pytestmark = pytest.mark.gpu
 
-AUTO, MULTI, COOP = hws.HWS_LAUNCH_AUTO, hws.HWS_LAUNCH_MULTI, hws.HWS_LAUNCH_COOPERATIVE
-BOTH = pytest.mark.parametrize("launch", [AUTO, MULTI], ids=["single", "multi"])
+AUTO, MULTI, COOP, SINGLE = (hws.HWS_LAUNCH_AUTO, hws.HWS_LAUNCH_MULTI, hws.HWS_LAUNCH_COOPERATIVE,
+                              hws.HWS_LAUNCH_SINGLE)
+BOTH = pytest.mark.parametrize("launch", [SINGLE, MULTI], ids=["single", "multi"])
 
 
 def _run(wl, pairs=None, sequences=None, verbose=True, launch=AUTO, **kw):
@@ -138,12 +139,19 @@ def test_single_launch_matches_multi(cfg, kw):
     that ran (its profile stage is recorded)."""
     wl = W.make_workload(cfg, **kw)
     st = DecodeSetup(wl)
-    single = "fused" if (wl.score_mode == "full" and wl.G == 4 and not wl.rope_theta) else "tail"
+    fused = wl.score_mode == "full" and wl.G == 4 and not wl.rope_theta
+    single = "fused" if fused else "tail"
     st.ctx.profile_enable(True)
-    st.ctx.set_launch_mode(AUTO)
+    st.ctx.set_launch_mode(AUTO)                      # fused launch where it applies, else per stage
+    auto = st.decode(debug=True)
+    prof = st.ctx.profile_read()
+    assert prof["fused" if fused else "select"][1] == 1, prof
+    st.ctx.set_launch_mode(SINGLE)
     a = st.decode(debug=True)
     prof = st.ctx.profile_read()
     assert prof[single][1] == 1 and prof["select"][1] == 0, prof
+    for key in ("out", "lse", "sel_counts", "sel_idx", "scores"):
+        np.testing.assert_array_equal(auto[key], (a if fused else auto)[key])
     st.ctx.set_launch_mode(MULTI)
     m = st.decode(debug=True)
     prof = st.ctx.profile_read()
