@@ -222,6 +222,8 @@ __device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, co
     any = true;
     SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
     unsigned long long* gh = PASS == 1 ? st->mass : (PASS == 2 ? st->mass2 : st->mass3);
+    // LDS bins: 64-bit fixed-point mass (top-p) or 32-bit counts (top-k)
+    unsigned int* h32 = reinterpret_cast<unsigned int*>(S.u.hist);
     for (int i = tid; i < NB; i += TT) S.u.hist[i] = 0ull;
     __syncthreads();
     const unsigned int key = ts[k].key;
@@ -230,12 +232,13 @@ __device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, co
       const unsigned int bits = __float_as_uint(av[k][u]);   // sign bit: no token
       if ((bits >> KEY_SHIFT) == key) {
         const unsigned int bin = (bits >> SHIFT) & (NB - 1);
-        atomicAdd(&S.u.hist[bin], bymass ? mass_fixed(av[k][u]) : 1ull);
+        if (bymass) atomicAdd(&S.u.hist[bin], mass_fixed(av[k][u]));
+        else atomicAdd(&h32[bin], 1u);
       }
     }
     __syncthreads();
     for (int i = tid; i < NB; i += TT) {
-      const unsigned long long v = S.u.hist[i];
+      const unsigned long long v = bymass ? S.u.hist[i] : (unsigned long long)h32[i];
       if (v != 0ull) atomicAdd(&gh[i], v);
     }
     __syncthreads();
@@ -908,11 +911,15 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   __syncthreads();
   const int nrows = (int)scan_cnt(S);
   const bool lds = nrows <= FUSED_LOGITS;
+  // this wave's TPT offsets are consecutive: read them all before any write
+  unsigned int base_off[TPT];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) base_off[u] = S.cnt[cnt_idx<true>(u, wave)];
 #pragma unroll
   for (int u = 0; u < TPT; ++u) {
     const unsigned long long bal = __ballot((keep >> u) & 1u);
     if ((keep >> u) & 1u) {
-      const int slot = S.cnt[cnt_idx<true>(u, wave)] + lane_rank(bal);
+      const int slot = base_off[u] + lane_rank(bal);
       const int off = slot_pos<true>(u, tid);
       S.u.rows[slot] = (unsigned short)off;
       const f32x4 v = (f32x4){x[u][0], x[u][1], x[u][2], x[u][3]};
