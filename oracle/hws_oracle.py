@@ -184,6 +184,14 @@ def full_logits(q_rot, k_rot, attn_scale: float):
     return s, attn_scale * s
 
 
+def head_probs(logits) -> np.ndarray:
+    """pi_{g,i} = softmax_i(l_g) for each query head g (rows of the result)."""
+    l = np.asarray(logits, dtype=np.float64)
+    m = l.max(axis=1, keepdims=True)
+    e = np.exp(l - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
 def group_aggregate(logits) -> np.ndarray:
     """a_i = mean over the group's query heads of softmax_i(l_g).
 
@@ -192,11 +200,7 @@ def group_aggregate(logits) -> np.ndarray:
     the GQA group, [AoH] Methodology §4), which keeps sum(a) = 1 so that a
     cumulative-mass threshold keeps its meaning.
     """
-    l = np.asarray(logits, dtype=np.float64)
-    m = l.max(axis=1, keepdims=True)
-    e = np.exp(l - m)
-    pi = e / e.sum(axis=1, keepdims=True)
-    return pi.mean(axis=0)
+    return head_probs(logits).mean(axis=0)
 
 
 def _desc_order(a) -> np.ndarray:
@@ -286,7 +290,8 @@ def decode_head_ref(q_pre, k_pre, k_store, v_store, *, kind: str, proj=None,
                     score_mode: str = "index", select_mode: str = "top_p",
                     top_p: float = 0.9, top_k: int = 0, n_sink: int = 0,
                     window: int = 0, attn_scale: float, index_scale: float = 1.0,
-                    rope_theta: float = 0.0, fixed_set=None, with_full_mass: bool = False):
+                    rope_theta: float = 0.0, fixed_set=None, with_full_mass: bool = False,
+                    scope: str = "kv"):
     """Decode one step for one (sequence, KV head).
 
     q_pre [G, d] pre-RoPE queries; k_pre [N, d] pre-RoPE keys (the index
@@ -298,12 +303,45 @@ def decode_head_ref(q_pre, k_pre, k_store, v_store, *, kind: str, proj=None,
     Returns a dict: o [G, d] float32, lse [G] float32, o64 / lse64 float64,
     S (ascending), t (threshold or None), scores (raw s, retrieval only),
     a (aggregate), index_mass, full_mass.
+
+    scope "query" (retrieval heads): every query head g keeps its own set by
+    the same rule applied to its own distribution softmax(l_g) and attends over
+    that set only ([ICS] §2: the sparsity pattern differs per token, per query
+    and per head; [RTPurbo] Methodology §3: the budget adapts per query).  The
+    result then also holds S_heads, t_heads, a_heads and index_mass_heads (one
+    entry per query head); S is their union.  ``fixed_set`` is then a list of
+    G sets.
     """
     q_pre = np.asarray(q_pre, dtype=np.float64)
     n = k_store.shape[0]
     pos_q = n - 1
     q_rot = rope(q_pre, np.full(q_pre.shape[0], pos_q), rope_theta)
     out = {"t": None, "scores": None, "a": None, "index_mass": None}
+    if kind == "retrieval" and scope == "query":
+        if score_mode == "index":
+            s, l = index_logits(q_pre, k_pre, proj, index_scale)
+        else:
+            s, l = full_logits(q_rot, k_store, attn_scale)
+        pi = head_probs(l)
+        sets, ts, o, lse = [], [], [], []
+        for g in range(q_pre.shape[0]):
+            if fixed_set is not None:
+                S_g, t_g = np.asarray(fixed_set[g], dtype=np.int64), None
+            elif select_mode == "top_p":
+                S_g, t_g = select_top_p(pi[g], top_p)
+            else:
+                S_g, t_g = select_top_k(pi[g], top_k)
+            o_g, lse_g = sparse_attend(q_rot[g:g + 1], k_store[S_g], v_store[S_g], attn_scale)
+            sets.append(S_g)
+            ts.append(t_g)
+            o.append(o_g[0])
+            lse.append(lse_g[0])
+        o, lse = np.stack(o), np.asarray(lse)
+        out.update(scores=s, a=None, a_heads=pi, S_heads=sets, t_heads=ts,
+                   index_mass_heads=[float(pi[g][sets[g]].sum()) for g in range(len(sets))],
+                   S=np.unique(np.concatenate(sets)), full_mass=None,
+                   o64=o, lse64=lse, o=o.astype(np.float32), lse=lse.astype(np.float32))
+        return out
     if kind == "retrieval":
         if score_mode == "index":
             s, l = index_logits(q_pre, k_pre, proj, index_scale)
@@ -336,7 +374,7 @@ def decode_head_ref(q_pre, k_pre, k_store, v_store, *, kind: str, proj=None,
 def decode_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, proj=None, score_mode="index",
                         select_mode="top_p", top_p=0.9, top_k=0, n_sink=0, window=0,
                         attn_scale, index_scale=1.0, rope_theta=0.0, kv_fp8=False,
-                        segments=None, heads=None, fixed_sets=None, with_full_mass=False):
+                        segments=None, heads=None, fixed_sets=None, with_full_mass=False, scope="kv"):
     """Decode one step of one sequence for the KV heads in ``heads``.
 
     q_pre [Hq, d]; k_pre, v_in [N, Hkv, d] as appended (bf16-exact values);
@@ -363,5 +401,5 @@ def decode_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, proj=None, score_mode
             window=window, attn_scale=attn_scale, index_scale=index_scale,
             rope_theta=rope_theta,
             fixed_set=None if fixed_sets is None else fixed_sets.get(h),
-            with_full_mass=with_full_mass)
+            with_full_mass=with_full_mass, scope=scope)
     return res

@@ -370,3 +370,76 @@ def test_fp8_path_uses_dequantised_rows():
     kd = O.fp8_store_rows(k[:, 0].astype(np.float64), [(0, 40)])[2]
     vd = O.fp8_store_rows(v[:, 0].astype(np.float64), [(0, 40)])[2]
     np.testing.assert_allclose(res[0]["o64"], _sdpa(q[:4].astype(np.float64), kd, vd, 0.088), atol=1e-12)
+
+
+# -- per-query-head selection (scope "query") ----------------------------------
+
+ATTN = 1.0 / np.sqrt(128)
+
+
+def _qhead_case(G=4, n=300, seed=41, same_q=False):
+    rng = np.random.default_rng(seed)
+    q = O.bf16_round(rng.standard_normal((1 if same_q else G, 128)) * 1.5)
+    q = np.repeat(q, G, axis=0) if same_q else q
+    k = O.bf16_round(rng.standard_normal((n, 128)))
+    v = O.bf16_round(rng.standard_normal((n, 128)))
+    return q, k, v
+
+
+@pytest.mark.parametrize("select_mode", ["top_p", "top_k"])
+def test_query_scope_with_one_head_is_the_group_set(select_mode):
+    """G = 1: the head's own distribution is the group aggregate."""
+    q, k, v = _qhead_case(G=1)
+    kw = dict(kind="retrieval", score_mode="full", select_mode=select_mode, top_p=0.8, top_k=37,
+              attn_scale=ATTN)
+    a = O.decode_head_ref(q, k, k, v, scope="kv", **kw)
+    b = O.decode_head_ref(q, k, k, v, scope="query", **kw)
+    np.testing.assert_array_equal(a["S"], b["S_heads"][0])
+    np.testing.assert_array_equal(a["o64"], b["o64"])
+
+
+def test_query_scope_identical_heads_share_the_group_set():
+    """All G queries equal: every per-head distribution equals their mean."""
+    q, k, v = _qhead_case(same_q=True)
+    kw = dict(kind="retrieval", score_mode="full", select_mode="top_p", top_p=0.9, attn_scale=ATTN)
+    a = O.decode_head_ref(q, k, k, v, scope="kv", **kw)
+    b = O.decode_head_ref(q, k, k, v, scope="query", **kw)
+    for g in range(4):
+        np.testing.assert_array_equal(b["S_heads"][g], a["S"])
+    np.testing.assert_allclose(b["o64"], a["o64"], rtol=0, atol=1e-12)
+
+
+def test_query_scope_heads_are_independent():
+    """Changing one query head changes no other head's set or output (a group
+    aggregate anywhere would couple them)."""
+    q, k, v = _qhead_case()
+    kw = dict(kind="retrieval", score_mode="full", select_mode="top_p", top_p=0.9, attn_scale=ATTN,
+              scope="query")
+    a = O.decode_head_ref(q, k, k, v, **kw)
+    q2 = q.copy()
+    q2[2] = O.bf16_round(np.random.default_rng(5).standard_normal(128) * 3)
+    b = O.decode_head_ref(q2, k, k, v, **kw)
+    for g in (0, 1, 3):
+        np.testing.assert_array_equal(a["S_heads"][g], b["S_heads"][g])
+        np.testing.assert_array_equal(a["o64"][g], b["o64"][g])
+    assert not np.array_equal(a["S_heads"][2], b["S_heads"][2])
+    np.testing.assert_array_equal(a["S"], np.unique(np.concatenate(a["S_heads"])))
+
+
+def test_query_scope_brute_force_and_dense():
+    """Each head's set is the brute-force minimal top-p subset of its own
+    softmax (tiny N); p = 1 gives dense attention per head (torch SDPA)."""
+    rng = np.random.default_rng(77)
+    n = 9
+    q = O.bf16_round(rng.standard_normal((4, 128)) * 2)
+    k = O.bf16_round(rng.standard_normal((n, 128)))
+    v = O.bf16_round(rng.standard_normal((n, 128)))
+    r = O.decode_head_ref(q, k, k, v, kind="retrieval", score_mode="full", select_mode="top_p",
+                          top_p=0.7, attn_scale=ATTN, scope="query")
+    z = ATTN * (q.astype(np.float64) @ k.astype(np.float64).T)
+    for g in range(4):
+        pi = scipy.special.softmax(z[g])
+        np.testing.assert_array_equal(r["S_heads"][g], np.sort(_brute_top_p(pi, 0.7)))
+    d = O.decode_head_ref(q, k, k, v, kind="retrieval", score_mode="full", select_mode="top_p",
+                          top_p=1.0, attn_scale=ATTN, scope="query")
+    np.testing.assert_allclose(d["o64"], _sdpa(q, k, v, ATTN), rtol=0, atol=1e-6)
