@@ -63,6 +63,8 @@ def parse_args(argv=None):
                     help="auto: the library's default; single: one launch after (or with) the scoring "
                          "scan, grid sized to the device; cooperative: the same as a cooperative launch; "
                          "multi: a kernel per stage")
+    ap.add_argument("--scope", choices=["kv", "query"], default="kv",
+                    help="one token set per KV head (kv) or per query head (query)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -187,7 +189,7 @@ def main(argv=None) -> int:
     from head_wise_sparse_02_amd import workloads as W
     from head_wise_sparse_02_amd.runner import DecodeSetup
 
-    wl = W.make_workload(args.config, seed=args.seed)
+    wl = W.make_workload(args.config, seed=args.seed, select_scope=args.scope)
     want_cpu = not args.no_cpu_baseline
     print(f"[bench] building workload {args.config}: {W.CONFIG_NAMES[args.config]}",
           file=sys.stderr, flush=True)
@@ -226,6 +228,19 @@ def main(argv=None) -> int:
     ctx.profile_enable(False)
 
     sel_counts = setup.sel_counts.cpu().numpy()
+    if wl.select_scope == "query":
+        # bytes follow the union of a group's per-query-head sets (one untimed debug call)
+        dbg = setup.decode(debug=True)
+        kv_counts = np.zeros((wl.B, wl.Hkv), np.int64)
+        for b in range(wl.B):
+            for h in range(wl.Hkv):
+                if h in wl.retrieval_heads:
+                    hr = wl.retrieval_heads.index(h)
+                    sets = [dbg["sel_idx"][b, hr, g][:dbg["sel_counts"][b, h * wl.G + g]] for g in range(wl.G)]
+                    kv_counts[b, h] = np.unique(np.concatenate(sets)).size
+                else:
+                    kv_counts[b, h] = sel_counts[b, h * wl.G]
+        sel_counts = kv_counts
     by = algorithmic_bytes(wl, sel_counts)
     stages = {}
     for name, (ms, calls) in prof.items():
@@ -275,7 +290,8 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "description": W.CONFIG_NAMES[wl.cfg], "batch": wl.B,
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
                    "context": int(max(wl.seq_lens)), "score_mode": wl.score_mode,
-                   "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype, "launch": args.launch},
+                   "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype, "launch": args.launch,
+                   "select_scope": wl.select_scope},
         "step_bytes": by["total"], "step_GBps": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_GBS, 4),
         "selected_per_head_mean": round(float(sel_counts[:, [h for h in wl.retrieval_heads]].mean()), 1)

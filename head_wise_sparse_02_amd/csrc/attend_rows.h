@@ -28,12 +28,14 @@ struct AttRB {
 // RET: the rows are known to be a retrieval head's (no K path compiled in).
 // lds_logits (full-dim scores only): the scores of row r at lds_logits[r*G];
 // null reads them from the scores buffer at the row's position.
+// row_mask (retrieval rows, one set per query head): bit g of row_mask[r] says
+// whether query head g keeps row r; null means every head keeps every row.
 template <int G, bool FP8, int MODE, int RB, bool RET = false>
 __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, int h, int hr, int lo, int nrows,
                                                 int r_begin, int r_step, int sub, const unsigned short* rows,
                                                 const int* pages, const int* ltok, const int* lpg,
                                                 const float* lds_logits, float (&m)[G], float (&l)[G],
-                                                float (&o)[G][8]) {
+                                                float (&o)[G][8], const unsigned char* row_mask = nullptr) {
   static_assert(!RET || MODE != 0, "retrieval rows read K only in index mode");
   constexpr bool NEED_K = MODE != 1 && !RET;
   const bool is_ret = RET || hr >= 0;
@@ -161,6 +163,15 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
     for (int u = 0; u < RB; ++u) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) vv[u][j] = ok[u] ? (FP8 ? vv[u][j] * vs[u] : vv[u][j]) : 0.f;
+    }
+    if (is_ret && row_mask != nullptr) {         // heads that do not keep a row skip it
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const unsigned int mk = row_mask[min(r0 + u, nrows - 1)];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (!((mk >> g) & 1u)) z[u][g] = NEG_INF;
+      }
     }
 
     // one rescale per batch

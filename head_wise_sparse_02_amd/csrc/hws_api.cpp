@@ -91,7 +91,8 @@ void rebuild_slots(hws_ctx* c) {
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode) {
+// GS: selection states per retrieval head (1, or G with one set per query head).
+Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode, int GS) {
   Layout L{};
   const int G = c->G;
   // The G=4 full-dim scan (bf16 queries, RoPE off) uses longer chunks.
@@ -109,9 +110,9 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode)
   size_t off = 0;
   L.scores = off;   off = align_up(off + nRb * Nmax * G * sizeof(float));
   L.Nagg = (Nmax + 63) & ~63;
-  L.agg = off;      off = align_up(off + nRb * L.Nagg * sizeof(float));
+  L.agg = off;      off = align_up(off + nRb * GS * L.Nagg * sizeof(float));
   L.spart = off;    off = align_up(off + nRb * L.n_score_chunks * G * sizeof(float2));
-  L.sel = off;      off = align_up(off + nRb * sizeof(SelState));
+  L.sel = off;      off = align_up(off + nRb * GS * sizeof(SelState));
   const size_t nsp = (size_t)B * c->cfg.num_kv_heads * L.max_splits * G;
   L.apart_ml = off; off = align_up(off + nsp * sizeof(float2));
   L.apart_o = off;  off = align_up(off + nsp * D * sizeof(float));
@@ -274,12 +275,14 @@ hws_status hws_bind(hws_ctx* ctx, const hws_buffers* buf) {
 }
 
 hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq_len, int32_t score_mode,
-                              size_t* bytes) {
+                              int32_t select_scope, size_t* bytes) {
   if (ctx == nullptr || bytes == nullptr) return HWS_ERR_INVALID_ARG;
   if (batch < 1 || max_seq_len < 1) return HWS_ERR_INVALID_ARG;
   if (score_mode != HWS_SCORE_INDEX && score_mode != HWS_SCORE_FULL) return HWS_ERR_INVALID_ARG;
+  if (select_scope != HWS_SCOPE_KV_HEAD && select_scope != HWS_SCOPE_QUERY_HEAD) return HWS_ERR_INVALID_ARG;
   if ((long long)max_seq_len > (long long)ctx->cfg.max_blocks_per_seq * BS) return HWS_ERR_CAPACITY;
-  *bytes = make_layout(ctx, batch, max_seq_len, ctx->cfg.rope_theta > 0.f, score_mode).total;
+  *bytes = make_layout(ctx, batch, max_seq_len, ctx->cfg.rope_theta > 0.f, score_mode,
+                       select_scope == HWS_SCOPE_QUERY_HEAD ? ctx->G : 1).total;
   return HWS_OK;
 }
 
@@ -331,6 +334,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
     return fail(ctx, HWS_ERR_INVALID_ARG, "select_mode = %d", a->select_mode);
   if (a->score_mode != HWS_SCORE_INDEX && a->score_mode != HWS_SCORE_FULL)
     return fail(ctx, HWS_ERR_INVALID_ARG, "score_mode = %d", a->score_mode);
+  if (a->select_scope != HWS_SCOPE_KV_HEAD && a->select_scope != HWS_SCOPE_QUERY_HEAD)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "select_scope = %d", a->select_scope);
   if (a->q == nullptr || a->block_tables == nullptr || a->seq_lens == nullptr || a->out == nullptr)
     return fail(ctx, HWS_ERR_INVALID_ARG, "null device pointer (q, block_tables, seq_lens or out)");
   if (ctx->nR > 0) {
@@ -345,7 +350,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   if (ctx->nR > 0 && a->score_mode == HWS_SCORE_FULL && c.kv_dtype != HWS_KV_BF16)
     return fail(ctx, HWS_ERR_UNSUPPORTED, "full-dim scoring needs a bf16 cache");
   const bool rope = c.rope_theta > 0.f;
-  const Layout L = make_layout(ctx, a->batch, a->max_seq_len, rope, a->score_mode);
+  const int GS = a->select_scope == HWS_SCOPE_QUERY_HEAD ? ctx->G : 1;
+  const Layout L = make_layout(ctx, a->batch, a->max_seq_len, rope, a->score_mode, GS);
   if (a->workspace == nullptr || a->workspace_bytes < L.total)
     return fail(ctx, HWS_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, L.total);
 
@@ -355,6 +361,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.Hq = c.num_q_heads;
   p.Hkv = c.num_kv_heads;
   p.G = ctx->G;
+  p.GS = GS;
   p.nR = ctx->nR;
   p.nL = ctx->nL;
   p.Nmax = a->max_seq_len;
@@ -415,7 +422,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   // per workgroup, for full-dim G = 4 scoring) when every tile fits the
   // grid the device holds at once; otherwise one kernel per stage.
   const bool coop = ctx->launch_mode == HWS_LAUNCH_COOPERATIVE;
-  const bool single = ctx->nR > 0 && ctx->launch_mode != HWS_LAUNCH_MULTI;
+  // (one set per query head runs in the per-stage kernels)
+  const bool single = ctx->nR > 0 && ctx->launch_mode != HWS_LAUNCH_MULTI && GS == 1;
   const bool tail_ok = ctx->launch_mode == HWS_LAUNCH_SINGLE || coop;   // AUTO: fused launch only
   const int nwf = single ? fused_grid(p, coop) : 0;
   if (nwf > 0 && L.tail_ntiles <= nwf) {

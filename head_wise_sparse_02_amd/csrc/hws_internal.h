@@ -68,6 +68,7 @@ constexpr int SELSTATE_WORDS = (int)(sizeof(SelState) / 4);
 // Everything a decode kernel needs, passed by value.
 struct DecodeParams {
   int B, Hq, Hkv, G, nR, nL, Nmax, max_blocks, num_blocks;
+  int GS;                       // selection states per retrieval head: 1, or G (one per query head)
   int Nagg;                     // row stride of agg (Nmax rounded up to 64)
   int select_mode, score_mode;
   int n_sink, window;
@@ -86,9 +87,9 @@ struct DecodeParams {
   const float* proj;
   float* scores;                // [B][nR][Nmax][G]
   int scores_out;               // the caller asked for every score (else only kept ones may be written)
-  float* agg;                   // [B][nR][Nagg]
+  float* agg;                   // [B][nR][GS][Nagg]
   float2* spart;                // [B][nR][n_score_chunks][G]  (max, sum) in log2 units
-  SelState* sel;                // [B][nR]
+  SelState* sel;                // [B][nR][GS]
   float2* apart_ml;             // [B][Hkv][max_splits][G]  (max, sum)
   float* apart_o;               // [B][Hkv][max_splits][G][D]
   float* qrot;                  // [B][Hq][D] fp32 rotated queries (RoPE on) or null

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   const int* bt = p.block_tables + (size_t)b * p.max_blocks;
 
   __shared__ unsigned short rows_s[ATT_ROWS_MAX];   // retrieval: offset in the chunk
+  __shared__ unsigned char rmask_s[ATT_ROWS_MAX];   // retrieval, one set per query head: head bits
   __shared__ int pages_s[LOCAL_CHUNK];              // retrieval: chunk pages; local: row pages
   __shared__ int ltok_s[LOCAL_CHUNK];               // local: row tokens
   __shared__ unsigned int tmp[8];
@@ -94,47 +95,67 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     lo = split * chunk;
     const int hi = min(N, lo + chunk);
     if (lo < hi) {
-      const SelState* st = p.sel + (size_t)b * p.nR + hr;
-      const unsigned int tstar = st->tstar, flags = st->flags;
-      const float* agg = p.agg + (size_t)(b * p.nR + hr) * p.Nagg;
       const int i0 = lo + tid * per;
-      float av[16];
-      if (i0 + per <= hi) {
-        for (int j = 0; j < per; j += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(agg + i0 + j);
-          av[j] = v.x; av[j + 1] = v.y; av[j + 2] = v.z; av[j + 3] = v.w;
-        }
-      } else {
-        for (int j = 0; j < per; ++j) av[j] = (i0 + j < hi) ? agg[i0 + j] : -1.0f;
-      }
       const int npg = (hi - lo + BS - 1) / BS;
       if (tid < npg) pages_s[tid] = bt[(lo >> 4) + tid];
-      unsigned int gt_mask = 0, eq_mask = 0;
-      for (int j = 0; j < per; ++j) {
-        const unsigned int bits = __float_as_uint(av[j]);
-        if (i0 + j < hi) {
-          if (bits > tstar) gt_mask |= 1u << j;
-          else if (bits == tstar) eq_mask |= 1u << j;
+      // kept by any of the GS sets; with one set per query head, hb holds
+      // each position's head bits (one byte per position, 4 per word)
+      unsigned int keep_any = 0u, hb[4] = {0u, 0u, 0u, 0u};
+      for (int gs = 0; gs < p.GS; ++gs) {
+        const size_t srow = ((size_t)b * p.nR + hr) * p.GS + gs;
+        SelState* st = p.sel + srow;
+        const unsigned int tstar = st->tstar, flags = st->flags;
+        const float* agg = p.agg + srow * p.Nagg;
+        float av[16];
+        if (i0 + per <= hi) {
+          for (int j = 0; j < per; j += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(agg + i0 + j);
+            av[j] = v.x; av[j + 1] = v.y; av[j + 2] = v.z; av[j + 3] = v.w;
+          }
+        } else {
+          for (int j = 0; j < per; ++j) av[j] = (i0 + j < hi) ? agg[i0 + j] : -1.0f;
         }
+        unsigned int gt_mask = 0, eq_mask = 0;
+        for (int j = 0; j < per; ++j) {
+          const unsigned int bits = __float_as_uint(av[j]);
+          if (i0 + j < hi) {
+            if (bits > tstar) gt_mask |= 1u << j;
+            else if (bits == tstar) eq_mask |= 1u << j;
+          }
+        }
+        if (flags & SEL_TIE) {
+          // keep a tie only while its position-ordered rank stays below the quota
+          const unsigned int before = ties_before(agg, lo, tstar, tmp);
+          const unsigned int quota = st->quota;
+          const unsigned int myrank = block_excl_scan256((unsigned int)__popc(eq_mask), tmp) + before;
+          unsigned int r = myrank, keep = 0;
+          for (int j = 0; j < per; ++j)
+            if (eq_mask & (1u << j)) { if (r < quota) keep |= 1u << j; ++r; }
+          eq_mask = keep;
+        }
+        const unsigned int kept = gt_mask | eq_mask;
+        if (p.select_mode == 0) {                  // top-p: |S| summed over chunks
+          block_excl_scan256((unsigned int)__popc(kept), tmp);
+          if (tid == 0 && tmp[4] > 0u) atomicAdd(&st->nsel, tmp[4]);
+          __syncthreads();
+        }
+        if (p.GS > 1) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if ((kept >> j) & 1u) hb[j >> 2] |= (1u << gs) << ((j & 3) * 8);
+        }
+        keep_any |= kept;
       }
-      if (flags & SEL_TIE) {
-        // keep a tie only while its position-ordered rank stays below the quota
-        const unsigned int before = ties_before(agg, lo, tstar, tmp);
-        const unsigned int quota = st->quota;
-        const unsigned int myrank = block_excl_scan256((unsigned int)__popc(eq_mask), tmp) + before;
-        unsigned int r = myrank, keep = 0;
-        for (int j = 0; j < per; ++j)
-          if (eq_mask & (1u << j)) { if (r < quota) keep |= 1u << j; ++r; }
-        eq_mask = keep;
-      }
-      const unsigned int mask = gt_mask | eq_mask;
-      const unsigned int off = block_excl_scan256((unsigned int)__popc(mask), tmp);
+      const unsigned int off = block_excl_scan256((unsigned int)__popc(keep_any), tmp);
       nrows = (int)tmp[4];
-      if (p.select_mode == 0 && tid == 0 && nrows > 0)        // top-p: |S| summed over chunks
-        atomicAdd(&p.sel[(size_t)b * p.nR + hr].nsel, (unsigned int)nrows);
       unsigned int k = off;
-      for (int j = 0; j < per; ++j)
-        if (mask & (1u << j)) rows_s[k++] = (unsigned short)(i0 + j - lo);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < per && (keep_any & (1u << j))) {
+          rows_s[k] = (unsigned short)(i0 + j - lo);
+          rmask_s[k] = (unsigned char)((hb[j >> 2] >> ((j & 3) * 8)) & 0xFFu);
+          ++k;
+        }
       __syncthreads();
     }
   } else if (MODE != 1) {
@@ -162,7 +183,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   float m[G], l[G], o[G][8];
   constexpr int RB = AttRB<G, MODE>::value;
   accumulate_rows<G, FP8, MODE, RB>(p, b, h, hr, lo, nrows, proc * RB, 16 * RB, sub, rows_s, pages_s, ltok_s,
-                                    pages_s, nullptr, m, l, o);
+                                    pages_s, nullptr, m, l, o, p.GS > 1 ? rmask_s : nullptr);
   combine_wave_procs<G>(m, l, o);
   if (lane < 16) {
 #pragma unroll
@@ -232,15 +253,17 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   }
   p.out[((size_t)b * p.Hq + h * G + g) * D + d] = L > 0.f ? O / L : 0.f;
   if (d == 0 && p.lse != nullptr) p.lse[(size_t)b * p.Hq + h * G + g] = (M + log2f(L)) * LN2;
-  if (g == 0 && d == 0 && p.sel_counts != nullptr) {
+  // |S| per KV head, or per query head with one set per query head
+  if ((g == 0 || p.GS > 1) && d == 0 && p.sel_counts != nullptr) {
     int cnt;
     if (hr >= 0) {
-      cnt = (int)p.sel[(size_t)b * p.nR + hr].nsel;
+      cnt = (int)p.sel[((size_t)b * p.nR + hr) * p.GS + (p.GS > 1 ? g : 0)].nsel;
     } else {
       const int L1 = min(p.n_sink, N);
       cnt = L1 + (N - max(L1, N - p.window));
     }
-    p.sel_counts[(size_t)b * p.Hkv + h] = cnt;
+    if (p.GS > 1) p.sel_counts[(size_t)b * p.Hq + h * G + g] = cnt;
+    else p.sel_counts[(size_t)b * p.Hkv + h] = cnt;
   }
 }
 

@@ -17,14 +17,15 @@
 
 namespace hws {
 
-// Zero this chunk's share of the (b, hr) selection state.
+// Zero this chunk's share of the (b, hr) selection states (GS of them).
 __device__ __forceinline__ void zero_state_share(const DecodeParams& p, SelState* st, int b, int hr, int c,
                                                  int nchunks) {
   // the chunks that exist share the work; chunk 0 also runs for an empty sequence
   const int nz = nchunks > 0 ? nchunks : 1;
   if (c >= nz) return;
   unsigned int* w = reinterpret_cast<unsigned int*>(st);
-  for (int i = c * 256 + (int)threadIdx.x; i < SELSTATE_WORDS; i += nz * 256) w[i] = 0u;
+  const int words = SELSTATE_WORDS * p.GS;
+  for (int i = c * 256 + (int)threadIdx.x; i < words; i += nz * 256) w[i] = 0u;
   // split arrival counters of the single-launch tail (and its error word)
   if (p.tail_sync != nullptr && c == 0 && hr == 0) {
     for (int h = threadIdx.x; h < p.Hkv; h += 256) p.tail_sync[1 + b * p.Hkv + h] = 0u;
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int N = min(p.seq_lens[b], p.Nmax);
   const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;  // == p.score_chunk here
-  SelState* st = p.sel + (size_t)b * p.nR + hr;
+  SelState* st = p.sel + ((size_t)b * p.nR + hr) * p.GS;
   zero_state_share(p, st, b, hr, c, nchunks);
   if (c >= nchunks) return;
 
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int N = min(p.seq_lens[b], p.Nmax);
   const int nchunks = (N + SCORE_CHUNK - 1) / SCORE_CHUNK;  // == p.score_chunk here
-  SelState* st = p.sel + (size_t)b * p.nR + hr;
+  SelState* st = p.sel + ((size_t)b * p.nR + hr) * p.GS;
   zero_state_share(p, st, b, hr, c, nchunks);
   if (c >= nchunks) return;
 
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(256) void score_full_g4_kernel(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int N = min(p.seq_lens[b], p.Nmax);
   const int nchunks = (N + CH - 1) / CH;
-  SelState* st = p.sel + (size_t)b * p.nR + hr;
+  SelState* st = p.sel + ((size_t)b * p.nR + hr) * p.GS;
   zero_state_share(p, st, b, hr, c, nchunks);
   if (c >= nchunks) return;
 

@@ -192,12 +192,16 @@ __device__ void flush_hist(SelState* st, const unsigned long long* hm, const uns
 template <int G, bool BYMASS>
 __global__ __launch_bounds__(NT) void select_pass1_kernel(DecodeParams p) {
   constexpr int TB = G <= 4 ? SEL_PER_THREAD : SEL_PER_THREAD / 2;   // tokens per load batch
-  const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
+  // blockIdx.y = hr * GS + gq: one selection state per (retrieval head, query
+  // head gq) with one set per query head, else one per retrieval head (gq = 0)
+  const int c = blockIdx.x, hs = blockIdx.y, b = blockIdx.z;
+  const int hr = hs / p.GS, gq = hs % p.GS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = min(p.seq_lens[b], p.Nmax);
   const int nwg = (N + SEL_CHUNK - 1) / SEL_CHUNK;
   if (c >= nwg) return;
-  SelState* st = p.sel + (size_t)b * p.nR + hr;
+  const size_t srow = (size_t)b * p.nR * p.GS + hs;      // selection row
+  SelState* st = p.sel + srow;
 
   __shared__ unsigned long long hm[BYMASS ? HIST_BINS : 1];
   __shared__ unsigned int hc[BYMASS ? 1 : HIST_BINS];
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(NT) void select_pass1_kernel(DecodeParams p) {
 
   const size_t row = (size_t)(b * p.nR + hr);
   const float* sc = p.scores + row * p.Nmax * G;
-  float* agg = p.agg + row * p.Nagg;
+  float* agg = p.agg + srow * p.Nagg;
   const int base = c * SEL_CHUNK;
 
   // log2-sum-exp2 of query head g = wave, from the scoring partials
@@ -271,9 +275,17 @@ __global__ __launch_bounds__(NT) void select_pass1_kernel(DecodeParams p) {
       const int i = base + (j0 + u) * NT + tid;
       if (i < N) {
         float a = 0.f;
+        if (p.GS == 1) {                 // mean of the group's distributions
 #pragma unroll
-        for (int g = 0; g < G; ++g) a += fast_exp2(x[u][g] * c2 - lse[g]);
-        a *= invG;
+          for (int g = 0; g < G; ++g) a += fast_exp2(x[u][g] * c2 - lse[g]);
+          a *= invG;
+        } else {                         // query head gq's own distribution
+          float xg = x[u][0], lg = lse[0];
+#pragma unroll
+          for (int g = 1; g < G; ++g)
+            if (g == gq) { xg = x[u][g]; lg = lse[g]; }
+          a = fast_exp2(xg * c2 - lg);
+        }
         agg[i] = a;
         const unsigned int bin = (__float_as_uint(a) >> P1_SHIFT) & (HIST_BINS - 1);
         if (BYMASS) atomicAdd(&hm[bin], mass_fixed(a));
@@ -311,12 +323,13 @@ __global__ __launch_bounds__(NT) void select_refine_kernel(DecodeParams p) {
   constexpr int NB = PASS == 2 ? P2_BINS : P3_BINS;
   constexpr int SHIFT = PASS == 2 ? P2_SHIFT : 0;
   constexpr int KEY_SHIFT = PASS == 2 ? P1_SHIFT : P2_SHIFT;   // bits already fixed
-  const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
+  const int c = blockIdx.x, hs = blockIdx.y, b = blockIdx.z;     // hs = hr * GS + gq
   const int tid = threadIdx.x;
   const int N = min(p.seq_lens[b], p.Nmax);
   const int nwg = (N + SEL_CHUNK - 1) / SEL_CHUNK;
   if (c >= nwg) return;
-  SelState* st = p.sel + (size_t)b * p.nR + hr;
+  const size_t srow = (size_t)b * p.nR * p.GS + hs;
+  SelState* st = p.sel + srow;
 
   __shared__ unsigned long long hm[BYMASS ? NB : 1];
   __shared__ unsigned int hc[BYMASS ? 1 : NB];
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(NT) void select_refine_kernel(DecodeParams p) {
   __shared__ int flag_s, bin_s;
   __shared__ unsigned long long above_s;
 
-  const float* agg = p.agg + (size_t)(b * p.nR + hr) * p.Nagg;
+  const float* agg = p.agg + srow * p.Nagg;
   const int base = c * SEL_CHUNK;
   float a[SEL_PER_THREAD];
 #pragma unroll
@@ -407,15 +420,16 @@ __device__ __forceinline__ unsigned int block_rank256(bool f, unsigned int* tmp)
 }
 
 __global__ __launch_bounds__(256) void emit_sel_kernel(DecodeParams p) {
-  const int hr = blockIdx.x, b = blockIdx.y;
+  const int hs = blockIdx.x, b = blockIdx.y;      // hs = hr * GS + gq
   const int tid = threadIdx.x;
   const int N = min(p.seq_lens[b], p.Nmax);
-  const SelState* st = p.sel + (size_t)b * p.nR + hr;
+  const size_t srow = (size_t)b * p.nR * p.GS + hs;
+  const SelState* st = p.sel + srow;
   const unsigned int tstar = st->tstar;
   const bool tie = (st->flags & SEL_TIE) != 0;
   const unsigned int quota = tie ? st->quota : 0xFFFFFFFFu;
-  const float* agg = p.agg + (size_t)(b * p.nR + hr) * p.Nagg;
-  int* dst = p.sel_idx + (size_t)(b * p.nR + hr) * p.sel_cap;
+  const float* agg = p.agg + srow * p.Nagg;
+  int* dst = p.sel_idx + srow * p.sel_cap;
   __shared__ unsigned int tmp[8];
   unsigned int written = 0, ties = 0;
   for (int base = 0; base < N; base += 256) {
@@ -436,12 +450,12 @@ __global__ __launch_bounds__(256) void emit_sel_kernel(DecodeParams p) {
 
 template <int G, bool BYMASS>
 static hipError_t launch_pass1(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return launch_kernel(select_pass1_kernel<G, BYMASS>, dim3(p.n_sel_chunks, p.nR, p.B), dim3(NT), s, e0, e1, p);
+  return launch_kernel(select_pass1_kernel<G, BYMASS>, dim3(p.n_sel_chunks, p.nR * p.GS, p.B), dim3(NT), s, e0, e1, p);
 }
 
 template <bool BYMASS>
 static hipError_t launch_select_m(const DecodeParams& p, hipStream_t s, int pass, hipEvent_t e0, hipEvent_t e1) {
-  const dim3 grid(p.n_sel_chunks, p.nR, p.B);
+  const dim3 grid(p.n_sel_chunks, p.nR * p.GS, p.B);
   switch (pass) {
     case 1:
       switch (p.G) {
@@ -463,7 +477,7 @@ hipError_t launch_select(const DecodeParams& p, hipStream_t s, int pass, hipEven
 }
 
 hipError_t launch_emit(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(emit_sel_kernel, dim3(p.nR, p.B), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(emit_sel_kernel, dim3(p.nR * p.GS, p.B), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ HWS_KV_BF16, HWS_KV_FP8_E4M3 = 0, 1
 HWS_HEAD_LOCAL, HWS_HEAD_RETRIEVAL = 0, 1
 HWS_SELECT_TOP_P, HWS_SELECT_TOP_K = 0, 1
 HWS_SCORE_INDEX, HWS_SCORE_FULL = 0, 1
+HWS_SCOPE_KV_HEAD, HWS_SCOPE_QUERY_HEAD = 0, 1
 HWS_LAUNCH_AUTO, HWS_LAUNCH_MULTI, HWS_LAUNCH_COOPERATIVE, HWS_LAUNCH_SINGLE = 0, 1, 2, 3
 
 EXPORTED = (
@@ -59,7 +60,7 @@ class Buffers(ctypes.Structure):
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("select_mode", ctypes.c_int32), ("score_mode", ctypes.c_int32),
-                ("q", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
+                ("select_scope", ctypes.c_int32), ("q", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
                 ("seq_lens", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
                 ("top_k", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("sel_counts", ctypes.c_void_p), ("sel_idx", ctypes.c_void_p),
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
         "hws_classify_by_scores": (i32, [vp, P(ctypes.c_float), i32, i32]),
         "hws_get_head_kinds": (i32, [vp, P(ctypes.c_uint8)]),
         "hws_bind": (i32, [vp, P(Buffers)]),
-        "hws_workspace_size": (i32, [vp, i32, i32, i32, P(ctypes.c_size_t)]),
+        "hws_workspace_size": (i32, [vp, i32, i32, i32, i32, P(ctypes.c_size_t)]),
         "hws_append": (i32, [vp, i32, i32, vp, vp, vp, vp, vp]),
         "hws_decode": (i32, [vp, P(DecodeArgs), vp]),
         "hws_profile_enable": (i32, [vp, i32]),
@@ -182,9 +183,9 @@ class Context:
         self._buf = Buffers(_ptr(k_pool), _ptr(v_pool), _ptr(kv_scales), _ptr(index_pool), _ptr(proj))
         self._check(self._L.hws_bind(self.handle, ctypes.byref(self._buf)), "hws_bind")
 
-    def workspace_size(self, batch: int, max_seq_len: int, score_mode: int) -> int:
+    def workspace_size(self, batch: int, max_seq_len: int, score_mode: int, select_scope: int = 0) -> int:
         n = ctypes.c_size_t()
-        self._check(self._L.hws_workspace_size(self.handle, batch, max_seq_len, score_mode,
+        self._check(self._L.hws_workspace_size(self.handle, batch, max_seq_len, score_mode, select_scope,
                                                ctypes.byref(n)), "hws_workspace_size")
         return n.value
 
@@ -197,8 +198,9 @@ class Context:
 
     def decode(self, *, q, block_tables, seq_lens, max_seq_len: int, select_mode: int,
                score_mode: int, out, workspace, top_p=None, top_k=None, lse=None,
-               sel_counts=None, sel_idx=None, scores=None, stream=None):
+               sel_counts=None, sel_idx=None, scores=None, stream=None, select_scope: int = 0):
         a = DecodeArgs()
+        a.select_scope = int(select_scope)
         a.batch = int(q.shape[0]) if q is not None else 0
         a.max_seq_len = int(max_seq_len)
         a.select_mode, a.score_mode = int(select_mode), int(score_mode)

@@ -88,11 +88,13 @@ class DecodeSetup:
         self.top_k = torch.from_numpy(np.asarray(wl.top_k, np.int32)).to(self.dev)
         self.select_mode = hws.HWS_SELECT_TOP_P if wl.select_mode == "top_p" else hws.HWS_SELECT_TOP_K
         self.score_mode = hws.HWS_SCORE_INDEX if wl.score_mode == "index" else hws.HWS_SCORE_FULL
-        ws = self.ctx.workspace_size(B, self.Nmax, self.score_mode)
+        self.scope = hws.HWS_SCOPE_QUERY_HEAD if wl.select_scope == "query" else hws.HWS_SCOPE_KV_HEAD
+        ws = self.ctx.workspace_size(B, self.Nmax, self.score_mode, self.scope)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.dev)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=self.dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=self.dev)
-        self.sel_counts = torch.empty((B, Hkv), dtype=torch.int32, device=self.dev)
+        # |S| per KV head, or per query head with one set per query head
+        self.sel_counts = torch.empty((B, Hq if self.scope else Hkv), dtype=torch.int32, device=self.dev)
 
     def decode(self, *, debug: bool = False, sel_cap: int | None = None, stream=None):
         """Run one decode step.  With debug=True also return the raw scores and
@@ -102,12 +104,14 @@ class DecodeSetup:
         if debug and self.nR:
             scores = torch.empty((B, self.nR, self.Nmax, G), dtype=torch.float32, device=self.dev)
             cap = sel_cap or self.Nmax
-            sel_idx = torch.full((B, self.nR, cap), -1, dtype=torch.int32, device=self.dev)
+            shape = (B, self.nR, G, cap) if self.scope else (B, self.nR, cap)
+            sel_idx = torch.full(shape, -1, dtype=torch.int32, device=self.dev)
         self.ctx.decode(q=self.q, block_tables=self.block_tables, seq_lens=self.seq_lens,
                         max_seq_len=self.Nmax, select_mode=self.select_mode,
                         score_mode=self.score_mode, out=self.out, workspace=self.workspace,
                         top_p=self.top_p, top_k=self.top_k, lse=self.lse,
-                        sel_counts=self.sel_counts, sel_idx=sel_idx, scores=scores, stream=stream)
+                        sel_counts=self.sel_counts, sel_idx=sel_idx, scores=scores, stream=stream,
+                        select_scope=self.scope)
         if not debug:
             return None
         torch.cuda.synchronize(self.dev)

@@ -73,6 +73,7 @@ class Workload:
     window: int
     kv_dtype: str                    # "bf16" | "fp8"
     rope_theta: float = 0.0
+    select_scope: str = "kv"         # "kv": one set per KV head | "query": one per query head
     d: int = D
     r: int = R
     n_needles: int = 0

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define HWS_ABI_VERSION 1
+#define HWS_ABI_VERSION 2
 
 typedef int32_t hws_status;
 enum {
@@ -72,6 +72,9 @@ enum { HWS_SELECT_TOP_P = 0, HWS_SELECT_TOP_K = 1 };
 /* Selection score: INDEX = 16-dim pre-RoPE index ([RTPurbo] Methodology §2);
  * FULL = full-dim q.k, i.e. exact "oracle top-k" ([ICS] §2). */
 enum { HWS_SCORE_INDEX = 0, HWS_SCORE_FULL = 1 };
+/* Selection scope: one set per KV head shared by its query heads, or one set
+ * per query head ([ICS] §2: sparsity differs per token, query and head). */
+enum { HWS_SCOPE_KV_HEAD = 0, HWS_SCOPE_QUERY_HEAD = 1 };
 enum { HWS_LAUNCH_AUTO = 0, HWS_LAUNCH_MULTI = 1, HWS_LAUNCH_COOPERATIVE = 2, HWS_LAUNCH_SINGLE = 3 };
 
 typedef struct hws_ctx hws_ctx; /* opaque host object, owned by the library */
@@ -118,6 +121,7 @@ typedef struct {
   int32_t max_seq_len;       /* host upper bound of seq_lens (sizes grids)    */
   int32_t select_mode;       /* HWS_SELECT_*                                  */
   int32_t score_mode;        /* HWS_SCORE_*                                   */
+  int32_t select_scope;      /* HWS_SCOPE_* (0 = one set per KV head)         */
   const void* q;             /* [B][Hq][128] bf16, pre-RoPE queries           */
   const int32_t* block_tables; /* [B][max_blocks_per_seq] page ids            */
   const int32_t* seq_lens;   /* [B] context lengths incl. the current token   */
@@ -125,8 +129,13 @@ typedef struct {
   const int32_t* top_k;      /* [B] (TOP_K); k >= N keeps every token         */
   float* out;                /* [B][Hq][128] fp32 attention output            */
   float* lse;                /* [B][Hq] natural-log LSE over the set, or NULL */
-  int32_t* sel_counts;       /* [B][Hkv] |S| per head, or NULL                */
-  int32_t* sel_idx;          /* [B][n_retrieval][sel_cap] ascending, or NULL  */
+  int32_t* sel_counts;       /* [B][Hkv] |S| per KV head (KV scope) or
+                                [B][Hq] per query head (query scope; a local
+                                head's query heads all report its set), or
+                                NULL                                          */
+  int32_t* sel_idx;          /* [B][n_retrieval][sel_cap] (KV scope) or
+                                [B][n_retrieval][G][sel_cap] (query scope)
+                                ascending positions, or NULL                  */
   int32_t sel_cap;           /* row length of sel_idx (host)                  */
   float* scores;             /* [B][n_retrieval][max_seq_len][G] raw scores
                                 (P q).(P k) or q.k, or NULL (then kept in the
@@ -171,9 +180,11 @@ hws_status hws_get_head_kinds(const hws_ctx* ctx, uint8_t* kinds);
 /* Bind the caller's pools (pointers copied; memory stays caller-owned). */
 hws_status hws_bind(hws_ctx* ctx, const hws_buffers* buf);
 
-/* Workspace bytes that hws_decode needs for this batch and length bound. */
+/* Workspace bytes that hws_decode needs for this batch, length bound, score
+ * mode and selection scope (the query scope keeps G selection states and
+ * aggregates per retrieval head). */
 hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq_len,
-                              int32_t score_mode, size_t* bytes);
+                              int32_t score_mode, int32_t select_scope, size_t* bytes);
 
 /* Append n_tok tokens to each of n_seq sequences: token t of sequence s goes to
  * position start_pos[s] + t, i.e. slot pos % 16 of page

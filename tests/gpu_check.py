@@ -34,7 +34,7 @@ def oracle_head(setup: DecodeSetup, b: int, h: int, fixed_set=None):
         score_mode=wl.score_mode, select_mode=wl.select_mode, top_p=float(wl.top_p[b]),
         top_k=int(wl.top_k[b]), n_sink=wl.n_sink, window=wl.window, attn_scale=wl.attn_scale,
         index_scale=wl.index_scale, rope_theta=wl.rope_theta, kv_fp8=setup.fp8,
-        segments=append_segments(n), heads=[h],
+        segments=append_segments(n), heads=[h], scope=wl.select_scope,
         fixed_sets=None if fixed_set is None else {h: fixed_set})[h]
 
 
@@ -95,7 +95,27 @@ def check_decode(setup: DecodeSetup, res: dict, pairs=None, check_scores=True, v
         kind = wl.head_kinds[h]
         ref = oracle_head(setup, b, h)
         rep = {"b": b, "h": h, "kind": kind}
-        if kind == "retrieval":
+        if kind == "retrieval" and wl.select_scope == "query":
+            # one set per query head: each checked against that head's own distribution
+            hr = wl.retrieval_heads.index(h)
+            sets, diff = [], 0
+            for g in range(G):
+                cnt = int(res["sel_counts"][b, h * G + g])
+                S_g = res["sel_idx"][b, hr, g][:cnt].astype(np.int64)
+                assert cnt >= 1 and (np.diff(S_g) > 0).all() and S_g[-1] < n and S_g[0] >= 0
+                r = check_set(ref["a_heads"][g], S_g, ref["S_heads"][g], ref["t_heads"][g],
+                              wl.select_mode, float(wl.top_p[b]), int(wl.top_k[b]))
+                diff += r["n_diff"]
+                sets.append(S_g)
+            rep.update(n_diff=diff, n_gpu=[len(x) for x in sets], n_ref=[len(x) for x in ref["S_heads"]])
+            if check_scores:
+                s_gpu = res["scores"][b, hr, :n, :].T.astype(np.float64)
+                worst = float((np.abs(s_gpu - ref["scores"]) / _score_bound(setup, b, h, n)).max())
+                rep["score_err_ratio"] = worst
+                assert worst <= 1.0, f"scores off at (b={b}, h={h}): {worst} x tolerance"
+            if diff:
+                ref = oracle_head(setup, b, h, fixed_set=sets)
+        elif kind == "retrieval":
             hr = wl.retrieval_heads.index(h)
             cnt = int(res["sel_counts"][b, h])
             S_gpu = res["sel_idx"][b, hr][:cnt].astype(np.int64)
@@ -111,6 +131,8 @@ def check_decode(setup: DecodeSetup, res: dict, pairs=None, check_scores=True, v
                                  float(wl.top_p[b]), int(wl.top_k[b])))
             if rep["n_diff"]:
                 ref = oracle_head(setup, b, h, fixed_set=S_gpu)
+        elif wl.select_scope == "query":
+            assert (res["sel_counts"][b, h * G:(h + 1) * G] == ref["S"].size).all()
         else:
             assert int(res["sel_counts"][b, h]) == ref["S"].size
         o_gpu = out[b, h * G:(h + 1) * G].astype(np.float64)

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(hws.EXPORTED) == decl
-    assert L.hws_abi_version() == 1
+    assert L.hws_abi_version() == 2
     assert L.hws_status_string(hws.HWS_ERR_WORKSPACE) == b"workspace too small"
 
 
@@ -171,6 +171,8 @@ def test_decode_validation_without_gpu():
         (dict(max_seq_len=0), hws.HWS_ERR_INVALID_ARG),
         (dict(select_mode=2), hws.HWS_ERR_INVALID_ARG),
         (dict(score_mode=5), hws.HWS_ERR_INVALID_ARG),
+        (dict(select_scope=2), hws.HWS_ERR_INVALID_ARG),
+        (dict(select_scope=-1), hws.HWS_ERR_INVALID_ARG),
         (dict(q=None), hws.HWS_ERR_INVALID_ARG),
         (dict(top_p=None), hws.HWS_ERR_INVALID_ARG),
         (dict(select_mode=1), hws.HWS_ERR_INVALID_ARG),  # top-k without top_k
@@ -207,3 +209,14 @@ def test_workspace_size_rules():
         c.workspace_size(0, 10, 0)
     # scores region: 4 bytes x G per token per retrieval head at least
     assert n1 >= 500 * 4 * 4 + 500 * 4
+    # one set per query head: G aggregates and G selection states per retrieval head
+    nq = c.workspace_size(1, 500, 0, hws.HWS_SCOPE_QUERY_HEAD)
+    assert nq >= n1 + 3 * 500 * 4
+    with pytest.raises(hws.HwsError) as e:
+        c.workspace_size(1, 500, 0, 7)
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG
+    # a workspace sized for one set per KV head is too small for one per query head
+    c.bind(4096, 4096, None, 4096, 4096)
+    with pytest.raises(hws.HwsError) as e:
+        _decode(c, max_seq_len=500, workspace=_FakeT(nbytes=n1), select_scope=hws.HWS_SCOPE_QUERY_HEAD)
+    assert e.value.status == hws.HWS_ERR_WORKSPACE

@@ -271,3 +271,53 @@ def test_fused_timed_path_matches_debug_path():
     np.testing.assert_array_equal(st.out.cpu().numpy(), full["out"])
     np.testing.assert_array_equal(st.lse.cpu().numpy(), full["lse"])
     np.testing.assert_array_equal(st.sel_counts.cpu().numpy(), full["sel_counts"])
+
+
+# -- one token set per query head (select_scope = query) ------------------------
+
+@pytest.mark.parametrize("select_mode", ["top_p", "top_k"])
+def test_query_scope_tiny_and_layer(select_mode):
+    kw = {} if select_mode == "top_p" else dict(select_mode="top_k", top_k=np.array([61], np.int32))
+    _run(W.make_workload(1, select_scope="query", **kw))
+    kw2 = {} if select_mode == "top_p" else dict(select_mode="top_k", top_k=np.array([100, 7], np.int32))
+    _run(W.make_workload(2, n=9000, batch=2, select_scope="query", **kw2), verbose=False)
+
+
+def test_query_scope_peaky_and_diffuse_heads():
+    """The 70B-shaped group (G = 8): peaky query heads keep a few tokens,
+    diffuse ones thousands; each head attends over its own set."""
+    wl = W.make_workload(4, n=20000, select_scope="query")
+    st, res, reps = _run(wl, pairs=[(0, 0), (0, 3)])
+    G = wl.G
+    counts = res["sel_counts"][0, :G]
+    print("per-query-head |S|:", counts.tolist(), flush=True)
+    assert counts.max() > 20 * counts.min()
+
+
+def test_query_scope_full_scores_and_degenerate():
+    _run(W.make_workload(3, n=6000, batch=2, select_scope="query"))
+    n = 777
+    wl = W.make_workload(1, n=n, select_scope="query", top_p=np.array([1.0], np.float32))
+    _, res, _ = _run(wl)
+    assert (res["sel_counts"][0, :4] == n).all()
+    wl = W.make_workload(1, n=n, select_scope="query", top_p=np.array([1e-7], np.float32))
+    _, res, _ = _run(wl)
+    assert (res["sel_counts"][0, :4] == 1).all()
+
+
+def test_query_scope_ties_and_single_launch_falls_back():
+    n = 30000
+    seq = W.make_workload(1, n=n).sequence(0)
+    seq.k[:, 0, :] = seq.k[0, 0, :]                  # every logit of head 0 equal
+    wl = W.make_workload(1, n=n, select_scope="query", select_mode="top_k", top_k=np.array([1234], np.int32))
+    st = DecodeSetup(wl, keep_host=True, sequences=[seq])
+    st.ctx.set_launch_mode(SINGLE)                   # one set per query head runs per stage
+    st.ctx.profile_enable(True)
+    res = st.decode(debug=True)
+    prof = st.ctx.profile_read()
+    st.ctx.profile_enable(False)
+    assert prof["select"][1] == 1 and prof["tail"][1] == 0, prof
+    check_decode(st, res)
+    for g in range(wl.G):
+        assert res["sel_counts"][0, g] == 1234
+        np.testing.assert_array_equal(res["sel_idx"][0, 0, g, :1234], np.arange(1234))
