@@ -99,9 +99,16 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode,
   L.score_chunk = (score_mode == HWS_SCORE_FULL && G == 4 && !rope) ? G4_SCORE_CHUNK : SCORE_CHUNK;
   L.n_score_chunks = cdiv(Nmax, L.score_chunk);
   L.n_sel_chunks = cdiv(Nmax, SEL_CHUNK);
-  // Retrieval attention chunk: longer contexts get longer chunks so that the
-  // split partials stay small next to the gathered rows.
-  L.att_chunk_R = Nmax >= 65536 ? 4096 : (Nmax >= 16384 ? 2048 : 1024);
+  // Retrieval attention chunk: long enough that the split partials stay small
+  // next to the gathered rows, short enough that the chunks of the whole batch
+  // give about two workgroups per compute unit (a few sequences and heads at a
+  // long context would otherwise leave most of the chip idle).
+  {
+    const long long units = (long long)B * std::max(c->nR, 1) * Nmax;
+    int chunk = 1024;
+    while (chunk < 4096 && units / (2 * chunk) >= 2 * 256) chunk *= 2;
+    L.att_chunk_R = chunk;
+  }
   L.ncR = cdiv(Nmax, L.att_chunk_R);
   const long long local_rows = std::min<long long>(Nmax, (long long)c->cfg.n_sink + c->cfg.window);
   L.ncL = std::max(1, cdiv(local_rows, LOCAL_CHUNK));

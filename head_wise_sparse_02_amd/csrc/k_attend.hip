@@ -211,12 +211,25 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
 }
 
 // out_g = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);  lse = (M + log2 L) ln 2.
-// One workgroup per (sequence, KV head, query head), one thread per dim; the
-// partials of up to 32 splits are loaded at once and folded in online.
+// One workgroup per (sequence, KV head, query head): MERGE_GROUPS groups of D
+// threads (one per dim) fold every MERGE_GROUPS-th split online, 16 splits'
+// partials loaded at once, then group 0 combines the groups' results.
+constexpr int MERGE_GROUPS = 4;
+
+__device__ __forceinline__ void merge_fold(float& M, float& L, float& O, float m2, float l2, float o2) {
+  if (!(l2 > 0.f)) return;                              // empty splits left no output
+  const float mt = fmaxf(M, m2);
+  const float c1 = fast_exp2(M - mt), c2 = fast_exp2(m2 - mt);   // c1 = 0 while nothing was folded in
+  L = L * c1 + l2 * c2;
+  O = O * c1 + o2 * c2;
+  M = mt;
+}
+
 template <int G>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
-  constexpr int SB = 32;
-  const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+__global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p) {
+  constexpr int SB = 16;
+  const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int d = threadIdx.x % D, grp = threadIdx.x / D;
   const int hr = p.ret_slot[h];
   const int nspl = hr >= 0 ? p.ncR : p.ncL;
   const int N = min(p.seq_lens[b], p.Nmax);
@@ -224,33 +237,25 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const float2* ml = p.apart_ml + base;                 // split s at ml[s * G]
   const float* po = p.apart_o + base * D + d;           // split s at po[s * G * D]
   float M = NEG_INF, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < nspl; s0 += SB) {
+  for (int s0 = grp; s0 < nspl; s0 += SB * MERGE_GROUPS) {
     float2 v[SB];
     float ov[SB];
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const bool in = s0 + u < nspl;
-      v[u] = in ? ml[(size_t)(s0 + u) * G] : make_float2(NEG_INF, 0.f);
-      ov[u] = in ? po[(size_t)(s0 + u) * G * D] : 0.f;
+      const int sp = s0 + u * MERGE_GROUPS;
+      const bool in = sp < nspl;
+      v[u] = in ? ml[(size_t)sp * G] : make_float2(NEG_INF, 0.f);
+      ov[u] = in ? po[(size_t)sp * G * D] : 0.f;
     }
-    float mt = M;
 #pragma unroll
-    for (int u = 0; u < SB; ++u)
-      if (v[u].y > 0.f) mt = fmaxf(mt, v[u].x);
-    if (mt == NEG_INF) continue;
-    const float cf = fast_exp2(M - mt);                 // 0 while nothing was folded in
-    L *= cf;
-    O *= cf;
-#pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      if (v[u].y > 0.f) {                               // empty splits left no output
-        const float w = fast_exp2(v[u].x - mt);
-        L = fmaf(v[u].y, w, L);
-        O = fmaf(ov[u], w, O);
-      }
-    }
-    M = mt;
+    for (int u = 0; u < SB; ++u) merge_fold(M, L, O, v[u].x, v[u].y, ov[u]);
   }
+  __shared__ float gm[MERGE_GROUPS], gl[MERGE_GROUPS], go[MERGE_GROUPS][D];
+  if (d == 0) { gm[grp] = M; gl[grp] = L; }
+  go[grp][d] = O;
+  __syncthreads();
+  if (grp != 0) return;
+  for (int k = 1; k < MERGE_GROUPS; ++k) merge_fold(M, L, O, gm[k], gl[k], go[k][d]);
   p.out[((size_t)b * p.Hq + h * G + g) * D + d] = L > 0.f ? O / L : 0.f;
   if (d == 0 && p.lse != nullptr) p.lse[(size_t)b * p.Hq + h * G + g] = (M + log2f(L)) * LN2;
   // |S| per KV head, or per query head with one set per query head
@@ -309,7 +314,7 @@ hipError_t launch_attend(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hi
 }
 
 hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const dim3 grid(p.G, p.Hkv, p.B), blk(D);
+  const dim3 grid(p.G, p.Hkv, p.B), blk(D * MERGE_GROUPS);
   switch (p.G) {
     case 1: return launch_kernel(merge_kernel<1>, grid, blk, s, e0, e1, p);
     case 2: return launch_kernel(merge_kernel<2>, grid, blk, s, e0, e1, p);
