@@ -34,6 +34,8 @@ from .hws_oracle import (  # noqa: F401
     fp8_store_rows,
     full_logits,
     group_aggregate,
+    head_probs,
+    index_keys,
     index_logits,
     local_token_set,
     rope,

@@ -162,18 +162,29 @@ def stored_rows(x_pre, positions, *, rope_theta: float, kv_fp8: bool, segments, 
 # Selection scores  ([RTPurbo] Methodology §2; [ICS] §2 "Oracle top-k")
 # ---------------------------------------------------------------------------
 
-def index_logits(q_pre, k_pre, proj, index_scale: float):
+def index_keys(k_pre, proj, index_bf16: bool = False) -> np.ndarray:
+    """The stored index k~ = P k of every token ([RTPurbo] Methodology §2).
+
+    reading: fp32 storage keeps P k as computed; a bf16 index (32 B per
+    token instead of 64) holds P k evaluated in fp64 and rounded once to bf16.
+    """
+    kt = np.asarray(k_pre, dtype=np.float64) @ np.asarray(proj, dtype=np.float64).T
+    return bf16_round(kt) if index_bf16 else kt
+
+
+def index_logits(q_pre, k_pre, proj, index_scale: float, index_bf16: bool = False):
     """Low-dim pre-RoPE index: q~ = P q, k~ = P k, s = q~ . k~.
 
     [RTPurbo] Methodology §2: a projection to r = 16 dims is applied to the
     query and key features before RoPE and relevance is estimated there.
     reading: one fp32 projection per retrieval KV head, shared by q and k and
-    by the group's query heads; the logit is index_scale * s.
+    by the group's query heads; the logit is index_scale * s.  With a bf16
+    index the stored k~ is rounded to bf16 (index_keys); q~ is not stored.
     Returns (s [G, N], logits [G, N]).
     """
     P = np.asarray(proj, dtype=np.float64)
     qt = np.asarray(q_pre, dtype=np.float64) @ P.T
-    kt = np.asarray(k_pre, dtype=np.float64) @ P.T
+    kt = index_keys(k_pre, proj, index_bf16)
     s = qt @ kt.T
     return s, index_scale * s
 
@@ -291,7 +302,7 @@ def decode_head_ref(q_pre, k_pre, k_store, v_store, *, kind: str, proj=None,
                     top_p: float = 0.9, top_k: int = 0, n_sink: int = 0,
                     window: int = 0, attn_scale: float, index_scale: float = 1.0,
                     rope_theta: float = 0.0, fixed_set=None, with_full_mass: bool = False,
-                    scope: str = "kv"):
+                    scope: str = "kv", index_bf16: bool = False):
     """Decode one step for one (sequence, KV head).
 
     q_pre [G, d] pre-RoPE queries; k_pre [N, d] pre-RoPE keys (the index
@@ -319,7 +330,7 @@ def decode_head_ref(q_pre, k_pre, k_store, v_store, *, kind: str, proj=None,
     out = {"t": None, "scores": None, "a": None, "index_mass": None}
     if kind == "retrieval" and scope == "query":
         if score_mode == "index":
-            s, l = index_logits(q_pre, k_pre, proj, index_scale)
+            s, l = index_logits(q_pre, k_pre, proj, index_scale, index_bf16)
         else:
             s, l = full_logits(q_rot, k_store, attn_scale)
         pi = head_probs(l)
@@ -344,7 +355,7 @@ def decode_head_ref(q_pre, k_pre, k_store, v_store, *, kind: str, proj=None,
         return out
     if kind == "retrieval":
         if score_mode == "index":
-            s, l = index_logits(q_pre, k_pre, proj, index_scale)
+            s, l = index_logits(q_pre, k_pre, proj, index_scale, index_bf16)
         else:
             s, l = full_logits(q_rot, k_store, attn_scale)
         a = group_aggregate(l)
@@ -374,7 +385,8 @@ def decode_head_ref(q_pre, k_pre, k_store, v_store, *, kind: str, proj=None,
 def decode_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, proj=None, score_mode="index",
                         select_mode="top_p", top_p=0.9, top_k=0, n_sink=0, window=0,
                         attn_scale, index_scale=1.0, rope_theta=0.0, kv_fp8=False,
-                        segments=None, heads=None, fixed_sets=None, with_full_mass=False, scope="kv"):
+                        segments=None, heads=None, fixed_sets=None, with_full_mass=False, scope="kv",
+                        index_bf16=False):
     """Decode one step of one sequence for the KV heads in ``heads``.
 
     q_pre [Hq, d]; k_pre, v_in [N, Hkv, d] as appended (bf16-exact values);
@@ -401,5 +413,5 @@ def decode_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, proj=None, score_mode
             window=window, attn_scale=attn_scale, index_scale=index_scale,
             rope_theta=rope_theta,
             fixed_set=None if fixed_sets is None else fixed_sets.get(h),
-            with_full_mass=with_full_mass, scope=scope)
+            with_full_mass=with_full_mass, scope=scope, index_bf16=index_bf16)
     return res

@@ -131,6 +131,36 @@ def test_index_scores_brute_force_and_orientation():
             assert abs(s[g, i] - sum(a * b for a, b in zip(qt, kt))) < 1e-9 * (1 + abs(s[g, i]))
 
 
+def test_bf16_index_selecting_projection_is_exact():
+    """P selecting 16 coordinates of bf16 keys: k~ is already bf16, so the
+    bf16 index equals the fp32 one exactly (closed form)."""
+    rng = np.random.default_rng(71)
+    q = O.bf16_round(rng.standard_normal((4, 128)))
+    k = O.bf16_round(rng.standard_normal((40, 128)))
+    P = np.zeros((16, 128))
+    P[np.arange(16), rng.choice(128, 16, replace=False)] = 1.0
+    s32, _ = O.index_logits(q, k, P, 1.0)
+    s16, _ = O.index_logits(q, k, P, 1.0, index_bf16=True)
+    np.testing.assert_array_equal(s16, s32)
+    np.testing.assert_array_equal(O.index_keys(k, P, True), k @ P.T)
+
+
+def test_bf16_index_brute_force():
+    """Scalar loop: k~_j = bf16(sum_t P[j,t] k[t]) (fp64 sum, one rounding)
+    and s = q~ . k~ with q~ unrounded; torch's cast does the rounding."""
+    rng = np.random.default_rng(72)
+    q, k, P = rng.standard_normal((2, 128)), rng.standard_normal((5, 128)), rng.standard_normal((16, 128)) / 11
+    s, _ = O.index_logits(q, k, P, 1.0, index_bf16=True)
+    for i in range(5):
+        kt = [float(torch.tensor(sum(P[j, t] * k[i, t] for t in range(128)), dtype=torch.float64)
+                    .to(torch.bfloat16).to(torch.float64)) for j in range(16)]
+        for g in range(2):
+            qt = [sum(P[j, t] * q[g, t] for t in range(128)) for j in range(16)]
+            assert abs(s[g, i] - sum(a * b for a, b in zip(qt, kt))) < 1e-9 * (1 + abs(s[g, i]))
+    s32, _ = O.index_logits(q, k, P, 1.0)
+    assert not np.array_equal(s, s32)              # the rounding is really applied
+
+
 def test_full_scores_brute_force():
     rng = np.random.default_rng(8)
     q, k = rng.standard_normal((2, 128)), rng.standard_normal((5, 128))
