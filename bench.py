@@ -63,6 +63,8 @@ def parse_args(argv=None):
                     help="auto: the library's default; single: one launch after (or with) the scoring "
                          "scan, grid sized to the device; cooperative: the same as a cooperative launch; "
                          "multi: a kernel per stage")
+    ap.add_argument("--index", choices=["f32", "bf16"], default="f32",
+                    help="storage of the r=16 index (64 or 32 bytes per token and retrieval head)")
     ap.add_argument("--scope", choices=["kv", "query"], default="kv",
                     help="one token set per KV head (kv) or per query head (query)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -79,8 +81,9 @@ def parse_args(argv=None):
 def algorithmic_bytes(wl, sel_counts) -> dict:
     """Required HBM bytes of one decode step, by stage.
 
-    score : every token of every retrieval head once: the 16-dim fp32 index
-            (64 B) or, with full-dim scores, the K row (256 B bf16 / 128 B fp8);
+    score : every token of every retrieval head once: the 16-dim index
+            (64 B fp32 / 32 B bf16) or, with full-dim scores, the K row
+            (256 B bf16 / 128 B fp8);
     attend: K and V rows of every selected token (V only with full-dim
             scores, whose logits are already known) and of the local heads'
             sinks + window; fp8 adds 8 B of scales per page and head touched;
@@ -94,7 +97,7 @@ def algorithmic_bytes(wl, sel_counts) -> dict:
         for h, kind in enumerate(wl.head_kinds):
             cnt = int(sel_counts[b, h])
             if kind == "retrieval":
-                score += n * (row if wl.score_mode == "full" else 64)
+                score += n * (row if wl.score_mode == "full" else (32 if wl.index_dtype == "bf16" else 64))
                 attend += cnt * (row if wl.score_mode == "full" else 2 * row)
             else:
                 attend += cnt * 2 * row
@@ -189,7 +192,7 @@ def main(argv=None) -> int:
     from head_wise_sparse_02_amd import workloads as W
     from head_wise_sparse_02_amd.runner import DecodeSetup
 
-    wl = W.make_workload(args.config, seed=args.seed, select_scope=args.scope)
+    wl = W.make_workload(args.config, seed=args.seed, select_scope=args.scope, index_dtype=args.index)
     want_cpu = not args.no_cpu_baseline
     print(f"[bench] building workload {args.config}: {W.CONFIG_NAMES[args.config]}",
           file=sys.stderr, flush=True)
@@ -291,7 +294,7 @@ def main(argv=None) -> int:
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
                    "context": int(max(wl.seq_lens)), "score_mode": wl.score_mode,
                    "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype, "launch": args.launch,
-                   "select_scope": wl.select_scope},
+                   "select_scope": wl.select_scope, "index_dtype": wl.index_dtype},
         "step_bytes": by["total"], "step_GBps": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_GBS, 4),
         "selected_per_head_mean": round(float(sel_counts[:, [h for h in wl.retrieval_heads]].mean()), 1)

@@ -201,6 +201,7 @@ hws_status hws_create(const hws_config* cfg, hws_ctx** out) {
   if (c.head_dim != D || c.index_dim != R || c.block_size != BS) return HWS_ERR_UNSUPPORTED;
   if (c.num_blocks < 1 || c.max_blocks_per_seq < 1 || c.max_blocks_per_seq > (1 << 26)) return HWS_ERR_INVALID_ARG;
   if (c.kv_dtype != HWS_KV_BF16 && c.kv_dtype != HWS_KV_FP8_E4M3) return HWS_ERR_INVALID_ARG;
+  if (c.index_dtype != HWS_INDEX_F32 && c.index_dtype != HWS_INDEX_BF16) return HWS_ERR_INVALID_ARG;
   if (c.n_sink < 0 || c.window < 0 || (long long)c.n_sink + c.window < 1) return HWS_ERR_INVALID_ARG;
   if (!finite_f(c.attn_scale) || !(c.attn_scale > 0.f) || !finite_f(c.index_scale) ||
       !finite_f(c.rope_theta) || c.rope_theta < 0.f)
@@ -320,6 +321,7 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
   p.v_pool = ctx->buf.v_pool;
   p.kv_scales = ctx->buf.kv_scales;
   p.index_pool = ctx->buf.index_pool;
+  p.index_bf16 = ctx->cfg.index_dtype == HWS_INDEX_BF16 ? 1 : 0;
   p.proj = ctx->buf.proj;
   std::memcpy(p.ret_slot, ctx->ret_slot, sizeof(p.ret_slot));
   ctx->appended = true;
@@ -393,6 +395,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.v_pool = ctx->buf.v_pool;
   p.kv_scales = c.kv_dtype == HWS_KV_FP8_E4M3 ? ctx->buf.kv_scales : nullptr;
   p.index_pool = ctx->buf.index_pool;
+  p.index_bf16 = ctx->cfg.index_dtype == HWS_INDEX_BF16 ? 1 : 0;
   p.proj = ctx->buf.proj;
   p.scores = a->scores != nullptr ? a->scores : reinterpret_cast<float*>(ws + L.scores);
   p.scores_out = a->scores != nullptr ? 1 : 0;

@@ -83,7 +83,8 @@ struct DecodeParams {
   const void* k_pool;
   const void* v_pool;
   const float* kv_scales;
-  const float* index_pool;
+  const void* index_pool;       // [blocks][nR][16][16] fp32, or bf16 when index_bf16
+  int index_bf16;
   const float* proj;
   float* scores;                // [B][nR][Nmax][G]
   int scores_out;               // the caller asked for every score (else only kept ones may be written)
@@ -118,7 +119,8 @@ struct AppendParams {
   void* k_pool;
   void* v_pool;
   float* kv_scales;
-  float* index_pool;
+  void* index_pool;             // fp32, or bf16 when index_bf16
+  int index_bf16;
   const float* proj;
   signed char ret_slot[MAX_KV];
 };

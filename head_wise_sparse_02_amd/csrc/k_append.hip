@@ -51,9 +51,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int r = tid >> 4, j = tid & 15;
     if (r < nrows) {
       const float* prow = p.proj + ((size_t)h * R + j) * D;
-      float acc = 0.f;
-      for (int e = 0; e < D; ++e) acc = fmaf(prow[e], ks[r][e], acc);
-      p.index_pool[(((size_t)phys * p.nR + hr) * BS + slot0 + r) * R + j] = acc;
+      const size_t o = (((size_t)phys * p.nR + hr) * BS + slot0 + r) * R + j;
+      if (p.index_bf16) {           // P k in fp64, rounded once to bf16
+        double acc = 0.0;
+        for (int e = 0; e < D; ++e) acc = fma((double)prow[e], (double)ks[r][e], acc);
+        reinterpret_cast<uint16_t*>(p.index_pool)[o] = f64_to_bf16_rne(acc);
+      } else {
+        float acc = 0.f;
+        for (int e = 0; e < D; ++e) acc = fmaf(prow[e], ks[r][e], acc);
+        reinterpret_cast<float*>(p.index_pool)[o] = acc;
+      }
     }
   }
   __syncthreads();

@@ -43,14 +43,23 @@ __device__ __forceinline__ void wave_lse_reduce(float& m, float& s, int from_mas
 }
 
 // ---------------------------------------------------------------------------
-// INDEX mode
-// Lane l of a wave holds token slot l/4 of a page and index dims 4*(l%4)..+3.
-// After a 2-step butterfly over the 4 lanes of a token, lane l keeps the
-// score of query head g = l%4 (+4 for G = 8).
+// INDEX mode.  A wave scores 256 consecutive tokens (16 pages) with coalesced
+// 1 KiB loads: fp32 index (1 KiB per page): lane l holds token slot l/4 of
+// the page and index dims 4*(l%4)..+3, a 2-step butterfly over the 4 lanes of
+// a token leaves lane l with the score of query head g = l%4 (+4 for G = 8).
+// bf16 index (512 B per page, two pages per load): lane l holds page l/32 of
+// the pair, token slot (l%32)/2 and dims 8*(l%2)..+7; one butterfly step
+// leaves lane l with query heads g = l%2, +2, +4, ...  The wave's page ids
+// come in with one load and are read back wave-uniform, so no load waits on
+// another; pages past the end read page 0 and are masked.
 // ---------------------------------------------------------------------------
-template <int G>
+template <int G, bool BF16>
 __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
-  constexpr int NOWN = (G + 3) / 4;       // scores owned per lane per token
+  constexpr int LPT = BF16 ? 2 : 4;                   // lanes per token
+  constexpr int DPL = R / LPT;                        // index dims per lane
+  constexpr int NOWN = (G + LPT - 1) / LPT;           // scores owned per lane per token
+  constexpr int TPL = 64 / LPT;                       // tokens per wave load
+  constexpr int NLD = 256 / TPL;                      // loads per wave: 16 (fp32) or 8 (bf16)
   const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int N = min(p.seq_lens[b], p.Nmax);
@@ -74,32 +83,38 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
     }
     qt_s[g][j] = acc;
   }
-  __syncthreads();
 
-  const int sub = lane & 3;
-  float qv[G][4];
+  const int tok0 = c * SCORE_CHUNK + wave * 256;
+  const int page0 = tok0 >> 4;
+  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
+  const int my_blk = (lane < 16 && (page0 + lane) * BS < N) ? bt[page0 + lane] : -1;
+  const int sub = lane % LPT;
+  const int pin = BF16 ? (lane >> 5) : 0;             // page of the pair (bf16)
+  const size_t page_elems = (size_t)BS * R;
+  u32x4 kw[NLD];
+  unsigned valid = 0u;
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    // load i covers page i (fp32) or pages 2i, 2i+1 (bf16); every lane reads
+    // both candidates wave-uniformly and picks its own
+    const int pa = BF16 ? 2 * i : i;
+    const int blk_a = __builtin_amdgcn_readlane(my_blk, pa);
+    const int blk_b = BF16 ? __builtin_amdgcn_readlane(my_blk, pa + 1) : blk_a;
+    const bool ok_a = (unsigned)blk_a < (unsigned)p.num_blocks;
+    const bool ok_b = (unsigned)blk_b < (unsigned)p.num_blocks;
+    valid |= (ok_a ? 1u : 0u) << (2 * i);
+    valid |= (ok_b ? 1u : 0u) << (2 * i + 1);
+    const int blk = pin ? (ok_b ? blk_b : 0) : (ok_a ? blk_a : 0);
+    const char* pg = reinterpret_cast<const char*>(p.index_pool) +
+                     (((size_t)blk * p.nR + hr) * page_elems) * (BF16 ? 2 : 4);
+    kw[i] = load_nt16(pg + (BF16 ? (lane & 31) : lane) * 16);
+  }
+  __syncthreads();                                    // qt_s ready
+  float qv[G][DPL];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qv[g][j] = qt_s[g][sub * 4 + j];
-
-  const int tok0 = c * SCORE_CHUNK + wave * 256;
-  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
-  float4 kv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = tok0 + i * BS;
-    kv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < N) {
-      const int blk = bt[t >> 4];
-      if ((unsigned)blk < (unsigned)p.num_blocks) {
-        const float4* src = reinterpret_cast<const float4*>(
-            p.index_pool + ((size_t)blk * p.nR + hr) * (BS * R));
-        const u32x4 w = load_nt16(src + lane);
-        kv[i] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
-      }
-    }
-  }
+    for (int j = 0; j < DPL; ++j) qv[g][j] = qt_s[g][sub * DPL + j];
 
   float* out = p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G;
   float m[NOWN], s[NOWN];
@@ -108,22 +123,30 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
   const float c2 = p.c2_score;
 
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = tok0 + i * BS + (lane >> 2);
+  for (int i = 0; i < NLD; ++i) {
+    const int t = tok0 + i * TPL + (BF16 ? pin * BS + ((lane & 31) >> 1) : (lane >> 2));
+    const bool ok = ((valid >> (BF16 ? 2 * i + pin : 2 * i)) & 1u) != 0u;
+    float kx[DPL];
+    if (BF16) {
+      kx[0] = bf16_lo(kw[i].x); kx[1] = bf16_hi(kw[i].x); kx[2] = bf16_lo(kw[i].y); kx[3] = bf16_hi(kw[i].y);
+      kx[4] = bf16_lo(kw[i].z); kx[5] = bf16_hi(kw[i].z); kx[6] = bf16_lo(kw[i].w); kx[DPL - 1] = bf16_hi(kw[i].w);
+    } else {
+      kx[0] = __uint_as_float(kw[i].x); kx[1] = __uint_as_float(kw[i].y);
+      kx[2] = __uint_as_float(kw[i].z); kx[DPL - 1] = __uint_as_float(kw[i].w);
+    }
     float part[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float a = qv[g][0] * kv[i].x;
-      a = fmaf(qv[g][1], kv[i].y, a);
-      a = fmaf(qv[g][2], kv[i].z, a);
-      a = fmaf(qv[g][3], kv[i].w, a);
+      float a = qv[g][0] * kx[0];
+#pragma unroll
+      for (int j = 1; j < DPL; ++j) a = fmaf(qv[g][j], kx[j], a);
       a += __shfl_xor(a, 1);
-      a += __shfl_xor(a, 2);
-      part[g] = a;
+      if (!BF16) a += __shfl_xor(a, 2);
+      part[g] = ok ? a : 0.f;                          // an invalid page scores 0
     }
 #pragma unroll
     for (int k = 0; k < NOWN; ++k) {
-      const int g = sub + 4 * k;
+      const int g = sub + LPT * k;
       float v = part[0];
 #pragma unroll
       for (int gg = 1; gg < G; ++gg) v = (g == gg) ? part[gg] : v;
@@ -136,12 +159,12 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
       }
     }
   }
-  // lanes with equal (lane & 3) hold the same query heads: reduce over bits 2..5
+  // lanes with equal (lane % LPT) hold the same query heads
 #pragma unroll
   for (int k = 0; k < NOWN; ++k) {
-    wave_lse_reduce(m[k], s[k], 4, 32);
-    const int g = sub + 4 * k;
-    if (lane < 4 && g < G) { red_m[wave][g] = m[k]; red_s[wave][g] = s[k]; }
+    wave_lse_reduce(m[k], s[k], LPT, 32);
+    const int g = sub + LPT * k;
+    if (lane < LPT && g < G) { red_m[wave][g] = m[k]; red_s[wave][g] = s[k]; }
   }
   __syncthreads();
   if (tid < G) {
@@ -420,7 +443,10 @@ constexpr bool G4_PF = true;      // issue the next step's loads before this ste
 template <int G>
 static hipError_t launch_score_g(const DecodeParams& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.n_score_chunks, p.nR, p.B), blk(256);
-  if (p.score_mode == 0) return launch_kernel(score_index_kernel<G>, grid, blk, st, e0, e1, p);
+  if (p.score_mode == 0) {
+    if (p.index_bf16) return launch_kernel(score_index_kernel<G, true>, grid, blk, st, e0, e1, p);
+    return launch_kernel(score_index_kernel<G, false>, grid, blk, st, e0, e1, p);
+  }
   if (p.qrot != nullptr) return launch_kernel(score_full_kernel<G, true>, grid, blk, st, e0, e1, p);
   if (G == 4) return launch_kernel(score_full_g4_kernel<G4_SCORE_CHUNK, G4_GP, G4_PF>, grid, blk, st, e0, e1, p);
   return launch_kernel(score_full_kernel<G, false>, grid, blk, st, e0, e1, p);

@@ -27,6 +27,7 @@ HWS_HEAD_LOCAL, HWS_HEAD_RETRIEVAL = 0, 1
 HWS_SELECT_TOP_P, HWS_SELECT_TOP_K = 0, 1
 HWS_SCORE_INDEX, HWS_SCORE_FULL = 0, 1
 HWS_SCOPE_KV_HEAD, HWS_SCOPE_QUERY_HEAD = 0, 1
+HWS_INDEX_F32, HWS_INDEX_BF16 = 0, 1
 HWS_LAUNCH_AUTO, HWS_LAUNCH_MULTI, HWS_LAUNCH_COOPERATIVE, HWS_LAUNCH_SINGLE = 0, 1, 2, 3
 
 EXPORTED = (
@@ -46,7 +47,7 @@ class HwsError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_q_heads", "num_kv_heads", "head_dim", "index_dim", "block_size", "num_blocks",
-        "max_blocks_per_seq", "kv_dtype", "n_sink", "window")] + [
+        "max_blocks_per_seq", "kv_dtype", "index_dtype", "n_sink", "window")] + [
         ("attn_scale", ctypes.c_float), ("index_scale", ctypes.c_float),
         ("rope_theta", ctypes.c_float)]
 
@@ -134,11 +135,12 @@ class Context:
     def __init__(self, *, num_q_heads: int, num_kv_heads: int, num_blocks: int,
                  max_blocks_per_seq: int, n_sink: int, window: int, attn_scale: float,
                  index_scale: float = 1.0, rope_theta: float = 0.0, kv_dtype: int = HWS_KV_BF16,
-                 head_dim: int = 128, index_dim: int = 16, block_size: int = 16):
+                 index_dtype: int = HWS_INDEX_F32, head_dim: int = 128, index_dim: int = 16,
+                 block_size: int = 16):
         self._L = lib()
         self.cfg = Config(num_q_heads, num_kv_heads, head_dim, index_dim, block_size, num_blocks,
-                          max_blocks_per_seq, kv_dtype, n_sink, window, attn_scale, index_scale,
-                          rope_theta)
+                          max_blocks_per_seq, kv_dtype, index_dtype, n_sink, window, attn_scale,
+                          index_scale, rope_theta)
         h = ctypes.c_void_p()
         st = self._L.hws_create(ctypes.byref(self.cfg), ctypes.byref(h))
         if st != HWS_OK:

@@ -39,7 +39,8 @@ class DecodeSetup:
             max_blocks_per_seq=self.max_blocks, n_sink=max(wl.n_sink, 0),
             window=max(wl.window, 1 if wl.n_sink == 0 else 0),
             attn_scale=wl.attn_scale, index_scale=wl.index_scale, rope_theta=wl.rope_theta,
-            kv_dtype=hws.HWS_KV_FP8_E4M3 if self.fp8 else hws.HWS_KV_BF16)
+            kv_dtype=hws.HWS_KV_FP8_E4M3 if self.fp8 else hws.HWS_KV_BF16,
+            index_dtype=hws.HWS_INDEX_BF16 if wl.index_dtype == "bf16" else hws.HWS_INDEX_F32)
         self.ctx.set_head_kinds([KIND_CODE[k] for k in wl.head_kinds])
         self.nR = len(wl.retrieval_heads)
 
@@ -50,7 +51,8 @@ class DecodeSetup:
         self.v_pool = torch.zeros((self.num_blocks, Hkv, 16, d), dtype=kv_dt, device=self.dev)
         self.kv_scales = (torch.ones((self.num_blocks, Hkv, 2), dtype=torch.float32, device=self.dev)
                           if self.fp8 else None)
-        self.index_pool = (torch.zeros((self.num_blocks, max(self.nR, 1), 16, 16), dtype=torch.float32,
+        idx_dt = torch.bfloat16 if wl.index_dtype == "bf16" else torch.float32
+        self.index_pool = (torch.zeros((self.num_blocks, max(self.nR, 1), 16, 16), dtype=idx_dt,
                                        device=self.dev) if self.nR else None)
         self.proj_host = wl.projections()
         self.proj = torch.from_numpy(self.proj_host).to(self.dev)

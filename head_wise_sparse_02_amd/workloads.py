@@ -74,6 +74,7 @@ class Workload:
     kv_dtype: str                    # "bf16" | "fp8"
     rope_theta: float = 0.0
     select_scope: str = "kv"         # "kv": one set per KV head | "query": one per query head
+    index_dtype: str = "f32"         # stored r=16 index: "f32" | "bf16"
     d: int = D
     r: int = R
     n_needles: int = 0

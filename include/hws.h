@@ -72,6 +72,9 @@ enum { HWS_SELECT_TOP_P = 0, HWS_SELECT_TOP_K = 1 };
 /* Selection score: INDEX = 16-dim pre-RoPE index ([RTPurbo] Methodology §2);
  * FULL = full-dim q.k, i.e. exact "oracle top-k" ([ICS] §2). */
 enum { HWS_SCORE_INDEX = 0, HWS_SCORE_FULL = 1 };
+/* Storage of the r = 16 index k~ = P k: fp32 as computed (64 B per token and
+ * retrieval head), or bf16 of P k evaluated in fp64 and rounded once (32 B). */
+enum { HWS_INDEX_F32 = 0, HWS_INDEX_BF16 = 1 };
 /* Selection scope: one set per KV head shared by its query heads, or one set
  * per query head ([ICS] §2: sparsity differs per token, query and head). */
 enum { HWS_SCOPE_KV_HEAD = 0, HWS_SCOPE_QUERY_HEAD = 1 };
@@ -88,6 +91,7 @@ typedef struct {
   int32_t num_blocks;         /* pages in the pools                          */
   int32_t max_blocks_per_seq; /* row length of every block table             */
   int32_t kv_dtype;           /* HWS_KV_*                                    */
+  int32_t index_dtype;        /* HWS_INDEX_*: fp32 (64 B/token) or bf16      */
   int32_t n_sink;             /* local heads: sink tokens 0..n_sink-1        */
   int32_t window;             /* local heads: last `window` tokens           */
   float attn_scale;           /* softmax scale of attention, e.g. 1/sqrt(d)  */
@@ -102,16 +106,16 @@ typedef struct {
  *                   + d%32; K is stored after RoPE (when rope_theta > 0).
  *   v_pool:         [num_blocks][Hkv][16][128] bf16 or e4m3 bytes, row-major.
  *   kv_scales:      [num_blocks][Hkv][2] fp32 (K scale, V scale); FP8 only.
- *   index_pool:     [num_blocks][n_retrieval][16][16] fp32, the projected
- *                   pre-RoPE keys of retrieval heads in KV-head order; may be
- *                   NULL when no head is a retrieval head.
+ *   index_pool:     [num_blocks][n_retrieval][16][16] fp32 or bf16 (index_dtype),
+ *                   the projected pre-RoPE keys of retrieval heads in KV-head
+ *                   order; may be NULL when no head is a retrieval head.
  *   proj:           [Hkv][16][128] fp32 index projections (rows of local
  *                   heads are ignored); may be NULL when no head is retrieval. */
 typedef struct {
   void* k_pool;
   void* v_pool;
   float* kv_scales;
-  float* index_pool;
+  void* index_pool;
   const float* proj;
 } hws_buffers;
 

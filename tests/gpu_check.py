@@ -35,6 +35,7 @@ def oracle_head(setup: DecodeSetup, b: int, h: int, fixed_set=None):
         top_k=int(wl.top_k[b]), n_sink=wl.n_sink, window=wl.window, attn_scale=wl.attn_scale,
         index_scale=wl.index_scale, rope_theta=wl.rope_theta, kv_fp8=setup.fp8,
         segments=append_segments(n), heads=[h], scope=wl.select_scope,
+        index_bf16=wl.index_dtype == "bf16",
         fixed_sets=None if fixed_set is None else {h: fixed_set})[h]
 
 

@@ -20,7 +20,7 @@ def _declared():
 
 def _cfg(**kw):
     base = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, index_dim=16, block_size=16,
-                num_blocks=64, max_blocks_per_seq=32, kv_dtype=0, n_sink=4, window=256,
+                num_blocks=64, max_blocks_per_seq=32, kv_dtype=0, index_dtype=0, n_sink=4, window=256,
                 attn_scale=0.0883883, index_scale=0.7071, rope_theta=0.0)
     base.update(kw)
     return hws.Config(*[base[n] for n, _ in hws.Config._fields_])
@@ -57,6 +57,8 @@ def test_library_exports_every_declared_symbol():
     (dict(attn_scale=float("nan")), hws.HWS_ERR_INVALID_ARG),
     (dict(rope_theta=-1.0), hws.HWS_ERR_INVALID_ARG),
     (dict(kv_dtype=2), hws.HWS_ERR_INVALID_ARG),
+    (dict(index_dtype=2), hws.HWS_ERR_INVALID_ARG),
+    (dict(index_dtype=-1), hws.HWS_ERR_INVALID_ARG),
     (dict(num_blocks=0), hws.HWS_ERR_INVALID_ARG),
 ])
 def test_create_rejects(kw, status):

@@ -321,3 +321,45 @@ def test_query_scope_ties_and_single_launch_falls_back():
     for g in range(wl.G):
         assert res["sel_counts"][0, g] == 1234
         np.testing.assert_array_equal(res["sel_idx"][0, 0, g, :1234], np.arange(1234))
+
+
+# -- bf16 index (32 B per token and retrieval head) ------------------------------
+
+@pytest.mark.parametrize("n", [1, 17, 1025, 20001])
+def test_bf16_index_ragged(n):
+    _run(W.make_workload(1, n=n, index_dtype="bf16", extra={"needle_range": (0, None)}))
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (16, 2), (8, 8)])
+def test_bf16_index_group_sizes(hq, hkv):
+    _run(W.make_workload(1, n=5000, Hq=hq, Hkv=hkv, head_kinds=["retrieval"] + ["local"] * (hkv - 1),
+                         index_dtype="bf16"))
+
+
+def test_bf16_index_layer_fp8_rope_and_query_scope():
+    _run(W.make_workload(2, n=9000, batch=2, index_dtype="bf16"), verbose=False)
+    _run(W.make_workload(5, n=30000, batch=6, index_dtype="bf16"), verbose=False)
+    _run(W.make_workload(1, n=3000, rope_theta=10000.0, index_dtype="bf16"))
+    _run(W.make_workload(1, n=6000, select_scope="query", index_dtype="bf16"))
+
+
+def test_bf16_index_pool_values():
+    """The stored index is bf16(P k) with P k in fp64: equal to the oracle's
+    except where the fp64 value sits within 1e-12 of a bf16 rounding boundary
+    (the two fp64 sums may round differently there)."""
+    wl = W.make_workload(2, n=3000, batch=2, index_dtype="bf16")
+    st = DecodeSetup(wl, keep_host=True)
+    ip = st.index_pool.float().cpu().numpy()
+    for b in range(wl.B):
+        n = wl.seq_lens[b]
+        for hr, h in enumerate(wl.retrieval_heads):
+            ref = O.index_keys(st.host[b].k[:n, h], st.proj_host[h], index_bf16=True)
+            raw = st.host[b].k[:n, h].astype(np.float64) @ st.proj_host[h].astype(np.float64).T
+            got = np.stack([ip[st.block_tables_host[b, i // 16], hr, i % 16] for i in range(n)])
+            diff = got != ref
+            if diff.any():
+                # a differing element must be a near-tie of the rounding
+                ulp = 2.0 ** (np.floor(np.log2(np.abs(raw[diff]))) - 7)       # bf16 spacing at |raw|
+                mid = np.abs(np.abs(raw[diff] - ref[diff]) - ulp / 2)
+                assert (mid <= 1e-12 * np.abs(raw[diff]) + 1e-30).all()
+            assert diff.mean() < 1e-6
