@@ -29,6 +29,7 @@ from .hws_oracle import (  # noqa: F401
     decode_head_ref,
     decode_sequence_ref,
     e4m3_decode,
+    effective_rank,
     e4m3_encode,
     e4m3_table,
     fp8_store_rows,

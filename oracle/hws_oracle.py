@@ -415,3 +415,31 @@ def decode_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, proj=None, score_mode
             fixed_set=None if fixed_sets is None else fixed_sets.get(h),
             with_full_mass=with_full_mass, scope=scope, index_bf16=index_bf16)
     return res
+
+
+# ---------------------------------------------------------------------------
+# Data-free head classification  ([AoH] Methodology §1-§4)
+# ---------------------------------------------------------------------------
+
+def effective_rank(w_q, w_k) -> np.ndarray:
+    """Effective rank of every query head's query-key kernel.
+
+    [AoH] Methodology §1: the kernel of query head g (KV head h = g // G) is
+    M_g = W_K^h^T W_Q^g (d_model x d_model), with W_Q^g, W_K^h the d_head x
+    d_model projections.  §2: eff_rank = exp(-sum_k s_k log s_k) over its
+    singular values normalised to sum 1 (reading: zero singular values add
+    nothing, 0 log 0 = 0).  Computed here from the SVD of M_g itself (the
+    plain definition); low values mark concentrated spectra (retrieval heads).
+    w_q [Hq, d_head, d_model], w_k [Hkv, d_head, d_model].  Returns [Hq].
+    """
+    wq = np.asarray(w_q, dtype=np.float64)
+    wk = np.asarray(w_k, dtype=np.float64)
+    G = wq.shape[0] // wk.shape[0]
+    er = np.empty(wq.shape[0])
+    for g in range(wq.shape[0]):
+        M = wk[g // G].T @ wq[g]
+        sv = np.linalg.svd(M, compute_uv=False)
+        s = sv / sv.sum()
+        s = s[s > 0]
+        er[g] = np.exp(-(s * np.log(s)).sum())
+    return er

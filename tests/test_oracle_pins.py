@@ -473,3 +473,52 @@ def test_query_scope_brute_force_and_dense():
     d = O.decode_head_ref(q, k, k, v, kind="retrieval", score_mode="full", select_mode="top_p",
                           top_p=1.0, attn_scale=ATTN, scope="query")
     np.testing.assert_allclose(d["o64"], _sdpa(q, k, v, ATTN), rtol=0, atol=1e-6)
+
+
+# -- data-free head classification (effective rank) ------------------------------
+
+def _weights_with_spectrum(sv, d_model, rng):
+    """W_Q = U diag(sv) V^T (d_head x d_model) with W_K = [I 0]: M = W_K^T W_Q has
+    singular values sv exactly."""
+    d = len(sv)
+    U, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    V, _ = np.linalg.qr(rng.standard_normal((d_model, d)))
+    wq = U @ np.diag(sv) @ V.T
+    wk = np.zeros((d, d_model))
+    wk[np.arange(d), np.arange(d)] = 1.0
+    return wq, wk
+
+
+def test_effective_rank_closed_forms():
+    rng = np.random.default_rng(90)
+    d_model = 160
+    cases = [(np.ones(128), 128.0),                                  # flat spectrum: full rank
+             (np.r_[1.0, np.zeros(127)], 1.0),                       # rank one
+             (np.r_[2.0, 1.0, 1.0, np.zeros(125)], 2.0 ** 1.5),      # entropy of (1/2, 1/4, 1/4)
+             (np.r_[np.ones(5), np.zeros(123)] * 7.0, 5.0)]          # scale-free
+    for sv, expect in cases:
+        wq, wk = _weights_with_spectrum(sv, d_model, rng)
+        er = O.effective_rank(wq[None], wk[None])
+        assert abs(er[0] - expect) < 1e-9 * expect, (er, expect)
+
+
+def test_effective_rank_invariances_and_gqa():
+    """Orthogonal changes of the model basis and a scale leave it unchanged;
+    the query heads of a group share W_K; the Sylvester route (eigenvalues of
+    (W_Q W_Q^T)(W_K W_K^T)) gives the same singular values."""
+    rng = np.random.default_rng(91)
+    d_model = 200
+    wq = rng.standard_normal((4, 128, d_model)) * np.linspace(0.2, 3, 128)[None, :, None]
+    wk = rng.standard_normal((2, 128, d_model))
+    er = O.effective_rank(wq, wk)
+    Q, _ = np.linalg.qr(rng.standard_normal((d_model, d_model)))
+    np.testing.assert_allclose(O.effective_rank(wq @ Q, wk @ Q), er, rtol=1e-10)
+    np.testing.assert_allclose(O.effective_rank(3.0 * wq, wk), er, rtol=1e-10)
+    np.testing.assert_allclose(O.effective_rank(wq[2:], wk[1:]), er[2:], rtol=1e-12)
+    for g in range(4):
+        C = (wq[g] @ wq[g].T) @ (wk[g // 2] @ wk[g // 2].T)
+        lam = np.sort(np.clip(np.linalg.eigvals(C).real, 0, None))[::-1]
+        sv = np.sqrt(lam)
+        s = sv / sv.sum()
+        s = s[s > 0]
+        assert abs(np.exp(-(s * np.log(s)).sum()) - er[g]) < 1e-8 * er[g]
