@@ -471,6 +471,26 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   return HWS_OK;
 }
 
+hws_status hws_effective_rank_workspace(int32_t num_q_heads, int32_t num_kv_heads, size_t* bytes) {
+  if (bytes == nullptr || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return HWS_ERR_INVALID_ARG;
+  *bytes = rank_workspace_bytes(num_q_heads, num_kv_heads);
+  return HWS_OK;
+}
+
+hws_status hws_effective_rank(int32_t num_q_heads, int32_t num_kv_heads, int32_t d_model, const float* w_q,
+                              const float* w_k, float* eff_rank, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 || d_model < 1)
+    return HWS_ERR_INVALID_ARG;
+  if (w_q == nullptr || w_k == nullptr || eff_rank == nullptr) return HWS_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < rank_workspace_bytes(num_q_heads, num_kv_heads))
+    return HWS_ERR_WORKSPACE;
+  const hipError_t e = launch_effective_rank(num_q_heads, num_kv_heads, d_model, w_q, w_k, eff_rank, workspace,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HWS_OK : HWS_ERR_HIP;
+}
+
 hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode) {
   if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
   if (mode != HWS_LAUNCH_AUTO && mode != HWS_LAUNCH_MULTI && mode != HWS_LAUNCH_COOPERATIVE &&

@@ -35,6 +35,7 @@ EXPORTED = (
     "hws_set_head_kinds", "hws_classify_by_scores", "hws_get_head_kinds", "hws_bind",
     "hws_workspace_size", "hws_append", "hws_decode", "hws_profile_enable",
     "hws_profile_read", "hws_profile_stage_name", "hws_set_launch_mode",
+    "hws_effective_rank_workspace", "hws_effective_rank",
 )
 
 
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
         "hws_decode": (i32, [vp, P(DecodeArgs), vp]),
         "hws_profile_enable": (i32, [vp, i32]),
         "hws_set_launch_mode": (i32, [vp, i32]),
+        "hws_effective_rank_workspace": (i32, [i32, i32, P(ctypes.c_size_t)]),
+        "hws_effective_rank": (i32, [i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "hws_profile_read": (i32, [vp, P(ctypes.c_double), P(i32), i32]),
         "hws_profile_stage_name": (ctypes.c_char_p, [i32]),
     }
@@ -238,3 +241,22 @@ class Context:
             if name:
                 out[name] = (ms[i], calls[i])
         return out
+
+
+def effective_rank_workspace(num_q_heads: int, num_kv_heads: int) -> int:
+    n = ctypes.c_size_t()
+    st = lib().hws_effective_rank_workspace(num_q_heads, num_kv_heads, ctypes.byref(n))
+    if st != HWS_OK:
+        raise HwsError(st, f"hws_effective_rank_workspace: {status_string(st)}")
+    return n.value
+
+
+def effective_rank(w_q, w_k, eff_rank, workspace, stream=None):
+    """Effective rank per query head ([AoH] Methodology §1-§3) of device fp32
+    weights w_q [Hq, 128, d_model], w_k [Hkv, 128, d_model] into eff_rank [Hq]."""
+    hq, hkv, d_model = int(w_q.shape[0]), int(w_k.shape[0]), int(w_q.shape[2])
+    nbytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    st = lib().hws_effective_rank(hq, hkv, d_model, _ptr(w_q), _ptr(w_k), _ptr(eff_rank), _ptr(workspace),
+                                  nbytes, _stream(stream))
+    if st != HWS_OK:
+        raise HwsError(st, f"hws_effective_rank: {status_string(st)}")

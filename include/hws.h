@@ -178,6 +178,22 @@ hws_status hws_set_head_kinds(hws_ctx* ctx, const uint8_t* kinds);
 hws_status hws_classify_by_scores(hws_ctx* ctx, const float* q_head_scores,
                                   int32_t n_retrieval_kv, int32_t lower_is_retrieval);
 
+/* Effective rank of every query head's query-key kernel, from frozen
+ * weights and no data ([AoH] Methodology §1-§3): M_g = W_K^T W_Q of query
+ * head g and its KV head (d_model x d_model); eff_rank = exp of the Shannon
+ * entropy of its singular values normalised to sum 1.  A low value marks a
+ * concentrated spectrum, i.e. a retrieval head: pass the values (copied to the
+ * host) to hws_classify_by_scores with lower_is_retrieval = 1.  Computed in
+ * fp64 from the d_head x d_head matrices W_Q W_Q^T and W_K W_K^T.
+ * w_q: [num_q_heads][128][d_model] fp32, w_k: [num_kv_heads][128][d_model]
+ * fp32 (device, rows are the head's output dims); eff_rank: [num_q_heads]
+ * fp32 (device); workspace: hws_effective_rank_workspace() bytes (device).
+ * No context is needed.  Asynchronous on `stream`. */
+hws_status hws_effective_rank_workspace(int32_t num_q_heads, int32_t num_kv_heads, size_t* bytes);
+hws_status hws_effective_rank(int32_t num_q_heads, int32_t num_kv_heads, int32_t d_model,
+                              const float* w_q, const float* w_k, float* eff_rank,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Copy the current head kinds into kinds[Hkv] (host). */
 hws_status hws_get_head_kinds(const hws_ctx* ctx, uint8_t* kinds);
 

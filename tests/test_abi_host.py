@@ -222,3 +222,18 @@ def test_workspace_size_rules():
     with pytest.raises(hws.HwsError) as e:
         _decode(c, max_seq_len=500, workspace=_FakeT(nbytes=n1), select_scope=hws.HWS_SCOPE_QUERY_HEAD)
     assert e.value.status == hws.HWS_ERR_WORKSPACE
+
+
+def test_effective_rank_validation_without_gpu():
+    assert hws.effective_rank_workspace(8, 2) == (3 * 8 + 2) * 128 * 128 * 8
+    for hq, hkv in ((0, 1), (8, 3), (4, 0)):
+        with pytest.raises(hws.HwsError) as e:
+            hws.effective_rank_workspace(hq, hkv)
+        assert e.value.status == hws.HWS_ERR_INVALID_ARG
+    L = hws.lib()
+    ws = 1 << 30
+    assert L.hws_effective_rank(8, 2, 0, 4096, 4096, 4096, 4096, ws, None) == hws.HWS_ERR_INVALID_ARG
+    assert L.hws_effective_rank(8, 3, 64, 4096, 4096, 4096, 4096, ws, None) == hws.HWS_ERR_INVALID_ARG
+    assert L.hws_effective_rank(8, 2, 64, None, 4096, 4096, 4096, ws, None) == hws.HWS_ERR_INVALID_ARG
+    assert L.hws_effective_rank(8, 2, 64, 4096, 4096, 4096, 4096, 100, None) == hws.HWS_ERR_WORKSPACE
+    assert L.hws_effective_rank(8, 2, 64, 4096, 4096, 4096, None, ws, None) == hws.HWS_ERR_WORKSPACE
