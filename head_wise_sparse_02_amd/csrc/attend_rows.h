@@ -21,8 +21,26 @@ struct AttRB {
   static constexpr int value = MODE == 1 ? 8 : (G <= 2 ? 8 : (G == 4 ? 4 : 2));
 };
 
+// Where local-head row `tok` of sequence b (local head number l) is stored:
+// its 16-row page pg and its index ii (slot ii % 16 of the page).  Without a
+// ring these are the sequence's cache page and the position; with a ring,
+// the ring row of the token (sinks first, then the window modulo its length)
+// in the sequence's ring slot, or pg = -1 for a slot out of range.
+__device__ __forceinline__ void local_row_at(const DecodeParams& p, int b, int l, int tok, int& ii, int& pg) {
+  if (p.ring_rows > 0) {
+    const int slot = p.seq_slots[b];
+    const int rr = tok < p.n_sink ? tok : p.n_sink + (p.window > 0 ? (tok - p.n_sink) % p.window : 0);
+    ii = rr;
+    pg = (unsigned)slot < (unsigned)p.max_seqs ? (int)((((long long)slot * p.nL + l) * p.ring_rows + rr) >> 4) : -1;
+  } else {
+    ii = tok;
+    pg = p.block_tables[(size_t)b * p.max_blocks + (tok >> 4)];
+  }
+}
+
 // Row r of the list: retrieval rows are offsets (from lo) in `rows`, whose
-// page is pages[offset / 16]; local rows are tokens ltok[r] on page lpg[r].
+// page is pages[offset / 16]; local rows are at index ltok[r] of page lpg[r]
+// (local_row_at), in the ring pools when there is a ring.
 // MODE 0: logits q.k from K rows; MODE 1: retrieval heads only, logits from
 // the stored full-dim scores; MODE 2: both (scores for retrieval heads).
 // RET: the rows are known to be a retrieval head's (no K path compiled in).
@@ -62,6 +80,14 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
     }
   }
   const float* sc = use_scores ? p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G : nullptr;
+  // the rows' pools: the pages (Hp heads each, this head at pool_slot[h]) or
+  // the local ring (one head per page)
+  const bool ring = !is_ret && p.ring_rows > 0;
+  const void* kpool = ring ? p.lk_pool : p.k_pool;
+  const void* vpool = ring ? p.lv_pool : p.v_pool;
+  const int hstride = ring ? 1 : p.Hp;
+  const int hslot = ring ? 0 : p.pool_slot[h];
+  const unsigned plim = ring ? (unsigned)p.ring_pages : (unsigned)p.num_blocks;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = NEG_INF;
@@ -90,7 +116,7 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
     }
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      ok[u] = r0 + u < nrows && (unsigned)pg[u] < (unsigned)p.num_blocks;
+      ok[u] = r0 + u < nrows && (unsigned)pg[u] < plim;
       if (!ok[u]) { pg[u] = 0; ii[u] = 0; }
     }
 
@@ -101,11 +127,11 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
     float ks[RB], vs[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u)
-      load_row8<FP8>(p.v_pool, ((size_t)pg[u] * p.Hkv + h) * BS + (ii[u] & 15), sub, vv[u]);
+      load_row8<FP8>(vpool, ((size_t)pg[u] * hstride + hslot) * BS + (ii[u] & 15), sub, vv[u]);
     if (FP8) {
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
-        const float2 s2 = *reinterpret_cast<const float2*>(p.kv_scales + ((size_t)pg[u] * p.Hkv + h) * 2);
+        const float2 s2 = *reinterpret_cast<const float2*>(p.kv_scales + ((size_t)pg[u] * hstride + hslot) * 2);
         ks[u] = s2.x;
         vs[u] = s2.y;
       }
@@ -134,7 +160,7 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
     } else if (NEED_K) {
 #pragma unroll
       for (int u = 0; u < RB; ++u)
-        load_krow8<FP8>(p.k_pool, (size_t)pg[u] * p.Hkv + h, ii[u] & 15, sub, kx[NEED_K ? u : 0]);
+        load_krow8<FP8>(kpool, (size_t)pg[u] * hstride + hslot, ii[u] & 15, sub, kx[NEED_K ? u : 0]);
     }
 
     // logits (log2 units), masked rows at -inf

@@ -48,6 +48,10 @@ struct hws_ctx {
   signed char ret_slot[MAX_KV];
   signed char ret_head[MAX_KV];
   signed char loc_head[MAX_KV];
+  signed char pool_slot[MAX_KV];   // head -> index within a page (-1: local head in the ring)
+  signed char loc_slot[MAX_KV];    // head -> local head number (-1: retrieval head)
+  int Hp = 0;                      // heads per page
+  int ring_rows = 0;               // local ring rows per (slot, local head); 0 = no ring
   bool appended = false, bound = false;
   hws_buffers buf{};
   std::string err;
@@ -76,17 +80,26 @@ hws_status hip_fail(hws_ctx* ctx, hipError_t e, const char* what) {
   return fail(ctx, HWS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Head numbering: retrieval and local heads in KV-head order; with a local
+// ring the pages hold only the retrieval heads.
 void rebuild_slots(hws_ctx* c) {
   c->nR = c->nL = 0;
-  for (int h = 0; h < MAX_KV; ++h) { c->ret_slot[h] = -1; c->ret_head[h] = -1; c->loc_head[h] = -1; }
+  for (int h = 0; h < MAX_KV; ++h) {
+    c->ret_slot[h] = c->ret_head[h] = c->loc_head[h] = c->pool_slot[h] = c->loc_slot[h] = -1;
+  }
   for (int h = 0; h < c->cfg.num_kv_heads; ++h) {
     if (c->kinds[h] == HWS_HEAD_RETRIEVAL) {
       c->ret_slot[h] = (signed char)c->nR;
       c->ret_head[c->nR++] = (signed char)h;
     } else {
+      c->loc_slot[h] = (signed char)c->nL;
       c->loc_head[c->nL++] = (signed char)h;
     }
   }
+  const bool ring = c->cfg.local_ring != 0;
+  c->Hp = ring ? c->nR : c->cfg.num_kv_heads;
+  for (int h = 0; h < c->cfg.num_kv_heads; ++h) c->pool_slot[h] = ring ? c->ret_slot[h] : (signed char)h;
+  c->ring_rows = ring ? (c->cfg.n_sink + c->cfg.window + BS - 1) / BS * BS : 0;
 }
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -203,6 +216,13 @@ hws_status hws_create(const hws_config* cfg, hws_ctx** out) {
   if (c.kv_dtype != HWS_KV_BF16 && c.kv_dtype != HWS_KV_FP8_E4M3) return HWS_ERR_INVALID_ARG;
   if (c.index_dtype != HWS_INDEX_F32 && c.index_dtype != HWS_INDEX_BF16) return HWS_ERR_INVALID_ARG;
   if (c.n_sink < 0 || c.window < 0 || (long long)c.n_sink + c.window < 1) return HWS_ERR_INVALID_ARG;
+  if (c.local_ring != 0 && c.local_ring != 1) return HWS_ERR_INVALID_ARG;
+  if (c.local_ring) {
+    if (c.kv_dtype != HWS_KV_BF16) return HWS_ERR_UNSUPPORTED;   // fp8 scales live with pages
+    if (c.max_seqs < 1 || (long long)c.n_sink + c.window > (1 << 26)) return HWS_ERR_INVALID_ARG;
+    const long long rows = ((long long)c.n_sink + c.window + BS - 1) / BS * BS;
+    if ((long long)c.max_seqs * c.num_kv_heads * rows / BS >= (1LL << 31)) return HWS_ERR_INVALID_ARG;
+  }
   if (!finite_f(c.attn_scale) || !(c.attn_scale > 0.f) || !finite_f(c.index_scale) ||
       !finite_f(c.rope_theta) || c.rope_theta < 0.f)
     return HWS_ERR_INVALID_ARG;
@@ -277,6 +297,8 @@ hws_status hws_bind(hws_ctx* ctx, const hws_buffers* buf) {
   if (buf->k_pool == nullptr || buf->v_pool == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "k_pool / v_pool is NULL");
   if (ctx->cfg.kv_dtype == HWS_KV_FP8_E4M3 && buf->kv_scales == nullptr)
     return fail(ctx, HWS_ERR_INVALID_ARG, "fp8 cache needs kv_scales");
+  if (ctx->cfg.local_ring && (buf->local_k_pool == nullptr || buf->local_v_pool == nullptr))
+    return fail(ctx, HWS_ERR_INVALID_ARG, "local_ring needs local_k_pool and local_v_pool");
   ctx->buf = *buf;
   ctx->bound = true;
   return HWS_OK;
@@ -295,7 +317,8 @@ hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq
 }
 
 hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t* block_tables,
-                      const int32_t* start_pos, const void* k, const void* v, void* stream) {
+                      const int32_t* start_pos, const int32_t* seq_slots, const void* k, const void* v,
+                      void* stream) {
   if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
   if (!ctx->bound) return fail(ctx, HWS_ERR_STATE, "append before bind");
   if (n_seq < 1 || n_tok < 1) return fail(ctx, HWS_ERR_INVALID_ARG, "n_seq = %d, n_tok = %d", n_seq, n_tok);
@@ -305,6 +328,8 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
     return fail(ctx, HWS_ERR_CAPACITY, "n_tok = %d exceeds the block table", n_tok);
   if (ctx->nR > 0 && (ctx->buf.index_pool == nullptr || ctx->buf.proj == nullptr))
     return fail(ctx, HWS_ERR_INVALID_ARG, "retrieval heads need index_pool and proj");
+  if (ctx->ring_rows > 0 && ctx->nL > 0 && seq_slots == nullptr)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "local_ring needs seq_slots");
   AppendParams p{};
   p.n_seq = n_seq;
   p.n_tok = n_tok;
@@ -320,10 +345,20 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
   p.k_pool = ctx->buf.k_pool;
   p.v_pool = ctx->buf.v_pool;
   p.kv_scales = ctx->buf.kv_scales;
+  p.Hp = ctx->Hp;
+  p.n_sink = ctx->cfg.n_sink;
+  p.window = ctx->cfg.window;
+  p.ring_rows = ctx->ring_rows;
+  p.max_seqs = ctx->cfg.max_seqs;
+  p.seq_slots = seq_slots;
+  p.lk_pool = ctx->buf.local_k_pool;
+  p.lv_pool = ctx->buf.local_v_pool;
   p.index_pool = ctx->buf.index_pool;
   p.index_bf16 = ctx->cfg.index_dtype == HWS_INDEX_BF16 ? 1 : 0;
   p.proj = ctx->buf.proj;
   std::memcpy(p.ret_slot, ctx->ret_slot, sizeof(p.ret_slot));
+  std::memcpy(p.pool_slot, ctx->pool_slot, sizeof(p.pool_slot));
+  std::memcpy(p.loc_slot, ctx->loc_slot, sizeof(p.loc_slot));
   ctx->appended = true;
   const hipError_t e = launch_append(p, ctx->cfg.kv_dtype == HWS_KV_FP8_E4M3, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(ctx, e, "append launch");
@@ -356,6 +391,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
       return fail(ctx, HWS_ERR_INVALID_ARG, "index scoring needs index_pool and proj");
   }
   if (a->sel_idx != nullptr && a->sel_cap < 1) return fail(ctx, HWS_ERR_INVALID_ARG, "sel_cap = %d", a->sel_cap);
+  if (ctx->ring_rows > 0 && ctx->nL > 0 && a->seq_slots == nullptr)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "local_ring needs seq_slots");
   if (ctx->nR > 0 && a->score_mode == HWS_SCORE_FULL && c.kv_dtype != HWS_KV_BF16)
     return fail(ctx, HWS_ERR_UNSUPPORTED, "full-dim scoring needs a bf16 cache");
   const bool rope = c.rope_theta > 0.f;
@@ -394,6 +431,13 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.k_pool = ctx->buf.k_pool;
   p.v_pool = ctx->buf.v_pool;
   p.kv_scales = c.kv_dtype == HWS_KV_FP8_E4M3 ? ctx->buf.kv_scales : nullptr;
+  p.Hp = ctx->Hp;
+  p.ring_rows = ctx->ring_rows;
+  p.ring_pages = (int)((long long)c.max_seqs * ctx->nL * ctx->ring_rows / BS);
+  p.max_seqs = c.max_seqs;
+  p.seq_slots = a->seq_slots;
+  p.lk_pool = ctx->buf.local_k_pool;
+  p.lv_pool = ctx->buf.local_v_pool;
   p.index_pool = ctx->buf.index_pool;
   p.index_bf16 = ctx->cfg.index_dtype == HWS_INDEX_BF16 ? 1 : 0;
   p.proj = ctx->buf.proj;
@@ -424,6 +468,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   std::memcpy(p.ret_slot, ctx->ret_slot, sizeof(p.ret_slot));
   std::memcpy(p.ret_head, ctx->ret_head, sizeof(p.ret_head));
   std::memcpy(p.loc_head, ctx->loc_head, sizeof(p.loc_head));
+  std::memcpy(p.pool_slot, ctx->pool_slot, sizeof(p.pool_slot));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;

@@ -80,9 +80,16 @@ struct DecodeParams {
   const int* seq_lens;          // [B]
   const float* top_p;           // [B]
   const int* top_k;             // [B]
-  const void* k_pool;
+  const void* k_pool;           // [blocks][Hp][16 x 128] (pages hold Hp heads)
   const void* v_pool;
   const float* kv_scales;
+  int Hp;                       // heads per page: Hkv, or nR with a local ring
+  int ring_rows;                // local ring: rows per (slot, local head), a multiple of 16; 0 = no ring
+  int ring_pages;               // local ring: 16-row pages in each ring pool
+  int max_seqs;
+  const int* seq_slots;         // [B] ring slot of each sequence (ring only)
+  const void* lk_pool;          // [max_seqs][nL][ring_rows][128] ring pools (K in 16-row pages)
+  const void* lv_pool;
   const void* index_pool;       // [blocks][nR][16][16] fp32, or bf16 when index_bf16
   int index_bf16;
   const float* proj;
@@ -107,6 +114,7 @@ struct DecodeParams {
   signed char ret_slot[MAX_KV];
   signed char ret_head[MAX_KV];
   signed char loc_head[MAX_KV];
+  signed char pool_slot[MAX_KV];  // head's index within a page (-1: not in the pages)
 };
 
 struct AppendParams {
@@ -119,10 +127,18 @@ struct AppendParams {
   void* k_pool;
   void* v_pool;
   float* kv_scales;
+  int Hp;                       // heads per page
+  int n_sink, window;
+  int ring_rows, max_seqs;      // local ring (ring_rows = 0: none)
+  const int* seq_slots;         // [n_seq] ring slots
+  void* lk_pool;
+  void* lv_pool;
   void* index_pool;             // fp32, or bf16 when index_bf16
   int index_bf16;
   const float* proj;
   signed char ret_slot[MAX_KV];
+  signed char pool_slot[MAX_KV];
+  signed char loc_slot[MAX_KV];   // local head's index among the local heads
 };
 
 // Launch a kernel; with timing events the start/stop timestamps are taken

@@ -10,6 +10,12 @@
 // bf16.  FP8 pages hold OCP e4m3fn codes of x / scale; a call that writes
 // slot 0 of a page sets that page's scale to amax/448 over the rows it
 // writes there (1.0 if they are all zero); later calls keep the scale.
+//
+// Local ring ([RTPurbo] Methodology §1: a local head attends to its sinks and
+// its window only): local heads write the sequence's ring slot instead of the
+// pages, and only the rows a decode can still read, i.e. the sinks and the
+// last `window` positions of the call (distinct ring rows, so no two writers
+// meet); older window rows are overwritten as the sequence grows.
 #include "hws_device.h"
 
 namespace hws {
@@ -32,8 +38,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int blk_l = p0 / BS + jb;
   const int lo = max(p0, blk_l * BS), hi = min(p0 + p.n_tok, blk_l * BS + BS);
   if (lo >= hi || blk_l >= p.max_blocks) return;
-  const int phys = p.block_tables[(size_t)s * p.max_blocks + blk_l];
-  if ((unsigned)phys >= (unsigned)p.num_blocks) return;
+  const int hr = p.ret_slot[h];
+  const bool ring = p.ring_rows > 0 && hr < 0;
+  int phys = 0, seq_slot = 0;
+  if (ring) {
+    seq_slot = p.seq_slots[s];
+    if ((unsigned)seq_slot >= (unsigned)p.max_seqs) return;
+    if (lo >= p.n_sink && hi <= p0 + p.n_tok - p.window) return;   // no row of this page is kept
+  } else {
+    phys = p.block_tables[(size_t)s * p.max_blocks + blk_l];
+    if ((unsigned)phys >= (unsigned)p.num_blocks) return;
+  }
   const int nrows = hi - lo, slot0 = lo - blk_l * BS;
 
   __shared__ float ks[BS][D], vs[BS][D];
@@ -46,7 +61,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
   __syncthreads();
 
-  const int hr = p.ret_slot[h];
   if (hr >= 0) {
     const int r = tid >> 4, j = tid & 15;
     if (r < nrows) {
@@ -79,8 +93,24 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     __syncthreads();
   }
 
-  const size_t row0 = ((size_t)phys * p.Hkv + h) * BS + slot0;
-  const size_t page0 = ((size_t)phys * p.Hkv + h) * BS * D;      // K page (blocked layout)
+  if (ring) {                       // bf16 only
+    uint16_t* kp = reinterpret_cast<uint16_t*>(p.lk_pool);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(p.lv_pool);
+    const int keep_from = p0 + p.n_tok - p.window;
+    const size_t ring0 = ((size_t)seq_slot * (p.Hkv - p.nR) + p.loc_slot[h]) * p.ring_rows;
+    for (int e = tid; e < nrows * D; e += 256) {
+      const int r = e / D, d = e % D, t = lo + r;
+      if (t >= p.n_sink && t < keep_from) continue;
+      const int rr = t < p.n_sink ? t : p.n_sink + (t - p.n_sink) % p.window;
+      const size_t grow = ring0 + rr;
+      kp[(grow >> 4) * (BS * D) + kpage_off(rr & 15, d)] = f32_to_bf16_rne(ks[r][d]);
+      vp[grow * D + d] = f32_to_bf16_rne(vs[r][d]);
+    }
+    return;
+  }
+
+  const size_t row0 = ((size_t)phys * p.Hp + p.pool_slot[h]) * BS + slot0;
+  const size_t page0 = ((size_t)phys * p.Hp + p.pool_slot[h]) * BS * D;      // K page (blocked layout)
   if (!FP8) {
     uint16_t* kp = reinterpret_cast<uint16_t*>(p.k_pool);
     uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool);
@@ -90,7 +120,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       vp[(row0 + r) * D + d] = f32_to_bf16_rne(vs[r][d]);
     }
   } else {
-    float* sc = p.kv_scales + ((size_t)phys * p.Hkv + h) * 2;
+    float* sc = p.kv_scales + ((size_t)phys * p.Hp + p.pool_slot[h]) * 2;
     float kscale, vscale;
     if (slot0 == 0) {
       float ka = 0.f, va = 0.f;

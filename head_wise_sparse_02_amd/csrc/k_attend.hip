@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   const int proc = tid >> 4, sub = tid & 15;     // 16 row processors of 16 lanes
   const int w = blockIdx.x;
   const int nret = p.B * p.nR * p.ncR;
-  int b, h, split, hr = -1;
+  int b, h, split, hr = -1, lh = 0;              // lh: local head number
   if (w < nret) {
     split = w % p.ncR;
     const int t = w / p.ncR;
@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     split = w2 % p.ncL;
     const int t = w2 / p.ncL;
     b = t / p.nL;
-    h = p.loc_head[t % p.nL];
+    lh = t % p.nL;
+    h = p.loc_head[lh];
   }
   const bool is_ret = hr >= 0;
   const int N = min(p.seq_lens[b], p.Nmax);
@@ -166,9 +167,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     const int hi = min(L, llo + LOCAL_CHUNK);
     const int r = llo + tid;
     if (r < hi) {
-      const int tok = r < L1 ? r : start2 + (r - L1);
-      ltok_s[tid] = tok;
-      pages_s[tid] = bt[tok >> 4];
+      local_row_at(p, b, lh, r < L1 ? r : start2 + (r - L1), ltok_s[tid], pages_s[tid]);
     }
     nrows = max(0, hi - llo);
     __syncthreads();

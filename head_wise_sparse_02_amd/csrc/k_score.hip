@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
       if (tpage[u] < N) blk = bt[pg];
       if ((unsigned)blk < (unsigned)p.num_blocks) {
         // blocked page: step s of all 16 rows is one contiguous 1 KiB run
-        const uint16_t* src = kpool + ((size_t)blk * p.Hkv + h) * (BS * D) + row * 32 + 8 * quad;
+        const uint16_t* src = kpool + ((size_t)blk * p.Hp + p.pool_slot[h]) * (BS * D) + row * 32 + 8 * quad;
 #pragma unroll
         for (int s = 0; s < 4; ++s) bfrag[u][s] = __builtin_bit_cast(bf16x8, load_nt16(src + 512 * s));
       } else {
@@ -353,8 +353,8 @@ __global__ __launch_bounds__(256) void score_full_g4_kernel(DecodeParams p) {
   const int page0 = c * (CH / BS) + wave * PW;
   const int my_blk = (lane < PW && (page0 + lane) * BS < N) ? bt[page0 + lane] : -1;
   const int npages = min(PW, max(0, (N - page0 * BS + BS - 1) / BS));
-  const size_t page_stride = (size_t)p.Hkv * (BS * D);
-  const uint16_t* kbase = kpool + (size_t)h * (BS * D) + (size_t)row * 32 + 8 * quad;
+  const size_t page_stride = (size_t)p.Hp * (BS * D);
+  const uint16_t* kbase = kpool + (size_t)p.pool_slot[h] * (BS * D) + (size_t)row * 32 + 8 * quad;
 
   // GP pages per step; invalid pages read page 0 and are zeroed after the MFMA
   bf16x8 cur[GP][4], nxt[GP][4];

@@ -426,9 +426,7 @@ __device__ __forceinline__ int local_rows(const DecodeParams& p, TailLds& S, int
   const int tid = threadIdx.x;
   if (tid < nrows) {
     const int r = llo + tid;
-    const int tok = r < L1 ? r : start2 + (r - L1);
-    S.ltok[tid] = tok;
-    S.lpg[tid] = p.block_tables[(size_t)b * p.max_blocks + (tok >> 4)];
+    local_row_at(p, b, t % p.nL, r < L1 ? r : start2 + (r - L1), S.ltok[tid], S.lpg[tid]);
   }
   return nrows;
 }
@@ -777,8 +775,9 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   S.pages[0][wave * FPW + lane] = blkA;
   S.pages[0][wave * FPW + 64 + lane] = blkB;
   const int ngroups = min(TPT, max(0, (N - page0 * BS + 4 * BS - 1) / (4 * BS)));
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(p.k_pool) + (size_t)h * (BS * D) + (size_t)row * 32 + 8 * quad;
-  const size_t page_stride = (size_t)p.Hkv * (BS * D);
+  const uint16_t* kbase =
+      reinterpret_cast<const uint16_t*>(p.k_pool) + (size_t)p.pool_slot[h] * (BS * D) + (size_t)row * 32 + 8 * quad;
+  const size_t page_stride = (size_t)p.Hp * (BS * D);
   const float c2 = p.c2_score;
   float x[TPT][G];
   float m[G], sm[G];

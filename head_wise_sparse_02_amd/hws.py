@@ -48,7 +48,8 @@ class HwsError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_q_heads", "num_kv_heads", "head_dim", "index_dim", "block_size", "num_blocks",
-        "max_blocks_per_seq", "kv_dtype", "index_dtype", "n_sink", "window")] + [
+        "max_blocks_per_seq", "kv_dtype", "index_dtype", "n_sink", "window", "local_ring",
+        "max_seqs")] + [
         ("attn_scale", ctypes.c_float), ("index_scale", ctypes.c_float),
         ("rope_theta", ctypes.c_float)]
 
@@ -56,14 +57,15 @@ class Config(ctypes.Structure):
 class Buffers(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("kv_scales", ctypes.c_void_p), ("index_pool", ctypes.c_void_p),
-                ("proj", ctypes.c_void_p)]
+                ("proj", ctypes.c_void_p), ("local_k_pool", ctypes.c_void_p),
+                ("local_v_pool", ctypes.c_void_p)]
 
 
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("select_mode", ctypes.c_int32), ("score_mode", ctypes.c_int32),
                 ("select_scope", ctypes.c_int32), ("q", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
-                ("seq_lens", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("seq_slots", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
                 ("top_k", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("sel_counts", ctypes.c_void_p), ("sel_idx", ctypes.c_void_p),
                 ("sel_cap", ctypes.c_int32), ("scores", ctypes.c_void_p),
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
         "hws_get_head_kinds": (i32, [vp, P(ctypes.c_uint8)]),
         "hws_bind": (i32, [vp, P(Buffers)]),
         "hws_workspace_size": (i32, [vp, i32, i32, i32, i32, P(ctypes.c_size_t)]),
-        "hws_append": (i32, [vp, i32, i32, vp, vp, vp, vp, vp]),
+        "hws_append": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp]),
         "hws_decode": (i32, [vp, P(DecodeArgs), vp]),
         "hws_profile_enable": (i32, [vp, i32]),
         "hws_set_launch_mode": (i32, [vp, i32]),
@@ -138,12 +140,12 @@ class Context:
     def __init__(self, *, num_q_heads: int, num_kv_heads: int, num_blocks: int,
                  max_blocks_per_seq: int, n_sink: int, window: int, attn_scale: float,
                  index_scale: float = 1.0, rope_theta: float = 0.0, kv_dtype: int = HWS_KV_BF16,
-                 index_dtype: int = HWS_INDEX_F32, head_dim: int = 128, index_dim: int = 16,
-                 block_size: int = 16):
+                 index_dtype: int = HWS_INDEX_F32, local_ring: bool = False, max_seqs: int = 0,
+                 head_dim: int = 128, index_dim: int = 16, block_size: int = 16):
         self._L = lib()
         self.cfg = Config(num_q_heads, num_kv_heads, head_dim, index_dim, block_size, num_blocks,
-                          max_blocks_per_seq, kv_dtype, index_dtype, n_sink, window, attn_scale,
-                          index_scale, rope_theta)
+                          max_blocks_per_seq, kv_dtype, index_dtype, n_sink, window, int(bool(local_ring)),
+                          max_seqs, attn_scale, index_scale, rope_theta)
         h = ctypes.c_void_p()
         st = self._L.hws_create(ctypes.byref(self.cfg), ctypes.byref(h))
         if st != HWS_OK:
@@ -184,8 +186,10 @@ class Context:
         return list(arr)
 
     # -- memory --------------------------------------------------------------
-    def bind(self, k_pool, v_pool, kv_scales=None, index_pool=None, proj=None):
-        self._buf = Buffers(_ptr(k_pool), _ptr(v_pool), _ptr(kv_scales), _ptr(index_pool), _ptr(proj))
+    def bind(self, k_pool, v_pool, kv_scales=None, index_pool=None, proj=None, local_k_pool=None,
+             local_v_pool=None):
+        self._buf = Buffers(_ptr(k_pool), _ptr(v_pool), _ptr(kv_scales), _ptr(index_pool), _ptr(proj),
+                            _ptr(local_k_pool), _ptr(local_v_pool))
         self._check(self._L.hws_bind(self.handle, ctypes.byref(self._buf)), "hws_bind")
 
     def workspace_size(self, batch: int, max_seq_len: int, score_mode: int, select_scope: int = 0) -> int:
@@ -195,21 +199,24 @@ class Context:
         return n.value
 
     # -- device work -----------------------------------------------------------
-    def append(self, block_tables, start_pos, k, v, stream=None):
-        """k, v: [n_seq, n_tok, Hkv, 128] bf16 device tensors."""
+    def append(self, block_tables, start_pos, k, v, stream=None, seq_slots=None):
+        """k, v: [n_seq, n_tok, Hkv, 128] bf16 device tensors; seq_slots: [n_seq]
+        int32 ring slots (local ring only)."""
         n_seq, n_tok = int(k.shape[0]), int(k.shape[1])
         self._check(self._L.hws_append(self.handle, n_seq, n_tok, _ptr(block_tables), _ptr(start_pos),
-                                       _ptr(k), _ptr(v), _stream(stream)), "hws_append")
+                                       _ptr(seq_slots), _ptr(k), _ptr(v), _stream(stream)), "hws_append")
 
     def decode(self, *, q, block_tables, seq_lens, max_seq_len: int, select_mode: int,
                score_mode: int, out, workspace, top_p=None, top_k=None, lse=None,
-               sel_counts=None, sel_idx=None, scores=None, stream=None, select_scope: int = 0):
+               sel_counts=None, sel_idx=None, scores=None, stream=None, select_scope: int = 0,
+               seq_slots=None):
         a = DecodeArgs()
         a.select_scope = int(select_scope)
         a.batch = int(q.shape[0]) if q is not None else 0
         a.max_seq_len = int(max_seq_len)
         a.select_mode, a.score_mode = int(select_mode), int(score_mode)
         a.q, a.block_tables, a.seq_lens = _ptr(q), _ptr(block_tables), _ptr(seq_lens)
+        a.seq_slots = _ptr(seq_slots)
         a.top_p, a.top_k = _ptr(top_p), _ptr(top_k)
         a.out, a.lse, a.sel_counts = _ptr(out), _ptr(lse), _ptr(sel_counts)
         a.sel_idx = _ptr(sel_idx)

@@ -23,9 +23,20 @@ def append_segments(n: int) -> list:
     return [(0, n - 1), (n - 1, 1)] if n > 1 else [(0, 1)]
 
 
+def ring_rows(n_sink: int, window: int) -> int:
+    """Rows per (sequence slot, local head) of the local ring: sinks + window, to 16."""
+    return (n_sink + window + 15) // 16 * 16
+
+
 class DecodeSetup:
+    """``segments``: optional function n -> [(start, count)] giving the append
+    calls of a sequence of length n (default ``append_segments``).  With
+    ``wl.local_ring`` the pages hold only the retrieval heads and the local
+    heads live in ring pools of ``max_seqs`` = B + 3 slots, assigned to the
+    sequences by a seeded permutation."""
+
     def __init__(self, wl: Workload, device: str = "cuda", spare_pages: int = 2,
-                 keep_host: bool = False, sequences=None):
+                 keep_host: bool = False, sequences=None, segments=None):
         self.wl = wl
         self.dev = torch.device(device)
         B, Hkv, Hq, d = wl.B, wl.Hkv, wl.Hq, wl.d
@@ -34,23 +45,38 @@ class DecodeSetup:
         pages = [(n + 15) // 16 + spare_pages for n in wl.seq_lens]
         self.num_blocks = int(sum(pages))
         self.fp8 = wl.kv_dtype == "fp8"
+        self.ring = bool(wl.local_ring)
+        self.max_seqs = B + 3 if self.ring else 0
+        n_sink_c = max(wl.n_sink, 0)
+        window_c = max(wl.window, 1 if wl.n_sink == 0 else 0)
         self.ctx = hws.Context(
             num_q_heads=Hq, num_kv_heads=Hkv, num_blocks=self.num_blocks,
-            max_blocks_per_seq=self.max_blocks, n_sink=max(wl.n_sink, 0),
-            window=max(wl.window, 1 if wl.n_sink == 0 else 0),
+            max_blocks_per_seq=self.max_blocks, n_sink=n_sink_c, window=window_c,
+            local_ring=self.ring, max_seqs=self.max_seqs,
             attn_scale=wl.attn_scale, index_scale=wl.index_scale, rope_theta=wl.rope_theta,
             kv_dtype=hws.HWS_KV_FP8_E4M3 if self.fp8 else hws.HWS_KV_BF16,
             index_dtype=hws.HWS_INDEX_BF16 if wl.index_dtype == "bf16" else hws.HWS_INDEX_F32)
         self.ctx.set_head_kinds([KIND_CODE[k] for k in wl.head_kinds])
         self.nR = len(wl.retrieval_heads)
+        self.nL = Hkv - self.nR
 
         # pools and a seeded random page assignment (pages are not contiguous)
         kv_dt = torch.uint8 if self.fp8 else torch.bfloat16
         # K pages are dim-blocked [4][16][32]; V pages are row-major [16][128]
-        self.k_pool = torch.zeros((self.num_blocks, Hkv, 4, 16, 32), dtype=kv_dt, device=self.dev)
-        self.v_pool = torch.zeros((self.num_blocks, Hkv, 16, d), dtype=kv_dt, device=self.dev)
-        self.kv_scales = (torch.ones((self.num_blocks, Hkv, 2), dtype=torch.float32, device=self.dev)
+        Hp = max(self.nR, 1) if self.ring else Hkv          # heads per page
+        self.k_pool = torch.zeros((self.num_blocks, Hp, 4, 16, 32), dtype=kv_dt, device=self.dev)
+        self.v_pool = torch.zeros((self.num_blocks, Hp, 16, d), dtype=kv_dt, device=self.dev)
+        self.kv_scales = (torch.ones((self.num_blocks, Hp, 2), dtype=torch.float32, device=self.dev)
                           if self.fp8 else None)
+        self.local_k_pool = self.local_v_pool = self.seq_slots = None
+        if self.ring:
+            W = ring_rows(n_sink_c, window_c)
+            nl = max(self.nL, 1)
+            self.local_k_pool = torch.zeros((self.max_seqs, nl, W // 16, 4, 16, 32), dtype=kv_dt, device=self.dev)
+            self.local_v_pool = torch.zeros((self.max_seqs, nl, W, d), dtype=kv_dt, device=self.dev)
+            srng = np.random.default_rng(np.random.SeedSequence([wl.cfg, wl.seed, 3001]))
+            self.seq_slots_host = srng.permutation(self.max_seqs)[:B].astype(np.int32)
+            self.seq_slots = torch.from_numpy(self.seq_slots_host).to(self.dev)
         idx_dt = torch.bfloat16 if wl.index_dtype == "bf16" else torch.float32
         self.index_pool = (torch.zeros((self.num_blocks, max(self.nR, 1), 16, 16), dtype=idx_dt,
                                        device=self.dev) if self.nR else None)
@@ -67,7 +93,7 @@ class DecodeSetup:
         self.block_tables = torch.from_numpy(bt).to(self.dev)
         self.seq_lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=self.dev)
         self.ctx.bind(self.k_pool, self.v_pool, self.kv_scales, self.index_pool,
-                      self.proj if self.nR else None)
+                      self.proj if self.nR else None, self.local_k_pool, self.local_v_pool)
 
         # fill the cache, sequence by sequence
         self.q_host = np.zeros((B, Hq, d), dtype=np.float32)
@@ -79,10 +105,11 @@ class DecodeSetup:
                 self.host.append(seq)
             k = torch.from_numpy(seq.k).to(torch.bfloat16).to(self.dev)[None]
             v = torch.from_numpy(seq.v).to(torch.bfloat16).to(self.dev)[None]
-            for start, cnt in append_segments(wl.seq_lens[b]):
+            for start, cnt in (segments or append_segments)(wl.seq_lens[b]):
                 sp = torch.tensor([start], dtype=torch.int32, device=self.dev)
                 self.ctx.append(self.block_tables[b:b + 1], sp, k[:, start:start + cnt].contiguous(),
-                                v[:, start:start + cnt].contiguous())
+                                v[:, start:start + cnt].contiguous(),
+                                seq_slots=None if self.seq_slots is None else self.seq_slots[b:b + 1])
             del k, v
         torch.cuda.synchronize(self.dev)
         self.q = torch.from_numpy(self.q_host).to(torch.bfloat16).to(self.dev)
@@ -113,7 +140,7 @@ class DecodeSetup:
                         score_mode=self.score_mode, out=self.out, workspace=self.workspace,
                         top_p=self.top_p, top_k=self.top_k, lse=self.lse,
                         sel_counts=self.sel_counts, sel_idx=sel_idx, scores=scores, stream=stream,
-                        select_scope=self.scope)
+                        select_scope=self.scope, seq_slots=self.seq_slots)
         if not debug:
             return None
         torch.cuda.synchronize(self.dev)

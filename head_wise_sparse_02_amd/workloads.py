@@ -75,6 +75,7 @@ class Workload:
     rope_theta: float = 0.0
     select_scope: str = "kv"         # "kv": one set per KV head | "query": one per query head
     index_dtype: str = "f32"         # stored r=16 index: "f32" | "bf16"
+    local_ring: bool = False         # local heads keep sinks + window in a per-sequence ring
     d: int = D
     r: int = R
     n_needles: int = 0

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define HWS_ABI_VERSION 2
+#define HWS_ABI_VERSION 3
 
 typedef int32_t hws_status;
 enum {
@@ -94,18 +94,33 @@ typedef struct {
   int32_t index_dtype;        /* HWS_INDEX_*: fp32 (64 B/token) or bf16      */
   int32_t n_sink;             /* local heads: sink tokens 0..n_sink-1        */
   int32_t window;             /* local heads: last `window` tokens           */
+  int32_t local_ring;         /* 1: local heads keep only sinks + window rows
+                                 in per-sequence ring pools (bf16 cache only);
+                                 0: every head keeps every row in the pages */
+  int32_t max_seqs;           /* local_ring: sequence slots in the ring pools */
   float attn_scale;           /* softmax scale of attention, e.g. 1/sqrt(d)  */
   float index_scale;          /* logit = index_scale * (P q).(P k)           */
   float rope_theta;           /* > 0: rotate-half RoPE with this base; 0: off */
 } hws_config;
 
-/* Caller-owned device buffers.  Layouts (row-major):
- *   k_pool:         [num_blocks][Hkv][4][16][32] bf16 (or e4m3 bytes for FP8):
+/* Caller-owned device buffers.  Layouts (row-major); Hp is the number of
+ * heads a page holds: Hkv, or n_retrieval with local_ring (then the pages hold
+ * the retrieval heads only, in KV-head order):
+ *   k_pool:         [num_blocks][Hp][4][16][32] bf16 (or e4m3 bytes for FP8):
  *                   each 16-token page is stored in four 32-dim blocks, i.e.
  *                   element (slot r, dim d) of a page is at ((d/32)*16 + r)*32
  *                   + d%32; K is stored after RoPE (when rope_theta > 0).
- *   v_pool:         [num_blocks][Hkv][16][128] bf16 or e4m3 bytes, row-major.
- *   kv_scales:      [num_blocks][Hkv][2] fp32 (K scale, V scale); FP8 only.
+ *   v_pool:         [num_blocks][Hp][16][128] bf16 or e4m3 bytes, row-major.
+ *   kv_scales:      [num_blocks][Hp][2] fp32 (K scale, V scale); FP8 only.
+ *   local_k_pool,   local_ring only: [max_seqs][n_local][W][128] bf16 with
+ *   local_v_pool:   W = n_sink + window rounded up to a multiple of 16 and the
+ *                   local heads in KV-head order.  Token t of a sequence sits
+ *                   in ring row t (t < n_sink) or n_sink + (t - n_sink) % window;
+ *                   K rows are grouped in 16-row pages laid out like k_pool
+ *                   pages, V rows are plain rows.  [RTPurbo] Methodology §1:
+ *                   a local head only ever reads its sinks and window, so
+ *                   older rows need not be kept ([AoH] Results: the KV memory
+ *                   saving of local heads).
  *   index_pool:     [num_blocks][n_retrieval][16][16] fp32 or bf16 (index_dtype),
  *                   the projected pre-RoPE keys of retrieval heads in KV-head
  *                   order; may be NULL when no head is a retrieval head.
@@ -117,6 +132,8 @@ typedef struct {
   float* kv_scales;
   void* index_pool;
   const float* proj;
+  void* local_k_pool;
+  void* local_v_pool;
 } hws_buffers;
 
 /* One decode step for a batch.  Device pointers unless noted. */
@@ -128,7 +145,10 @@ typedef struct {
   int32_t select_scope;      /* HWS_SCOPE_* (0 = one set per KV head)         */
   const void* q;             /* [B][Hq][128] bf16, pre-RoPE queries           */
   const int32_t* block_tables; /* [B][max_blocks_per_seq] page ids            */
-  const int32_t* seq_lens;   /* [B] context lengths incl. the current token   */
+  const int32_t* seq_lens;   /* [B] context lengths incl. the current token;
+                                with local_ring, the appended length          */
+  const int32_t* seq_slots;  /* [B] ring slot of each sequence (local_ring),
+                                or NULL                                       */
   const float* top_p;        /* [B] (TOP_P); p >= 1 keeps every token         */
   const int32_t* top_k;      /* [B] (TOP_K); k >= N keeps every token         */
   float* out;                /* [B][Hq][128] fp32 attention output            */
@@ -209,6 +229,11 @@ hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq
 /* Append n_tok tokens to each of n_seq sequences: token t of sequence s goes to
  * position start_pos[s] + t, i.e. slot pos % 16 of page
  * block_tables[s][pos / 16].  k, v: [n_seq][n_tok][Hkv][128] bf16, pre-RoPE.
+ * With local_ring, local heads write ring slot seq_slots[s] instead (device
+ * [n_seq], each in [0, max_seqs), NULL otherwise): the sinks and the last
+ * `window` positions of the call, so a sequence must be appended in position
+ * order and a later call overwrites the rows that left the window; a slot
+ * out of range skips that sequence's local rows.
  * For each retrieval head the projected key P_h k (fp32, before RoPE) goes to
  * the index pool ([RTPurbo] Methodology §2).  With RoPE on, K is rotated at its
  * position and rounded to bf16 before it is stored.  FP8: when a call writes
@@ -218,7 +243,8 @@ hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq
  * ([AoH] Problem statement).  block_tables and start_pos are device arrays;
  * max_blocks_per_seq (from the config) is the row stride of block_tables. */
 hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t* block_tables,
-                      const int32_t* start_pos, const void* k, const void* v, void* stream);
+                      const int32_t* start_pos, const int32_t* seq_slots, const void* k, const void* v,
+                      void* stream);
 
 /* One decode step ([RTPurbo] Methodology §1: retrieval heads switch to dynamic
  * sparse selection during decoding, local heads use sinks plus a window).
@@ -227,7 +253,9 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
  * softmax_i(l_g); S = top-p set (smallest descending prefix with mass >= p,
  * all ties at the threshold kept) or top-k set (ties at the k-th value by
  * lowest position).  Local head: S = {0..n_sink-1} U {N-window..N-1}.  Then
- * out_g = sum_{i in S} softmax_S(attn_scale q_g.k_i) v_i. */
+ * out_g = sum_{i in S} softmax_S(attn_scale q_g.k_i) v_i.  With local_ring
+ * the local heads read their rows from ring slot seq_slots[b]; a slot out of
+ * range reads no rows (that sequence's local heads output 0 with lse -inf). */
 hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
 /* (FULL scoring requires a bf16 cache: HWS_ERR_UNSUPPORTED otherwise.) */
 

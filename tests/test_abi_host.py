@@ -21,7 +21,7 @@ def _declared():
 def _cfg(**kw):
     base = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, index_dim=16, block_size=16,
                 num_blocks=64, max_blocks_per_seq=32, kv_dtype=0, index_dtype=0, n_sink=4, window=256,
-                attn_scale=0.0883883, index_scale=0.7071, rope_theta=0.0)
+                local_ring=0, max_seqs=0, attn_scale=0.0883883, index_scale=0.7071, rope_theta=0.0)
     base.update(kw)
     return hws.Config(*[base[n] for n, _ in hws.Config._fields_])
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(hws.EXPORTED) == decl
-    assert L.hws_abi_version() == 2
+    assert L.hws_abi_version() == 3
     assert L.hws_status_string(hws.HWS_ERR_WORKSPACE) == b"workspace too small"
 
 
@@ -60,6 +60,10 @@ def test_library_exports_every_declared_symbol():
     (dict(index_dtype=2), hws.HWS_ERR_INVALID_ARG),
     (dict(index_dtype=-1), hws.HWS_ERR_INVALID_ARG),
     (dict(num_blocks=0), hws.HWS_ERR_INVALID_ARG),
+    (dict(local_ring=2, max_seqs=4), hws.HWS_ERR_INVALID_ARG),
+    (dict(local_ring=1, max_seqs=0), hws.HWS_ERR_INVALID_ARG),
+    (dict(local_ring=1, max_seqs=4, kv_dtype=1), hws.HWS_ERR_UNSUPPORTED),   # fp8 scales live with pages
+    (dict(local_ring=1, max_seqs=1 << 28), hws.HWS_ERR_INVALID_ARG),          # ring pages overflow int32
 ])
 def test_create_rejects(kw, status):
     st, h = _create(**kw)
@@ -77,7 +81,8 @@ def test_create_null_arguments():
 def _ctx(**kw):
     return hws.Context(num_q_heads=kw.get("hq", 8), num_kv_heads=kw.get("hkv", 2), num_blocks=64,
                        max_blocks_per_seq=32, n_sink=4, window=256, attn_scale=0.088,
-                       index_scale=0.707, kv_dtype=kw.get("kv", 0))
+                       index_scale=0.707, kv_dtype=kw.get("kv", 0), local_ring=kw.get("ring", False),
+                       max_seqs=kw.get("max_seqs", 0))
 
 
 def test_head_kinds_and_classification():
@@ -120,6 +125,33 @@ def test_bind_and_state_errors():
     with pytest.raises(hws.HwsError) as e:
         c8.bind(16, 16)                  # fp8 without scales
     assert e.value.status == hws.HWS_ERR_INVALID_ARG
+
+
+def test_local_ring_rules():
+    # a ring context with max_seqs = 0 is rejected; with the ring off, max_seqs is ignored
+    st, h = _create(local_ring=0, max_seqs=-5)
+    assert st == hws.HWS_OK
+    hws.lib().hws_destroy(h)
+    c = _ctx(ring=True, max_seqs=4)
+    c.set_head_kinds([1, 0])
+    with pytest.raises(hws.HwsError) as e:
+        c.bind(4096, 4096, None, 4096, 4096)                     # no ring pools
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG
+    c.bind(4096, 4096, None, 4096, 4096, 4096, 4096)
+    with pytest.raises(hws.HwsError) as e:                        # local heads need seq_slots
+        c.append(block_tables=_FakeT(), start_pos=_FakeT(), k=_FakeT(), v=_FakeT(), stream=0)
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG and b"seq_slots" in hws.lib().hws_last_error(c.handle)
+    with pytest.raises(hws.HwsError) as e:
+        _decode(c)
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG and b"seq_slots" in hws.lib().hws_last_error(c.handle)
+    # every head a retrieval head: nothing goes to the ring, seq_slots may be NULL (the
+    # decode then fails only on the workspace check, the last host check)
+    c2 = _ctx(ring=True, max_seqs=4)
+    c2.set_head_kinds([1, 1])
+    c2.bind(4096, 4096, None, 4096, 4096, 4096, 4096)
+    with pytest.raises(hws.HwsError) as e:
+        _decode(c2, workspace=_FakeT(nbytes=100))
+    assert e.value.status == hws.HWS_ERR_WORKSPACE
 
 
 def test_launch_mode_values():
