@@ -67,6 +67,8 @@ def parse_args(argv=None):
                     help="storage of the r=16 index (64 or 32 bytes per token and retrieval head)")
     ap.add_argument("--scope", choices=["kv", "query"], default="kv",
                     help="one token set per KV head (kv) or per query head (query)")
+    ap.add_argument("--ring", action="store_true",
+                    help="local heads keep only sinks + window in a per-sequence ring (bf16 caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -192,7 +194,11 @@ def main(argv=None) -> int:
     from head_wise_sparse_02_amd import workloads as W
     from head_wise_sparse_02_amd.runner import DecodeSetup
 
-    wl = W.make_workload(args.config, seed=args.seed, select_scope=args.scope, index_dtype=args.index)
+    wl = W.make_workload(args.config, seed=args.seed, select_scope=args.scope, index_dtype=args.index,
+                         local_ring=args.ring)
+    if args.ring and wl.kv_dtype != "bf16":
+        print("--ring needs a bf16 cache", file=sys.stderr)
+        return 2
     want_cpu = not args.no_cpu_baseline
     print(f"[bench] building workload {args.config}: {W.CONFIG_NAMES[args.config]}",
           file=sys.stderr, flush=True)
@@ -294,7 +300,11 @@ def main(argv=None) -> int:
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
                    "context": int(max(wl.seq_lens)), "score_mode": wl.score_mode,
                    "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype, "launch": args.launch,
-                   "select_scope": wl.select_scope, "index_dtype": wl.index_dtype},
+                   "select_scope": wl.select_scope, "index_dtype": wl.index_dtype,
+                   "local_ring": wl.local_ring},
+        "kv_cache_bytes": int(sum(t.numel() * t.element_size() for t in (
+            setup.k_pool, setup.v_pool, setup.kv_scales, setup.index_pool, setup.local_k_pool,
+            setup.local_v_pool) if t is not None)),
         "step_bytes": by["total"], "step_GBps": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_GBS, 4),
         "selected_per_head_mean": round(float(sel_counts[:, [h for h in wl.retrieval_heads]].mean()), 1)
