@@ -39,6 +39,8 @@ from .hws_oracle import (  # noqa: F401
     index_keys,
     index_logits,
     local_token_set,
+    prefill_mask,
+    prefill_sequence_ref,
     rope,
     select_top_k,
     select_top_p,

@@ -418,6 +418,66 @@ def decode_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, proj=None, score_mode
 
 
 # ---------------------------------------------------------------------------
+# Head-wise prefill  ([RTPurbo] Methodology §1 and Results; [AoH] Methodology §4)
+# ---------------------------------------------------------------------------
+
+def prefill_mask(positions, n_keys: int, *, kind: str, n_sink: int, window: int) -> np.ndarray:
+    """Which keys each query position attends to during prefill: [T, n_keys] bool.
+
+    Causal: query position i sees keys j <= i.  A retrieval head keeps all of
+    them in the prefill phase ([RTPurbo] Methodology §1: retrieval heads keep
+    the full KV cache during prefill, the sparse selection starts at decode);
+    a local head keeps its sinks and its window ([RTPurbo] Methodology §1;
+    [AoH] Methodology §4: streaming heads in chunked prefill).
+    reading: the local set of query position i is the decode-time local set of
+    a context of length i + 1, i.e. positions 0..n_sink-1 and i-window+1..i.
+    """
+    i = np.asarray(positions, dtype=np.int64)[:, None]
+    j = np.arange(n_keys, dtype=np.int64)[None, :]
+    m = j <= i
+    if kind == "local":
+        m &= (j < n_sink) | (j > i - window)
+    return m
+
+
+def prefill_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, start: int, n_sink: int, window: int,
+                         attn_scale: float, rope_theta: float = 0.0, heads=None, rows=None,
+                         dense_all: bool = False):
+    """Prefill attention of the query positions start..start+T-1 of one sequence.
+
+    q_pre [T, Hq, d] pre-RoPE queries; k_pre, v_in [N, Hkv, d] the appended
+    rows (bf16-exact, N >= start + T).  For KV head h and its query heads g:
+    z = attn_scale * rope(q_g, i) . k_j over the stored (rotated, bf16) keys,
+    masked by ``prefill_mask``; o = softmax(z) V and lse = log sum exp z, all
+    in float64 as masked matrix products.  ``dense_all`` treats every head as a
+    retrieval head (plain causal attention).  ``rows``: indices into the T
+    positions to evaluate (default all).  Returns {h: (o [T', G, d], lse [T', G])}.
+    """
+    q_pre = np.asarray(q_pre, dtype=np.float64)
+    T, hq, d = q_pre.shape
+    n, hkv, _ = k_pre.shape
+    G = hq // hkv
+    sel = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    pos = start + sel
+    keys = np.arange(n)
+    res = {}
+    for h in (range(hkv) if heads is None else heads):
+        ks = stored_rows(k_pre[:, h, :], keys, rope_theta=rope_theta, kv_fp8=False, segments=None,
+                         rotate=True)
+        vs = np.asarray(v_in[:, h, :], dtype=np.float64)
+        kind = "retrieval" if dense_all else head_kinds[h]
+        mask = prefill_mask(pos, n, kind=kind, n_sink=n_sink, window=window)      # [T', n]
+        qr = rope(q_pre[sel, h * G:(h + 1) * G, :], pos[:, None], rope_theta)    # [T', G, d]
+        z = attn_scale * (qr @ ks.T)                                             # [T', G, n]
+        z = np.where(mask[:, None, :], z, -np.inf)
+        m = z.max(axis=2, keepdims=True)
+        w = np.exp(z - m)
+        l = w.sum(axis=2, keepdims=True)
+        res[h] = ((w @ vs) / l, (m + np.log(l))[:, :, 0])
+    return res
+
+
+# ---------------------------------------------------------------------------
 # Data-free head classification  ([AoH] Methodology §1-§4)
 # ---------------------------------------------------------------------------
 

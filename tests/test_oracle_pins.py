@@ -522,3 +522,94 @@ def test_effective_rank_invariances_and_gqa():
         s = sv / sv.sum()
         s = s[s > 0]
         assert abs(np.exp(-(s * np.log(s)).sum()) - er[g]) < 1e-8 * er[g]
+
+
+# ---------------------------------------------------------------- prefill
+
+def _prefill_seq(n=300, t=300, hq=8, hkv=2, seed=31):
+    rng = np.random.default_rng(seed)
+    q = W.bf16_rne(rng.standard_normal((t, hq, 128)).astype(np.float32))
+    k = W.bf16_rne(rng.standard_normal((n, hkv, 128)).astype(np.float32))
+    v = W.bf16_rne(rng.standard_normal((n, hkv, 128)).astype(np.float32))
+    return q, k, v
+
+
+@pytest.mark.parametrize("rope_theta", [0.0, 10000.0])
+def test_prefill_dense_is_torch_causal_sdpa(rope_theta):
+    """Every head dense from position 0: torch's causal attention (fp64, CPU)
+    on the rotated queries and the stored keys."""
+    q, k, v = _prefill_seq()
+    n, G = k.shape[0], 4
+    sc = 1 / np.sqrt(128)
+    res = O.prefill_sequence_ref(q, k, v, head_kinds=["local", "retrieval"], start=0, n_sink=4,
+                                 window=16, attn_scale=sc, rope_theta=rope_theta, dense_all=True)
+    pos = np.arange(n)
+    for h in range(2):
+        kr = k[:, h].astype(np.float64)
+        if rope_theta > 0:
+            kr = O.bf16_round(O.rope(kr, pos, rope_theta))
+        for g in range(G):
+            qr = O.rope(q[:, h * G + g].astype(np.float64), pos, rope_theta)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(qr)[None, None], torch.from_numpy(kr)[None, None],
+                torch.from_numpy(v[:, h].astype(np.float64))[None, None], is_causal=True, scale=sc)
+            np.testing.assert_allclose(res[h][0][:, g], ref[0, 0].numpy(), rtol=0, atol=1e-12)
+            z = sc * (qr @ kr.T)
+            z[np.triu_indices(n, 1)] = -np.inf
+            np.testing.assert_allclose(res[h][1][:, g], scipy.special.logsumexp(z, axis=1), rtol=1e-13)
+
+
+def test_prefill_local_mask_brute_force():
+    for n_sink, window in ((4, 16), (0, 1), (3, 1), (20, 5), (0, 1000), (7, 0)):
+        pos = np.arange(40, 90)
+        m = O.prefill_mask(pos, 100, kind="local", n_sink=n_sink, window=window)
+        for r, i in enumerate(pos):
+            want = {j for j in range(100) if j <= i and (j < n_sink or i - j < window)}
+            assert set(np.flatnonzero(m[r]).tolist()) == want
+            np.testing.assert_array_equal(np.flatnonzero(m[r]), O.local_token_set(i + 1, n_sink, window))
+        full = O.prefill_mask(pos, 100, kind="retrieval", n_sink=n_sink, window=window)
+        np.testing.assert_array_equal(full, np.arange(100)[None, :] <= pos[:, None])
+
+
+@pytest.mark.parametrize("rope_theta", [0.0, 10000.0])
+def test_prefill_rows_are_decode_steps(rope_theta):
+    """Row i of a chunk is the decode of the prefix 0..i: dense for a
+    retrieval head (top-p = 1 keeps every token), sinks + window for a local
+    head (both pinned separately above)."""
+    q, k, v = _prefill_seq(n=500, t=120)
+    start = 380
+    rows = [0, 1, 57, 118, 119]
+    sc = 1 / np.sqrt(128)
+    res = O.prefill_sequence_ref(q, k, v, head_kinds=["retrieval", "local"], start=start, n_sink=4,
+                                 window=64, attn_scale=sc, rope_theta=rope_theta, rows=rows)
+    for r, t in enumerate(rows):
+        i = start + t
+        dec = O.decode_sequence_ref(q[t], k[:i + 1], v[:i + 1], head_kinds=["retrieval", "local"],
+                                    score_mode="full", select_mode="top_p", top_p=1.0, n_sink=4,
+                                    window=64, attn_scale=sc, rope_theta=rope_theta)
+        for h in range(2):
+            np.testing.assert_allclose(res[h][0][r], dec[h]["o64"], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(res[h][1][r], dec[h]["lse64"], rtol=1e-13)
+
+
+def test_prefill_closed_forms():
+    q, k, v = _prefill_seq(n=200, t=200)
+    v_const = np.broadcast_to(np.linspace(-1, 1, 128), v.shape).copy()
+    res = O.prefill_sequence_ref(q, k, v_const, head_kinds=["retrieval", "local"], start=0, n_sink=2,
+                                 window=9, attn_scale=0.09)
+    for h in range(2):
+        np.testing.assert_allclose(res[h][0], np.broadcast_to(v_const[0, 0], res[h][0].shape), atol=1e-13)
+    # position 0 sees only itself: o = v_0, lse = z_00
+    res = O.prefill_sequence_ref(q, k, v, head_kinds=["local", "retrieval"], start=0, n_sink=0,
+                                 window=3, attn_scale=0.09, rows=[0])
+    for h in range(2):
+        np.testing.assert_array_equal(res[h][0][0], np.repeat(v[0:1, h].astype(np.float64), 4, 0))
+        np.testing.assert_allclose(res[h][1][0], 0.09 * q[0, 4 * h:4 * h + 4].astype(np.float64)
+                                   @ k[0, h].astype(np.float64), rtol=0, atol=1e-13)
+    # a window that covers everything makes a local head a retrieval head
+    a = O.prefill_sequence_ref(q, k, v, head_kinds=["local", "local"], start=0, n_sink=0, window=200,
+                               attn_scale=0.09)
+    b = O.prefill_sequence_ref(q, k, v, head_kinds=["retrieval", "retrieval"], start=0, n_sink=0,
+                               window=1, attn_scale=0.09)
+    for h in range(2):
+        np.testing.assert_array_equal(a[h][0], b[h][0])
