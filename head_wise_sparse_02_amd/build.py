@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhws.so")
 
-SOURCES = ["hws_api.cpp", "k_score.hip", "k_select.hip", "k_attend.hip", "k_append.hip", "k_tail.hip", "k_rank.hip"]
+SOURCES = ["hws_api.cpp", "k_score.hip", "k_select.hip", "k_attend.hip", "k_append.hip", "k_tail.hip", "k_rank.hip", "k_prefill.hip"]
 ARCH = "gfx950"
 
 COMMON = [

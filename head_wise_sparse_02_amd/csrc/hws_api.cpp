@@ -20,8 +20,8 @@ using namespace hws;
 
 namespace {
 
-constexpr int NUM_STAGES = 6;
-const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge", "tail", "fused"};
+constexpr int NUM_STAGES = 7;
+const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge", "tail", "fused", "prefill"};
 
 struct EvPair {
   hipEvent_t a, b;
@@ -513,6 +513,65 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   if ((e = launch_merge(p, s, em.start, em.stop)) != hipSuccess) return hip_fail(ctx, e, "merge launch");
   if (ctx->nR > 0 && a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess)
     return hip_fail(ctx, e, "emit launch");
+  return HWS_OK;
+}
+
+hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (a == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "args is NULL");
+  if (!ctx->bound) return fail(ctx, HWS_ERR_STATE, "prefill before bind");
+  const hws_config& c = ctx->cfg;
+  if (a->n_seq < 1 || a->n_tok < 1)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "n_seq = %d, n_tok = %d", a->n_seq, a->n_tok);
+  if (a->dense != 0 && a->dense != 1) return fail(ctx, HWS_ERR_INVALID_ARG, "dense = %d", a->dense);
+  if (a->q == nullptr || a->block_tables == nullptr || a->start_pos == nullptr || a->out == nullptr)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "null device pointer (q, block_tables, start_pos or out)");
+  if ((long long)a->n_tok > (long long)c.max_blocks_per_seq * BS)
+    return fail(ctx, HWS_ERR_CAPACITY, "n_tok = %d exceeds the block table", a->n_tok);
+  if (c.kv_dtype != HWS_KV_BF16) return fail(ctx, HWS_ERR_UNSUPPORTED, "prefill needs a bf16 cache");
+  if (ctx->ring_rows > 0 && ctx->nL > 0)
+    return fail(ctx, HWS_ERR_UNSUPPORTED, "prefill reads every head from the pages (no local_ring)");
+  const int rows = prefill_rows_per_tile();
+  const int qp = rows / ctx->G;
+  const long long ntq = (a->n_tok + qp - 1) / qp;
+  if ((long long)a->n_seq * c.num_kv_heads * ntq >= (1LL << 31))
+    return fail(ctx, HWS_ERR_CAPACITY, "too many query tiles");
+  PrefillParams p{};
+  p.n_seq = a->n_seq;
+  p.n_tok = a->n_tok;
+  p.Hq = c.num_q_heads;
+  p.Hkv = c.num_kv_heads;
+  p.G = ctx->G;
+  p.max_blocks = c.max_blocks_per_seq;
+  p.num_blocks = c.num_blocks;
+  p.Hp = ctx->Hp;
+  p.n_sink = c.n_sink;
+  p.window = c.window;
+  p.ntq = (int)ntq;
+  p.c2 = (float)((double)c.attn_scale * 1.4426950408889634);
+  p.rope_theta = c.rope_theta;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.block_tables = a->block_tables;
+  p.start_pos = a->start_pos;
+  p.k_pool = ctx->buf.k_pool;
+  p.v_pool = ctx->buf.v_pool;
+  p.out = a->out;
+  p.lse = a->lse;
+  std::memcpy(p.pool_slot, ctx->pool_slot, sizeof(p.pool_slot));
+  for (int h = 0; h < MAX_KV; ++h) { p.ret_head[h] = -1; p.loc_head[h] = -1; }
+  if (a->dense) {
+    p.nR = c.num_kv_heads;
+    p.nL = 0;
+    for (int h = 0; h < c.num_kv_heads; ++h) p.ret_head[h] = (signed char)h;
+  } else {
+    p.nR = ctx->nR;
+    p.nL = ctx->nL;
+    std::memcpy(p.ret_head, ctx->ret_head, sizeof(p.ret_head));
+    std::memcpy(p.loc_head, ctx->loc_head, sizeof(p.loc_head));
+  }
+  const StageEv ev = stage_events(ctx, 6);
+  const hipError_t e = launch_prefill(p, static_cast<hipStream_t>(stream), ev.start, ev.stop);
+  if (e != hipSuccess) return hip_fail(ctx, e, "prefill launch");
   return HWS_OK;
 }
 

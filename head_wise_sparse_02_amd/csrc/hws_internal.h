@@ -141,6 +141,26 @@ struct AppendParams {
   signed char loc_slot[MAX_KV];   // local head's index among the local heads
 };
 
+// One chunked-prefill call: n_tok query positions per sequence from start_pos.
+struct PrefillParams {
+  int n_seq, n_tok, Hq, Hkv, G, max_blocks, num_blocks, Hp;
+  int n_sink, window;
+  int nR, nL;                   // heads walked as retrieval (all keys) / local (sinks + window)
+  int ntq;                      // query tiles per (sequence, KV head)
+  float c2;                     // attn_scale * log2(e)
+  float rope_theta;
+  const uint16_t* q;            // [n_seq][n_tok][Hq][D] bf16, pre-RoPE
+  const int* block_tables;      // [n_seq][max_blocks]
+  const int* start_pos;         // [n_seq]
+  const void* k_pool;
+  const void* v_pool;
+  float* out;                   // [n_seq][n_tok][Hq][D]
+  float* lse;                   // [n_seq][n_tok][Hq] or null
+  signed char ret_head[MAX_KV];
+  signed char loc_head[MAX_KV];
+  signed char pool_slot[MAX_KV];
+};
+
 // Launch a kernel; with timing events the start/stop timestamps are taken
 // by the dispatch packet itself (no extra barrier packets in the stream).
 template <typename K, typename... A>
@@ -176,6 +196,8 @@ hipError_t launch_fused(const DecodeParams& p, int nwg, bool cooperative, hipStr
                         hipEvent_t e1);
 hipError_t launch_append(const AppendParams& p, int kv_fp8, hipStream_t s);
 // Effective rank of the query-key kernels (fp64 Gram, Cholesky, Jacobi).
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+int prefill_rows_per_tile();
 size_t rank_workspace_bytes(int hq, int hkv);
 hipError_t launch_effective_rank(int hq, int hkv, int d_model, const float* w_q, const float* w_k,
                                  float* eff_rank, void* workspace, hipStream_t s);

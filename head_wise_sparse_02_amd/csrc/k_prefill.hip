@@ -1,0 +1,325 @@
+// Head-wise chunked prefill attention on the paged cache.
+//
+// [RTPurbo] Methodology §1: during prefill a retrieval head keeps its whole
+// cache (causal attention over every earlier position) while a local head
+// attends to its sinks and its sliding window; the prefill speed-up of the
+// method comes from the local heads ([RTPurbo] Results; [AoH] Results).
+// Query position i of a local head sees keys 0..n_sink-1 and i-window+1..i.
+//
+// One workgroup per (sequence, KV head, tile of 128 query rows), a query row
+// being one (position, query head of the group) pair, so the G query heads of
+// a KV head share every K/V tile.  Key tiles of 64 keys (4 pages) go through
+// LDS, double-buffered: K in its page-blocked layout, V transposed to
+// [dim][key].  Each wave owns 32 query rows and computes
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims from LDS,
+//                  B = the wave's queries, kept in registers)
+//   O^T += V^T P^T (A = 16 dims x 32 keys of V^T, B = P in bf16),
+// with the online softmax in log2 units between the two.  The S^T layout
+// leaves each lane with 4 keys of one query per 16-key block, which is the
+// B-operand shape of P^T once both operands enumerate the 32 keys of a step
+// in the same (permuted) order.  A retrieval head walks key tiles 0..last;
+// a local head walks its sink tile(s) and the tiles its window touches.
+// Masks are evaluated only on tiles that cross a boundary.
+//
+// With RoPE on, queries are rotated in fp64 at their position and split as
+// q = hi + lo (two bf16 parts), so S keeps fp32-level accuracy; P is rounded
+// to bf16 for the P V product.
+#include "hws_device.h"
+
+namespace hws {
+
+namespace {
+
+constexpr int PF_ROWS = 128;      // query rows per workgroup (4 waves x 32)
+constexpr int PF_KT = 64;         // keys per tile
+constexpr int VT_STRIDE = 68;     // padded key stride of the transposed V tile
+
+struct PfLds {
+  uint16_t k[2][4 * BS * D];      // 4 pages, page-blocked layout (16 KiB each)
+  uint16_t vt[2][D * VT_STRIDE];  // V^T [dim][key] (17 KiB each)
+};
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero8() { return (bf16x8)(__bf16)0.f; }
+
+template <int G, bool ROPE>
+__global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParams p) {
+  constexpr int QP = PF_ROWS / G;                  // query positions per tile
+  __shared__ PfLds S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+
+  // work item -> (sequence, KV head, query tile); retrieval items first and
+  // the tiles with the most keys first
+  int item = blockIdx.x;
+  const int nret = p.n_seq * p.nR * p.ntq;
+  bool ret;
+  int s, h, qt;
+  if (item < nret) {
+    ret = true;
+    const int per = p.n_seq * p.nR;
+    qt = p.ntq - 1 - item / per;
+    const int rem = item % per;
+    s = rem / p.nR;
+    h = p.ret_head[rem % p.nR];
+  } else {
+    item -= nret;
+    ret = false;
+    const int per = p.n_seq * p.nL;
+    qt = p.ntq - 1 - item / per;
+    const int rem = item % per;
+    s = rem / p.nL;
+    h = p.loc_head[rem % p.nL];
+  }
+  const int start = p.start_pos[s];
+  if (start < 0) return;
+  const int t0l = qt * QP;                         // first position of the tile within the chunk
+  const int nq = min(QP, p.n_tok - t0l);
+  const int t0 = start + t0l, tl = t0 + nq - 1;    // first / last query position
+
+  // key tiles: [0, ns_t) sink tiles, then [lo_t, last_t]
+  const int last_t = tl / PF_KT;
+  int ns_t = 0, lo_t = 0;
+  if (!ret) {
+    ns_t = p.n_sink > 0 ? min((p.n_sink - 1) / PF_KT + 1, last_t + 1) : 0;
+    lo_t = max(ns_t, max(0, t0 - p.window + 1) / PF_KT);
+  }
+  const int n_tiles = ns_t + max(0, last_t - lo_t + 1);
+
+  // queries of this wave: rows 32*wave + 16*qb + col = (position, head) pairs
+  int qpos[2];
+  bool qok[2];
+  bf16x8 qf[2][4], ql[ROPE ? 2 : 1][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = 32 * wave + 16 * qb + col;
+    const int pl = r / G, g = r % G;
+    qok[qb] = pl < nq;
+    qpos[qb] = t0 + pl;
+    const uint16_t* qrow = p.q + (((size_t)s * p.n_tok + t0l + (qok[qb] ? pl : 0)) * p.Hq + h * G + g) * D;
+    if (!ROPE) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        qf[qb][st] = qok[qb] ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * st + 8 * quad))
+                             : zero8();
+    } else {
+      // dims 32*st + 8*quad + e (st = 0, 1) pair with the same dims + 64 (st + 2)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(qrow + 32 * st + 8 * quad);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(qrow + 32 * (st + 2) + 8 * quad);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double x1 = (e & 1) ? bf16_hi(a[e >> 1]) : bf16_lo(a[e >> 1]);
+          const double x2 = (e & 1) ? bf16_hi(b[e >> 1]) : bf16_lo(b[e >> 1]);
+          const int j = 32 * st + 8 * quad + e;
+          const double inv = pow((double)p.rope_theta, -2.0 * (double)j / (double)D);
+          double sn, cs;
+          sincos((double)qpos[qb] * inv, &sn, &cs);
+          const double r1 = qok[qb] ? x1 * cs - x2 * sn : 0.0;
+          const double r2 = qok[qb] ? x2 * cs + x1 * sn : 0.0;
+          const float h1 = bf16_to_f32(f64_to_bf16_rne(r1)), h2 = bf16_to_f32(f64_to_bf16_rne(r2));
+          qf[qb][st][e] = (__bf16)h1;
+          qf[qb][st + 2][e] = (__bf16)h2;
+          ql[ROPE ? qb : 0][st][e] = (__bf16)bf16_to_f32(f64_to_bf16_rne(r1 - (double)h1));
+          ql[ROPE ? qb : 0][st + 2][e] = (__bf16)bf16_to_f32(f64_to_bf16_rne(r2 - (double)h2));
+        }
+      }
+    }
+  }
+
+  const int* bt = p.block_tables + (size_t)s * p.max_blocks;
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
+  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
+  const int hslot = p.pool_slot[h];
+  const int kg = tid >> 4, dg = tid & 15;          // V loader: keys 4kg..4kg+3, dims 8dg..8dg+7
+
+  // global -> registers for key tile kt (pages past the last query read page 0;
+  // V rows of keys past the last query are zeroed, so stale slots never reach P V)
+  u32x4 kreg[4], vreg[4];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int lp = kt * 4 + u;
+      int blk = (lp * BS <= tl && lp < p.max_blocks) ? bt[lp] : 0;
+      blk = (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
+      kreg[u] = *reinterpret_cast<const u32x4*>(kpool + ((size_t)blk * p.Hp + hslot) * (BS * D) + tid * 8);
+    }
+    const int lp = kt * 4 + (kg >> 2);
+    int blk = (lp * BS <= tl && lp < p.max_blocks) ? bt[lp] : 0;
+    blk = (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
+    const uint16_t* vsrc = vpool + (((size_t)blk * p.Hp + hslot) * BS + (4 * kg & 15)) * D + 8 * dg;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(vsrc + e * D);
+      vreg[e] = kt * PF_KT + 4 * kg + e <= tl ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(&S.k[buf][u * (BS * D) + tid * 8]) = kreg[u];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {                 // dims 8dg + 2w (low halves) and + 2w + 1 (high)
+      const unsigned lo01 = (vreg[0][w] & 0xFFFFu) | (vreg[1][w] << 16);
+      const unsigned lo23 = (vreg[2][w] & 0xFFFFu) | (vreg[3][w] << 16);
+      const unsigned hi01 = (vreg[0][w] >> 16) | (vreg[1][w] & 0xFFFF0000u);
+      const unsigned hi23 = (vreg[2][w] >> 16) | (vreg[3][w] & 0xFFFF0000u);
+      *reinterpret_cast<uint2*>(&S.vt[buf][(8 * dg + 2 * w) * VT_STRIDE + 4 * kg]) = make_uint2(lo01, lo23);
+      *reinterpret_cast<uint2*>(&S.vt[buf][(8 * dg + 2 * w + 1) * VT_STRIDE + 4 * kg]) = make_uint2(hi01, hi23);
+    }
+  };
+
+  float m[2] = {NEG_INF, NEG_INF}, lsum[2] = {0.f, 0.f};
+  f32x4 o[8][2];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float c2 = p.c2;
+
+  if (n_tiles > 0) {
+    load_tile(ns_t > 0 ? 0 : lo_t);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kt = it < ns_t ? it : lo_t + (it - ns_t);
+    const int buf = it & 1;
+    if (it + 1 < n_tiles) load_tile(it + 1 < ns_t ? it + 1 : lo_t + (it + 1 - ns_t));
+
+    // S^T = K Q^T for the 4 key blocks x 2 query blocks of this wave
+    f32x4 sacc[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&S.k[buf][kb * (BS * D) + st * 512 + col * 32 + quad * 8]));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sacc[kb][qb] = mfma(a, qf[qb][st], sacc[kb][qb]);
+          if (ROPE) sacc[kb][qb] = mfma(a, ql[ROPE ? qb : 0][st], sacc[kb][qb]);
+        }
+      }
+    }
+
+    // masks, only where the tile crosses the causal edge, the window's lower
+    // edge or the end of the sinks
+    const int key0 = kt * PF_KT;
+    const bool inside = key0 + PF_KT - 1 <= t0 &&
+                        (ret || key0 + PF_KT - 1 < p.n_sink || key0 > tl - p.window);
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (!inside || !qok[qb]) {
+        const int qi = qpos[qb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = key0 + 16 * kb + 4 * quad + i;
+            const bool ok = qok[qb] && j <= qi && (ret || j < p.n_sink || j > qi - p.window);
+            sacc[kb][qb][i] = ok ? sacc[kb][qb][i] : NEG_INF;
+          }
+      }
+      float mx = sacc[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m[qb], mx * c2);
+      const float m_use = m_new == NEG_INF ? 0.f : m_new;
+      const float alpha = fast_exp2(m[qb] - m_use);
+      m[qb] = m_new;
+      float ps = 0.f;
+      float pv[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[kb][i] = fast_exp2(fmaf(sacc[kb][qb][i], c2, -m_use));
+          ps += pv[kb][i];
+        }
+      lsum[qb] = lsum[qb] * alpha + ps;
+      if (__any(alpha != 1.f)) {                       // rescale only when a max moved
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[qb][ks][i] = (__bf16)pv[2 * ks][i];
+          pb[qb][ks][4 + i] = (__bf16)pv[2 * ks + 1][i];
+        }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t* base = &S.vt[buf][(16 * db + col) * VT_STRIDE + 32 * ks + 4 * quad];
+        const uint2 lo = *reinterpret_cast<const uint2*>(base);
+        const uint2 hi = *reinterpret_cast<const uint2*>(base + 16);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma(a, pb[qb][ks], o[db][qb]);
+      }
+    }
+
+    if (it + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // normalise and write: lane holds dims 16*db + 4*quad + i of its query row
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = lsum[qb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!qok[qb]) continue;
+    const int r = 32 * wave + 16 * qb + col;
+    const int pl = r / G, g = r % G;
+    const size_t orow = ((size_t)s * p.n_tok + t0l + pl) * p.Hq + h * G + g;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const f32x4 v = o[db][qb] * inv;
+      *reinterpret_cast<float4*>(p.out + orow * D + 16 * db + 4 * quad) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    if (quad == 0 && p.lse != nullptr) p.lse[orow] = (m[qb] + log2f(l)) * LN2;
+  }
+}
+
+template <int G>
+hipError_t launch_g(const PrefillParams& p, int nwg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.rope_theta > 0.f) return launch_kernel(prefill_kernel<G, true>, dim3(nwg), dim3(256), s, e0, e1, p);
+  return launch_kernel(prefill_kernel<G, false>, dim3(nwg), dim3(256), s, e0, e1, p);
+}
+
+}  // namespace
+
+int prefill_rows_per_tile() { return PF_ROWS; }
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const long long nwg = (long long)p.n_seq * (p.nR + p.nL) * p.ntq;
+  if (nwg <= 0) return hipSuccess;
+  switch (p.G) {
+    case 1: return launch_g<1>(p, (int)nwg, s, e0, e1);
+    case 2: return launch_g<2>(p, (int)nwg, s, e0, e1);
+    case 4: return launch_g<4>(p, (int)nwg, s, e0, e1);
+    default: return launch_g<8>(p, (int)nwg, s, e0, e1);
+  }
+}
+
+}  // namespace hws

@@ -35,7 +35,7 @@ EXPORTED = (
     "hws_set_head_kinds", "hws_classify_by_scores", "hws_get_head_kinds", "hws_bind",
     "hws_workspace_size", "hws_append", "hws_decode", "hws_profile_enable",
     "hws_profile_read", "hws_profile_stage_name", "hws_set_launch_mode",
-    "hws_effective_rank_workspace", "hws_effective_rank",
+    "hws_effective_rank_workspace", "hws_effective_rank", "hws_prefill",
 )
 
 
@@ -72,6 +72,12 @@ class DecodeArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("n_tok", ctypes.c_int32), ("dense", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("block_tables", ctypes.c_void_p), ("start_pos", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -99,6 +105,7 @@ def lib() -> ctypes.CDLL:
         "hws_workspace_size": (i32, [vp, i32, i32, i32, i32, P(ctypes.c_size_t)]),
         "hws_append": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp]),
         "hws_decode": (i32, [vp, P(DecodeArgs), vp]),
+        "hws_prefill": (i32, [vp, P(PrefillArgs), vp]),
         "hws_profile_enable": (i32, [vp, i32]),
         "hws_set_launch_mode": (i32, [vp, i32]),
         "hws_effective_rank_workspace": (i32, [i32, i32, P(ctypes.c_size_t)]),
@@ -225,6 +232,19 @@ class Context:
         a.workspace = _ptr(workspace)
         a.workspace_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
         self._check(self._L.hws_decode(self.handle, ctypes.byref(a), _stream(stream)), "hws_decode")
+
+    def prefill(self, *, q, block_tables, start_pos, out, lse=None, dense: bool = False, stream=None):
+        """Chunked prefill attention: q [n_seq, n_tok, Hq, 128] bf16 of the positions
+        start_pos[s]..start_pos[s]+n_tok-1 (already appended); out [n_seq, n_tok, Hq, 128]
+        fp32, lse [n_seq, n_tok, Hq] or None; dense: every head attends to every
+        earlier position."""
+        a = PrefillArgs()
+        a.n_seq = int(q.shape[0]) if q is not None else 0
+        a.n_tok = int(q.shape[1]) if q is not None else 0
+        a.dense = int(bool(dense))
+        a.q, a.block_tables, a.start_pos = _ptr(q), _ptr(block_tables), _ptr(start_pos)
+        a.out, a.lse = _ptr(out), _ptr(lse)
+        self._check(self._L.hws_prefill(self.handle, ctypes.byref(a), _stream(stream)), "hws_prefill")
 
     # -- timing ------------------------------------------------------------------
     def set_launch_mode(self, mode: int):

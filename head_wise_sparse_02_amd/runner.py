@@ -125,6 +125,17 @@ class DecodeSetup:
         # |S| per KV head, or per query head with one set per query head
         self.sel_counts = torch.empty((B, Hq if self.scope else Hkv), dtype=torch.int32, device=self.dev)
 
+    def prefill(self, q, start_pos, *, dense: bool = False, stream=None):
+        """Prefill attention of the chunk q [B, n_tok, Hq, d] (bf16 device tensor)
+        at positions start_pos[b].. (int32 device tensor); the cache already holds
+        them.  Returns (out, lse) device tensors."""
+        B, n_tok = int(q.shape[0]), int(q.shape[1])
+        out = torch.empty((B, n_tok, self.wl.Hq, self.wl.d), dtype=torch.float32, device=self.dev)
+        lse = torch.empty((B, n_tok, self.wl.Hq), dtype=torch.float32, device=self.dev)
+        self.ctx.prefill(q=q, block_tables=self.block_tables, start_pos=start_pos, out=out, lse=lse,
+                         dense=dense, stream=stream)
+        return out, lse
+
     def decode(self, *, debug: bool = False, sel_cap: int | None = None, stream=None):
         """Run one decode step.  With debug=True also return the raw scores and
         the ascending selected positions (host numpy arrays)."""

@@ -111,6 +111,11 @@ class Workload:
     def sequence(self, b: int) -> Sequence:
         return _SEQ_BUILDERS[self.cfg](self, b)
 
+    def prefill_queries(self, b: int, n_tok: int) -> np.ndarray:
+        """Queries of a prefill chunk of sequence b: [n_tok, Hq, d] bf16-exact N(0, 1)."""
+        rng = np.random.default_rng(np.random.SeedSequence([self.cfg, self.seed, 4000 + b]))
+        return bf16_rne(rng.standard_normal((n_tok, self.Hq, self.d), dtype=np.float32))
+
 
 # ---------------------------------------------------------------------------
 # per-config sequence builders

@@ -259,6 +259,33 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
 hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
 /* (FULL scoring requires a bf16 cache: HWS_ERR_UNSUPPORTED otherwise.) */
 
+/* One chunked-prefill attention call ([RTPurbo] Methodology §1: during
+ * prefill a retrieval head keeps its whole cache while a local head attends
+ * to its sinks and window; [AoH] Methodology §4: this fits chunked prefill).
+ * For query position i = start_pos[s] + t of sequence s and query head g of
+ * KV head h: out = sum_j softmax_j(attn_scale q_g.k_j) v_j over j <= i
+ * (retrieval head, or every head with dense = 1) or over j in
+ * {0..n_sink-1} U {i-window+1..i}, j <= i (local head); q and k rotated at
+ * their positions when rope_theta > 0.  K/V are read from the pages, so the
+ * chunk must have been appended first (the cache holds positions
+ * 0..start_pos[s]+n_tok-1).  Computed with bf16 MFMA products: logits in
+ * fp32 (the rotated query is split into two bf16 parts), softmax weights
+ * rounded to bf16 for the weighted sum of V.  A negative start_pos[s] skips
+ * that sequence.  Needs a bf16 cache without local_ring
+ * (HWS_ERR_UNSUPPORTED otherwise: the ring no longer holds the earlier
+ * window rows of a chunk).  No workspace. */
+typedef struct {
+  int32_t n_seq;               /* sequences (host), >= 1                       */
+  int32_t n_tok;               /* query positions per sequence (host), >= 1    */
+  int32_t dense;               /* 1: every head attends to all of j <= i       */
+  const void* q;               /* [n_seq][n_tok][Hq][128] bf16, pre-RoPE       */
+  const int32_t* block_tables; /* [n_seq][max_blocks_per_seq]                  */
+  const int32_t* start_pos;    /* [n_seq] position of each sequence's first query */
+  float* out;                  /* [n_seq][n_tok][Hq][128] fp32                 */
+  float* lse;                  /* [n_seq][n_tok][Hq] natural-log LSE, or NULL  */
+} hws_prefill_args;
+hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream);
+
 /* Launch shape of hws_decode.
  *  HWS_LAUNCH_MULTI: one kernel per stage (score, select passes, attend,
  *    merge); no workgroup waits for another.

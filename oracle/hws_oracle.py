@@ -442,7 +442,7 @@ def prefill_mask(positions, n_keys: int, *, kind: str, n_sink: int, window: int)
 
 def prefill_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, start: int, n_sink: int, window: int,
                          attn_scale: float, rope_theta: float = 0.0, heads=None, rows=None,
-                         dense_all: bool = False):
+                         dense_all: bool = False, with_abs_v: bool = False):
     """Prefill attention of the query positions start..start+T-1 of one sequence.
 
     q_pre [T, Hq, d] pre-RoPE queries; k_pre, v_in [N, Hkv, d] the appended
@@ -451,7 +451,9 @@ def prefill_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, start: int, n_sink: 
     masked by ``prefill_mask``; o = softmax(z) V and lse = log sum exp z, all
     in float64 as masked matrix products.  ``dense_all`` treats every head as a
     retrieval head (plain causal attention).  ``rows``: indices into the T
-    positions to evaluate (default all).  Returns {h: (o [T', G, d], lse [T', G])}.
+    positions to evaluate (default all).  Returns {h: (o [T', G, d], lse [T', G])},
+    with ``with_abs_v`` also the softmax-weighted mean of |v| per output
+    element (sum_j p_j |v_jd|, the scale of a relative error in the weights).
     """
     q_pre = np.asarray(q_pre, dtype=np.float64)
     T, hq, d = q_pre.shape
@@ -474,6 +476,8 @@ def prefill_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, start: int, n_sink: 
         w = np.exp(z - m)
         l = w.sum(axis=2, keepdims=True)
         res[h] = ((w @ vs) / l, (m + np.log(l))[:, :, 0])
+        if with_abs_v:
+            res[h] = res[h] + ((w @ np.abs(vs)) / l,)
     return res
 
 

@@ -166,7 +166,8 @@ def test_launch_mode_values():
         assert e.value.status == hws.HWS_ERR_INVALID_ARG
     assert hws.lib().hws_profile_stage_name(4) == b"tail"
     assert hws.lib().hws_profile_stage_name(5) == b"fused"
-    assert hws.lib().hws_profile_stage_name(6) == b""
+    assert hws.lib().hws_profile_stage_name(6) == b"prefill"
+    assert hws.lib().hws_profile_stage_name(7) == b""
 
 
 class _FakeT:
@@ -269,3 +270,48 @@ def test_effective_rank_validation_without_gpu():
     assert L.hws_effective_rank(8, 2, 64, None, 4096, 4096, 4096, ws, None) == hws.HWS_ERR_INVALID_ARG
     assert L.hws_effective_rank(8, 2, 64, 4096, 4096, 4096, 4096, 100, None) == hws.HWS_ERR_WORKSPACE
     assert L.hws_effective_rank(8, 2, 64, 4096, 4096, 4096, None, ws, None) == hws.HWS_ERR_WORKSPACE
+
+
+def _prefill(c, **kw):
+    args = dict(q=_FakeT((2, 300, 8, 128)), block_tables=_FakeT(), start_pos=_FakeT(), out=_FakeT(),
+                stream=0)
+    args.update(kw)
+    c.prefill(**args)
+
+
+def test_prefill_validation_without_gpu():
+    c = _ctx()
+    with pytest.raises(hws.HwsError) as e:
+        _prefill(c)
+    assert e.value.status == hws.HWS_ERR_STATE          # before bind
+    c.set_head_kinds([1, 0])
+    c.bind(4096, 4096, None, 4096, 4096)
+    cases = [
+        (dict(q=_FakeT((0, 5, 8, 128))), hws.HWS_ERR_INVALID_ARG),
+        (dict(q=_FakeT((1, 0, 8, 128))), hws.HWS_ERR_INVALID_ARG),
+        (dict(q=None), hws.HWS_ERR_INVALID_ARG),
+        (dict(out=None), hws.HWS_ERR_INVALID_ARG),
+        (dict(start_pos=None), hws.HWS_ERR_INVALID_ARG),
+        (dict(block_tables=None), hws.HWS_ERR_INVALID_ARG),
+        (dict(q=_FakeT((1, 32 * 16 + 1, 8, 128))), hws.HWS_ERR_CAPACITY),
+    ]
+    for kw, status in cases:
+        with pytest.raises(hws.HwsError) as e:
+            _prefill(c, **kw)
+        assert e.value.status == status, (kw, e.value)
+    L = hws.lib()
+    a = hws.PrefillArgs(1, 4, 2, 4096, 4096, 4096, 4096, None)       # dense must be 0 or 1
+    assert L.hws_prefill(c.handle, ctypes.byref(a), None) == hws.HWS_ERR_INVALID_ARG
+    assert L.hws_prefill(c.handle, None, None) == hws.HWS_ERR_INVALID_ARG
+    # fp8 caches and the local ring are not read by prefill
+    c8 = _ctx(kv=1)
+    c8.bind(4096, 4096, 4096, 4096, 4096)
+    with pytest.raises(hws.HwsError) as e:
+        _prefill(c8)
+    assert e.value.status == hws.HWS_ERR_UNSUPPORTED
+    cr = _ctx(ring=True, max_seqs=2)
+    cr.set_head_kinds([1, 0])
+    cr.bind(4096, 4096, None, 4096, 4096, 4096, 4096)
+    with pytest.raises(hws.HwsError) as e:
+        _prefill(cr)
+    assert e.value.status == hws.HWS_ERR_UNSUPPORTED

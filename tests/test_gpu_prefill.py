@@ -1,0 +1,151 @@
+"""GPU parity of the head-wise chunked prefill against the CPU oracle.
+
+Tolerance (from the arithmetic of the kernel), per query row:
+* logits: bf16 inputs with fp32 accumulation, as the decode scores, so each
+  logit is within delta = 1e-5 * attn_scale * |q| * max_j |k_j| (the decode
+  score bound in natural-log units); with RoPE the rotated query is split
+  into two bf16 parts, which adds 2^-15 * attn_scale * |q| * max_j |k_j|;
+* the softmax weights are rounded once to bf16 (8 significant bits: relative
+  error <= 2^-8) before the weighted sum of V, and a logit error delta moves
+  a normalised weight by at most 2 delta (relative).  Hence per element
+    |o_gpu - o_ref| <= (2^-8 + 2 delta) * sum_j p_j |v_jd| + 1e-5,
+  with p the oracle's weights (``with_abs_v``);
+* lse (summed from the unrounded weights): within 2e-5 + delta.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from head_wise_sparse_02_amd import hws
+from head_wise_sparse_02_amd import workloads as W
+from head_wise_sparse_02_amd.runner import DecodeSetup
+
+pytestmark = pytest.mark.gpu
+
+REL = 2.0 ** -8
+
+
+def _run(wl, n_tok, *, dense=False, rows=None, q_fn=None, stride=1):
+    print(f"\n[case] prefill {wl.name} B={wl.B} N={wl.seq_lens[:4]} n_tok={n_tok} G={wl.G} "
+          f"window={wl.window} sinks={wl.n_sink} rope={wl.rope_theta} dense={dense}", flush=True)
+    st = DecodeSetup(wl, keep_host=True)
+    starts = [wl.seq_lens[b] - n_tok for b in range(wl.B)]
+    qh = np.stack([wl.prefill_queries(b, n_tok) for b in range(wl.B)])
+    if q_fn is not None:
+        qh = q_fn(st, qh, starts)
+    q = torch.from_numpy(qh).to(torch.bfloat16).cuda()
+    sp = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    out, lse = st.prefill(q, sp, dense=dense)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    G = wl.G
+    rows = np.arange(0, n_tok, stride) if rows is None else np.asarray(rows)
+    worst = 0.0
+    for b in range(wl.B):
+        n = wl.seq_lens[b]
+        seq = st.host[b]
+        ref = O.prefill_sequence_ref(qh[b], seq.k[:n], seq.v[:n], head_kinds=wl.head_kinds, start=starts[b],
+                                     n_sink=wl.n_sink, window=wl.window, attn_scale=wl.attn_scale,
+                                     rope_theta=wl.rope_theta, rows=rows, dense_all=dense, with_abs_v=True)
+        for h in range(wl.Hkv):
+            o_ref, lse_ref, absv = ref[h]
+            qn = np.linalg.norm(qh[b, rows, h * G:(h + 1) * G].astype(np.float64), axis=2)     # [T', G]
+            kmax = float(np.linalg.norm(seq.k[:n, h].astype(np.float64), axis=1).max())
+            delta = (1e-5 + (2.0 ** -15 if wl.rope_theta > 0 else 0.0)) * wl.attn_scale * qn * kmax
+            o_gpu = out[b, rows, h * G:(h + 1) * G].astype(np.float64)
+            err = np.abs(o_gpu - o_ref)
+            bound = (REL + 2 * delta[:, :, None]) * absv + 1e-5
+            ratio = float((err / bound).max())
+            worst = max(worst, ratio)
+            assert ratio <= 1.0, f"output off at (b={b}, h={h}): {ratio:.3f} x tolerance"
+            el = np.abs(lse[b, rows, h * G:(h + 1) * G] - lse_ref)
+            assert (el <= 2e-5 + delta).all(), f"lse off at (b={b}, h={h}): {float(el.max())}"
+    print(f"[ok] worst error / tolerance = {worst:.3f}", flush=True)
+    return st, out, lse
+
+
+@pytest.mark.parametrize("n", [1, 17, 64, 65, 200, 259, 700, 1500])
+def test_prefill_whole_sequence(n):
+    """Chunks from position 0: partial query tiles, tiles across the window's
+    lower edge (window 256), the sink tile, a single position."""
+    _run(W.make_workload(1, n=n, extra={"needle_range": (0, None)}), n)
+
+
+@pytest.mark.parametrize("n_tok", [1, 33, 300])
+def test_prefill_chunk_at_offset(n_tok):
+    _run(W.make_workload(1, n=3000), n_tok)
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 2)])
+def test_prefill_group_sizes(hq, hkv):
+    _run(W.make_workload(1, n=900, Hq=hq, Hkv=hkv), 900)
+
+
+@pytest.mark.parametrize("n_tok", [700, 129])
+def test_prefill_rope(n_tok):
+    _run(W.make_workload(1, n=700, rope_theta=10000.0), n_tok)
+
+
+def test_prefill_dense_every_head():
+    _run(W.make_workload(1, n=1000), 1000, dense=True)
+
+
+def test_prefill_layer_shape_sampled_rows():
+    """32 query / 8 KV heads, 2 retrieval + 6 local heads, window 1024."""
+    wl = W.make_workload(2, n=2600, batch=2)
+    _run(wl, 2600, stride=13)
+
+
+def test_prefill_ragged_batch_offsets():
+    wl = W.make_workload(2, n=2000, batch=3)
+    wl.seq_lens = [900, 1300, 2000]
+    _run(wl, 500)
+
+
+def test_prefill_peaky_queries():
+    """Queries aimed at one earlier key (4x its direction): one weight near 1,
+    which rounds exactly, and many tiny ones."""
+    def aim(st, qh, starts):
+        rng = np.random.default_rng(5)
+        wl = st.wl
+        for b in range(wl.B):
+            for t in range(qh.shape[1]):
+                i = starts[b] + t
+                for hq in range(wl.Hq):
+                    h = hq // wl.G
+                    lo = max(0, i - wl.window + 1) if wl.head_kinds[h] == "local" else 0
+                    j = int(rng.integers(lo, i + 1))
+                    qh[b, t, hq] = W.bf16_rne((4.0 * st.host[b].k[j, h]).astype(np.float32))
+        return qh
+    _run(W.make_workload(1, n=800), 400, q_fn=aim)
+
+
+def test_prefill_negative_start_skips_sequence():
+    wl = W.make_workload(2, n=600, batch=2)
+    st = DecodeSetup(wl, keep_host=False)
+    q = torch.from_numpy(np.stack([wl.prefill_queries(b, 100) for b in range(2)])).to(torch.bfloat16).cuda()
+    out = torch.full((2, 100, wl.Hq, 128), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.full((2, 100, wl.Hq), 7.0, dtype=torch.float32, device="cuda")
+    sp = torch.tensor([500, -1], dtype=torch.int32, device="cuda")
+    st.ctx.prefill(q=q, block_tables=st.block_tables, start_pos=sp, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert (out[1] == 7.0).all() and (lse[1] == 7.0).all()
+    assert torch.isfinite(out[0]).all() and not (out[0] == 7.0).all()
+
+
+def test_prefill_profile_stage_and_repeat():
+    wl = W.make_workload(1, n=1200)
+    st = DecodeSetup(wl)
+    q = torch.from_numpy(wl.prefill_queries(0, 1200)[None]).to(torch.bfloat16).cuda()
+    sp = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st.ctx.profile_enable(True)
+    a, la = st.prefill(q, sp)
+    b, lb = st.prefill(q, sp)
+    prof = st.ctx.profile_read()
+    st.ctx.profile_enable(False)
+    assert prof["prefill"][1] == 2, prof
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
