@@ -25,6 +25,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_GBS = 8000.0          # MI355X HBM3E peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -69,6 +71,10 @@ def parse_args(argv=None):
                     help="one token set per KV head (kv) or per query head (query)")
     ap.add_argument("--ring", action="store_true",
                     help="local heads keep only sinks + window in a per-sequence ring (bf16 caches)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the head-wise chunked prefill (Llama-3-8B layer shape) instead of decode")
+    ap.add_argument("--prefill-len", type=int, default=32768,
+                    help="with --prefill: positions prefilled in one chunk from position 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -178,6 +184,93 @@ def cpu_baseline(wl, setup, reps: int) -> dict:
                       f"median of {len(times)} runs, {t:.2f} s per step"}
 
 
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak
+
+
+def prefill_flops(wl, n_tok: int, dense: bool) -> int:
+    """Algorithmic flops of one prefill of positions 0..n_tok-1: 4 * d per
+    (query row, attended key) (q.k and p v), over each head's key sets."""
+    n = np.arange(1, n_tok + 1, dtype=np.int64)              # keys of position i: i + 1
+    loc = np.minimum(n, wl.n_sink + wl.window)               # |sinks U window| of a context of n
+    per_head = {"retrieval": int(n.sum()), "local": int(loc.sum())}
+    total = 0
+    for kind in wl.head_kinds:
+        total += wl.G * per_head["retrieval" if dense else kind]
+    return 4 * wl.d * total
+
+
+def prefill_main(args) -> int:
+    import torch
+    from head_wise_sparse_02_amd import workloads as W
+    from head_wise_sparse_02_amd.runner import DecodeSetup
+
+    N = args.prefill_len
+    wl = W.make_workload(2, n=N, batch=1, seed=args.seed)
+    print(f"[bench] prefill: building a {N}-token cache (Llama-3-8B layer shape)", file=sys.stderr, flush=True)
+    st = DecodeSetup(wl, keep_host=not args.no_cpu_baseline)
+    qh = wl.prefill_queries(0, N)
+    q = torch.from_numpy(qh[None]).to(torch.bfloat16).cuda()
+    sp = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, N, wl.Hq, wl.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, N, wl.Hq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for dense in (False, True):
+        for _ in range(args.warmup):
+            st.ctx.prefill(q=q, block_tables=st.block_tables, start_pos=sp, out=out, lse=lse, dense=dense)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            st.ctx.prefill(q=q, block_tables=st.block_tables, start_pos=sp, out=out, lse=lse, dense=dense)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        st.ctx.profile_enable(True)
+        st.ctx.profile_read()
+        for _ in range(args.steps):
+            st.ctx.prefill(q=q, block_tables=st.block_tables, start_pos=sp, out=out, lse=lse, dense=dense)
+        torch.cuda.synchronize()
+        kms, calls = st.ctx.profile_read()["prefill"]
+        st.ctx.profile_enable(False)
+        fl = prefill_flops(wl, N, dense)
+        res[dense] = {"ms": ms, "kernel_us": 1000.0 * kms / calls, "flops": fl}
+    hw = res[False]
+    achieved = hw["flops"] / (hw["kernel_us"] * 1e-6) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        rows = np.linspace(0, N - 1, 32).astype(np.int64)          # a bounded sample of positions
+        seq = st.host[0]
+        t0 = time.perf_counter()
+        O.prefill_sequence_ref(qh, seq.k, seq.v, head_kinds=wl.head_kinds, start=0, n_sink=wl.n_sink,
+                               window=wl.window, attn_scale=wl.attn_scale, rows=rows)
+        t = time.perf_counter() - t0
+        cpu = {"value": round(rows.size / t, 2), "unit": "tokens/s", "cores": os.cpu_count() or 1,
+               "kind": "oracle", "sample": f"{rows.size} evenly spaced positions of the {N}-token chunk, "
+                                           f"all heads, {t:.2f} s"}
+    line = {
+        "metric": "head-wise chunked prefill tokens/s and achieved bf16 TFLOP/s, 1 GPU",
+        "value": round(N / (hw["ms"] / 1000.0), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(hw["ms"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and structure of the workload, no dataset or weights)",
+        "config": {"workload": "llama3_8b_layer_prefill", "batch": 1, "q_heads": wl.Hq,
+                   "kv_heads": wl.Hkv, "head_dim": wl.d, "prefill_len": N, "n_sink": wl.n_sink,
+                   "window": wl.window, "head_kinds": wl.head_kinds},
+        "dense_ms_per_step": round(res[True]["ms"], 4),
+        "speedup_vs_dense": round(res[True]["ms"] / hw["ms"], 3),
+        "dense_tflops": round(res[True]["flops"] / (res[True]["kernel_us"] * 1e-6) / 1e12, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "flops_per_launch": hw["flops"],
+                     "avg_launch_us": round(hw["kernel_us"], 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -187,6 +280,8 @@ def main(argv=None) -> int:
     if args.calibrate_copy:
         calibrate_copy()
         return 0
+    if args.prefill:
+        return prefill_main(args)
 
     import numpy as np
     import torch

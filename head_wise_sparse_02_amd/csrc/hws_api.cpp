@@ -531,7 +531,7 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {
   if (c.kv_dtype != HWS_KV_BF16) return fail(ctx, HWS_ERR_UNSUPPORTED, "prefill needs a bf16 cache");
   if (ctx->ring_rows > 0 && ctx->nL > 0)
     return fail(ctx, HWS_ERR_UNSUPPORTED, "prefill reads every head from the pages (no local_ring)");
-  const int rows = prefill_rows_per_tile();
+  const int rows = prefill_rows_per_tile(c.rope_theta > 0.f);
   const int qp = rows / ctx->G;
   const long long ntq = (a->n_tok + qp - 1) / qp;
   if ((long long)a->n_seq * c.num_kv_heads * ntq >= (1LL << 31))

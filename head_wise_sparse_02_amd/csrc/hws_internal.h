@@ -197,7 +197,7 @@ hipError_t launch_fused(const DecodeParams& p, int nwg, bool cooperative, hipStr
 hipError_t launch_append(const AppendParams& p, int kv_fp8, hipStream_t s);
 // Effective rank of the query-key kernels (fp64 Gram, Cholesky, Jacobi).
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
-int prefill_rows_per_tile();
+int prefill_rows_per_tile(bool rope);
 size_t rank_workspace_bytes(int hq, int hkv);
 hipError_t launch_effective_rank(int hq, int hkv, int d_model, const float* w_q, const float* w_k,
                                  float* eff_rank, void* workspace, hipStream_t s);

@@ -9,8 +9,10 @@
 // One workgroup per (sequence, KV head, tile of 128 query rows), a query row
 // being one (position, query head of the group) pair, so the G query heads of
 // a KV head share every K/V tile.  Key tiles of 64 keys (4 pages) go through
-// LDS, double-buffered: K in its page-blocked layout, V transposed to
-// [dim][key].  Each wave owns 32 query rows and computes
+// LDS, double-buffered: K in its page-blocked layout with the 16-byte chunks
+// of each row swizzled, V transposed to [dim][key]; the next tile's loads
+// are in flight during the current tile's products.  Each wave owns 32 query
+// rows and computes
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims from LDS,
 //                  B = the wave's queries, kept in registers)
 //   O^T += V^T P^T (A = 16 dims x 32 keys of V^T, B = P in bf16),
@@ -30,7 +32,14 @@ namespace hws {
 
 namespace {
 
-constexpr int PF_ROWS = 128;      // query rows per workgroup (4 waves x 32)
+// Waves per workgroup, 32 query rows each (8 waves sharing each tile measured
+// no faster: the loop is bound by its softmax and LDS reads, not by the tile
+// loads it shares).
+template <bool ROPE> struct PfShape {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROWS = 32 * WAVES;
+};
 constexpr int PF_KT = 64;         // keys per tile
 constexpr int VT_STRIDE = 68;     // padded key stride of the transposed V tile
 
@@ -45,9 +54,25 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ bf16x8 zero8() { return (bf16x8)(__bf16)0.f; }
 
+// Reductions over lanes i, i^16, i^32 with the gfx950 lane swaps (each call
+// returns the value pair {v[i], v[i^16]} or {v[i], v[i^32]} in some order).
+__device__ __forceinline__ float max_x16_x32(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_x16_x32(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int G, bool ROPE>
-__global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParams p) {
-  constexpr int QP = PF_ROWS / G;                  // query positions per tile
+__global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_kernel(PrefillParams p) {
+  constexpr int PF_THREADS = PfShape<ROPE>::THREADS;
+  constexpr int QP = PfShape<ROPE>::ROWS / G;      // query positions per tile
   __shared__ PfLds S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
@@ -135,40 +160,71 @@ __global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParam
   const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
   const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
   const int hslot = p.pool_slot[h];
-  const int kg = tid >> 4, dg = tid & 15;          // V loader: keys 4kg..4kg+3, dims 8dg..8dg+7
+  // Tile loaders: a tile is 4 pages x 256 16-byte chunks of K and 64 keys x
+  // 16 groups of 8 dims of V.  Each thread moves KC chunks of K (chunk
+  // tid + PF_THREADS * u, page c / 256) and KPT keys x 8 dims of V: keys
+  // KPT*kg.., dims 8dg.., kg varying fastest so that the lanes of a
+  // transposed write hit different banks.
+  constexpr int KC = 1024 / PF_THREADS, KPT = 1024 / PF_THREADS, NKG = 64 / KPT;
+  const int kg = tid % NKG, dg = tid / NKG;
+  // K in LDS: the 16-byte chunk q of row r (of a 32-dim block) is stored at
+  // chunk q ^ ((r >> 1) & 3), so the 8 lanes of an A-operand read (rows 0..7,
+  // one chunk) fall in 8 different bank groups
+  const int kcp = tid & 255;                       // chunk within its page
+  const int kw_row = (kcp >> 2) & 15;
+  const int kw_off = (kcp >> 6) * 512 + kw_row * 32 + 8 * ((kcp & 3) ^ ((kw_row >> 1) & 3));
+  const int kr_off = col * 32 + 8 * (quad ^ ((col >> 1) & 3));
 
-  // global -> registers for key tile kt (pages past the last query read page 0;
-  // V rows of keys past the last query are zeroed, so stale slots never reach P V)
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int kt) {
+  // global -> registers -> LDS for key tile kt.  Page ids are fetched one
+  // tile ahead (scalar loads, unconditional so none waits behind a branch);
+  // entries past the last query's page read page 0.  The registers are not
+  // touched until the tile is stored after the compute of the current tile,
+  // so the loads overlap it; V rows of keys past the last query are zeroed
+  // there, so stale slots never reach P V.
+  u32x4 kreg[KC], vreg[KPT];
+  const int lp_max = min(p.max_blocks - 1, tl / BS);
+  auto tile_pages = [&](int kt, int (&ids)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int lp = kt * 4 + u;
-      int blk = (lp * BS <= tl && lp < p.max_blocks) ? bt[lp] : 0;
-      blk = (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
-      kreg[u] = *reinterpret_cast<const u32x4*>(kpool + ((size_t)blk * p.Hp + hslot) * (BS * D) + tid * 8);
-    }
-    const int lp = kt * 4 + (kg >> 2);
-    int blk = (lp * BS <= tl && lp < p.max_blocks) ? bt[lp] : 0;
-    blk = (unsigned)blk < (unsigned)p.num_blocks ? blk : 0;
-    const uint16_t* vsrc = vpool + (((size_t)blk * p.Hp + hslot) * BS + (4 * kg & 15)) * D + 8 * dg;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(vsrc + e * D);
-      vreg[e] = kt * PF_KT + 4 * kg + e <= tl ? v : u32x4{0u, 0u, 0u, 0u};
+      const int blk = bt[min(lp, lp_max)];
+      ids[u] = ((lp <= lp_max) & ((unsigned)blk < (unsigned)p.num_blocks)) ? blk : 0;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto pick = [](const int (&ids)[4], int i) { return i == 0 ? ids[0] : (i == 1 ? ids[1] : (i == 2 ? ids[2] : ids[3])); };
+  auto load_tile = [&](const int (&ids)[4]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(&S.k[buf][u * (BS * D) + tid * 8]) = kreg[u];
+    for (int u = 0; u < KC; ++u) {
+      const int pg = (tid + PF_THREADS * u) >> 8;  // wave-uniform
+      kreg[u] = *reinterpret_cast<const u32x4*>(kpool + ((size_t)pick(ids, pg) * p.Hp + hslot) * (BS * D) + kcp * 8);
+    }
+    const int blk = pick(ids, (KPT * kg) >> 4);    // this thread's V page within the tile
+    const uint16_t* vsrc = vpool + (((size_t)blk * p.Hp + hslot) * BS + ((KPT * kg) & 15)) * D + 8 * dg;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) vreg[e] = *reinterpret_cast<const u32x4*>(vsrc + e * D);
+  };
+  auto store_tile = [&](int buf, int kt) {
+#pragma unroll
+    for (int u = 0; u < KC; ++u)
+      *reinterpret_cast<u32x4*>(&S.k[buf][((tid + PF_THREADS * u) >> 8) * (BS * D) + kw_off]) = kreg[u];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+      if (kt * PF_KT + KPT * kg + e > tl) vreg[e] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {                 // dims 8dg + 2w (low halves) and + 2w + 1 (high)
       const unsigned lo01 = (vreg[0][w] & 0xFFFFu) | (vreg[1][w] << 16);
-      const unsigned lo23 = (vreg[2][w] & 0xFFFFu) | (vreg[3][w] << 16);
       const unsigned hi01 = (vreg[0][w] >> 16) | (vreg[1][w] & 0xFFFF0000u);
-      const unsigned hi23 = (vreg[2][w] >> 16) | (vreg[3][w] & 0xFFFF0000u);
-      *reinterpret_cast<uint2*>(&S.vt[buf][(8 * dg + 2 * w) * VT_STRIDE + 4 * kg]) = make_uint2(lo01, lo23);
-      *reinterpret_cast<uint2*>(&S.vt[buf][(8 * dg + 2 * w + 1) * VT_STRIDE + 4 * kg]) = make_uint2(hi01, hi23);
+      uint16_t* d0 = &S.vt[buf][(8 * dg + 2 * w) * VT_STRIDE + KPT * kg];
+      uint16_t* d1 = &S.vt[buf][(8 * dg + 2 * w + 1) * VT_STRIDE + KPT * kg];
+      if constexpr (KPT == 4) {
+        const unsigned lo23 = (vreg[KPT > 2 ? 2 : 0][w] & 0xFFFFu) | (vreg[KPT > 3 ? 3 : 0][w] << 16);
+        const unsigned hi23 = (vreg[KPT > 2 ? 2 : 0][w] >> 16) | (vreg[KPT > 3 ? 3 : 0][w] & 0xFFFF0000u);
+        *reinterpret_cast<uint2*>(d0) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(d1) = make_uint2(hi01, hi23);
+      } else {
+        *reinterpret_cast<unsigned*>(d0) = lo01;
+        *reinterpret_cast<unsigned*>(d1) = hi01;
+      }
     }
   };
 
@@ -180,15 +236,19 @@ __global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParam
     for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float c2 = p.c2;
 
+  auto tile_at = [&](int it) { return it < ns_t ? it : lo_t + (it - ns_t); };
+  int ids[4];
   if (n_tiles > 0) {
-    load_tile(ns_t > 0 ? 0 : lo_t);
-    store_tile(0);
+    tile_pages(tile_at(0), ids);
+    load_tile(ids);
+    store_tile(0, tile_at(0));
   }
+  if (n_tiles > 1) tile_pages(tile_at(1), ids);
   __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
-    const int kt = it < ns_t ? it : lo_t + (it - ns_t);
+    const int kt = tile_at(it);
     const int buf = it & 1;
-    if (it + 1 < n_tiles) load_tile(it + 1 < ns_t ? it + 1 : lo_t + (it + 1 - ns_t));
+    if (it + 1 < n_tiles) load_tile(ids);             // tile it + 1, overlapping the compute below
 
     // S^T = K Q^T for the 4 key blocks x 2 query blocks of this wave
     f32x4 sacc[4][2];
@@ -201,7 +261,7 @@ __global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParam
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&S.k[buf][kb * (BS * D) + st * 512 + col * 32 + quad * 8]));
+            bf16x8, *reinterpret_cast<const u32x4*>(&S.k[buf][kb * (BS * D) + st * 512 + kr_off]));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           sacc[kb][qb] = mfma(a, qf[qb][st], sacc[kb][qb]);
@@ -218,14 +278,17 @@ __global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParam
     bf16x8 pb[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      if (!inside || !qok[qb]) {
-        const int qi = qpos[qb];
+      // (rows past the chunk's end hold zero queries: finite, and never written)
+      if (!inside) {                                   // wave-uniform
+        const int rel = qpos[qb] - key0 - 4 * quad;    // key offset 16*kb + i is causal iff <= rel
+        const int wlo = rel - p.window;                // ... and in the window iff > wlo
+        const int slim = ret ? 0x7FFFFFFF : p.n_sink - key0 - 4 * quad;   // ... or a sink iff < slim
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int j = key0 + 16 * kb + 4 * quad + i;
-            const bool ok = qok[qb] && j <= qi && (ret || j < p.n_sink || j > qi - p.window);
+            const int jo = 16 * kb + i;
+            const bool ok = (jo <= rel) & ((jo > wlo) | (jo < slim) | ret);
             sacc[kb][qb][i] = ok ? sacc[kb][qb][i] : NEG_INF;
           }
       }
@@ -234,8 +297,7 @@ __global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParam
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_x16_x32(mx);
       const float m_new = fmaxf(m[qb], mx * c2);
       const float m_use = m_new == NEG_INF ? 0.f : m_new;
       const float alpha = fast_exp2(m[qb] - m_use);
@@ -277,16 +339,15 @@ __global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParam
       }
     }
 
-    if (it + 1 < n_tiles) store_tile(buf ^ 1);
+    if (it + 2 < n_tiles) tile_pages(tile_at(it + 2), ids);
+    if (it + 1 < n_tiles) store_tile(buf ^ 1, tile_at(it + 1));
     __syncthreads();
   }
 
   // normalise and write: lane holds dims 16*db + 4*quad + i of its query row
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float l = lsum[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_x16_x32(lsum[qb]);
     if (!qok[qb]) continue;
     const int r = 32 * wave + 16 * qb + col;
     const int pl = r / G, g = r % G;
@@ -303,13 +364,14 @@ __global__ __launch_bounds__(256, ROPE ? 1 : 2) void prefill_kernel(PrefillParam
 
 template <int G>
 hipError_t launch_g(const PrefillParams& p, int nwg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (p.rope_theta > 0.f) return launch_kernel(prefill_kernel<G, true>, dim3(nwg), dim3(256), s, e0, e1, p);
-  return launch_kernel(prefill_kernel<G, false>, dim3(nwg), dim3(256), s, e0, e1, p);
+  if (p.rope_theta > 0.f)
+    return launch_kernel(prefill_kernel<G, true>, dim3(nwg), dim3(PfShape<true>::THREADS), s, e0, e1, p);
+  return launch_kernel(prefill_kernel<G, false>, dim3(nwg), dim3(PfShape<false>::THREADS), s, e0, e1, p);
 }
 
 }  // namespace
 
-int prefill_rows_per_tile() { return PF_ROWS; }
+int prefill_rows_per_tile(bool rope) { return rope ? PfShape<true>::ROWS : PfShape<false>::ROWS; }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const long long nwg = (long long)p.n_seq * (p.nR + p.nL) * p.ntq;
