@@ -56,7 +56,6 @@ struct TailLds {
   unsigned int cnt[TPT * TW];                 // per (u, wave) counts for ordered compaction
   float lse[MAXT][MAX_G];
   float wm[TW][MAX_G], wl[TW][MAX_G];
-  unsigned long long wsum[TW];
   unsigned long long above;
   unsigned int tmp[TW + 1];
   int bin;
@@ -140,33 +139,47 @@ __device__ __forceinline__ void count_flags(TailLds& S, unsigned int mask) {
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ unsigned long long wave_prefix(unsigned long long v, int lane) {
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
 // Scan `nbins` LDS bins from the top down, starting from `above`; the bin
 // where the cumulative sum first reaches `target` (-1 if it never does) and
-// the sum strictly above it.
+// the sum strictly above it.  One wave does it (no workgroup barrier between
+// the levels): lane l sums its run of nbins/64 bins from the top, a wave
+// prefix sum finds the run that crosses the target, and a second one over
+// that run's bins (one per lane) finds the bin.
 __device__ __forceinline__ void scan_top(TailLds& S, int nbins, unsigned long long above, unsigned long long target,
                          int& out_bin, unsigned long long& out_above) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = nbins / TT;                 // 8, 2 or 1
-  const int top = nbins - 1 - tid * per;
-  unsigned long long m = 0ull;
-  for (int k = 0; k < per; ++k) m += S.u.hist[top - k];
-  unsigned long long inc = m;
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long t = __shfl_up(inc, off);
-    if (lane >= off) inc += t;
-  }
-  if (lane == 63) S.wsum[wave] = inc;
-  if (tid == 0) S.bin = -1;
-  __syncthreads();
-  unsigned long long cm = above + inc - m;
-  for (int w2 = 0; w2 < wave; ++w2) cm += S.wsum[w2];
-  for (int k = 0; k < per; ++k) {
-    const unsigned long long nm = cm + S.u.hist[top - k];
-    if (cm < target && nm >= target) {        // one bin at most: the sum is monotone
-      S.bin = top - k;
-      S.above = cm;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int per = nbins / 64;               // 64, 16 or 8
+    const int top = nbins - 1 - tid * per;
+    unsigned long long m = 0ull;
+    // the lanes' runs are 8*per bytes apart: each lane starts its sum at a
+    // different offset of its run so that one read instruction spreads over
+    // the banks
+    for (int k = 0; k < per; ++k) m += S.u.hist[top - ((k + tid) & (per - 1))];
+    const unsigned long long inc = wave_prefix(m, tid);
+    const unsigned long long cm = above + inc - m;              // sum above this lane's run
+    const unsigned long long run = __ballot(cm < target && cm + m >= target);   // one lane at most
+    if (tid == 0) S.bin = -1;
+    if (run != 0ull) {                                          // wave-uniform
+      const int c = __ffsll((long long)run) - 1;
+      const int ctop = nbins - 1 - c * per;
+      const unsigned long long cabove = __shfl(cm, c);
+      const unsigned long long v = tid < per ? S.u.hist[ctop - tid] : 0ull;
+      const unsigned long long pre = cabove + wave_prefix(v, tid);
+      if (tid < per && pre - v < target && pre >= target) {      // one lane: the bin
+        S.bin = ctop - tid;
+        S.above = pre - v;
+      }
     }
-    cm = nm;
   }
   __syncthreads();
   out_bin = S.bin;
