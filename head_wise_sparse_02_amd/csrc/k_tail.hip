@@ -919,19 +919,29 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
 
   // ---- ordered compaction; the kept tokens' scores (the attention's logits)
   // go to LDS next to the row list, or to the scores buffer if too many ----
-  count_flags<true>(S, keep);
-  __syncthreads();
-  const int nrows = (int)scan_cnt(S);
-  const bool lds = nrows <= FUSED_LOGITS;
-  // this wave's TPT offsets are consecutive: read them all before any write
-  unsigned int base_off[TPT];
+  // A wave owns 2048 consecutive positions (slot u, lane): its kept tokens
+  // go after those of the waves before it, in (u, lane) order.
+  unsigned int wcount = 0u;
 #pragma unroll
-  for (int u = 0; u < TPT; ++u) base_off[u] = S.cnt[cnt_idx<true>(u, wave)];
+  for (int u = 0; u < TPT; ++u) wcount += (unsigned int)__popcll(__ballot((keep >> u) & 1u));
+  if (lane == 0) S.tmp[wave] = wcount;
+  __syncthreads();
+  unsigned int run = 0u, total = 0u;
+#pragma unroll
+  for (int w2 = 0; w2 < TW; ++w2) {
+    const unsigned int c = S.tmp[w2];
+    run += w2 < wave ? c : 0u;
+    total += c;
+  }
+  const int nrows = (int)total;
+  const bool lds = nrows <= FUSED_LOGITS;
 #pragma unroll
   for (int u = 0; u < TPT; ++u) {
     const unsigned long long bal = __ballot((keep >> u) & 1u);
+    const unsigned int slot0 = run;
+    run += (unsigned int)__popcll(bal);
     if ((keep >> u) & 1u) {
-      const int slot = base_off[u] + lane_rank(bal);
+      const int slot = slot0 + lane_rank(bal);
       const int off = slot_pos<true>(u, tid);
       S.u.rows[slot] = (unsigned short)off;
       const f32x4 v = (f32x4){x[u][0], x[u][1], x[u][2], x[u][3]};
