@@ -223,27 +223,34 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
   }
 }
 
+// One combine step of the processors in lanes i and i^X: symmetric in the
+// two lanes, so both end with the same (m, l, o).
+template <int G, int X>
+__device__ __forceinline__ void combine_lane_pairs(float (&m)[G], float (&l)[G], float (&o)[G][8]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float ma, mb, la, lb;
+    lane_pair<X>(m[g], ma, mb);
+    lane_pair<X>(l[g], la, lb);
+    const float mn = fmaxf(ma, mb);
+    const float ca = (mn == NEG_INF) ? 0.f : fast_exp2(ma - mn);
+    const float cb = (mn == NEG_INF) ? 0.f : fast_exp2(mb - mn);
+    l[g] = la * ca + lb * cb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float oa, ob;
+      lane_pair<X>(o[g][j], oa, ob);
+      o[g][j] = oa * ca + ob * cb;
+    }
+    m[g] = mn;
+  }
+}
+
 // Combine the 4 processors of a wave (lanes sub, sub+16, sub+32, sub+48).
 template <int G>
 __device__ __forceinline__ void combine_wave_procs(float (&m)[G], float (&l)[G], float (&o)[G][8]) {
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m2 = __shfl_xor(m[g], off);
-      const float l2 = __shfl_xor(l[g], off);
-      const float mn = fmaxf(m[g], m2);
-      const float c1 = (mn == NEG_INF) ? 0.f : fast_exp2(m[g] - mn);
-      const float c2 = (mn == NEG_INF) ? 0.f : fast_exp2(m2 - mn);
-      l[g] = l[g] * c1 + l2 * c2;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float o2 = __shfl_xor(o[g][j], off);
-        o[g][j] = o[g][j] * c1 + o2 * c2;
-      }
-      m[g] = mn;
-    }
-  }
+  combine_lane_pairs<G, 16>(m, l, o);
+  combine_lane_pairs<G, 32>(m, l, o);
 }
 
 }  // namespace hws

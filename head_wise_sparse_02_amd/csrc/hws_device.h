@@ -49,6 +49,24 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The values of lanes i and i^16 (X16) or i and i^32 (X32), in a lane-dependent
+// but register-independent order: a and b come from the same two lanes for
+// every call, so symmetric combines of several registers stay consistent.
+template <int X>
+__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
+  static_assert(X == 16 || X == 32, "lane swaps exist for 16 and 32");
+  const unsigned int u = __float_as_uint(v);
+  if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
 // OCP e4m3fn encode of an fp32 value: saturate to +-448, round to nearest
 // even, sign copied from the input.
 __device__ __forceinline__ uint8_t e4m3_encode(float y) {
