@@ -498,13 +498,24 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
     if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
     return HWS_OK;
   }
+  // AUTO otherwise: the whole selection in one launch (its workgroups hand
+  // the radix passes to each other, as in the single launch) when its tiles
+  // fit, then the per-stage attention and merge.
+  const int nws = (single && ctx->launch_mode == HWS_LAUNCH_AUTO) ? tail_grid(p, false, true) : 0;
+  const bool sel1 = nws > 0 && (long long)L.tail_ntiles <= (long long)TAIL_MAXT * nws;
   if (ctx->nR > 0) {
     const StageEv es = stage_events(ctx, 0);
     if ((e = launch_score(p, s, es.start, es.stop)) != hipSuccess) return hip_fail(ctx, e, "score launch");
     const StageEv ev = stage_events(ctx, 1);
-    for (int pass = 1; pass <= 3; ++pass) {
-      if ((e = launch_select(p, s, pass, pass == 1 ? ev.start : nullptr, pass == 3 ? ev.stop : nullptr)) != hipSuccess)
+    if (sel1) {
+      p.agg_out = 1;
+      if ((e = launch_tail(p, nws, false, s, ev.start, ev.stop, true)) != hipSuccess)
         return hip_fail(ctx, e, "select launch");
+    } else {
+      for (int pass = 1; pass <= 3; ++pass) {
+        if ((e = launch_select(p, s, pass, pass == 1 ? ev.start : nullptr, pass == 3 ? ev.stop : nullptr)) != hipSuccess)
+          return hip_fail(ctx, e, "select launch");
+      }
     }
   }
   const StageEv ea = stage_events(ctx, 2);

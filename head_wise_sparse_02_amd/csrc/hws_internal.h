@@ -111,6 +111,8 @@ struct DecodeParams {
   unsigned int* tail_sync;      // [0] error word, [1 + b*Hkv + h] split arrivals (zeroed by the scan)
   unsigned int* tail_ties;      // [tail_ntiles] ties at t* per tile
   int n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
+  int agg_out;                  // the single-launch selection ran: a_i is in agg, and the merge
+                                // checks the hand-off error word
   signed char ret_slot[MAX_KV];
   signed char ret_head[MAX_KV];
   signed char loc_head[MAX_KV];
@@ -186,9 +188,11 @@ hipError_t launch_emit(const DecodeParams& p, hipStream_t s);
 // workgroups of the instantiation `p` needs that the device holds at once (0
 // if there is no such instantiation, or `cooperative` and the device has no
 // cooperative launches).
-int tail_grid(const DecodeParams& p, bool cooperative);
+// select_only: the launch stops after the selection (threshold, top-k ties,
+// a_i in agg), for the per-stage attention and merge to follow.
+int tail_grid(const DecodeParams& p, bool cooperative, bool select_only = false);
 hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
-                       hipEvent_t e1);
+                       hipEvent_t e1, bool select_only = false);
 // The same with the scoring scan inside (full-dim scores, G = 4, bf16, no
 // RoPE: 0 workgroups otherwise); launch_fused also resets the selection state.
 int fused_grid(const DecodeParams& p, bool cooperative);

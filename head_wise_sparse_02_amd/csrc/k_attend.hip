@@ -255,8 +255,11 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
   __syncthreads();
   if (grp != 0) return;
   for (int k = 1; k < MERGE_GROUPS; ++k) merge_fold(M, L, O, gm[k], gl[k], go[k][d]);
-  p.out[((size_t)b * p.Hq + h * G + g) * D + d] = L > 0.f ? O / L : 0.f;
-  if (d == 0 && p.lse != nullptr) p.lse[(size_t)b * p.Hq + h * G + g] = (M + log2f(L)) * LN2;
+  // (a single-launch selection that gave up a wait leaves the error word set)
+  const bool bad = p.agg_out && __hip_atomic_load(&p.tail_sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+  const float nan = __builtin_nanf("");
+  p.out[((size_t)b * p.Hq + h * G + g) * D + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
+  if (d == 0 && p.lse != nullptr) p.lse[(size_t)b * p.Hq + h * G + g] = bad ? nan : (M + log2f(L)) * LN2;
   // |S| per KV head, or per query head with one set per query head
   if ((g == 0 || p.GS > 1) && d == 0 && p.sel_counts != nullptr) {
     int cnt;

@@ -625,7 +625,7 @@ __device__ __forceinline__ void select_tiles(const DecodeParams& p, TailLds& S, 
     const float c2 = p.c2_score;
     const float invG = 1.0f / (float)G;
     const float* sc = p.scores + row * p.Nmax * G;
-    float* agg = p.sel_idx != nullptr ? p.agg + row * p.Nagg : nullptr;
+    float* agg = (p.sel_idx != nullptr || p.agg_out) ? p.agg + row * p.Nagg : nullptr;
     // loads of UB tokens in flight at once; positions past the end re-read
     // the last token and are masked, so no load sits behind a per-lane branch
     constexpr int UB = G <= 2 ? 32 : (G == 4 ? 16 : 8);
@@ -727,6 +727,18 @@ __global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
     else empty_split<G>(p, b, h, split);
     finish_split<G>(p, S, b, h, hr);
   }
+}
+
+// Selection only: a_i of every token (written to agg), the threshold and the
+// top-k tie quota of every retrieval head (written to its state), in one
+// launch; the per-stage attention and merge follow.
+template <int G>
+__global__ __launch_bounds__(TT) void select_single_kernel(DecodeParams p) {
+  __shared__ TailLds S;
+  Tile tl[MAXT];
+  unsigned int keepm[MAXT];
+  int my_tiles = 0;
+  if (blockIdx.x < p.tail_ntiles) select_tiles<G>(p, S, tl, keepm, my_tiles, p.tail_sync);
 }
 
 // ---------------------------------------------------------------------------
@@ -1008,20 +1020,20 @@ void* pick_mode(const DecodeParams& p) {
   return p.nL == 0 ? TailKernel<G, false, 1>::fn() : TailKernel<G, false, 2>::fn();
 }
 
-void* pick_kernel(const DecodeParams& p) {
+void* pick_kernel(const DecodeParams& p, bool select_only) {
   switch (p.G) {
-    case 1: return pick_mode<1>(p);
-    case 2: return pick_mode<2>(p);
-    case 4: return pick_mode<4>(p);
-    case 8: return pick_mode<8>(p);
+    case 1: return select_only ? reinterpret_cast<void*>(&select_single_kernel<1>) : pick_mode<1>(p);
+    case 2: return select_only ? reinterpret_cast<void*>(&select_single_kernel<2>) : pick_mode<2>(p);
+    case 4: return select_only ? reinterpret_cast<void*>(&select_single_kernel<4>) : pick_mode<4>(p);
+    case 8: return select_only ? reinterpret_cast<void*>(&select_single_kernel<8>) : pick_mode<8>(p);
   }
   return nullptr;
 }
 
 }  // namespace
 
-int tail_grid(const DecodeParams& p, bool cooperative) {
-  void* fn = pick_kernel(p);
+int tail_grid(const DecodeParams& p, bool cooperative, bool select_only) {
+  void* fn = pick_kernel(p, select_only);
   if (fn == nullptr) return 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -1104,8 +1116,8 @@ hipError_t launch_fused(const DecodeParams& p, int nwg, bool cooperative, hipStr
 }
 
 hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
-                       hipEvent_t e1) {
-  void* fn = pick_kernel(p);
+                       hipEvent_t e1, bool select_only) {
+  void* fn = pick_kernel(p, select_only);
   if (fn == nullptr || nwg < 1) return hipErrorInvalidValue;
   return launch_single(fn, p, nwg, cooperative, s, e0, e1);
 }

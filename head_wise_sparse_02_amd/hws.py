@@ -258,7 +258,7 @@ class Context:
         self._check(self._L.hws_profile_enable(self.handle, int(enable)), "hws_profile_enable")
 
     def profile_read(self) -> dict:
-        n = 8
+        n = 16
         ms = (ctypes.c_double * n)()
         calls = (ctypes.c_int32 * n)()
         self._check(self._L.hws_profile_read(self.handle, ms, calls, n), "hws_profile_read")
