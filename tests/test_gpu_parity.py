@@ -168,6 +168,12 @@ def test_single_launch_matches_multi(cfg, kw):
     np.testing.assert_array_equal(a["scores"], m["scores"])
     np.testing.assert_allclose(a["out"], m["out"], rtol=0, atol=2e-5)
     np.testing.assert_allclose(a["lse"], m["lse"], rtol=0, atol=2e-5)
+    if not fused:
+        # AUTO: the selection in one launch, then the per-stage attention and
+        # merge: the sets of the three-launch selection, and the same kernels
+        # after it
+        for key in ("sel_counts", "sel_idx", "scores", "out", "lse"):
+            np.testing.assert_array_equal(auto[key], m[key])
 
 
 def test_fp8_codes_and_scales_bit_exact():
