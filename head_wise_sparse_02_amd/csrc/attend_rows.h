@@ -177,10 +177,7 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
           float a = qf[NEED_K ? g : 0][0] * kx[NEED_K ? u : 0][0];
 #pragma unroll
           for (int j = 1; j < 8; ++j) a = fmaf(qf[NEED_K ? g : 0][j], kx[NEED_K ? u : 0][j], a);
-          a += __shfl_xor(a, 1);
-          a += __shfl_xor(a, 2);
-          a += __shfl_xor(a, 4);
-          a += __shfl_xor(a, 8);
+          a = row16_sum(a);
           z[u][g] = ok[u] ? (FP8 ? a * ks[u] : a) : NEG_INF;
         }
       }

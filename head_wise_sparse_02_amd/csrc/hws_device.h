@@ -49,6 +49,18 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum over the 16 lanes of a row (lanes 16r..16r+15), in every lane of the
+// row: two quad swaps, then rotations of the row by 4 and by 8 (DPP moves, no
+// LDS).  Quads 0/2 and 1/3 associate the four quad sums differently, so the
+// lanes may differ in the last bit.
+__device__ __forceinline__ float row16_sum(float a) {
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x124, 0xF, 0xF, false));  // row_ror 4
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x128, 0xF, 0xF, false));  // row_ror 8
+  return a;
+}
+
 // The values of lanes i and i^16 (X16) or i and i^32 (X32), in a lane-dependent
 // but register-independent order: a and b come from the same two lanes for
 // every call, so symmetric combines of several registers stay consistent.
