@@ -213,7 +213,6 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
 // One workgroup per (sequence, KV head, query head): MERGE_GROUPS groups of D
 // threads (one per dim) fold every MERGE_GROUPS-th split online, 16 splits'
 // partials loaded at once, then group 0 combines the groups' results.
-constexpr int MERGE_GROUPS = 4;
 
 __device__ __forceinline__ void merge_fold(float& M, float& L, float& O, float m2, float l2, float o2) {
   if (!(l2 > 0.f)) return;                              // empty splits left no output
@@ -224,7 +223,7 @@ __device__ __forceinline__ void merge_fold(float& M, float& L, float& O, float m
   M = mt;
 }
 
-template <int G>
+template <int G, int MERGE_GROUPS>
 __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p) {
   constexpr int SB = 16;
   const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -315,15 +314,22 @@ hipError_t launch_attend(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hi
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const dim3 grid(p.G, p.Hkv, p.B), blk(D * MERGE_GROUPS);
+template <int MG>
+static hipError_t launch_merge_mg(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 grid(p.G, p.Hkv, p.B), blk(D * MG);
   switch (p.G) {
-    case 1: return launch_kernel(merge_kernel<1>, grid, blk, s, e0, e1, p);
-    case 2: return launch_kernel(merge_kernel<2>, grid, blk, s, e0, e1, p);
-    case 4: return launch_kernel(merge_kernel<4>, grid, blk, s, e0, e1, p);
-    case 8: return launch_kernel(merge_kernel<8>, grid, blk, s, e0, e1, p);
+    case 1: return launch_kernel(merge_kernel<1, MG>, grid, blk, s, e0, e1, p);
+    case 2: return launch_kernel(merge_kernel<2, MG>, grid, blk, s, e0, e1, p);
+    case 4: return launch_kernel(merge_kernel<4, MG>, grid, blk, s, e0, e1, p);
+    case 8: return launch_kernel(merge_kernel<8, MG>, grid, blk, s, e0, e1, p);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  // many splits (a long context in few workgroups' worth of heads): 8 groups
+  // of threads per output row halve the serial load rounds; otherwise 4
+  return p.max_splits >= 128 ? launch_merge_mg<8>(p, s, e0, e1) : launch_merge_mg<4>(p, s, e0, e1);
 }
 
 hipError_t launch_prep_q(const DecodeParams& p, hipStream_t s) {

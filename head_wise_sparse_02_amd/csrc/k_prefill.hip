@@ -37,8 +37,9 @@ namespace {
 // loads it shares).
 template <bool ROPE> struct PfShape {
   static constexpr int WAVES = 4;
+  static constexpr int QB = 2;                   // 16-row query blocks per wave
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int ROWS = 32 * WAVES;
+  static constexpr int ROWS = 16 * QB * WAVES;
 };
 constexpr int PF_KT = 64;         // keys per tile
 constexpr int VT_STRIDE = 68;     // padded key stride of the transposed V tile
@@ -73,6 +74,7 @@ template <int G, bool ROPE>
 __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_kernel(PrefillParams p) {
   constexpr int PF_THREADS = PfShape<ROPE>::THREADS;
   constexpr int QP = PfShape<ROPE>::ROWS / G;      // query positions per tile
+  constexpr int QB = PfShape<ROPE>::QB;
   __shared__ PfLds S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
@@ -115,12 +117,12 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   const int n_tiles = ns_t + max(0, last_t - lo_t + 1);
 
   // queries of this wave: rows 32*wave + 16*qb + col = (position, head) pairs
-  int qpos[2];
-  bool qok[2];
-  bf16x8 qf[2][4], ql[ROPE ? 2 : 1][4];
+  int qpos[QB];
+  bool qok[QB];
+  bf16x8 qf[QB][4], ql[ROPE ? QB : 1][4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = 32 * wave + 16 * qb + col;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = 16 * (QB * wave + qb) + col;
     const int pl = r / G, g = r % G;
     qok[qb] = pl < nq;
     qpos[qb] = t0 + pl;
@@ -228,12 +230,14 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     }
   };
 
-  float m[2] = {NEG_INF, NEG_INF}, lsum[2] = {0.f, 0.f};
-  f32x4 o[8][2];
+  float m[QB], lsum[QB];
+  f32x4 o[8][QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m[qb] = NEG_INF; lsum[qb] = 0.f; }
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float c2 = p.c2;
 
   auto tile_at = [&](int it) { return it < ns_t ? it : lo_t + (it - ns_t); };
@@ -251,11 +255,11 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     if (it + 1 < n_tiles) load_tile(ids);             // tile it + 1, overlapping the compute below
 
     // S^T = K Q^T for the 4 key blocks x 2 query blocks of this wave
-    f32x4 sacc[4][2];
+    f32x4 sacc[4][QB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(&S.k[buf][kb * (BS * D) + st * 512 + kr_off]));
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           sacc[kb][qb] = mfma(a, qf[qb][st], sacc[kb][qb]);
           if (ROPE) sacc[kb][qb] = mfma(a, ql[ROPE ? qb : 0][st], sacc[kb][qb]);
         }
@@ -275,9 +279,9 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     const int key0 = kt * PF_KT;
     const bool inside = key0 + PF_KT - 1 <= t0 &&
                         (ret || key0 + PF_KT - 1 < p.n_sink || key0 > tl - p.window);
-    bf16x8 pb[2][2];
+    bf16x8 pb[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       // (rows past the chunk's end hold zero queries: finite, and never written)
       if (!inside) {                                   // wave-uniform
         const int rel = qpos[qb] - key0 - 4 * quad;    // key offset 16*kb + i is causal iff <= rel
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
         const uint2 hi = *reinterpret_cast<const uint2*>(base + 16);
         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma(a, pb[qb][ks], o[db][qb]);
+        for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a, pb[qb][ks], o[db][qb]);
       }
     }
 
@@ -346,10 +350,10 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
 
   // normalise and write: lane holds dims 16*db + 4*quad + i of its query row
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float l = sum_x16_x32(lsum[qb]);
     if (!qok[qb]) continue;
-    const int r = 32 * wave + 16 * qb + col;
+    const int r = 16 * (QB * wave + qb) + col;
     const int pl = r / G, g = r % G;
     const size_t orow = ((size_t)s * p.n_tok + t0l + pl) * p.Hq + h * G + g;
     const float inv = l > 0.f ? 1.f / l : 0.f;
