@@ -183,7 +183,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   // touched until the tile is stored after the compute of the current tile,
   // so the loads overlap it; V rows of keys past the last query are zeroed
   // there, so stale slots never reach P V.
-  u32x4 kreg[KC], vreg[KPT];
+  u32x4 kA[KC], vA[KPT], kB[KC], vB[KPT];      // two tiles in flight
   const int lp_max = min(p.max_blocks - 1, tl / BS);
   auto tile_pages = [&](int kt, int (&ids)[4]) {
 #pragma unroll
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     }
   };
   auto pick = [](const int (&ids)[4], int i) { return i == 0 ? ids[0] : (i == 1 ? ids[1] : (i == 2 ? ids[2] : ids[3])); };
-  auto load_tile = [&](const int (&ids)[4]) {
+  auto load_tile = [&](const int (&ids)[4], u32x4 (&kreg)[KC], u32x4 (&vreg)[KPT]) {
 #pragma unroll
     for (int u = 0; u < KC; ++u) {
       const int pg = (tid + PF_THREADS * u) >> 8;  // wave-uniform
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
 #pragma unroll
     for (int e = 0; e < KPT; ++e) vreg[e] = *reinterpret_cast<const u32x4*>(vsrc + e * D);
   };
-  auto store_tile = [&](int buf, int kt) {
+  auto store_tile = [&](int buf, int kt, u32x4 (&kreg)[KC], u32x4 (&vreg)[KPT]) {
 #pragma unroll
     for (int u = 0; u < KC; ++u)
       *reinterpret_cast<u32x4*>(&S.k[buf][((tid + PF_THREADS * u) >> 8) * (BS * D) + kw_off]) = kreg[u];
@@ -241,19 +241,8 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   const float c2 = p.c2;
 
   auto tile_at = [&](int it) { return it < ns_t ? it : lo_t + (it - ns_t); };
-  int ids[4];
-  if (n_tiles > 0) {
-    tile_pages(tile_at(0), ids);
-    load_tile(ids);
-    store_tile(0, tile_at(0));
-  }
-  if (n_tiles > 1) tile_pages(tile_at(1), ids);
-  __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const int kt = tile_at(it);
-    const int buf = it & 1;
-    if (it + 1 < n_tiles) load_tile(ids);             // tile it + 1, overlapping the compute below
-
+  // compute on tile kt in LDS buffer buf
+  auto compute = [&](int buf, int kt) {
     // S^T = K Q^T for the 4 key blocks x 2 query blocks of this wave
     f32x4 sacc[4][QB];
 #pragma unroll
@@ -343,8 +332,36 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
       }
     }
 
-    if (it + 2 < n_tiles) tile_pages(tile_at(it + 2), ids);
-    if (it + 1 < n_tiles) store_tile(buf ^ 1, tile_at(it + 1));
+  };
+
+  // Tile t is loaded into register set t % 2 two tiles ahead of its use and
+  // stored to LDS buffer t % 2 after the compute of tile t - 1, so each load
+  // has the compute of two tiles to arrive.
+  int ids[4];
+  if (n_tiles > 0) {
+    tile_pages(tile_at(0), ids);
+    load_tile(ids, kA, vA);
+    store_tile(0, tile_at(0), kA, vA);
+  }
+  if (n_tiles > 1) { tile_pages(tile_at(1), ids); load_tile(ids, kB, vB); }
+  if (n_tiles > 2) { tile_pages(tile_at(2), ids); load_tile(ids, kA, vA); }
+  if (n_tiles > 3) tile_pages(tile_at(3), ids);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; it += 2) {
+    compute(0, tile_at(it));                          // even tile in buffer 0
+    if (it + 1 < n_tiles) store_tile(1, tile_at(it + 1), kB, vB);
+    if (it + 3 < n_tiles) {
+      load_tile(ids, kB, vB);                         // tile it + 3
+      if (it + 4 < n_tiles) tile_pages(tile_at(it + 4), ids);
+    }
+    __syncthreads();
+    if (it + 1 >= n_tiles) break;
+    compute(1, tile_at(it + 1));                      // odd tile in buffer 1
+    if (it + 2 < n_tiles) store_tile(0, tile_at(it + 2), kA, vA);
+    if (it + 4 < n_tiles) {
+      load_tile(ids, kA, vA);                         // tile it + 4
+      if (it + 5 < n_tiles) tile_pages(tile_at(it + 5), ids);
+    }
     __syncthreads();
   }
 
