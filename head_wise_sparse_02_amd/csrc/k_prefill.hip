@@ -10,8 +10,9 @@
 // being one (position, query head of the group) pair, so the G query heads of
 // a KV head share every K/V tile.  Key tiles of 64 keys (4 pages) go through
 // LDS, double-buffered: K in its page-blocked layout with the 16-byte chunks
-// of each row swizzled, V transposed to [dim][key]; the next tile's loads
-// are in flight during the current tile's products.  Each wave owns 32 query
+// of each row swizzled, V row-major (read back transposed by the gfx950
+// transposing LDS read); the next tiles' loads are in flight during the
+// current tile's products.  Each wave owns 32 query
 // rows and computes
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims from LDS,
 //                  B = the wave's queries, kept in registers)
@@ -42,11 +43,11 @@ template <bool ROPE> struct PfShape {
   static constexpr int ROWS = 16 * QB * WAVES;
 };
 constexpr int PF_KT = 64;         // keys per tile
-constexpr int VT_STRIDE = 68;     // padded key stride of the transposed V tile
+constexpr int V_STRIDE = 144;     // padded row of the V tile in LDS (288 B: 4 rows hit 4 bank groups)
 
 struct PfLds {
   uint16_t k[2][4 * BS * D];      // 4 pages, page-blocked layout (16 KiB each)
-  uint16_t vt[2][D * VT_STRIDE];  // V^T [dim][key] (17 KiB each)
+  uint16_t v[2][PF_KT * V_STRIDE]; // V [key][dim], rows padded (18 KiB each)
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -54,6 +55,9 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ bf16x8 zero8() { return (bf16x8)(__bf16)0.f; }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 // Reductions over lanes i, i^16, i^32 with the gfx950 lane swaps (each call
 // returns the value pair {v[i], v[i^16]} or {v[i], v[i^32]} in some order).
@@ -163,12 +167,9 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
   const int hslot = p.pool_slot[h];
   // Tile loaders: a tile is 4 pages x 256 16-byte chunks of K and 64 keys x
-  // 16 groups of 8 dims of V.  Each thread moves KC chunks of K (chunk
-  // tid + PF_THREADS * u, page c / 256) and KPT keys x 8 dims of V: keys
-  // KPT*kg.., dims 8dg.., kg varying fastest so that the lanes of a
-  // transposed write hit different banks.
-  constexpr int KC = 1024 / PF_THREADS, KPT = 1024 / PF_THREADS, NKG = 64 / KPT;
-  const int kg = tid % NKG, dg = tid / NKG;
+  // 16 chunks of 8 dims of V.  Each thread moves KC chunks of each (chunk
+  // tid + PF_THREADS * u: page c / 256; for V key c / 16, dims 8 (c % 16)).
+  constexpr int KC = 1024 / PF_THREADS;
   // K in LDS: the 16-byte chunk q of row r (of a 32-dim block) is stored at
   // chunk q ^ ((r >> 1) & 3), so the 8 lanes of an A-operand read (rows 0..7,
   // one chunk) fall in 8 different bank groups
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   // touched until the tile is stored after the compute of the current tile,
   // so the loads overlap it; V rows of keys past the last query are zeroed
   // there, so stale slots never reach P V.
-  u32x4 kA[KC], vA[KPT], kB[KC], vB[KPT];      // two tiles in flight
+  u32x4 kA[KC], vA[KC], kB[KC], vB[KC];        // two tiles in flight
   const int lp_max = min(p.max_blocks - 1, tl / BS);
   auto tile_pages = [&](int kt, int (&ids)[4]) {
 #pragma unroll
@@ -194,39 +195,23 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     }
   };
   auto pick = [](const int (&ids)[4], int i) { return i == 0 ? ids[0] : (i == 1 ? ids[1] : (i == 2 ? ids[2] : ids[3])); };
-  auto load_tile = [&](const int (&ids)[4], u32x4 (&kreg)[KC], u32x4 (&vreg)[KPT]) {
+  auto load_tile = [&](const int (&ids)[4], u32x4 (&kreg)[KC], u32x4 (&vreg)[KC]) {
 #pragma unroll
     for (int u = 0; u < KC; ++u) {
-      const int pg = (tid + PF_THREADS * u) >> 8;  // wave-uniform
-      kreg[u] = *reinterpret_cast<const u32x4*>(kpool + ((size_t)pick(ids, pg) * p.Hp + hslot) * (BS * D) + kcp * 8);
+      const int c = tid + PF_THREADS * u;
+      const size_t page = (size_t)pick(ids, c >> 8) * p.Hp + hslot;   // wave-uniform
+      kreg[u] = *reinterpret_cast<const u32x4*>(kpool + page * (BS * D) + kcp * 8);
+      vreg[u] = *reinterpret_cast<const u32x4*>(vpool + (page * BS + ((c >> 4) & 15)) * D + 8 * (c & 15));
     }
-    const int blk = pick(ids, (KPT * kg) >> 4);    // this thread's V page within the tile
-    const uint16_t* vsrc = vpool + (((size_t)blk * p.Hp + hslot) * BS + ((KPT * kg) & 15)) * D + 8 * dg;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) vreg[e] = *reinterpret_cast<const u32x4*>(vsrc + e * D);
   };
-  auto store_tile = [&](int buf, int kt, u32x4 (&kreg)[KC], u32x4 (&vreg)[KPT]) {
+  auto store_tile = [&](int buf, int kt, u32x4 (&kreg)[KC], u32x4 (&vreg)[KC]) {
 #pragma unroll
-    for (int u = 0; u < KC; ++u)
-      *reinterpret_cast<u32x4*>(&S.k[buf][((tid + PF_THREADS * u) >> 8) * (BS * D) + kw_off]) = kreg[u];
-#pragma unroll
-    for (int e = 0; e < KPT; ++e)
-      if (kt * PF_KT + KPT * kg + e > tl) vreg[e] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {                 // dims 8dg + 2w (low halves) and + 2w + 1 (high)
-      const unsigned lo01 = (vreg[0][w] & 0xFFFFu) | (vreg[1][w] << 16);
-      const unsigned hi01 = (vreg[0][w] >> 16) | (vreg[1][w] & 0xFFFF0000u);
-      uint16_t* d0 = &S.vt[buf][(8 * dg + 2 * w) * VT_STRIDE + KPT * kg];
-      uint16_t* d1 = &S.vt[buf][(8 * dg + 2 * w + 1) * VT_STRIDE + KPT * kg];
-      if constexpr (KPT == 4) {
-        const unsigned lo23 = (vreg[KPT > 2 ? 2 : 0][w] & 0xFFFFu) | (vreg[KPT > 3 ? 3 : 0][w] << 16);
-        const unsigned hi23 = (vreg[KPT > 2 ? 2 : 0][w] >> 16) | (vreg[KPT > 3 ? 3 : 0][w] & 0xFFFF0000u);
-        *reinterpret_cast<uint2*>(d0) = make_uint2(lo01, lo23);
-        *reinterpret_cast<uint2*>(d1) = make_uint2(hi01, hi23);
-      } else {
-        *reinterpret_cast<unsigned*>(d0) = lo01;
-        *reinterpret_cast<unsigned*>(d1) = hi01;
-      }
+    for (int u = 0; u < KC; ++u) {
+      const int c = tid + PF_THREADS * u;
+      *reinterpret_cast<u32x4*>(&S.k[buf][(c >> 8) * (BS * D) + kw_off]) = kreg[u];
+      const int key = c >> 4;
+      *reinterpret_cast<u32x4*>(&S.v[buf][key * V_STRIDE + 8 * (c & 15)]) =
+          kt * PF_KT + key <= tl ? vreg[u] : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -323,10 +308,16 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint16_t* base = &S.vt[buf][(16 * db + col) * VT_STRIDE + 32 * ks + 4 * quad];
-        const uint2 lo = *reinterpret_cast<const uint2*>(base);
-        const uint2 hi = *reinterpret_cast<const uint2*>(base + 16);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        // transposing reads (ds_read_b64_tr_b16): within each 16-lane group,
+        // lane i gets element i % 4 of the 8-byte chunks addressed by lanes
+        // 4j + i / 4 (j = 0..3); lane k addresses dims 16db + 4 (k % 4) .. + 3
+        // of key k / 4 of the quad's 4 keys, so lane i (= col) receives dim
+        // 16db + i of those 4 keys: keys 32ks + 4 quad + 0..3, then + 16
+        uint16_t* base = &S.v[buf][(32 * ks + 4 * quad + (col >> 2)) * V_STRIDE + 16 * db + 4 * (col & 3)];
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)base);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(base + 16 * V_STRIDE));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, (v8i16){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a, pb[qb][ks], o[db][qb]);
       }
