@@ -306,10 +306,13 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  *    runtime guarantees that all workgroups are resident (costs a few tens of
  *    microseconds of launch latency per call).
  *  HWS_LAUNCH_AUTO (the default): HWS_LAUNCH_SINGLE where the scan runs
- *    inside the launch (it is then faster), else HWS_LAUNCH_MULTI.  The
+ *    inside the launch (it is then faster); otherwise the scoring kernel,
+ *    then the selection as ONE launch of the single-launch kind (same waits
+ *    and time-out; one set per KV head, when its tiles fit the device), then
+ *    the per-stage attention and merge; otherwise HWS_LAUNCH_MULTI.  (The
  *    single launch without the scan gathers each tile's kept rows in one
- *    workgroup, which loses to the per-stage kernels when many rows are kept
- *    or many local-head chunks run beside it.
+ *    workgroup, which loses to the per-stage attention when many rows are
+ *    kept or many local-head chunks run beside it.)
  * All shapes select the same token sets; outputs differ only by the fp32
  * rounding order of the attention splits.  Returns HWS_ERR_INVALID_ARG for an
  * unknown mode. */
