@@ -11,8 +11,8 @@
 // a KV head share every K/V tile.  Key tiles of 64 keys (4 pages) go through
 // LDS, double-buffered: K in its page-blocked layout with the 16-byte chunks
 // of each row swizzled, V row-major (read back transposed by the gfx950
-// transposing LDS read); the next tiles' loads are in flight during the
-// current tile's products.  Each wave owns 32 query
+// transposing LDS read); each tile's loads are issued two tiles ahead, so
+// they are in flight during two tiles' products.  Each wave owns 32 query
 // rows and computes
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims from LDS,
 //                  B = the wave's queries, kept in registers)
