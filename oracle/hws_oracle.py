@@ -442,12 +442,14 @@ def prefill_mask(positions, n_keys: int, *, kind: str, n_sink: int, window: int)
 
 def prefill_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, start: int, n_sink: int, window: int,
                          attn_scale: float, rope_theta: float = 0.0, heads=None, rows=None,
-                         dense_all: bool = False, with_abs_v: bool = False):
+                         dense_all: bool = False, with_abs_v: bool = False, kv_fp8: bool = False,
+                         segments=None):
     """Prefill attention of the query positions start..start+T-1 of one sequence.
 
     q_pre [T, Hq, d] pre-RoPE queries; k_pre, v_in [N, Hkv, d] the appended
     rows (bf16-exact, N >= start + T).  For KV head h and its query heads g:
-    z = attn_scale * rope(q_g, i) . k_j over the stored (rotated, bf16) keys,
+    z = attn_scale * rope(q_g, i) . k_j over the stored keys (rotated, bf16, or
+    the fp8-decoded rows of the append calls ``segments`` with ``kv_fp8``),
     masked by ``prefill_mask``; o = softmax(z) V and lse = log sum exp z, all
     in float64 as masked matrix products.  ``dense_all`` treats every head as a
     retrieval head (plain causal attention).  ``rows``: indices into the T
@@ -464,9 +466,11 @@ def prefill_sequence_ref(q_pre, k_pre, v_in, *, head_kinds, start: int, n_sink: 
     keys = np.arange(n)
     res = {}
     for h in (range(hkv) if heads is None else heads):
-        ks = stored_rows(k_pre[:, h, :], keys, rope_theta=rope_theta, kv_fp8=False, segments=None,
+        segs = segments if segments is not None else [(0, n)]
+        ks = stored_rows(k_pre[:, h, :], keys, rope_theta=rope_theta, kv_fp8=kv_fp8, segments=segs,
                          rotate=True)
-        vs = np.asarray(v_in[:, h, :], dtype=np.float64)
+        vs = stored_rows(v_in[:, h, :], keys, rope_theta=rope_theta, kv_fp8=kv_fp8, segments=segs,
+                         rotate=False)
         kind = "retrieval" if dense_all else head_kinds[h]
         mask = prefill_mask(pos, n, kind=kind, n_sink=n_sink, window=window)      # [T', n]
         qr = rope(q_pre[sel, h * G:(h + 1) * G, :], pos[:, None], rope_theta)    # [T', G, d]

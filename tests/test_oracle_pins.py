@@ -571,25 +571,35 @@ def test_prefill_local_mask_brute_force():
         np.testing.assert_array_equal(full, np.arange(100)[None, :] <= pos[:, None])
 
 
-@pytest.mark.parametrize("rope_theta", [0.0, 10000.0])
-def test_prefill_rows_are_decode_steps(rope_theta):
+@pytest.mark.parametrize("rope_theta,kv_fp8", [(0.0, False), (10000.0, False), (0.0, True)])
+def test_prefill_rows_are_decode_steps(rope_theta, kv_fp8):
     """Row i of a chunk is the decode of the prefix 0..i: dense for a
     retrieval head (top-p = 1 keeps every token), sinks + window for a local
-    head (both pinned separately above)."""
+    head (both pinned separately above); with fp8 storage both read the rows
+    the append calls stored (the decode's fp8 path is pinned above)."""
     q, k, v = _prefill_seq(n=500, t=120)
     start = 380
     rows = [0, 1, 57, 118, 119]
     sc = 1 / np.sqrt(128)
+    segs = [(0, 380), (380, 120)]
     res = O.prefill_sequence_ref(q, k, v, head_kinds=["retrieval", "local"], start=start, n_sink=4,
-                                 window=64, attn_scale=sc, rope_theta=rope_theta, rows=rows)
+                                 window=64, attn_scale=sc, rope_theta=rope_theta, rows=rows,
+                                 kv_fp8=kv_fp8, segments=segs)
+    n = k.shape[0]
+    # the rows the cache holds after the appends (fp8: page scales set by the
+    # call that writes slot 0 of the page, over every row it writes there)
+    store = {h: (O.stored_rows(k[:, h], np.arange(n), rope_theta=rope_theta, kv_fp8=kv_fp8, segments=segs,
+                               rotate=True),
+                 O.stored_rows(v[:, h], np.arange(n), rope_theta=rope_theta, kv_fp8=kv_fp8, segments=segs,
+                               rotate=False)) for h in range(2)}
     for r, t in enumerate(rows):
         i = start + t
-        dec = O.decode_sequence_ref(q[t], k[:i + 1], v[:i + 1], head_kinds=["retrieval", "local"],
-                                    score_mode="full", select_mode="top_p", top_p=1.0, n_sink=4,
+        for h, kind in enumerate(["retrieval", "local"]):
+            dec = O.decode_head_ref(q[t, 4 * h:4 * h + 4], k[:i + 1, h], store[h][0][:i + 1], store[h][1][:i + 1],
+                                    kind=kind, score_mode="full", select_mode="top_p", top_p=1.0, n_sink=4,
                                     window=64, attn_scale=sc, rope_theta=rope_theta)
-        for h in range(2):
-            np.testing.assert_allclose(res[h][0][r], dec[h]["o64"], rtol=0, atol=1e-12)
-            np.testing.assert_allclose(res[h][1][r], dec[h]["lse64"], rtol=1e-13)
+            np.testing.assert_allclose(res[h][0][r], dec["o64"], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(res[h][1][r], dec["lse64"], rtol=1e-13)
 
 
 def test_prefill_closed_forms():
