@@ -75,6 +75,8 @@ def parse_args(argv=None):
                     help="time the head-wise chunked prefill (Llama-3-8B layer shape) instead of decode")
     ap.add_argument("--prefill-len", type=int, default=32768,
                     help="with --prefill: positions prefilled in one chunk from position 0")
+    ap.add_argument("--prefill-fp8", action="store_true",
+                    help="with --prefill: the cache in fp8 (e4m3 with per-page scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -202,10 +204,12 @@ def prefill_flops(wl, n_tok: int, dense: bool) -> int:
 def prefill_main(args) -> int:
     import torch
     from head_wise_sparse_02_amd import workloads as W
-    from head_wise_sparse_02_amd.runner import DecodeSetup
+    from head_wise_sparse_02_amd.runner import DecodeSetup, append_segments
 
     N = args.prefill_len
     wl = W.make_workload(2, n=N, batch=1, seed=args.seed)
+    if args.prefill_fp8:
+        wl.kv_dtype = "fp8"
     print(f"[bench] prefill: building a {N}-token cache (Llama-3-8B layer shape)", file=sys.stderr, flush=True)
     st = DecodeSetup(wl, keep_host=not args.no_cpu_baseline)
     qh = wl.prefill_queries(0, N)
@@ -244,7 +248,8 @@ def prefill_main(args) -> int:
         seq = st.host[0]
         t0 = time.perf_counter()
         O.prefill_sequence_ref(qh, seq.k, seq.v, head_kinds=wl.head_kinds, start=0, n_sink=wl.n_sink,
-                               window=wl.window, attn_scale=wl.attn_scale, rows=rows)
+                               window=wl.window, attn_scale=wl.attn_scale, rows=rows,
+                               kv_fp8=args.prefill_fp8, segments=append_segments(N))
         t = time.perf_counter() - t0
         cpu = {"value": round(rows.size / t, 2), "unit": "tokens/s", "cores": os.cpu_count() or 1,
                "kind": "oracle", "sample": f"{rows.size} evenly spaced positions of the {N}-token chunk, "
@@ -255,7 +260,8 @@ def prefill_main(args) -> int:
         "warmup": args.warmup, "ms_per_step": round(hw["ms"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; shapes and structure of the workload, no dataset or weights)",
-        "config": {"workload": "llama3_8b_layer_prefill", "batch": 1, "q_heads": wl.Hq,
+        "config": {"workload": "llama3_8b_layer_prefill" + ("_fp8" if args.prefill_fp8 else ""),
+                   "kv_dtype": wl.kv_dtype, "batch": 1, "q_heads": wl.Hq,
                    "kv_heads": wl.Hkv, "head_dim": wl.d, "prefill_len": N, "n_sink": wl.n_sink,
                    "window": wl.window, "head_kinds": wl.head_kinds},
         "dense_ms_per_step": round(res[True]["ms"], 4),

@@ -539,7 +539,6 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {
     return fail(ctx, HWS_ERR_INVALID_ARG, "null device pointer (q, block_tables, start_pos or out)");
   if ((long long)a->n_tok > (long long)c.max_blocks_per_seq * BS)
     return fail(ctx, HWS_ERR_CAPACITY, "n_tok = %d exceeds the block table", a->n_tok);
-  if (c.kv_dtype != HWS_KV_BF16) return fail(ctx, HWS_ERR_UNSUPPORTED, "prefill needs a bf16 cache");
   if (ctx->ring_rows > 0 && ctx->nL > 0)
     return fail(ctx, HWS_ERR_UNSUPPORTED, "prefill reads every head from the pages (no local_ring)");
   const int rows = prefill_rows_per_tile(c.rope_theta > 0.f);
@@ -566,6 +565,7 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {
   p.start_pos = a->start_pos;
   p.k_pool = ctx->buf.k_pool;
   p.v_pool = ctx->buf.v_pool;
+  p.kv_scales = c.kv_dtype == HWS_KV_FP8_E4M3 ? ctx->buf.kv_scales : nullptr;
   p.out = a->out;
   p.lse = a->lse;
   std::memcpy(p.pool_slot, ctx->pool_slot, sizeof(p.pool_slot));

@@ -156,6 +156,7 @@ struct PrefillParams {
   const int* start_pos;         // [n_seq]
   const void* k_pool;
   const void* v_pool;
+  const float* kv_scales;       // FP8 pages: [blocks][Hp][2]; null for bf16
   float* out;                   // [n_seq][n_tok][Hq][D]
   float* lse;                   // [n_seq][n_tok][Hq] or null
   signed char ret_head[MAX_KV];

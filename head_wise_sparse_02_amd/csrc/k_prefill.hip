@@ -27,6 +27,14 @@
 // With RoPE on, queries are rotated in fp64 at their position and split as
 // q = hi + lo (two bf16 parts), so S keeps fp32-level accuracy; P is rounded
 // to bf16 for the P V product.
+//
+// FP8 pages: the e4m3 codes are widened to bf16 on their way into LDS (exact:
+// every e4m3 value is a bf16 value), so the products are those of the bf16
+// path on the codes; each 16-key block of S is then multiplied by its page's
+// K scale, and each weight by its page's V scale before it is rounded to
+// bf16 for P V (the softmax sum is taken from the unscaled weights).  Both
+// scales enter the exponent: the weight times the V scale is
+// exp2(s * c2 * ks + log2(vs) - m), for raw product s and the running max m.
 #include "hws_device.h"
 
 namespace hws {
@@ -45,10 +53,29 @@ template <bool ROPE> struct PfShape {
 constexpr int PF_KT = 64;         // keys per tile
 constexpr int V_STRIDE = 144;     // padded row of the V tile in LDS (288 B: 4 rows hit 4 bank groups)
 
-struct PfLds {
+struct alignas(16) PfLds {        // 16-byte aligned: the tile moves as 16-byte LDS accesses
   uint16_t k[2][4 * BS * D];      // 4 pages, page-blocked layout (16 KiB each)
   uint16_t v[2][PF_KT * V_STRIDE]; // V [key][dim], rows padded (18 KiB each)
+  float sc[2][8];                 // FP8: K scales of the 4 pages, then V scales
 };
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 8 elements of a row as stored: 16 bytes of bf16 or 8 bytes of e4m3 codes
+template <bool FP8> struct PfChunk { typedef u32x4 T; };
+template <> struct PfChunk<true> { typedef u32x2 T; };
+
+__device__ __forceinline__ u32x4 chunk_bf16(u32x4 w) { return w; }
+
+// 8 e4m3 codes -> 8 bf16 (exact; the conversion's scale operand is 1)
+__device__ __forceinline__ u32x4 chunk_bf16(u32x2 w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  auto cvt = [](unsigned x, bool hi) {
+    return hi ? __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true))
+              : __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+  };
+  return u32x4{cvt(w[0], false), cvt(w[0], true), cvt(w[1], false), cvt(w[1], true)};
+}
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -74,7 +101,7 @@ __device__ __forceinline__ float sum_x16_x32(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int G, bool ROPE>
+template <int G, bool ROPE, bool FP8>
 __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_kernel(PrefillParams p) {
   constexpr int PF_THREADS = PfShape<ROPE>::THREADS;
   constexpr int QP = PfShape<ROPE>::ROWS / G;      // query positions per tile
@@ -163,9 +190,12 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   }
 
   const int* bt = p.block_tables + (size_t)s * p.max_blocks;
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
+  typedef typename PfChunk<FP8>::T Chunk;
+  constexpr int ES = FP8 ? 1 : 2;                  // bytes per stored element
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(p.v_pool);
   const int hslot = p.pool_slot[h];
+  const float* scales = FP8 ? p.kv_scales + 2 * hslot : nullptr;   // (K, V) scale of page 0 of this head
   // Tile loaders: a tile is 4 pages x 256 16-byte chunks of K and 64 keys x
   // 16 chunks of 8 dims of V.  Each thread moves KC chunks of each (chunk
   // tid + PF_THREADS * u: page c / 256; for V key c / 16, dims 8 (c % 16)).
@@ -183,35 +213,55 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   // entries past the last query's page read page 0.  The registers are not
   // touched until the tile is stored after the compute of the current tile,
   // so the loads overlap it; V rows of keys past the last query are zeroed
-  // there, so stale slots never reach P V.
-  u32x4 kA[KC], vA[KC], kB[KC], vB[KC];        // two tiles in flight
+  // there, so stale slots never reach P V.  FP8: the page scales travel with
+  // the tile (1 for entries past the last query's page, whose keys are all
+  // masked, so that no unwritten scale reaches the softmax).
+  Chunk kA[KC], vA[KC], kB[KC], vB[KC];        // two tiles in flight
+  float scA[FP8 ? 8 : 1], scB[FP8 ? 8 : 1];
   const int lp_max = min(p.max_blocks - 1, tl / BS);
+  int live = 0;                                // FP8: bit u set if page u of the tile is before lp_max
   auto tile_pages = [&](int kt, int (&ids)[4]) {
+    live = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int lp = kt * 4 + u;
       const int blk = bt[min(lp, lp_max)];
       ids[u] = ((lp <= lp_max) & ((unsigned)blk < (unsigned)p.num_blocks)) ? blk : 0;
+      live |= (lp <= lp_max) << u;
     }
   };
   auto pick = [](const int (&ids)[4], int i) { return i == 0 ? ids[0] : (i == 1 ? ids[1] : (i == 2 ? ids[2] : ids[3])); };
-  auto load_tile = [&](const int (&ids)[4], u32x4 (&kreg)[KC], u32x4 (&vreg)[KC]) {
+  auto load_tile = [&](const int (&ids)[4], Chunk (&kreg)[KC], Chunk (&vreg)[KC], float (&sc)[FP8 ? 8 : 1]) {
 #pragma unroll
     for (int u = 0; u < KC; ++u) {
       const int c = tid + PF_THREADS * u;
       const size_t page = (size_t)pick(ids, c >> 8) * p.Hp + hslot;   // wave-uniform
-      kreg[u] = *reinterpret_cast<const u32x4*>(kpool + page * (BS * D) + kcp * 8);
-      vreg[u] = *reinterpret_cast<const u32x4*>(vpool + (page * BS + ((c >> 4) & 15)) * D + 8 * (c & 15));
+      kreg[u] = *reinterpret_cast<const Chunk*>(kpool + (page * (BS * D) + kcp * 8) * ES);
+      vreg[u] = *reinterpret_cast<const Chunk*>(vpool + ((page * BS + ((c >> 4) & 15)) * D + 8 * (c & 15)) * ES);
+    }
+    if constexpr (FP8) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x2 s2 = *reinterpret_cast<const f32x2*>(scales + (size_t)ids[u] * (2 * p.Hp));
+        sc[u] = (live >> u) & 1 ? s2.x : 1.f;
+        sc[4 + u] = (live >> u) & 1 ? s2.y : 1.f;
+      }
     }
   };
-  auto store_tile = [&](int buf, int kt, u32x4 (&kreg)[KC], u32x4 (&vreg)[KC]) {
+  auto store_tile = [&](int buf, int kt, Chunk (&kreg)[KC], Chunk (&vreg)[KC], float (&sc)[FP8 ? 8 : 1]) {
 #pragma unroll
     for (int u = 0; u < KC; ++u) {
       const int c = tid + PF_THREADS * u;
-      *reinterpret_cast<u32x4*>(&S.k[buf][(c >> 8) * (BS * D) + kw_off]) = kreg[u];
+      *reinterpret_cast<u32x4*>(&S.k[buf][(c >> 8) * (BS * D) + kw_off]) = chunk_bf16(kreg[u]);
       const int key = c >> 4;
       *reinterpret_cast<u32x4*>(&S.v[buf][key * V_STRIDE + 8 * (c & 15)]) =
-          kt * PF_KT + key <= tl ? vreg[u] : u32x4{0u, 0u, 0u, 0u};
+          chunk_bf16(kt * PF_KT + key <= tl ? vreg[u] : Chunk{});    // (code 0 is +0)
+    }
+    if constexpr (FP8) {
+      if (tid == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S.sc[buf][i] = sc[i];
+      }
     }
   };
 
@@ -248,6 +298,21 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
       }
     }
 
+    // FP8: per 16-key page, c2 times its K scale, log2 of its V scale and the
+    // reciprocal of that scale (the scales are positive)
+    float ksc[4], c2k[4], lvs[4], ivs[4];
+    if constexpr (FP8) {
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(&S.sc[buf][0]);
+      const f32x4 vv = *reinterpret_cast<const f32x4*>(&S.sc[buf][4]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        ksc[kb] = kv[kb];
+        c2k[kb] = p.c2 * kv[kb];
+        lvs[kb] = __builtin_amdgcn_logf(vv[kb]);
+        ivs[kb] = __builtin_amdgcn_rcpf(vv[kb]);
+      }
+    }
+
     // masks, only where the tile crosses the causal edge, the window's lower
     // edge or the end of the sinks
     const int key0 = kt * PF_KT;
@@ -270,25 +335,49 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
             sacc[kb][qb][i] = ok ? sacc[kb][qb][i] : NEG_INF;
           }
       }
-      float mx = sacc[0][qb][0];
+      float mx = NEG_INF;
+      if constexpr (FP8) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb) {
+          float mk = sacc[kb][qb][0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
+          for (int i = 1; i < 4; ++i) mk = fmaxf(mk, sacc[kb][qb][i]);
+          mx = fmaxf(mx, mk * ksc[kb]);
+        }
+      } else {
+        mx = sacc[0][qb][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][qb][i]);
+      }
       mx = max_x16_x32(mx);
       const float m_new = fmaxf(m[qb], mx * c2);
       const float m_use = m_new == NEG_INF ? 0.f : m_new;
       const float alpha = fast_exp2(m[qb] - m_use);
       m[qb] = m_new;
       float ps = 0.f;
-      float pv[4][4];
+      float pv[4][4];                                  // FP8: weight times the V scale
+      if constexpr (FP8) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb) {
+          float pk = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[kb][i] = fast_exp2(fmaf(sacc[kb][qb][i], c2, -m_use));
-          ps += pv[kb][i];
+          for (int i = 0; i < 4; ++i) {
+            pv[kb][i] = fast_exp2(fmaf(sacc[kb][qb][i], c2k[kb], lvs[kb] - m_use));
+            pk += pv[kb][i];
+          }
+          ps = fmaf(pk, ivs[kb], ps);
         }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pv[kb][i] = fast_exp2(fmaf(sacc[kb][qb][i], c2, -m_use));
+            ps += pv[kb][i];
+          }
+      }
       lsum[qb] = lsum[qb] * alpha + ps;
       if (__any(alpha != 1.f)) {                       // rescale only when a max moved
 #pragma unroll
@@ -331,26 +420,26 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   int ids[4];
   if (n_tiles > 0) {
     tile_pages(tile_at(0), ids);
-    load_tile(ids, kA, vA);
-    store_tile(0, tile_at(0), kA, vA);
+    load_tile(ids, kA, vA, scA);
+    store_tile(0, tile_at(0), kA, vA, scA);
   }
-  if (n_tiles > 1) { tile_pages(tile_at(1), ids); load_tile(ids, kB, vB); }
-  if (n_tiles > 2) { tile_pages(tile_at(2), ids); load_tile(ids, kA, vA); }
+  if (n_tiles > 1) { tile_pages(tile_at(1), ids); load_tile(ids, kB, vB, scB); }
+  if (n_tiles > 2) { tile_pages(tile_at(2), ids); load_tile(ids, kA, vA, scA); }
   if (n_tiles > 3) tile_pages(tile_at(3), ids);
   __syncthreads();
   for (int it = 0; it < n_tiles; it += 2) {
     compute(0, tile_at(it));                          // even tile in buffer 0
-    if (it + 1 < n_tiles) store_tile(1, tile_at(it + 1), kB, vB);
+    if (it + 1 < n_tiles) store_tile(1, tile_at(it + 1), kB, vB, scB);
     if (it + 3 < n_tiles) {
-      load_tile(ids, kB, vB);                         // tile it + 3
+      load_tile(ids, kB, vB, scB);                    // tile it + 3
       if (it + 4 < n_tiles) tile_pages(tile_at(it + 4), ids);
     }
     __syncthreads();
     if (it + 1 >= n_tiles) break;
     compute(1, tile_at(it + 1));                      // odd tile in buffer 1
-    if (it + 2 < n_tiles) store_tile(0, tile_at(it + 2), kA, vA);
+    if (it + 2 < n_tiles) store_tile(0, tile_at(it + 2), kA, vA, scA);
     if (it + 4 < n_tiles) {
-      load_tile(ids, kA, vA);                         // tile it + 4
+      load_tile(ids, kA, vA, scA);                    // tile it + 4
       if (it + 5 < n_tiles) tile_pages(tile_at(it + 5), ids);
     }
     __syncthreads();
@@ -374,11 +463,16 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   }
 }
 
+template <int G, bool FP8>
+hipError_t launch_gf(const PrefillParams& p, int nwg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.rope_theta > 0.f)
+    return launch_kernel(prefill_kernel<G, true, FP8>, dim3(nwg), dim3(PfShape<true>::THREADS), s, e0, e1, p);
+  return launch_kernel(prefill_kernel<G, false, FP8>, dim3(nwg), dim3(PfShape<false>::THREADS), s, e0, e1, p);
+}
+
 template <int G>
 hipError_t launch_g(const PrefillParams& p, int nwg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (p.rope_theta > 0.f)
-    return launch_kernel(prefill_kernel<G, true>, dim3(nwg), dim3(PfShape<true>::THREADS), s, e0, e1, p);
-  return launch_kernel(prefill_kernel<G, false>, dim3(nwg), dim3(PfShape<false>::THREADS), s, e0, e1, p);
+  return p.kv_scales != nullptr ? launch_gf<G, true>(p, nwg, s, e0, e1) : launch_gf<G, false>(p, nwg, s, e0, e1);
 }
 
 }  // namespace

@@ -270,10 +270,12 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
  * chunk must have been appended first (the cache holds positions
  * 0..start_pos[s]+n_tok-1).  Computed with bf16 MFMA products: logits in
  * fp32 (the rotated query is split into two bf16 parts), softmax weights
- * rounded to bf16 for the weighted sum of V.  A negative start_pos[s] skips
- * that sequence.  Needs a bf16 cache without local_ring
- * (HWS_ERR_UNSUPPORTED otherwise: the ring no longer holds the earlier
- * window rows of a chunk).  No workspace. */
+ * rounded to bf16 for the weighted sum of V.  FP8 cache: the products run on
+ * the e4m3 codes (exact in bf16), logits are then multiplied by the page's
+ * K scale and weights by its V scale before that rounding.  A negative
+ * start_pos[s] skips that sequence.  Not with local_ring
+ * (HWS_ERR_UNSUPPORTED: the ring no longer holds the earlier window rows of
+ * a chunk).  No workspace. */
 typedef struct {
   int32_t n_seq;               /* sequences (host), >= 1                       */
   int32_t n_tok;               /* query positions per sequence (host), >= 1    */

@@ -303,12 +303,12 @@ def test_prefill_validation_without_gpu():
     a = hws.PrefillArgs(1, 4, 2, 4096, 4096, 4096, 4096, None)       # dense must be 0 or 1
     assert L.hws_prefill(c.handle, ctypes.byref(a), None) == hws.HWS_ERR_INVALID_ARG
     assert L.hws_prefill(c.handle, None, None) == hws.HWS_ERR_INVALID_ARG
-    # fp8 caches and the local ring are not read by prefill
+    # an fp8 cache goes through the same checks; the local ring is not read by prefill
     c8 = _ctx(kv=1)
     c8.bind(4096, 4096, 4096, 4096, 4096)
     with pytest.raises(hws.HwsError) as e:
-        _prefill(c8)
-    assert e.value.status == hws.HWS_ERR_UNSUPPORTED
+        _prefill(c8, out=None)
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG
     cr = _ctx(ring=True, max_seqs=2)
     cr.set_head_kinds([1, 0])
     cr.bind(4096, 4096, None, 4096, 4096, 4096, 4096)
