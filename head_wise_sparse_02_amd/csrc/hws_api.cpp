@@ -109,7 +109,8 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode,
   Layout L{};
   const int G = c->G;
   // The G=4 full-dim scan (bf16 queries, RoPE off) uses longer chunks.
-  L.score_chunk = (score_mode == HWS_SCORE_FULL && G == 4 && !rope) ? G4_SCORE_CHUNK : SCORE_CHUNK;
+  L.score_chunk = (score_mode == HWS_SCORE_FULL && G == 4 && !rope && c->cfg.kv_dtype == HWS_KV_BF16)
+                      ? G4_SCORE_CHUNK : SCORE_CHUNK;
   L.n_score_chunks = cdiv(Nmax, L.score_chunk);
   L.n_sel_chunks = cdiv(Nmax, SEL_CHUNK);
   // Retrieval attention chunk: long enough that the split partials stay small
@@ -393,8 +394,6 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   if (a->sel_idx != nullptr && a->sel_cap < 1) return fail(ctx, HWS_ERR_INVALID_ARG, "sel_cap = %d", a->sel_cap);
   if (ctx->ring_rows > 0 && ctx->nL > 0 && a->seq_slots == nullptr)
     return fail(ctx, HWS_ERR_INVALID_ARG, "local_ring needs seq_slots");
-  if (ctx->nR > 0 && a->score_mode == HWS_SCORE_FULL && c.kv_dtype != HWS_KV_BF16)
-    return fail(ctx, HWS_ERR_UNSUPPORTED, "full-dim scoring needs a bf16 cache");
   const bool rope = c.rope_theta > 0.f;
   const int GS = a->select_scope == HWS_SCOPE_QUERY_HEAD ? ctx->G : 1;
   const Layout L = make_layout(ctx, a->batch, a->max_seq_len, rope, a->score_mode, GS);

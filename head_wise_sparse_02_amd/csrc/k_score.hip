@@ -8,7 +8,9 @@
 // FULL mode ([ICS] "Inference-time context sparsity: illusion or
 // opportunity?", §2 "Oracle Top-K"): s_{g,i} = q_g . k_i over all 128 dims,
 // reading every K row once.  The G x 16-token x 128 tile is a dense bf16
-// contraction, done with v_mfma_f32_16x16x32_bf16.
+// contraction, done with v_mfma_f32_16x16x32_bf16; e4m3 pages are widened to
+// bf16 codes (exactly) and each 16-token page's products multiplied by its K
+// scale.
 //
 // Both write the raw scores to [B][nR][Nmax][G] and, per workgroup chunk,
 // the (max, sum) of 2^(c2 * s) for each query head, so that the selection
@@ -16,6 +18,24 @@
 #include "hws_device.h"
 
 namespace hws {
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte load that does not allocate in the caches (data streamed once).
+__device__ __forceinline__ u32x2 load_nt8(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+// 8 e4m3 codes -> 8 bf16, element e from byte e (exact: every e4m3 value is a
+// bf16 value, and the conversion's scale operand is 1).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 // Zero this chunk's share of the (b, hr) selection states (GS of them).
 __device__ __forceinline__ void zero_state_share(const DecodeParams& p, SelState* st, int b, int hr, int c,
@@ -184,7 +204,7 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
 // the same dim for the same (lane, element), so the product sums over all
 // 128 dims.  C[row][col] sits in lane col + 16*(row/4), element row%4.
 // ---------------------------------------------------------------------------
-template <int G, bool SPLITQ>
+template <int G, bool SPLITQ, bool FP8>
 __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   const int c = blockIdx.x, hr = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
@@ -221,7 +241,8 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   }
 
   const int* bt = p.block_tables + (size_t)b * p.max_blocks;
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
+  const char* kpool = reinterpret_cast<const char*>(p.k_pool);
+  constexpr int ES = FP8 ? 1 : 2;                          // bytes per stored element
   float* out = p.scores + ((size_t)(b * p.nR + hr) * p.Nmax) * G;
   const float c2 = p.c2_score;
   float m[4], sm[4];
@@ -234,17 +255,27 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   for (int i0 = 0; i0 < 16; i0 += U) {
     bf16x8 bfrag[U][4];
     int tpage[U];
+    float ksc[U];                                          // FP8: the page's K scale
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int pg = page0 + i0 + u;
       tpage[u] = pg * BS;
+      ksc[u] = 1.f;
       int blk = -1;
       if (tpage[u] < N) blk = bt[pg];
       if ((unsigned)blk < (unsigned)p.num_blocks) {
-        // blocked page: step s of all 16 rows is one contiguous 1 KiB run
-        const uint16_t* src = kpool + ((size_t)blk * p.Hp + p.pool_slot[h]) * (BS * D) + row * 32 + 8 * quad;
+        // blocked page: step s of all 16 rows is one contiguous run (1 KiB bf16, 512 B e4m3)
+        const size_t page = (size_t)blk * p.Hp + p.pool_slot[h];
+        const char* src = kpool + (page * (BS * D) + row * 32 + 8 * quad) * ES;
+        if constexpr (FP8) {
+          // e4m3 codes widened to bf16 (exact); the product is scaled after the MFMAs
+          ksc[u] = p.kv_scales[page * 2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag[u][s] = __builtin_bit_cast(bf16x8, load_nt16(src + 512 * s));
+          for (int s = 0; s < 4; ++s) bfrag[u][s] = fp8x8_to_bf16x8(load_nt8(src + 512 * s));
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) bfrag[u][s] = __builtin_bit_cast(bf16x8, load_nt16(src + 2 * 512 * s));
+        }
       } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s) bfrag[u][s] = (bf16x8)(__bf16)0.f;
@@ -267,6 +298,10 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] += __shfl_down(v[i], off);
         }
+      }
+      if (FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= ksc[u];
       }
       // Lanes holding query heads: quad < G/4 (G >= 4) or quad 0 (G < 4).
       const bool owner = (G >= 4) ? (quad < G / 4) : (quad == 0);
@@ -447,9 +482,13 @@ static hipError_t launch_score_g(const DecodeParams& p, hipStream_t st, hipEvent
     if (p.index_bf16) return launch_kernel(score_index_kernel<G, true>, grid, blk, st, e0, e1, p);
     return launch_kernel(score_index_kernel<G, false>, grid, blk, st, e0, e1, p);
   }
-  if (p.qrot != nullptr) return launch_kernel(score_full_kernel<G, true>, grid, blk, st, e0, e1, p);
+  if (p.kv_scales != nullptr) {                  // fp8 cache
+    if (p.qrot != nullptr) return launch_kernel(score_full_kernel<G, true, true>, grid, blk, st, e0, e1, p);
+    return launch_kernel(score_full_kernel<G, false, true>, grid, blk, st, e0, e1, p);
+  }
+  if (p.qrot != nullptr) return launch_kernel(score_full_kernel<G, true, false>, grid, blk, st, e0, e1, p);
   if (G == 4) return launch_kernel(score_full_g4_kernel<G4_SCORE_CHUNK, G4_GP, G4_PF>, grid, blk, st, e0, e1, p);
-  return launch_kernel(score_full_kernel<G, false>, grid, blk, st, e0, e1, p);
+  return launch_kernel(score_full_kernel<G, false, false>, grid, blk, st, e0, e1, p);
 }
 
 hipError_t launch_score(const DecodeParams& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {

@@ -509,6 +509,10 @@ __device__ __forceinline__ void tie_keep(const DecodeParams& p, TailLds& S, cons
       st->tstar = tstar;
       st->quota = ts[k].quota;
       st->flags = SEL_FINISHED | (ts[k].tie ? SEL_TIE : 0u);
+      // selection alone (the per-stage attention follows): top-k keeps
+      // min(k, N) tokens (the tie quota tops the set up to k); top-p sets
+      // are counted by the attention
+      if (p.agg_out && p.select_mode != 0) st->nsel = (unsigned int)min((unsigned long long)tl[k].N, ts[k].target);
     }
     unsigned int gt = 0u, eq = 0u;
 #pragma unroll

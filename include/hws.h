@@ -257,7 +257,9 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
  * the local heads read their rows from ring slot seq_slots[b]; a slot out of
  * range reads no rows (that sequence's local heads output 0 with lse -inf). */
 hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
-/* (FULL scoring requires a bf16 cache: HWS_ERR_UNSUPPORTED otherwise.) */
+/* (FULL scoring of an fp8 cache multiplies each page's products of the e4m3
+ * codes, widened exactly to bf16, by the page's K scale; it runs in the
+ * per-stage kernels, as HWS_LAUNCH_MULTI or AUTO's one-launch selection.) */
 
 /* One chunked-prefill attention call ([RTPurbo] Methodology §1: during
  * prefill a retrieval head keeps its whole cache while a local head attends

@@ -222,13 +222,15 @@ def test_decode_validation_without_gpu():
         assert hws.lib().hws_last_error(c.handle)
 
 
-def test_full_scores_need_bf16_cache():
+def test_full_scores_with_fp8_cache_pass_validation():
+    """Full-dim scores read fp8 pages too: the call is checked like any other
+    (a missing workspace is the error it reports, not the cache type)."""
     c = _ctx(kv=1)
     c.set_head_kinds([1, 0])
     c.bind(4096, 4096, 4096, 4096, 4096)
     with pytest.raises(hws.HwsError) as e:
-        _decode(c, score_mode=1)
-    assert e.value.status == hws.HWS_ERR_UNSUPPORTED
+        _decode(c, score_mode=1, workspace=None)
+    assert e.value.status == hws.HWS_ERR_WORKSPACE
 
 
 def test_workspace_size_rules():

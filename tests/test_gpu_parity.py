@@ -66,6 +66,32 @@ def test_full_scores_top_p_and_index_top_k(launch):
                          top_k=np.array([37, 1], np.int32)), launch=launch)
 
 
+def test_auto_top_k_counts():
+    """The default launch shape with top-k on the per-stage path (index scores,
+    and full-dim scores at G = 2): |S| = min(k, N) for every head."""
+    wl = W.make_workload(2, n=3000, batch=3, select_mode="top_k", top_k=np.array([37, 1, 5000], np.int32))
+    _, res, reps = _run(wl, launch=AUTO)
+    for r in reps:
+        if r["kind"] == "retrieval":
+            assert r["n_gpu"] == min(int(wl.top_k[r["b"]]), wl.seq_lens[r["b"]])
+    wl = W.make_workload(1, n=4000, Hq=4, Hkv=2, score_mode="full", select_mode="top_k",
+                         top_k=np.array([100], np.int32))
+    _, res, reps = _run(wl, launch=AUTO)
+    assert [r["n_gpu"] for r in reps if r["kind"] == "retrieval"] == [100]
+
+
+@pytest.mark.parametrize("launch", [AUTO, SINGLE, MULTI], ids=["auto", "single", "multi"])
+def test_full_scores_fp8_cache(launch):
+    """Full-dim scores over e4m3 pages (products on the codes, scaled by each
+    page's K scale): top-k with local heads in a ragged batch, top-p at G = 4,
+    and G = 2 with RoPE (split query)."""
+    _run(W.make_workload(5, n=20000, batch=4, score_mode="full", select_mode="top_k",
+                         top_k=np.array([300, 1, 5000, 20000], np.int32)), launch=launch)
+    _run(W.make_workload(1, n=6000, kv_dtype="fp8", score_mode="full"), launch=launch)
+    _run(W.make_workload(1, n=5000, Hq=4, Hkv=2, kv_dtype="fp8", score_mode="full", rope_theta=10000.0),
+         launch=launch)
+
+
 @BOTH
 @pytest.mark.parametrize("mode", ["top_p_one", "top_k_all", "window_all", "tiny_p"])
 def test_reductions_to_dense_and_degenerate(mode, launch):
