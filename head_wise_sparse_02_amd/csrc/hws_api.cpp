@@ -219,7 +219,6 @@ hws_status hws_create(const hws_config* cfg, hws_ctx** out) {
   if (c.n_sink < 0 || c.window < 0 || (long long)c.n_sink + c.window < 1) return HWS_ERR_INVALID_ARG;
   if (c.local_ring != 0 && c.local_ring != 1) return HWS_ERR_INVALID_ARG;
   if (c.local_ring) {
-    if (c.kv_dtype != HWS_KV_BF16) return HWS_ERR_UNSUPPORTED;   // fp8 scales live with pages
     if (c.max_seqs < 1 || (long long)c.n_sink + c.window > (1 << 26)) return HWS_ERR_INVALID_ARG;
     const long long rows = ((long long)c.n_sink + c.window + BS - 1) / BS * BS;
     if ((long long)c.max_seqs * c.num_kv_heads * rows / BS >= (1LL << 31)) return HWS_ERR_INVALID_ARG;

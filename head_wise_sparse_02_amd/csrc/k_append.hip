@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     __syncthreads();
   }
 
-  if (ring) {                       // bf16 only
+  if (ring) {                       // bf16 rows, whatever the page type
     uint16_t* kp = reinterpret_cast<uint16_t*>(p.lk_pool);
     uint16_t* vp = reinterpret_cast<uint16_t*>(p.lv_pool);
     const int keep_from = p0 + p.n_tok - p.window;

@@ -39,6 +39,7 @@ class DecodeSetup:
                  keep_host: bool = False, sequences=None, segments=None):
         self.wl = wl
         self.dev = torch.device(device)
+        self.segments = segments or append_segments
         B, Hkv, Hq, d = wl.B, wl.Hkv, wl.Hq, wl.d
         self.Nmax = int(max(wl.seq_lens))
         self.max_blocks = (self.Nmax + 15) // 16 + spare_pages
@@ -72,8 +73,10 @@ class DecodeSetup:
         if self.ring:
             W = ring_rows(n_sink_c, window_c)
             nl = max(self.nL, 1)
-            self.local_k_pool = torch.zeros((self.max_seqs, nl, W // 16, 4, 16, 32), dtype=kv_dt, device=self.dev)
-            self.local_v_pool = torch.zeros((self.max_seqs, nl, W, d), dtype=kv_dt, device=self.dev)
+            # the ring holds bf16 rows whatever the page type
+            self.local_k_pool = torch.zeros((self.max_seqs, nl, W // 16, 4, 16, 32), dtype=torch.bfloat16,
+                                            device=self.dev)
+            self.local_v_pool = torch.zeros((self.max_seqs, nl, W, d), dtype=torch.bfloat16, device=self.dev)
             srng = np.random.default_rng(np.random.SeedSequence([wl.cfg, wl.seed, 3001]))
             self.seq_slots_host = srng.permutation(self.max_seqs)[:B].astype(np.int32)
             self.seq_slots = torch.from_numpy(self.seq_slots_host).to(self.dev)

@@ -95,8 +95,9 @@ typedef struct {
   int32_t n_sink;             /* local heads: sink tokens 0..n_sink-1        */
   int32_t window;             /* local heads: last `window` tokens           */
   int32_t local_ring;         /* 1: local heads keep only sinks + window rows
-                                 in per-sequence ring pools (bf16 cache only);
-                                 0: every head keeps every row in the pages */
+                                 in per-sequence ring pools (bf16 rows, also
+                                 with fp8 pages); 0: every head keeps every
+                                 row in the pages                           */
   int32_t max_seqs;           /* local_ring: sequence slots in the ring pools */
   float attn_scale;           /* softmax scale of attention, e.g. 1/sqrt(d)  */
   float index_scale;          /* logit = index_scale * (P q).(P k)           */
@@ -112,7 +113,8 @@ typedef struct {
  *                   + d%32; K is stored after RoPE (when rope_theta > 0).
  *   v_pool:         [num_blocks][Hp][16][128] bf16 or e4m3 bytes, row-major.
  *   kv_scales:      [num_blocks][Hp][2] fp32 (K scale, V scale); FP8 only.
- *   local_k_pool,   local_ring only: [max_seqs][n_local][W][128] bf16 with
+ *   local_k_pool,   local_ring only: [max_seqs][n_local][W][128] bf16 (also
+ *                   when kv_dtype is FP8: the ring keeps exact rows) with
  *   local_v_pool:   W = n_sink + window rounded up to a multiple of 16 and the
  *                   local heads in KV-head order.  Token t of a sequence sits
  *                   in ring row t (t < n_sink) or n_sink + (t - n_sink) % window;

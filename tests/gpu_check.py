@@ -26,15 +26,19 @@ OUT_ATOL = 2e-3
 
 
 def oracle_head(setup: DecodeSetup, b: int, h: int, fixed_set=None):
+    """The oracle's decode of head h of sequence b, on the rows the cache holds:
+    fp8 pages from the setup's append calls, or bf16 rows for a local head
+    kept in the ring."""
     wl = setup.wl
     seq = setup.host[b]
     n = wl.seq_lens[b]
+    fp8 = setup.fp8 and not (setup.ring and wl.head_kinds[h] == "local")
     return O.decode_sequence_ref(
         seq.q, seq.k, seq.v, head_kinds=wl.head_kinds, proj=setup.proj_host,
         score_mode=wl.score_mode, select_mode=wl.select_mode, top_p=float(wl.top_p[b]),
         top_k=int(wl.top_k[b]), n_sink=wl.n_sink, window=wl.window, attn_scale=wl.attn_scale,
-        index_scale=wl.index_scale, rope_theta=wl.rope_theta, kv_fp8=setup.fp8,
-        segments=append_segments(n), heads=[h], scope=wl.select_scope,
+        index_scale=wl.index_scale, rope_theta=wl.rope_theta, kv_fp8=fp8,
+        segments=setup.segments(n), heads=[h], scope=wl.select_scope,
         index_bf16=wl.index_dtype == "bf16",
         fixed_sets=None if fixed_set is None else {h: fixed_set})[h]
 
@@ -51,7 +55,7 @@ def _score_bound(setup, b, h, n):
     else:
         qr = O.rope(q, np.full(G, n - 1), wl.rope_theta)
         ks = O.stored_rows(seq.k[:n, h], np.arange(n), rope_theta=wl.rope_theta, kv_fp8=setup.fp8,
-                           segments=append_segments(n), rotate=True)
+                           segments=setup.segments(n), rotate=True)
         qn = np.linalg.norm(qr, axis=1)
         kn = np.linalg.norm(ks, axis=1)
     return SCORE_RTOL * qn[:, None] * kn[None, :] + 1e-30

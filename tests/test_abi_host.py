@@ -62,12 +62,18 @@ def test_library_exports_every_declared_symbol():
     (dict(num_blocks=0), hws.HWS_ERR_INVALID_ARG),
     (dict(local_ring=2, max_seqs=4), hws.HWS_ERR_INVALID_ARG),
     (dict(local_ring=1, max_seqs=0), hws.HWS_ERR_INVALID_ARG),
-    (dict(local_ring=1, max_seqs=4, kv_dtype=1), hws.HWS_ERR_UNSUPPORTED),   # fp8 scales live with pages
     (dict(local_ring=1, max_seqs=1 << 28), hws.HWS_ERR_INVALID_ARG),          # ring pages overflow int32
 ])
 def test_create_rejects(kw, status):
     st, h = _create(**kw)
     assert st == status and not h.value
+
+
+def test_ring_with_fp8_pages_is_accepted():
+    """The ring keeps bf16 rows, so it combines with fp8 pages."""
+    st, h = _create(local_ring=1, max_seqs=4, kv_dtype=1)
+    assert st == hws.HWS_OK and h.value
+    hws.lib().hws_destroy(h)
 
 
 def test_create_null_arguments():

@@ -105,10 +105,26 @@ def test_ring_single_launch_with_scan_inside():
     check_decode(st, r, verbose=True)
 
 
-def test_ring_rows_hold_sinks_and_window():
+@pytest.mark.parametrize("launch", [AUTO, SINGLE, MULTI], ids=["auto", "single", "multi"])
+def test_ring_with_fp8_pages(launch):
+    """fp8 pages for the retrieval heads, bf16 ring rows for the local heads,
+    in a ragged batch appended in calls of random lengths (page scales set by
+    several calls), against the oracle."""
+    wl = W.make_workload(5, n=12000, batch=6)
+    wl.local_ring = True
+    print(f"\n[case] ring fp8 {wl.name} B={wl.B} N={wl.seq_lens} launch={launch}", flush=True)
+    st = DecodeSetup(wl, keep_host=True, segments=_schedule(7))
+    st.ctx.set_launch_mode(launch)
+    r = st.decode(debug=True)
+    check_decode(st, r, verbose=False)
+    assert st.k_pool.dtype == torch.uint8 and st.local_k_pool.dtype == torch.bfloat16
+
+
+@pytest.mark.parametrize("cfg", [2, 5], ids=["bf16", "fp8_pages"])
+def test_ring_rows_hold_sinks_and_window(cfg):
     """After appends the ring holds exactly the bf16 rows of the sinks and the
     window, at the documented ring rows; rows of evicted tokens are gone."""
-    wl = W.make_workload(2, n=2100, batch=2)
+    wl = W.make_workload(cfg, n=2100, batch=2)
     wl.local_ring = True
     st = DecodeSetup(wl, keep_host=True, segments=_schedule(3))
     torch.cuda.synchronize()
