@@ -96,7 +96,8 @@ def algorithmic_bytes(wl, sel_counts) -> dict:
             (256 B bf16 / 128 B fp8);
     attend: K and V rows of every selected token (V only with full-dim
             scores, whose logits are already known) and of the local heads'
-            sinks + window; fp8 adds 8 B of scales per page and head touched;
+            sinks + window (bf16 rows when a local ring holds them); fp8
+            adds 8 B of scales per page and head touched;
     io    : queries (bf16) and outputs (fp32).
     Scratch (scores, aggregates, histograms, partials) and block-table reads
     are not counted.
@@ -109,6 +110,9 @@ def algorithmic_bytes(wl, sel_counts) -> dict:
             if kind == "retrieval":
                 score += n * (row if wl.score_mode == "full" else (32 if wl.index_dtype == "bf16" else 64))
                 attend += cnt * (row if wl.score_mode == "full" else 2 * row)
+            elif wl.local_ring:
+                attend += cnt * 2 * 256              # the ring keeps bf16 rows
+                continue
             else:
                 attend += cnt * 2 * row
             if wl.kv_dtype == "fp8":
@@ -297,9 +301,6 @@ def main(argv=None) -> int:
 
     wl = W.make_workload(args.config, seed=args.seed, select_scope=args.scope, index_dtype=args.index,
                          local_ring=args.ring)
-    if args.ring and wl.kv_dtype != "bf16":
-        print("--ring needs a bf16 cache", file=sys.stderr)
-        return 2
     want_cpu = not args.no_cpu_baseline
     print(f"[bench] building workload {args.config}: {W.CONFIG_NAMES[args.config]}",
           file=sys.stderr, flush=True)
