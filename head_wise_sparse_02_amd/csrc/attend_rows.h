@@ -29,7 +29,7 @@ struct AttRB {
 __device__ __forceinline__ void local_row_at(const DecodeParams& p, int b, int l, int tok, int& ii, int& pg) {
   if (p.ring_rows > 0) {
     const int slot = p.seq_slots[b];
-    const int rr = tok < p.n_sink ? tok : p.n_sink + (p.window > 0 ? (tok - p.n_sink) % p.window : 0);
+    const int rr = ring_row(tok, p.ring_sink, p.ring_mod);
     ii = rr;
     pg = (unsigned)slot < (unsigned)p.max_seqs ? (int)((((long long)slot * p.nL + l) * p.ring_rows + rr) >> 4) : -1;
   } else {

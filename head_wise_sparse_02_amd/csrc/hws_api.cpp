@@ -52,6 +52,7 @@ struct hws_ctx {
   signed char loc_slot[MAX_KV];    // head -> local head number (-1: retrieval head)
   int Hp = 0;                      // heads per page
   int ring_rows = 0;               // local ring rows per (slot, local head); 0 = no ring
+  int ring_sink = 0, ring_mod = 0; // ring geometry: first positions, then positions modulo ring_mod
   bool appended = false, bound = false;
   hws_buffers buf{};
   std::string err;
@@ -99,7 +100,12 @@ void rebuild_slots(hws_ctx* c) {
   const bool ring = c->cfg.local_ring != 0;
   c->Hp = ring ? c->nR : c->cfg.num_kv_heads;
   for (int h = 0; h < c->cfg.num_kv_heads; ++h) c->pool_slot[h] = ring ? c->ret_slot[h] : (signed char)h;
-  c->ring_rows = ring ? (c->cfg.n_sink + c->cfg.window + BS - 1) / BS * BS : 0;
+  // positions below ring_sink (the sinks, rounded up to a 64-key tile) keep
+  // their own rows; later positions cycle through ring_mod rows (window +
+  // slack, rounded up to a page)
+  c->ring_sink = ring ? (c->cfg.n_sink + 63) / 64 * 64 : 0;
+  c->ring_mod = ring ? (int)(((long long)c->cfg.window + c->cfg.ring_slack + BS - 1) / BS * BS) : 0;
+  c->ring_rows = ring ? c->ring_sink + c->ring_mod : 0;
 }
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -219,8 +225,9 @@ hws_status hws_create(const hws_config* cfg, hws_ctx** out) {
   if (c.n_sink < 0 || c.window < 0 || (long long)c.n_sink + c.window < 1) return HWS_ERR_INVALID_ARG;
   if (c.local_ring != 0 && c.local_ring != 1) return HWS_ERR_INVALID_ARG;
   if (c.local_ring) {
-    if (c.max_seqs < 1 || (long long)c.n_sink + c.window > (1 << 26)) return HWS_ERR_INVALID_ARG;
-    const long long rows = ((long long)c.n_sink + c.window + BS - 1) / BS * BS;
+    if (c.max_seqs < 1 || c.ring_slack < 0 || (long long)c.n_sink + c.window + c.ring_slack > (1 << 26))
+      return HWS_ERR_INVALID_ARG;
+    const long long rows = ((long long)c.n_sink + 63) / 64 * 64 + ((long long)c.window + c.ring_slack + BS - 1) / BS * BS;
     if ((long long)c.max_seqs * c.num_kv_heads * rows / BS >= (1LL << 31)) return HWS_ERR_INVALID_ARG;
   }
   if (!finite_f(c.attn_scale) || !(c.attn_scale > 0.f) || !finite_f(c.index_scale) ||
@@ -349,6 +356,8 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
   p.n_sink = ctx->cfg.n_sink;
   p.window = ctx->cfg.window;
   p.ring_rows = ctx->ring_rows;
+  p.ring_sink = ctx->ring_sink;
+  p.ring_mod = ctx->ring_mod;
   p.max_seqs = ctx->cfg.max_seqs;
   p.seq_slots = seq_slots;
   p.lk_pool = ctx->buf.local_k_pool;
@@ -431,6 +440,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.kv_scales = c.kv_dtype == HWS_KV_FP8_E4M3 ? ctx->buf.kv_scales : nullptr;
   p.Hp = ctx->Hp;
   p.ring_rows = ctx->ring_rows;
+  p.ring_sink = ctx->ring_sink;
+  p.ring_mod = ctx->ring_mod;
   p.ring_pages = (int)((long long)c.max_seqs * ctx->nL * ctx->ring_rows / BS);
   p.max_seqs = c.max_seqs;
   p.seq_slots = a->seq_slots;
@@ -537,8 +548,13 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {
     return fail(ctx, HWS_ERR_INVALID_ARG, "null device pointer (q, block_tables, start_pos or out)");
   if ((long long)a->n_tok > (long long)c.max_blocks_per_seq * BS)
     return fail(ctx, HWS_ERR_CAPACITY, "n_tok = %d exceeds the block table", a->n_tok);
-  if (ctx->ring_rows > 0 && ctx->nL > 0)
-    return fail(ctx, HWS_ERR_UNSUPPORTED, "prefill reads every head from the pages (no local_ring)");
+  if (ctx->ring_rows > 0 && ctx->nL > 0) {
+    if (a->dense) return fail(ctx, HWS_ERR_UNSUPPORTED, "dense prefill needs every row of the local heads (no local_ring)");
+    if (a->seq_slots == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "local_ring needs seq_slots");
+    if ((long long)a->n_tok > (long long)c.ring_slack + 1)
+      return fail(ctx, HWS_ERR_CAPACITY, "n_tok = %d exceeds ring_slack + 1 = %lld", a->n_tok,
+                  (long long)c.ring_slack + 1);
+  }
   const int rows = prefill_rows_per_tile(c.rope_theta > 0.f);
   const int qp = rows / ctx->G;
   const long long ntq = (a->n_tok + qp - 1) / qp;
@@ -564,6 +580,15 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {
   p.k_pool = ctx->buf.k_pool;
   p.v_pool = ctx->buf.v_pool;
   p.kv_scales = c.kv_dtype == HWS_KV_FP8_E4M3 ? ctx->buf.kv_scales : nullptr;
+  if (ctx->ring_rows > 0 && ctx->nL > 0) {
+    p.ring_rows = ctx->ring_rows;
+    p.ring_sink = ctx->ring_sink;
+    p.ring_mod = ctx->ring_mod;
+    p.max_seqs = c.max_seqs;
+    p.seq_slots = a->seq_slots;
+    p.lk_pool = ctx->buf.local_k_pool;
+    p.lv_pool = ctx->buf.local_v_pool;
+  }
   p.out = a->out;
   p.lse = a->lse;
   std::memcpy(p.pool_slot, ctx->pool_slot, sizeof(p.pool_slot));

@@ -84,7 +84,9 @@ struct DecodeParams {
   const void* v_pool;
   const float* kv_scales;
   int Hp;                       // heads per page: Hkv, or nR with a local ring
-  int ring_rows;                // local ring: rows per (slot, local head), a multiple of 16; 0 = no ring
+  int ring_rows;                // local ring: rows per (slot, local head) = ring_sink + ring_mod; 0 = no ring
+  int ring_sink, ring_mod;      // local ring: rows of positions 0..ring_sink-1, then position t at
+                                // ring_sink + t % ring_mod (ring_sink a multiple of 64, ring_mod of 16)
   int ring_pages;               // local ring: 16-row pages in each ring pool
   int max_seqs;
   const int* seq_slots;         // [B] ring slot of each sequence (ring only)
@@ -132,6 +134,7 @@ struct AppendParams {
   int Hp;                       // heads per page
   int n_sink, window;
   int ring_rows, max_seqs;      // local ring (ring_rows = 0: none)
+  int ring_sink, ring_mod;      // ring geometry (as in DecodeParams)
   const int* seq_slots;         // [n_seq] ring slots
   void* lk_pool;
   void* lv_pool;
@@ -159,10 +162,21 @@ struct PrefillParams {
   const float* kv_scales;       // FP8 pages: [blocks][Hp][2]; null for bf16
   float* out;                   // [n_seq][n_tok][Hq][D]
   float* lse;                   // [n_seq][n_tok][Hq] or null
+  int ring_rows, ring_sink, ring_mod, max_seqs;   // local ring (ring_rows = 0: none)
+  const int* seq_slots;         // [n_seq] ring slots
+  const void* lk_pool;          // ring pools (bf16)
+  const void* lv_pool;
+  int item0;                    // work item of workgroup 0 (a launch may cover a range of items)
   signed char ret_head[MAX_KV];
   signed char loc_head[MAX_KV];
   signed char pool_slot[MAX_KV];
 };
+
+// Ring row of position t (ring_sink rows of the first positions, then t
+// modulo ring_mod); the caller checks that the ring still holds t.
+__host__ __device__ __forceinline__ int ring_row(int t, int ring_sink, int ring_mod) {
+  return t < ring_sink ? t : (ring_mod > 0 ? ring_sink + t % ring_mod : 0);
+}
 
 // Launch a kernel; with timing events the start/stop timestamps are taken
 // by the dispatch packet itself (no extra barrier packets in the stream).

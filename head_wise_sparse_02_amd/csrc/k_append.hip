@@ -13,9 +13,10 @@
 //
 // Local ring ([RTPurbo] Methodology §1: a local head attends to its sinks and
 // its window only): local heads write the sequence's ring slot instead of the
-// pages, and only the rows a decode can still read, i.e. the sinks and the
-// last `window` positions of the call (distinct ring rows, so no two writers
-// meet); older window rows are overwritten as the sequence grows.
+// pages, and only the rows a decode or a prefill chunk can still read: the
+// first ring_sink positions (the sinks, rounded up to a 64-key tile) and the
+// last ring_mod positions of the call (window + slack, in distinct ring rows,
+// so no two writers meet); older rows are overwritten as the sequence grows.
 #include "hws_device.h"
 
 namespace hws {
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   if (ring) {
     seq_slot = p.seq_slots[s];
     if ((unsigned)seq_slot >= (unsigned)p.max_seqs) return;
-    if (lo >= p.n_sink && hi <= p0 + p.n_tok - p.window) return;   // no row of this page is kept
+    if (lo >= p.ring_sink && hi <= p0 + p.n_tok - p.ring_mod) return;   // no row of this page is kept
   } else {
     phys = p.block_tables[(size_t)s * p.max_blocks + blk_l];
     if ((unsigned)phys >= (unsigned)p.num_blocks) return;
@@ -96,12 +97,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   if (ring) {                       // bf16 rows, whatever the page type
     uint16_t* kp = reinterpret_cast<uint16_t*>(p.lk_pool);
     uint16_t* vp = reinterpret_cast<uint16_t*>(p.lv_pool);
-    const int keep_from = p0 + p.n_tok - p.window;
+    // positions below ring_sink, and the last ring_mod positions of the call
+    const int keep_from = p0 + p.n_tok - p.ring_mod;
     const size_t ring0 = ((size_t)seq_slot * (p.Hkv - p.nR) + p.loc_slot[h]) * p.ring_rows;
     for (int e = tid; e < nrows * D; e += 256) {
       const int r = e / D, d = e % D, t = lo + r;
-      if (t >= p.n_sink && t < keep_from) continue;
-      const int rr = t < p.n_sink ? t : p.n_sink + (t - p.n_sink) % p.window;
+      if (t >= p.ring_sink && t < keep_from) continue;
+      const int rr = ring_row(t, p.ring_sink, p.ring_mod);
       const size_t grow = ring0 + rr;
       kp[(grow >> 4) * (BS * D) + kpage_off(rr & 15, d)] = f32_to_bf16_rne(ks[r][d]);
       vp[grow * D + d] = f32_to_bf16_rne(vs[r][d]);

@@ -112,10 +112,10 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
 
   // work item -> (sequence, KV head, query tile); retrieval items first and
   // the tiles with the most keys first
-  int item = blockIdx.x;
+  int item = blockIdx.x + p.item0;
   const int nret = p.n_seq * p.nR * p.ntq;
   bool ret;
-  int s, h, qt;
+  int s, h, qt, lh = 0;                            // lh: local head number
   if (item < nret) {
     ret = true;
     const int per = p.n_seq * p.nR;
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     qt = p.ntq - 1 - item / per;
     const int rem = item % per;
     s = rem / p.nL;
-    h = p.loc_head[rem % p.nL];
+    lh = rem % p.nL;
+    h = p.loc_head[lh];
   }
   const int start = p.start_pos[s];
   if (start < 0) return;
@@ -145,7 +146,13 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     ns_t = p.n_sink > 0 ? min((p.n_sink - 1) / PF_KT + 1, last_t + 1) : 0;
     lo_t = max(ns_t, max(0, t0 - p.window + 1) / PF_KT);
   }
-  const int n_tiles = ns_t + max(0, last_t - lo_t + 1);
+  // a local head with a ring reads its rows from the sequence's ring slot
+  // (positions below ring_sink in their own rows, later ones modulo
+  // ring_mod); a slot out of range reads nothing (output 0, lse -inf)
+  const bool ring = !ret && p.ring_rows > 0;
+  const int rslot = ring ? p.seq_slots[s] : 0;
+  const bool slot_ok = !ring || (unsigned)rslot < (unsigned)p.max_seqs;
+  const int n_tiles = slot_ok ? ns_t + max(0, last_t - lo_t + 1) : 0;
 
   // queries of this wave: rows 32*wave + 16*qb + col = (position, head) pairs
   int qpos[QB];
@@ -192,9 +199,11 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   const int* bt = p.block_tables + (size_t)s * p.max_blocks;
   typedef typename PfChunk<FP8>::T Chunk;
   constexpr int ES = FP8 ? 1 : 2;                  // bytes per stored element
-  const char* kpool = reinterpret_cast<const char*>(p.k_pool);
-  const char* vpool = reinterpret_cast<const char*>(p.v_pool);
-  const int hslot = p.pool_slot[h];
+  const char* kpool = reinterpret_cast<const char*>(ring ? p.lk_pool : p.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(ring ? p.lv_pool : p.v_pool);
+  const int hslot = ring ? 0 : p.pool_slot[h];
+  const int hp = ring ? 1 : p.Hp;                  // heads per page of the pool read
+  const size_t rbase = ring ? ((size_t)(slot_ok ? rslot : 0) * p.nL + lh) * (size_t)(p.ring_rows / BS) : 0;
   const float* scales = FP8 ? p.kv_scales + 2 * hslot : nullptr;   // (K, V) scale of page 0 of this head
   // Tile loaders: a tile is 4 pages x 256 16-byte chunks of K and 64 keys x
   // 16 chunks of 8 dims of V.  Each thread moves KC chunks of each (chunk
@@ -225,8 +234,15 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int lp = kt * 4 + u;
-      const int blk = bt[min(lp, lp_max)];
-      ids[u] = ((lp <= lp_max) & ((unsigned)blk < (unsigned)p.num_blocks)) ? blk : 0;
+      if (ring) {                                  // wave-uniform
+        const int pos = lp * BS;
+        const int rp = pos < p.ring_sink ? lp
+                     : (p.ring_mod > 0 ? (p.ring_sink + pos % p.ring_mod) / BS : 0);
+        ids[u] = (int)rbase + (lp <= lp_max ? rp : 0);
+      } else {
+        const int blk = bt[min(lp, lp_max)];
+        ids[u] = ((lp <= lp_max) & ((unsigned)blk < (unsigned)p.num_blocks)) ? blk : 0;
+      }
       live |= (lp <= lp_max) << u;
     }
   };
@@ -235,14 +251,14 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
 #pragma unroll
     for (int u = 0; u < KC; ++u) {
       const int c = tid + PF_THREADS * u;
-      const size_t page = (size_t)pick(ids, c >> 8) * p.Hp + hslot;   // wave-uniform
+      const size_t page = (size_t)pick(ids, c >> 8) * hp + hslot;   // wave-uniform
       kreg[u] = *reinterpret_cast<const Chunk*>(kpool + (page * (BS * D) + kcp * 8) * ES);
       vreg[u] = *reinterpret_cast<const Chunk*>(vpool + ((page * BS + ((c >> 4) & 15)) * D + 8 * (c & 15)) * ES);
     }
     if constexpr (FP8) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const f32x2 s2 = *reinterpret_cast<const f32x2*>(scales + (size_t)ids[u] * (2 * p.Hp));
+        const f32x2 s2 = *reinterpret_cast<const f32x2*>(scales + (size_t)ids[u] * (2 * hp));
         sc[u] = (live >> u) & 1 ? s2.x : 1.f;
         sc[4 + u] = (live >> u) & 1 ? s2.y : 1.f;
       }
@@ -470,9 +486,20 @@ hipError_t launch_gf(const PrefillParams& p, int nwg, hipStream_t s, hipEvent_t 
   return launch_kernel(prefill_kernel<G, false, FP8>, dim3(nwg), dim3(PfShape<false>::THREADS), s, e0, e1, p);
 }
 
+// All work items in one launch; with fp8 pages and a ring, the retrieval
+// items (fp8 pages) and the local items (bf16 ring rows) in two launches,
+// timed from the first one's start to the second one's end.
 template <int G>
-hipError_t launch_g(const PrefillParams& p, int nwg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  return p.kv_scales != nullptr ? launch_gf<G, true>(p, nwg, s, e0, e1) : launch_gf<G, false>(p, nwg, s, e0, e1);
+hipError_t launch_g(const PrefillParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const long long nret = (long long)p.n_seq * p.nR * p.ntq;
+  const long long nall = (long long)p.n_seq * (p.nR + p.nL) * p.ntq;
+  if (p.kv_scales == nullptr) return launch_gf<G, false>(p, (int)nall, s, e0, e1);
+  if (p.ring_rows == 0 || nret == nall) return launch_gf<G, true>(p, (int)nall, s, e0, e1);
+  hipError_t e = hipSuccess;
+  if (nret > 0 && (e = launch_gf<G, true>(p, (int)nret, s, e0, nullptr)) != hipSuccess) return e;
+  PrefillParams q = p;
+  q.item0 = (int)nret;
+  return launch_gf<G, false>(q, (int)(nall - nret), s, nret > 0 ? nullptr : e0, e1);
 }
 
 }  // namespace
@@ -483,10 +510,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s, hipEvent_t e0, 
   const long long nwg = (long long)p.n_seq * (p.nR + p.nL) * p.ntq;
   if (nwg <= 0) return hipSuccess;
   switch (p.G) {
-    case 1: return launch_g<1>(p, (int)nwg, s, e0, e1);
-    case 2: return launch_g<2>(p, (int)nwg, s, e0, e1);
-    case 4: return launch_g<4>(p, (int)nwg, s, e0, e1);
-    default: return launch_g<8>(p, (int)nwg, s, e0, e1);
+    case 1: return launch_g<1>(p, s, e0, e1);
+    case 2: return launch_g<2>(p, s, e0, e1);
+    case 4: return launch_g<4>(p, s, e0, e1);
+    default: return launch_g<8>(p, s, e0, e1);
   }
 }
 

@@ -49,7 +49,7 @@ class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_q_heads", "num_kv_heads", "head_dim", "index_dim", "block_size", "num_blocks",
         "max_blocks_per_seq", "kv_dtype", "index_dtype", "n_sink", "window", "local_ring",
-        "max_seqs")] + [
+        "max_seqs", "ring_slack")] + [
         ("attn_scale", ctypes.c_float), ("index_scale", ctypes.c_float),
         ("rope_theta", ctypes.c_float)]
 
@@ -75,7 +75,7 @@ class DecodeArgs(ctypes.Structure):
 class PrefillArgs(ctypes.Structure):
     _fields_ = [("n_seq", ctypes.c_int32), ("n_tok", ctypes.c_int32), ("dense", ctypes.c_int32),
                 ("q", ctypes.c_void_p), ("block_tables", ctypes.c_void_p), ("start_pos", ctypes.c_void_p),
-                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+                ("seq_slots", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
 def lib_path() -> str:
@@ -148,11 +148,11 @@ class Context:
                  max_blocks_per_seq: int, n_sink: int, window: int, attn_scale: float,
                  index_scale: float = 1.0, rope_theta: float = 0.0, kv_dtype: int = HWS_KV_BF16,
                  index_dtype: int = HWS_INDEX_F32, local_ring: bool = False, max_seqs: int = 0,
-                 head_dim: int = 128, index_dim: int = 16, block_size: int = 16):
+                 ring_slack: int = 0, head_dim: int = 128, index_dim: int = 16, block_size: int = 16):
         self._L = lib()
         self.cfg = Config(num_q_heads, num_kv_heads, head_dim, index_dim, block_size, num_blocks,
                           max_blocks_per_seq, kv_dtype, index_dtype, n_sink, window, int(bool(local_ring)),
-                          max_seqs, attn_scale, index_scale, rope_theta)
+                          max_seqs, ring_slack, attn_scale, index_scale, rope_theta)
         h = ctypes.c_void_p()
         st = self._L.hws_create(ctypes.byref(self.cfg), ctypes.byref(h))
         if st != HWS_OK:
@@ -233,16 +233,18 @@ class Context:
         a.workspace_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
         self._check(self._L.hws_decode(self.handle, ctypes.byref(a), _stream(stream)), "hws_decode")
 
-    def prefill(self, *, q, block_tables, start_pos, out, lse=None, dense: bool = False, stream=None):
+    def prefill(self, *, q, block_tables, start_pos, out, lse=None, dense: bool = False, stream=None,
+                seq_slots=None):
         """Chunked prefill attention: q [n_seq, n_tok, Hq, 128] bf16 of the positions
         start_pos[s]..start_pos[s]+n_tok-1 (already appended); out [n_seq, n_tok, Hq, 128]
         fp32, lse [n_seq, n_tok, Hq] or None; dense: every head attends to every
-        earlier position."""
+        earlier position; seq_slots: [n_seq] int32 ring slots (local ring)."""
         a = PrefillArgs()
         a.n_seq = int(q.shape[0]) if q is not None else 0
         a.n_tok = int(q.shape[1]) if q is not None else 0
         a.dense = int(bool(dense))
         a.q, a.block_tables, a.start_pos = _ptr(q), _ptr(block_tables), _ptr(start_pos)
+        a.seq_slots = _ptr(seq_slots)
         a.out, a.lse = _ptr(out), _ptr(lse)
         self._check(self._L.hws_prefill(self.handle, ctypes.byref(a), _stream(stream)), "hws_prefill")
 

@@ -23,9 +23,20 @@ def append_segments(n: int) -> list:
     return [(0, n - 1), (n - 1, 1)] if n > 1 else [(0, 1)]
 
 
-def ring_rows(n_sink: int, window: int) -> int:
-    """Rows per (sequence slot, local head) of the local ring: sinks + window, to 16."""
-    return (n_sink + window + 15) // 16 * 16
+def ring_rows(n_sink: int, window: int, slack: int = 0) -> int:
+    """Rows per (sequence slot, local head) of the local ring: the first
+    positions (sinks rounded up to 64), then window + slack rounded up to 16."""
+    return ring_sink(n_sink) + ring_mod(window, slack)
+
+
+def ring_sink(n_sink: int) -> int:
+    """Ring rows of the first positions (position t < this sits in row t)."""
+    return (n_sink + 63) // 64 * 64
+
+
+def ring_mod(window: int, slack: int = 0) -> int:
+    """Ring rows that later positions cycle through (t sits in row ring_sink + t % this)."""
+    return (window + slack + 15) // 16 * 16
 
 
 class DecodeSetup:
@@ -33,10 +44,11 @@ class DecodeSetup:
     calls of a sequence of length n (default ``append_segments``).  With
     ``wl.local_ring`` the pages hold only the retrieval heads and the local
     heads live in ring pools of ``max_seqs`` = B + 3 slots, assigned to the
-    sequences by a seeded permutation."""
+    sequences by a seeded permutation, keeping ``ring_slack`` rows beyond the
+    window (prefill chunks of up to ring_slack + 1 positions)."""
 
     def __init__(self, wl: Workload, device: str = "cuda", spare_pages: int = 2,
-                 keep_host: bool = False, sequences=None, segments=None):
+                 keep_host: bool = False, sequences=None, segments=None, ring_slack: int = 0):
         self.wl = wl
         self.dev = torch.device(device)
         self.segments = segments or append_segments
@@ -53,7 +65,7 @@ class DecodeSetup:
         self.ctx = hws.Context(
             num_q_heads=Hq, num_kv_heads=Hkv, num_blocks=self.num_blocks,
             max_blocks_per_seq=self.max_blocks, n_sink=n_sink_c, window=window_c,
-            local_ring=self.ring, max_seqs=self.max_seqs,
+            local_ring=self.ring, max_seqs=self.max_seqs, ring_slack=ring_slack,
             attn_scale=wl.attn_scale, index_scale=wl.index_scale, rope_theta=wl.rope_theta,
             kv_dtype=hws.HWS_KV_FP8_E4M3 if self.fp8 else hws.HWS_KV_BF16,
             index_dtype=hws.HWS_INDEX_BF16 if wl.index_dtype == "bf16" else hws.HWS_INDEX_F32)
@@ -71,7 +83,7 @@ class DecodeSetup:
                           if self.fp8 else None)
         self.local_k_pool = self.local_v_pool = self.seq_slots = None
         if self.ring:
-            W = ring_rows(n_sink_c, window_c)
+            W = ring_rows(n_sink_c, window_c, ring_slack)
             nl = max(self.nL, 1)
             # the ring holds bf16 rows whatever the page type
             self.local_k_pool = torch.zeros((self.max_seqs, nl, W // 16, 4, 16, 32), dtype=torch.bfloat16,
@@ -136,7 +148,7 @@ class DecodeSetup:
         out = torch.empty((B, n_tok, self.wl.Hq, self.wl.d), dtype=torch.float32, device=self.dev)
         lse = torch.empty((B, n_tok, self.wl.Hq), dtype=torch.float32, device=self.dev)
         self.ctx.prefill(q=q, block_tables=self.block_tables, start_pos=start_pos, out=out, lse=lse,
-                         dense=dense, stream=stream)
+                         dense=dense, stream=stream, seq_slots=self.seq_slots)
         return out, lse
 
     def decode(self, *, debug: bool = False, sel_cap: int | None = None, stream=None):

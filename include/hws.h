@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define HWS_ABI_VERSION 3
+#define HWS_ABI_VERSION 4
 
 typedef int32_t hws_status;
 enum {
@@ -99,6 +99,9 @@ typedef struct {
                                  with fp8 pages); 0: every head keeps every
                                  row in the pages                           */
   int32_t max_seqs;           /* local_ring: sequence slots in the ring pools */
+  int32_t ring_slack;         /* local_ring: rows kept beyond the window, >= 0;
+                                 hws_prefill takes chunks of at most
+                                 ring_slack + 1 positions                    */
   float attn_scale;           /* softmax scale of attention, e.g. 1/sqrt(d)  */
   float index_scale;          /* logit = index_scale * (P q).(P k)           */
   float rope_theta;           /* > 0: rotate-half RoPE with this base; 0: off */
@@ -114,15 +117,15 @@ typedef struct {
  *   v_pool:         [num_blocks][Hp][16][128] bf16 or e4m3 bytes, row-major.
  *   kv_scales:      [num_blocks][Hp][2] fp32 (K scale, V scale); FP8 only.
  *   local_k_pool,   local_ring only: [max_seqs][n_local][W][128] bf16 (also
- *                   when kv_dtype is FP8: the ring keeps exact rows) with
- *   local_v_pool:   W = n_sink + window rounded up to a multiple of 16 and the
- *                   local heads in KV-head order.  Token t of a sequence sits
- *                   in ring row t (t < n_sink) or n_sink + (t - n_sink) % window;
- *                   K rows are grouped in 16-row pages laid out like k_pool
- *                   pages, V rows are plain rows.  [RTPurbo] Methodology §1:
- *                   a local head only ever reads its sinks and window, so
- *                   older rows need not be kept ([AoH] Results: the KV memory
- *                   saving of local heads).
+ *   local_v_pool:   when kv_dtype is FP8: the ring keeps exact rows) with the
+ *                   local heads in KV-head order, W = S + M, S = n_sink rounded
+ *                   up to a multiple of 64 and M = window + ring_slack rounded
+ *                   up to a multiple of 16.  Position t of a sequence sits in
+ *                   ring row t (t < S) or S + t % M.  K rows are grouped in
+ *                   16-row pages laid out like k_pool pages, V rows are plain
+ *                   rows.  [RTPurbo] Methodology §1: a local head only ever
+ *                   reads its sinks and window, so older rows need not be kept
+ *                   ([AoH] Results: the KV memory saving of local heads).
  *   index_pool:     [num_blocks][n_retrieval][16][16] fp32 or bf16 (index_dtype),
  *                   the projected pre-RoPE keys of retrieval heads in KV-head
  *                   order; may be NULL when no head is a retrieval head.
@@ -232,10 +235,11 @@ hws_status hws_workspace_size(const hws_ctx* ctx, int32_t batch, int32_t max_seq
  * position start_pos[s] + t, i.e. slot pos % 16 of page
  * block_tables[s][pos / 16].  k, v: [n_seq][n_tok][Hkv][128] bf16, pre-RoPE.
  * With local_ring, local heads write ring slot seq_slots[s] instead (device
- * [n_seq], each in [0, max_seqs), NULL otherwise): the sinks and the last
- * `window` positions of the call, so a sequence must be appended in position
- * order and a later call overwrites the rows that left the window; a slot
- * out of range skips that sequence's local rows.
+ * [n_seq], each in [0, max_seqs), NULL otherwise): the positions below S and
+ * the last M positions of the call (the ring layout above), so a sequence
+ * must be appended in position order and a later call overwrites the rows
+ * that left the window and the slack; a slot out of range skips that
+ * sequence's local rows.
  * For each retrieval head the projected key P_h k (fp32, before RoPE) goes to
  * the index pool ([RTPurbo] Methodology §2).  With RoPE on, K is rotated at its
  * position and rounded to bf16 before it is stored.  FP8: when a call writes
@@ -277,9 +281,11 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
  * rounded to bf16 for the weighted sum of V.  FP8 cache: the products run on
  * the e4m3 codes (exact in bf16), logits are then multiplied by the page's
  * K scale and weights by its V scale before that rounding.  A negative
- * start_pos[s] skips that sequence.  Not with local_ring
- * (HWS_ERR_UNSUPPORTED: the ring no longer holds the earlier window rows of
- * a chunk).  No workspace. */
+ * start_pos[s] skips that sequence.  With local_ring the local heads read
+ * ring slot seq_slots[s] (device [n_seq]; a slot out of range gives that
+ * sequence's local heads output 0 and lse -inf), which still holds every
+ * row a chunk needs when n_tok <= ring_slack + 1 (HWS_ERR_CAPACITY
+ * otherwise).  No workspace. */
 typedef struct {
   int32_t n_seq;               /* sequences (host), >= 1                       */
   int32_t n_tok;               /* query positions per sequence (host), >= 1    */
@@ -287,6 +293,7 @@ typedef struct {
   const void* q;               /* [n_seq][n_tok][Hq][128] bf16, pre-RoPE       */
   const int32_t* block_tables; /* [n_seq][max_blocks_per_seq]                  */
   const int32_t* start_pos;    /* [n_seq] position of each sequence's first query */
+  const int32_t* seq_slots;    /* [n_seq] ring slots (local_ring), else NULL    */
   float* out;                  /* [n_seq][n_tok][Hq][128] fp32                 */
   float* lse;                  /* [n_seq][n_tok][Hq] natural-log LSE, or NULL  */
 } hws_prefill_args;

@@ -21,7 +21,8 @@ def _declared():
 def _cfg(**kw):
     base = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, index_dim=16, block_size=16,
                 num_blocks=64, max_blocks_per_seq=32, kv_dtype=0, index_dtype=0, n_sink=4, window=256,
-                local_ring=0, max_seqs=0, attn_scale=0.0883883, index_scale=0.7071, rope_theta=0.0)
+                local_ring=0, max_seqs=0, ring_slack=0, attn_scale=0.0883883, index_scale=0.7071,
+                rope_theta=0.0)
     base.update(kw)
     return hws.Config(*[base[n] for n, _ in hws.Config._fields_])
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(hws.EXPORTED) == decl
-    assert L.hws_abi_version() == 3
+    assert L.hws_abi_version() == 4
     assert L.hws_status_string(hws.HWS_ERR_WORKSPACE) == b"workspace too small"
 
 
@@ -63,6 +64,7 @@ def test_library_exports_every_declared_symbol():
     (dict(local_ring=2, max_seqs=4), hws.HWS_ERR_INVALID_ARG),
     (dict(local_ring=1, max_seqs=0), hws.HWS_ERR_INVALID_ARG),
     (dict(local_ring=1, max_seqs=1 << 28), hws.HWS_ERR_INVALID_ARG),          # ring pages overflow int32
+    (dict(local_ring=1, max_seqs=4, ring_slack=-1), hws.HWS_ERR_INVALID_ARG),
 ])
 def test_create_rejects(kw, status):
     st, h = _create(**kw)
@@ -88,7 +90,7 @@ def _ctx(**kw):
     return hws.Context(num_q_heads=kw.get("hq", 8), num_kv_heads=kw.get("hkv", 2), num_blocks=64,
                        max_blocks_per_seq=32, n_sink=4, window=256, attn_scale=0.088,
                        index_scale=0.707, kv_dtype=kw.get("kv", 0), local_ring=kw.get("ring", False),
-                       max_seqs=kw.get("max_seqs", 0))
+                       max_seqs=kw.get("max_seqs", 0), ring_slack=kw.get("ring_slack", 0))
 
 
 def test_head_kinds_and_classification():
@@ -317,9 +319,14 @@ def test_prefill_validation_without_gpu():
     with pytest.raises(hws.HwsError) as e:
         _prefill(c8, out=None)
     assert e.value.status == hws.HWS_ERR_INVALID_ARG
-    cr = _ctx(ring=True, max_seqs=2)
+    # the local ring: seq_slots required, chunks of at most ring_slack + 1
+    # positions, no dense prefill (the ring lacks the local heads' older rows)
+    cr = _ctx(ring=True, max_seqs=2, ring_slack=299)
     cr.set_head_kinds([1, 0])
     cr.bind(4096, 4096, None, 4096, 4096, 4096, 4096)
-    with pytest.raises(hws.HwsError) as e:
-        _prefill(cr)
-    assert e.value.status == hws.HWS_ERR_UNSUPPORTED
+    for kw, status in [(dict(), hws.HWS_ERR_INVALID_ARG),
+                       (dict(seq_slots=_FakeT(), q=_FakeT((2, 301, 8, 128))), hws.HWS_ERR_CAPACITY),
+                       (dict(seq_slots=_FakeT(), dense=True), hws.HWS_ERR_UNSUPPORTED)]:
+        with pytest.raises(hws.HwsError) as e:
+            _prefill(cr, **kw)
+        assert e.value.status == status, (kw, e.value)

@@ -36,12 +36,14 @@ def chunk_segments(n_tok):
     return lambda n: [(0, n - n_tok), (n - n_tok, n_tok)] if n > n_tok else [(0, n)]
 
 
-def _run(wl, n_tok, *, dense=False, rows=None, q_fn=None, stride=1, segments=None):
+def _run(wl, n_tok, *, dense=False, rows=None, q_fn=None, stride=1, segments=None, ring_slack=None):
+    """ring_slack: keep the local heads in a ring with this slack."""
+    wl.local_ring = ring_slack is not None
     print(f"\n[case] prefill {wl.name} B={wl.B} N={wl.seq_lens[:4]} n_tok={n_tok} G={wl.G} "
-          f"window={wl.window} sinks={wl.n_sink} rope={wl.rope_theta} kv={wl.kv_dtype} dense={dense}",
-          flush=True)
+          f"window={wl.window} sinks={wl.n_sink} rope={wl.rope_theta} kv={wl.kv_dtype} dense={dense} "
+          f"ring_slack={ring_slack}", flush=True)
     segments = segments or append_segments
-    st = DecodeSetup(wl, keep_host=True, segments=segments)
+    st = DecodeSetup(wl, keep_host=True, segments=segments, ring_slack=ring_slack or 0)
     starts = [wl.seq_lens[b] - n_tok for b in range(wl.B)]
     qh = np.stack([wl.prefill_queries(b, n_tok) for b in range(wl.B)])
     if q_fn is not None:
@@ -58,10 +60,15 @@ def _run(wl, n_tok, *, dense=False, rows=None, q_fn=None, stride=1, segments=Non
     for b in range(wl.B):
         n = wl.seq_lens[b]
         seq = st.host[b]
-        ref = O.prefill_sequence_ref(qh[b], seq.k[:n], seq.v[:n], head_kinds=wl.head_kinds, start=starts[b],
-                                     n_sink=wl.n_sink, window=wl.window, attn_scale=wl.attn_scale,
-                                     rope_theta=wl.rope_theta, rows=rows, dense_all=dense, with_abs_v=True,
-                                     kv_fp8=st.fp8, segments=segments(n))
+        # rows as the cache holds them: fp8 pages, or bf16 for local heads in the ring
+        ref = {}
+        for heads, fp8 in (([h for h in range(wl.Hkv) if not (st.ring and wl.head_kinds[h] == "local")], st.fp8),
+                           ([h for h in range(wl.Hkv) if st.ring and wl.head_kinds[h] == "local"], False)):
+            if heads:
+                ref.update(O.prefill_sequence_ref(
+                    qh[b], seq.k[:n], seq.v[:n], head_kinds=wl.head_kinds, start=starts[b], n_sink=wl.n_sink,
+                    window=wl.window, attn_scale=wl.attn_scale, rope_theta=wl.rope_theta, heads=heads, rows=rows,
+                    dense_all=dense, with_abs_v=True, kv_fp8=fp8, segments=segments(n)))
         for h in range(wl.Hkv):
             o_ref, lse_ref, absv = ref[h]
             qn = np.linalg.norm(qh[b, rows, h * G:(h + 1) * G].astype(np.float64), axis=2)     # [T', G]
@@ -150,6 +157,86 @@ def test_prefill_fp8_ragged_chunks(n_tok):
 def test_prefill_fp8_whole_sequence_rope_and_dense():
     _run(W.make_workload(1, n=1100, kv_dtype="fp8", rope_theta=10000.0), 1100)
     _run(W.make_workload(1, n=900, kv_dtype="fp8"), 900, dense=True)
+
+
+@pytest.mark.parametrize("n,n_tok,slack", [(700, 700, 699), (3000, 300, 299), (3000, 300, 1000),
+                                           (3000, 1, 0), (70, 70, 69)])
+def test_prefill_ring(n, n_tok, slack):
+    """Local heads read their rows from the ring (sinks in their own rows, the
+    rest cycling through window + slack rows), which still holds every row a
+    chunk of up to slack + 1 positions needs, after wrapping many times."""
+    _run(W.make_workload(1, n=n), n_tok, ring_slack=slack)
+
+
+def test_prefill_ring_with_fp8_pages():
+    """fp8 pages (retrieval heads) and the bf16 ring (local heads): two
+    launches of the kernel, one per row type."""
+    wl = W.make_workload(5, n=2000, batch=3)
+    wl.seq_lens = [700, 1301, 2000]
+    _run(wl, 400, segments=chunk_segments(400), ring_slack=399)
+
+
+def test_prefill_ring_chunks_in_order():
+    """Chunked prefill as a server runs it: append a chunk, prefill it, append
+    the next.  The cache is rebuilt up to each chunk's end by appending the
+    prefix again (every ring row is rewritten, so the ring is as a fresh
+    append leaves it)."""
+    wl = W.make_workload(2, n=2600, batch=2)
+    n_tok, G = 500, wl.G
+    wl.local_ring = True
+    st = DecodeSetup(wl, keep_host=True, ring_slack=n_tok - 1, segments=chunk_segments(100))
+    for e in (500, 1500, 2600):
+        for b in range(wl.B):
+            seq = st.host[b]
+            k = torch.from_numpy(seq.k[:e]).to(torch.bfloat16).cuda()[None]
+            v = torch.from_numpy(seq.v[:e]).to(torch.bfloat16).cuda()[None]
+            for a in range(0, e, n_tok):
+                c = min(n_tok, e - a)
+                st.ctx.append(st.block_tables[b:b + 1], torch.tensor([a], dtype=torch.int32, device="cuda"),
+                              k[:, a:a + c].contiguous(), v[:, a:a + c].contiguous(),
+                              seq_slots=st.seq_slots[b:b + 1])
+        t0 = e - min(n_tok, e)
+        nt = e - t0
+        print(f"[case] ring chunk [{t0}, {e})", flush=True)
+        qh = np.stack([wl.prefill_queries(b, nt) for b in range(wl.B)])
+        q = torch.from_numpy(qh).to(torch.bfloat16).cuda()
+        out, lse = st.prefill(q, torch.full((wl.B,), t0, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        rows = np.arange(0, nt, 7)
+        for b in range(wl.B):
+            seq = st.host[b]
+            ref = O.prefill_sequence_ref(qh[b], seq.k[:e], seq.v[:e], head_kinds=wl.head_kinds, start=t0,
+                                         n_sink=wl.n_sink, window=wl.window, attn_scale=wl.attn_scale,
+                                         rows=rows, with_abs_v=True)
+            for h in range(wl.Hkv):
+                o_ref, lse_ref, absv = ref[h]
+                qn = np.linalg.norm(qh[b, rows, h * G:(h + 1) * G].astype(np.float64), axis=2)
+                kmax = float(np.linalg.norm(seq.k[:e, h].astype(np.float64), axis=1).max())
+                delta = 1e-5 * wl.attn_scale * qn * kmax
+                err = np.abs(out[b, rows, h * G:(h + 1) * G].astype(np.float64) - o_ref)
+                assert (err <= (REL + 2 * delta[:, :, None]) * absv + 1e-5).all(), (e, b, h)
+                assert (np.abs(lse[b, rows, h * G:(h + 1) * G] - lse_ref) <= 2e-5 + delta).all(), (e, b, h)
+
+
+def test_prefill_ring_slot_out_of_range_reads_nothing():
+    wl = W.make_workload(2, n=600, batch=2)
+    wl.local_ring = True
+    st = DecodeSetup(wl, ring_slack=99)
+    q = torch.from_numpy(np.stack([wl.prefill_queries(b, 100) for b in range(2)])).to(torch.bfloat16).cuda()
+    sp = torch.tensor([500, 500], dtype=torch.int32, device="cuda")
+    good, lgood = st.prefill(q, sp)
+    st.seq_slots[1] = st.max_seqs + 5
+    bad, lbad = st.prefill(q, sp)
+    torch.cuda.synchronize()
+    G = wl.G
+    for h, kind in enumerate(wl.head_kinds):
+        qs = slice(h * G, (h + 1) * G)
+        if kind == "local":
+            assert (bad[1, :, qs] == 0).all() and torch.isneginf(lbad[1, :, qs]).all()
+        else:
+            assert torch.equal(bad[1, :, qs], good[1, :, qs])
+        assert torch.equal(bad[0, :, qs], good[0, :, qs])
 
 
 def test_prefill_negative_start_skips_sequence():

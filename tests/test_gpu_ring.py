@@ -13,7 +13,7 @@ import torch
 
 from head_wise_sparse_02_amd import hws
 from head_wise_sparse_02_amd import workloads as W
-from head_wise_sparse_02_amd.runner import DecodeSetup, ring_rows
+from head_wise_sparse_02_amd.runner import DecodeSetup, ring_mod, ring_rows, ring_sink
 from gpu_check import check_decode
 
 pytestmark = pytest.mark.gpu
@@ -48,10 +48,12 @@ def _same(r, p):
 
 
 @pytest.mark.parametrize("launch", [MULTI, SINGLE], ids=["multi", "single"])
-@pytest.mark.parametrize("n", [1, 17, 200, 260, 261, 1000, 5000])
+@pytest.mark.parametrize("n", [1, 17, 63, 64, 65, 200, 320, 321, 1000, 5000])
 def test_ring_tiny_matches_oracle_and_pages(n, launch):
-    """Sinks 4, window 256: lengths inside the ring (no eviction), exactly at
-    its size, one past it, and far beyond it."""
+    """Sinks 4, window 256: the ring keeps positions 0..63 in their own rows
+    and cycles later ones through 256 rows; lengths inside the first rows, at
+    and past their end, inside the first cycle, at its end, one past it, and
+    far beyond it."""
     wl = W.make_workload(1, n=n, extra={"needle_range": (0, None)})
     _, r, p = _pair(wl, launch=launch)
     _same(r, p)
@@ -140,7 +142,8 @@ def test_ring_rows_hold_sinks_and_window(cfg):
         for l, h in enumerate(local):
             kpage = lk[slot, l].transpose(0, 2, 1, 3).reshape(W_, 128)   # page-blocked -> rows
             for t in toks:
-                rr = t if t < wl.n_sink else wl.n_sink + (t - wl.n_sink) % wl.window
+                S, M = ring_sink(wl.n_sink), ring_mod(wl.window)
+                rr = t if t < S else S + t % M
                 np.testing.assert_array_equal(kpage[rr], st.host[b].k[t, h])
                 np.testing.assert_array_equal(lv[slot, l, rr], st.host[b].v[t, h])
     # the pages hold the retrieval heads only
