@@ -24,8 +24,9 @@ struct AttRB {
 // Where local-head row `tok` of sequence b (local head number l) is stored:
 // its 16-row page pg and its index ii (slot ii % 16 of the page).  Without a
 // ring these are the sequence's cache page and the position; with a ring,
-// the ring row of the token (sinks first, then the window modulo its length)
-// in the sequence's ring slot, or pg = -1 for a slot out of range.
+// the ring row of the token (ring_row: the first positions in their own
+// rows, later ones modulo ring_mod) in the sequence's ring slot, or pg = -1
+// for a slot out of range.
 __device__ __forceinline__ void local_row_at(const DecodeParams& p, int b, int l, int tok, int& ii, int& pg) {
   if (p.ring_rows > 0) {
     const int slot = p.seq_slots[b];

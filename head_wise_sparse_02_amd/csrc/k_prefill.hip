@@ -22,7 +22,9 @@
 // B-operand shape of P^T once both operands enumerate the 32 keys of a step
 // in the same (permuted) order.  A retrieval head walks key tiles 0..last;
 // a local head walks its sink tile(s) and the tiles its window touches.
-// Masks are evaluated only on tiles that cross a boundary.
+// Masks are evaluated only on tiles that cross a boundary.  With a local
+// ring, a local head's tiles come from its ring slot instead of the pages:
+// every 16 positions from a multiple of 16 sit in one ring page.
 //
 // With RoPE on, queries are rotated in fp64 at their position and split as
 // q = hi + lo (two bf16 parts), so S keeps fp32-level accuracy; P is rounded
