@@ -168,6 +168,15 @@ def test_prefill_ring(n, n_tok, slack):
     _run(W.make_workload(1, n=n), n_tok, ring_slack=slack)
 
 
+@pytest.mark.parametrize("n_sink,window,slack,n_tok", [(70, 100, 150, 151), (0, 300, 63, 64), (5, 0, 0, 1),
+                                                        (200, 64, 20, 21)])
+def test_prefill_ring_geometry_edges(n_sink, window, slack, n_tok):
+    """Sinks over one 64-key tile (two sink tiles, 128 sink rows), no sinks,
+    sinks only (no cycling rows), and sinks longer than the window."""
+    wl = W.make_workload(1, n=1500, n_sink=n_sink, window=window, extra={"needle_range": (0, None)})
+    _run(wl, n_tok, ring_slack=slack)
+
+
 def test_prefill_ring_with_fp8_pages():
     """fp8 pages (retrieval heads) and the bf16 ring (local heads): two
     launches of the kernel, one per row type."""

@@ -107,6 +107,15 @@ def test_ring_single_launch_with_scan_inside():
     check_decode(st, r, verbose=True)
 
 
+@pytest.mark.parametrize("n_sink,window", [(70, 100), (0, 300), (5, 0), (200, 64)])
+def test_ring_geometry_edges(n_sink, window):
+    """Sinks over one 64-key tile, no sinks, sinks only, sinks longer than the
+    window: decode from the ring against the oracle and the paged cache."""
+    wl = W.make_workload(1, n=3001, n_sink=n_sink, window=window, extra={"needle_range": (0, None)})
+    _, r, p = _pair(wl, launch=MULTI, segments=_schedule(9))
+    _same(r, p)
+
+
 @pytest.mark.parametrize("launch", [AUTO, SINGLE, MULTI], ids=["auto", "single", "multi"])
 def test_ring_with_fp8_pages(launch):
     """fp8 pages for the retrieval heads, bf16 ring rows for the local heads,
