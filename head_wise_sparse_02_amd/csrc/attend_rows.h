@@ -49,7 +49,7 @@ __device__ __forceinline__ void local_row_at(const DecodeParams& p, int b, int l
 // null reads them from the scores buffer at the row's position.
 // row_mask (retrieval rows, one set per query head): bit g of row_mask[r] says
 // whether query head g keeps row r; null means every head keeps every row.
-template <int G, bool FP8, int MODE, int RB, bool RET = false>
+template <int G, bool FP8, int MODE, int RB, bool RET = false, bool ROW_ORDER = FP8>
 __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, int h, int hr, int lo, int nrows,
                                                 int r_begin, int r_step, int sub, const unsigned short* rows,
                                                 const int* pages, const int* ltok, const int* lpg,
@@ -198,25 +198,56 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
       }
     }
 
-    // one rescale per batch
+    // one rescale per batch, then the rows in order.  ROW_ORDER walks row by
+    // row (fewer values live at once: the fp8 kernels fit one more wave per
+    // SIMD), otherwise head by head (more independent work in flight); per
+    // head and dim both add the same terms in the same order.
+    if constexpr (ROW_ORDER) {
+      bool live[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mn = m[g];
+      for (int g = 0; g < G; ++g) {
+        float mn = m[g];
 #pragma unroll
-      for (int u = 0; u < RB; ++u) mn = fmaxf(mn, z[u][g]);
-      if (mn == NEG_INF) continue;                   // uniform over the processor
-      const float cf = fast_exp2(m[g] - mn);
-      l[g] *= cf;
+        for (int u = 0; u < RB; ++u) mn = fmaxf(mn, z[u][g]);
+        live[g] = mn != NEG_INF;                     // uniform over the processor
+        if (!live[g]) continue;
+        const float cf = fast_exp2(m[g] - mn);
+        l[g] *= cf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[g][j] *= cf;
+        for (int j = 0; j < 8; ++j) o[g][j] *= cf;
+        m[g] = mn;
+      }
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
-        const float pz = fast_exp2(z[u][g] - mn);
-        l[g] += pz;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pz, vv[u][j], o[g][j]);
+        for (int g = 0; g < G; ++g) {
+          if (!live[g]) continue;
+          const float pz = fast_exp2(z[u][g] - m[g]);
+          l[g] += pz;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pz, vv[u][j], o[g][j]);
+        }
       }
-      m[g] = mn;
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mn = m[g];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) mn = fmaxf(mn, z[u][g]);
+        if (mn == NEG_INF) continue;                 // uniform over the processor
+        const float cf = fast_exp2(m[g] - mn);
+        l[g] *= cf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] *= cf;
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const float pz = fast_exp2(z[u][g] - mn);
+          l[g] += pz;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pz, vv[u][j], o[g][j]);
+        }
+        m[g] = mn;
+      }
     }
   }
 }

@@ -182,8 +182,8 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   float m[G], l[G], o[G][8];
   constexpr int RB = AttRB<G, MODE>::value;
   if (FP8 && !is_ret && p.ring_rows > 0)         // the ring holds bf16 rows
-    accumulate_rows<G, false, MODE, RB>(p, b, h, hr, lo, nrows, proc * RB, 16 * RB, sub, rows_s, pages_s, ltok_s,
-                                        pages_s, nullptr, m, l, o, nullptr);
+    accumulate_rows<G, false, MODE, RB, false, true>(p, b, h, hr, lo, nrows, proc * RB, 16 * RB, sub, rows_s,
+                                                     pages_s, ltok_s, pages_s, nullptr, m, l, o, nullptr);
   else
     accumulate_rows<G, FP8, MODE, RB>(p, b, h, hr, lo, nrows, proc * RB, 16 * RB, sub, rows_s, pages_s, ltok_s,
                                       pages_s, nullptr, m, l, o, p.GS > 1 ? rmask_s : nullptr);

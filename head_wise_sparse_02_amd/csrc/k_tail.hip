@@ -313,8 +313,8 @@ __device__ __forceinline__ void attend_rows(const DecodeParams& p, TailLds& S, i
   float* po = p.apart_o + pbase * G * D;
   float m[G], l[G], o[G][8];
   if (FP8 && !RET && hr < 0 && p.ring_rows > 0)   // local rows from the ring: bf16
-    accumulate_rows<G, false, MODE, RB, RET>(p, b, h, hr, lo, nrows, proc * RB, NPROC * RB, sub, S.u.rows, pages,
-                                             S.ltok, S.lpg, lds_logits, m, l, o);
+    accumulate_rows<G, false, MODE, RB, RET, true>(p, b, h, hr, lo, nrows, proc * RB, NPROC * RB, sub, S.u.rows,
+                                                   pages, S.ltok, S.lpg, lds_logits, m, l, o);
   else
     accumulate_rows<G, FP8, MODE, RB, RET>(p, b, h, hr, lo, nrows, proc * RB, NPROC * RB, sub, S.u.rows, pages,
                                            S.ltok, S.lpg, lds_logits, m, l, o);
