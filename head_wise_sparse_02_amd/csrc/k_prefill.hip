@@ -37,7 +37,7 @@
 // bf16 for P V (the softmax sum is taken from the unscaled weights).  Both
 // scales enter the exponent: the weight times the V scale is
 // exp2(s * c2 * ks + log2(vs) - m), for raw product s and the running max m.
-#include "hws_device.h"
+#include "mfma_tile.h"
 
 namespace hws {
 
@@ -53,55 +53,12 @@ template <bool ROPE> struct PfShape {
   static constexpr int ROWS = 16 * QB * WAVES;
 };
 constexpr int PF_KT = 64;         // keys per tile
-constexpr int V_STRIDE = 144;     // padded row of the V tile in LDS (288 B: 4 rows hit 4 bank groups)
 
 struct alignas(16) PfLds {        // 16-byte aligned: the tile moves as 16-byte LDS accesses
   uint16_t k[2][4 * BS * D];      // 4 pages, page-blocked layout (16 KiB each)
   uint16_t v[2][PF_KT * V_STRIDE]; // V [key][dim], rows padded (18 KiB each)
   float sc[2][8];                 // FP8: K scales of the 4 pages, then V scales
 };
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// 8 elements of a row as stored: 16 bytes of bf16 or 8 bytes of e4m3 codes
-template <bool FP8> struct PfChunk { typedef u32x4 T; };
-template <> struct PfChunk<true> { typedef u32x2 T; };
-
-__device__ __forceinline__ u32x4 chunk_bf16(u32x4 w) { return w; }
-
-// 8 e4m3 codes -> 8 bf16 (exact; the conversion's scale operand is 1)
-__device__ __forceinline__ u32x4 chunk_bf16(u32x2 w) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  auto cvt = [](unsigned x, bool hi) {
-    return hi ? __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true))
-              : __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
-  };
-  return u32x4{cvt(w[0], false), cvt(w[0], true), cvt(w[1], false), cvt(w[1], true)};
-}
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 zero8() { return (bf16x8)(__bf16)0.f; }
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-
-// Reductions over lanes i, i^16, i^32 with the gfx950 lane swaps (each call
-// returns the value pair {v[i], v[i^16]} or {v[i], v[i^32]} in some order).
-__device__ __forceinline__ float max_x16_x32(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_x16_x32(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 template <int G, bool ROPE, bool FP8>
 __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_kernel(PrefillParams p) {
@@ -199,7 +156,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
   }
 
   const int* bt = p.block_tables + (size_t)s * p.max_blocks;
-  typedef typename PfChunk<FP8>::T Chunk;
+  typedef typename KvChunk<FP8>::T Chunk;
   constexpr int ES = FP8 ? 1 : 2;                  // bytes per stored element
   const char* kpool = reinterpret_cast<const char*>(ring ? p.lk_pool : p.k_pool);
   const char* vpool = reinterpret_cast<const char*>(ring ? p.lv_pool : p.v_pool);
@@ -415,16 +372,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        // transposing reads (ds_read_b64_tr_b16): within each 16-lane group,
-        // lane i gets element i % 4 of the 8-byte chunks addressed by lanes
-        // 4j + i / 4 (j = 0..3); lane k addresses dims 16db + 4 (k % 4) .. + 3
-        // of key k / 4 of the quad's 4 keys, so lane i (= col) receives dim
-        // 16db + i of those 4 keys: keys 32ks + 4 quad + 0..3, then + 16
-        uint16_t* base = &S.v[buf][(32 * ks + 4 * quad + (col >> 2)) * V_STRIDE + 16 * db + 4 * (col & 3)];
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)base);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(base + 16 * V_STRIDE));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, (v8i16){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        const bf16x8 a = vt_frag(S.v[buf], ks, db, col, quad);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a, pb[qb][ks], o[db][qb]);
       }
