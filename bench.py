@@ -77,6 +77,8 @@ def parse_args(argv=None):
                     help="with --prefill: positions prefilled in one chunk from position 0")
     ap.add_argument("--prefill-fp8", action="store_true",
                     help="with --prefill: the cache in fp8 (e4m3 with per-page scales)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the decode step captured once as a HIP graph and replayed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -326,6 +328,29 @@ def main(argv=None) -> int:
     total_ms = ev0.elapsed_time(ev1)
     ms_per_step = total_ms / args.steps
 
+    # optionally: one decode step captured as a HIP graph (its kernels only),
+    # replayed `steps` times
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            setup.decode()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            setup.decode()
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = ev0.elapsed_time(ev1) / args.steps
+        del g
+
     # per-kernel durations: the same `steps` decode calls again, each stage's
     # first/last dispatch carrying HIP timing events on the decode stream (the
     # events add bubbles between dispatches, so this loop is not the one timed
@@ -397,6 +422,7 @@ def main(argv=None) -> int:
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.kv_dtype == "bf16" else "fp8",
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "data": "synthetic (seeded; shapes and structure of the workload, no dataset or weights)",
         "config": {"workload": wl.name, "description": W.CONFIG_NAMES[wl.cfg], "batch": wl.B,
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
