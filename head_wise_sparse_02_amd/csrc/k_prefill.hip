@@ -367,15 +367,17 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
         }
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T, each V^T fragment read one step ahead of its products
+    // (the LDS read then overlaps the previous step's MFMAs: -3.5 %)
+    bf16x8 a_cur = vt_frag(S.v[buf], 0, 0, col, quad);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int step = 0; step < 16; ++step) {
+      const int db = step >> 1, ks = step & 1;
+      bf16x8 a_next = a_cur;
+      if (step + 1 < 16) a_next = vt_frag(S.v[buf], (step + 1) & 1, (step + 1) >> 1, col, quad);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = vt_frag(S.v[buf], ks, db, col, quad);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a, pb[qb][ks], o[db][qb]);
-      }
+      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a_cur, pb[qb][ks], o[db][qb]);
+      a_cur = a_next;
     }
 
   };
