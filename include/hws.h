@@ -31,6 +31,11 @@
  *   - A launch failure returns HWS_ERR_HIP with the HIP error text; a fault
  *     inside a kernel surfaces at the caller's next synchronisation.
  *   - A context is not thread-safe: use one context per stream.
+ *   - hws_append, hws_decode and hws_prefill enqueue kernel launches only (no
+ *     allocation, memset or synchronisation), so a call can be captured into
+ *     a HIP graph on the caller's stream, with profile timing off; a decode
+ *     step's own kernels reset its selection state in the workspace, so
+ *     replays need nothing else.
  *
  * Supported shapes: head_dim 128, index_dim 16, block_size 16, GQA group
  * G = num_q_heads / num_kv_heads in {1, 2, 4, 8}, num_kv_heads <= 64.
