@@ -287,7 +287,7 @@ def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the decode path "
-              "has no multi-GPU mode in this build.", file=sys.stderr)
+              "has no multi-GPU mode.", file=sys.stderr)
         return 2
     if args.calibrate_copy:
         calibrate_copy()

@@ -9,7 +9,7 @@ Tolerances (written here, used by every GPU parity test):
   above an included one, mass >= p - 1e-5, and the tokens clearly above its
   smallest value hold < p + 1e-5;
 * outputs: max |o_gpu - o_ref| <= 2e-3 with o_ref the oracle's attention on the
-  GPU's selected set (set-level differences are judged by the set check);
+  GPU's selected set (set-level differences are left to the set check);
   lse within 2e-3.
 """
 
