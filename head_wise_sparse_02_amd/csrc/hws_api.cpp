@@ -110,6 +110,9 @@ void rebuild_slots(hws_ctx* c) {
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// Longest context for which AUTO prefers the single launch after the scan.
+constexpr int AUTO_TAIL_MAX_LEN = 4096;
+
 // GS: selection states per retrieval head (1, or G with one set per query head).
 Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode, int GS) {
   Layout L{};
@@ -488,7 +491,11 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   const bool coop = ctx->launch_mode == HWS_LAUNCH_COOPERATIVE;
   // (one set per query head runs in the per-stage kernels)
   const bool single = ctx->nR > 0 && ctx->launch_mode != HWS_LAUNCH_MULTI && GS == 1;
-  const bool tail_ok = ctx->launch_mode == HWS_LAUNCH_SINGLE || coop;   // AUTO: fused launch only
+  // AUTO takes the single launch after the scan only for short contexts (one
+  // 4096-position stretch per head: there the per-stage launches' latency
+  // dominates; measured 40.5 against 44.1 us at 4096, slower from 8192 on)
+  const bool tail_ok = ctx->launch_mode == HWS_LAUNCH_SINGLE || coop ||
+                       (ctx->launch_mode == HWS_LAUNCH_AUTO && a->max_seq_len <= AUTO_TAIL_MAX_LEN);
   const int nwf = single ? fused_grid(p, coop) : 0;
   if (nwf > 0 && L.tail_ntiles <= nwf) {
     p.n_score_chunks = L.tail_tph;                 // one (max, sum) partial per tile

@@ -324,7 +324,8 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  *    runtime guarantees that all workgroups are resident (costs a few tens of
  *    microseconds of launch latency per call).
  *  HWS_LAUNCH_AUTO (the default): HWS_LAUNCH_SINGLE where the scan runs
- *    inside the launch (it is then faster); otherwise the scoring kernel,
+ *    inside the launch (it is then faster) or where max_seq_len <= 4096
+ *    (short contexts, where launch latency dominates); otherwise the scoring kernel,
  *    then the selection as ONE launch of the single-launch kind (same waits
  *    and time-out; one set per KV head, when its tiles fit the device), then
  *    the per-stage attention and merge; otherwise HWS_LAUNCH_MULTI.  (The

@@ -202,6 +202,20 @@ def test_single_launch_matches_multi(cfg, kw):
             np.testing.assert_array_equal(auto[key], m[key])
 
 
+@pytest.mark.parametrize("n,tail", [(4096, True), (4097, False)])
+def test_auto_short_contexts_take_single_launch(n, tail):
+    """AUTO runs short contexts (max_seq_len <= 4096) as the single launch
+    after the scan, longer ones per stage; both against the oracle."""
+    wl = W.make_workload(2, n=n, batch=2)
+    st = DecodeSetup(wl, keep_host=True)
+    st.ctx.profile_enable(True)
+    res = st.decode(debug=True)
+    prof = st.ctx.profile_read()
+    st.ctx.profile_enable(False)
+    assert (prof["tail"][1], prof["select"][1]) == ((1, 0) if tail else (0, 1)), prof
+    check_decode(st, res, verbose=False)
+
+
 def test_fp8_codes_and_scales_bit_exact():
     wl = W.make_workload(5, n=600, batch=3)
     st = DecodeSetup(wl, keep_host=True)
