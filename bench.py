@@ -99,7 +99,8 @@ def algorithmic_bytes(wl, sel_counts) -> dict:
     attend: K and V rows of every selected token (V only with full-dim
             scores, whose logits are already known) and of the local heads'
             sinks + window (bf16 rows when a local ring holds them); fp8
-            adds 8 B of scales per page and head touched;
+            adds one 8 B K/V scale pair per 16 rows gathered (a page's
+            worth: the fewest pages the rows can come from);
     io    : queries (bf16) and outputs (fp32).
     Scratch (scores, aggregates, histograms, partials) and block-table reads
     are not counted.
