@@ -57,6 +57,8 @@ struct hws_ctx {
   hws_buffers buf{};
   std::string err;
   int launch_mode = HWS_LAUNCH_AUTO;
+  unsigned int spin_limit = 1u << 20;  // polls per hand-off wait (~1 us each)
+  unsigned int wait_bias = 0;
   bool prof = false;
   std::vector<EvPair> recorded;
   std::vector<hipEvent_t> pool;
@@ -477,6 +479,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.tail_ntiles = L.tail_ntiles;
   p.tail_sync = reinterpret_cast<unsigned int*>(ws + L.tail_sync);
   p.tail_ties = reinterpret_cast<unsigned int*>(ws + L.tail_ties);
+  p.spin_limit = ctx->spin_limit;
+  p.wait_bias = ctx->wait_bias;
   std::memcpy(p.ret_slot, ctx->ret_slot, sizeof(p.ret_slot));
   std::memcpy(p.ret_head, ctx->ret_head, sizeof(p.ret_head));
   std::memcpy(p.loc_head, ctx->loc_head, sizeof(p.loc_head));
@@ -642,6 +646,16 @@ hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode) {
       mode != HWS_LAUNCH_SINGLE)
     return fail(ctx, HWS_ERR_INVALID_ARG, "launch mode = %d", mode);
   ctx->launch_mode = mode;
+  return HWS_OK;
+}
+
+hws_status hws_set_wait_limit(hws_ctx* ctx, uint32_t max_polls, int32_t unreachable) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (max_polls > (1u << 24))
+    return fail(ctx, HWS_ERR_INVALID_ARG, "max_polls = %u (at most 2^24)", max_polls);
+  // waits check the limit every 256 polls
+  ctx->spin_limit = max_polls == 0 ? (1u << 20) : ((max_polls + 255u) & ~255u);
+  ctx->wait_bias = unreachable != 0 ? 1u : 0u;
   return HWS_OK;
 }
 

@@ -112,6 +112,8 @@ struct DecodeParams {
   int tail_tph, tail_ntiles;    // tail: tiles per retrieval head, total tiles
   unsigned int* tail_sync;      // [0] error word, [1 + b*Hkv + h] split arrivals (zeroed by the scan)
   unsigned int* tail_ties;      // [tail_ntiles] ties at t* per tile
+  unsigned int spin_limit;      // polls before a hand-off wait gives up (multiple of 256)
+  unsigned int wait_bias;       // added to every hand-off target (0; 1 makes each wait give up)
   int n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
   int agg_out;                  // the single-launch selection ran: a_i is in agg, and the merge
                                 // checks the hand-off error word

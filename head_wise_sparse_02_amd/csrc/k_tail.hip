@@ -43,7 +43,6 @@ constexpr int TW = TT / 64;                   // 8 waves
 constexpr int TPT = TAIL_TPT;                 // tokens per thread per tile
 constexpr int MAXT = TAIL_MAXT;
 constexpr int NPROC = TT / 16;                // 16-lane row processors
-constexpr unsigned int SPIN_LIMIT = 1u << 20; // polls (~1 us each): a wait gives up after ~1 s
 
 struct TailLds {
   union {
@@ -71,12 +70,14 @@ __device__ __forceinline__ unsigned int lane_rank(unsigned long long bal) {
 }
 
 // Thread 0 polls `ctr` until it reaches `target`.  Returns false (and sets
-// the error word) if the limit passes or another workgroup already failed.
-__device__ __forceinline__ bool spin_until(const unsigned int* ctr, unsigned int target, unsigned int* err) {
+// the error word) once `limit` polls have passed (checked every 256, so every
+// wait ends) or another workgroup already failed.
+__device__ __forceinline__ bool spin_until(const unsigned int* ctr, unsigned int target, unsigned int* err,
+                                           unsigned int limit) {
   unsigned int it = 0;
   while (load_u32_coherent(ctr) < target) {
     ++it;
-    if ((it & 255u) == 0u && (it >= SPIN_LIMIT || load_u32_coherent(err) != 0u)) {
+    if ((it & 255u) == 0u && (it >= limit || load_u32_coherent(err) != 0u)) {
       atomicOr(err, 1u);
       return false;
     }
@@ -85,10 +86,12 @@ __device__ __forceinline__ bool spin_until(const unsigned int* ctr, unsigned int
   return true;
 }
 
-// Everyone waits for thread 0's spin.
-__device__ __forceinline__ void block_wait(TailLds& S, const unsigned int* ctr, unsigned int target, unsigned int* err) {
+// Everyone waits for thread 0's spin (the host's wait bias, 0 in normal use,
+// raises the target past what can arrive, for tests of the time-out path).
+__device__ __forceinline__ void block_wait(const DecodeParams& p, const unsigned int* ctr, unsigned int target,
+                                           unsigned int* err) {
   __syncthreads();
-  if (threadIdx.x == 0) spin_until(ctr, target, err);
+  if (threadIdx.x == 0) spin_until(ctr, target + p.wait_bias, err, p.spin_limit);
   __syncthreads();
 }
 
@@ -269,7 +272,7 @@ __device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, co
     if (tl[k].t < 0 || ts[k].done) continue;
     SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
     const unsigned long long* gh = PASS == 1 ? st->mass : (PASS == 2 ? st->mass2 : st->mass3);
-    block_wait(S, &st->arrive, base + (unsigned int)(PASS * p.tail_tph), err);
+    block_wait(p, &st->arrive, base + (unsigned int)(PASS * p.tail_tph), err);
     unsigned long long v[NB / TT];
 #pragma unroll
     for (int e = 0; e < NB / TT; ++e) v[e] = load_u64_coherent(&gh[tid + e * TT]);
@@ -488,7 +491,7 @@ __device__ __forceinline__ void tie_keep(const DecodeParams& p, TailLds& S, cons
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
       if (tl[k].t < 0 || !ts[k].tie) continue;
-      block_wait(S, &p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].tie_arrive, (unsigned int)p.tail_tph, err);
+      block_wait(p, &p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].tie_arrive, (unsigned int)p.tail_tph, err);
       if (tid == 0) {
         unsigned int sum = 0u;
         const int t0 = tl[k].t - tl[k].j;
@@ -892,7 +895,7 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   wait_memory_ops();
   __syncthreads();
   if (tid == 0) atomicAdd(&st->arrive, 1u);
-  block_wait(S, &st->arrive, (unsigned int)p.tail_tph, err);
+  block_wait(p, &st->arrive, (unsigned int)p.tail_tph, err);
   if (wave < G) {
     float mm = NEG_INF, ss = 0.f;
     for (int jj = lane; jj < p.tail_tph; jj += 64)

@@ -35,7 +35,7 @@ EXPORTED = (
     "hws_set_head_kinds", "hws_classify_by_scores", "hws_get_head_kinds", "hws_bind",
     "hws_workspace_size", "hws_append", "hws_decode", "hws_profile_enable",
     "hws_profile_read", "hws_profile_stage_name", "hws_set_launch_mode",
-    "hws_effective_rank_workspace", "hws_effective_rank", "hws_prefill",
+    "hws_effective_rank_workspace", "hws_effective_rank", "hws_prefill", "hws_set_wait_limit",
 )
 
 
@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
         "hws_prefill": (i32, [vp, P(PrefillArgs), vp]),
         "hws_profile_enable": (i32, [vp, i32]),
         "hws_set_launch_mode": (i32, [vp, i32]),
+        "hws_set_wait_limit": (i32, [vp, ctypes.c_uint32, i32]),
         "hws_effective_rank_workspace": (i32, [i32, i32, P(ctypes.c_size_t)]),
         "hws_effective_rank": (i32, [i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "hws_profile_read": (i32, [vp, P(ctypes.c_double), P(i32), i32]),
@@ -255,6 +256,13 @@ class Context:
         (the same as a cooperative launch) or HWS_LAUNCH_MULTI (one kernel per
         stage)."""
         self._check(self._L.hws_set_launch_mode(self.handle, int(mode)), "hws_set_launch_mode")
+
+    def set_wait_limit(self, max_polls: int = 0, unreachable: bool = False):
+        """Polls before a hand-off wait of the single launch gives up (0: the
+        default 2^20); ``unreachable`` makes every wait give up (the step then
+        ends normally with NaN outputs for the heads whose selection gave up)."""
+        self._check(self._L.hws_set_wait_limit(self.handle, int(max_polls), int(bool(unreachable))),
+                    "hws_set_wait_limit")
 
     def profile_enable(self, enable: bool = True):
         self._check(self._L.hws_profile_enable(self.handle, int(enable)), "hws_profile_enable")

@@ -337,6 +337,22 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  * unknown mode. */
 hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode);
 
+/* Time-out of the single launch's hand-off waits (the selection launch of
+ * HWS_LAUNCH_AUTO, HWS_LAUNCH_SINGLE and HWS_LAUNCH_COOPERATIVE; the
+ * per-stage kernels of HWS_LAUNCH_MULTI never wait).  Not part of the method:
+ * a control for callers that want a shorter bound and for tests of the
+ * failure path.  A waiting workgroup gives up after max_polls polls of its
+ * counter (about a microsecond each; rounded up to a multiple of 256; 0
+ * restores the default 2^20, at most 2^24), sets an error word, and every
+ * other wait then gives up too; the step still runs to its end and writes
+ * NaN into out and lse of every retrieval head whose selection gave up (of
+ * every head when the per-stage attention follows the selection).  unreachable != 0 raises every wait's
+ * target by one, so each wait gives up: every kernel still exits normally
+ * and the next step with unreachable = 0 is correct again (the step resets
+ * its own selection state).  Applies to later hws_decode calls on ctx.
+ * Returns HWS_ERR_INVALID_ARG for max_polls > 2^24. */
+hws_status hws_set_wait_limit(hws_ctx* ctx, uint32_t max_polls, int32_t unreachable);
+
 /* Optional per-stage timing with HIP events on the decode stream.
  * hws_profile_enable(ctx, 1) starts recording one event pair per stage per
  * decode call; hws_profile_read(ctx, ms, calls, n) waits for the recorded

@@ -178,6 +178,18 @@ def test_launch_mode_values():
     assert hws.lib().hws_profile_stage_name(7) == b""
 
 
+def test_wait_limit_values():
+    c = _ctx()
+    for polls in (0, 1, 256, 1000, 1 << 24):
+        c.set_wait_limit(polls)
+    c.set_wait_limit(256, unreachable=True)
+    c.set_wait_limit(0, unreachable=False)
+    with pytest.raises(hws.HwsError) as e:
+        c.set_wait_limit((1 << 24) + 1)
+    assert e.value.status == hws.HWS_ERR_INVALID_ARG
+    assert hws.lib().hws_set_wait_limit(None, 0, 0) == hws.HWS_ERR_INVALID_ARG
+
+
 class _FakeT:
     """Stand-in for a tensor: only shapes and addresses are read on the host."""
     def __init__(self, shape=(1, 1, 2, 128), nbytes=1 << 20):

@@ -1,0 +1,52 @@
+"""GPU: the time-out path of the single launch's hand-off waits.
+
+The host raises every wait's target past what can arrive (hws_set_wait_limit
+with unreachable = 1) and shortens the bound to 256 polls, so each wait of the
+step gives up after a few hundred microseconds: every kernel still exits,
+the step's retrieval heads come out NaN, and the next step with the normal
+limit is correct again.  Nothing here faults or hangs: each wait is bounded
+by the poll limit whatever the counters hold.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from head_wise_sparse_02_amd import workloads as W
+from head_wise_sparse_02_amd.runner import DecodeSetup
+from gpu_check import check_decode
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # (workload, AUTO's single launch, whether the per-stage attention follows)
+    "fused_128k_shape": (lambda: W.make_workload(3, n=32768, batch=1), "fused", False),
+    "tail_4k": (lambda: W.make_workload(1), "tail", False),
+    "select_then_attend_8k": (lambda: W.make_workload(2, n=8192, batch=2), "select", True),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_waits_that_cannot_finish_end_with_nan_and_recover(case):
+    make, stage, per_stage_after = CASES[case]
+    wl = make()
+    print(f"\n[case] {case}: {wl.name} B={wl.B} N={wl.seq_lens[0]}", flush=True)
+    st = DecodeSetup(wl, keep_host=True)
+
+    st.ctx.set_wait_limit(256, unreachable=True)
+    st.ctx.profile_enable(True)
+    bad = st.decode(debug=True)                       # returns after a device sync
+    prof = st.ctx.profile_read()
+    st.ctx.profile_enable(False)
+    assert prof[stage][1] == 1, prof                  # the launch that waits ran
+    G = wl.G
+    for h in wl.retrieval_heads:
+        assert np.isnan(bad["out"][:, h * G:(h + 1) * G]).all(), f"head {h} not NaN"
+        assert np.isnan(bad["lse"][:, h * G:(h + 1) * G]).all(), f"head {h} lse not NaN"
+    if per_stage_after:
+        assert np.isnan(bad["out"]).all() and np.isnan(bad["lse"]).all()
+
+    st.ctx.set_wait_limit(0, unreachable=False)
+    good = st.decode(debug=True)
+    check_decode(st, good, verbose=False)
+    torch.cuda.synchronize()
