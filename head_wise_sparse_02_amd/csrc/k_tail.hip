@@ -55,6 +55,7 @@ struct TailLds {
   unsigned int cnt[TPT * TW];                 // per (u, wave) counts for ordered compaction
   float lse[MAXT][MAX_G];
   float wm[TW][MAX_G], wl[TW][MAX_G];
+  unsigned long long runs[TT];                // radix scan: sums of runs of nbins / TT bins
   unsigned long long above;
   unsigned int tmp[TW + 1];
   int bin;
@@ -153,28 +154,46 @@ __device__ __forceinline__ unsigned long long wave_prefix(unsigned long long v, 
 
 // Scan `nbins` LDS bins from the top down, starting from `above`; the bin
 // where the cumulative sum first reaches `target` (-1 if it never does) and
-// the sum strictly above it.  One wave does it (no workgroup barrier between
-// the levels): lane l sums its run of nbins/64 bins from the top, a wave
-// prefix sum finds the run that crosses the target, and a second one over
-// that run's bins (one per lane) finds the bin.
-__device__ __forceinline__ void scan_top(TailLds& S, int nbins, unsigned long long above, unsigned long long target,
-                         int& out_bin, unsigned long long& out_above) {
+// the sum strictly above it.  Lane l of wave 0 takes the l-th group of
+// nbins/64 bins from the top: a wave prefix sum over the groups' sums finds
+// the group that crosses the target, and a second one over that group's bins
+// (one per lane) finds the bin.  With more than 8 bins per group every thread
+// first sums a run of nbins/TT bins, so that a lane adds 8 run sums instead
+// of reading its whole group in turn.
+template <int NBINS>
+__device__ __forceinline__ void scan_top(TailLds& S, unsigned long long above, unsigned long long target,
+                                         int& out_bin, unsigned long long& out_above) {
+  constexpr int per = NBINS / 64;             // 64, 16 or 8
+  constexpr int RL = NBINS / TT;              // 8, 2 or 1
+  static_assert(per == 8 * RL, "a group is 8 runs");
   const int tid = threadIdx.x;
+  if constexpr (RL > 1) {
+    // neighbouring threads' runs are 8*RL bytes apart: each starts at a
+    // different offset of its run so that one read spreads over the banks
+    unsigned long long r = 0ull;
+#pragma unroll
+    for (int k = 0; k < RL; ++k) r += S.u.hist[tid * RL + ((k + tid) & (RL - 1))];
+    S.runs[tid] = r;
+    __syncthreads();
+  }
   if (tid < 64) {
-    const int per = nbins / 64;               // 64, 16 or 8
-    const int top = nbins - 1 - tid * per;
+    const int top = NBINS - 1 - tid * per;
     unsigned long long m = 0ull;
-    // the lanes' runs are 8*per bytes apart: each lane starts its sum at a
-    // different offset of its run so that one read instruction spreads over
-    // the banks
-    for (int k = 0; k < per; ++k) m += S.u.hist[top - ((k + tid) & (per - 1))];
+    if constexpr (RL > 1) {
+      const int r0 = TT - 8 * (tid + 1);      // the group's lowest run
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m += S.runs[r0 + ((k + tid) & 7)];
+    } else {
+#pragma unroll
+      for (int k = 0; k < per; ++k) m += S.u.hist[top - ((k + tid) & (per - 1))];
+    }
     const unsigned long long inc = wave_prefix(m, tid);
     const unsigned long long cm = above + inc - m;              // sum above this lane's run
     const unsigned long long run = __ballot(cm < target && cm + m >= target);   // one lane at most
     if (tid == 0) S.bin = -1;
     if (run != 0ull) {                                          // wave-uniform
       const int c = __ffsll((long long)run) - 1;
-      const int ctop = nbins - 1 - c * per;
+      const int ctop = NBINS - 1 - c * per;
       const unsigned long long cabove = __shfl(cm, c);
       const unsigned long long v = tid < per ? S.u.hist[ctop - tid] : 0ull;
       const unsigned long long pre = cabove + wave_prefix(v, tid);
@@ -282,7 +301,7 @@ __device__ __forceinline__ void radix_pass(const DecodeParams& p, TailLds& S, co
     const unsigned long long target = ts[k].target;
     int bin;
     unsigned long long above;
-    scan_top(S, NB, ts[k].above, target, bin, above);
+    scan_top<NB>(S, ts[k].above, target, bin, above);
     if (bin < 0) {                             // rounding left the total short: keep all
       ts[k].done = true;
       ts[k].tstar = 0u;
