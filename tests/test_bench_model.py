@@ -152,3 +152,21 @@ def test_stage_kernel_names():
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_traffic_record_needs_matching_source_hash(tmp_path, monkeypatch):
+    """bench.py reports HBM traffic only from a counter summary taken on the
+    current kernel sources."""
+    rec = {"kernel": "k", "workload": "w", "traffic_bytes_per_launch": 123,
+           "source_sha256": bench.kernel_source_sha("fused")}
+    path = tmp_path / "k_w_traffic.md"
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    path.write_text("# summary\n\n```json\n" + json.dumps(rec) + "\n```\n")
+    assert bench._read_traffic("fused", "k", "w") == 123
+    rec["source_sha256"] = "0" * 64
+    path.write_text("```json\n" + json.dumps(rec) + "\n```\n")
+    assert bench._read_traffic("fused", "k", "w") is None
+    assert bench._read_traffic("fused", "k", "missing") is None
+    # the fused and tail stages hash the same kernel file, the score stage another
+    assert bench.kernel_source_sha("fused") == bench.kernel_source_sha("tail")
+    assert bench.kernel_source_sha("score") != bench.kernel_source_sha("fused")

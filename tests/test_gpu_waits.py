@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+from head_wise_sparse_02_amd import hws
 from head_wise_sparse_02_amd import workloads as W
 from head_wise_sparse_02_amd.runner import DecodeSetup
 from gpu_check import check_decode
@@ -21,6 +22,7 @@ pytestmark = pytest.mark.gpu
 CASES = {
     # (workload, AUTO's single launch, whether the per-stage attention follows)
     "fused_128k_shape": (lambda: W.make_workload(3, n=32768, batch=1), "fused", False),
+    "fused_cooperative": (lambda: W.make_workload(3, n=32768, batch=1), "fused", False),
     "tail_4k": (lambda: W.make_workload(1), "tail", False),
     "select_then_attend_8k": (lambda: W.make_workload(2, n=8192, batch=2), "select", True),
 }
@@ -32,6 +34,8 @@ def test_waits_that_cannot_finish_end_with_nan_and_recover(case):
     wl = make()
     print(f"\n[case] {case}: {wl.name} B={wl.B} N={wl.seq_lens[0]}", flush=True)
     st = DecodeSetup(wl, keep_host=True)
+    if case.endswith("cooperative"):
+        st.ctx.set_launch_mode(hws.HWS_LAUNCH_COOPERATIVE)
 
     st.ctx.set_wait_limit(256, unreachable=True)
     st.ctx.profile_enable(True)
