@@ -316,8 +316,8 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  *    occupancy) and launched as an ordinary dispatch: it relies on this
  *    process having the device's compute units (no CU masking); a kernel
  *    running concurrently on another stream only delays it.  A launch that
- *    cannot make progress ends after about a second per wait with NaN
- *    outputs.  Used when the device supports it and the tiles fit the grid
+ *    cannot make progress ends after about a second per wait (by default;
+ *    hws_set_wait_limit) with NaN outputs.  Used when the device supports it and the tiles fit the grid
  *    (one tile per workgroup with the scan inside, else two); otherwise the
  *    decode runs as HWS_LAUNCH_MULTI.
  *  HWS_LAUNCH_COOPERATIVE: HWS_LAUNCH_SINGLE as a cooperative launch, so the
