@@ -91,18 +91,6 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
   const int h = p.ret_head[hr];
   __shared__ float qt_s[G][R];
   __shared__ float red_m[4][G], red_s[4][G];
-  if (tid < G * R) {
-    const int g = tid / R, j = tid % R;
-    const float* prow = p.proj + ((size_t)h * R + j) * D;
-    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(p.q + ((size_t)b * p.Hq + h * G + g) * D);
-    float acc = 0.f;
-    for (int e = 0; e < D / 2; ++e) {
-      const uint32_t w = qrow[e];
-      acc = fmaf(prow[2 * e], bf16_lo(w), acc);
-      acc = fmaf(prow[2 * e + 1], bf16_hi(w), acc);
-    }
-    qt_s[g][j] = acc;
-  }
 
   const int tok0 = c * SCORE_CHUNK + wave * 256;
   const int page0 = tok0 >> 4;
@@ -128,6 +116,33 @@ __global__ __launch_bounds__(256) void score_index_kernel(DecodeParams p) {
     const char* pg = reinterpret_cast<const char*>(p.index_pool) +
                      (((size_t)blk * p.nR + hr) * page_elems) * (BF16 ? 2 : 4);
     kw[i] = load_nt16(pg + (BF16 ? (lane & 31) : lane) * 16);
+  }
+  // the projected queries q~ = P q, while the index loads are in flight:
+  // each of the G*R dot products is split over 256/(G*R) neighbouring lanes
+  {
+    constexpr int TPD = 256 / (G * R);                // lanes per dot product: 16, 8, 4 or 2
+    constexpr int EPT = D / TPD;                      // dims per lane: 8..64
+    const int dot = tid / TPD, part = tid % TPD;
+    const int g = dot / R, j = dot % R;
+    const float4* prow = reinterpret_cast<const float4*>(p.proj + ((size_t)h * R + j) * D + part * EPT);
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(p.q + ((size_t)b * p.Hq + h * G + g) * D + part * EPT);
+    float acc = 0.f;
+#pragma unroll
+    for (int e8 = 0; e8 < EPT / 8; ++e8) {
+      const u32x4 w = qrow[e8];
+      const float4 pa = prow[2 * e8], pb = prow[2 * e8 + 1];
+      acc = fmaf(pa.x, bf16_lo(w[0]), acc);
+      acc = fmaf(pa.y, bf16_hi(w[0]), acc);
+      acc = fmaf(pa.z, bf16_lo(w[1]), acc);
+      acc = fmaf(pa.w, bf16_hi(w[1]), acc);
+      acc = fmaf(pb.x, bf16_lo(w[2]), acc);
+      acc = fmaf(pb.y, bf16_hi(w[2]), acc);
+      acc = fmaf(pb.z, bf16_lo(w[3]), acc);
+      acc = fmaf(pb.w, bf16_hi(w[3]), acc);
+    }
+#pragma unroll
+    for (int off = 1; off < TPD; off <<= 1) acc += __shfl_xor(acc, off);
+    if (part == 0) qt_s[g][j] = acc;
   }
   __syncthreads();                                    // qt_s ready
   float qv[G][DPL];
