@@ -120,6 +120,14 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
       ok[u] = r0 + u < nrows && (unsigned)pg[u] < plim;
       if (!ok[u]) { pg[u] = 0; ii[u] = 0; }
     }
+    // debug: count each row this processor reads at its position (ring rows
+    // are indexed by ring row, not position, and are not counted)
+    if (p.rows_read != nullptr && sub == 0 && !ring) {
+      int* rr = p.rows_read + (size_t)(b * p.Hkv + h) * p.Nmax;
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+        if (ok[u]) atomicAdd(rr + ii[u], 1);
+    }
 
     // every load of the batch
     float vv[RB][8];

@@ -195,6 +195,14 @@ StageEv stage_events(hws_ctx* ctx, int stage) {
   return ev;
 }
 
+// Last launch of a decode step: the status word, when the caller asked for it
+// (`waited`: a single launch with hand-off waits ran in this step).
+hws_status finish_step(hws_ctx* ctx, const DecodeParams& p, const hws_decode_args* a, bool waited, hipStream_t s) {
+  if (a->status == nullptr) return HWS_OK;
+  const hipError_t e = launch_step_status(p, a->status, waited, s);
+  return e == hipSuccess ? HWS_OK : hip_fail(ctx, e, "status launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,6 +476,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   p.sel_counts = a->sel_counts;
   p.sel_idx = a->sel_idx;
   p.sel_cap = a->sel_cap;
+  p.rows_read = a->rows_read;
+  p.sel_mass = a->sel_mass;
   p.score_chunk = L.score_chunk;
   p.n_score_chunks = L.n_score_chunks;
   p.n_sel_chunks = L.n_sel_chunks;
@@ -488,6 +498,8 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (p.rows_read != nullptr && (e = launch_clear_rows_read(p, s)) != hipSuccess)
+    return hip_fail(ctx, e, "rows_read clear launch");
   if (rope && (e = launch_prep_q(p, s)) != hipSuccess) return hip_fail(ctx, e, "prep_q launch");
   // Single launch after the scoring scan (or with the scan inside, one tile
   // per workgroup, for full-dim G = 4 scoring) when every tile fits the
@@ -506,7 +518,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
     const StageEv ef = stage_events(ctx, 5);
     if ((e = launch_fused(p, nwf, coop, s, ef.start, ef.stop)) != hipSuccess) return hip_fail(ctx, e, "fused launch");
     if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
-    return HWS_OK;
+    return finish_step(ctx, p, a, true, s);
   }
   const int nwg = (single && tail_ok) ? tail_grid(p, coop) : 0;
   const bool tail = nwg > 0 && (long long)L.tail_ntiles <= (long long)TAIL_MAXT * nwg;
@@ -516,7 +528,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
     const StageEv et = stage_events(ctx, 4);
     if ((e = launch_tail(p, nwg, coop, s, et.start, et.stop)) != hipSuccess) return hip_fail(ctx, e, "tail launch");
     if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
-    return HWS_OK;
+    return finish_step(ctx, p, a, true, s);
   }
   // AUTO otherwise: the whole selection in one launch (its workgroups hand
   // the radix passes to each other, as in the single launch) when its tiles
@@ -544,7 +556,7 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   if ((e = launch_merge(p, s, em.start, em.stop)) != hipSuccess) return hip_fail(ctx, e, "merge launch");
   if (ctx->nR > 0 && a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess)
     return hip_fail(ctx, e, "emit launch");
-  return HWS_OK;
+  return finish_step(ctx, p, a, sel1, s);
 }
 
 hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {

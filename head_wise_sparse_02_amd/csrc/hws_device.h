@@ -129,6 +129,25 @@ __device__ __forceinline__ void store_f32_coherent(float* p, float v) {
 // data with agent-scope atomic loads after it has seen the counter.
 __device__ __forceinline__ void wait_memory_ops() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Add the fixed-point mass round(a * 2^40) of this thread's kept tokens
+// (bit u of `keep` marks av[u]) to *acc: a sum over the wave, then one
+// device-scope atomic per wave.  Integer sums do not depend on the order in
+// which the waves add them.
+template <int N>
+__device__ __forceinline__ void add_kept_mass(unsigned long long* acc, const float (&av)[N], unsigned int keep) {
+  unsigned long long m = 0ull;
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    if ((keep >> u) & 1u) m += __float2ull_rn(av[u] * MASS_SCALE);
+  for (int off = 1; off < 64; off <<= 1) m += __shfl_xor(m, off);
+  if ((threadIdx.x & 63) == 0 && m != 0ull) atomicAdd(acc, m);
+}
+
+// Fixed-point mass back to a fraction (NaN marks a head without a set).
+__device__ __forceinline__ float mass_value(unsigned long long m) {
+  return (float)((double)m * (1.0 / 1099511627776.0));
+}
+
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Load 8 consecutive elements of a V row as fp32 (bf16 or e4m3 codes).

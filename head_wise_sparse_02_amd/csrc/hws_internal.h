@@ -60,6 +60,7 @@ struct alignas(256) SelState {
   // head count their arrivals here.
   unsigned int arrive;      // tiles done with a radix pass (monotonic over passes)
   unsigned int tie_arrive;  // tiles that published their tie count
+  unsigned long long kept_mass;  // fixed-point sum of a_i over the kept tokens (only when asked for)
   unsigned long long mass2[P2_BINS];
   unsigned long long mass3[P3_BINS];
 };
@@ -108,6 +109,8 @@ struct DecodeParams {
   int* sel_counts;
   int* sel_idx;
   int sel_cap;
+  int* rows_read;               // debug [B][Hkv][Nmax]: reads of each cached row by the attention, or null
+  float* sel_mass;              // [B][Hkv] or [B][Hq]: kept aggregate mass, or null
   int score_chunk;              // tokens per scoring workgroup
   int tail_tph, tail_ntiles;    // tail: tiles per retrieval head, total tiles
   unsigned int* tail_sync;      // [0] error word, [1 + b*Hkv + h] split arrivals (zeroed by the scan)
@@ -201,6 +204,10 @@ hipError_t launch_select(const DecodeParams& p, hipStream_t s, int pass, hipEven
 hipError_t launch_attend(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_emit(const DecodeParams& p, hipStream_t s);
+// Debug row-read counters to zero; the step's status word (waited: a single
+// launch with hand-off waits ran in this step).
+hipError_t launch_clear_rows_read(const DecodeParams& p, hipStream_t s);
+hipError_t launch_step_status(const DecodeParams& p, int* status, bool waited, hipStream_t s);
 // Single launch for select + attend + merge.  tail_grid() is the number of
 // workgroups of the instantiation `p` needs that the device holds at once (0
 // if there is no such instantiation, or `cooperative` and the device has no

@@ -17,6 +17,8 @@
 //
 // Each workgroup produces (max, sum, unnormalised output) per query head in
 // log2 units; merge_kernel combines them.
+#include <algorithm>
+
 #include "attend_rows.h"
 
 namespace hws {
@@ -135,6 +137,8 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
           eq_mask = keep;
         }
         const unsigned int kept = gt_mask | eq_mask;
+        // kept mass, unless the single-launch selection already summed it
+        if (p.sel_mass != nullptr && !p.agg_out) add_kept_mass(&st->kept_mass, av, kept);
         if (p.select_mode == 0) {                  // top-p: |S| summed over chunks
           block_excl_scan256((unsigned int)__popc(kept), tmp);
           if (tid == 0 && tmp[4] > 0u) atomicAdd(&st->nsel, tmp[4]);
@@ -275,6 +279,23 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
     if (p.GS > 1) p.sel_counts[(size_t)b * p.Hq + h * G + g] = cnt;
     else p.sel_counts[(size_t)b * p.Hkv + h] = cnt;
   }
+  if ((g == 0 || p.GS > 1) && d == 0 && p.sel_mass != nullptr) {
+    const float mv = hr >= 0 ? mass_value(p.sel[((size_t)b * p.nR + hr) * p.GS + (p.GS > 1 ? g : 0)].kept_mass)
+                             : __builtin_nanf("");
+    if (p.GS > 1) p.sel_mass[(size_t)b * p.Hq + h * G + g] = mv;
+    else p.sel_mass[(size_t)b * p.Hkv + h] = mv;
+  }
+}
+
+// Debug row-read counters back to zero before a step (n int32 values).
+__global__ __launch_bounds__(256) void clear_i32_kernel(int* x, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) x[i] = 0;
+}
+
+// The step's status: whether a hand-off wait of the single launch gave up.
+__global__ void step_status_kernel(const unsigned int* err, int* status, int waited) {
+  if (threadIdx.x == 0)
+    *status = (waited && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) ? 1 : 0;
 }
 
 // Rotated fp32 queries at position N-1 (rotate-half pairs (j, j+64)); the
@@ -334,6 +355,19 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hip
   // many splits (a long context in few workgroups' worth of heads): 8 groups
   // of threads per output row halve the serial load rounds; otherwise 4
   return p.max_splits >= 128 ? launch_merge_mg<8>(p, s, e0, e1) : launch_merge_mg<4>(p, s, e0, e1);
+}
+
+hipError_t launch_clear_rows_read(const DecodeParams& p, hipStream_t s) {
+  const size_t n = (size_t)p.B * p.Hkv * p.Nmax;
+  const int nwg = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(clear_i32_kernel, dim3(nwg), dim3(256), 0, s, p.rows_read, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_status(const DecodeParams& p, int* status, bool waited, hipStream_t s) {
+  hipLaunchKernelGGL(step_status_kernel, dim3(1), dim3(64), 0, s, (const unsigned int*)p.tail_sync, status,
+                     waited ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_prep_q(const DecodeParams& p, hipStream_t s) {

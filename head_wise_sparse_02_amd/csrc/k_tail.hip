@@ -447,6 +447,9 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, TailLds& S, 
     }
     p.sel_counts[(size_t)b * p.Hkv + h] = cnt;
   }
+  if (tid == 0 && p.sel_mass != nullptr)
+    p.sel_mass[(size_t)b * p.Hkv + h] =
+        hr >= 0 ? mass_value(load_u64_coherent(&p.sel[(size_t)b * p.nR + hr].kept_mass)) : __builtin_nanf("");
 }
 
 // Rows of one local-head chunk of LOCAL_CHUNK rows (sinks first, then the
@@ -710,7 +713,11 @@ __device__ __forceinline__ void select_tiles(const DecodeParams& p, TailLds& S, 
   radix_pass<3, MAXT>(p, S, tl, av, ts, bymass, err, 0u);
   tie_keep<MAXT, false>(p, S, tl, av, ts, keepm, err);
 #pragma unroll
-  for (int k = 0; k < MAXT; ++k) my_tiles += tl[k].t >= 0 ? 1 : 0;
+  for (int k = 0; k < MAXT; ++k) {
+    my_tiles += tl[k].t >= 0 ? 1 : 0;
+    if (p.sel_mass != nullptr && tl[k].t >= 0)
+      add_kept_mass(&p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].kept_mass, av[k], keepm[k]);
+  }
 }
 
 template <int G, bool FP8, int MODE>
@@ -958,6 +965,7 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   unsigned int keepm[1];
   tie_keep<1, true>(p, S, tl, av, ts, keepm, err);
   const unsigned int keep = keepm[0];
+  if (p.sel_mass != nullptr) add_kept_mass(&st->kept_mass, av[0], keep);
 
   // ---- ordered compaction; the kept tokens' scores (the attention's logits)
   // go to LDS next to the row list, or to the scores buffer if too many ----
@@ -1033,6 +1041,7 @@ __global__ __launch_bounds__(256) void reset_state_kernel(DecodeParams p) {
     st->arrive = 0u;
     st->tie_arrive = 0u;
     st->nsel = 0u;
+    st->kept_mass = 0ull;
   }
   for (int i = threadIdx.x; i < 1 + p.B * p.Hkv; i += 256) p.tail_sync[i] = 0u;
 }

@@ -29,6 +29,7 @@ HWS_SCORE_INDEX, HWS_SCORE_FULL = 0, 1
 HWS_SCOPE_KV_HEAD, HWS_SCOPE_QUERY_HEAD = 0, 1
 HWS_INDEX_F32, HWS_INDEX_BF16 = 0, 1
 HWS_LAUNCH_AUTO, HWS_LAUNCH_MULTI, HWS_LAUNCH_COOPERATIVE, HWS_LAUNCH_SINGLE = 0, 1, 2, 3
+HWS_STEP_OK, HWS_STEP_WAIT_TIMEOUT = 0, 1
 
 EXPORTED = (
     "hws_abi_version", "hws_status_string", "hws_last_error", "hws_create", "hws_destroy",
@@ -69,7 +70,8 @@ class DecodeArgs(ctypes.Structure):
                 ("top_k", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("sel_counts", ctypes.c_void_p), ("sel_idx", ctypes.c_void_p),
                 ("sel_cap", ctypes.c_int32), ("scores", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("rows_read", ctypes.c_void_p), ("sel_mass", ctypes.c_void_p), ("status", ctypes.c_void_p)]
 
 
 class PrefillArgs(ctypes.Structure):
@@ -217,7 +219,7 @@ class Context:
     def decode(self, *, q, block_tables, seq_lens, max_seq_len: int, select_mode: int,
                score_mode: int, out, workspace, top_p=None, top_k=None, lse=None,
                sel_counts=None, sel_idx=None, scores=None, stream=None, select_scope: int = 0,
-               seq_slots=None):
+               seq_slots=None, rows_read=None, sel_mass=None, status=None):
         a = DecodeArgs()
         a.select_scope = int(select_scope)
         a.batch = int(q.shape[0]) if q is not None else 0
@@ -232,6 +234,7 @@ class Context:
         a.scores = _ptr(scores)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+        a.rows_read, a.sel_mass, a.status = _ptr(rows_read), _ptr(sel_mass), _ptr(status)
         self._check(self._L.hws_decode(self.handle, ctypes.byref(a), _stream(stream)), "hws_decode")
 
     def prefill(self, *, q, block_tables, start_pos, out, lse=None, dense: bool = False, stream=None,

@@ -9,6 +9,9 @@ token, then the decode step.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -48,7 +51,7 @@ class DecodeSetup:
     window (prefill chunks of up to ring_slack + 1 positions)."""
 
     def __init__(self, wl: Workload, device: str = "cuda", spare_pages: int = 2,
-                 keep_host: bool = False, sequences=None, segments=None, ring_slack: int = 0):
+                 keep_host=False, sequences=None, segments=None, ring_slack: int = 0):
         self.wl = wl
         self.dev = torch.device(device)
         self.segments = segments or append_segments
@@ -110,14 +113,37 @@ class DecodeSetup:
         self.ctx.bind(self.k_pool, self.v_pool, self.kv_scales, self.index_pool,
                       self.proj if self.nR else None, self.local_k_pool, self.local_v_pool)
 
-        # fill the cache, sequence by sequence
+        # fill the cache, sequence by sequence (keep_host: True keeps every
+        # sequence's host arrays, a collection of indices keeps only those)
         self.q_host = np.zeros((B, Hq, d), dtype=np.float32)
-        self.host = [] if keep_host else None
+        if keep_host is True:
+            keep = set(range(B))
+        elif keep_host:
+            keep = {int(x) for x in keep_host}
+        else:
+            keep = None
+        self.host = [] if keep is not None else None
+        # sequences are drawn on a few threads (numpy releases the GIL while it
+        # fills arrays), at most `ahead` of them beyond the one being appended
+        ahead = max(1, min(8, os.cpu_count() or 1, B))
+        pool = ThreadPoolExecutor(ahead) if sequences is None and B > 1 else None
+        pending = {}
+
+        def fetch(b: int):
+            if sequences is not None:
+                return sequences[b]
+            if pool is None:
+                return wl.sequence(b)
+            for nb in range(b, min(B, b + ahead + 1)):
+                if nb not in pending:
+                    pending[nb] = pool.submit(wl.sequence, nb)
+            return pending.pop(b).result()
+
         for b in range(B):
-            seq = wl.sequence(b) if sequences is None else sequences[b]
+            seq = fetch(b)
             self.q_host[b] = seq.q
-            if keep_host:
-                self.host.append(seq)
+            if keep is not None:
+                self.host.append(seq if b in keep else None)
             k = torch.from_numpy(seq.k).to(torch.bfloat16).to(self.dev)[None]
             v = torch.from_numpy(seq.v).to(torch.bfloat16).to(self.dev)[None]
             for start, cnt in (segments or append_segments)(wl.seq_lens[b]):
@@ -125,7 +151,9 @@ class DecodeSetup:
                 self.ctx.append(self.block_tables[b:b + 1], sp, k[:, start:start + cnt].contiguous(),
                                 v[:, start:start + cnt].contiguous(),
                                 seq_slots=None if self.seq_slots is None else self.seq_slots[b:b + 1])
-            del k, v
+            del k, v, seq
+        if pool is not None:
+            pool.shutdown()
         torch.cuda.synchronize(self.dev)
         self.q = torch.from_numpy(self.q_host).to(torch.bfloat16).to(self.dev)
         self.top_p = torch.from_numpy(np.asarray(wl.top_p, np.float32)).to(self.dev)
@@ -139,6 +167,8 @@ class DecodeSetup:
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=self.dev)
         # |S| per KV head, or per query head with one set per query head
         self.sel_counts = torch.empty((B, Hq if self.scope else Hkv), dtype=torch.int32, device=self.dev)
+        self.sel_mass = torch.empty((B, Hq if self.scope else Hkv), dtype=torch.float32, device=self.dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=self.dev)
 
     def prefill(self, q, start_pos, *, dense: bool = False, stream=None):
         """Prefill attention of the chunk q [B, n_tok, Hq, d] (bf16 device tensor)
@@ -151,28 +181,44 @@ class DecodeSetup:
                          dense=dense, stream=stream, seq_slots=self.seq_slots)
         return out, lse
 
-    def decode(self, *, debug: bool = False, sel_cap: int | None = None, stream=None):
-        """Run one decode step.  With debug=True also return the raw scores and
-        the ascending selected positions (host numpy arrays)."""
+    def decode(self, *, debug: bool = False, sel_cap: int | None = None, stream=None,
+               rows_read: bool | None = None, mass: bool | None = None):
+        """Run one decode step.  With debug=True also return the raw scores,
+        the ascending selected positions, the per-position row-read counts of
+        the attention, the kept aggregate mass and the step status (host numpy
+        arrays); ``rows_read`` / ``mass`` switch those two off or on alone."""
         B, G = self.wl.B, self.wl.G
         scores = sel_idx = None
+        rows_read = debug if rows_read is None else rows_read
+        mass = debug if mass is None else mass
         if debug and self.nR:
             scores = torch.empty((B, self.nR, self.Nmax, G), dtype=torch.float32, device=self.dev)
             cap = sel_cap or self.Nmax
             shape = (B, self.nR, G, cap) if self.scope else (B, self.nR, cap)
             sel_idx = torch.full(shape, -1, dtype=torch.int32, device=self.dev)
+        rr = (torch.full((B, self.wl.Hkv, self.Nmax), -7, dtype=torch.int32, device=self.dev)
+              if rows_read else None)
+        sm = self.sel_mass if mass else None
+        status = self.status if debug else None
+        if status is not None:
+            status.fill_(-7)
         self.ctx.decode(q=self.q, block_tables=self.block_tables, seq_lens=self.seq_lens,
                         max_seq_len=self.Nmax, select_mode=self.select_mode,
                         score_mode=self.score_mode, out=self.out, workspace=self.workspace,
                         top_p=self.top_p, top_k=self.top_k, lse=self.lse,
                         sel_counts=self.sel_counts, sel_idx=sel_idx, scores=scores, stream=stream,
-                        select_scope=self.scope, seq_slots=self.seq_slots)
+                        select_scope=self.scope, seq_slots=self.seq_slots, rows_read=rr,
+                        sel_mass=sm, status=status)
         if not debug:
             return None
         torch.cuda.synchronize(self.dev)
         res = {"out": self.out.cpu().numpy(), "lse": self.lse.cpu().numpy(),
-               "sel_counts": self.sel_counts.cpu().numpy()}
+               "sel_counts": self.sel_counts.cpu().numpy(), "status": int(self.status.item())}
         if scores is not None:
             res["scores"] = scores.cpu().numpy()
             res["sel_idx"] = sel_idx.cpu().numpy()
+        if rr is not None:
+            res["rows_read"] = rr.cpu().numpy()
+        if sm is not None:
+            res["sel_mass"] = sm.cpu().numpy()
         return res

@@ -28,11 +28,22 @@ NEEDLE_JITTER = 0.05
 
 
 def bf16_rne(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 precision (ties to even), as float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
-    return r.view(np.float32)
+    """Round float32 values to bfloat16 precision (ties to even), as float32.
+
+    Adds 0x7FFF plus the lowest kept bit to the bit pattern and clears the
+    16 dropped bits (in place on a copy, in slices, to keep temporaries small)."""
+    out = np.array(x, dtype=np.float32, order="C", copy=True)
+    flat = out.reshape(-1).view(np.uint32)
+    tmp = np.empty(min(flat.size, 1 << 22), dtype=np.uint32)
+    for lo in range(0, flat.size, tmp.size):
+        u = flat[lo:lo + tmp.size]
+        t = tmp[:u.size]
+        np.right_shift(u, np.uint32(16), out=t)
+        np.bitwise_and(t, np.uint32(1), out=t)
+        np.add(t, np.uint32(0x7FFF), out=t)
+        np.add(u, t, out=u)
+        np.bitwise_and(u, np.uint32(0xFFFF0000), out=u)
+    return out
 
 
 def _unit(v: np.ndarray) -> np.ndarray:

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HWS_ABI_VERSION 4
+#define HWS_ABI_VERSION 5
 
 typedef int32_t hws_status;
 enum {
@@ -176,7 +176,27 @@ typedef struct {
                                 workspace)                                    */
   void* workspace;           /* hws_workspace_size() bytes                    */
   size_t workspace_bytes;
+  /* ABI 5 (all optional, NULL = not wanted): */
+  int32_t* rows_read;        /* debug: [B][Hkv][max_seq_len] int32, how many
+                                times the attention read the cached row of
+                                each position for each KV head (K and V, or V
+                                alone when FULL scores give the logits).  The
+                                step clears it first.  Rows of local heads
+                                kept in a ring are not counted.               */
+  float* sel_mass;           /* [B][Hkv] (KV scope) or [B][Hq] (query scope):
+                                the aggregate mass the selected set keeps,
+                                sum of a_i over S (a query head's own
+                                probabilities in the query scope), in
+                                [0, 1]; NaN for local heads ([RTPurbo] Main
+                                results: attention mass retained)             */
+  int32_t* status;           /* device int32: HWS_STEP_OK, or
+                                HWS_STEP_WAIT_TIMEOUT when a hand-off wait of
+                                the single launch gave up (the affected
+                                outputs are then NaN)                         */
 } hws_decode_args;
+
+/* Values of hws_decode_args.status (written on the device by the step). */
+enum { HWS_STEP_OK = 0, HWS_STEP_WAIT_TIMEOUT = 1 };
 
 /* ABI version of the loaded library (HWS_ABI_VERSION). */
 int32_t hws_abi_version(void);

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(hws.EXPORTED) == decl
-    assert L.hws_abi_version() == 4
+    assert L.hws_abi_version() == 5
     assert L.hws_status_string(hws.HWS_ERR_WORKSPACE) == b"workspace too small"
 
 

@@ -134,15 +134,61 @@ def test_llama8b_layer_full_size():
     _run(W.make_workload(2), verbose=False)
 
 
-def test_oracle_topk_128k_sampled():
+def _sample_pairs(wl, n_pairs: int, must=()):
+    """A seeded sample of n_pairs distinct (sequence, KV head) pairs that
+    includes ``must``; it covers every sequence before repeating one."""
+    rng = np.random.default_rng(np.random.SeedSequence([wl.cfg, wl.seed, 5000]))
+    pairs = list(dict.fromkeys(tuple(x) for x in must))
+    order = rng.permutation(wl.B * wl.Hkv)
+    for b_first in (True, False):
+        for i in order:
+            b, h = int(i) // wl.Hkv, int(i) % wl.Hkv
+            if len(pairs) >= n_pairs:
+                break
+            if (b, h) in pairs or (b_first and any(pb == b for pb, _ in pairs)):
+                continue
+            pairs.append((b, h))
+    return pairs[:n_pairs]
+
+
+def test_oracle_topk_128k_sampled_and_timed_path():
+    """The headline workload at its full size (B = 4, N = 131072, the fused
+    launch over 256 tiles): 8 sampled (sequence, KV head) pairs against the
+    oracle, then the timed call (no debug outputs, only kept scores written)
+    bitwise equal to the debug call."""
     wl = W.make_workload(3)
-    _run(wl, pairs=[(0, 0), (1, 3), (2, 5), (3, 7)])
+    pairs = _sample_pairs(wl, 8)
+    st = DecodeSetup(wl, keep_host=sorted({b for b, _ in pairs}))
+    st.ctx.profile_enable(True)
+    res = st.decode(debug=True)
+    assert st.ctx.profile_read()["fused"][1] == 1
+    check_decode(st, res, pairs=pairs, verbose=True)
+    st.decode()
+    prof = st.ctx.profile_read()
+    st.ctx.profile_enable(False)
+    assert prof["fused"][1] == 1, prof
+    torch.cuda.synchronize()
+    for key, t in (("out", st.out), ("lse", st.lse), ("sel_counts", st.sel_counts)):
+        np.testing.assert_array_equal(t.cpu().numpy(), res[key], err_msg=key)
 
 
-def test_long_256k_sampled():
+def test_long_256k_all_heads():
     wl = W.make_workload(4)
-    _, res, reps = _run(wl, pairs=[(0, 0), (0, 1), (0, 7)])
+    _, res, reps = _run(wl, pairs=[(0, h) for h in range(wl.Hkv)])
     print("config 4 retrieval |S| =", res["sel_counts"][0, 0], flush=True)
+
+
+def test_ragged_fp8_mix_full_size_sampled():
+    """The ragged fp8 workload at its full size (B = 32, contexts drawn from
+    8K..128K, the default launch shape): 8 sampled (sequence, KV head) pairs,
+    among them both retrieval heads of the longest sequence."""
+    wl = W.make_workload(5)
+    longest = int(np.argmax(wl.seq_lens))
+    pairs = _sample_pairs(wl, 8, must=[(longest, h) for h in wl.retrieval_heads])
+    print(f"\n[case] ragged fp8 full size: longest N={wl.seq_lens[longest]}, pairs {pairs}", flush=True)
+    st = DecodeSetup(wl, keep_host=sorted({b for b, _ in pairs}))
+    res = st.decode(debug=True)
+    check_decode(st, res, pairs=pairs, verbose=True)
 
 
 @BOTH

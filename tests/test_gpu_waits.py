@@ -4,7 +4,8 @@ The host raises every wait's target past what can arrive (hws_set_wait_limit
 with unreachable = 1) and shortens the bound to 256 polls, so each wait of the
 step gives up after a few hundred microseconds: every kernel still exits,
 the step's retrieval heads come out NaN, and the next step with the normal
-limit is correct again.  Nothing here faults or hangs: each wait is bounded
+limit is correct again.  The step's status word says which step gave up
+(HWS_STEP_WAIT_TIMEOUT) and which did not.  Nothing here faults or hangs: each wait is bounded
 by the poll limit whatever the counters hold.
 """
 
@@ -43,6 +44,7 @@ def test_waits_that_cannot_finish_end_with_nan_and_recover(case):
     prof = st.ctx.profile_read()
     st.ctx.profile_enable(False)
     assert prof[stage][1] == 1, prof                  # the launch that waits ran
+    assert bad["status"] == hws.HWS_STEP_WAIT_TIMEOUT, bad["status"]   # visible to the caller
     G = wl.G
     for h in wl.retrieval_heads:
         assert np.isnan(bad["out"][:, h * G:(h + 1) * G]).all(), f"head {h} not NaN"
@@ -52,5 +54,6 @@ def test_waits_that_cannot_finish_end_with_nan_and_recover(case):
 
     st.ctx.set_wait_limit(0, unreachable=False)
     good = st.decode(debug=True)
+    assert good["status"] == hws.HWS_STEP_OK
     check_decode(st, good, verbose=False)
     torch.cuda.synchronize()

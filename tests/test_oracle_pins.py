@@ -475,6 +475,80 @@ def test_query_scope_brute_force_and_dense():
     np.testing.assert_allclose(d["o64"], _sdpa(q, k, v, ATTN), rtol=0, atol=1e-6)
 
 
+# -- retained-mass diagnostics ([RTPurbo] Main results: attention mass kept) ----
+
+def _two_level_mass_case(n=200, m=8):
+    """Keys that give two-level logits, different in the index and in full dim.
+
+    P selects dims 0..15 (index_scale 1) and attention uses attn_scale 1.
+    Query head g = c_g e0 + f_g e20 with c = (1, 2), f = (1, 0); the m needle
+    keys (positions 10, 20, ...) are 3 e0, the other keys 2 e20.  Index logits:
+    3 c_g for needles, 0 otherwise; full-dim logits: 3 c_g for needles, 2 f_g
+    otherwise (e20 lies outside the index's span)."""
+    q = np.zeros((2, 128))
+    q[0, 0], q[0, 20] = 1.0, 1.0
+    q[1, 0] = 2.0
+    k = np.zeros((n, 128))
+    k[:, 20] = 2.0
+    needles = np.arange(1, m + 1) * 10
+    k[needles] = 0.0
+    k[needles, 0] = 3.0
+    P = np.zeros((16, 128))
+    P[np.arange(16), np.arange(16)] = 1.0
+    v = O.bf16_round(np.random.default_rng(9).standard_normal((n, 128)))
+    return q, k, v, P, needles
+
+
+def test_retained_mass_two_level_closed_form():
+    """S = the needles.  Index mass = mean_g m e^{3c_g} / (m e^{3c_g} + n - m);
+    full-dim mass = mean_g m e^{3c_g} / (m e^{3c_g} + (n - m) e^{2 f_g}).  A mass
+    taken from the wrong logits, a softmax of the mean logits, or a mean over
+    the wrong axis each gives another number."""
+    n, m = 200, 8
+    q, k, v, P, needles = _two_level_mass_case(n, m)
+    r = O.decode_head_ref(q, k, k, v, kind="retrieval", proj=P, score_mode="index", select_mode="top_p",
+                          top_p=0.6, attn_scale=1.0, index_scale=1.0, with_full_mass=True)
+    np.testing.assert_array_equal(r["S"], needles)
+    c, f = np.array([1.0, 2.0]), np.array([1.0, 0.0])
+    idx = np.mean(m * np.exp(3 * c) / (m * np.exp(3 * c) + n - m))
+    full = np.mean(m * np.exp(3 * c) / (m * np.exp(3 * c) + (n - m) * np.exp(2 * f)))
+    assert abs(idx - 0.69973) < 1e-5 and abs(full - 0.52279) < 1e-5   # evaluated by hand
+    np.testing.assert_allclose(r["index_mass"], idx, rtol=1e-12)
+    np.testing.assert_allclose(r["full_mass"], full, rtol=1e-12)
+    # per query head (scope "query", p = 0.4): head 0 keeps the needles
+    # (7 of them hold only 0.399), head 1 reaches p after 4 and keeps their ties
+    rq = O.decode_head_ref(q, k, k, v, kind="retrieval", proj=P, score_mode="index", select_mode="top_p",
+                           top_p=0.4, attn_scale=1.0, index_scale=1.0, scope="query")
+    for g in range(2):
+        np.testing.assert_array_equal(rq["S_heads"][g], needles)
+        np.testing.assert_allclose(rq["index_mass_heads"][g],
+                                   m * np.exp(3 * c[g]) / (m * np.exp(3 * c[g]) + n - m), rtol=1e-12)
+
+
+def test_retained_mass_all_tokens_and_local_heads():
+    """p = 1 keeps every token: both masses are 1.  A local head over keys whose
+    logit is A on its sinks and window and 0 elsewhere keeps
+    |S| e^A / (|S| e^A + n - |S|) of the full-dim mass."""
+    n = 300
+    q, k, v, P, _ = _two_level_mass_case(n)
+    r = O.decode_head_ref(q, k, k, v, kind="retrieval", proj=P, score_mode="index", select_mode="top_p",
+                          top_p=1.0, attn_scale=1.0, index_scale=1.0, with_full_mass=True)
+    assert r["S"].size == n
+    np.testing.assert_allclose([r["index_mass"], r["full_mass"]], [1.0, 1.0], rtol=1e-12)
+    n_sink, window, A = 4, 50, 1.5
+    S = O.local_token_set(n, n_sink, window)
+    assert S.size == n_sink + window
+    ql = np.zeros((2, 128))
+    ql[:, 0] = 1.0
+    kl = np.zeros((n, 128))
+    kl[S, 0] = A
+    rl = O.decode_head_ref(ql, kl, kl, v, kind="local", n_sink=n_sink, window=window, attn_scale=1.0,
+                           with_full_mass=True)
+    L = S.size
+    np.testing.assert_allclose(rl["full_mass"], L * np.exp(A) / (L * np.exp(A) + n - L), rtol=1e-12)
+    assert rl["index_mass"] is None
+
+
 # -- data-free head classification (effective rank) ------------------------------
 
 def _weights_with_spectrum(sv, d_model, rng):
