@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -203,6 +204,40 @@ hws_status finish_step(hws_ctx* ctx, const DecodeParams& p, const hws_decode_arg
   return e == hipSuccess ? HWS_OK : hip_fail(ctx, e, "status launch");
 }
 
+// Workspace of hws_decode_noalloc: one static device array, which every GPU
+// that loads the library holds its own copy of.  Host code never passes the
+// array's name to a kernel (in host code it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns for
+// the current device, looked up once per device.
+__device__ __align__(256) unsigned char scratch[HWS_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddr {
+  int dev;
+  char* ptr;
+};
+std::mutex scratch_mu;
+std::vector<ScratchAddr> scratch_addrs;
+
+hws_status scratch_of_current_device(hws_ctx* ctx, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  for (const ScratchAddr& s : scratch_addrs)
+    if (s.dev == dev) {
+      *out = s.ptr;
+      return HWS_OK;
+    }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr) return hip_fail(ctx, e, "hipGetSymbolAddress(scratch)");
+  scratch_addrs.push_back(ScratchAddr{dev, static_cast<char*>(ptr)});
+  *out = static_cast<char*>(ptr);
+  return HWS_OK;
+}
+
+hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, bool noalloc);
+
 }  // namespace
 
 extern "C" {
@@ -388,6 +423,20 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
 }
 
 hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
+  return decode_step(ctx, a, stream, false);
+}
+
+hws_status hws_decode_noalloc(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
+  return decode_step(ctx, a, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One decode step; `noalloc` takes the workspace from the static scratch
+// array of the current device instead of the caller's.
+hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, bool noalloc) {
   if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
   if (a == nullptr) return fail(ctx, HWS_ERR_INVALID_ARG, "args is NULL");
   if (!ctx->bound) return fail(ctx, HWS_ERR_STATE, "decode before bind");
@@ -418,10 +467,18 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
   const bool rope = c.rope_theta > 0.f;
   const int GS = a->select_scope == HWS_SCOPE_QUERY_HEAD ? ctx->G : 1;
   const Layout L = make_layout(ctx, a->batch, a->max_seq_len, rope, a->score_mode, GS);
-  if (a->workspace == nullptr || a->workspace_bytes < L.total)
-    return fail(ctx, HWS_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, L.total);
-
-  char* ws = static_cast<char*>(a->workspace);
+  char* ws = nullptr;
+  if (noalloc) {
+    if (L.total > (size_t)HWS_NOALLOC_SCRATCH_BYTES)
+      return fail(ctx, HWS_ERR_CAPACITY, "step needs %zu bytes of workspace; the static scratch array holds %u",
+                  L.total, (unsigned)HWS_NOALLOC_SCRATCH_BYTES);
+    const hws_status st = scratch_of_current_device(ctx, &ws);
+    if (st != HWS_OK) return st;
+  } else {
+    if (a->workspace == nullptr || a->workspace_bytes < L.total)
+      return fail(ctx, HWS_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, L.total);
+    ws = static_cast<char*>(a->workspace);
+  }
   DecodeParams p{};
   p.B = a->batch;
   p.Hq = c.num_q_heads;
@@ -558,6 +615,10 @@ hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* a, void* stream) {
     return hip_fail(ctx, e, "emit launch");
   return finish_step(ctx, p, a, sel1, s);
 }
+
+}  // namespace
+
+extern "C" {
 
 hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {
   if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;

@@ -37,7 +37,9 @@ EXPORTED = (
     "hws_workspace_size", "hws_append", "hws_decode", "hws_profile_enable",
     "hws_profile_read", "hws_profile_stage_name", "hws_set_launch_mode",
     "hws_effective_rank_workspace", "hws_effective_rank", "hws_prefill", "hws_set_wait_limit",
+    "hws_decode_noalloc",
 )
+HWS_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class HwsError(RuntimeError):
@@ -107,6 +109,7 @@ def lib() -> ctypes.CDLL:
         "hws_workspace_size": (i32, [vp, i32, i32, i32, i32, P(ctypes.c_size_t)]),
         "hws_append": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp]),
         "hws_decode": (i32, [vp, P(DecodeArgs), vp]),
+        "hws_decode_noalloc": (i32, [vp, P(DecodeArgs), vp]),
         "hws_prefill": (i32, [vp, P(PrefillArgs), vp]),
         "hws_profile_enable": (i32, [vp, i32]),
         "hws_set_launch_mode": (i32, [vp, i32]),
@@ -219,7 +222,9 @@ class Context:
     def decode(self, *, q, block_tables, seq_lens, max_seq_len: int, select_mode: int,
                score_mode: int, out, workspace, top_p=None, top_k=None, lse=None,
                sel_counts=None, sel_idx=None, scores=None, stream=None, select_scope: int = 0,
-               seq_slots=None, rows_read=None, sel_mass=None, status=None):
+               seq_slots=None, rows_read=None, sel_mass=None, status=None, noalloc: bool = False):
+        """hws_decode (or, with noalloc=True, hws_decode_noalloc, which ignores
+        ``workspace`` and uses the library's static scratch array)."""
         a = DecodeArgs()
         a.select_scope = int(select_scope)
         a.batch = int(q.shape[0]) if q is not None else 0
@@ -235,7 +240,17 @@ class Context:
         a.workspace = _ptr(workspace)
         a.workspace_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
         a.rows_read, a.sel_mass, a.status = _ptr(rows_read), _ptr(sel_mass), _ptr(status)
-        self._check(self._L.hws_decode(self.handle, ctypes.byref(a), _stream(stream)), "hws_decode")
+        if noalloc:
+            self._check(self._L.hws_decode_noalloc(self.handle, ctypes.byref(a), _stream(stream)),
+                        "hws_decode_noalloc")
+        else:
+            self._check(self._L.hws_decode(self.handle, ctypes.byref(a), _stream(stream)), "hws_decode")
+
+    def decode_noalloc(self, **kw):
+        """hws_decode_noalloc: the decode step with its workspace in the
+        library's static device array (``workspace`` may be None)."""
+        kw.setdefault("workspace", None)
+        self.decode(noalloc=True, **kw)
 
     def prefill(self, *, q, block_tables, start_pos, out, lse=None, dense: bool = False, stream=None,
                 seq_slots=None):

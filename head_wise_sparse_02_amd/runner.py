@@ -182,11 +182,13 @@ class DecodeSetup:
         return out, lse
 
     def decode(self, *, debug: bool = False, sel_cap: int | None = None, stream=None,
-               rows_read: bool | None = None, mass: bool | None = None):
+               rows_read: bool | None = None, mass: bool | None = None, noalloc: bool = False):
         """Run one decode step.  With debug=True also return the raw scores,
         the ascending selected positions, the per-position row-read counts of
         the attention, the kept aggregate mass and the step status (host numpy
-        arrays); ``rows_read`` / ``mass`` switch those two off or on alone."""
+        arrays); ``rows_read`` / ``mass`` switch those two off or on alone.
+        ``noalloc`` calls hws_decode_noalloc (the library's static scratch
+        array instead of this setup's workspace)."""
         B, G = self.wl.B, self.wl.G
         scores = sel_idx = None
         rows_read = debug if rows_read is None else rows_read
@@ -208,7 +210,7 @@ class DecodeSetup:
                         top_p=self.top_p, top_k=self.top_k, lse=self.lse,
                         sel_counts=self.sel_counts, sel_idx=sel_idx, scores=scores, stream=stream,
                         select_scope=self.scope, seq_slots=self.seq_slots, rows_read=rr,
-                        sel_mass=sm, status=status)
+                        sel_mass=sm, status=status, noalloc=noalloc)
         if not debug:
             return None
         torch.cuda.synchronize(self.dev)

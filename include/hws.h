@@ -288,6 +288,26 @@ hws_status hws_append(hws_ctx* ctx, int32_t n_seq, int32_t n_tok, const int32_t*
  * the local heads read their rows from ring slot seq_slots[b]; a slot out of
  * range reads no rows (that sequence's local heads output 0 with lse -inf). */
 hws_status hws_decode(hws_ctx* ctx, const hws_decode_args* args, void* stream);
+
+/* Largest workspace (hws_workspace_size bytes) hws_decode_noalloc can serve:
+ * the size of the library's static device scratch array. */
+#define HWS_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* hws_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * same step with the same kernels and results, but its workspace is a
+ * library-owned static device array of HWS_NOALLOC_SCRATCH_BYTES on each GPU
+ * (held by the loaded library until the process ends); args->workspace and
+ * args->workspace_bytes are ignored.  A step whose hws_workspace_size exceeds
+ * HWS_NOALLOC_SCRATCH_BYTES returns HWS_ERR_CAPACITY (host check, before any
+ * HIP call).  The first call on a device looks up that device's copy of the
+ * array (with the device current; make one call before capturing a graph).
+ * Nothing is allocated, set or synchronised: the step's own kernels reset
+ * every counter and state they read, so each call starts clean whatever the
+ * previous call left in the array.  Every call on a GPU shares that GPU's
+ * array, so calls that overlap on one GPU (two streams, or two host threads)
+ * race: the caller must order them on one stream. */
+hws_status hws_decode_noalloc(hws_ctx* ctx, const hws_decode_args* args, void* stream);
 /* (FULL scoring of an fp8 cache multiplies each page's products of the e4m3
  * codes, widened exactly to bf16, by the page's K scale; it runs in the
  * per-stage kernels, as HWS_LAUNCH_MULTI or AUTO's one-launch selection.) */

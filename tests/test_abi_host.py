@@ -342,3 +342,29 @@ def test_prefill_validation_without_gpu():
         with pytest.raises(hws.HwsError) as e:
             _prefill(cr, **kw)
         assert e.value.status == status, (kw, e.value)
+
+
+def test_decode_noalloc_validation_without_gpu():
+    """hws_decode_noalloc checks a call like hws_decode (it needs no caller
+    workspace) and refuses a step whose workspace exceeds its static scratch
+    array, all before any HIP call."""
+    c = _ctx()
+    with pytest.raises(hws.HwsError) as e:
+        _decode(c, workspace=None, noalloc=True)
+    assert e.value.status == hws.HWS_ERR_STATE          # before bind
+    c.set_head_kinds([1, 0])
+    c.bind(4096, 4096, None, 4096, 4096)
+    big = 600
+    assert c.workspace_size(big, 512, 0) > hws.HWS_NOALLOC_SCRATCH_BYTES >= c.workspace_size(1, 512, 0)
+    cases = [
+        (dict(q=_FakeT((big, 8, 128)), max_seq_len=512), hws.HWS_ERR_CAPACITY),
+        (dict(max_seq_len=32 * 16 + 1), hws.HWS_ERR_CAPACITY),
+        (dict(q=None), hws.HWS_ERR_INVALID_ARG),
+        (dict(select_mode=2), hws.HWS_ERR_INVALID_ARG),
+        (dict(top_p=None), hws.HWS_ERR_INVALID_ARG),
+    ]
+    for kw, status in cases:
+        with pytest.raises(hws.HwsError) as e:
+            _decode(c, workspace=None, noalloc=True, **kw)
+        assert e.value.status == status, (kw, e.value)
+        assert b"hws_decode_noalloc" in str(e.value).encode() and hws.lib().hws_last_error(c.handle)
