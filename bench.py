@@ -30,7 +30,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_GBS = 8000.0          # MI355X HBM3E peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-STAGE_SOURCE = {"score": "k_score.hip", "attend": "k_attend.hip", "tail": "k_tail.hip", "fused": "k_tail.hip"}
+STAGE_SOURCE = {"score": "k_score.hip", "attend": "k_attend.hip", "tail": "k_tail.hip", "fused": "k_tail.hip",
+                "fused_index": "k_tail.hip", "select": "k_tail.hip"}
 
 
 def stage_kernel(stage: str, wl) -> str:
@@ -39,13 +40,14 @@ def stage_kernel(stage: str, wl) -> str:
         if wl.score_mode == "index":
             return "score_index_kernel"
         return "score_full_g4_kernel" if (wl.G == 4 and not wl.rope_theta) else "score_full_kernel"
-    return {"attend": "attend_kernel", "tail": "tail_kernel", "fused": "fused_g4_kernel"}.get(stage, stage)
+    return {"attend": "attend_kernel", "tail": "tail_kernel", "fused": "fused_g4_kernel",
+            "fused_index": "fused_index_kernel", "select": "select_single_kernel"}.get(stage, stage)
 
 
 def stage_bytes(stage: str, by: dict) -> int:
     """Algorithmic bytes a stage moves: the fused launch moves all of them, the
     tail launch the attention's and the step's inputs/outputs."""
-    if stage == "fused":
+    if stage in ("fused", "fused_index"):
         return by["total"]
     if stage == "tail":
         return by["attend"] + by["io"]
@@ -61,10 +63,12 @@ def parse_args(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cold-iters", type=int, default=20,
                     help="extra steps each preceded by a 1 GiB cache flush (0 = skip)")
-    ap.add_argument("--launch", choices=["auto", "single", "multi", "cooperative"], default="auto",
-                    help="auto: the library's default; single: one launch after (or with) the scoring "
+    ap.add_argument("--launch", choices=["auto", "single", "multi", "cooperative", "scan-select", "scan-single"],
+                    default="auto",
+                    help="auto: the library's default; single: one launch with (or after) the scoring "
                          "scan, grid sized to the device; cooperative: the same as a cooperative launch; "
-                         "multi: a kernel per stage")
+                         "multi: a kernel per stage; scan-single: the scan, then the single launch; "
+                         "scan-select: the scan, the selection as one launch, then attention and merge")
     ap.add_argument("--index", choices=["f32", "bf16"], default="f32",
                     help="storage of the r=16 index (64 or 32 bytes per token and retrieval head)")
     ap.add_argument("--scope", choices=["kv", "query"], default="kv",
@@ -310,7 +314,9 @@ def main(argv=None) -> int:
     setup = DecodeSetup(wl, keep_host=want_cpu)
     setup.ctx.set_launch_mode({"auto": hws.HWS_LAUNCH_AUTO, "multi": hws.HWS_LAUNCH_MULTI,
                                "single": hws.HWS_LAUNCH_SINGLE,
-                               "cooperative": hws.HWS_LAUNCH_COOPERATIVE}[args.launch])
+                               "cooperative": hws.HWS_LAUNCH_COOPERATIVE,
+                               "scan-select": hws.HWS_LAUNCH_SCAN_SELECT,
+                               "scan-single": hws.HWS_LAUNCH_SCAN_SINGLE}[args.launch])
     print("[bench] cache filled; warming up", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         setup.decode()

@@ -40,8 +40,9 @@ __device__ __forceinline__ void local_row_at(const DecodeParams& p, int b, int l
 }
 
 // Row r of the list: retrieval rows are offsets (from lo) in `rows`, whose
-// page is pages[offset / 16]; local rows are at index ltok[r] of page lpg[r]
-// (local_row_at), in the ring pools when there is a ring.
+// page is pages[offset / 16]; local rows -- and retrieval rows when `rows` is
+// null -- are at index ltok[r] of page lpg[r] (local_row_at), local ones in
+// the ring pools when there is a ring.
 // MODE 0: logits q.k from K rows; MODE 1: retrieval heads only, logits from
 // the stored full-dim scores; MODE 2: both (scores for retrieval heads).
 // RET: the rows are known to be a retrieval head's (no K path compiled in).
@@ -49,12 +50,14 @@ __device__ __forceinline__ void local_row_at(const DecodeParams& p, int b, int l
 // null reads them from the scores buffer at the row's position.
 // row_mask (retrieval rows, one set per query head): bit g of row_mask[r] says
 // whether query head g keeps row r; null means every head keeps every row.
+// init = false continues the (m, l, o) of an earlier call on the same head.
 template <int G, bool FP8, int MODE, int RB, bool RET = false, bool ROW_ORDER = FP8>
 __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, int h, int hr, int lo, int nrows,
                                                 int r_begin, int r_step, int sub, const unsigned short* rows,
                                                 const int* pages, const int* ltok, const int* lpg,
                                                 const float* lds_logits, float (&m)[G], float (&l)[G],
-                                                float (&o)[G][8], const unsigned char* row_mask = nullptr) {
+                                                float (&o)[G][8], const unsigned char* row_mask = nullptr,
+                                                bool init = true) {
   static_assert(!RET || MODE != 0, "retrieval rows read K only in index mode");
   constexpr bool NEED_K = MODE != 1 && !RET;
   const bool is_ret = RET || hr >= 0;
@@ -89,18 +92,20 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
   const int hstride = ring ? 1 : p.Hp;
   const int hslot = ring ? 0 : p.pool_slot[h];
   const unsigned plim = ring ? (unsigned)p.ring_pages : (unsigned)p.num_blocks;
+  if (init) {                                    // else: more rows of the same head
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = NEG_INF;
-    l[g] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      m[g] = NEG_INF;
+      l[g] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+      for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+    }
   }
 
   for (int r0 = r_begin; r0 < nrows; r0 += r_step) {
     int ii[RB], pg[RB];
     bool ok[RB];
-    if (is_ret) {
+    if (is_ret && rows != nullptr) {
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         const int off = rows[min(r0 + u, nrows - 1)];
@@ -291,3 +296,4 @@ __device__ __forceinline__ void combine_wave_procs(float (&m)[G], float (&l)[G],
 }
 
 }  // namespace hws
+

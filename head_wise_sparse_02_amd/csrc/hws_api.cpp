@@ -19,10 +19,13 @@
 
 using namespace hws;
 
+static_assert(PHASES == HWS_PHASES, "phase count of the profiling hook");
+
 namespace {
 
-constexpr int NUM_STAGES = 7;
-const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge", "tail", "fused", "prefill"};
+constexpr int NUM_STAGES = 8;
+const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge", "tail", "fused", "prefill",
+                                             "fused_index"};
 
 struct EvPair {
   hipEvent_t a, b;
@@ -34,6 +37,7 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace regions of one decode call.
 struct Layout {
   size_t scores, agg, spart, sel, apart_ml, apart_o, qrot, tail_sync, tail_ties, total;
+  size_t row_list, tile_cnt, pair_rows, item_base, bal_ml, bal_o;   // attention balanced by kept rows
   int Nagg;
   int score_chunk, n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
   int tail_tph, tail_ntiles;
@@ -61,6 +65,8 @@ struct hws_ctx {
   unsigned int spin_limit = 1u << 20;  // polls per hand-off wait (~1 us each)
   unsigned int wait_bias = 0;
   bool prof = false;
+  uint64_t* phase_t = nullptr;     // phase timestamps of the single launches (profiling aid)
+  int phase_wgs = 0;
   std::vector<EvPair> recorded;
   std::vector<hipEvent_t> pool;
 };
@@ -138,7 +144,9 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode,
   L.ncR = cdiv(Nmax, L.att_chunk_R);
   const long long local_rows = std::min<long long>(Nmax, (long long)c->cfg.n_sink + c->cfg.window);
   L.ncL = std::max(1, cdiv(local_rows, LOCAL_CHUNK));
-  L.max_splits = std::max(c->nR > 0 ? L.ncR : 1, c->nL > 0 ? L.ncL : 1);
+  // (the single launch with the index scan inside has one split per tile, of
+  // at least FI_TILE_MIN positions)
+  L.max_splits = std::max(c->nR > 0 ? std::max(L.ncR, cdiv(Nmax, FI_TILE_MIN)) : 1, c->nL > 0 ? L.ncL : 1);
   const size_t nRb = (size_t)B * c->nR;
   size_t off = 0;
   L.scores = off;   off = align_up(off + nRb * Nmax * G * sizeof(float));
@@ -154,7 +162,20 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode,
   L.tail_tph = cdiv(Nmax, TAIL_TILE);
   L.tail_ntiles = (int)(nRb * L.tail_tph);
   L.tail_sync = off; off = align_up(off + (1 + (size_t)B * c->cfg.num_kv_heads) * sizeof(unsigned int));
-  L.tail_ties = off; off = align_up(off + (size_t)L.tail_ntiles * sizeof(unsigned int));
+  // tie counts per tile: for the smallest tiles any single launch uses
+  L.tail_ties = off; off = align_up(off + nRb * cdiv(Nmax, FI_TILE_MIN) * sizeof(unsigned int));
+  // attention balanced by kept rows (index scores, one set per KV head)
+  if (score_mode == HWS_SCORE_INDEX && GS == 1) {
+    // items: at most min(BAL_ITEMS, rows / BAL_RMIN) plus one per pair
+    const size_t npairs = (size_t)B * c->cfg.num_kv_heads;
+    const size_t nitems = std::min<size_t>(BAL_ITEMS, (npairs * Nmax + BAL_RMIN - 1) / BAL_RMIN) + npairs;
+    L.row_list = off;  off = align_up(off + nRb * Nmax * sizeof(int2));
+    L.tile_cnt = off;  off = align_up(off + (size_t)L.tail_ntiles * sizeof(unsigned int));
+    L.pair_rows = off; off = align_up(off + nRb * sizeof(int));
+    L.item_base = off; off = align_up(off + (npairs + 1) * sizeof(int));
+    L.bal_ml = off;    off = align_up(off + nitems * G * sizeof(float2));
+    L.bal_o = off;     off = align_up(off + nitems * G * D * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -548,10 +569,13 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
   p.tail_ties = reinterpret_cast<unsigned int*>(ws + L.tail_ties);
   p.spin_limit = ctx->spin_limit;
   p.wait_bias = ctx->wait_bias;
+  p.phase_t = reinterpret_cast<unsigned long long*>(ctx->phase_t);
+  p.phase_wgs = ctx->phase_wgs;
   std::memcpy(p.ret_slot, ctx->ret_slot, sizeof(p.ret_slot));
   std::memcpy(p.ret_head, ctx->ret_head, sizeof(p.ret_head));
   std::memcpy(p.loc_head, ctx->loc_head, sizeof(p.loc_head));
   std::memcpy(p.pool_slot, ctx->pool_slot, sizeof(p.pool_slot));
+  std::memcpy(p.loc_slot, ctx->loc_slot, sizeof(p.loc_slot));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -561,21 +585,50 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
   // Single launch after the scoring scan (or with the scan inside, one tile
   // per workgroup, for full-dim G = 4 scoring) when every tile fits the
   // grid the device holds at once; otherwise one kernel per stage.
-  const bool coop = ctx->launch_mode == HWS_LAUNCH_COOPERATIVE;
+  const int mode = ctx->launch_mode;
+  const bool coop = mode == HWS_LAUNCH_COOPERATIVE;
   // (one set per query head runs in the per-stage kernels)
-  const bool single = ctx->nR > 0 && ctx->launch_mode != HWS_LAUNCH_MULTI && GS == 1;
+  const bool single = ctx->nR > 0 && mode != HWS_LAUNCH_MULTI && GS == 1;
+  // the scan inside the single launch: AUTO, SINGLE and COOPERATIVE
+  const bool scan_inside = single && (mode == HWS_LAUNCH_AUTO || mode == HWS_LAUNCH_SINGLE || coop);
   // AUTO takes the single launch after the scan only for short contexts (one
   // 4096-position stretch per head: there the per-stage launches' latency
   // dominates; measured 40.5 against 44.1 us at 4096, slower from 8192 on)
-  const bool tail_ok = ctx->launch_mode == HWS_LAUNCH_SINGLE || coop ||
-                       (ctx->launch_mode == HWS_LAUNCH_AUTO && a->max_seq_len <= AUTO_TAIL_MAX_LEN);
-  const int nwf = single ? fused_grid(p, coop) : 0;
+  const bool tail_ok = mode == HWS_LAUNCH_SINGLE || coop || mode == HWS_LAUNCH_SCAN_SINGLE ||
+                       (mode == HWS_LAUNCH_AUTO && a->max_seq_len <= AUTO_TAIL_MAX_LEN);
+  const int nwf = scan_inside ? fused_grid(p, coop) : 0;
   if (nwf > 0 && L.tail_ntiles <= nwf) {
     p.n_score_chunks = L.tail_tph;                 // one (max, sum) partial per tile
     const StageEv ef = stage_events(ctx, 5);
     if ((e = launch_fused(p, nwf, coop, s, ef.start, ef.stop)) != hipSuccess) return hip_fail(ctx, e, "fused launch");
     if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
     return finish_step(ctx, p, a, true, s);
+  }
+  // index scores: the scan inside the launch too, in tiles of 2048 positions,
+  // or 8192 where 2048 would need more workgroups than the device holds
+  // (measured: 2048-position tiles beat 8192 at the 8B layer shape, 53.8
+  // against 74.4 us, the scan of a tile being bound by one workgroup's loads
+  // in flight).  AUTO takes it for G <= 4: a dense G = 8 selection gathers
+  // too few rows per workgroup at once (256K-token workload: 107 against
+  // 90.8 us for the per-stage attention).
+  if (scan_inside && a->score_mode == HWS_SCORE_INDEX && (mode != HWS_LAUNCH_AUTO || ctx->G <= 4)) {
+    int pick = 0, pick_nw = 0;
+    for (const int sp : {4, 16}) {
+      const long long ntiles = (long long)a->batch * ctx->nR * cdiv(a->max_seq_len, (long long)TAIL_THREADS * sp);
+      const int nwi = fused_index_grid(p, sp, coop);
+      if (pick == 0 && nwi > 0 && ntiles <= nwi) { pick = sp; pick_nw = nwi; }
+    }
+    if (pick > 0) {
+      const int tph = cdiv(a->max_seq_len, (long long)TAIL_THREADS * pick);
+      p.tail_tph = tph;
+      p.tail_ntiles = a->batch * ctx->nR * tph;
+      p.n_score_chunks = tph;                        // one (max, sum) partial per tile
+      const StageEv ef = stage_events(ctx, 7);
+      if ((e = launch_fused_index(p, pick, pick_nw, coop, s, ef.start, ef.stop)) != hipSuccess)
+        return hip_fail(ctx, e, "fused index launch");
+      if (a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess) return hip_fail(ctx, e, "emit launch");
+      return finish_step(ctx, p, a, true, s);
+    }
   }
   const int nwg = (single && tail_ok) ? tail_grid(p, coop) : 0;
   const bool tail = nwg > 0 && (long long)L.tail_ntiles <= (long long)TAIL_MAXT * nwg;
@@ -590,14 +643,25 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
   // AUTO otherwise: the whole selection in one launch (its workgroups hand
   // the radix passes to each other, as in the single launch) when its tiles
   // fit, then the per-stage attention and merge.
-  const int nws = (single && ctx->launch_mode == HWS_LAUNCH_AUTO) ? tail_grid(p, false, true) : 0;
+  const int nws = (single && (mode == HWS_LAUNCH_AUTO || mode == HWS_LAUNCH_SCAN_SELECT)) ? tail_grid(p, false, true) : 0;
   const bool sel1 = nws > 0 && (long long)L.tail_ntiles <= (long long)TAIL_MAXT * nws;
+  // SCAN_SELECT with index scores: the attention balanced by kept rows (the
+  // selection writes every tile's kept offsets); AUTO keeps the per-stage
+  // attention, measured faster so far (ragged fp8 workload 84 against 79 us,
+  // 256K-token workload 36 against 58 plus a longer merge)
+  const bool balanced = sel1 && mode == HWS_LAUNCH_SCAN_SELECT && a->score_mode == HWS_SCORE_INDEX && L.bal_o != 0 &&
+                        (long long)a->batch * c.num_kv_heads <= BAL_MAX_HEADS;
   if (ctx->nR > 0) {
     const StageEv es = stage_events(ctx, 0);
     if ((e = launch_score(p, s, es.start, es.stop)) != hipSuccess) return hip_fail(ctx, e, "score launch");
     const StageEv ev = stage_events(ctx, 1);
     if (sel1) {
       p.agg_out = 1;
+      if (balanced) {
+        p.row_list = reinterpret_cast<int2*>(ws + L.row_list);
+        p.tile_cnt = reinterpret_cast<unsigned int*>(ws + L.tile_cnt);
+        p.pair_rows = reinterpret_cast<int*>(ws + L.pair_rows);
+      }
       if ((e = launch_tail(p, nws, false, s, ev.start, ev.stop, true)) != hipSuccess)
         return hip_fail(ctx, e, "select launch");
     } else {
@@ -608,7 +672,16 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
     }
   }
   const StageEv ea = stage_events(ctx, 2);
-  if ((e = launch_attend(p, s, ea.start, ea.stop)) != hipSuccess) return hip_fail(ctx, e, "attend launch");
+  if (balanced) {
+    p.pair_rows = reinterpret_cast<int*>(ws + L.pair_rows);
+    p.row_list = reinterpret_cast<int2*>(ws + L.row_list);
+    p.item_base = reinterpret_cast<int*>(ws + L.item_base);
+    p.bal_ml = reinterpret_cast<float2*>(ws + L.bal_ml);
+    p.bal_o = reinterpret_cast<float*>(ws + L.bal_o);
+    if ((e = launch_attend_balanced(p, s, ea.start, ea.stop)) != hipSuccess) return hip_fail(ctx, e, "attend launch");
+  } else if ((e = launch_attend(p, s, ea.start, ea.stop)) != hipSuccess) {
+    return hip_fail(ctx, e, "attend launch");
+  }
   const StageEv em = stage_events(ctx, 3);
   if ((e = launch_merge(p, s, em.start, em.stop)) != hipSuccess) return hip_fail(ctx, e, "merge launch");
   if (ctx->nR > 0 && a->sel_idx != nullptr && (e = launch_emit(p, s)) != hipSuccess)
@@ -693,6 +766,79 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* a, void* stream) {
   return HWS_OK;
 }
 
+namespace {
+
+// Workspace of hws_dense_lse: rotated queries (RoPE on), then the chunk partials.
+struct DenseLayout {
+  size_t qrot, spart, total;
+  int nch;
+};
+
+DenseLayout dense_layout(const hws_ctx* c, int B, int Nmax) {
+  DenseLayout L{};
+  L.nch = cdiv(Nmax, DENSE_CHUNK);
+  size_t off = 0;
+  L.qrot = off;
+  off = align_up(off + (c->cfg.rope_theta > 0.f ? (size_t)B * c->cfg.num_q_heads * D * sizeof(float) : 0));
+  L.spart = off;
+  off = align_up(off + (size_t)B * c->cfg.num_kv_heads * L.nch * c->G * sizeof(float2));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+hws_status hws_dense_lse_workspace(const hws_ctx* ctx, int32_t batch, int32_t max_seq_len, size_t* bytes) {
+  if (ctx == nullptr || bytes == nullptr || batch < 1 || max_seq_len < 1) return HWS_ERR_INVALID_ARG;
+  if ((long long)max_seq_len > (long long)ctx->cfg.max_blocks_per_seq * BS) return HWS_ERR_CAPACITY;
+  *bytes = dense_layout(ctx, batch, max_seq_len).total;
+  return HWS_OK;
+}
+
+hws_status hws_dense_lse(hws_ctx* ctx, int32_t batch, int32_t max_seq_len, const void* q,
+                         const int32_t* block_tables, const int32_t* seq_lens, float* lse_full, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, HWS_ERR_STATE, "dense lse before bind");
+  const hws_config& c = ctx->cfg;
+  if (batch < 1 || max_seq_len < 1) return fail(ctx, HWS_ERR_INVALID_ARG, "batch = %d, max_seq_len = %d", batch, max_seq_len);
+  if ((long long)max_seq_len > (long long)c.max_blocks_per_seq * BS)
+    return fail(ctx, HWS_ERR_CAPACITY, "max_seq_len = %d exceeds %d pages of 16", max_seq_len, c.max_blocks_per_seq);
+  if (q == nullptr || block_tables == nullptr || seq_lens == nullptr || lse_full == nullptr)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "null device pointer (q, block_tables, seq_lens or lse_full)");
+  if (ctx->ring_rows > 0 && ctx->nL > 0)
+    return fail(ctx, HWS_ERR_UNSUPPORTED, "local heads in a ring keep only their sinks and window");
+  const DenseLayout L = dense_layout(ctx, batch, max_seq_len);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(ctx, HWS_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  DecodeParams p{};
+  p.B = batch;
+  p.Hq = c.num_q_heads;
+  p.Hkv = c.num_kv_heads;
+  p.G = ctx->G;
+  p.Nmax = max_seq_len;
+  p.max_blocks = c.max_blocks_per_seq;
+  p.num_blocks = c.num_blocks;
+  p.rope_theta = c.rope_theta;
+  p.c2_attn = (float)((double)c.attn_scale * 1.4426950408889634);
+  p.q = static_cast<const uint16_t*>(q);
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.k_pool = ctx->buf.k_pool;
+  p.kv_scales = c.kv_dtype == HWS_KV_FP8_E4M3 ? ctx->buf.kv_scales : nullptr;
+  p.Hp = ctx->Hp;
+  std::memcpy(p.pool_slot, ctx->pool_slot, sizeof(p.pool_slot));
+  p.qrot = c.rope_theta > 0.f ? reinterpret_cast<float*>(ws + L.qrot) : nullptr;
+  p.spart = reinterpret_cast<float2*>(ws + L.spart);
+  p.n_score_chunks = L.nch;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (p.qrot != nullptr && (e = launch_prep_q(p, s)) != hipSuccess) return hip_fail(ctx, e, "prep_q launch");
+  if ((e = launch_dense_lse(p, lse_full, s)) != hipSuccess) return hip_fail(ctx, e, "dense lse launch");
+  return HWS_OK;
+}
+
 hws_status hws_effective_rank_workspace(int32_t num_q_heads, int32_t num_kv_heads, size_t* bytes) {
   if (bytes == nullptr || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
     return HWS_ERR_INVALID_ARG;
@@ -715,8 +861,7 @@ hws_status hws_effective_rank(int32_t num_q_heads, int32_t num_kv_heads, int32_t
 
 hws_status hws_set_launch_mode(hws_ctx* ctx, int32_t mode) {
   if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
-  if (mode != HWS_LAUNCH_AUTO && mode != HWS_LAUNCH_MULTI && mode != HWS_LAUNCH_COOPERATIVE &&
-      mode != HWS_LAUNCH_SINGLE)
+  if (mode < HWS_LAUNCH_AUTO || mode > HWS_LAUNCH_SCAN_SINGLE)
     return fail(ctx, HWS_ERR_INVALID_ARG, "launch mode = %d", mode);
   ctx->launch_mode = mode;
   return HWS_OK;
@@ -758,6 +903,15 @@ hws_status hws_profile_read(hws_ctx* ctx, double* ms, int32_t* calls, int32_t n)
   }
   ctx->recorded.clear();
   return st;
+}
+
+hws_status hws_profile_phases(hws_ctx* ctx, uint64_t* buf, int32_t max_workgroups) {
+  if (check_ctx(ctx)) return HWS_ERR_INVALID_ARG;
+  if (buf != nullptr && max_workgroups < 1)
+    return fail(ctx, HWS_ERR_INVALID_ARG, "max_workgroups = %d", max_workgroups);
+  ctx->phase_t = buf;
+  ctx->phase_wgs = buf != nullptr ? max_workgroups : 0;
+  return HWS_OK;
 }
 
 const char* hws_profile_stage_name(int32_t i) {

@@ -150,6 +150,13 @@ __device__ __forceinline__ float mass_value(unsigned long long m) {
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Phase timestamp of this workgroup (profiling aid; p.phase_t is null unless
+// the caller asked for it): the constant 100 MHz device clock.
+__device__ __forceinline__ void stamp_phase(const DecodeParams& p, int k) {
+  if (p.phase_t != nullptr && threadIdx.x == 0 && (int)blockIdx.x < p.phase_wgs)
+    p.phase_t[(size_t)blockIdx.x * PHASES + k] = __builtin_amdgcn_s_memrealtime();
+}
+
 // Load 8 consecutive elements of a V row as fp32 (bf16 or e4m3 codes).
 template <bool FP8>
 __device__ __forceinline__ void load_row8(const void* pool, size_t row_off, int sub, float* x) {

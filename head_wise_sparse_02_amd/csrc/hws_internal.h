@@ -21,6 +21,12 @@ constexpr int SEL_PER_THREAD = 16;
 constexpr int SEL_CHUNK = SEL_THREADS * SEL_PER_THREAD;   // 16384 tokens
 constexpr int HIST_BINS = 4096;   // pass 1 bins: bits 30..19 of the fp32 pattern
 constexpr int LOCAL_CHUNK = 256;  // rows per local-head attention workgroup
+constexpr int PHASES = 12;        // phase timestamps per workgroup (HWS_PHASES)
+// Attention balanced by kept rows: the rows of all heads are cut into about
+// BAL_ITEMS items of at least BAL_RMIN rows (one item more per head at most).
+constexpr int BAL_ITEMS = 2048;
+constexpr int BAL_RMIN = 64;
+constexpr int BAL_MAX_HEADS = 2048;  // (sequence, KV head) pairs the item table holds in LDS
 
 // Single-launch tail (selection + attention + merge in one cooperative launch)
 constexpr int TAIL_THREADS = 512;
@@ -60,6 +66,7 @@ struct alignas(256) SelState {
   // head count their arrivals here.
   unsigned int arrive;      // tiles done with a radix pass (monotonic over passes)
   unsigned int tie_arrive;  // tiles that published their tie count
+  unsigned int cnt_arrive;  // tiles that published their kept count (row lists for the attention)
   unsigned long long kept_mass;  // fixed-point sum of a_i over the kept tokens (only when asked for)
   unsigned long long mass2[P2_BINS];
   unsigned long long mass3[P3_BINS];
@@ -117,13 +124,26 @@ struct DecodeParams {
   unsigned int* tail_ties;      // [tail_ntiles] ties at t* per tile
   unsigned int spin_limit;      // polls before a hand-off wait gives up (multiple of 256)
   unsigned int wait_bias;       // added to every hand-off target (0; 1 makes each wait give up)
+  unsigned long long* phase_t;  // [phase_wgs][HWS_PHASES] phase timestamps of the single launches, or null
+  int phase_wgs;
   int n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
   int agg_out;                  // the single-launch selection ran: a_i is in agg, and the merge
                                 // checks the hand-off error word
+  // Attention balanced by kept rows (after the one-launch selection): the
+  // selection writes each retrieval head's kept rows as one list in position
+  // order; the attention cuts every head's rows into items of about the same
+  // number of rows.
+  int2* row_list;               // [B][nR][Nmax] (position, page) of the kept rows, or null
+  unsigned int* tile_cnt;       // [tail_ntiles] kept rows of each selection tile
+  int* pair_rows;               // [B * nR] kept rows of each retrieval head
+  int* item_base;               // [B * Hkv + 1] first item of each (sequence, KV head), head order
+  float2* bal_ml;               // [BAL_ITEMS + B * Hkv][G] (max, sum) of each item
+  float* bal_o;                 // [BAL_ITEMS + B * Hkv][G][D] unnormalised output of each item
   signed char ret_slot[MAX_KV];
   signed char ret_head[MAX_KV];
   signed char loc_head[MAX_KV];
   signed char pool_slot[MAX_KV];  // head's index within a page (-1: not in the pages)
+  signed char loc_slot[MAX_KV];   // head's number among the local heads (-1: retrieval head)
 };
 
 struct AppendParams {
@@ -203,10 +223,19 @@ hipError_t launch_score(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hip
 hipError_t launch_select(const DecodeParams& p, hipStream_t s, int pass, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_attend(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+// Attention balanced by kept rows (index scores, one set per KV head, after
+// the one-launch selection wrote sel_rows / tile_cnt) and its merge.
+hipError_t launch_attend_balanced(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_merge_balanced(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_emit(const DecodeParams& p, hipStream_t s);
 // Debug row-read counters to zero; the step's status word (waited: a single
 // launch with hand-off waits ran in this step).
 hipError_t launch_clear_rows_read(const DecodeParams& p, hipStream_t s);
+// Dense log-sum-exp over every cached row (diagnostic): chunk partials of
+// DENSE_CHUNK rows into p.spart ([B][Hkv][chunks][G], log2 units), then the
+// reduction into lse_full [B][Hq] (natural log).
+constexpr int DENSE_CHUNK = 1024;
+hipError_t launch_dense_lse(const DecodeParams& p, float* lse_full, hipStream_t s);
 hipError_t launch_step_status(const DecodeParams& p, int* status, bool waited, hipStream_t s);
 // Single launch for select + attend + merge.  tail_grid() is the number of
 // workgroups of the instantiation `p` needs that the device holds at once (0
@@ -222,6 +251,13 @@ hipError_t launch_tail(const DecodeParams& p, int nwg, bool cooperative, hipStre
 int fused_grid(const DecodeParams& p, bool cooperative);
 hipError_t launch_fused(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
                         hipEvent_t e1);
+// The same with the r = 16 index scan inside (KV-scope sets), in tiles of
+// TAIL_THREADS * sp positions (sp = 4 or 16); p.tail_tph / tail_ntiles /
+// n_score_chunks must describe those tiles.
+constexpr int FI_TILE_MIN = TAIL_THREADS * 4;            // smallest index tile: 2048 positions
+int fused_index_grid(const DecodeParams& p, int sp, bool cooperative);
+hipError_t launch_fused_index(const DecodeParams& p, int sp, int nwg, bool cooperative, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_append(const AppendParams& p, int kv_fp8, hipStream_t s);
 // Effective rank of the query-key kernels (fp64 Gram, Cholesky, Jacobi).
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1);

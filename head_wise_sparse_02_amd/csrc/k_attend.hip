@@ -237,11 +237,21 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
   const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int d = threadIdx.x % D, grp = threadIdx.x / D;
   const int hr = p.ret_slot[h];
-  const int nspl = hr >= 0 ? p.ncR : p.ncL;
   const int N = min(p.seq_lens[b], p.Nmax);
-  const size_t base = (size_t)(b * p.Hkv + h) * p.max_splits * G + g;
-  const float2* ml = p.apart_ml + base;                 // split s at ml[s * G]
-  const float* po = p.apart_o + base * D + d;           // split s at po[s * G * D]
+  int nspl;
+  const float2* ml;                                     // split s at ml[s * G]
+  const float* po;                                      // split s at po[s * G * D]
+  if (p.item_base != nullptr) {                         // balanced attention: this head's items
+    const int i0 = p.item_base[b * p.Hkv + h];
+    nspl = p.item_base[b * p.Hkv + h + 1] - i0;
+    ml = p.bal_ml + (size_t)i0 * G + g;
+    po = p.bal_o + ((size_t)i0 * G + g) * D + d;
+  } else {
+    nspl = hr >= 0 ? p.ncR : p.ncL;
+    const size_t base = (size_t)(b * p.Hkv + h) * p.max_splits * G + g;
+    ml = p.apart_ml + base;
+    po = p.apart_o + base * D + d;
+  }
   float M = NEG_INF, L = 0.f, O = 0.f;
   for (int s0 = grp; s0 < nspl; s0 += SB * MERGE_GROUPS) {
     float2 v[SB];
@@ -285,6 +295,284 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
     if (p.GS > 1) p.sel_mass[(size_t)b * p.Hq + h * G + g] = mv;
     else p.sel_mass[(size_t)b * p.Hkv + h] = mv;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Attention balanced by kept rows ([ICS] §2: the sparsity is irregular per
+// token, query and head, so chunks cut by position leave a few dense ones as
+// the long pole).  Every workgroup builds the same item table: (sequence, KV
+// head) pair i = b * Hkv + h has c_i rows -- the kept rows the selection
+// listed (retrieval) or its sinks and window (local) --, C = sum c_i, an item
+// is R = max(BAL_RMIN, ceil(C / BAL_ITEMS)) rows and pair i has ceil(c_i / R)
+// items, numbered in pair order.  Workgroups take items round-robin, load the
+// item's (position, page) list BAL_LIST rows at a time into LDS, gather the
+// rows with the register batches of accumulate_rows and store one partial per
+// item; workgroup 0 writes the table's first item per pair for the merge.
+// Index scores only (the rows carry K and V), one set per KV head.
+// ---------------------------------------------------------------------------
+constexpr int BAL_THREADS = 256;
+constexpr int BAL_LIST = 512;                 // rows per (position, page) list in LDS
+constexpr int BAL_TABLE = BAL_MAX_HEADS;      // pairs the LDS table holds
+
+// In-place exclusive scan of x[0..n) (n <= BAL_TABLE) over a 256-thread
+// block; returns the total.
+__device__ int block_scan_excl(int* x, int n, int* tmp) {
+  constexpr int PER = BAL_TABLE / BAL_THREADS;  // 8 entries per thread
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int v[PER], run = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid * PER + k;
+    v[k] = i < n ? x[i] : 0;
+    run += v[k];
+  }
+  int inc = run;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  int base = inc - run;
+  for (int w = 0; w < wave; ++w) base += tmp[w];
+  const int total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid * PER + k;
+    if (i < n) x[i] = base;
+    base += v[k];
+  }
+  __syncthreads();
+  return total;
+}
+
+// Rows of pair (b, h): the kept rows the selection listed, or the sinks and
+// window.
+__device__ __forceinline__ int pair_row_count(const DecodeParams& p, int b, int h) {
+  const int hr = p.ret_slot[h];
+  if (hr >= 0) return p.pair_rows[(size_t)b * p.nR + hr];
+  const int N = min(p.seq_lens[b], p.Nmax);
+  const int L1 = min(p.n_sink, N);
+  return L1 + (N - max(L1, N - p.window));
+}
+
+template <int G, bool FP8>
+__global__ __launch_bounds__(BAL_THREADS) void attend_balanced_kernel(DecodeParams p) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int proc = tid >> 4, sub = tid & 15;
+  const int npairs = p.B * p.Hkv;
+  __shared__ int base_s[BAL_TABLE + 1];
+  __shared__ int cnt_s[BAL_TABLE];
+  __shared__ int tmp[8];
+  __shared__ long long csum_s[4];
+  __shared__ int tok_s[BAL_LIST], pg_s[BAL_LIST];
+  __shared__ float wm[4][MAX_G], wl[4][MAX_G];
+  __shared__ float wo[4][MAX_G][D];
+
+  // ---- the item table (the same in every workgroup) ----
+  long long csum = 0;
+  for (int i = tid; i < npairs; i += BAL_THREADS) {
+    const int c = pair_row_count(p, i / p.Hkv, i % p.Hkv);
+    cnt_s[i] = c;
+    csum += c;
+  }
+  for (int off = 1; off < 64; off <<= 1) csum += __shfl_xor(csum, off);
+  if (lane == 0) csum_s[wave] = csum;
+  __syncthreads();
+  const long long C = csum_s[0] + csum_s[1] + csum_s[2] + csum_s[3];
+  const int R = (int)max((long long)BAL_RMIN, (C + BAL_ITEMS - 1) / BAL_ITEMS);
+  for (int i = tid; i < npairs; i += BAL_THREADS) base_s[i] = (cnt_s[i] + R - 1) / R;
+  __syncthreads();
+  const int nitems = block_scan_excl(base_s, npairs, tmp);
+  if (tid == 0) base_s[npairs] = nitems;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int i = tid; i <= npairs; i += BAL_THREADS) p.item_base[i] = base_s[i];
+
+  constexpr int RB = AttRB<G, 0>::value;
+  for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+    // the pair of item `it`: the last i with base_s[i] <= it
+    int lo_i = 0, hi_i = npairs;
+    while (hi_i - lo_i > 1) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if (base_s[mid] <= it) lo_i = mid; else hi_i = mid;
+    }
+    const int b = lo_i / p.Hkv, h = lo_i % p.Hkv;
+    const int hr = p.ret_slot[h];
+    const int N = min(p.seq_lens[b], p.Nmax);
+    const int r0 = (it - base_s[lo_i]) * R, r1 = min(r0 + R, cnt_s[lo_i]);
+    const int L1 = min(p.n_sink, N), start2 = max(L1, N - p.window);
+    const int2* list = hr >= 0 ? p.row_list + ((size_t)b * p.nR + hr) * p.Nmax : nullptr;
+    float m[G], l[G], o[G][8];
+    for (int rs = r0; rs < r1 || rs == r0; rs += BAL_LIST) {
+      const int nl = max(0, min(BAL_LIST, r1 - rs));
+      for (int q = tid; q < nl; q += BAL_THREADS) {
+        const int r = rs + q;
+        if (hr >= 0) {
+          const int2 e = list[r];
+          tok_s[q] = e.x;
+          pg_s[q] = e.y;
+        } else {
+          local_row_at(p, b, p.loc_slot[h], r < L1 ? r : start2 + (r - L1), tok_s[q], pg_s[q]);
+        }
+      }
+      __syncthreads();
+      if (FP8 && hr < 0 && p.ring_rows > 0)       // the ring holds bf16 rows
+        accumulate_rows<G, false, 0, RB, false, true>(p, b, h, hr, 0, nl, proc * RB, 16 * RB, sub, nullptr,
+                                                      nullptr, tok_s, pg_s, nullptr, m, l, o, nullptr, rs == r0);
+      else
+        accumulate_rows<G, FP8, 0, RB>(p, b, h, hr, 0, nl, proc * RB, 16 * RB, sub, nullptr, nullptr, tok_s,
+                                       pg_s, nullptr, m, l, o, nullptr, rs == r0);
+      __syncthreads();                            // the list is reused
+    }
+    combine_wave_procs<G>(m, l, o);
+    if (lane < 16) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wo[wave][g][8 * sub + j] = o[g][j];
+      }
+    }
+    __syncthreads();
+    float2* ml = p.bal_ml + (size_t)it * G;
+    float* po = p.bal_o + (size_t)it * G * D;
+    for (int e = tid; e < G * D; e += BAL_THREADS) {
+      const int g = e / D, d = e % D;
+      float mm = NEG_INF;
+      for (int k = 0; k < 4; ++k) mm = fmaxf(mm, wm[k][g]);
+      float ll = 0.f, oo = 0.f;
+      for (int k = 0; k < 4; ++k) {
+        if (wm[k][g] == NEG_INF) continue;
+        const float cf = fast_exp2(wm[k][g] - mm);
+        ll += wl[k][g] * cf;
+        oo += wo[k][g][d] * cf;
+      }
+      po[(size_t)g * D + d] = oo;
+      if (d == 0) ml[g] = make_float2(mm, ll);
+    }
+    __syncthreads();                              // wm / wo are reused by the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dense log-sum-exp (diagnostic): every cached row of every KV head, q.k for
+// the group's query heads, online (max, sum of 2^x) per query head.  One
+// workgroup per (DENSE_CHUNK rows, KV head, sequence); its 16 processors take
+// every 16th row, RB rows per batch with all loads in flight.
+// ---------------------------------------------------------------------------
+template <int G, bool FP8>
+__global__ __launch_bounds__(256) void dense_lse_kernel(DecodeParams p) {
+  constexpr int RB = 4;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, proc = tid >> 4, sub = tid & 15, lane = tid & 63, wave = tid >> 6;
+  const int N = min(p.seq_lens[b], p.Nmax);
+  const int lo = c * DENSE_CHUNK, hi = min(N, lo + DENSE_CHUNK);
+  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
+  float qf[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const size_t qo = ((size_t)b * p.Hq + h * G + g) * D + 8 * sub;
+    if (p.qrot != nullptr) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[g][j] = p.qrot[qo + j];
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4*>(p.q + qo);
+      qf[g][0] = bf16_lo(u.x); qf[g][1] = bf16_hi(u.x); qf[g][2] = bf16_lo(u.y); qf[g][3] = bf16_hi(u.y);
+      qf[g][4] = bf16_lo(u.z); qf[g][5] = bf16_hi(u.z); qf[g][6] = bf16_lo(u.w); qf[g][7] = bf16_hi(u.w);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qf[g][j] *= p.c2_attn;
+  }
+  float m[G], s[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { m[g] = NEG_INF; s[g] = 0.f; }
+  const int hslot = p.pool_slot[h];
+  for (int r0 = lo + proc * RB; r0 < hi; r0 += 16 * RB) {
+    float kx[RB][8], ks[RB];
+    bool ok[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int i = min(r0 + u, hi - 1);
+      int pg = bt[i >> 4];
+      ok[u] = r0 + u < hi && (unsigned)pg < (unsigned)p.num_blocks;
+      if (!ok[u]) pg = 0;
+      load_krow8<FP8>(p.k_pool, (size_t)pg * p.Hp + hslot, i & 15, sub, kx[u]);
+      ks[u] = FP8 ? p.kv_scales[((size_t)pg * p.Hp + hslot) * 2] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float a = qf[g][0] * kx[u][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) a = fmaf(qf[g][j], kx[u][j], a);
+        a = row16_sum(a) * ks[u];
+        if (ok[u]) {
+          const float mn = fmaxf(m[g], a);
+          s[g] = s[g] * fast_exp2(m[g] - mn) + fast_exp2(a - mn);
+          m[g] = mn;
+        }
+      }
+    }
+  }
+  // the 64 lanes of a wave hold 4 processors (every lane of a processor the
+  // same values), then the 4 waves
+  __shared__ float wm[4][MAX_G], ws[4][MAX_G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    for (int off = 16; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m[g], off), s2 = __shfl_xor(s[g], off);
+      lse_combine(m[g], s[g], m2, s2);
+    }
+    if (lane == 0) { wm[wave][g] = m[g]; ws[wave][g] = s[g]; }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mm = wm[0][tid], ss = ws[0][tid];
+    for (int w = 1; w < 4; ++w) lse_combine(mm, ss, wm[w][tid], ws[w][tid]);
+    p.spart[(((size_t)b * p.Hkv + h) * p.n_score_chunks + c) * G + tid] = make_float2(mm, ss);
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(64) void dense_lse_reduce_kernel(DecodeParams p, float* lse_full) {
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int N = min(p.seq_lens[b], p.Nmax);
+  const int nch = (N + DENSE_CHUNK - 1) / DENSE_CHUNK;
+  for (int g = 0; g < G; ++g) {
+    float m = NEG_INF, s = 0.f;
+    for (int c = lane; c < nch; c += 64) {
+      const float2 v = p.spart[(((size_t)b * p.Hkv + h) * p.n_score_chunks + c) * G + g];
+      lse_combine(m, s, v.x, v.y);
+    }
+    for (int off = 1; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+      lse_combine(m, s, m2, s2);
+    }
+    if (lane == 0) lse_full[(size_t)b * p.Hq + h * G + g] = (m + log2f(s)) * LN2;
+  }
+}
+
+template <int G>
+static hipError_t launch_dense_lse_g(const DecodeParams& p, float* lse_full, hipStream_t s) {
+  const dim3 grid(p.n_score_chunks, p.Hkv, p.B);
+  if (p.kv_scales != nullptr) hipLaunchKernelGGL((dense_lse_kernel<G, true>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((dense_lse_kernel<G, false>), grid, dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dense_lse_reduce_kernel<G>, dim3(p.Hkv, p.B), dim3(64), 0, s, p, lse_full);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_lse(const DecodeParams& p, float* lse_full, hipStream_t s) {
+  switch (p.G) {
+    case 1: return launch_dense_lse_g<1>(p, lse_full, s);
+    case 2: return launch_dense_lse_g<2>(p, lse_full, s);
+    case 4: return launch_dense_lse_g<4>(p, lse_full, s);
+    case 8: return launch_dense_lse_g<8>(p, lse_full, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Debug row-read counters back to zero before a step (n int32 values).
@@ -355,6 +643,29 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hip
   // many splits (a long context in few workgroups' worth of heads): 8 groups
   // of threads per output row halve the serial load rounds; otherwise 4
   return p.max_splits >= 128 ? launch_merge_mg<8>(p, s, e0, e1) : launch_merge_mg<4>(p, s, e0, e1);
+}
+
+template <int G>
+static hipError_t launch_attend_balanced_g(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  // about four workgroups per compute unit; they loop over the items
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 256;
+  const dim3 grid(std::max(1, std::min(4 * ncu, BAL_ITEMS + p.B * p.Hkv))), blk(BAL_THREADS);
+  if (p.kv_scales != nullptr) return launch_kernel(attend_balanced_kernel<G, true>, grid, blk, s, e0, e1, p);
+  return launch_kernel(attend_balanced_kernel<G, false>, grid, blk, s, e0, e1, p);
+}
+
+hipError_t launch_attend_balanced(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.B * p.Hkv > BAL_TABLE) return hipErrorInvalidValue;
+  switch (p.G) {
+    case 1: return launch_attend_balanced_g<1>(p, s, e0, e1);
+    case 2: return launch_attend_balanced_g<2>(p, s, e0, e1);
+    case 4: return launch_attend_balanced_g<4>(p, s, e0, e1);
+    case 8: return launch_attend_balanced_g<8>(p, s, e0, e1);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_clear_rows_read(const DecodeParams& p, hipStream_t s) {

@@ -16,7 +16,7 @@
 // rows and computes
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims from LDS,
 //                  B = the wave's queries, kept in registers)
-//   O^T += V^T P^T (A = 16 dims x 32 keys of V^T, B = P in bf16),
+//   O^T += V^T P^T (A = 16 dims x 32 keys of V^T, B = P as two bf16 parts),
 // with the online softmax in log2 units between the two.  The S^T layout
 // leaves each lane with 4 keys of one query per 16-key block, which is the
 // B-operand shape of P^T once both operands enumerate the 32 keys of a step
@@ -27,15 +27,18 @@
 // every 16 positions from a multiple of 16 sit in one ring page.
 //
 // With RoPE on, queries are rotated in fp64 at their position and split as
-// q = hi + lo (two bf16 parts), so S keeps fp32-level accuracy; P is rounded
-// to bf16 for the P V product.
+// q = hi + lo (two bf16 parts), so S keeps fp32-level accuracy.  The softmax
+// weights are split the same way for the P V product, P = hi + lo with
+// hi = bf16(P) and lo = bf16(P - hi) (about 17 significant bits), and V^T
+// multiplies both parts: a single bf16 rounding of P (2^-9 relative) moves
+// outputs by up to a few 1e-3, the split by about 1e-5.
 //
 // FP8 pages: the e4m3 codes are widened to bf16 on their way into LDS (exact:
 // every e4m3 value is a bf16 value), so the products are those of the bf16
 // path on the codes; each 16-key block of S is then multiplied by its page's
-// K scale, and each weight by its page's V scale before it is rounded to
-// bf16 for P V (the softmax sum is taken from the unscaled weights).  Both
-// scales enter the exponent: the weight times the V scale is
+// K scale, and each weight by its page's V scale before it is split into its
+// two bf16 parts for P V (the softmax sum is taken from the unscaled
+// weights).  Both scales enter the exponent: the weight times the V scale is
 // exp2(s * c2 * ks + log2(vs) - m), for raw product s and the running max m.
 #include "mfma_tile.h"
 
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     const int key0 = kt * PF_KT;
     const bool inside = key0 + PF_KT - 1 <= t0 &&
                         (ret || key0 + PF_KT - 1 < p.n_sink || key0 > tl - p.window);
-    bf16x8 pb[QB][2];
+    bf16x8 pb[QB][2], pl[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // (rows past the chunk's end hold zero queries: finite, and never written)
@@ -362,8 +365,11 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pb[qb][ks][i] = (__bf16)pv[2 * ks][i];
-          pb[qb][ks][4 + i] = (__bf16)pv[2 * ks + 1][i];
+          const __bf16 h0 = (__bf16)pv[2 * ks][i], h1 = (__bf16)pv[2 * ks + 1][i];
+          pb[qb][ks][i] = h0;
+          pb[qb][ks][4 + i] = h1;
+          pl[qb][ks][i] = (__bf16)(pv[2 * ks][i] - (float)h0);
+          pl[qb][ks][4 + i] = (__bf16)(pv[2 * ks + 1][i] - (float)h1);
         }
     }
 
@@ -377,6 +383,8 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
       if (step + 1 < 16) a_next = vt_frag(S.v[buf], (step + 1) & 1, (step + 1) >> 1, col, quad);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a_cur, pb[qb][ks], o[db][qb]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a_cur, pl[qb][ks], o[db][qb]);
       a_cur = a_next;
     }
 

@@ -124,13 +124,13 @@ __device__ __forceinline__ unsigned int scan_cnt(TailLds& S) {
 }
 
 // Token slot u of a thread: position u*TT + tid of the tile (slot-major, the
-// tail's layout) or wave*TPT*64 + u*64 + lane (wave-major, the fused scan's:
-// a wave owns 2048 consecutive positions).  cnt_idx orders the per-(u, wave)
-// counts by position.
+// tail's layout) or wave*SP*64 + u*64 + lane (wave-major, the fused scans':
+// a wave owns SP*64 consecutive positions, SP = the slots in use).  cnt_idx
+// orders the per-(u, wave) counts by position.
 template <bool WM>
 __device__ __forceinline__ int cnt_idx(int u, int wave) { return WM ? wave * TPT + u : u * TW + wave; }
-template <bool WM>
-__device__ __forceinline__ int slot_pos(int u, int tid) { return WM ? (tid >> 6) * (TPT * 64) + u * 64 + (tid & 63) : u * TT + tid; }
+template <bool WM, int SP = TPT>
+__device__ __forceinline__ int slot_pos(int u, int tid) { return WM ? (tid >> 6) * (SP * 64) + u * 64 + (tid & 63) : u * TT + tid; }
 
 // Count the flagged tokens per (u, wave) in S.cnt (not yet scanned).
 template <bool WM>
@@ -768,14 +768,72 @@ __global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
 
 // Selection only: a_i of every token (written to agg), the threshold and the
 // top-k tie quota of every retrieval head (written to its state), in one
-// launch; the per-stage attention and merge follow.
+// launch; the attention and merge follow.  With p.row_list set (the attention
+// balanced by kept rows follows), the tiles of a head also exchange their
+// kept counts (each tile publishes before it waits, so no cycle forms) and
+// every tile writes its kept rows, (position, page) in position order, at its
+// offset in the head's list; the head's last tile writes the head's total,
+// and top-p sets are counted here.
 template <int G>
 __global__ __launch_bounds__(TT) void select_single_kernel(DecodeParams p) {
   __shared__ TailLds S;
   Tile tl[MAXT];
   unsigned int keepm[MAXT];
   int my_tiles = 0;
-  if (blockIdx.x < p.tail_ntiles) select_tiles<G>(p, S, tl, keepm, my_tiles, p.tail_sync);
+  if (blockIdx.x >= p.tail_ntiles) return;
+  unsigned int* err = p.tail_sync;
+  select_tiles<G>(p, S, tl, keepm, my_tiles, err);
+  if (p.row_list == nullptr) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // ---- publish every tile's kept count, then arrive ----
+#pragma unroll
+  for (int k = 0; k < MAXT; ++k) {
+    if (tl[k].t < 0) continue;                        // uniform
+    unsigned int c = (unsigned int)__popc(keepm[k]);
+    for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off);
+    __syncthreads();
+    if (lane == 0) S.tmp[wave] = c;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned int tot = 0u;
+      for (int w2 = 0; w2 < TW; ++w2) tot += S.tmp[w2];
+      __hip_atomic_store(&p.tile_cnt[tl[k].t], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  wait_memory_ops();
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k)
+      if (tl[k].t >= 0) atomicAdd(&p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].cnt_arrive, 1u);
+  }
+  // ---- each tile: its offset in the head's list, then its rows ----
+#pragma unroll
+  for (int k = 0; k < MAXT; ++k) {
+    if (tl[k].t < 0) continue;
+    SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
+    block_wait(p, &st->cnt_arrive, (unsigned int)p.tail_tph, err);
+    if (tid == 0) {
+      unsigned int before = 0u;
+      const int t0 = tl[k].t - tl[k].j;
+      for (int jj = 0; jj < tl[k].j; ++jj) before += load_u32_coherent(&p.tile_cnt[t0 + jj]);
+      S.tmp[TW] = before;
+    }
+    __syncthreads();
+    const unsigned int off = S.tmp[TW];
+    const int nrows = compact_rows<false>(S, keepm[k]);
+    __syncthreads();
+    int2* dst = p.row_list + ((size_t)tl[k].b * p.nR + tl[k].hr) * p.Nmax + off;
+    for (int r = tid; r < nrows; r += TT) {
+      const int o16 = S.u.rows[r];
+      dst[r] = make_int2(tl[k].lo + o16, S.pages[k][o16 >> 4]);
+    }
+    if (tid == 0) {
+      if (tl[k].j == p.tail_tph - 1) p.pair_rows[(size_t)tl[k].b * p.nR + tl[k].hr] = (int)off + nrows;
+      if (p.select_mode == 0 && nrows > 0) atomicAdd(&st->nsel, (unsigned int)nrows);
+    }
+    __syncthreads();                                  // S.u and S.tmp are reused by the next tile
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -891,6 +949,7 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
     }
   }
 
+  stamp_phase(p, 1);
   // ---- log-sum-exp of the head: this tile's partial, exchanged between tiles ----
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -938,6 +997,7 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
 #pragma unroll
   for (int g = 0; g < G; ++g) lse[g] = S.lse[0][g];
   if (j == 0 && tid < G) st->lse2[tid] = S.lse[0][tid];
+  stamp_phase(p, 2);
 
   // ---- a_i = mean_g 2^(x_gi - LSE2_g) ----
   float av[1][TPT];
@@ -959,13 +1019,18 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
 
   // ---- radix passes (the arrival counter already holds the exchange) ----
   const unsigned int base = (unsigned int)p.tail_tph;
+  stamp_phase(p, 3);
   radix_pass<1, 1>(p, S, tl, av, ts, bymass, err, base);
+  stamp_phase(p, 4);
   radix_pass<2, 1>(p, S, tl, av, ts, bymass, err, base);
+  stamp_phase(p, 5);
   radix_pass<3, 1>(p, S, tl, av, ts, bymass, err, base);
+  stamp_phase(p, 6);
   unsigned int keepm[1];
   tie_keep<1, true>(p, S, tl, av, ts, keepm, err);
   const unsigned int keep = keepm[0];
   if (p.sel_mass != nullptr) add_kept_mass(&st->kept_mass, av[0], keep);
+  stamp_phase(p, 7);
 
   // ---- ordered compaction; the kept tokens' scores (the attention's logits)
   // go to LDS next to the row list, or to the scores buffer if too many ----
@@ -1002,12 +1067,15 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   if (!lds) wait_memory_ops();
   if (tid == 0 && nrows > 0) atomicAdd(&st->nsel, (unsigned int)nrows);
   __syncthreads();
+  stamp_phase(p, 8);
   if (nrows > 0)
     attend_rows<G, false, MODE, FUSED_RB, true>(p, S, b, h, hr, j, lo, nrows, S.pages[0],
                                                 lds ? reinterpret_cast<const float*>(logits) : nullptr);
   else
     empty_split<G>(p, b, h, j);
+  stamp_phase(p, 9);
   finish_split<G>(p, S, b, h, hr);
+  stamp_phase(p, 10);
 }
 
 template <int MODE>
@@ -1016,6 +1084,7 @@ __global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
   __shared__ f32x4 logits[FUSED_LOGITS];
   const int w = blockIdx.x, nwg = gridDim.x;
   unsigned int* err = p.tail_sync;
+  stamp_phase(p, 0);
   if (w < p.tail_ntiles) fused_tile<MODE>(p, S, logits, err);
   if constexpr (MODE != 1) {
     // local-head chunks: item i goes to workgroup (ntiles + i) mod nwg
@@ -1031,6 +1100,352 @@ __global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
       finish_split<4>(p, S, b, h, -1);
     }
   }
+  stamp_phase(p, 11);
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode with r = 16 index scores ([RTPurbo] Methodology §2: the index
+// scan streams 64 B (fp32) or 32 B (bf16) per token and retrieval head): the
+// scan runs inside the launch, one tile of TT * SP tokens per workgroup, and
+// the tile's scores stay in registers.  Wave w scans the tile's pages
+// w*4*SP .. w*4*SP + 4*SP - 1, four pages per slot u.  fp32 index: a page
+// (16 tokens x 16 dims, 1 KiB) is one wave load, lane l holding four dims of
+// token l % 16 -- 16-lane group j holds dims 4*s(j) .. +3 with s = (0, 2, 1, 3)
+// -- and the four pages' partial dot products are summed over the groups by
+// one x32 and one x16 lane swap, which leave lane l with the scores of token
+// l of the slot's 64 positions; the additions pair the same terms as the
+// per-stage scan (dims 0-3 with 4-7, 8-11 with 12-15, then the two halves),
+// so both give the same scores.  bf16 index: one wave load covers two 512 B
+// pages (lanes 0-31 and 32-63), a lane holding eight dims, and the x16 swap
+// alone completes the sums.  Then, as in the full-dim fused launch: the
+// log-sum-exp exchange between the tiles of the head, a_i, the radix passes,
+// ties, the ordered compaction, and the gathered attention over the kept
+// rows (K and V rows, logits from q.k) with the last split merging.
+// ---------------------------------------------------------------------------
+template <int G, bool FP8, int SP>
+__device__ __forceinline__ void fused_index_tile(const DecodeParams& p, TailLds& S, unsigned int* err) {
+  static_assert(SP <= TPT && SP % 4 == 0 && 4 * SP <= 64, "slots in use; a page id per lane");
+  constexpr int FPW_I = 4 * SP;                          // pages per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, slot = lane & 15;
+  const bool bymass = p.select_mode == 0;
+  const bool bf16 = p.index_bf16 != 0;
+  Tile tl[1];
+  TileSel ts[1];
+  {
+    const int t = blockIdx.x, head = t / p.tail_tph;
+    tl[0].t = t;
+    tl[0].j = t % p.tail_tph;
+    tl[0].b = head / p.nR;
+    tl[0].hr = head % p.nR;
+    tl[0].N = min(p.seq_lens[tl[0].b], p.Nmax);
+    tl[0].lo = tl[0].j * (TT * SP);
+    tl[0].hi = min(tl[0].N, tl[0].lo + TT * SP);
+    ts[0] = TileSel{false, 0u, 0ull, 0u, false, 0u, 0ull};
+    bool all;
+    ts[0].target = sel_target(p, tl[0].b, tl[0].N, all);
+    ts[0].done = all;
+  }
+  const int b = tl[0].b, hr = tl[0].hr, j = tl[0].j, N = tl[0].N, lo = tl[0].lo, hi = tl[0].hi;
+  const int h = p.ret_head[hr];
+  const size_t hrow = (size_t)(b * p.nR + hr);
+  SelState* st = p.sel + hrow;
+
+  // ---- page ids of this wave (one per lane), then every index load of the
+  // first group of slots, before the projected queries are formed ----
+  const int* bt = p.block_tables + (size_t)b * p.max_blocks;
+  const int page0 = (lo >> 4) + wave * FPW_I;
+  const int my_blk = (lane < FPW_I && (page0 + lane) * BS < N) ? bt[page0 + lane] : -1;
+  if (lane < FPW_I) S.pages[0][wave * FPW_I + lane] = my_blk;
+  const int nslots = min(SP, max(0, (N - page0 * BS + 4 * BS - 1) / (4 * BS)));
+  const char* ipool = reinterpret_cast<const char*>(p.index_pool);
+  const size_t page_bytes = (size_t)BS * R * (bf16 ? 2 : 4);
+  // lane's byte offset in a page: fp32: token `slot`, dims 4*s(grp); bf16:
+  // token `slot`, dims 8*(grp & 1) of the half's page
+  const int sgrp = ((grp & 1) << 1) | (grp >> 1);       // s = (0, 2, 1, 3)
+  const int lane_off = bf16 ? slot * 32 + (grp & 1) * 16 : slot * 64 + sgrp * 16;
+  // the index load of page q (0..3) of slot u for this lane: fp32 every lane
+  // reads page q; bf16 lanes 0-31 read page q and lanes 32-63 page q + 2.
+  // Bit q (and q + 2) of `valid` records whether the page id is in range;
+  // an out-of-range page reads page 0 and its scores are zeroed.
+  auto load_page = [&](int u, int q, unsigned& valid) -> u32x4 {
+    const int pg = 4 * u + q;
+    const int blk_a = __builtin_amdgcn_readlane(my_blk, pg);
+    const int blk_b = __builtin_amdgcn_readlane(my_blk, bf16 ? pg + 2 : pg);
+    const bool ok_a = (unsigned)blk_a < (unsigned)p.num_blocks;
+    const bool ok_b = (unsigned)blk_b < (unsigned)p.num_blocks;
+    valid |= (ok_a ? 1u : 0u) << q;
+    if (bf16) valid |= (ok_b ? 1u : 0u) << (q + 2);
+    const bool upper = bf16 && lane >= 32;
+    const int blk = upper ? (ok_b ? blk_b : 0) : (ok_a ? blk_a : 0);
+    return load_nt16(ipool + ((size_t)blk * p.nR + hr) * page_bytes + lane_off);
+  };
+
+  // ---- projected queries q~ = P q, split like the per-stage scan's (the
+  // first 256 threads, the same partial sums), then this lane's dims ----
+  __shared__ float qt_s[MAX_G][R];
+  if (tid < 256) {
+    constexpr int TPD = 256 / (G * R);
+    constexpr int EPT = D / TPD;
+    const int dot = tid / TPD, part = tid % TPD;
+    const int g = dot / R, jj = dot % R;
+    const float4* prow = reinterpret_cast<const float4*>(p.proj + ((size_t)h * R + jj) * D + part * EPT);
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(p.q + ((size_t)b * p.Hq + h * G + g) * D + part * EPT);
+    float acc = 0.f;
+#pragma unroll
+    for (int e8 = 0; e8 < EPT / 8; ++e8) {
+      const u32x4 w = qrow[e8];
+      const float4 pa = prow[2 * e8], pb = prow[2 * e8 + 1];
+      acc = fmaf(pa.x, bf16_lo(w[0]), acc);
+      acc = fmaf(pa.y, bf16_hi(w[0]), acc);
+      acc = fmaf(pa.z, bf16_lo(w[1]), acc);
+      acc = fmaf(pa.w, bf16_hi(w[1]), acc);
+      acc = fmaf(pb.x, bf16_lo(w[2]), acc);
+      acc = fmaf(pb.y, bf16_hi(w[2]), acc);
+      acc = fmaf(pb.z, bf16_lo(w[3]), acc);
+      acc = fmaf(pb.w, bf16_hi(w[3]), acc);
+    }
+#pragma unroll
+    for (int off = 1; off < TPD; off <<= 1) acc += __shfl_xor(acc, off);
+    if (part == 0) qt_s[g][jj] = acc;
+  }
+  __syncthreads();
+  float qv[G][8];
+  {
+    const int d0 = bf16 ? 8 * (grp & 1) : 4 * sgrp;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[g][e] = (bf16 || e < 4) ? qt_s[g][min(d0 + e, R - 1)] : 0.f;
+  }
+
+  // ---- scan: x[u][g] = raw index score of this lane's token of slot u ----
+  const float c2 = p.c2_score;
+  float x[SP][G];
+  float m[G], sm[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { m[g] = NEG_INF; sm[g] = 0.f; }
+#pragma unroll
+  for (int u0 = 0; u0 < SP; u0 += 4) {
+    u32x4 kw[4][4];
+    unsigned valid[4];
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      valid[uu] = 0u;
+      if (u0 + uu < nslots) {                               // wave-uniform
+        if (bf16) {
+          kw[uu][0] = load_page(u0 + uu, 0, valid[uu]);
+          kw[uu][1] = load_page(u0 + uu, 1, valid[uu]);
+        } else {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) kw[uu][q4] = load_page(u0 + uu, q4, valid[uu]);
+        }
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const int u = u0 + uu;
+#pragma unroll
+      for (int g = 0; g < G; ++g) x[u][g] = 0.f;
+      if (u >= nslots) continue;                            // wave-uniform
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float v;
+        if (bf16) {
+          // X = pages 0 | 2 (the two halves), Y = pages 1 | 3
+          float part[2];
+#pragma unroll
+          for (int ld = 0; ld < 2; ++ld) {
+            const u32x4 w = kw[uu][ld];
+            float a = qv[g][0] * bf16_lo(w[0]);
+            a = fmaf(qv[g][1], bf16_hi(w[0]), a);
+            a = fmaf(qv[g][2], bf16_lo(w[1]), a);
+            a = fmaf(qv[g][3], bf16_hi(w[1]), a);
+            a = fmaf(qv[g][4], bf16_lo(w[2]), a);
+            a = fmaf(qv[g][5], bf16_hi(w[2]), a);
+            a = fmaf(qv[g][6], bf16_lo(w[3]), a);
+            a = fmaf(qv[g][7], bf16_hi(w[3]), a);
+            part[ld] = a;
+          }
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                           false, false);
+          v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        } else {
+          float part[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const u32x4 w = kw[uu][q4];
+            float a = qv[g][0] * __uint_as_float(w[0]);
+            a = fmaf(qv[g][1], __uint_as_float(w[1]), a);
+            a = fmaf(qv[g][2], __uint_as_float(w[2]), a);
+            a = fmaf(qv[g][3], __uint_as_float(w[3]), a);
+            part[q4] = a;
+          }
+          // pages (0, 2) and (1, 3) over the x32 pairs of groups, then the
+          // x16 pairs
+          const auto r02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]),
+                                                             false, false);
+          const auto r13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]),
+                                                             false, false);
+          const float a0 = __uint_as_float(r02[0]) + __uint_as_float(r02[1]);
+          const float a1 = __uint_as_float(r13[0]) + __uint_as_float(r13[1]);
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+          v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        x[u][g] = ((valid[uu] >> grp) & 1u) ? v : 0.f;      // an invalid page scores 0
+      }
+      if (lo + wave * (SP * 64) + u * 64 + lane < hi) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float z = x[u][g] * c2;
+          const float mn = fmaxf(m[g], z);
+          sm[g] = sm[g] * fast_exp2(m[g] - mn) + fast_exp2(z - mn);
+          m[g] = mn;
+        }
+      }
+    }
+  }
+
+  stamp_phase(p, 1);
+  // ---- log-sum-exp of the head: this tile's partial, exchanged between tiles ----
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    for (int off = 1; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m[g], off), s2 = __shfl_xor(sm[g], off);
+      lse_combine(m[g], sm[g], m2, s2);
+    }
+    if (lane == 0) { S.wm[wave][g] = m[g]; S.wl[wave][g] = sm[g]; }
+  }
+  __syncthreads();
+  {
+    constexpr int NBIN = HIST_BINS + P2_BINS + P3_BINS;
+    for (int e = j * TT + tid; e < NBIN; e += p.tail_tph * TT) {
+      unsigned long long* bin = e < HIST_BINS ? &st->mass[e]
+                              : (e < HIST_BINS + P2_BINS ? &st->mass2[e - HIST_BINS] : &st->mass3[e - HIST_BINS - P2_BINS]);
+      __hip_atomic_store(bin, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  float* spf = reinterpret_cast<float*>(p.spart) + hrow * p.n_score_chunks * G * 2;   // [tile][g] (max, sum)
+  if (tid < G) {
+    float mm = S.wm[0][tid], ss = S.wl[0][tid];
+    for (int w2 = 1; w2 < TW; ++w2) lse_combine(mm, ss, S.wm[w2][tid], S.wl[w2][tid]);
+    store_f32_coherent(spf + ((size_t)j * G + tid) * 2, mm);
+    store_f32_coherent(spf + ((size_t)j * G + tid) * 2 + 1, ss);
+  }
+  wait_memory_ops();
+  __syncthreads();
+  if (tid == 0) atomicAdd(&st->arrive, 1u);
+  block_wait(p, &st->arrive, (unsigned int)p.tail_tph, err);
+  if (wave < G) {
+    float mm = NEG_INF, ss = 0.f;
+    for (int jj = lane; jj < p.tail_tph; jj += 64)
+      lse_combine(mm, ss, load_f32_coherent(spf + ((size_t)jj * G + wave) * 2),
+                  load_f32_coherent(spf + ((size_t)jj * G + wave) * 2 + 1));
+    for (int off = 1; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(mm, off), s2 = __shfl_xor(ss, off);
+      lse_combine(mm, ss, m2, s2);
+    }
+    if (lane == 0) S.lse[0][wave] = mm + log2f(ss);
+  }
+  __syncthreads();
+  float lse[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) lse[g] = S.lse[0][g];
+  if (j == 0 && tid < G) st->lse2[tid] = S.lse[0][tid];
+  stamp_phase(p, 2);
+
+  // ---- a_i = mean_g 2^(x_gi - LSE2_g); slots past SP hold no token ----
+  float av[1][TPT];
+  float* agg = p.sel_idx != nullptr ? p.agg + hrow * p.Nagg : nullptr;
+  float* sc = p.scores + hrow * p.Nmax * G;
+  const float invG = 1.0f / (float)G;
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    if (u >= SP) { av[0][u] = -1.0f; continue; }
+    const int i = lo + wave * (SP * 64) + u * 64 + lane;
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) a += fast_exp2(x[u < SP ? u : 0][g] * c2 - lse[g]);
+    a *= invG;
+    av[0][u] = i < hi ? a : -1.0f;
+    if (i < hi) {
+      if (agg != nullptr) agg[i] = a;
+      if (p.scores_out) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[(size_t)i * G + g] = x[u < SP ? u : 0][g];
+      }
+    }
+  }
+
+  // ---- radix passes (the arrival counter already holds the exchange) ----
+  const unsigned int base = (unsigned int)p.tail_tph;
+  stamp_phase(p, 3);
+  radix_pass<1, 1>(p, S, tl, av, ts, bymass, err, base);
+  stamp_phase(p, 4);
+  radix_pass<2, 1>(p, S, tl, av, ts, bymass, err, base);
+  stamp_phase(p, 5);
+  radix_pass<3, 1>(p, S, tl, av, ts, bymass, err, base);
+  stamp_phase(p, 6);
+  unsigned int keepm[1];
+  tie_keep<1, true>(p, S, tl, av, ts, keepm, err);
+  const unsigned int keep = keepm[0];
+  if (p.sel_mass != nullptr) add_kept_mass(&st->kept_mass, av[0], keep);
+  stamp_phase(p, 7);
+
+  // ---- ordered compaction: a wave's kept tokens after those of the waves
+  // before it, in (u, lane) order ----
+  unsigned int wcount = 0u;
+#pragma unroll
+  for (int u = 0; u < SP; ++u) wcount += (unsigned int)__popcll(__ballot((keep >> u) & 1u));
+  if (lane == 0) S.tmp[wave] = wcount;
+  __syncthreads();
+  unsigned int run = 0u, total = 0u;
+#pragma unroll
+  for (int w2 = 0; w2 < TW; ++w2) {
+    const unsigned int c = S.tmp[w2];
+    run += w2 < wave ? c : 0u;
+    total += c;
+  }
+  const int nrows = (int)total;
+#pragma unroll
+  for (int u = 0; u < SP; ++u) {
+    const unsigned long long bal = __ballot((keep >> u) & 1u);
+    const unsigned int slot0 = run;
+    run += (unsigned int)__popcll(bal);
+    if ((keep >> u) & 1u) S.u.rows[slot0 + lane_rank(bal)] = (unsigned short)slot_pos<true, SP>(u, tid);
+  }
+  if (tid == 0 && nrows > 0) atomicAdd(&st->nsel, (unsigned int)nrows);
+  __syncthreads();
+  stamp_phase(p, 8);
+  if (nrows > 0)
+    attend_rows<G, FP8, 0>(p, S, b, h, hr, j, lo, nrows, S.pages[0]);
+  else
+    empty_split<G>(p, b, h, j);
+  stamp_phase(p, 9);
+  finish_split<G>(p, S, b, h, hr);
+  stamp_phase(p, 10);
+}
+
+template <int G, bool FP8, int SP>
+__global__ __launch_bounds__(TT) void fused_index_kernel(DecodeParams p) {
+  __shared__ TailLds S;
+  const int w = blockIdx.x, nwg = gridDim.x;
+  unsigned int* err = p.tail_sync;
+  stamp_phase(p, 0);
+  if (w < p.tail_ntiles) fused_index_tile<G, FP8, SP>(p, S, err);
+  // local-head chunks: item i goes to workgroup (ntiles + i) mod nwg
+  const int nitems = p.B * p.nL * p.ncL;
+  const int first_item = ((w - p.tail_ntiles) % nwg + nwg) % nwg;
+  for (int it = first_item; it < nitems; it += nwg) {
+    int b, h, c;
+    __syncthreads();
+    const int nrows = local_rows(p, S, it, b, h, c);
+    __syncthreads();
+    if (nrows > 0) attend_rows<G, FP8, 0>(p, S, b, h, -1, c, 0, nrows, nullptr);
+    else empty_split<G>(p, b, h, c);
+    finish_split<G>(p, S, b, h, -1);
+  }
+  stamp_phase(p, 11);
 }
 
 // Counters back to zero before a fused launch (the radix bins are cleared by
@@ -1069,14 +1484,30 @@ void* pick_kernel(const DecodeParams& p, bool select_only) {
   return nullptr;
 }
 
+template <int G, bool FP8>
+void* pick_index_sp(int sp) {
+  switch (sp) {
+    case 4: return reinterpret_cast<void*>(&fused_index_kernel<G, FP8, 4>);
+    // (G = 8 with 16 slots would spill: only the 2048-position tiles)
+    case 16: return G == 8 ? nullptr : reinterpret_cast<void*>(&fused_index_kernel<G, FP8, G == 8 ? 4 : 16>);
+  }
+  return nullptr;
+}
+
+template <int G>
+void* pick_index_g(const DecodeParams& p, int sp) {
+  return p.kv_scales != nullptr ? pick_index_sp<G, true>(sp) : pick_index_sp<G, false>(sp);
+}
+
 }  // namespace
 
-int tail_grid(const DecodeParams& p, bool cooperative, bool select_only) {
-  void* fn = pick_kernel(p, select_only);
+// Workgroups of `fn` (TT threads each) that the current device holds at once,
+// looked up once per (kernel, device); 0 when `cooperative` and the device
+// has no cooperative launches.
+static int resident_grid(void* fn, bool cooperative) {
   if (fn == nullptr) return 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  // (kernel, device) -> workgroups resident at once, computed once
   struct Entry { void* fn; int dev; int nwg; int coop; };
   static std::mutex mu;
   static std::vector<Entry> cache;
@@ -1095,6 +1526,10 @@ int tail_grid(const DecodeParams& p, bool cooperative, bool select_only) {
     hit = &cache.back();
   }
   return (cooperative && hit->coop == 0) ? 0 : hit->nwg;
+}
+
+int tail_grid(const DecodeParams& p, bool cooperative, bool select_only) {
+  return resident_grid(pick_kernel(p, select_only), cooperative);
 }
 
 void* pick_fused(const DecodeParams& p) {
@@ -1102,29 +1537,21 @@ void* pick_fused(const DecodeParams& p) {
   return p.nL == 0 ? reinterpret_cast<void*>(&fused_g4_kernel<1>) : reinterpret_cast<void*>(&fused_g4_kernel<2>);
 }
 
-int fused_grid(const DecodeParams& p, bool cooperative) {
-  void* fn = pick_fused(p);
-  if (fn == nullptr) return 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  struct Entry { void* fn; int dev; int nwg; int coop; };
-  static std::mutex mu;
-  static std::vector<Entry> cache;
-  std::lock_guard<std::mutex> lock(mu);
-  const Entry* hit = nullptr;
-  for (const Entry& e : cache)
-    if (e.fn == fn && e.dev == dev) hit = &e;
-  if (hit == nullptr) {
-    int ncu = 0, occ = 0, coop = 0;
-    int nwg = 0;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(fn), TT, 0) == hipSuccess)
-      nwg = ncu * occ;
-    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
-    cache.push_back(Entry{fn, dev, nwg, coop});
-    hit = &cache.back();
+int fused_grid(const DecodeParams& p, bool cooperative) { return resident_grid(pick_fused(p), cooperative); }
+
+void* pick_fused_index(const DecodeParams& p, int sp) {
+  if (p.score_mode != 0 || p.GS != 1) return nullptr;
+  switch (p.G) {
+    case 1: return pick_index_g<1>(p, sp);
+    case 2: return pick_index_g<2>(p, sp);
+    case 4: return pick_index_g<4>(p, sp);
+    case 8: return pick_index_g<8>(p, sp);
   }
-  return (cooperative && hit->coop == 0) ? 0 : hit->nwg;
+  return nullptr;
+}
+
+int fused_index_grid(const DecodeParams& p, int sp, bool cooperative) {
+  return resident_grid(pick_fused_index(p, sp), cooperative);
 }
 
 // Launch `fn` on nwg workgroups; e0 / e1 (optional) time the dispatch itself.
@@ -1147,6 +1574,16 @@ hipError_t launch_single(void* fn, const DecodeParams& p, int nwg, bool cooperat
 hipError_t launch_fused(const DecodeParams& p, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
                         hipEvent_t e1) {
   void* fn = pick_fused(p);
+  if (fn == nullptr || nwg < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reset_state_kernel, dim3(1), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_single(fn, p, nwg, cooperative, s, e0, e1);
+}
+
+hipError_t launch_fused_index(const DecodeParams& p, int sp, int nwg, bool cooperative, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1) {
+  void* fn = pick_fused_index(p, sp);
   if (fn == nullptr || nwg < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reset_state_kernel, dim3(1), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();

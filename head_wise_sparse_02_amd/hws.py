@@ -29,6 +29,7 @@ HWS_SCORE_INDEX, HWS_SCORE_FULL = 0, 1
 HWS_SCOPE_KV_HEAD, HWS_SCOPE_QUERY_HEAD = 0, 1
 HWS_INDEX_F32, HWS_INDEX_BF16 = 0, 1
 HWS_LAUNCH_AUTO, HWS_LAUNCH_MULTI, HWS_LAUNCH_COOPERATIVE, HWS_LAUNCH_SINGLE = 0, 1, 2, 3
+HWS_LAUNCH_SCAN_SELECT, HWS_LAUNCH_SCAN_SINGLE = 4, 5
 HWS_STEP_OK, HWS_STEP_WAIT_TIMEOUT = 0, 1
 
 EXPORTED = (
@@ -37,8 +38,9 @@ EXPORTED = (
     "hws_workspace_size", "hws_append", "hws_decode", "hws_profile_enable",
     "hws_profile_read", "hws_profile_stage_name", "hws_set_launch_mode",
     "hws_effective_rank_workspace", "hws_effective_rank", "hws_prefill", "hws_set_wait_limit",
-    "hws_decode_noalloc",
+    "hws_decode_noalloc", "hws_profile_phases", "hws_dense_lse_workspace", "hws_dense_lse",
 )
+HWS_PHASES = 12
 HWS_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -118,6 +120,9 @@ def lib() -> ctypes.CDLL:
         "hws_effective_rank": (i32, [i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "hws_profile_read": (i32, [vp, P(ctypes.c_double), P(i32), i32]),
         "hws_profile_stage_name": (ctypes.c_char_p, [i32]),
+        "hws_profile_phases": (i32, [vp, vp, i32]),
+        "hws_dense_lse_workspace": (i32, [vp, i32, i32, P(ctypes.c_size_t)]),
+        "hws_dense_lse": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -252,6 +257,21 @@ class Context:
         kw.setdefault("workspace", None)
         self.decode(noalloc=True, **kw)
 
+    def dense_lse_workspace(self, batch: int, max_seq_len: int) -> int:
+        n = ctypes.c_size_t()
+        self._check(self._L.hws_dense_lse_workspace(self.handle, batch, max_seq_len, ctypes.byref(n)),
+                    "hws_dense_lse_workspace")
+        return n.value
+
+    def dense_lse(self, *, q, block_tables, seq_lens, max_seq_len: int, lse_full, workspace, stream=None):
+        """ln sum_i exp(attn_scale q.k_i) over every cached row, per query head:
+        q [B, Hq, 128] bf16, lse_full [B, Hq] fp32 (device tensors)."""
+        nbytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+        batch = int(q.shape[0]) if q is not None else 0
+        self._check(self._L.hws_dense_lse(self.handle, batch, int(max_seq_len), _ptr(q),
+                                          _ptr(block_tables), _ptr(seq_lens), _ptr(lse_full), _ptr(workspace),
+                                          nbytes, _stream(stream)), "hws_dense_lse")
+
     def prefill(self, *, q, block_tables, start_pos, out, lse=None, dense: bool = False, stream=None,
                 seq_slots=None):
         """Chunked prefill attention: q [n_seq, n_tok, Hq, 128] bf16 of the positions
@@ -271,8 +291,10 @@ class Context:
     def set_launch_mode(self, mode: int):
         """HWS_LAUNCH_AUTO (default), HWS_LAUNCH_SINGLE (one launch after or
         with the scoring scan, grid sized to the device), HWS_LAUNCH_COOPERATIVE
-        (the same as a cooperative launch) or HWS_LAUNCH_MULTI (one kernel per
-        stage)."""
+        (the same as a cooperative launch), HWS_LAUNCH_MULTI (one kernel per
+        stage), HWS_LAUNCH_SCAN_SINGLE (the scan, then the single launch) or
+        HWS_LAUNCH_SCAN_SELECT (the scan, the selection as one launch, then the
+        per-stage attention and merge)."""
         self._check(self._L.hws_set_launch_mode(self.handle, int(mode)), "hws_set_launch_mode")
 
     def set_wait_limit(self, max_polls: int = 0, unreachable: bool = False):
@@ -284,6 +306,12 @@ class Context:
 
     def profile_enable(self, enable: bool = True):
         self._check(self._L.hws_profile_enable(self.handle, int(enable)), "hws_profile_enable")
+
+    def profile_phases(self, buf=None, max_workgroups: int = 0):
+        """Phase timestamps of later single-launch decodes into ``buf`` (a device
+        int64 tensor of max_workgroups * HWS_PHASES entries), or off (None)."""
+        self._check(self._L.hws_profile_phases(self.handle, _ptr(buf), int(max_workgroups)),
+                    "hws_profile_phases")
 
     def profile_read(self) -> dict:
         n = 16

@@ -170,6 +170,15 @@ class DecodeSetup:
         self.sel_mass = torch.empty((B, Hq if self.scope else Hkv), dtype=torch.float32, device=self.dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=self.dev)
 
+    def dense_lse(self, stream=None) -> np.ndarray:
+        """ln sum_i exp(attn_scale q.k_i) over every cached row, [B, Hq] (host)."""
+        ws = torch.empty(self.ctx.dense_lse_workspace(self.wl.B, self.Nmax), dtype=torch.uint8, device=self.dev)
+        out = torch.empty((self.wl.B, self.wl.Hq), dtype=torch.float32, device=self.dev)
+        self.ctx.dense_lse(q=self.q, block_tables=self.block_tables, seq_lens=self.seq_lens, max_seq_len=self.Nmax,
+                           lse_full=out, workspace=ws, stream=stream)
+        torch.cuda.synchronize(self.dev)
+        return out.cpu().numpy()
+
     def prefill(self, q, start_pos, *, dense: bool = False, stream=None):
         """Prefill attention of the chunk q [B, n_tok, Hq, d] (bf16 device tensor)
         at positions start_pos[b].. (int32 device tensor); the cache already holds

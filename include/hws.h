@@ -83,7 +83,8 @@ enum { HWS_INDEX_F32 = 0, HWS_INDEX_BF16 = 1 };
 /* Selection scope: one set per KV head shared by its query heads, or one set
  * per query head ([ICS] §2: sparsity differs per token, query and head). */
 enum { HWS_SCOPE_KV_HEAD = 0, HWS_SCOPE_QUERY_HEAD = 1 };
-enum { HWS_LAUNCH_AUTO = 0, HWS_LAUNCH_MULTI = 1, HWS_LAUNCH_COOPERATIVE = 2, HWS_LAUNCH_SINGLE = 3 };
+enum { HWS_LAUNCH_AUTO = 0, HWS_LAUNCH_MULTI = 1, HWS_LAUNCH_COOPERATIVE = 2, HWS_LAUNCH_SINGLE = 3,
+       HWS_LAUNCH_SCAN_SELECT = 4, HWS_LAUNCH_SCAN_SINGLE = 5 };
 
 typedef struct hws_ctx hws_ctx; /* opaque host object, owned by the library */
 
@@ -312,6 +313,22 @@ hws_status hws_decode_noalloc(hws_ctx* ctx, const hws_decode_args* args, void* s
  * codes, widened exactly to bf16, by the page's K scale; it runs in the
  * per-stage kernels, as HWS_LAUNCH_MULTI or AUTO's one-launch selection.) */
 
+/* Dense log-sum-exp of every query head over its whole cache: a diagnostic
+ * beside the decode step, not part of it.  lse_full[b][g] = ln sum_{i < N_b}
+ * exp(attn_scale q_g . k_i) over every cached row of sequence b (rotated q
+ * and k when rope_theta > 0; fp8 rows as stored, code times page scale), for
+ * every query head, retrieval and local.  With the decode's lse over the
+ * kept set S, exp(lse - lse_full) is the full-dim attention mass that S
+ * keeps ([RTPurbo] Main results: retained attention mass; the index mass is
+ * hws_decode_args.sel_mass).  q: [B][Hq][128] bf16, block_tables, seq_lens
+ * as for hws_decode; lse_full: [B][Hq] fp32 (device); workspace:
+ * hws_dense_lse_workspace() bytes.  HWS_ERR_UNSUPPORTED with a local ring
+ * that has local heads (their older rows are gone). */
+hws_status hws_dense_lse_workspace(const hws_ctx* ctx, int32_t batch, int32_t max_seq_len, size_t* bytes);
+hws_status hws_dense_lse(hws_ctx* ctx, int32_t batch, int32_t max_seq_len, const void* q,
+                         const int32_t* block_tables, const int32_t* seq_lens, float* lse_full, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* One chunked-prefill attention call ([RTPurbo] Methodology §1: during
  * prefill a retrieval head keeps its whole cache while a local head attends
  * to its sinks and window; [AoH] Methodology §4: this fits chunked prefill).
@@ -349,9 +366,21 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  *    merge); no workgroup waits for another.
  *  HWS_LAUNCH_SINGLE: everything after the scoring scan runs as ONE launch
  *    whose workgroups hand results to each other through device memory and
- *    wait for each other (bounded spins); for full-dim scores with G = 4, a
- *    bf16 cache and RoPE off, the scan itself runs inside it too, one
- *    16384-position tile per workgroup with the tile's scores in registers.
+ *    wait for each other (bounded spins); the scan itself runs inside it too,
+ *    with each tile's scores in registers, for full-dim scores with G = 4, a
+ *    bf16 cache and RoPE off (one 16384-position tile per workgroup) and for
+ *    r = 16 index scores with one set per KV head (tiles of 2048 positions,
+ *    or 8192 when that needs fewer workgroups than the device holds; G = 8
+ *    takes 2048 only).
+ *  HWS_LAUNCH_SCAN_SINGLE: the scoring scan as its own kernel, then the rest
+ *    as the single launch (the shape HWS_LAUNCH_SINGLE falls back to).
+ *  HWS_LAUNCH_SCAN_SELECT: the scoring scan, then the selection alone as one
+ *    launch of the single-launch kind, then the attention and merge: with
+ *    index scores the attention balanced by kept rows (the selection writes
+ *    each tile's kept positions; every head's rows, kept or sinks + window,
+ *    are cut into items of about the same size, at most 2048 items plus one
+ *    per (sequence, KV head), for up to 2048 such pairs), else the per-stage
+ *    attention.
  *    The grid is sized to what the device holds at once (compute units x
  *    occupancy) and launched as an ordinary dispatch: it relies on this
  *    process having the device's compute units (no CU masking); a kernel
@@ -364,11 +393,11 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  *    runtime guarantees that all workgroups are resident (costs a few tens of
  *    microseconds of launch latency per call).
  *  HWS_LAUNCH_AUTO (the default): HWS_LAUNCH_SINGLE where the scan runs
- *    inside the launch (it is then faster) or where max_seq_len <= 4096
- *    (short contexts, where launch latency dominates); otherwise the scoring kernel,
- *    then the selection as ONE launch of the single-launch kind (same waits
- *    and time-out; one set per KV head, when its tiles fit the device), then
- *    the per-stage attention and merge; otherwise HWS_LAUNCH_MULTI.  (The
+ *    inside the launch (full-dim scores; index scores with G <= 4) or where
+ *    max_seq_len <= 4096 (short contexts, where launch latency dominates);
+ *    otherwise the scoring scan, the one-launch selection (same waits and
+ *    time-out; one set per KV head, when its tiles fit the device), the
+ *    per-stage attention and merge; otherwise HWS_LAUNCH_MULTI.  (The
  *    single launch without the scan gathers each tile's kept rows in one
  *    workgroup, which loses to the per-stage attention when many rows are
  *    kept or many local-head chunks run beside it.)
@@ -400,11 +429,24 @@ hws_status hws_set_wait_limit(hws_ctx* ctx, uint32_t max_polls, int32_t unreacha
  * of timed calls to calls[i] for i < n, then clears the record.  The stage
  * names come from hws_profile_stage_name(i) ("" past the last stage):
  * score, select, attend, merge, tail (the single launch that replaces
- * select, attend and merge) and fused (the single launch that also does the
- * scoring scan). */
+ * select, attend and merge), fused (the single launch that also does the
+ * full-dim scoring scan) and fused_index (the one that also does the r = 16
+ * index scan). */
 hws_status hws_profile_enable(hws_ctx* ctx, int32_t enable);
 hws_status hws_profile_read(hws_ctx* ctx, double* ms, int32_t* calls, int32_t n);
 const char* hws_profile_stage_name(int32_t i);
+
+/* Optional phase timestamps of the single launches (a profiling aid, off by
+ * default): with buf != NULL, thread 0 of workgroup w of every later
+ * single-launch decode on ctx writes the device's constant 100 MHz clock
+ * (s_memrealtime) at the end of phase k to buf[w * HWS_PHASES + k] (device
+ * memory, uint64, max_workgroups * HWS_PHASES entries; workgroups beyond
+ * max_workgroups write nothing; a phase a workgroup does not run stays as the
+ * caller left it).  Phases: 0 start, 1 scan, 2 log-sum-exp exchange, 3 a_i,
+ * 4-6 radix passes 1-3, 7 ties, 8 compaction, 9 attention, 10 merge,
+ * 11 local-head chunks.  buf = NULL turns it off. */
+#define HWS_PHASES 12
+hws_status hws_profile_phases(hws_ctx* ctx, uint64_t* buf, int32_t max_workgroups);
 
 #ifdef __cplusplus
 }

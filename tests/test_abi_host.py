@@ -167,15 +167,18 @@ def test_launch_mode_values():
     c.set_launch_mode(hws.HWS_LAUNCH_MULTI)
     c.set_launch_mode(hws.HWS_LAUNCH_COOPERATIVE)
     c.set_launch_mode(hws.HWS_LAUNCH_SINGLE)
+    c.set_launch_mode(hws.HWS_LAUNCH_SCAN_SELECT)
+    c.set_launch_mode(hws.HWS_LAUNCH_SCAN_SINGLE)
     c.set_launch_mode(hws.HWS_LAUNCH_AUTO)
-    for bad in (-1, 4, 99):
+    for bad in (-1, 6, 99):
         with pytest.raises(hws.HwsError) as e:
             c.set_launch_mode(bad)
         assert e.value.status == hws.HWS_ERR_INVALID_ARG
     assert hws.lib().hws_profile_stage_name(4) == b"tail"
     assert hws.lib().hws_profile_stage_name(5) == b"fused"
     assert hws.lib().hws_profile_stage_name(6) == b"prefill"
-    assert hws.lib().hws_profile_stage_name(7) == b""
+    assert hws.lib().hws_profile_stage_name(7) == b"fused_index"
+    assert hws.lib().hws_profile_stage_name(8) == b""
 
 
 def test_wait_limit_values():
@@ -268,7 +271,7 @@ def test_workspace_size_rules():
     assert n1 >= 500 * 4 * 4 + 500 * 4
     # one set per query head: G aggregates and G selection states per retrieval head
     nq = c.workspace_size(1, 500, 0, hws.HWS_SCOPE_QUERY_HEAD)
-    assert nq >= n1 + 3 * 500 * 4
+    assert nq >= 500 * 4 * 4 + 4 * 500 * 4
     with pytest.raises(hws.HwsError) as e:
         c.workspace_size(1, 500, 0, 7)
     assert e.value.status == hws.HWS_ERR_INVALID_ARG
@@ -368,3 +371,28 @@ def test_decode_noalloc_validation_without_gpu():
             _decode(c, workspace=None, noalloc=True, **kw)
         assert e.value.status == status, (kw, e.value)
         assert b"hws_decode_noalloc" in str(e.value).encode() and hws.lib().hws_last_error(c.handle)
+
+
+def test_dense_lse_validation_without_gpu():
+    c = _ctx()
+    ws = _FakeT(nbytes=1 << 30)
+    call = dict(q=_FakeT((1, 8, 128)), block_tables=_FakeT(), seq_lens=_FakeT(), max_seq_len=100,
+                lse_full=_FakeT(), workspace=ws, stream=0)
+    with pytest.raises(hws.HwsError) as e:
+        c.dense_lse(**call)
+    assert e.value.status == hws.HWS_ERR_STATE          # before bind
+    c.set_head_kinds([1, 0])
+    c.bind(4096, 4096, None, 4096, 4096)
+    assert 0 < c.dense_lse_workspace(1, 100) < c.dense_lse_workspace(8, 512)
+    for kw, status in [(dict(max_seq_len=32 * 16 + 1), hws.HWS_ERR_CAPACITY), (dict(lse_full=None), hws.HWS_ERR_INVALID_ARG),
+                       (dict(workspace=_FakeT(nbytes=8)), hws.HWS_ERR_WORKSPACE),
+                       (dict(q=None), hws.HWS_ERR_INVALID_ARG)]:
+        with pytest.raises(hws.HwsError) as e:
+            c.dense_lse(**{**call, **kw})
+        assert e.value.status == status, (kw, e.value)
+    r = _ctx(ring=True, max_seqs=2)
+    r.set_head_kinds([1, 0])
+    r.bind(4096, 4096, None, 4096, 4096, 4096, 4096)
+    with pytest.raises(hws.HwsError) as e:
+        r.dense_lse(**call)
+    assert e.value.status == hws.HWS_ERR_UNSUPPORTED

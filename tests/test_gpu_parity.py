@@ -206,59 +206,76 @@ def test_rope_on(score_mode, launch):
 @pytest.mark.parametrize("cfg,kw", [(3, dict(n=40000, batch=4)), (2, dict(n=33000, batch=3)),
                                     (5, dict(n=30000, batch=8))])
 def test_single_launch_matches_multi(cfg, kw):
-    """Same token sets from both launch shapes; outputs equal up to the fp32
-    rounding order of the attention splits.  The single launch is the one
-    that ran (its profile stage is recorded)."""
+    """Same token sets from every launch shape; outputs equal up to the fp32
+    rounding order of the attention splits.  AUTO and SINGLE run the single
+    launch with the scan inside (full-dim G = 4: fused; index scores:
+    fused_index), which the recorded profile stages confirm; COOPERATIVE is
+    the same kernel and grid, bit for bit; SCAN_SINGLE and SCAN_SELECT run
+    the scan as its own kernel first."""
     wl = W.make_workload(cfg, **kw)
     st = DecodeSetup(wl)
-    fused = wl.score_mode == "full" and wl.G == 4 and not wl.rope_theta
-    single = "fused" if fused else "tail"
+    single = "fused" if wl.score_mode == "full" else "fused_index"
     st.ctx.profile_enable(True)
-    st.ctx.set_launch_mode(AUTO)                      # fused launch where it applies, else per stage
-    auto = st.decode(debug=True)
-    prof = st.ctx.profile_read()
-    assert prof["fused" if fused else "select"][1] == 1, prof
-    st.ctx.set_launch_mode(SINGLE)
-    a = st.decode(debug=True)
-    prof = st.ctx.profile_read()
-    assert prof[single][1] == 1 and prof["select"][1] == 0, prof
-    for key in ("out", "lse", "sel_counts", "sel_idx", "scores"):
-        np.testing.assert_array_equal(auto[key], (a if fused else auto)[key])
-    st.ctx.set_launch_mode(MULTI)
-    m = st.decode(debug=True)
-    prof = st.ctx.profile_read()
-    assert prof["tail"][1] == 0 and prof["select"][1] == 1, prof
-    st.ctx.set_launch_mode(COOP)
-    c = st.decode(debug=True)
-    prof = st.ctx.profile_read()
-    assert prof[single][1] == 1 and prof["select"][1] == 0, prof
+
+    def run(mode, stage, absent=()):
+        st.ctx.set_launch_mode(mode)
+        res = st.decode(debug=True)
+        prof = st.ctx.profile_read()
+        assert prof[stage][1] == 1, (mode, prof)
+        for other in absent:
+            assert prof[other][1] == 0, (mode, prof)
+        assert res["status"] == 0
+        return res
+
+    auto = run(AUTO, single, ("select", "tail"))
+    a = run(SINGLE, single, ("select", "tail"))
+    m = run(MULTI, "select", ("tail", "fused", "fused_index"))
+    c = run(COOP, single, ("select", "tail"))
+    ss = run(hws.HWS_LAUNCH_SCAN_SINGLE, "tail", ("select", "fused", "fused_index"))
+    sel = run(hws.HWS_LAUNCH_SCAN_SELECT, "select", ("tail", "fused", "fused_index"))
     st.ctx.profile_enable(False)
-    for key in ("out", "lse", "sel_counts", "sel_idx", "scores"):   # same kernel, same grid
-        np.testing.assert_array_equal(a[key], c[key])
-    np.testing.assert_array_equal(a["sel_counts"], m["sel_counts"])
-    np.testing.assert_array_equal(a["sel_idx"], m["sel_idx"])
-    np.testing.assert_array_equal(a["scores"], m["scores"])
-    np.testing.assert_allclose(a["out"], m["out"], rtol=0, atol=2e-5)
-    np.testing.assert_allclose(a["lse"], m["lse"], rtol=0, atol=2e-5)
-    if not fused:
-        # AUTO: the selection in one launch, then the per-stage attention and
-        # merge: the sets of the three-launch selection, and the same kernels
-        # after it
-        for key in ("sel_counts", "sel_idx", "scores", "out", "lse"):
-            np.testing.assert_array_equal(auto[key], m[key])
+    for key in ("out", "lse", "sel_counts", "sel_idx", "scores", "rows_read", "sel_mass"):
+        np.testing.assert_array_equal(auto[key], a[key], err_msg=key)
+        np.testing.assert_array_equal(a[key], c[key], err_msg=key)    # same kernel, same grid
+    for other in (m, ss, sel):
+        for key in ("sel_counts", "sel_idx", "scores", "rows_read"):
+            np.testing.assert_array_equal(a[key], other[key], err_msg=key)
+        for key in ("out", "lse"):
+            np.testing.assert_allclose(a[key], other[key], rtol=0, atol=2e-5, err_msg=key)
+        np.testing.assert_allclose(a["sel_mass"], other["sel_mass"], rtol=0, atol=1e-6)
+    # the one-launch selection and the three selection kernels give the same
+    # sets (after it, index scores take the attention balanced by kept rows,
+    # full-dim scores the per-stage attention of MULTI: then bit for bit)
+    for key in ("sel_counts", "sel_idx", "scores", "rows_read"):
+        np.testing.assert_array_equal(sel[key], m[key], err_msg=key)
+    for key in ("out", "lse"):
+        if wl.score_mode == "full":
+            np.testing.assert_array_equal(sel[key], m[key], err_msg=key)
+        else:
+            np.testing.assert_allclose(sel[key], m[key], rtol=0, atol=2e-5, err_msg=key)
 
 
-@pytest.mark.parametrize("n,tail", [(4096, True), (4097, False)])
-def test_auto_short_contexts_take_single_launch(n, tail):
-    """AUTO runs short contexts (max_seq_len <= 4096) as the single launch
-    after the scan, longer ones per stage; both against the oracle."""
+@pytest.mark.parametrize("n,expect", [(4096, "tail"), (4097, "select")])
+def test_auto_short_contexts_take_single_launch(n, expect):
+    """Full-dim scores at G = 2 (no scan inside a launch for them): AUTO runs
+    short contexts (max_seq_len <= 4096) as the single launch after the scan,
+    longer ones as the one-launch selection and the per-stage attention; index
+    scores run the launch with the scan inside at either length.  All against
+    the oracle."""
+    wl = W.make_workload(1, n=n, Hq=4, Hkv=2, score_mode="full", batch=2)
+    st = DecodeSetup(wl, keep_host=True)
+    st.ctx.profile_enable(True)
+    res = st.decode(debug=True)
+    prof = st.ctx.profile_read()
+    assert prof[expect][1] == 1 and prof["fused_index"][1] == 0, prof
+    check_decode(st, res, verbose=False)
     wl = W.make_workload(2, n=n, batch=2)
     st = DecodeSetup(wl, keep_host=True)
     st.ctx.profile_enable(True)
     res = st.decode(debug=True)
     prof = st.ctx.profile_read()
     st.ctx.profile_enable(False)
-    assert (prof["tail"][1], prof["select"][1]) == ((1, 0) if tail else (0, 1)), prof
+    assert prof["fused_index"][1] == 1 and prof["score"][1] == 0, prof
     check_decode(st, res, verbose=False)
 
 
@@ -455,3 +472,51 @@ def test_bf16_index_pool_values():
                 mid = np.abs(np.abs(raw[diff] - ref[diff]) - ulp / 2)
                 assert (mid <= 1e-12 * np.abs(raw[diff]) + 1e-30).all()
             assert diff.mean() < 1e-6
+
+
+# -- retained full-dim mass: the dense log-sum-exp diagnostic -----------------------
+
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(n=6000, batch=2)), (5, dict(n=20000, batch=3)),
+                                    (1, dict(n=3000, rope_theta=10000.0)), (4, dict(n=9000))])
+def test_dense_lse_and_full_dim_mass(cfg, kw):
+    """hws_dense_lse against the oracle's log-sum-exp of every full-dim logit
+    (fp8 rows as stored, RoPE rotated), and the full-dim mass the GPU's sets
+    keep, mean_g exp(lse_S - lse_full), against the oracle's full_mass on the
+    same sets ([RTPurbo] Main results: attention mass retained)."""
+    import scipy.special
+    wl = W.make_workload(cfg, **kw)
+    print(f"\n[case] dense lse {wl.name} B={wl.B} N={wl.seq_lens[:3]} kv={wl.kv_dtype} rope={wl.rope_theta}",
+          flush=True)
+    st = DecodeSetup(wl, keep_host=True)
+    res = st.decode(debug=True)
+    lf = st.dense_lse()
+    G = wl.G
+    worst_lse = worst_mass = 0.0
+    for b in range(wl.B):
+        seq = st.host[b]
+        n = wl.seq_lens[b]
+        for h in range(wl.Hkv):
+            q_rot = O.rope(seq.q[h * G:(h + 1) * G].astype(np.float64), np.full(G, n - 1), wl.rope_theta)
+            ks = O.stored_rows(seq.k[:n, h], np.arange(n), rope_theta=wl.rope_theta, kv_fp8=st.fp8,
+                               segments=st.segments(n), rotate=True)
+            _, z = O.full_logits(q_rot, ks, wl.attn_scale)
+            lse_ref = scipy.special.logsumexp(z, axis=1)
+            e = float(np.abs(lf[b, h * G:(h + 1) * G] - lse_ref).max())
+            worst_lse = max(worst_lse, e)
+            assert e <= 1e-4, f"dense lse off at (b={b}, h={h}): {e}"
+            if wl.head_kinds[h] == "retrieval":
+                hr = wl.retrieval_heads.index(h)
+                S = res["sel_idx"][b, hr][:res["sel_counts"][b, h]].astype(np.int64)
+            else:
+                S = O.local_token_set(n, wl.n_sink, wl.window)
+            ref = O.decode_sequence_ref(
+                seq.q, seq.k, seq.v, head_kinds=wl.head_kinds, proj=st.proj_host, score_mode=wl.score_mode,
+                select_mode=wl.select_mode, top_p=float(wl.top_p[b]), top_k=int(wl.top_k[b]), n_sink=wl.n_sink,
+                window=wl.window, attn_scale=wl.attn_scale, index_scale=wl.index_scale, rope_theta=wl.rope_theta,
+                kv_fp8=st.fp8, segments=st.segments(n), heads=[h], fixed_sets={h: S}, with_full_mass=True)[h]
+            m_gpu = float(np.mean(np.exp(res["lse"][b, h * G:(h + 1) * G].astype(np.float64)
+                                         - lf[b, h * G:(h + 1) * G].astype(np.float64))))
+            em = abs(m_gpu - ref["full_mass"])
+            worst_mass = max(worst_mass, em)
+            assert em <= 1e-4, f"full-dim mass off at (b={b}, h={h}): {m_gpu} vs {ref['full_mass']}"
+    print(f"[ok] dense lse err {worst_lse:.2e}, full-dim mass err {worst_mass:.2e}", flush=True)

@@ -5,12 +5,17 @@ Tolerance (from the arithmetic of the kernel), per query row:
   logit is within delta = 1e-5 * attn_scale * |q| * max_j |k_j| (the decode
   score bound in natural-log units); with RoPE the rotated query is split
   into two bf16 parts, which adds 2^-15 * attn_scale * |q| * max_j |k_j|;
-* the softmax weights are rounded once to bf16 (8 significant bits: relative
-  error <= 2^-8) before the weighted sum of V, and a logit error delta moves
-  a normalised weight by at most 2 delta (relative).  Hence per element
-    |o_gpu - o_ref| <= (2^-8 + 2 delta) * sum_j p_j |v_jd| + 1e-5,
+* the softmax weights enter the weighted sum of V as two bf16 parts,
+  hi = bf16(p) and lo = bf16(p - hi), whose sum is within 2^-18 of p
+  (relative; REL allows 2^-16), and a logit error delta moves a normalised
+  weight by at most 2 delta (relative); the fp32 sums over n keys (one
+  rounding per 32-key MFMA step, plus the online rescales) add at most
+  (n / 16 + 4) 2^-24 (relative).  Hence per element
+    |o_gpu - o_ref| <= (REL + 2 delta + (n / 16 + 4) 2^-24) * sum_j p_j |v_jd| + 1e-5,
   with p the oracle's weights (``with_abs_v``);
-* lse (summed from the unrounded weights): within 2e-5 + delta.
+* lse (summed from the unrounded weights): within 2e-5 + delta;
+* and, whatever that bound allows, max |o_gpu - o_ref| <= 2e-3 (the decode
+  attention tolerance) on every row checked.
 FP8 cache: the products run on the e4m3 codes, exact in bf16, and the page
 scales multiply the logits and the weights in fp32, so the same bound holds
 with the stored (decoded) rows in place of k and v.
@@ -27,7 +32,9 @@ from head_wise_sparse_02_amd.runner import DecodeSetup, append_segments
 
 pytestmark = pytest.mark.gpu
 
-REL = 2.0 ** -8
+REL = 2.0 ** -16
+ABS_CAP = 2e-3
+WORST_ABS = {"out": 0.0}
 
 
 def chunk_segments(n_tok):
@@ -56,7 +63,7 @@ def _run(wl, n_tok, *, dense=False, rows=None, q_fn=None, stride=1, segments=Non
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     G = wl.G
     rows = np.arange(0, n_tok, stride) if rows is None else np.asarray(rows)
-    worst = 0.0
+    worst = worst_abs = 0.0
     for b in range(wl.B):
         n = wl.seq_lens[b]
         seq = st.host[b]
@@ -78,13 +85,18 @@ def _run(wl, n_tok, *, dense=False, rows=None, q_fn=None, stride=1, segments=Non
             delta = (1e-5 + (2.0 ** -15 if wl.rope_theta > 0 else 0.0)) * wl.attn_scale * qn * kmax
             o_gpu = out[b, rows, h * G:(h + 1) * G].astype(np.float64)
             err = np.abs(o_gpu - o_ref)
-            bound = (REL + 2 * delta[:, :, None]) * absv + 1e-5
+            acc = (n / 16 + 4) * 2.0 ** -24
+            bound = (REL + acc + 2 * delta[:, :, None]) * absv + 1e-5
             ratio = float((err / bound).max())
             worst = max(worst, ratio)
+            worst_abs = max(worst_abs, float(err.max()))
             assert ratio <= 1.0, f"output off at (b={b}, h={h}): {ratio:.3f} x tolerance"
+            assert float(err.max()) <= ABS_CAP, f"output off at (b={b}, h={h}): {float(err.max())} > {ABS_CAP}"
             el = np.abs(lse[b, rows, h * G:(h + 1) * G] - lse_ref)
             assert (el <= 2e-5 + delta).all(), f"lse off at (b={b}, h={h}): {float(el.max())}"
-    print(f"[ok] worst error / tolerance = {worst:.3f}", flush=True)
+    WORST_ABS["out"] = max(WORST_ABS["out"], worst_abs)
+    print(f"[ok] worst error / tolerance = {worst:.3f}, max |o - o_ref| = {worst_abs:.3g} "
+          f"(largest so far {WORST_ABS['out']:.3g})", flush=True)
     return st, out, lse
 
 
@@ -118,6 +130,18 @@ def test_prefill_layer_shape_sampled_rows():
     """32 query / 8 KV heads, 2 retrieval + 6 local heads, window 1024."""
     wl = W.make_workload(2, n=2600, batch=2)
     _run(wl, 2600, stride=13)
+
+
+def test_prefill_layer_shape_benched_length_sampled_rows():
+    """The benched prefill: one 32768-position chunk from position 0 of the 8B
+    layer shape, on 48 sampled query positions (the first and last, the
+    window's lower edge, and a seeded spread)."""
+    n = 32768
+    wl = W.make_workload(2, n=n, batch=1)
+    rng = np.random.default_rng(np.random.SeedSequence([2, 0, 6000]))
+    rows = np.unique(np.concatenate([[0, 1, 3, 4, 1023, 1024, 1025, n - 2, n - 1],
+                                     rng.choice(n, size=39, replace=False)]))
+    _run(wl, n, rows=rows)
 
 
 def test_prefill_ragged_batch_offsets():

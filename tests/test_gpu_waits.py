@@ -24,8 +24,11 @@ CASES = {
     # (workload, AUTO's single launch, whether the per-stage attention follows)
     "fused_128k_shape": (lambda: W.make_workload(3, n=32768, batch=1), "fused", False),
     "fused_cooperative": (lambda: W.make_workload(3, n=32768, batch=1), "fused", False),
-    "tail_4k": (lambda: W.make_workload(1), "tail", False),
-    "select_then_attend_8k": (lambda: W.make_workload(2, n=8192, batch=2), "select", True),
+    "fused_index_8k": (lambda: W.make_workload(2, n=8192, batch=2), "fused_index", False),
+    "fused_index_cooperative": (lambda: W.make_workload(1), "fused_index", False),
+    "tail_4k": (lambda: W.make_workload(1, Hq=4, Hkv=2, score_mode="full"), "tail", False),
+    "select_then_attend_8k": (lambda: W.make_workload(1, n=8192, Hq=4, Hkv=2, score_mode="full", batch=2),
+                              "select", True),
 }
 
 

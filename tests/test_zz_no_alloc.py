@@ -23,9 +23,10 @@ pytestmark = pytest.mark.gpu
 KEYS = ("out", "lse", "sel_counts", "sel_idx", "scores", "rows_read", "sel_mass", "status")
 
 
-def _both(wl, stage):
+def _both(wl, stage, mode=hws.HWS_LAUNCH_AUTO):
     print(f"\n[case] noalloc {wl.name} B={wl.B} N={wl.seq_lens[:3]} expects {stage}", flush=True)
     st = DecodeSetup(wl, keep_host=True)
+    st.ctx.set_launch_mode(mode)
     need = st.ctx.workspace_size(wl.B, st.Nmax, st.score_mode, st.scope)
     assert need <= hws.HWS_NOALLOC_SCRATCH_BYTES, need
     ref = st.decode(debug=True)
@@ -49,7 +50,9 @@ def test_noalloc_matches_decode_then_smaller_call():
     # 1: the single launch with the scan inside (full-dim scores, G = 4), 2 x 40000
     _both(W.make_workload(3, n=40000, batch=2), "fused")
     # 2: smaller, per-stage attention after the one-launch selection (index scores, local heads)
-    _both(W.make_workload(2, n=9000, batch=2), "select")
-    # 3: smaller still, the single launch after the scan (short context)
-    _both(W.make_workload(1, n=3000), "tail")
+    _both(W.make_workload(2, n=9000, batch=2), "select", hws.HWS_LAUNCH_SCAN_SELECT)
+    # 3: smaller, the single launch with the index scan inside
+    _both(W.make_workload(2, n=6000, batch=2), "fused_index")
+    # 4: smaller still, the single launch after the scan (short context)
+    _both(W.make_workload(1, n=3000), "tail", hws.HWS_LAUNCH_SCAN_SINGLE)
 
