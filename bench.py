@@ -61,8 +61,16 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = 128K headline)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cold-iters", type=int, default=20,
-                    help="extra steps each preceded by a 1 GiB cache flush (0 = skip)")
+    ap.add_argument("--context", type=int, default=None,
+                    help="context length of every sequence (workload 5: the longest drawn length), "
+                         "keeping the workload's recipe")
+    ap.add_argument("--batch", type=int, default=None, help="batch size, keeping the workload's recipe")
+    ap.add_argument("--top-k", type=float, default=None,
+                    help="retrieval heads keep a fixed top-k: a count, or a fraction of the context if < 1")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="retrieval heads keep the top-p set of this mass (every sequence)")
+    ap.add_argument("--cold-iters", type=int, default=100,
+                    help="graph replays each preceded by an untimed 1 GiB cache flush (0 = skip)")
     ap.add_argument("--launch", choices=["auto", "single", "multi", "cooperative", "scan-select", "scan-single"],
                     default="auto",
                     help="auto: the library's default; single: one launch with (or after) the scoring "
@@ -173,11 +181,26 @@ def cpu_baseline(wl, setup, reps: int) -> dict:
     import numpy as np
     import oracle as O
     from head_wise_sparse_02_amd.runner import append_segments
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
+    from threadpoolctl import threadpool_limits
+    cores = host_threads()
+    times = []
+    with threadpool_limits(limits=cores):
+        times = _time_oracle(wl, setup, reps, O, append_segments)
+    t = statistics.median(times)
+    return {"value": wl.B / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"whole decode step (all {wl.B} sequences x {wl.Hkv} KV heads), "
+                      f"median of {len(times)} runs, {t:.2f} s per step, BLAS/OpenMP pools at {cores} threads"}
+
+
+def host_threads() -> int:
+    """Threads the CPU baseline uses: the cores this process may run on,
+    capped by OMP_NUM_THREADS when that is set."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(aff, int(env))) if env.isdigit() else aff
+
+
+def _time_oracle(wl, setup, reps, O, append_segments) -> list:
     times = []
     for _ in range(max(1, reps)):
         t0 = time.perf_counter()
@@ -191,10 +214,7 @@ def cpu_baseline(wl, setup, reps: int) -> dict:
                 attn_scale=wl.attn_scale, index_scale=wl.index_scale, rope_theta=wl.rope_theta,
                 kv_fp8=wl.kv_dtype == "fp8", segments=append_segments(n))
         times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": wl.B / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"whole decode step (all {wl.B} sequences x {wl.Hkv} KV heads), "
-                      f"median of {len(times)} runs, {t:.2f} s per step"}
+    return times
 
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak
@@ -262,7 +282,7 @@ def prefill_main(args) -> int:
                                window=wl.window, attn_scale=wl.attn_scale, rows=rows,
                                kv_fp8=args.prefill_fp8, segments=append_segments(N))
         t = time.perf_counter() - t0
-        cpu = {"value": round(rows.size / t, 2), "unit": "tokens/s", "cores": os.cpu_count() or 1,
+        cpu = {"value": round(rows.size / t, 2), "unit": "tokens/s", "cores": host_threads(),
                "kind": "oracle", "sample": f"{rows.size} evenly spaced positions of the {N}-token chunk, "
                                            f"all heads, {t:.2f} s"}
     line = {
@@ -288,6 +308,121 @@ def prefill_main(args) -> int:
     return 0
 
 
+def build_workload(args, W):
+    """The workload ``--config`` names, with the context, batch and selection
+    overrides applied; an overridden workload's name carries them."""
+    if args.top_k is not None and args.top_p is not None:
+        raise SystemExit("--top-k and --top-p exclude each other")
+    wl = W.make_workload(args.config, seed=args.seed, n=args.context, batch=args.batch,
+                         select_scope=args.scope, index_dtype=args.index, local_ring=args.ring)
+    tags = []
+    if args.context is not None:
+        tags.append(f"n{args.context}")
+    if args.batch is not None:
+        tags.append(f"b{args.batch}")
+    if args.top_k is not None:
+        frac = args.top_k < 1.0
+        wl.select_mode = "top_k"
+        wl.top_k = np.array([int(args.top_k * n) if frac else int(args.top_k) for n in wl.seq_lens], np.int32)
+        wl.top_p = np.ones(wl.B, np.float32)
+        tags.append(f"topk{args.top_k * 100:g}pct" if frac else f"topk{int(args.top_k)}")
+    if args.top_p is not None:
+        wl.select_mode = "top_p"
+        wl.top_p = np.full(wl.B, args.top_p, np.float32)
+        wl.top_k = np.zeros(wl.B, np.int32)
+        tags.append(f"topp{args.top_p:g}")
+    if tags:
+        wl.name = wl.name + "_" + "_".join(tags)
+    return wl
+
+
+def dense_decode_bytes(wl) -> int:
+    """Bytes a dense decode step reads and writes: every cached K and V row of
+    every KV head (fp8: with one K/V scale pair per page), queries and outputs."""
+    row = 128 if wl.kv_dtype == "fp8" else 256
+    total = 0
+    for n in wl.seq_lens:
+        per_head = 2 * row * n + (8 * ((n + 15) // 16) if wl.kv_dtype == "fp8" else 0)
+        total += wl.Hkv * per_head
+    return total + wl.B * wl.Hq * wl.d * (2 + 4)
+
+
+def retained_mass(wl, setup) -> dict | None:
+    """Per retrieval head: the share of the aggregate index (or full-dim)
+    softmax mass the kept set holds, as the selection computed it, and the
+    full-dim softmax mass of every query head over its kept set,
+    exp(lse - lse_full), with lse_full from the dense log-sum-exp call.
+    Also the kept fraction of the context.  Untimed."""
+    import torch
+    if not wl.retrieval_heads:
+        return None
+    setup.decode(mass=True)
+    torch.cuda.synchronize()
+    sm = setup.sel_mass.cpu().numpy()
+    lse = setup.lse.cpu().numpy()
+    cnt = setup.sel_counts.cpu().numpy()
+    G = wl.G
+    ret = wl.retrieval_heads
+    qheads = [h * G + g for h in ret for g in range(G)]
+    if wl.select_scope == "query":
+        kept_mass = sm[:, qheads]
+        kept = cnt[:, qheads].astype(np.float64)
+    else:
+        kept_mass = sm[:, ret]
+        kept = cnt[:, ret].astype(np.float64)
+    n = np.asarray(wl.seq_lens, np.float64)[:, None]
+    out = {"selection_mass_mean": round(float(kept_mass.mean()), 5),
+           "selection_mass_min": round(float(kept_mass.min()), 5),
+           "selection_mass_of": "index" if wl.score_mode == "index" else "full-dim",
+           "kept_fraction_mean": round(float((kept / n).mean()), 5),
+           "sparsity_mean": round(float(1.0 - (kept / n).mean()), 5)}
+    if wl.local_ring and len(ret) < wl.Hkv:
+        out["full_dim_mass"] = None          # the dense pass cannot read the ring's local heads
+        return out
+    full = setup.dense_lse()
+    fm = np.exp(lse[:, qheads].astype(np.float64) - full[:, qheads].astype(np.float64))
+    out.update({"full_dim_mass_mean": round(float(fm.mean()), 5),
+                "full_dim_mass_min": round(float(fm.min()), 5)})
+    return out
+
+
+def cold_graph_steps(setup, stream, iters: int, warmup: int, use_graph: bool) -> dict:
+    """Step latencies with cold caches: the step captured once as a HIP graph,
+    each replay preceded by an untimed write of a 1 GiB buffer (larger than L2
+    and the Infinity Cache) and bracketed by HIP events on the stream."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    g = None
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            setup.decode()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            setup.decode()
+    run = g.replay if g is not None else setup.decode
+    for i in range(warmup):
+        flush.fill_(float(i))
+        run()
+    torch.cuda.synchronize()
+    times = []
+    for i in range(iters):
+        flush.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del g, flush
+    times.sort()
+    return {"graph": use_graph, "iters": iters, "p10_ms": round(times[len(times) // 10], 4),
+            "p50_ms": round(statistics.median(times), 4), "p90_ms": round(times[(9 * len(times)) // 10], 4)}
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -306,8 +441,7 @@ def main(argv=None) -> int:
     from head_wise_sparse_02_amd import workloads as W
     from head_wise_sparse_02_amd.runner import DecodeSetup
 
-    wl = W.make_workload(args.config, seed=args.seed, select_scope=args.scope, index_dtype=args.index,
-                         local_ring=args.ring)
+    wl = build_workload(args, W)
     want_cpu = not args.no_cpu_baseline
     print(f"[bench] building workload {args.config}: {W.CONFIG_NAMES[args.config]}",
           file=sys.stderr, flush=True)
@@ -405,20 +539,13 @@ def main(argv=None) -> int:
 
     cold = None
     if args.cold_iters > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        times = []
-        for i in range(args.cold_iters):
-            flush.fill_(float(i))
-            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            setup.decode()
-            b_.record(stream)
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b_))
-        times.sort()
-        cold = {"p10_ms": round(times[len(times) // 10], 4), "p50_ms": round(statistics.median(times), 4),
-                "p90_ms": round(times[(9 * len(times)) // 10], 4)}
-        del flush
+        cold = cold_graph_steps(setup, stream, args.cold_iters, min(args.warmup, 10),
+                                use_graph=args.launch != "cooperative")
+        cold_gbs = by["total"] / (cold["p50_ms"] * 1e6)
+        cold.update({"tokens_per_s_p50": round(wl.B / (cold["p50_ms"] / 1000.0), 1),
+                     "step_GBps_p50": round(cold_gbs, 1), "step_frac_of_peak_p50": round(cold_gbs / PEAK_GBS, 4)})
+    mass = retained_mass(wl, setup)
+    dense_bytes = dense_decode_bytes(wl)
 
     cpu = cpu_baseline(wl, setup, args.cpu_reps) if want_cpu else None
 
@@ -436,15 +563,21 @@ def main(argv=None) -> int:
                    "context": int(max(wl.seq_lens)), "score_mode": wl.score_mode,
                    "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype, "launch": args.launch,
                    "select_scope": wl.select_scope, "index_dtype": wl.index_dtype,
-                   "local_ring": wl.local_ring},
+                   "local_ring": wl.local_ring,
+                   "top_k": sorted({int(x) for x in wl.top_k}) if wl.select_mode == "top_k" else None,
+                   "top_p": sorted({round(float(x), 4) for x in wl.top_p}) if wl.select_mode == "top_p" else None},
         "kv_cache_bytes": int(sum(t.numel() * t.element_size() for t in (
             setup.k_pool, setup.v_pool, setup.kv_scales, setup.index_pool, setup.local_k_pool,
             setup.local_v_pool) if t is not None)),
         "step_bytes": by["total"], "step_GBps": round(step_gbs, 1),
         "step_frac_of_peak": round(step_gbs / PEAK_GBS, 4),
+        "dense_decode_bytes": dense_bytes, "dense_to_sparse_bytes": round(dense_bytes / by["total"], 2),
+        "retained_mass": mass,
+        "value_protocol": "warm: steps back to back on one stream, HIP events around the whole loop; "
+                          "cold_graph_step is the flushed, graph-replayed per-step distribution",
         "selected_per_head_mean": round(float(sel_counts[:, [h for h in wl.retrieval_heads]].mean()), 1)
         if wl.retrieval_heads else None,
-        "stages": stages, "cold_cache_step": cold,
+        "stages": stages, "cold_graph_step": cold,
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -10,6 +10,8 @@
 // for each one in turn).  The softmax runs online in log2 units.
 #pragma once
 
+#include <type_traits>
+
 #include "hws_device.h"
 
 namespace hws {
@@ -262,6 +264,147 @@ __device__ __forceinline__ void accumulate_rows(const DecodeParams& p, int b, in
         m[g] = mn;
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gathered attention with the next batch in flight.  The rows' (index, page)
+// coordinates are in LDS (tok[r], pgs[r] for r < nrows, filled by the
+// caller); processor `proc` takes batches of RB rows, batch j being rows
+// (16 j + proc) RB .. + RB - 1.  The K/V words (and fp8 scales) of batch j+1
+// are loaded, undecoded, before batch j is decoded and folded in, so a
+// processor always has a batch of loads outstanding while it computes.
+// Rows past the end (or on an out-of-range page) load row 0 of page 0 and are
+// masked.  Logits are q.k from the K rows (index scores), online softmax in
+// log2 units as in accumulate_rows.
+// ---------------------------------------------------------------------------
+template <bool FP8, int RB>
+struct RawBatch {
+  using W = typename std::conditional<FP8, uint2, uint4>::type;
+  W k[RB], v[RB];
+  float2 sc[FP8 ? RB : 1];
+  bool ok[RB];
+};
+
+template <bool FP8>
+__device__ __forceinline__ void decode8(uint4 w, float* x) {
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+}
+template <bool FP8>
+__device__ __forceinline__ void decode8(uint2 w, float* x) {
+  f32x2 t;
+  t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false); x[0] = t.x; x[1] = t.y;
+  t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);  x[2] = t.x; x[3] = t.y;
+  t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false); x[4] = t.x; x[5] = t.y;
+  t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);  x[6] = t.x; x[7] = t.y;
+}
+
+// Where the gather reads: the pools, heads per page, this head's slot, page limit.
+struct GatherSrc {
+  const void* kpool;
+  const void* vpool;
+  const float* scales;
+  int hstride, hslot;
+  unsigned plim;
+};
+
+// MARK: count each row read in rr at its position (debug).
+template <bool FP8, int RB, bool MARK>
+__device__ __forceinline__ void issue_batch(const GatherSrc& src, const int* tok, const int* pgs, int nrows,
+                                            int r0, int sub, RawBatch<FP8, RB>& rb, int* rr) {
+  using W = typename RawBatch<FP8, RB>::W;
+  constexpr int EB = FP8 ? 1 : 2;                       // bytes per element
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    const int rc = min(r0 + u, nrows - 1);
+    int ii = tok[rc], pg = pgs[rc];
+    rb.ok[u] = r0 + u < nrows && (unsigned)pg < src.plim;
+    if (!rb.ok[u]) { pg = 0; ii = 0; }
+    const size_t page = (size_t)pg * src.hstride + src.hslot;
+    const size_t koff = page * (BS * D) + (size_t)((((sub >> 2) << 4) + (ii & 15)) * 32 + 8 * (sub & 3));
+    const size_t voff = page * (BS * D) + (size_t)((ii & 15) * D + 8 * sub);
+    rb.k[u] = *reinterpret_cast<const W*>(reinterpret_cast<const unsigned char*>(src.kpool) + koff * EB);
+    rb.v[u] = *reinterpret_cast<const W*>(reinterpret_cast<const unsigned char*>(src.vpool) + voff * EB);
+    if (FP8) rb.sc[FP8 ? u : 0] = *reinterpret_cast<const float2*>(src.scales + page * 2);
+    if (MARK && sub == 0 && rb.ok[u]) atomicAdd(rr + ii, 1);
+  }
+}
+
+template <int G, bool FP8, int RB>
+__device__ __forceinline__ void fold_batch(const RawBatch<FP8, RB>& rb, const float (&qf)[G][8], float (&m)[G],
+                                           float (&l)[G], float (&o)[G][8]) {
+  float z[RB][G];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    float kx[8];
+    decode8<FP8>(rb.k[u], kx);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float a = qf[g][0] * kx[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) a = fmaf(qf[g][j], kx[j], a);
+      a = row16_sum(a);
+      z[u][g] = rb.ok[u] ? (FP8 ? a * rb.sc[FP8 ? u : 0].x : a) : NEG_INF;
+    }
+  }
+  // one rescale per batch (branch-free: a head with nothing yet keeps
+  // m = -inf, and its factors come out as 0)
+  float ms[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mn = m[g];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) mn = fmaxf(mn, z[u][g]);
+    ms[g] = mn == NEG_INF ? 0.f : mn;
+    const float cf = fast_exp2(m[g] - ms[g]);
+    l[g] *= cf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[g][j] *= cf;
+    m[g] = mn;
+  }
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    float vv[8];
+    decode8<FP8>(rb.v[u], vv);
+    const float vs = FP8 ? rb.sc[FP8 ? u : 0].y : 1.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vv[j] = rb.ok[u] ? (FP8 ? vv[j] * vs : vv[j]) : 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pz = fast_exp2(z[u][g] - ms[g]);
+      l[g] += pz;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pz, vv[j], o[g][j]);
+    }
+  }
+}
+
+// Rows 0..nrows-1 of the LDS list into (m, l, o) of processor `proc`
+// (continuing the values it holds).  qf: the group's queries in log2 units.
+// MARK: count every row read in rr[position] (debug; not for ring rows).
+template <int G, bool FP8, int RB, bool MARK = false>
+__device__ __forceinline__ void gather_pipelined(const GatherSrc& src, const int* tok, const int* pgs, int nrows,
+                                                 int proc, int sub, const float (&qf)[G][8], float (&m)[G],
+                                                 float (&l)[G], float (&o)[G][8], int* rr = nullptr) {
+  const int nb = (nrows + 16 * RB - 1) / (16 * RB);   // batches of the workgroup (uniform)
+  if (nb == 0) return;
+  // batches past the last are all masked rows: issuing them anyway keeps the
+  // loop free of branches, so the compiler waits only for the batch it folds
+  // (the scheduling barriers keep the compiler from pulling a batch's use
+  // up to its loads, which would leave nothing in flight)
+  RawBatch<FP8, RB> a, c;
+  issue_batch<FP8, RB, MARK>(src, tok, pgs, nrows, proc * RB, sub, a, rr);
+#pragma clang loop unroll(disable)
+  for (int j = 0; j < nb; j += 2) {
+    issue_batch<FP8, RB, MARK>(src, tok, pgs, nrows, ((j + 1) * 16 + proc) * RB, sub, c, rr);
+    __builtin_amdgcn_sched_barrier(0);
+    fold_batch<G, FP8, RB>(a, qf, m, l, o);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_batch<FP8, RB, MARK>(src, tok, pgs, nrows, ((j + 2) * 16 + proc) * RB, sub, a, rr);
+    __builtin_amdgcn_sched_barrier(0);
+    fold_batch<G, FP8, RB>(c, qf, m, l, o);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -172,7 +172,7 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode,
     L.row_list = off;  off = align_up(off + nRb * Nmax * sizeof(int2));
     L.tile_cnt = off;  off = align_up(off + (size_t)L.tail_ntiles * sizeof(unsigned int));
     L.pair_rows = off; off = align_up(off + nRb * sizeof(int));
-    L.item_base = off; off = align_up(off + (npairs + 1) * sizeof(int));
+    L.item_base = off; off = align_up(off + (npairs + 2) * sizeof(int));
     L.bal_ml = off;    off = align_up(off + nitems * G * sizeof(float2));
     L.bal_o = off;     off = align_up(off + nitems * G * D * sizeof(float));
   }
@@ -645,12 +645,16 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
   // fit, then the per-stage attention and merge.
   const int nws = (single && (mode == HWS_LAUNCH_AUTO || mode == HWS_LAUNCH_SCAN_SELECT)) ? tail_grid(p, false, true) : 0;
   const bool sel1 = nws > 0 && (long long)L.tail_ntiles <= (long long)TAIL_MAXT * nws;
-  // SCAN_SELECT with index scores: the attention balanced by kept rows (the
-  // selection writes every tile's kept offsets); AUTO keeps the per-stage
-  // attention, measured faster so far (ragged fp8 workload 84 against 79 us,
-  // 256K-token workload 36 against 58 plus a longer merge)
-  const bool balanced = sel1 && mode == HWS_LAUNCH_SCAN_SELECT && a->score_mode == HWS_SCORE_INDEX && L.bal_o != 0 &&
-                        (long long)a->batch * c.num_kv_heads <= BAL_MAX_HEADS;
+  // Index scores: the attention balanced by kept rows (the selection lists
+  // each head's kept rows) with SCAN_SELECT, and with AUTO for batches of
+  // many (sequence, KV head) pairs, where position chunks leave a few dense
+  // ones as the long pole (ragged fp8 workload, 256 pairs: attention 57 us
+  // against 83, at 10 us more for the lists in the selection).  With few
+  // pairs AUTO keeps the per-stage attention (256K-token workload, 8 pairs:
+  // attention 35 us either way, selection 30 against 37, merge 9 against 14).
+  const long long npairs = (long long)a->batch * c.num_kv_heads;
+  const bool balanced = sel1 && a->score_mode == HWS_SCORE_INDEX && L.bal_o != 0 && npairs <= BAL_MAX_HEADS &&
+                        (mode == HWS_LAUNCH_SCAN_SELECT || (mode == HWS_LAUNCH_AUTO && npairs >= BAL_AUTO_PAIRS));
   if (ctx->nR > 0) {
     const StageEv es = stage_events(ctx, 0);
     if ((e = launch_score(p, s, es.start, es.stop)) != hipSuccess) return hip_fail(ctx, e, "score launch");

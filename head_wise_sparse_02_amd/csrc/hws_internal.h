@@ -23,9 +23,11 @@ constexpr int HIST_BINS = 4096;   // pass 1 bins: bits 30..19 of the fp32 patter
 constexpr int LOCAL_CHUNK = 256;  // rows per local-head attention workgroup
 constexpr int PHASES = 12;        // phase timestamps per workgroup (HWS_PHASES)
 // Attention balanced by kept rows: the rows of all heads are cut into about
-// BAL_ITEMS items of at least BAL_RMIN rows (one item more per head at most).
+// At most BAL_ITEMS workgroups, each a segment of at least BAL_RMIN rows; a
+// segment leaves one partial per (sequence, KV head) piece it covers.
 constexpr int BAL_ITEMS = 2048;
 constexpr int BAL_RMIN = 64;
+constexpr int BAL_AUTO_PAIRS = 64;   // AUTO balances the attention from this many (sequence, KV head) pairs
 constexpr int BAL_MAX_HEADS = 2048;  // (sequence, KV head) pairs the item table holds in LDS
 
 // Single-launch tail (selection + attention + merge in one cooperative launch)
@@ -136,9 +138,10 @@ struct DecodeParams {
   int2* row_list;               // [B][nR][Nmax] (position, page) of the kept rows, or null
   unsigned int* tile_cnt;       // [tail_ntiles] kept rows of each selection tile
   int* pair_rows;               // [B * nR] kept rows of each retrieval head
-  int* item_base;               // [B * Hkv + 1] first item of each (sequence, KV head), head order
-  float2* bal_ml;               // [BAL_ITEMS + B * Hkv][G] (max, sum) of each item
-  float* bal_o;                 // [BAL_ITEMS + B * Hkv][G][D] unnormalised output of each item
+  int* item_base;               // [B * Hkv + 2] first listed row of each (sequence, KV head), the
+                                //   total, then the rows per workgroup of the balanced attention
+  float2* bal_ml;               // [BAL_ITEMS + B * Hkv][G] (max, sum) of each piece
+  float* bal_o;                 // [BAL_ITEMS + B * Hkv][G][D] unnormalised output of each piece
   signed char ret_slot[MAX_KV];
   signed char ret_head[MAX_KV];
   signed char loc_head[MAX_KV];

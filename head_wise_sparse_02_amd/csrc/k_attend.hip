@@ -18,6 +18,8 @@
 // Each workgroup produces (max, sum, unnormalised output) per query head in
 // log2 units; merge_kernel combines them.
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "attend_rows.h"
 
@@ -219,8 +221,9 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
 
 // out_g = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);  lse = (M + log2 L) ln 2.
 // One workgroup per (sequence, KV head, query head): MERGE_GROUPS groups of D
-// threads (one per dim) fold every MERGE_GROUPS-th split online, 16 splits'
-// partials loaded at once, then group 0 combines the groups' results.
+// threads (one per dim) fold every MERGE_GROUPS-th split online, 16 (32 with
+// 8 groups) splits' partials loaded at once, then group 0 combines the groups'
+// results.
 
 __device__ __forceinline__ void merge_fold(float& M, float& L, float& O, float m2, float l2, float o2) {
   if (!(l2 > 0.f)) return;                              // empty splits left no output
@@ -233,7 +236,7 @@ __device__ __forceinline__ void merge_fold(float& M, float& L, float& O, float m
 
 template <int G, int MERGE_GROUPS>
 __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p) {
-  constexpr int SB = 16;
+  constexpr int SB = MERGE_GROUPS >= 8 ? 32 : 16;
   const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int d = threadIdx.x % D, grp = threadIdx.x / D;
   const int hr = p.ret_slot[h];
@@ -241,11 +244,13 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
   int nspl;
   const float2* ml;                                     // split s at ml[s * G]
   const float* po;                                      // split s at po[s * G * D]
-  if (p.item_base != nullptr) {                         // balanced attention: this head's items
-    const int i0 = p.item_base[b * p.Hkv + h];
-    nspl = p.item_base[b * p.Hkv + h + 1] - i0;
-    ml = p.bal_ml + (size_t)i0 * G + g;
-    po = p.bal_o + ((size_t)i0 * G + g) * D + d;
+  if (p.item_base != nullptr) {                         // balanced attention: this pair's pieces
+    const int pi = b * p.Hkv + h;
+    const int r0 = p.item_base[pi], r1 = p.item_base[pi + 1], len = p.item_base[p.B * p.Hkv + 1];
+    const int w0 = r0 / len;
+    nspl = r1 > r0 ? (r1 - 1) / len - w0 + 1 : 0;
+    ml = p.bal_ml + (size_t)(w0 + pi) * G + g;
+    po = p.bal_o + ((size_t)(w0 + pi) * G + g) * D + d;
   } else {
     nspl = hr >= 0 ? p.ncR : p.ncL;
     const size_t base = (size_t)(b * p.Hkv + h) * p.max_splits * G + g;
@@ -300,18 +305,21 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
 // ---------------------------------------------------------------------------
 // Attention balanced by kept rows ([ICS] §2: the sparsity is irregular per
 // token, query and head, so chunks cut by position leave a few dense ones as
-// the long pole).  Every workgroup builds the same item table: (sequence, KV
-// head) pair i = b * Hkv + h has c_i rows -- the kept rows the selection
-// listed (retrieval) or its sinks and window (local) --, C = sum c_i, an item
-// is R = max(BAL_RMIN, ceil(C / BAL_ITEMS)) rows and pair i has ceil(c_i / R)
-// items, numbered in pair order.  Workgroups take items round-robin, load the
-// item's (position, page) list BAL_LIST rows at a time into LDS, gather the
-// rows with the register batches of accumulate_rows and store one partial per
-// item; workgroup 0 writes the table's first item per pair for the merge.
-// Index scores only (the rows carry K and V), one set per KV head.
+// the long pole).  The rows of all (sequence, KV head) pairs -- pair
+// i = b * Hkv + h has c_i rows, the kept rows the selection listed
+// (retrieval) or its sinks and window (local) -- are laid end to end in pair
+// order, C = sum c_i, and cut into equal segments of len rows, one per
+// workgroup: len = max(BAL_RMIN, C / grid rounded up to a whole batch).  A
+// workgroup walks the pairs its segment covers, loads each piece's
+// (position, page) list into LDS, gathers it with the next batch of loads in
+// flight, and stores one partial per piece.  Pieces form a monotone path
+// over (workgroup w, pair i), so w + i numbers them without gaps or
+// collisions; pair i's partials are w_first(i) + i .. w_last(i) + i.
+// Workgroup 0 writes the pair offsets and len for the merge.  Index scores
+// only (the rows carry K and V), one set per KV head.
 // ---------------------------------------------------------------------------
 constexpr int BAL_THREADS = 256;
-constexpr int BAL_LIST = 512;                 // rows per (position, page) list in LDS
+constexpr int BAL_LIST = 1024;                // rows per (position, page) list in LDS
 constexpr int BAL_TABLE = BAL_MAX_HEADS;      // pairs the LDS table holds
 
 // In-place exclusive scan of x[0..n) (n <= BAL_TABLE) over a 256-thread
@@ -356,103 +364,161 @@ __device__ __forceinline__ int pair_row_count(const DecodeParams& p, int b, int 
   return L1 + (N - max(L1, N - p.window));
 }
 
-template <int G, bool FP8>
+// The group's queries, dims 8*sub..8*sub+7, pre-scaled to log2 units.
+template <int G>
+__device__ __forceinline__ void load_group_q(const DecodeParams& p, int b, int h, int sub, float (&qf)[G][8]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const size_t qo = ((size_t)b * p.Hq + h * G + g) * D + 8 * sub;
+    const uint4 u = *reinterpret_cast<const uint4*>(p.q + qo);
+    qf[g][0] = bf16_lo(u.x); qf[g][1] = bf16_hi(u.x); qf[g][2] = bf16_lo(u.y); qf[g][3] = bf16_hi(u.y);
+    qf[g][4] = bf16_lo(u.z); qf[g][5] = bf16_hi(u.z); qf[g][6] = bf16_lo(u.w); qf[g][7] = bf16_hi(u.w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qf[g][j] *= p.c2_attn;
+  }
+}
+
+// RING_BF16: fp8 pools with the local heads in a (bf16) ring.  MARK: count
+// the rows read (debug).
+template <int G, bool FP8, bool RING_BF16, bool MARK>
 __global__ __launch_bounds__(BAL_THREADS) void attend_balanced_kernel(DecodeParams p) {
+  constexpr int RB = AttRB<G, 0>::value;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int proc = tid >> 4, sub = tid & 15;
   const int npairs = p.B * p.Hkv;
   __shared__ int base_s[BAL_TABLE + 1];
-  __shared__ int cnt_s[BAL_TABLE];
   __shared__ int tmp[8];
-  __shared__ long long csum_s[4];
   __shared__ int tok_s[BAL_LIST], pg_s[BAL_LIST];
   __shared__ float wm[4][MAX_G], wl[4][MAX_G];
   __shared__ float wo[4][MAX_G][D];
 
-  // ---- the item table (the same in every workgroup) ----
-  long long csum = 0;
-  for (int i = tid; i < npairs; i += BAL_THREADS) {
-    const int c = pair_row_count(p, i / p.Hkv, i % p.Hkv);
-    cnt_s[i] = c;
-    csum += c;
-  }
-  for (int off = 1; off < 64; off <<= 1) csum += __shfl_xor(csum, off);
-  if (lane == 0) csum_s[wave] = csum;
+  stamp_phase(p, 0);
+  // ---- pair offsets (the same in every workgroup) ----
+  for (int i = tid; i < npairs; i += BAL_THREADS) base_s[i] = pair_row_count(p, i / p.Hkv, i % p.Hkv);
   __syncthreads();
-  const long long C = csum_s[0] + csum_s[1] + csum_s[2] + csum_s[3];
-  const int R = (int)max((long long)BAL_RMIN, (C + BAL_ITEMS - 1) / BAL_ITEMS);
-  for (int i = tid; i < npairs; i += BAL_THREADS) base_s[i] = (cnt_s[i] + R - 1) / R;
+  const int C = block_scan_excl(base_s, npairs, tmp);
+  if (tid == 0) base_s[npairs] = C;
   __syncthreads();
-  const int nitems = block_scan_excl(base_s, npairs, tmp);
-  if (tid == 0) base_s[npairs] = nitems;
-  __syncthreads();
-  if (blockIdx.x == 0)
+  const int per = (C + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int len = max(BAL_RMIN, (per + 16 * RB - 1) / (16 * RB) * (16 * RB));
+  if (blockIdx.x == 0) {
     for (int i = tid; i <= npairs; i += BAL_THREADS) p.item_base[i] = base_s[i];
-
-  constexpr int RB = AttRB<G, 0>::value;
-  for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
-    // the pair of item `it`: the last i with base_s[i] <= it
+    if (tid == 0) p.item_base[npairs + 1] = len;
+  }
+  int g0 = (int)blockIdx.x * len;
+  const int g1 = min(C, g0 + len);
+  stamp_phase(p, 1);
+  if (g0 >= g1) return;
+  // the pair holding row g0: the last i with base_s[i] <= g0 (empty pairs skipped)
+  int pi = 0;
+  {
     int lo_i = 0, hi_i = npairs;
     while (hi_i - lo_i > 1) {
       const int mid = (lo_i + hi_i) >> 1;
-      if (base_s[mid] <= it) lo_i = mid; else hi_i = mid;
+      if (base_s[mid] <= g0) lo_i = mid; else hi_i = mid;
     }
-    const int b = lo_i / p.Hkv, h = lo_i % p.Hkv;
-    const int hr = p.ret_slot[h];
-    const int N = min(p.seq_lens[b], p.Nmax);
-    const int r0 = (it - base_s[lo_i]) * R, r1 = min(r0 + R, cnt_s[lo_i]);
-    const int L1 = min(p.n_sink, N), start2 = max(L1, N - p.window);
-    const int2* list = hr >= 0 ? p.row_list + ((size_t)b * p.nR + hr) * p.Nmax : nullptr;
-    float m[G], l[G], o[G][8];
-    for (int rs = r0; rs < r1 || rs == r0; rs += BAL_LIST) {
-      const int nl = max(0, min(BAL_LIST, r1 - rs));
-      for (int q = tid; q < nl; q += BAL_THREADS) {
-        const int r = rs + q;
+    pi = lo_i;
+  }
+  while (base_s[pi + 1] <= g0) ++pi;
+  // the current piece: pair pi, its queries and running (m, l, o)
+  float qf[G][8], m[G], l[G], o[G][8];
+  auto start_piece = [&]() {
+    load_group_q<G>(p, pi / p.Hkv, pi % p.Hkv, sub, qf);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = NEG_INF;
+      l[g] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+    }
+  };
+  start_piece();
+  // the segment's (position, page) list, BAL_LIST rows at a time, each chunk
+  // filled for all the pieces it holds in one round of loads
+  for (int cs = g0; cs < g1; cs += BAL_LIST) {
+    const int ce = min(g1, cs + BAL_LIST);
+    for (int pf = pi, gg = cs; gg < ce; ++pf) {
+      if (base_s[pf + 1] <= gg) continue;           // empty pair
+      const int pe = min(ce, base_s[pf + 1]);
+      const int b = pf / p.Hkv, h = pf % p.Hkv, hr = p.ret_slot[h];
+      const int N = min(p.seq_lens[b], p.Nmax);
+      const int L1 = min(p.n_sink, N), start2 = max(L1, N - p.window);
+      const int2* list = hr >= 0 ? p.row_list + ((size_t)b * p.nR + hr) * p.Nmax : nullptr;
+      for (int q = tid; q < pe - gg; q += BAL_THREADS) {
+        const int r = gg - base_s[pf] + q;          // row of the pair
+        int* tk = tok_s + (gg - cs) + q;
+        int* pg = pg_s + (gg - cs) + q;
         if (hr >= 0) {
           const int2 e = list[r];
-          tok_s[q] = e.x;
-          pg_s[q] = e.y;
+          *tk = e.x;
+          *pg = e.y;
         } else {
-          local_row_at(p, b, p.loc_slot[h], r < L1 ? r : start2 + (r - L1), tok_s[q], pg_s[q]);
+          local_row_at(p, b, p.loc_slot[h], r < L1 ? r : start2 + (r - L1), *tk, *pg);
+        }
+      }
+      gg = pe;
+    }
+    __syncthreads();
+    stamp_phase(p, 8);
+    for (int gg = cs; gg < ce;) {
+      const int pe = min(ce, base_s[pi + 1]);
+      const int b = pi / p.Hkv, h = pi % p.Hkv, hr = p.ret_slot[h];
+      const bool ring = hr < 0 && p.ring_rows > 0;
+      GatherSrc src;
+      src.kpool = ring ? p.lk_pool : p.k_pool;
+      src.vpool = ring ? p.lv_pool : p.v_pool;
+      src.scales = p.kv_scales;
+      src.hstride = ring ? 1 : p.Hp;
+      src.hslot = ring ? 0 : p.pool_slot[h];
+      src.plim = ring ? (unsigned)p.ring_pages : (unsigned)p.num_blocks;
+      const int* tk = tok_s + (gg - cs);
+      const int* pg = pg_s + (gg - cs);
+      if (RING_BF16 && ring) {                      // the ring holds bf16 rows (not counted)
+        gather_pipelined<G, false, RB>(src, tk, pg, pe - gg, proc, sub, qf, m, l, o);
+      } else {
+        int* rr = MARK ? p.rows_read + (size_t)(b * p.Hkv + h) * p.Nmax : nullptr;
+        gather_pipelined<G, FP8, RB, MARK>(src, tk, pg, pe - gg, proc, sub, qf, m, l, o, rr);
+      }
+      gg = pe;
+      if (pe < base_s[pi + 1] && pe < g1) continue;   // the piece goes on in the next chunk
+      // the piece ends: its partial at slot w + i
+      combine_wave_procs<G>(m, l, o);
+      if (lane < 16) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) wo[wave][g][8 * sub + j] = o[g][j];
         }
       }
       __syncthreads();
-      if (FP8 && hr < 0 && p.ring_rows > 0)       // the ring holds bf16 rows
-        accumulate_rows<G, false, 0, RB, false, true>(p, b, h, hr, 0, nl, proc * RB, 16 * RB, sub, nullptr,
-                                                      nullptr, tok_s, pg_s, nullptr, m, l, o, nullptr, rs == r0);
-      else
-        accumulate_rows<G, FP8, 0, RB>(p, b, h, hr, 0, nl, proc * RB, 16 * RB, sub, nullptr, nullptr, tok_s,
-                                       pg_s, nullptr, m, l, o, nullptr, rs == r0);
-      __syncthreads();                            // the list is reused
-    }
-    combine_wave_procs<G>(m, l, o);
-    if (lane < 16) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wo[wave][g][8 * sub + j] = o[g][j];
+      const size_t slot = (size_t)blockIdx.x + pi;
+      float2* ml = p.bal_ml + slot * G;
+      float* po = p.bal_o + slot * G * D;
+      for (int e = tid; e < G * D; e += BAL_THREADS) {
+        const int g = e / D, d = e % D;
+        float mm = NEG_INF;
+        for (int k = 0; k < 4; ++k) mm = fmaxf(mm, wm[k][g]);
+        float ll = 0.f, oo = 0.f;
+        for (int k = 0; k < 4; ++k) {
+          if (wm[k][g] == NEG_INF) continue;
+          const float cf = fast_exp2(wm[k][g] - mm);
+          ll += wl[k][g] * cf;
+          oo += wo[k][g][d] * cf;
+        }
+        po[(size_t)g * D + d] = oo;
+        if (d == 0) ml[g] = make_float2(mm, ll);
       }
+      __syncthreads();                              // wm / wo are reused by the next piece
+      if (pe >= g1) break;
+      ++pi;
+      while (base_s[pi + 1] <= pe) ++pi;            // empty pairs
+      start_piece();
     }
-    __syncthreads();
-    float2* ml = p.bal_ml + (size_t)it * G;
-    float* po = p.bal_o + (size_t)it * G * D;
-    for (int e = tid; e < G * D; e += BAL_THREADS) {
-      const int g = e / D, d = e % D;
-      float mm = NEG_INF;
-      for (int k = 0; k < 4; ++k) mm = fmaxf(mm, wm[k][g]);
-      float ll = 0.f, oo = 0.f;
-      for (int k = 0; k < 4; ++k) {
-        if (wm[k][g] == NEG_INF) continue;
-        const float cf = fast_exp2(wm[k][g] - mm);
-        ll += wl[k][g] * cf;
-        oo += wo[k][g][d] * cf;
-      }
-      po[(size_t)g * D + d] = oo;
-      if (d == 0) ml[g] = make_float2(mm, ll);
-    }
-    __syncthreads();                              // wm / wo are reused by the next item
+    __syncthreads();                                // the list is reused
+    stamp_phase(p, 9);
   }
+  stamp_phase(p, 10);
 }
 
 // ---------------------------------------------------------------------------
@@ -642,19 +708,51 @@ static hipError_t launch_merge_mg(const DecodeParams& p, hipStream_t s, hipEvent
 hipError_t launch_merge(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   // many splits (a long context in few workgroups' worth of heads): 8 groups
   // of threads per output row halve the serial load rounds; otherwise 4
-  return p.max_splits >= 128 ? launch_merge_mg<8>(p, s, e0, e1) : launch_merge_mg<4>(p, s, e0, e1);
+  // (the balanced attention spreads the dense head of a small batch over
+  // most workgroups; a large batch leaves every head a few pieces)
+  const bool many = p.max_splits >= 128 || (p.item_base != nullptr && p.B * p.Hkv < BAL_AUTO_PAIRS);
+  return many ? launch_merge_mg<8>(p, s, e0, e1) : launch_merge_mg<4>(p, s, e0, e1);
+}
+
+// Workgroups of `fn` the device holds at once (cached per kernel and device).
+static int resident_wgs(const void* fn, int threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  struct Entry { const void* fn; int dev; int nwg; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.fn == fn && e.dev == dev) return e.nwg;
+  int ncu = 0, occ = 0, nwg = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, threads, 0) == hipSuccess)
+    nwg = ncu * occ;
+  cache.push_back(Entry{fn, dev, nwg});
+  return nwg;
+}
+
+template <typename K>
+static hipError_t launch_balanced(K kernel, const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  // one segment per workgroup the device holds at once: every segment starts
+  // at once and none waits for a free slot
+  int nwg = resident_wgs(reinterpret_cast<const void*>(kernel), BAL_THREADS);
+  if (nwg <= 0) nwg = 512;
+  const dim3 grid(std::max(1, std::min(nwg, BAL_ITEMS))), blk(BAL_THREADS);
+  return launch_kernel(kernel, grid, blk, s, e0, e1, p);
 }
 
 template <int G>
 static hipError_t launch_attend_balanced_g(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  // about four workgroups per compute unit; they loop over the items
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    ncu = 256;
-  const dim3 grid(std::max(1, std::min(4 * ncu, BAL_ITEMS + p.B * p.Hkv))), blk(BAL_THREADS);
-  if (p.kv_scales != nullptr) return launch_kernel(attend_balanced_kernel<G, true>, grid, blk, s, e0, e1, p);
-  return launch_kernel(attend_balanced_kernel<G, false>, grid, blk, s, e0, e1, p);
+  const bool mark = p.rows_read != nullptr;
+  if (p.kv_scales == nullptr)
+    return mark ? launch_balanced(attend_balanced_kernel<G, false, false, true>, p, s, e0, e1)
+                : launch_balanced(attend_balanced_kernel<G, false, false, false>, p, s, e0, e1);
+  if (p.ring_rows > 0 && p.nL > 0)
+    return mark ? launch_balanced(attend_balanced_kernel<G, true, true, true>, p, s, e0, e1)
+                : launch_balanced(attend_balanced_kernel<G, true, true, false>, p, s, e0, e1);
+  return mark ? launch_balanced(attend_balanced_kernel<G, true, false, true>, p, s, e0, e1)
+              : launch_balanced(attend_balanced_kernel<G, true, false, false>, p, s, e0, e1);
 }
 
 hipError_t launch_attend_balanced(const DecodeParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {

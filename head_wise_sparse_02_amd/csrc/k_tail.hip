@@ -1122,6 +1122,23 @@ __global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
 // ties, the ordered compaction, and the gathered attention over the kept
 // rows (K and V rows, logits from q.k) with the last split merging.
 // ---------------------------------------------------------------------------
+// The local-head chunks of workgroup w (item i goes to workgroup
+// (ntiles + i) mod nwg), each gathered and finished as a split of its head.
+template <int G, bool FP8>
+__device__ __forceinline__ void local_items(const DecodeParams& p, TailLds& S, int w, int nwg) {
+  const int nitems = p.B * p.nL * p.ncL;
+  const int first_item = ((w - p.tail_ntiles) % nwg + nwg) % nwg;
+  for (int it = first_item; it < nitems; it += nwg) {
+    int b, h, c;
+    __syncthreads();
+    const int nrows = local_rows(p, S, it, b, h, c);
+    __syncthreads();
+    if (nrows > 0) attend_rows<G, FP8, 0>(p, S, b, h, -1, c, 0, nrows, nullptr);
+    else empty_split<G>(p, b, h, c);
+    finish_split<G>(p, S, b, h, -1);
+  }
+}
+
 template <int G, bool FP8, int SP>
 __device__ __forceinline__ void fused_index_tile(const DecodeParams& p, TailLds& S, unsigned int* err) {
   static_assert(SP <= TPT && SP % 4 == 0 && 4 * SP <= 64, "slots in use; a page id per lane");
@@ -1433,18 +1450,7 @@ __global__ __launch_bounds__(TT) void fused_index_kernel(DecodeParams p) {
   unsigned int* err = p.tail_sync;
   stamp_phase(p, 0);
   if (w < p.tail_ntiles) fused_index_tile<G, FP8, SP>(p, S, err);
-  // local-head chunks: item i goes to workgroup (ntiles + i) mod nwg
-  const int nitems = p.B * p.nL * p.ncL;
-  const int first_item = ((w - p.tail_ntiles) % nwg + nwg) % nwg;
-  for (int it = first_item; it < nitems; it += nwg) {
-    int b, h, c;
-    __syncthreads();
-    const int nrows = local_rows(p, S, it, b, h, c);
-    __syncthreads();
-    if (nrows > 0) attend_rows<G, FP8, 0>(p, S, b, h, -1, c, 0, nrows, nullptr);
-    else empty_split<G>(p, b, h, c);
-    finish_split<G>(p, S, b, h, -1);
-  }
+  local_items<G, FP8>(p, S, w, nwg);
   stamp_phase(p, 11);
 }
 

@@ -376,11 +376,11 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  *    as the single launch (the shape HWS_LAUNCH_SINGLE falls back to).
  *  HWS_LAUNCH_SCAN_SELECT: the scoring scan, then the selection alone as one
  *    launch of the single-launch kind, then the attention and merge: with
- *    index scores the attention balanced by kept rows (the selection writes
- *    each tile's kept positions; every head's rows, kept or sinks + window,
- *    are cut into items of about the same size, at most 2048 items plus one
- *    per (sequence, KV head), for up to 2048 such pairs), else the per-stage
- *    attention.
+ *    index scores the attention balanced by kept rows (the selection lists
+ *    each head's kept rows; the rows of all heads, kept or sinks + window,
+ *    laid end to end, are cut into one equal segment per resident
+ *    workgroup, for up to 2048 (sequence, KV head) pairs), else the
+ *    per-stage attention.
  *    The grid is sized to what the device holds at once (compute units x
  *    occupancy) and launched as an ordinary dispatch: it relies on this
  *    process having the device's compute units (no CU masking); a kernel
@@ -397,7 +397,9 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  *    max_seq_len <= 4096 (short contexts, where launch latency dominates);
  *    otherwise the scoring scan, the one-launch selection (same waits and
  *    time-out; one set per KV head, when its tiles fit the device), the
- *    per-stage attention and merge; otherwise HWS_LAUNCH_MULTI.  (The
+ *    per-stage attention and merge -- with index scores and at least 64
+ *    (sequence, KV head) pairs the attention balanced by kept rows, as in
+ *    HWS_LAUNCH_SCAN_SELECT --; otherwise HWS_LAUNCH_MULTI.  (The
  *    single launch without the scan gathers each tile's kept rows in one
  *    workgroup, which loses to the per-stage attention when many rows are
  *    kept or many local-head chunks run beside it.)
@@ -444,7 +446,10 @@ const char* hws_profile_stage_name(int32_t i);
  * max_workgroups write nothing; a phase a workgroup does not run stays as the
  * caller left it).  Phases: 0 start, 1 scan, 2 log-sum-exp exchange, 3 a_i,
  * 4-6 radix passes 1-3, 7 ties, 8 compaction, 9 attention, 10 merge,
- * 11 local-head chunks.  buf = NULL turns it off. */
+ * 11 local-head chunks.  The attention balanced by kept rows (launch mode
+ * HWS_LAUNCH_SCAN_SELECT) stamps 0 start, 1 segment table, 8 row list
+ * loaded, 9 rows gathered (the last list of its segment), 10 end.
+ * buf = NULL turns it off. */
 #define HWS_PHASES 12
 hws_status hws_profile_phases(hws_ctx* ctx, uint64_t* buf, int32_t max_workgroups);
 

@@ -23,7 +23,10 @@ AUTO, MULTI, SINGLE = hws.HWS_LAUNCH_AUTO, hws.HWS_LAUNCH_MULTI, hws.HWS_LAUNCH_
 @pytest.mark.parametrize("cfg,kw,launch", [
     (1, dict(n=5000), AUTO), (1, dict(n=5000), SINGLE), (2, dict(n=6000, batch=3), AUTO),
     (3, dict(n=40000, batch=2), AUTO), (5, dict(n=20000, batch=4), MULTI),
-], ids=["tiny-auto", "tiny-single", "layer-auto", "oracle-topk-fused", "ragged-fp8-multi"])
+    (4, dict(n=20000), AUTO), (5, dict(n=20000, batch=4), AUTO),
+    (5, dict(n=20000, batch=4), hws.HWS_LAUNCH_SCAN_SELECT), (2, dict(n=6000, batch=3), hws.HWS_LAUNCH_SCAN_SINGLE),
+], ids=["tiny-auto", "tiny-single", "layer-auto", "oracle-topk-fused", "ragged-fp8-multi", "long-auto",
+        "ragged-fp8-auto", "ragged-fp8-scan-select", "layer-scan-single"])
 def test_graph_replays_match_eager(cfg, kw, launch):
     wl = W.make_workload(cfg, **kw)
     print(f"\n[case] graph {wl.name} B={wl.B} N={wl.seq_lens[:4]} launch={launch}", flush=True)

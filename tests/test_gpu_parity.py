@@ -172,6 +172,26 @@ def test_oracle_topk_128k_sampled_and_timed_path():
         np.testing.assert_array_equal(t.cpu().numpy(), res[key], err_msg=key)
 
 
+def test_layer_recipe_128k_top_k_sampled():
+    """The r = 16 index path at a 128K context: the Llama-3-8B layer recipe
+    (B = 8, 2 retrieval + 6 local KV heads) at N = 131072 with a fixed top-k of
+    2 % (k = 2621) in place of top-p.  8 sampled pairs, among them both
+    retrieval heads of sequence 0, then the timed call bitwise equal to the
+    debug call."""
+    wl = W.make_workload(2, n=131072, select_mode="top_k", top_k=np.full(8, 2621, np.int32),
+                         top_p=np.ones(8, np.float32))
+    pairs = _sample_pairs(wl, 8, must=[(0, h) for h in wl.retrieval_heads])
+    print(f"\n[case] layer recipe 128K top-k 2%: pairs {pairs}", flush=True)
+    st = DecodeSetup(wl, keep_host=sorted({b for b, _ in pairs}))
+    res = st.decode(debug=True)
+    check_decode(st, res, pairs=pairs, verbose=True)
+    assert (res["sel_counts"][:, wl.retrieval_heads] == 2621).all()
+    st.decode()
+    torch.cuda.synchronize()
+    for key, t in (("out", st.out), ("lse", st.lse), ("sel_counts", st.sel_counts)):
+        np.testing.assert_array_equal(t.cpu().numpy(), res[key], err_msg=key)
+
+
 def test_long_256k_all_heads():
     wl = W.make_workload(4)
     _, res, reps = _run(wl, pairs=[(0, h) for h in range(wl.Hkv)])
@@ -253,6 +273,30 @@ def test_single_launch_matches_multi(cfg, kw):
             np.testing.assert_array_equal(sel[key], m[key], err_msg=key)
         else:
             np.testing.assert_allclose(sel[key], m[key], rtol=0, atol=2e-5, err_msg=key)
+
+
+SCAN_SELECT = hws.HWS_LAUNCH_SCAN_SELECT
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (1, dict(n=5000)),
+    (1, dict(n=3000, Hq=2, Hkv=2)),
+    (1, dict(n=3000, Hq=4, Hkv=2, batch=3)),
+    (2, dict(n=9000, batch=3)),
+    (2, dict(n=9000, batch=3, kv_dtype="fp8", local_ring=True)),
+    (2, dict(n=3000, batch=3, select_mode="top_k", top_k=np.array([1, 37, 5000], np.int32))),
+    (4, dict(n=60000)),
+    (5, dict(n=30000, batch=8)),
+], ids=["tiny", "g1", "g2-batch", "layer", "layer-fp8-ring", "topk-edges", "long-g8", "ragged-fp8"])
+def test_balanced_attention_against_oracle(cfg, kw):
+    """The attention balanced by kept rows (equal row segments over all
+    heads, the next batch of loads in flight) against the oracle: group sizes
+    1 to 8, bf16 and fp8 pools, a bf16 local ring beside an fp8 cache, top-k
+    sets of one row and of the whole context, a single retrieval head spread
+    over most workgroups (G = 8), ragged fp8 sequences."""
+    wl = W.make_workload(cfg, **kw)
+    _, res, _ = _run(wl, launch=SCAN_SELECT, verbose=False)
+    assert res["status"] == 0
 
 
 @pytest.mark.parametrize("n,expect", [(4096, "tail"), (4097, "select")])
