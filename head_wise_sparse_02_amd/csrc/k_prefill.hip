@@ -16,7 +16,8 @@
 // rows and computes
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims from LDS,
 //                  B = the wave's queries, kept in registers)
-//   O^T += V^T P^T (A = 16 dims x 32 keys of V^T, B = P as two bf16 parts),
+//   O^T += V^T P^T (v_mfma_f32_16x16x32_f16: A = 16 dims x 32 keys of V^T,
+//                  B = P, both fp16),
 // with the online softmax in log2 units between the two.  The S^T layout
 // leaves each lane with 4 keys of one query per 16-key block, which is the
 // B-operand shape of P^T once both operands enumerate the 32 keys of a step
@@ -27,19 +28,19 @@
 // every 16 positions from a multiple of 16 sit in one ring page.
 //
 // With RoPE on, queries are rotated in fp64 at their position and split as
-// q = hi + lo (two bf16 parts), so S keeps fp32-level accuracy.  The softmax
-// weights are split the same way for the P V product, P = hi + lo with
-// hi = bf16(P) and lo = bf16(P - hi) (about 17 significant bits), and V^T
-// multiplies both parts: a single bf16 rounding of P (2^-9 relative) moves
-// outputs by up to a few 1e-3, the split by about 1e-5.
+// q = hi + lo (two bf16 parts), so S keeps fp32-level accuracy.  The P V
+// product runs in fp16: V enters LDS as fp16 (exact for bf16 values of
+// magnitude 2^-14 .. 65504; smaller ones keep an absolute error below
+// 2^-25), and the softmax weights P in (0, 1] are rounded once to fp16
+// (2^-11 relative, where bf16 would give 2^-9 and move outputs by up to a few
+// 1e-3), with fp32 accumulation.
 //
-// FP8 pages: the e4m3 codes are widened to bf16 on their way into LDS (exact:
-// every e4m3 value is a bf16 value), so the products are those of the bf16
-// path on the codes; each 16-key block of S is then multiplied by its page's
-// K scale, and each weight by its page's V scale before it is split into its
-// two bf16 parts for P V (the softmax sum is taken from the unscaled
-// weights).  Both scales enter the exponent: the weight times the V scale is
-// exp2(s * c2 * ks + log2(vs) - m), for raw product s and the running max m.
+// FP8 pages: the e4m3 K codes are widened to bf16 on their way into LDS
+// (exact: every e4m3 value is a bf16 value), so S holds the products on the
+// codes and each 16-key block of S is multiplied by its page's K scale
+// (which enters the exponent: exp2(s * c2 * ks - m) for raw product s and
+// the running max m); the V codes enter LDS already multiplied by their
+// page's V scale, as fp16.
 #include "mfma_tile.h"
 
 namespace hws {
@@ -232,8 +233,10 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
       const int c = tid + PF_THREADS * u;
       *reinterpret_cast<u32x4*>(&S.k[buf][(c >> 8) * (BS * D) + kw_off]) = chunk_bf16(kreg[u]);
       const int key = c >> 4;
+      // V as fp16 (fp8: the code times its page's V scale); keys past the
+      // chunk's last position as +0
       *reinterpret_cast<u32x4*>(&S.v[buf][key * V_STRIDE + 8 * (c & 15)]) =
-          chunk_bf16(kt * PF_KT + key <= tl ? vreg[u] : Chunk{});    // (code 0 is +0)
+          chunk_v_f16(kt * PF_KT + key <= tl ? vreg[u] : Chunk{}, FP8 ? sc[4 + (key >> 4)] : 1.f);
     }
     if constexpr (FP8) {
       if (tid == 0) {
@@ -278,16 +281,13 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
 
     // FP8: per 16-key page, c2 times its K scale, log2 of its V scale and the
     // reciprocal of that scale (the scales are positive)
-    float ksc[4], c2k[4], lvs[4], ivs[4];
+    float ksc[4], c2k[4];
     if constexpr (FP8) {
       const f32x4 kv = *reinterpret_cast<const f32x4*>(&S.sc[buf][0]);
-      const f32x4 vv = *reinterpret_cast<const f32x4*>(&S.sc[buf][4]);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         ksc[kb] = kv[kb];
         c2k[kb] = p.c2 * kv[kb];
-        lvs[kb] = __builtin_amdgcn_logf(vv[kb]);
-        ivs[kb] = __builtin_amdgcn_rcpf(vv[kb]);
       }
     }
 
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
     const int key0 = kt * PF_KT;
     const bool inside = key0 + PF_KT - 1 <= t0 &&
                         (ret || key0 + PF_KT - 1 < p.n_sink || key0 > tl - p.window);
-    bf16x8 pb[QB][2], pl[QB][2];
+    f16x8 ph[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // (rows past the chunk's end hold zero queries: finite, and never written)
@@ -335,18 +335,15 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
       const float alpha = fast_exp2(m[qb] - m_use);
       m[qb] = m_new;
       float ps = 0.f;
-      float pv[4][4];                                  // FP8: weight times the V scale
+      float pv[4][4];
       if constexpr (FP8) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          float pk = 0.f;
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            pv[kb][i] = fast_exp2(fmaf(sacc[kb][qb][i], c2k[kb], lvs[kb] - m_use));
-            pk += pv[kb][i];
+            pv[kb][i] = fast_exp2(fmaf(sacc[kb][qb][i], c2k[kb], -m_use));
+            ps += pv[kb][i];
           }
-          ps = fmaf(pk, ivs[kb], ps);
-        }
       } else {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -365,26 +362,21 @@ __global__ __launch_bounds__(PfShape<ROPE>::THREADS, ROPE ? 1 : 2) void prefill_
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const __bf16 h0 = (__bf16)pv[2 * ks][i], h1 = (__bf16)pv[2 * ks + 1][i];
-          pb[qb][ks][i] = h0;
-          pb[qb][ks][4 + i] = h1;
-          pl[qb][ks][i] = (__bf16)(pv[2 * ks][i] - (float)h0);
-          pl[qb][ks][4 + i] = (__bf16)(pv[2 * ks + 1][i] - (float)h1);
+          ph[qb][ks][i] = (_Float16)pv[2 * ks][i];
+          ph[qb][ks][4 + i] = (_Float16)pv[2 * ks + 1][i];
         }
     }
 
     // O^T += V^T P^T, each V^T fragment read one step ahead of its products
     // (the LDS read then overlaps the previous step's MFMAs: -3.5 %)
-    bf16x8 a_cur = vt_frag(S.v[buf], 0, 0, col, quad);
+    f16x8 a_cur = vt_frag(S.v[buf], 0, 0, col, quad);
 #pragma unroll
     for (int step = 0; step < 16; ++step) {
       const int db = step >> 1, ks = step & 1;
-      bf16x8 a_next = a_cur;
+      f16x8 a_next = a_cur;
       if (step + 1 < 16) a_next = vt_frag(S.v[buf], (step + 1) & 1, (step + 1) >> 1, col, quad);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a_cur, pb[qb][ks], o[db][qb]);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a_cur, pl[qb][ks], o[db][qb]);
+      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma(a_cur, ph[qb][ks], o[db][qb]);
       a_cur = a_next;
     }
 

@@ -5,20 +5,25 @@ Tolerance (from the arithmetic of the kernel), per query row:
   logit is within delta = 1e-5 * attn_scale * |q| * max_j |k_j| (the decode
   score bound in natural-log units); with RoPE the rotated query is split
   into two bf16 parts, which adds 2^-15 * attn_scale * |q| * max_j |k_j|;
-* the softmax weights enter the weighted sum of V as two bf16 parts,
-  hi = bf16(p) and lo = bf16(p - hi), whose sum is within 2^-18 of p
-  (relative; REL allows 2^-16), and a logit error delta moves a normalised
-  weight by at most 2 delta (relative); the fp32 sums over n keys (one
-  rounding per 32-key MFMA step, plus the online rescales) add at most
-  (n / 16 + 4) 2^-24 (relative).  Hence per element
+* the weighted sum of V runs in fp16 with fp32 accumulation: each weight p
+  in (0, 1] is rounded once to fp16 (within 2^-11 of p, relative: REL), V
+  values are exact in fp16 (bf16 values of magnitude 2^-14 .. 65504; the
+  workloads' values are far inside; a smaller one is off by at most 2^-25,
+  inside the 1e-5 term), a logit error delta moves a normalised weight by at
+  most 2 delta (relative), and the fp32 sums over n keys (one rounding per
+  32-key MFMA step, plus the online rescales) add at most (n / 16 + 4) 2^-24
+  (relative).  Hence per element
     |o_gpu - o_ref| <= (REL + 2 delta + (n / 16 + 4) 2^-24) * sum_j p_j |v_jd| + 1e-5,
   with p the oracle's weights (``with_abs_v``);
 * lse (summed from the unrounded weights): within 2e-5 + delta;
 * and, whatever that bound allows, max |o_gpu - o_ref| <= 2e-3 (the decode
   attention tolerance) on every row checked.
-FP8 cache: the products run on the e4m3 codes, exact in bf16, and the page
-scales multiply the logits and the weights in fp32, so the same bound holds
-with the stored (decoded) rows in place of k and v.
+FP8 cache: the K products run on the e4m3 codes, exact in bf16, and the page
+K scales multiply the logits in fp32; each V code is multiplied by its page's
+V scale in fp32 and rounded to fp16 (2^-11 relative, inside REL for the same
+reason as the weights' rounding: the bound below counts REL once per element,
+so it takes 2^-10 for fp8 V), so the same bound holds with the stored
+(decoded) rows in place of k and v.
 """
 
 import numpy as np
@@ -32,7 +37,8 @@ from head_wise_sparse_02_amd.runner import DecodeSetup, append_segments
 
 pytestmark = pytest.mark.gpu
 
-REL = 2.0 ** -16
+REL = 2.0 ** -11
+REL_FP8 = 2.0 ** -10      # fp8 V: the code times its scale is rounded to fp16 too
 ABS_CAP = 2e-3
 WORST_ABS = {"out": 0.0}
 
@@ -86,7 +92,8 @@ def _run(wl, n_tok, *, dense=False, rows=None, q_fn=None, stride=1, segments=Non
             o_gpu = out[b, rows, h * G:(h + 1) * G].astype(np.float64)
             err = np.abs(o_gpu - o_ref)
             acc = (n / 16 + 4) * 2.0 ** -24
-            bound = (REL + acc + 2 * delta[:, :, None]) * absv + 1e-5
+            fp8_rows = st.fp8 and not (st.ring and wl.head_kinds[h] == "local")
+            bound = ((REL_FP8 if fp8_rows else REL) + acc + 2 * delta[:, :, None]) * absv + 1e-5
             ratio = float((err / bound).max())
             worst = max(worst, ratio)
             worst_abs = max(worst_abs, float(err.max()))
