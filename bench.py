@@ -31,7 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_GBS = 8000.0          # MI355X HBM3E peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 STAGE_SOURCE = {"score": "k_score.hip", "attend": "k_attend.hip", "tail": "k_tail.hip", "fused": "k_tail.hip",
-                "fused_index": "k_tail.hip", "select": "k_tail.hip"}
+                "fused_index": "k_tail.hip", "select": "k_tail.hip", "attend_balanced": "k_attend.hip",
+                "merge": "k_attend.hip"}
 
 
 def stage_kernel(stage: str, wl) -> str:
@@ -41,7 +42,8 @@ def stage_kernel(stage: str, wl) -> str:
             return "score_index_kernel"
         return "score_full_g4_kernel" if (wl.G == 4 and not wl.rope_theta) else "score_full_kernel"
     return {"attend": "attend_kernel", "tail": "tail_kernel", "fused": "fused_g4_kernel",
-            "fused_index": "fused_index_kernel", "select": "select_single_kernel"}.get(stage, stage)
+            "fused_index": "fused_index_kernel", "select": "select_single_kernel",
+            "attend_balanced": "attend_balanced_kernel", "merge": "merge_kernel"}.get(stage, stage)
 
 
 def stage_bytes(stage: str, by: dict) -> int:
@@ -51,6 +53,8 @@ def stage_bytes(stage: str, by: dict) -> int:
         return by["total"]
     if stage == "tail":
         return by["attend"] + by["io"]
+    if stage == "attend_balanced":
+        return by["attend"]
     return by.get(stage, 0)
 
 

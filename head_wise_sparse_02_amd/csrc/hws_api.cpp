@@ -23,9 +23,9 @@ static_assert(PHASES == HWS_PHASES, "phase count of the profiling hook");
 
 namespace {
 
-constexpr int NUM_STAGES = 8;
+constexpr int NUM_STAGES = 9;
 const char* const STAGE_NAMES[NUM_STAGES] = {"score", "select", "attend", "merge", "tail", "fused", "prefill",
-                                             "fused_index"};
+                                             "fused_index", "attend_balanced"};
 
 struct EvPair {
   hipEvent_t a, b;
@@ -675,7 +675,7 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
       }
     }
   }
-  const StageEv ea = stage_events(ctx, 2);
+  const StageEv ea = stage_events(ctx, balanced ? 8 : 2);
   if (balanced) {
     p.pair_rows = reinterpret_cast<int*>(ws + L.pair_rows);
     p.row_list = reinterpret_cast<int2*>(ws + L.row_list);

@@ -42,13 +42,11 @@ __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
 
 // 8 fp32 values -> 8 fp16 bit patterns (round to nearest even), as a 16-byte chunk
 __device__ __forceinline__ u32x4 chunk_f16(const float (&x)[8]) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   u32x4 r;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const unsigned lo = __builtin_bit_cast(unsigned short, (_Float16)x[2 * k]);
-    const unsigned hi = __builtin_bit_cast(unsigned short, (_Float16)x[2 * k + 1]);
-    r[k] = lo | (hi << 16);
-  }
+  for (int k = 0; k < 4; ++k)
+    r[k] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x[2 * k], x[2 * k + 1]}, f16x2));
   return r;
 }
 

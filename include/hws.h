@@ -432,8 +432,9 @@ hws_status hws_set_wait_limit(hws_ctx* ctx, uint32_t max_polls, int32_t unreacha
  * names come from hws_profile_stage_name(i) ("" past the last stage):
  * score, select, attend, merge, tail (the single launch that replaces
  * select, attend and merge), fused (the single launch that also does the
- * full-dim scoring scan) and fused_index (the one that also does the r = 16
- * index scan). */
+ * full-dim scoring scan), prefill, fused_index (the single launch that also
+ * does the r = 16 index scan) and attend_balanced (the attention balanced by
+ * kept rows, in place of attend). */
 hws_status hws_profile_enable(hws_ctx* ctx, int32_t enable);
 hws_status hws_profile_read(hws_ctx* ctx, double* ms, int32_t* calls, int32_t n);
 const char* hws_profile_stage_name(int32_t i);

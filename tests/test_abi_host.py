@@ -178,7 +178,8 @@ def test_launch_mode_values():
     assert hws.lib().hws_profile_stage_name(5) == b"fused"
     assert hws.lib().hws_profile_stage_name(6) == b"prefill"
     assert hws.lib().hws_profile_stage_name(7) == b"fused_index"
-    assert hws.lib().hws_profile_stage_name(8) == b""
+    assert hws.lib().hws_profile_stage_name(8) == b"attend_balanced"
+    assert hws.lib().hws_profile_stage_name(9) == b""
 
 
 def test_wait_limit_values():

@@ -1,8 +1,8 @@
 """GPU: hws_decode_noalloc, the decode step whose workspace is the library's
 static device array, against hws_decode with a caller workspace.
 
-Two calls in a row through the C ABI share the array: the first leaves its
-selection state, partials and counters there and the second, smaller one
+Four calls in a row through the C ABI share the array: each leaves its
+selection state, partials and counters there, and the next, smaller one
 (fewer sequences, shorter contexts, another launch shape) must still match
 hws_decode bit for bit, because the step's own kernels reset what they read.
 (The refusal of a step beyond the array is a host check, tested without a GPU
@@ -49,7 +49,8 @@ def _both(wl, stage, mode=hws.HWS_LAUNCH_AUTO):
 def test_noalloc_matches_decode_then_smaller_call():
     # 1: the single launch with the scan inside (full-dim scores, G = 4), 2 x 40000
     _both(W.make_workload(3, n=40000, batch=2), "fused")
-    # 2: smaller, per-stage attention after the one-launch selection (index scores, local heads)
+    # 2: smaller, the one-launch selection, then the attention balanced by kept
+    #    rows (index scores, local heads)
     _both(W.make_workload(2, n=9000, batch=2), "select", hws.HWS_LAUNCH_SCAN_SELECT)
     # 3: smaller, the single launch with the index scan inside
     _both(W.make_workload(2, n=6000, batch=2), "fused_index")
