@@ -37,7 +37,7 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace regions of one decode call.
 struct Layout {
   size_t scores, agg, spart, sel, apart_ml, apart_o, qrot, tail_sync, tail_ties, total;
-  size_t row_list, tile_cnt, pair_rows, item_base, bal_ml, bal_o;   // attention balanced by kept rows
+  size_t row_list, tile_cnt, item_base, bal_ml, bal_o;   // attention balanced by kept rows
   int Nagg;
   int score_chunk, n_score_chunks, n_sel_chunks, ncR, ncL, att_chunk_R, max_splits;
   int tail_tph, tail_ntiles;
@@ -166,12 +166,12 @@ Layout make_layout(const hws_ctx* c, int B, int Nmax, bool rope, int score_mode,
   L.tail_ties = off; off = align_up(off + nRb * cdiv(Nmax, FI_TILE_MIN) * sizeof(unsigned int));
   // attention balanced by kept rows (index scores, one set per KV head)
   if (score_mode == HWS_SCORE_INDEX && GS == 1) {
-    // items: at most min(BAL_ITEMS, rows / BAL_RMIN) plus one per pair
+    // pieces: at most one per workgroup, min(BAL_ITEMS, cost units / BAL_RMIN),
+    // plus one per pair
     const size_t npairs = (size_t)B * c->cfg.num_kv_heads;
-    const size_t nitems = std::min<size_t>(BAL_ITEMS, (npairs * Nmax + BAL_RMIN - 1) / BAL_RMIN) + npairs;
+    const size_t nitems = std::min<size_t>(BAL_ITEMS, (npairs * ((size_t)Nmax + BAL_PIECE_COST) + BAL_RMIN - 1) / BAL_RMIN) + npairs;
     L.row_list = off;  off = align_up(off + nRb * Nmax * sizeof(int2));
     L.tile_cnt = off;  off = align_up(off + (size_t)L.tail_ntiles * sizeof(unsigned int));
-    L.pair_rows = off; off = align_up(off + nRb * sizeof(int));
     L.item_base = off; off = align_up(off + (npairs + 2) * sizeof(int));
     L.bal_ml = off;    off = align_up(off + nitems * G * sizeof(float2));
     L.bal_o = off;     off = align_up(off + nitems * G * D * sizeof(float));
@@ -654,6 +654,7 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
   // attention 35 us either way, selection 30 against 37, merge 9 against 14).
   const long long npairs = (long long)a->batch * c.num_kv_heads;
   const bool balanced = sel1 && a->score_mode == HWS_SCORE_INDEX && L.bal_o != 0 && npairs <= BAL_MAX_HEADS &&
+                        npairs * ((long long)a->max_seq_len + BAL_PIECE_COST) < (1LL << 31) && L.tail_tph <= BAL_MAX_TPH &&
                         (mode == HWS_LAUNCH_SCAN_SELECT || (mode == HWS_LAUNCH_AUTO && npairs >= BAL_AUTO_PAIRS));
   if (ctx->nR > 0) {
     const StageEv es = stage_events(ctx, 0);
@@ -664,7 +665,6 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
       if (balanced) {
         p.row_list = reinterpret_cast<int2*>(ws + L.row_list);
         p.tile_cnt = reinterpret_cast<unsigned int*>(ws + L.tile_cnt);
-        p.pair_rows = reinterpret_cast<int*>(ws + L.pair_rows);
       }
       if ((e = launch_tail(p, nws, false, s, ev.start, ev.stop, true)) != hipSuccess)
         return hip_fail(ctx, e, "select launch");
@@ -677,7 +677,6 @@ hws_status decode_step(hws_ctx* ctx, const hws_decode_args* a, void* stream, boo
   }
   const StageEv ea = stage_events(ctx, balanced ? 8 : 2);
   if (balanced) {
-    p.pair_rows = reinterpret_cast<int*>(ws + L.pair_rows);
     p.row_list = reinterpret_cast<int2*>(ws + L.row_list);
     p.item_base = reinterpret_cast<int*>(ws + L.item_base);
     p.bal_ml = reinterpret_cast<float2*>(ws + L.bal_ml);

@@ -22,13 +22,16 @@ constexpr int SEL_CHUNK = SEL_THREADS * SEL_PER_THREAD;   // 16384 tokens
 constexpr int HIST_BINS = 4096;   // pass 1 bins: bits 30..19 of the fp32 pattern
 constexpr int LOCAL_CHUNK = 256;  // rows per local-head attention workgroup
 constexpr int PHASES = 12;        // phase timestamps per workgroup (HWS_PHASES)
-// Attention balanced by kept rows: the rows of all heads are cut into about
-// At most BAL_ITEMS workgroups, each a segment of at least BAL_RMIN rows; a
-// segment leaves one partial per (sequence, KV head) piece it covers.
+// Attention balanced by kept rows: at most BAL_ITEMS workgroups, each a
+// segment of at least BAL_RMIN cost units (a pair of c rows costs
+// BAL_PIECE_COST + c); a segment leaves one partial per (sequence, KV head)
+// piece it covers.
 constexpr int BAL_ITEMS = 2048;
 constexpr int BAL_RMIN = 64;
+constexpr int BAL_PIECE_COST = 128;  // a piece's fixed cost in rows (its list, queries and partial)
 constexpr int BAL_AUTO_PAIRS = 64;   // AUTO balances the attention from this many (sequence, KV head) pairs
-constexpr int BAL_MAX_HEADS = 2048;  // (sequence, KV head) pairs the item table holds in LDS
+constexpr int BAL_MAX_HEADS = 2048;
+constexpr int BAL_MAX_TPH = 256;    // selection tiles per head the balanced attention maps rows over  // (sequence, KV head) pairs the item table holds in LDS
 
 // Single-launch tail (selection + attention + merge in one cooperative launch)
 constexpr int TAIL_THREADS = 512;
@@ -135,9 +138,9 @@ struct DecodeParams {
   // selection writes each retrieval head's kept rows as one list in position
   // order; the attention cuts every head's rows into items of about the same
   // number of rows.
-  int2* row_list;               // [B][nR][Nmax] (position, page) of the kept rows, or null
+  int2* row_list;               // [B][nR][Nmax] (position, page) of the kept rows, tile j's at
+                                //   j * TAIL_TILE.., or null
   unsigned int* tile_cnt;       // [tail_ntiles] kept rows of each selection tile
-  int* pair_rows;               // [B * nR] kept rows of each retrieval head
   int* item_base;               // [B * Hkv + 2] first listed row of each (sequence, KV head), the
                                 //   total, then the rows per workgroup of the balanced attention
   float2* bal_ml;               // [BAL_ITEMS + B * Hkv][G] (max, sum) of each piece

@@ -246,9 +246,9 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
   const float* po;                                      // split s at po[s * G * D]
   if (p.item_base != nullptr) {                         // balanced attention: this pair's pieces
     const int pi = b * p.Hkv + h;
-    const int r0 = p.item_base[pi], r1 = p.item_base[pi + 1], len = p.item_base[p.B * p.Hkv + 1];
-    const int w0 = r0 / len;
-    nspl = r1 > r0 ? (r1 - 1) / len - w0 + 1 : 0;
+    const int x0 = p.item_base[pi] + BAL_PIECE_COST, x1 = p.item_base[pi + 1], len = p.item_base[p.B * p.Hkv + 1];
+    const int w0 = x0 / len;                            // the workgroups holding its rows' cost units
+    nspl = x1 > x0 ? (x1 - 1) / len - w0 + 1 : 0;
     ml = p.bal_ml + (size_t)(w0 + pi) * G + g;
     po = p.bal_o + ((size_t)(w0 + pi) * G + g) * D + d;
   } else {
@@ -305,18 +305,21 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
 // ---------------------------------------------------------------------------
 // Attention balanced by kept rows ([ICS] §2: the sparsity is irregular per
 // token, query and head, so chunks cut by position leave a few dense ones as
-// the long pole).  The rows of all (sequence, KV head) pairs -- pair
-// i = b * Hkv + h has c_i rows, the kept rows the selection listed
-// (retrieval) or its sinks and window (local) -- are laid end to end in pair
-// order, C = sum c_i, and cut into equal segments of len rows, one per
-// workgroup: len = max(BAL_RMIN, C / grid rounded up to a whole batch).  A
-// workgroup walks the pairs its segment covers, loads each piece's
-// (position, page) list into LDS, gathers it with the next batch of loads in
-// flight, and stores one partial per piece.  Pieces form a monotone path
-// over (workgroup w, pair i), so w + i numbers them without gaps or
-// collisions; pair i's partials are w_first(i) + i .. w_last(i) + i.
-// Workgroup 0 writes the pair offsets and len for the merge.  Index scores
-// only (the rows carry K and V), one set per KV head.
+// the long pole).  The (sequence, KV head) pairs -- pair i = b * Hkv + h has
+// c_i rows, the kept rows the selection listed (retrieval; tile j's rows at
+// j * TAIL_TILE in the head's list) or its sinks and window (local) -- are
+// laid end to end in pair order in cost units, pair i
+// costing BAL_PIECE_COST + c_i (its rows take the last c_i units), and the
+// total is cut into equal segments, one per resident workgroup: so a segment
+// that covers several pairs, each a piece with its own list, queries and
+// partial, gathers fewer rows.  A workgroup walks its pieces, loads each
+// piece's (position, page) list into LDS, gathers it with the next batch of
+// loads in flight, and stores one partial per piece.  Pieces form a monotone
+// path over (workgroup w, pair i), so w + i numbers them without collisions;
+// pair i's partials are w_first(i) + i .. w_last(i) + i, the workgroups that
+// hold its first and last row.  Workgroup 0 writes the pair offsets and the
+// segment length for the merge.  Index scores only (the rows carry K and V),
+// one set per KV head.
 // ---------------------------------------------------------------------------
 constexpr int BAL_THREADS = 256;
 constexpr int BAL_LIST = 1024;                // rows per (position, page) list in LDS
@@ -354,11 +357,16 @@ __device__ int block_scan_excl(int* x, int n, int* tmp) {
   return total;
 }
 
-// Rows of pair (b, h): the kept rows the selection listed, or the sinks and
-// window.
+// Rows of pair (b, h): the kept rows the selection listed (the sum over the
+// head's selection tiles), or the sinks and window.
 __device__ __forceinline__ int pair_row_count(const DecodeParams& p, int b, int h) {
   const int hr = p.ret_slot[h];
-  if (hr >= 0) return p.pair_rows[(size_t)b * p.nR + hr];
+  if (hr >= 0) {
+    const unsigned int* tc = p.tile_cnt + ((size_t)b * p.nR + hr) * p.tail_tph;
+    int c = 0;
+    for (int j = 0; j < p.tail_tph; ++j) c += (int)tc[j];
+    return c;
+  }
   const int N = min(p.seq_lens[b], p.Nmax);
   const int L1 = min(p.n_sink, N);
   return L1 + (N - max(L1, N - p.window));
@@ -379,9 +387,14 @@ __device__ __forceinline__ void load_group_q(const DecodeParams& p, int b, int h
 }
 
 // RING_BF16: fp8 pools with the local heads in a (bf16) ring.  MARK: count
-// the rows read (debug).
+// the rows read (debug).  The fp8 gather at G <= 4 is held to 3 waves per
+// SIMD (it fits in 168 registers; one wave more in flight per SIMD).
 template <int G, bool FP8, bool RING_BF16, bool MARK>
-__global__ __launch_bounds__(BAL_THREADS) void attend_balanced_kernel(DecodeParams p) {
+struct BalWaves { static constexpr int value = (FP8 && G <= 4 && !RING_BF16 && !MARK) ? 3 : 1; };
+
+template <int G, bool FP8, bool RING_BF16, bool MARK>
+__global__ __launch_bounds__(BAL_THREADS) __attribute__((amdgpu_waves_per_eu(BalWaves<G, FP8, RING_BF16, MARK>::value)))
+void attend_balanced_kernel(DecodeParams p) {
   constexpr int RB = AttRB<G, 0>::value;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int proc = tid >> 4, sub = tid & 15;
@@ -389,12 +402,17 @@ __global__ __launch_bounds__(BAL_THREADS) void attend_balanced_kernel(DecodePara
   __shared__ int base_s[BAL_TABLE + 1];
   __shared__ int tmp[8];
   __shared__ int tok_s[BAL_LIST], pg_s[BAL_LIST];
+  __shared__ int tpre_s[BAL_MAX_TPH + 1];       // retrieval piece: kept rows before each selection tile
   __shared__ float wm[4][MAX_G], wl[4][MAX_G];
   __shared__ float wo[4][MAX_G][D];
 
   stamp_phase(p, 0);
-  // ---- pair offsets (the same in every workgroup) ----
-  for (int i = tid; i < npairs; i += BAL_THREADS) base_s[i] = pair_row_count(p, i / p.Hkv, i % p.Hkv);
+  // ---- pair offsets in cost units (the same in every workgroup): a pair
+  // with c rows costs BAL_PIECE_COST + c, its rows taking the last c units ----
+  for (int i = tid; i < npairs; i += BAL_THREADS) {
+    const int c = pair_row_count(p, i / p.Hkv, i % p.Hkv);
+    base_s[i] = c > 0 ? c + BAL_PIECE_COST : 0;
+  }
   __syncthreads();
   const int C = block_scan_excl(base_s, npairs, tmp);
   if (tid == 0) base_s[npairs] = C;
@@ -405,25 +423,52 @@ __global__ __launch_bounds__(BAL_THREADS) void attend_balanced_kernel(DecodePara
     for (int i = tid; i <= npairs; i += BAL_THREADS) p.item_base[i] = base_s[i];
     if (tid == 0) p.item_base[npairs + 1] = len;
   }
-  int g0 = (int)blockIdx.x * len;
-  const int g1 = min(C, g0 + len);
+  const int x0 = (int)blockIdx.x * len;
+  const int x1 = min(C, x0 + len);
   stamp_phase(p, 1);
-  if (g0 >= g1) return;
-  // the pair holding row g0: the last i with base_s[i] <= g0 (empty pairs skipped)
+  if (x0 >= x1) return;
+  // the pair holding cost unit x0: the last i with base_s[i] <= x0 (empty pairs skipped)
   int pi = 0;
   {
     int lo_i = 0, hi_i = npairs;
     while (hi_i - lo_i > 1) {
       const int mid = (lo_i + hi_i) >> 1;
-      if (base_s[mid] <= g0) lo_i = mid; else hi_i = mid;
+      if (base_s[mid] <= x0) lo_i = mid; else hi_i = mid;
     }
     pi = lo_i;
   }
-  while (base_s[pi + 1] <= g0) ++pi;
-  // the current piece: pair pi, its queries and running (m, l, o)
-  float qf[G][8], m[G], l[G], o[G][8];
-  auto start_piece = [&]() {
-    load_group_q<G>(p, pi / p.Hkv, pi % p.Hkv, sub, qf);
+  for (int x = x0; x < x1; ++pi) {
+    if (base_s[pi + 1] <= x) continue;              // empty pair
+    const int rb = base_s[pi] + BAL_PIECE_COST;     // cost unit of the pair's row 0
+    if (x1 <= rb) break;                            // the segment ends before the pair's rows
+    const int r0 = max(x, rb) - rb, r1 = min(x1, base_s[pi + 1]) - rb;
+    x = base_s[pi + 1];
+    // ---- one piece: rows r0..r1-1 of pair pi ----
+    const int b = pi / p.Hkv, h = pi % p.Hkv, hr = p.ret_slot[h];
+    const int N = min(p.seq_lens[b], p.Nmax);
+    const int L1 = min(p.n_sink, N), start2 = max(L1, N - p.window);
+    const bool ring = hr < 0 && p.ring_rows > 0;
+    GatherSrc src;
+    src.kpool = ring ? p.lk_pool : p.k_pool;
+    src.vpool = ring ? p.lv_pool : p.v_pool;
+    src.scales = p.kv_scales;
+    src.hstride = ring ? 1 : p.Hp;
+    src.hslot = ring ? 0 : p.pool_slot[h];
+    src.plim = ring ? (unsigned)p.ring_pages : (unsigned)p.num_blocks;
+    const int2* list = hr >= 0 ? p.row_list + ((size_t)b * p.nR + hr) * p.Nmax : nullptr;
+    const int tph = p.tail_tph;
+    if (hr >= 0) {                                  // where each tile's rows start in the pair's order
+      const unsigned int* tc = p.tile_cnt + ((size_t)b * p.nR + hr) * tph;
+      for (int j = tid; j < tph; j += BAL_THREADS) tpre_s[j + 1] = (int)tc[j];
+      __syncthreads();
+      if (tid == 0) {
+        tpre_s[0] = 0;
+        for (int j = 1; j <= tph; ++j) tpre_s[j] += tpre_s[j - 1];
+      }
+      __syncthreads();
+    }
+    float qf[G][8], m[G], l[G], o[G][8];
+    load_group_q<G>(p, b, h, sub, qf);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       m[g] = NEG_INF;
@@ -431,92 +476,63 @@ __global__ __launch_bounds__(BAL_THREADS) void attend_balanced_kernel(DecodePara
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
     }
-  };
-  start_piece();
-  // the segment's (position, page) list, BAL_LIST rows at a time, each chunk
-  // filled for all the pieces it holds in one round of loads
-  for (int cs = g0; cs < g1; cs += BAL_LIST) {
-    const int ce = min(g1, cs + BAL_LIST);
-    for (int pf = pi, gg = cs; gg < ce; ++pf) {
-      if (base_s[pf + 1] <= gg) continue;           // empty pair
-      const int pe = min(ce, base_s[pf + 1]);
-      const int b = pf / p.Hkv, h = pf % p.Hkv, hr = p.ret_slot[h];
-      const int N = min(p.seq_lens[b], p.Nmax);
-      const int L1 = min(p.n_sink, N), start2 = max(L1, N - p.window);
-      const int2* list = hr >= 0 ? p.row_list + ((size_t)b * p.nR + hr) * p.Nmax : nullptr;
-      for (int q = tid; q < pe - gg; q += BAL_THREADS) {
-        const int r = gg - base_s[pf] + q;          // row of the pair
-        int* tk = tok_s + (gg - cs) + q;
-        int* pg = pg_s + (gg - cs) + q;
-        if (hr >= 0) {
-          const int2 e = list[r];
-          *tk = e.x;
-          *pg = e.y;
+    for (int rs = r0; rs < r1; rs += BAL_LIST) {
+      const int nl = min(BAL_LIST, r1 - rs);
+      for (int q = tid; q < nl; q += BAL_THREADS) {
+        const int r = rs + q;
+        if (hr >= 0) {                              // row r lies in tile j: the last with tpre_s[j] <= r
+          int lo_j = 0, hi_j = tph;
+          while (hi_j - lo_j > 1) {
+            const int mid = (lo_j + hi_j) >> 1;
+            if (tpre_s[mid] <= r) lo_j = mid; else hi_j = mid;
+          }
+          const int2 e = list[(size_t)lo_j * TAIL_TILE + (r - tpre_s[lo_j])];
+          tok_s[q] = e.x;
+          pg_s[q] = e.y;
         } else {
-          local_row_at(p, b, p.loc_slot[h], r < L1 ? r : start2 + (r - L1), *tk, *pg);
-        }
-      }
-      gg = pe;
-    }
-    __syncthreads();
-    stamp_phase(p, 8);
-    for (int gg = cs; gg < ce;) {
-      const int pe = min(ce, base_s[pi + 1]);
-      const int b = pi / p.Hkv, h = pi % p.Hkv, hr = p.ret_slot[h];
-      const bool ring = hr < 0 && p.ring_rows > 0;
-      GatherSrc src;
-      src.kpool = ring ? p.lk_pool : p.k_pool;
-      src.vpool = ring ? p.lv_pool : p.v_pool;
-      src.scales = p.kv_scales;
-      src.hstride = ring ? 1 : p.Hp;
-      src.hslot = ring ? 0 : p.pool_slot[h];
-      src.plim = ring ? (unsigned)p.ring_pages : (unsigned)p.num_blocks;
-      const int* tk = tok_s + (gg - cs);
-      const int* pg = pg_s + (gg - cs);
-      if (RING_BF16 && ring) {                      // the ring holds bf16 rows (not counted)
-        gather_pipelined<G, false, RB>(src, tk, pg, pe - gg, proc, sub, qf, m, l, o);
-      } else {
-        int* rr = MARK ? p.rows_read + (size_t)(b * p.Hkv + h) * p.Nmax : nullptr;
-        gather_pipelined<G, FP8, RB, MARK>(src, tk, pg, pe - gg, proc, sub, qf, m, l, o, rr);
-      }
-      gg = pe;
-      if (pe < base_s[pi + 1] && pe < g1) continue;   // the piece goes on in the next chunk
-      // the piece ends: its partial at slot w + i
-      combine_wave_procs<G>(m, l, o);
-      if (lane < 16) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) wo[wave][g][8 * sub + j] = o[g][j];
+          local_row_at(p, b, p.loc_slot[h], r < L1 ? r : start2 + (r - L1), tok_s[q], pg_s[q]);
         }
       }
       __syncthreads();
-      const size_t slot = (size_t)blockIdx.x + pi;
-      float2* ml = p.bal_ml + slot * G;
-      float* po = p.bal_o + slot * G * D;
-      for (int e = tid; e < G * D; e += BAL_THREADS) {
-        const int g = e / D, d = e % D;
-        float mm = NEG_INF;
-        for (int k = 0; k < 4; ++k) mm = fmaxf(mm, wm[k][g]);
-        float ll = 0.f, oo = 0.f;
-        for (int k = 0; k < 4; ++k) {
-          if (wm[k][g] == NEG_INF) continue;
-          const float cf = fast_exp2(wm[k][g] - mm);
-          ll += wl[k][g] * cf;
-          oo += wo[k][g][d] * cf;
-        }
-        po[(size_t)g * D + d] = oo;
-        if (d == 0) ml[g] = make_float2(mm, ll);
+      stamp_phase(p, 8);
+      if (RING_BF16 && ring) {                      // the ring holds bf16 rows (not counted)
+        gather_pipelined<G, false, RB>(src, tok_s, pg_s, nl, proc, sub, qf, m, l, o);
+      } else {
+        int* rr = MARK ? p.rows_read + (size_t)(b * p.Hkv + h) * p.Nmax : nullptr;
+        gather_pipelined<G, FP8, RB, MARK>(src, tok_s, pg_s, nl, proc, sub, qf, m, l, o, rr);
       }
-      __syncthreads();                              // wm / wo are reused by the next piece
-      if (pe >= g1) break;
-      ++pi;
-      while (base_s[pi + 1] <= pe) ++pi;            // empty pairs
-      start_piece();
+      __syncthreads();                              // the list is reused
+      stamp_phase(p, 9);
     }
-    __syncthreads();                                // the list is reused
-    stamp_phase(p, 9);
+    // the piece's partial at slot w + i
+    combine_wave_procs<G>(m, l, o);
+    if (lane < 16) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (lane == 0) { wm[wave][g] = m[g]; wl[wave][g] = l[g]; }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wo[wave][g][8 * sub + j] = o[g][j];
+      }
+    }
+    __syncthreads();
+    const size_t slot = (size_t)blockIdx.x + pi;
+    float2* ml = p.bal_ml + slot * G;
+    float* po = p.bal_o + slot * G * D;
+    for (int e = tid; e < G * D; e += BAL_THREADS) {
+      const int g = e / D, d = e % D;
+      float mm = NEG_INF;
+      for (int k = 0; k < 4; ++k) mm = fmaxf(mm, wm[k][g]);
+      float ll = 0.f, oo = 0.f;
+      for (int k = 0; k < 4; ++k) {
+        if (wm[k][g] == NEG_INF) continue;
+        const float cf = fast_exp2(wm[k][g] - mm);
+        ll += wl[k][g] * cf;
+        oo += wo[k][g][d] * cf;
+      }
+      po[(size_t)g * D + d] = oo;
+      if (d == 0) ml[g] = make_float2(mm, ll);
+    }
+    __syncthreads();                                // wm / wo are reused by the next piece
   }
   stamp_phase(p, 10);
 }

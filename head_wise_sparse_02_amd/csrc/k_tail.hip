@@ -769,11 +769,10 @@ __global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
 // Selection only: a_i of every token (written to agg), the threshold and the
 // top-k tie quota of every retrieval head (written to its state), in one
 // launch; the attention and merge follow.  With p.row_list set (the attention
-// balanced by kept rows follows), the tiles of a head also exchange their
-// kept counts (each tile publishes before it waits, so no cycle forms) and
-// every tile writes its kept rows, (position, page) in position order, at its
-// offset in the head's list; the head's last tile writes the head's total,
-// and top-p sets are counted here.
+// balanced by kept rows follows), every tile also writes its kept rows,
+// (position, page) in position order, into its own region of the head's list
+// and their count to tile_cnt (no exchange between tiles), and top-p sets are
+// counted here.
 template <int G>
 __global__ __launch_bounds__(TT) void select_single_kernel(DecodeParams p) {
   __shared__ TailLds S;
@@ -784,55 +783,26 @@ __global__ __launch_bounds__(TT) void select_single_kernel(DecodeParams p) {
   unsigned int* err = p.tail_sync;
   select_tiles<G>(p, S, tl, keepm, my_tiles, err);
   if (p.row_list == nullptr) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // ---- publish every tile's kept count, then arrive ----
-#pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
-    if (tl[k].t < 0) continue;                        // uniform
-    unsigned int c = (unsigned int)__popc(keepm[k]);
-    for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off);
-    __syncthreads();
-    if (lane == 0) S.tmp[wave] = c;
-    __syncthreads();
-    if (tid == 0) {
-      unsigned int tot = 0u;
-      for (int w2 = 0; w2 < TW; ++w2) tot += S.tmp[w2];
-      __hip_atomic_store(&p.tile_cnt[tl[k].t], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  wait_memory_ops();
-  __syncthreads();
-  if (tid == 0) {
-#pragma unroll
-    for (int k = 0; k < MAXT; ++k)
-      if (tl[k].t >= 0) atomicAdd(&p.sel[(size_t)tl[k].b * p.nR + tl[k].hr].cnt_arrive, 1u);
-  }
-  // ---- each tile: its offset in the head's list, then its rows ----
+  const int tid = threadIdx.x;
+  // ---- each tile: its kept rows, (position, page) in position order, at the
+  // start of its own region of the head's list (region j holds positions
+  // j * TAIL_TILE ..), and their count ----
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) {
     if (tl[k].t < 0) continue;
     SelState* st = p.sel + (size_t)tl[k].b * p.nR + tl[k].hr;
-    block_wait(p, &st->cnt_arrive, (unsigned int)p.tail_tph, err);
-    if (tid == 0) {
-      unsigned int before = 0u;
-      const int t0 = tl[k].t - tl[k].j;
-      for (int jj = 0; jj < tl[k].j; ++jj) before += load_u32_coherent(&p.tile_cnt[t0 + jj]);
-      S.tmp[TW] = before;
-    }
-    __syncthreads();
-    const unsigned int off = S.tmp[TW];
+    __syncthreads();                                  // S.u of the previous tile is free
     const int nrows = compact_rows<false>(S, keepm[k]);
     __syncthreads();
-    int2* dst = p.row_list + ((size_t)tl[k].b * p.nR + tl[k].hr) * p.Nmax + off;
+    int2* dst = p.row_list + ((size_t)tl[k].b * p.nR + tl[k].hr) * p.Nmax + tl[k].lo;
     for (int r = tid; r < nrows; r += TT) {
       const int o16 = S.u.rows[r];
       dst[r] = make_int2(tl[k].lo + o16, S.pages[k][o16 >> 4]);
     }
     if (tid == 0) {
-      if (tl[k].j == p.tail_tph - 1) p.pair_rows[(size_t)tl[k].b * p.nR + tl[k].hr] = (int)off + nrows;
+      p.tile_cnt[tl[k].t] = (unsigned int)nrows;
       if (p.select_mode == 0 && nrows > 0) atomicAdd(&st->nsel, (unsigned int)nrows);
     }
-    __syncthreads();                                  // S.u and S.tmp are reused by the next tile
   }
 }
 
