@@ -263,10 +263,15 @@ __global__ __launch_bounds__(D * MERGE_GROUPS) void merge_kernel(DecodeParams p)
     float ov[SB];
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
+      // unconditional loads (clamped split, masked after): a load behind a
+      // per-lane branch would be waited for before the next one is issued
       const int sp = s0 + u * MERGE_GROUPS;
       const bool in = sp < nspl;
-      v[u] = in ? ml[(size_t)sp * G] : make_float2(NEG_INF, 0.f);
-      ov[u] = in ? po[(size_t)sp * G * D] : 0.f;
+      const int spc = min(sp, nspl - 1);
+      const float2 mv = ml[(size_t)spc * G];
+      const float pv = po[(size_t)spc * G * D];
+      v[u] = in ? mv : make_float2(NEG_INF, 0.f);
+      ov[u] = in ? pv : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < SB; ++u) merge_fold(M, L, O, v[u].x, v[u].y, ov[u]);

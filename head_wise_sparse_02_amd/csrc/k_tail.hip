@@ -658,7 +658,9 @@ __device__ __forceinline__ void select_tiles(const DecodeParams& p, TailLds& S, 
     const float c2 = p.c2_score;
     const float invG = 1.0f / (float)G;
     const float* sc = p.scores + row * p.Nmax * G;
-    float* agg = (p.sel_idx != nullptr || p.agg_out) ? p.agg + row * p.Nagg : nullptr;
+    // a_i goes out for the sel_idx output and for the per-stage attention
+    // (the balanced attention reads the kept lists instead)
+    float* agg = (p.sel_idx != nullptr || (p.agg_out && p.row_list == nullptr)) ? p.agg + row * p.Nagg : nullptr;
     // loads of UB tokens in flight at once; positions past the end re-read
     // the last token and are masked, so no load sits behind a per-lane branch
     constexpr int UB = G <= 2 ? 32 : (G == 4 ? 16 : 8);
@@ -769,7 +771,8 @@ __global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
 // Selection only: a_i of every token (written to agg), the threshold and the
 // top-k tie quota of every retrieval head (written to its state), in one
 // launch; the attention and merge follow.  With p.row_list set (the attention
-// balanced by kept rows follows), every tile also writes its kept rows,
+// balanced by kept rows follows, and agg is written only for the sel_idx
+// output), every tile writes its kept rows,
 // (position, page) in position order, into its own region of the head's list
 // and their count to tile_cnt (no exchange between tiles), and top-p sets are
 // counted here.
