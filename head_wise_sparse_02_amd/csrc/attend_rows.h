@@ -380,6 +380,29 @@ __device__ __forceinline__ void fold_batch(const RawBatch<FP8, RB>& rb, const fl
   }
 }
 
+// The group's queries, dims 8*sub..8*sub+7, pre-scaled to log2 units: the
+// rotated fp32 queries when RoPE is on (K rows are stored rotated), else the
+// bf16 queries.
+template <int G>
+__device__ __forceinline__ void load_group_q(const DecodeParams& p, int b, int h, int sub, float (&qf)[G][8]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const size_t qo = ((size_t)b * p.Hq + h * G + g) * D + 8 * sub;
+    if (p.qrot != nullptr) {
+      const float4 a = *reinterpret_cast<const float4*>(p.qrot + qo);
+      const float4 c = *reinterpret_cast<const float4*>(p.qrot + qo + 4);
+      qf[g][0] = a.x; qf[g][1] = a.y; qf[g][2] = a.z; qf[g][3] = a.w;
+      qf[g][4] = c.x; qf[g][5] = c.y; qf[g][6] = c.z; qf[g][7] = c.w;
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4*>(p.q + qo);
+      qf[g][0] = bf16_lo(u.x); qf[g][1] = bf16_hi(u.x); qf[g][2] = bf16_lo(u.y); qf[g][3] = bf16_hi(u.y);
+      qf[g][4] = bf16_lo(u.z); qf[g][5] = bf16_hi(u.z); qf[g][6] = bf16_lo(u.w); qf[g][7] = bf16_hi(u.w);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qf[g][j] *= p.c2_attn;
+  }
+}
+
 // Rows 0..nrows-1 of the LDS list into (m, l, o) of processor `proc`
 // (continuing the values it holds).  qf: the group's queries in log2 units.
 // MARK: count every row read in rr[position] (debug; not for ring rows).

@@ -377,19 +377,7 @@ __device__ __forceinline__ int pair_row_count(const DecodeParams& p, int b, int 
   return L1 + (N - max(L1, N - p.window));
 }
 
-// The group's queries, dims 8*sub..8*sub+7, pre-scaled to log2 units.
-template <int G>
-__device__ __forceinline__ void load_group_q(const DecodeParams& p, int b, int h, int sub, float (&qf)[G][8]) {
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const size_t qo = ((size_t)b * p.Hq + h * G + g) * D + 8 * sub;
-    const uint4 u = *reinterpret_cast<const uint4*>(p.q + qo);
-    qf[g][0] = bf16_lo(u.x); qf[g][1] = bf16_hi(u.x); qf[g][2] = bf16_lo(u.y); qf[g][3] = bf16_hi(u.y);
-    qf[g][4] = bf16_lo(u.z); qf[g][5] = bf16_hi(u.z); qf[g][6] = bf16_lo(u.w); qf[g][7] = bf16_hi(u.w);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qf[g][j] *= p.c2_attn;
-  }
-}
+
 
 // RING_BF16: fp8 pools with the local heads in a (bf16) ring.  MARK: count
 // the rows read (debug).  The fp8 gather at G <= 4 is held to 3 waves per

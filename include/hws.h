@@ -378,9 +378,9 @@ hws_status hws_prefill(hws_ctx* ctx, const hws_prefill_args* args, void* stream)
  *    launch of the single-launch kind, then the attention and merge: with
  *    index scores the attention balanced by kept rows (the selection lists
  *    each head's kept rows; the rows of all heads, kept or sinks + window,
- *    laid end to end, are cut into one equal segment per resident
- *    workgroup, for up to 2048 (sequence, KV head) pairs), else the
- *    per-stage attention.
+ *    laid end to end with a fixed charge per head, are cut into one equal
+ *    segment per resident workgroup, for up to 2048 (sequence, KV head)
+ *    pairs), else the per-stage attention.
  *    The grid is sized to what the device holds at once (compute units x
  *    occupancy) and launched as an ordinary dispatch: it relies on this
  *    process having the device's compute units (no CU masking); a kernel

@@ -287,13 +287,19 @@ SCAN_SELECT = hws.HWS_LAUNCH_SCAN_SELECT
     (2, dict(n=3000, batch=3, select_mode="top_k", top_k=np.array([1, 37, 5000], np.int32))),
     (4, dict(n=60000)),
     (5, dict(n=30000, batch=8)),
-], ids=["tiny", "g1", "g2-batch", "layer", "layer-fp8-ring", "topk-edges", "long-g8", "ragged-fp8"])
+    (2, dict(n=300, batch=16, select_mode="top_k", top_k=np.full(16, 1, np.int32), window=40)),
+    (2, dict(n=5000, batch=3, rope_theta=10000.0)),
+    (5, dict(n=20000, batch=4, rope_theta=10000.0)),
+], ids=["tiny", "g1", "g2-batch", "layer", "layer-fp8-ring", "topk-edges", "long-g8", "ragged-fp8",
+        "many-small-pairs", "layer-rope", "ragged-fp8-rope"])
 def test_balanced_attention_against_oracle(cfg, kw):
     """The attention balanced by kept rows (equal row segments over all
     heads, the next batch of loads in flight) against the oracle: group sizes
     1 to 8, bf16 and fp8 pools, a bf16 local ring beside an fp8 cache, top-k
     sets of one row and of the whole context, a single retrieval head spread
-    over most workgroups (G = 8), ragged fp8 sequences."""
+    over most workgroups (G = 8), ragged fp8 sequences, 128 pairs of one or a
+    few dozen rows (segments that end inside a pair's fixed cost), and RoPE
+    (the rotated queries against the rotated K rows)."""
     wl = W.make_workload(cfg, **kw)
     _, res, _ = _run(wl, launch=SCAN_SELECT, verbose=False)
     assert res["status"] == 0
