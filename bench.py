@@ -73,6 +73,10 @@ def parse_args(argv=None):
                     help="retrieval heads keep a fixed top-k: a count, or a fraction of the context if < 1")
     ap.add_argument("--top-p", type=float, default=None,
                     help="retrieval heads keep the top-p set of this mass (every sequence)")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default=None,
+                    help="KV cache storage, overriding the workload's (fp8: e4m3 with per-page scales)")
+    ap.add_argument("--rope-theta", type=float, default=None,
+                    help="rotate-half RoPE with this base (K stored rotated, queries rotated at N-1)")
     ap.add_argument("--cold-iters", type=int, default=100,
                     help="graph replays each preceded by an untimed 1 GiB cache flush (0 = skip)")
     ap.add_argument("--launch", choices=["auto", "single", "multi", "cooperative", "scan-select", "scan-single"],
@@ -335,6 +339,12 @@ def build_workload(args, W):
         wl.top_p = np.full(wl.B, args.top_p, np.float32)
         wl.top_k = np.zeros(wl.B, np.int32)
         tags.append(f"topp{args.top_p:g}")
+    if args.kv is not None and args.kv != wl.kv_dtype:
+        wl.kv_dtype = args.kv
+        tags.append(args.kv)
+    if args.rope_theta:
+        wl.rope_theta = float(args.rope_theta)
+        tags.append(f"rope{args.rope_theta:g}")
     if tags:
         wl.name = wl.name + "_" + "_".join(tags)
     return wl
@@ -567,7 +577,7 @@ def main(argv=None) -> int:
                    "context": int(max(wl.seq_lens)), "score_mode": wl.score_mode,
                    "select_mode": wl.select_mode, "kv_dtype": wl.kv_dtype, "launch": args.launch,
                    "select_scope": wl.select_scope, "index_dtype": wl.index_dtype,
-                   "local_ring": wl.local_ring,
+                   "local_ring": wl.local_ring, "rope_theta": wl.rope_theta,
                    "top_k": sorted({int(x) for x in wl.top_k}) if wl.select_mode == "top_k" else None,
                    "top_p": sorted({round(float(x), 4) for x in wl.top_p}) if wl.select_mode == "top_p" else None},
         "kv_cache_bytes": int(sum(t.numel() * t.element_size() for t in (

@@ -9,6 +9,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // K pages are stored blocked by 32 dims: element (row r, dim d) of a page
 // (16 rows x 128 dims) sits at ((d / 32) * 16 + r) * 32 + d % 32.  One
@@ -20,6 +21,22 @@ __device__ __forceinline__ int kpage_off(int r, int d) { return (((d >> 5) << 4)
 // 16-byte load that does not allocate in the caches (data streamed once).
 __device__ __forceinline__ u32x4 load_nt16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// 8-byte load that does not allocate in the caches (data streamed once).
+__device__ __forceinline__ u32x2 load_nt8(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+// 8 e4m3 codes -> 8 bf16, element e from byte e (exact: every e4m3 value is a
+// bf16 value, and the conversion's scale operand is 1).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 constexpr float LOG2E = 1.4426950408889634f;

@@ -810,16 +810,23 @@ __global__ __launch_bounds__(TT) void select_single_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused decode: full-dim scores, G = 4, bf16 cache, unrotated queries.  The
-// scoring scan runs inside the same launch, one tile per workgroup, and the
-// tile's 16384 x 4 scores stay in registers: wave w scans pages
-// w*128 .. w*128+127 of the tile, four at a time (the MFMA layout of the
-// scoring kernel: lane quad u takes page u, so each lane owns one token of
-// every 4-page group, 32 tokens in all).  The log-sum-exp of every query
-// head is exchanged between the tiles of the head like a radix pass; then
-// a_i, the passes, the compaction and the attention follow as in the tail.
-// Only the kept tokens' scores are written out (the attention reads its
-// logits from there), unless all scores were asked for.
+// Fused decode: full-dim scores, G = 4.  The scoring scan runs inside the
+// same launch, one tile per workgroup, and the tile's 16384 x 4 scores stay
+// in registers: wave w scans pages w*128 .. w*128+127 of the tile, four at a
+// time (the MFMA layout of the scoring kernel: lane quad u takes page u, so
+// each lane owns one token of every 4-page group, 32 tokens in all).  The
+// query rows of the A operand repeat the group's four heads four times.
+// FP8: e4m3 pages widened to bf16 codes (exact), two groups of loads in
+// flight (the bytes of one bf16 group), each page's products times its K
+// scale.  SPLITQ (rotated fp32 queries): rows 0-3 carry each query's bf16
+// part and rows 4-7 the bf16 rounding of the rest, so a page's MFMAs give
+// both products and the lanes of quads 2k and 2k+1 add them with one swap.
+// The scores equal the per-stage scan's bit for bit (the same products,
+// additions and scaling).  The log-sum-exp of every query head is exchanged
+// between the tiles of the head like a radix pass; then a_i, the passes, the
+// compaction and the attention follow as in the tail.  Only the kept
+// tokens' scores are written out (the attention reads its logits from
+// there), unless all scores were asked for.
 // ---------------------------------------------------------------------------
 constexpr int FPW = TAIL_TILE / BS / TW;     // pages per wave: 128
 static_assert(FPW == 4 * TPT, "a lane owns one token of every 4-page group");
@@ -827,7 +834,7 @@ static_assert(FPW == 4 * TPT, "a lane owns one token of every 4-page group");
 constexpr int FUSED_LOGITS = 2048;          // kept rows whose logits stay in LDS
 constexpr int FUSED_RB = 12;                 // rows per processor per gather batch
 
-template <int MODE>
+template <int MODE, bool FP8, bool SPLITQ>
 __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f32x4* logits, unsigned int* err) {
   constexpr int G = 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -856,7 +863,18 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
 
   // ---- scoring scan: x[u] = the 4 raw scores q_g . k of this lane's token u ----
   bf16x8 afrag[4];
-  {
+  if constexpr (SPLITQ) {
+    const float* qg = p.qrot + ((size_t)b * p.Hq + h * G + (row & 3)) * D + 8 * quad;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xq = qg[32 * s2 + e];
+        const float hiq = bf16_to_f32(f32_to_bf16_rne(xq));
+        afrag[s2][e] = (__bf16)((row & 4) ? xq - hiq : hiq);
+      }
+    }
+  } else {
     const uint16_t* qg = p.q + ((size_t)b * p.Hq + h * G + (row & 3)) * D + 8 * quad;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) afrag[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qg + 32 * s2));
@@ -876,6 +894,85 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   float m[G], sm[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) { m[g] = NEG_INF; sm[g] = 0.f; }
+  // SPLITQ: lane quad q holds page q's bf16-part products (q even) or its
+  // rest products (q odd); it swaps the other kind of page q ^ 1 with its
+  // partner lane (lane ^ 16), and hi + lo is added in either lane
+  auto fold_split = [&](f32x4& v, const f32x4 (&acc)[4]) {
+    f32x4 w2 = acc[1];
+    w2 = quad == 1 ? acc[0] : w2;
+    w2 = quad == 2 ? acc[3] : w2;
+    w2 = quad == 3 ? acc[2] : w2;
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] += __shfl_xor(w2[g], 16);
+  };
+  auto online = [&](int u, const f32x4& v) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) x[u][g] = v[g];
+    if (lo + wave * (TPT * 64) + u * 64 + lane < hi) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float z = v[g] * c2;
+        const float mn = fmaxf(m[g], z);
+        sm[g] = sm[g] * fast_exp2(m[g] - mn) + fast_exp2(z - mn);
+        m[g] = mn;
+      }
+    }
+  };
+  if constexpr (FP8) {
+    // K scale of the lane's pages (1 for a page out of range: its products are zeroed)
+    const size_t hs = (size_t)p.pool_slot[h];
+    const float scA = (unsigned)blkA < (unsigned)p.num_blocks ? p.kv_scales[((size_t)blkA * p.Hp + hs) * 2] : 1.f;
+    const float scB = (unsigned)blkB < (unsigned)p.num_blocks ? p.kv_scales[((size_t)blkB * p.Hp + hs) * 2] : 1.f;
+    // byte offset of this lane's 8 codes in a page: step s2 adds 512
+    const char* kb8 = reinterpret_cast<const char*>(p.k_pool) + hs * (BS * D) + (size_t)row * 32 + 8 * quad;
+#pragma unroll
+    for (int u0 = 0; u0 < TPT; u0 += 2) {
+      u32x2 f[2][4][4];
+      unsigned valid[2] = {0u, 0u};
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        if (u0 + uu < ngroups) {                           // wave-uniform
+#pragma unroll
+          for (int pg = 0; pg < 4; ++pg) {
+            const int idx = 4 * (u0 + uu) + pg;
+            const int blk = __builtin_amdgcn_readlane(idx < 64 ? blkA : blkB, idx & 63);
+            const bool ok = (unsigned)blk < (unsigned)p.num_blocks;
+            valid[uu] |= ok ? (1u << pg) : 0u;
+            const char* src = kb8 + (size_t)(ok ? blk : 0) * page_stride;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) f[uu][pg][s2] = load_nt8(src + 512 * s2);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int u = u0 + uu;
+#pragma unroll
+        for (int g = 0; g < G; ++g) x[u][g] = 0.f;
+        if (u >= ngroups) continue;                        // wave-uniform
+        f32x4 acc[4];
+#pragma unroll
+        for (int pg = 0; pg < 4; ++pg) {
+          acc[pg] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            acc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s2], fp8x8_to_bf16x8(f[uu][pg][s2]), acc[pg], 0, 0, 0);
+          if (!((valid[uu] >> pg) & 1u)) acc[pg] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+        f32x4 v = acc[0];
+        v = quad == 1 ? acc[1] : v;
+        v = quad == 2 ? acc[2] : v;
+        v = quad == 3 ? acc[3] : v;
+        if constexpr (SPLITQ) fold_split(v, acc);
+        const float ks = __shfl(u < 16 ? scA : scB, (4 * u + quad) & 63);   // this lane's page
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] *= ks;
+        online(u, v);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
 #pragma unroll
   for (int u = 0; u < TPT; ++u) {
 #pragma unroll
@@ -907,19 +1004,11 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
       v = quad == 1 ? acc[1] : v;
       v = quad == 2 ? acc[2] : v;
       v = quad == 3 ? acc[3] : v;
-#pragma unroll
-      for (int g = 0; g < G; ++g) x[u][g] = v[g];
-      if (lo + wave * (TPT * 64) + u * 64 + lane < hi) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float z = v[g] * c2;
-          const float mn = fmaxf(m[g], z);
-          sm[g] = sm[g] * fast_exp2(m[g] - mn) + fast_exp2(z - mn);
-          m[g] = mn;
-        }
-      }
+      if constexpr (SPLITQ) fold_split(v, acc);
+      online(u, v);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
   }
 
   stamp_phase(p, 1);
@@ -1042,7 +1131,7 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   __syncthreads();
   stamp_phase(p, 8);
   if (nrows > 0)
-    attend_rows<G, false, MODE, FUSED_RB, true>(p, S, b, h, hr, j, lo, nrows, S.pages[0],
+    attend_rows<G, FP8, MODE, FUSED_RB, true>(p, S, b, h, hr, j, lo, nrows, S.pages[0],
                                                 lds ? reinterpret_cast<const float*>(logits) : nullptr);
   else
     empty_split<G>(p, b, h, j);
@@ -1051,14 +1140,14 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   stamp_phase(p, 10);
 }
 
-template <int MODE>
+template <int MODE, bool FP8, bool SPLITQ>
 __global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
   __shared__ TailLds S;
   __shared__ f32x4 logits[FUSED_LOGITS];
   const int w = blockIdx.x, nwg = gridDim.x;
   unsigned int* err = p.tail_sync;
   stamp_phase(p, 0);
-  if (w < p.tail_ntiles) fused_tile<MODE>(p, S, logits, err);
+  if (w < p.tail_ntiles) fused_tile<MODE, FP8, SPLITQ>(p, S, logits, err);
   if constexpr (MODE != 1) {
     // local-head chunks: item i goes to workgroup (ntiles + i) mod nwg
     const int nitems = p.B * p.nL * p.ncL;
@@ -1068,7 +1157,7 @@ __global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
       __syncthreads();
       const int nrows = local_rows(p, S, it, b, h, c);
       __syncthreads();
-      if (nrows > 0) attend_rows<4, false, MODE>(p, S, b, h, -1, c, 0, nrows, nullptr);
+      if (nrows > 0) attend_rows<4, FP8, MODE>(p, S, b, h, -1, c, 0, nrows, nullptr);
       else empty_split<4>(p, b, h, c);
       finish_split<4>(p, S, b, h, -1);
     }
@@ -1511,9 +1600,17 @@ int tail_grid(const DecodeParams& p, bool cooperative, bool select_only) {
   return resident_grid(pick_kernel(p, select_only), cooperative);
 }
 
+template <bool FP8, bool SPLITQ>
+void* pick_fused_mode(const DecodeParams& p) {
+  return p.nL == 0 ? reinterpret_cast<void*>(&fused_g4_kernel<1, FP8, SPLITQ>)
+                   : reinterpret_cast<void*>(&fused_g4_kernel<2, FP8, SPLITQ>);
+}
+
 void* pick_fused(const DecodeParams& p) {
-  if (p.G != 4 || p.score_mode != 1 || p.kv_scales != nullptr || p.qrot != nullptr) return nullptr;
-  return p.nL == 0 ? reinterpret_cast<void*>(&fused_g4_kernel<1>) : reinterpret_cast<void*>(&fused_g4_kernel<2>);
+  if (p.G != 4 || p.score_mode != 1) return nullptr;
+  const bool fp8 = p.kv_scales != nullptr, rot = p.qrot != nullptr;
+  if (fp8) return rot ? pick_fused_mode<true, true>(p) : pick_fused_mode<true, false>(p);
+  return rot ? pick_fused_mode<false, true>(p) : pick_fused_mode<false, false>(p);
 }
 
 int fused_grid(const DecodeParams& p, bool cooperative) { return resident_grid(pick_fused(p), cooperative); }

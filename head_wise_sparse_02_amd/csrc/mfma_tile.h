@@ -8,7 +8,6 @@
 
 namespace hws {
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 

@@ -92,6 +92,19 @@ def test_full_scores_fp8_cache(launch):
          launch=launch)
 
 
+@pytest.mark.parametrize("launch", [AUTO, MULTI], ids=["auto", "multi"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_full_scores_g4_rope(kv, launch):
+    """G = 4 full-dim scores with rotated queries (each split into a bf16 part
+    and the bf16 rounding of the rest), bf16 and e4m3 pages: AUTO runs them
+    in the fused launch, MULTI in the per-stage scan.  A ragged batch with a
+    local head (ragged tiles, local chunks in the same launch), then top-k
+    over one sequence of 40000 positions (three tiles)."""
+    _run(W.make_workload(1, n=9000, batch=3, kv_dtype=kv, score_mode="full", rope_theta=10000.0,
+                         seq_lens=[9000, 17, 4100]), launch=launch)
+    _run(W.make_workload(3, n=40000, batch=1, kv_dtype=kv, rope_theta=500000.0), launch=launch)
+
+
 @BOTH
 @pytest.mark.parametrize("mode", ["top_p_one", "top_k_all", "window_all", "tiny_p"])
 def test_reductions_to_dense_and_degenerate(mode, launch):
@@ -224,7 +237,11 @@ def test_rope_on(score_mode, launch):
 
 
 @pytest.mark.parametrize("cfg,kw", [(3, dict(n=40000, batch=4)), (2, dict(n=33000, batch=3)),
-                                    (5, dict(n=30000, batch=8))])
+                                    (5, dict(n=30000, batch=8)), (3, dict(n=40000, batch=2, kv_dtype="fp8")),
+                                    (3, dict(n=40000, batch=2, rope_theta=10000.0)),
+                                    (3, dict(n=33000, batch=2, kv_dtype="fp8", rope_theta=10000.0))],
+                         ids=["oracle-topk", "layer", "ragged-fp8", "oracle-topk-fp8", "oracle-topk-rope",
+                              "oracle-topk-fp8-rope"])
 def test_single_launch_matches_multi(cfg, kw):
     """Same token sets from every launch shape; outputs equal up to the fp32
     rounding order of the attention splits.  AUTO and SINGLE run the single
@@ -251,7 +268,12 @@ def test_single_launch_matches_multi(cfg, kw):
     a = run(SINGLE, single, ("select", "tail"))
     m = run(MULTI, "select", ("tail", "fused", "fused_index"))
     c = run(COOP, single, ("select", "tail"))
-    ss = run(hws.HWS_LAUNCH_SCAN_SINGLE, "tail", ("select", "fused", "fused_index"))
+    # (the single launch after a full-dim scan reads bf16 V rows only: with
+    # e4m3 pages SCAN_SINGLE runs the per-stage kernels)
+    if wl.score_mode == "full" and wl.kv_dtype == "fp8":
+        ss = run(hws.HWS_LAUNCH_SCAN_SINGLE, "select", ("tail", "fused", "fused_index"))
+    else:
+        ss = run(hws.HWS_LAUNCH_SCAN_SINGLE, "tail", ("select", "fused", "fused_index"))
     sel = run(hws.HWS_LAUNCH_SCAN_SELECT, "select", ("tail", "fused", "fused_index"))
     st.ctx.profile_enable(False)
     for key in ("out", "lse", "sel_counts", "sel_idx", "scores", "rows_read", "sel_mass"):
