@@ -894,17 +894,26 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   float m[G], sm[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) { m[g] = NEG_INF; sm[g] = 0.f; }
-  // SPLITQ: lane quad q holds page q's bf16-part products (q even) or its
-  // rest products (q odd); it swaps the other kind of page q ^ 1 with its
-  // partner lane (lane ^ 16), and hi + lo is added in either lane
-  auto fold_split = [&](f32x4& v, const f32x4 (&acc)[4]) {
-    f32x4 w2 = acc[1];
-    w2 = quad == 1 ? acc[0] : w2;
-    w2 = quad == 2 ? acc[3] : w2;
-    w2 = quad == 3 ? acc[2] : w2;
+  // SPLITQ: in page p's accumulator, 16-lane rows 0 and 2 hold the products
+  // of the queries' bf16 parts and rows 1 and 3 those of the rest.  One
+  // v_permlane16_swap of pages (0, 1) and one of pages (2, 3) exchange rows
+  // 1 <-> 0 and 3 <-> 2 across the pair, so that the two results hold, in
+  // every lane, the two kinds of the lane's own page; their sum is hi + lo.
+  auto fold_split = [&](const f32x4 (&acc)[4]) -> f32x4 {
+    f32x4 v;
 #pragma unroll
-    for (int g = 0; g < G; ++g) v[g] += __shfl_xor(w2[g], 16);
+    for (int g = 0; g < G; ++g) {
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[0][g]), __float_as_uint(acc[1][g]),
+                                                      false, false);
+      const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[2][g]), __float_as_uint(acc[3][g]),
+                                                      false, false);
+      const float r01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+      const float r23 = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+      v[g] = quad < 2 ? r01 : r23;
+    }
+    return v;
   };
+
   auto online = [&](int u, const f32x4& v) {
 #pragma unroll
     for (int g = 0; g < G; ++g) x[u][g] = v[g];
@@ -960,12 +969,25 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
             acc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s2], fp8x8_to_bf16x8(f[uu][pg][s2]), acc[pg], 0, 0, 0);
           if (!((valid[uu] >> pg) & 1u)) acc[pg] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
-        f32x4 v = acc[0];
-        v = quad == 1 ? acc[1] : v;
-        v = quad == 2 ? acc[2] : v;
-        v = quad == 3 ? acc[3] : v;
-        if constexpr (SPLITQ) fold_split(v, acc);
-        const float ks = __shfl(u < 16 ? scA : scB, (4 * u + quad) & 63);   // this lane's page
+        f32x4 v;
+        if constexpr (SPLITQ) {
+          v = fold_split(acc);
+        } else {
+          v = acc[0];
+          v = quad == 1 ? acc[1] : v;
+          v = quad == 2 ? acc[2] : v;
+          v = quad == 3 ? acc[3] : v;
+        }
+        // this lane's page 4u + quad: the four scales read as wave-uniform values
+        const int scw = __float_as_int(u < 16 ? scA : scB);
+        const float s0 = __int_as_float(__builtin_amdgcn_readlane(scw, (4 * u) & 63));
+        const float s1 = __int_as_float(__builtin_amdgcn_readlane(scw, (4 * u + 1) & 63));
+        const float s2 = __int_as_float(__builtin_amdgcn_readlane(scw, (4 * u + 2) & 63));
+        const float s3 = __int_as_float(__builtin_amdgcn_readlane(scw, (4 * u + 3) & 63));
+        float ks = s0;
+        ks = quad == 1 ? s1 : ks;
+        ks = quad == 2 ? s2 : ks;
+        ks = quad == 3 ? s3 : ks;
 #pragma unroll
         for (int g = 0; g < G; ++g) v[g] *= ks;
         online(u, v);
@@ -1000,11 +1022,15 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
           acc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s2], f[pg][s2], acc[pg], 0, 0, 0);
         if (!((valid >> pg) & 1u)) acc[pg] = (f32x4){0.f, 0.f, 0.f, 0.f};
       }
-      f32x4 v = acc[0];
-      v = quad == 1 ? acc[1] : v;
-      v = quad == 2 ? acc[2] : v;
-      v = quad == 3 ? acc[3] : v;
-      if constexpr (SPLITQ) fold_split(v, acc);
+      f32x4 v;
+      if constexpr (SPLITQ) {
+        v = fold_split(acc);
+      } else {
+        v = acc[0];
+        v = quad == 1 ? acc[1] : v;
+        v = quad == 2 ? acc[2] : v;
+        v = quad == 3 ? acc[3] : v;
+      }
       online(u, v);
       __builtin_amdgcn_sched_barrier(0);
     }
