@@ -23,11 +23,6 @@ __device__ __forceinline__ u32x4 load_nt16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// 8-byte load that does not allocate in the caches (data streamed once).
-__device__ __forceinline__ u32x2 load_nt8(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-}
-
 // 8 e4m3 codes -> 8 bf16, element e from byte e (exact: every e4m3 value is a
 // bf16 value, and the conversion's scale operand is 1).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
@@ -37,6 +32,30 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
   const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Full-dim scores over a K page (16 rows, blocked by 32 dims) with four
+// 16x16x32 MFMA steps: lane (row, quad) supplies 8 dims of row `row` to each
+// step t, and the query operand must enumerate the same dims.  bf16 pages:
+// step t takes dims 32t .. 32t + 31, 8 per quad (one 16-byte load per step).
+// e4m3 pages: a lane reads 16 codes at once, dims 32s + 16 (quad & 1) .. + 15
+// of 32-dim block s = quad >> 1 (load 0) and s = 2 + (quad >> 1) (load 1);
+// step t takes the low (t even) or high 8 codes of load t >> 1.
+template <bool FP8>
+__device__ __forceinline__ int mfma_dim0(int t, int quad) {
+  if constexpr (FP8) return 32 * (2 * (t >> 1) + (quad >> 1)) + 16 * (quad & 1) + 8 * (t & 1);
+  else return 32 * t + 8 * quad;
+}
+
+// Byte offset of this lane's first 16 codes in an e4m3 K page; the second
+// load is 1024 bytes further.
+__device__ __forceinline__ int fp8_page_lane_off(int row, int quad) {
+  return (quad >> 1) * 512 + row * 32 + (quad & 1) * 16;
+}
+
+// The B operand of step t from the lane's two 16-byte loads of an e4m3 page.
+__device__ __forceinline__ bf16x8 fp8_step(const u32x4& w, int t) {
+  return (t & 1) ? fp8x8_to_bf16x8((u32x2){w[2], w[3]}) : fp8x8_to_bf16x8((u32x2){w[0], w[1]});
 }
 
 constexpr float LOG2E = 1.4426950408889634f;

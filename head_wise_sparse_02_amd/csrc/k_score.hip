@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int d = 32 * s + 8 * quad + j;
+      const int d = mfma_dim0<FP8>(s, quad) + j;
       float v = 0.f;
       if (SPLITQ) {
         const int g = row < G ? row : row - G;
@@ -247,10 +247,13 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
   for (int i = 0; i < 4; ++i) { m[i] = NEG_INF; sm[i] = 0.f; }
 
   const int page0 = c * (SCORE_CHUNK / BS) + wave * 16;   // 16 pages per wave
-  constexpr int U = 4;                                     // pages in flight
+  // pages in flight: e4m3 pages are held as raw codes (8 registers a page)
+  // until their MFMAs, so twice as many fit
+  constexpr int U = FP8 ? 8 : 4;
 #pragma unroll 1
   for (int i0 = 0; i0 < 16; i0 += U) {
-    bf16x8 bfrag[U][4];
+    bf16x8 bfrag[FP8 ? 1 : U][4];
+    u32x4 raw[FP8 ? U : 1][2];
     int tpage[U];
     float ksc[U];                                          // FP8: the page's K scale
 #pragma unroll
@@ -263,19 +266,23 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
       if ((unsigned)blk < (unsigned)p.num_blocks) {
         // blocked page: step s of all 16 rows is one contiguous run (1 KiB bf16, 512 B e4m3)
         const size_t page = (size_t)blk * p.Hp + p.pool_slot[h];
-        const char* src = kpool + (page * (BS * D) + row * 32 + 8 * quad) * ES;
         if constexpr (FP8) {
           // e4m3 codes widened to bf16 (exact); the product is scaled after the MFMAs
           ksc[u] = p.kv_scales[page * 2];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) bfrag[u][s] = fp8x8_to_bf16x8(load_nt8(src + 512 * s));
+          const char* src8 = kpool + page * (BS * D) + fp8_page_lane_off(row, quad);
+          raw[FP8 ? u : 0][0] = load_nt16(src8);
+          raw[FP8 ? u : 0][1] = load_nt16(src8 + 1024);
         } else {
+          const char* src = kpool + (page * (BS * D) + row * 32 + 8 * quad) * ES;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) bfrag[u][s] = __builtin_bit_cast(bf16x8, load_nt16(src + 2 * 512 * s));
+          for (int s = 0; s < 4; ++s) bfrag[FP8 ? 0 : u][s] = __builtin_bit_cast(bf16x8, load_nt16(src + 2 * 512 * s));
         }
+      } else if constexpr (FP8) {
+        raw[FP8 ? u : 0][0] = (u32x4){0u, 0u, 0u, 0u};    // e4m3 code 0 is +0
+        raw[FP8 ? u : 0][1] = (u32x4){0u, 0u, 0u, 0u};
       } else {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag[u][s] = (bf16x8)(__bf16)0.f;
+        for (int s = 0; s < 4; ++s) bfrag[FP8 ? 0 : u][s] = (bf16x8)(__bf16)0.f;
       }
     }
 #pragma unroll
@@ -283,8 +290,10 @@ __global__ __launch_bounds__(256) void score_full_kernel(DecodeParams p) {
       if (tpage[u] >= N) continue;                         // wave-uniform
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s], bfrag[u][s], acc, 0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 bk = FP8 ? fp8_step(raw[FP8 ? u : 0][s >> 1], s) : bfrag[FP8 ? 0 : u][s];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s], bk, acc, 0, 0, 0);
+      }
       // Fold the lo rows onto the hi rows and keep the G scores of token `row`.
       float v[4] = {acc[0], acc[1], acc[2], acc[3]};
       if (SPLITQ) {

@@ -816,9 +816,10 @@ __global__ __launch_bounds__(TT) void select_single_kernel(DecodeParams p) {
 // time (the MFMA layout of the scoring kernel: lane quad u takes page u, so
 // each lane owns one token of every 4-page group, 32 tokens in all).  The
 // query rows of the A operand repeat the group's four heads four times.
-// FP8: e4m3 pages widened to bf16 codes (exact), two groups of loads in
-// flight (the bytes of one bf16 group), each page's products times its K
-// scale.  SPLITQ (rotated fp32 queries): rows 0-3 carry each query's bf16
+// FP8: e4m3 pages read 16 codes per lane load (the dims of the MFMA steps
+// permuted to match, in the query operand too), widened to bf16 (exact), two
+// groups of loads in flight (the bytes of one bf16 group), each page's
+// products times its K scale.  SPLITQ (rotated fp32 queries): rows 0-3 carry each query's bf16
 // part and rows 4-7 the bf16 rounding of the rest, so a page's MFMAs give
 // both products and the lanes of quads 2k and 2k+1 add them with one swap.
 // The scores equal the per-stage scan's bit for bit (the same products,
@@ -864,20 +865,21 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   // ---- scoring scan: x[u] = the 4 raw scores q_g . k of this lane's token u ----
   bf16x8 afrag[4];
   if constexpr (SPLITQ) {
-    const float* qg = p.qrot + ((size_t)b * p.Hq + h * G + (row & 3)) * D + 8 * quad;
+    const float* qg = p.qrot + ((size_t)b * p.Hq + h * G + (row & 3)) * D;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float xq = qg[32 * s2 + e];
+        const float xq = qg[mfma_dim0<FP8>(s2, quad) + e];
         const float hiq = bf16_to_f32(f32_to_bf16_rne(xq));
         afrag[s2][e] = (__bf16)((row & 4) ? xq - hiq : hiq);
       }
     }
   } else {
-    const uint16_t* qg = p.q + ((size_t)b * p.Hq + h * G + (row & 3)) * D + 8 * quad;
+    const uint16_t* qg = p.q + ((size_t)b * p.Hq + h * G + (row & 3)) * D;
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) afrag[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qg + 32 * s2));
+    for (int s2 = 0; s2 < 4; ++s2)
+      afrag[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qg + mfma_dim0<FP8>(s2, quad)));
   }
   const int* bt = p.block_tables + (size_t)b * p.max_blocks;
   const int page0 = (lo >> 4) + wave * FPW;                // sequence page of this wave's first page
@@ -932,11 +934,11 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
     const size_t hs = (size_t)p.pool_slot[h];
     const float scA = (unsigned)blkA < (unsigned)p.num_blocks ? p.kv_scales[((size_t)blkA * p.Hp + hs) * 2] : 1.f;
     const float scB = (unsigned)blkB < (unsigned)p.num_blocks ? p.kv_scales[((size_t)blkB * p.Hp + hs) * 2] : 1.f;
-    // byte offset of this lane's 8 codes in a page: step s2 adds 512
-    const char* kb8 = reinterpret_cast<const char*>(p.k_pool) + hs * (BS * D) + (size_t)row * 32 + 8 * quad;
+    // this lane's two 16-code loads of a page: at kb8 and kb8 + 1024
+    const char* kb8 = reinterpret_cast<const char*>(p.k_pool) + hs * (BS * D) + fp8_page_lane_off(row, quad);
 #pragma unroll
     for (int u0 = 0; u0 < TPT; u0 += 2) {
-      u32x2 f[2][4][4];
+      u32x4 f[2][4][2];
       unsigned valid[2] = {0u, 0u};
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
@@ -948,8 +950,8 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
             const bool ok = (unsigned)blk < (unsigned)p.num_blocks;
             valid[uu] |= ok ? (1u << pg) : 0u;
             const char* src = kb8 + (size_t)(ok ? blk : 0) * page_stride;
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) f[uu][pg][s2] = load_nt8(src + 512 * s2);
+            f[uu][pg][0] = load_nt16(src);
+            f[uu][pg][1] = load_nt16(src + 1024);
           }
         }
       }
@@ -966,7 +968,7 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
           acc[pg] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2)
-            acc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s2], fp8x8_to_bf16x8(f[uu][pg][s2]), acc[pg], 0, 0, 0);
+            acc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[s2], fp8_step(f[uu][pg][s2 >> 1], s2), acc[pg], 0, 0, 0);
           if (!((valid[uu] >> pg) & 1u)) acc[pg] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
         f32x4 v;
