@@ -209,6 +209,16 @@ __device__ __forceinline__ void scan_top(TailLds& S, unsigned long long above, u
   __syncthreads();
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup w runs on
+// XCD w mod 8).  The first n workgroups (n a multiple of 8) are renumbered so
+// that consecutive ids share an XCD: the tiles of one head, which have
+// consecutive ids, then stream and finish on one XCD, and a head waits only
+// for the XCD it runs on.  A bijection on [0, gridDim.x).
+__device__ __forceinline__ int xcd_local_id(int w, int n) {
+  if (w >= n || (n & 7) != 0) return w;
+  return (w & 7) * (n >> 3) + (w >> 3);
+}
+
 struct Tile {
   int t, b, hr, j, N, lo, hi;   // t < 0: no tile in this slot
 };
@@ -587,7 +597,7 @@ __device__ __forceinline__ int compact_rows(TailLds& S, unsigned int keep) {
   return nrows;
 }
 
-// Selection for the tiles of workgroup blockIdx.x (tile t = blockIdx.x + k *
+// Selection for the tiles of workgroup w (its XCD-local id, tile t = w + k *
 // gridDim.x): a_i of every token, the three radix passes, top-k ties.  Leaves
 // the tiles in tl, their kept-token masks in keepm and the block-table
 // entries in S.pages.
@@ -595,7 +605,7 @@ template <int G>
 __device__ __forceinline__ void select_tiles(const DecodeParams& p, TailLds& S, Tile (&tl)[MAXT], unsigned int (&keepm)[MAXT],
                              int& my_tiles, unsigned int* err) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int w = blockIdx.x, nwg = gridDim.x;
+  const int nwg = gridDim.x, w = xcd_local_id(blockIdx.x, min(p.tail_ntiles, nwg));
   const bool bymass = p.select_mode == 0;
   TileSel ts[MAXT];
   float av[MAXT][TPT];
@@ -727,7 +737,7 @@ __global__ __launch_bounds__(TT) void tail_kernel(DecodeParams p) {
   static_assert(MAXT == 2, "the work loop picks tile slots 0 / 1");
   __shared__ TailLds S;
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int w = blockIdx.x, nwg = gridDim.x;
+  const int nwg = gridDim.x, w = xcd_local_id(blockIdx.x, min(p.tail_ntiles, nwg));
   unsigned int* err = p.tail_sync;
 
   // Local-head chunks: item i goes to workgroup (ntiles + i) mod nwg, so the
@@ -782,7 +792,7 @@ __global__ __launch_bounds__(TT) void select_single_kernel(DecodeParams p) {
   Tile tl[MAXT];
   unsigned int keepm[MAXT];
   int my_tiles = 0;
-  if (blockIdx.x >= p.tail_ntiles) return;
+  if (xcd_local_id(blockIdx.x, min(p.tail_ntiles, (int)gridDim.x)) >= p.tail_ntiles) return;
   unsigned int* err = p.tail_sync;
   select_tiles<G>(p, S, tl, keepm, my_tiles, err);
   if (p.row_list == nullptr) return;
@@ -836,7 +846,8 @@ constexpr int FUSED_LOGITS = 2048;          // kept rows whose logits stay in LD
 constexpr int FUSED_RB = 12;                 // rows per processor per gather batch
 
 template <int MODE, bool FP8, bool SPLITQ>
-__device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f32x4* logits, unsigned int* err) {
+__device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f32x4* logits, unsigned int* err,
+                                           int t) {
   constexpr int G = 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, quad = lane >> 4;
@@ -844,7 +855,7 @@ __device__ __forceinline__ void fused_tile(const DecodeParams& p, TailLds& S, f3
   Tile tl[1];
   TileSel ts[1];
   {
-    const int t = blockIdx.x, head = t / p.tail_tph;
+    const int head = t / p.tail_tph;
     tl[0].t = t;
     tl[0].j = t % p.tail_tph;
     tl[0].b = head / p.nR;
@@ -1172,10 +1183,10 @@ template <int MODE, bool FP8, bool SPLITQ>
 __global__ __launch_bounds__(TT) void fused_g4_kernel(DecodeParams p) {
   __shared__ TailLds S;
   __shared__ f32x4 logits[FUSED_LOGITS];
-  const int w = blockIdx.x, nwg = gridDim.x;
+  const int nwg = gridDim.x, w = xcd_local_id(blockIdx.x, min(p.tail_ntiles, nwg));
   unsigned int* err = p.tail_sync;
   stamp_phase(p, 0);
-  if (w < p.tail_ntiles) fused_tile<MODE, FP8, SPLITQ>(p, S, logits, err);
+  if (w < p.tail_ntiles) fused_tile<MODE, FP8, SPLITQ>(p, S, logits, err, w);
   if constexpr (MODE != 1) {
     // local-head chunks: item i goes to workgroup (ntiles + i) mod nwg
     const int nitems = p.B * p.nL * p.ncL;
@@ -1230,7 +1241,7 @@ __device__ __forceinline__ void local_items(const DecodeParams& p, TailLds& S, i
 }
 
 template <int G, bool FP8, int SP>
-__device__ __forceinline__ void fused_index_tile(const DecodeParams& p, TailLds& S, unsigned int* err) {
+__device__ __forceinline__ void fused_index_tile(const DecodeParams& p, TailLds& S, unsigned int* err, int t) {
   static_assert(SP <= TPT && SP % 4 == 0 && 4 * SP <= 64, "slots in use; a page id per lane");
   constexpr int FPW_I = 4 * SP;                          // pages per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1240,7 +1251,7 @@ __device__ __forceinline__ void fused_index_tile(const DecodeParams& p, TailLds&
   Tile tl[1];
   TileSel ts[1];
   {
-    const int t = blockIdx.x, head = t / p.tail_tph;
+    const int head = t / p.tail_tph;
     tl[0].t = t;
     tl[0].j = t % p.tail_tph;
     tl[0].b = head / p.nR;
@@ -1536,10 +1547,10 @@ __device__ __forceinline__ void fused_index_tile(const DecodeParams& p, TailLds&
 template <int G, bool FP8, int SP>
 __global__ __launch_bounds__(TT) void fused_index_kernel(DecodeParams p) {
   __shared__ TailLds S;
-  const int w = blockIdx.x, nwg = gridDim.x;
+  const int nwg = gridDim.x, w = xcd_local_id(blockIdx.x, min(p.tail_ntiles, nwg));
   unsigned int* err = p.tail_sync;
   stamp_phase(p, 0);
-  if (w < p.tail_ntiles) fused_index_tile<G, FP8, SP>(p, S, err);
+  if (w < p.tail_ntiles) fused_index_tile<G, FP8, SP>(p, S, err, w);
   local_items<G, FP8>(p, S, w, nwg);
   stamp_phase(p, 11);
 }
