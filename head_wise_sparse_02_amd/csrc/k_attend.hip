@@ -186,7 +186,9 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     return;
   }
   float m[G], l[G], o[G][8];
-  constexpr int RB = AttRB<G, MODE>::value;
+  // (G = 8 with K rows: 4 rows per processor per batch here, where the
+  // kernel has the registers for them; the single launches keep 2)
+  constexpr int RB = (G == 8 && MODE == 0) ? 4 : AttRB<G, MODE>::value;
   if (FP8 && !is_ret && p.ring_rows > 0)         // the ring holds bf16 rows
     accumulate_rows<G, false, MODE, RB, false, true>(p, b, h, hr, lo, nrows, proc * RB, 16 * RB, sub, rows_s,
                                                      pages_s, ltok_s, pages_s, nullptr, m, l, o, nullptr);
