@@ -461,5 +461,190 @@ __device__ __forceinline__ void combine_wave_procs(float (&m)[G], float (&l)[G],
   combine_lane_pairs<G, 32>(m, l, o);
 }
 
+// ---------------------------------------------------------------------------
+// Rows with K at G = 8 (index scores or local heads), bf16 rows, queries not
+// rotated.  The 8 dot products per row are a dense contraction of the rows
+// with the group's queries, so they run on the matrix cores: a wave takes 32
+// rows per batch as two 16-row A operands of v_mfma_f32_16x16x32_bf16 (lane
+// (col, quad) loads the 8 dims 32 st + 8 quad of row col, 16 bytes of the
+// page-blocked K layout), B = the queries (column g < 8 = query head g, the
+// other 8 columns zero), 4 MFMAs per 16 rows over the 128 dims.  Lane
+// (col, quad) then holds the logits of query head col for rows 4 quad .. +3
+// of each tile: the wave's online softmax per head runs there (max and sum
+// over the four lane groups by lane swaps), and the weights go through LDS to
+// the row processors (16 lanes, dims 8 sub .. 8 sub + 7, 8 rows each), which
+// add p v on the vector ALUs.  Every processor of a wave shares the wave's
+// running max, so the processors' partials differ only in o: on return m is
+// the wave's max, l the wave's sum in processor 0 and 0 in the others, which
+// combine_wave_procs adds up exactly.  wscr: 288 floats of LDS owned by the
+// wave.  Products of bf16 values are exact in fp32; only the order of the
+// fp32 sums differs from the vector path.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void accumulate_rows_mfma8(const DecodeParams& p, int b, int h, int hr, int lo, int nrows,
+                                                      const unsigned short* rows, const int* pages, const int* ltok,
+                                                      const int* lpg, float* wscr, float (&m)[8], float (&l)[8],
+                                                      float (&o)[8][8]) {
+  constexpr int G = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int col = lane & 15, quad = lane >> 4;   // MFMA operand lane; also (sub, proc) of the row processors
+  const bool is_ret = hr >= 0;
+  const bool ring = !is_ret && p.ring_rows > 0;
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(ring ? p.lk_pool : p.k_pool);
+  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(ring ? p.lv_pool : p.v_pool);
+  const int hstride = ring ? 1 : p.Hp;
+  const int hslot = ring ? 0 : p.pool_slot[h];
+  const unsigned plim = ring ? (unsigned)p.ring_pages : (unsigned)p.num_blocks;
+  int* rr = (p.rows_read != nullptr && col == 0 && !ring) ? p.rows_read + (size_t)(b * p.Hkv + h) * p.Nmax : nullptr;
+
+  bf16x8 qb[4];
+  {
+    const uint16_t* qrow = p.q + ((size_t)b * p.Hq + h * G + (col & 7)) * D + 8 * quad;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * st);
+      qb[st] = __builtin_bit_cast(bf16x8, col < G ? w : u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  // row r of the list: its position and page; false (position 0, page 0,
+  // loaded but masked) past the list or for a page outside the pool
+  auto row_at = [&](int r, int& ii, int& pg) {
+    const int rc = min(r, nrows - 1);
+    if (is_ret) {
+      const int off = rows[rc];
+      ii = lo + off;
+      pg = pages[off >> 4];
+    } else {
+      ii = ltok[rc];
+      pg = lpg[rc];
+    }
+    const bool ok = r < nrows && (unsigned)pg < plim;
+    if (!ok) { ii = 0; pg = 0; }
+    return ok;
+  };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  float m_run = NEG_INF, l_run = 0.f;            // query head col (col < 8), over the wave's rows
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+
+  for (int r0 = wave * 32; r0 < nrows; r0 += nwaves * 32) {
+    int iiA[2], pgA[2], iiV[8], pgV[8];
+    bool okA[2], okV[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) okA[t] = row_at(r0 + 16 * t + col, iiA[t], pgA[t]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) okV[u] = row_at(r0 + 8 * quad + u, iiV[u], pgV[u]);
+    if (rr != nullptr) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (okV[u]) atomicAdd(rr + iiV[u], 1);
+    }
+    // every load of the batch: 8 V chunks (processor rows), 8 K chunks (A rows)
+    u32x4 vw[8], kw[2][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      vw[u] = *reinterpret_cast<const u32x4*>(vpool + (((size_t)pgV[u] * hstride + hslot) * BS + (iiV[u] & 15)) * D +
+                                              8 * col);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        kw[t][st] = *reinterpret_cast<const u32x4*>(kpool + ((size_t)pgA[t] * hstride + hslot) * (BS * D) +
+                                                    (size_t)(st * 16 + (iiA[t] & 15)) * 32 + 8 * quad);
+    const unsigned okb0 = (unsigned)__ballot(okA[0]) & 0xFFFFu, okb1 = (unsigned)__ballot(okA[1]) & 0xFFFFu;
+
+    // logits in log2 units: z[t][i] = row 16 t + 4 quad + i, query head col
+    float z[2][4];
+    float mx = NEG_INF;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[t][st]), qb[st], acc, 0, 0, 0);
+      const unsigned okb = t ? okb1 : okb0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[t][i] = ((okb >> (4 * quad + i)) & 1u) ? acc[i] * p.c2_attn : NEG_INF;
+        mx = fmaxf(mx, z[t][i]);
+      }
+    }
+    float a, c;
+    lane_pair<16>(mx, a, c);
+    mx = fmaxf(a, c);
+    lane_pair<32>(mx, a, c);
+    mx = fmaxf(a, c);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == NEG_INF ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[t][i] = fast_exp2(z[t][i] - m_use);
+        ps += z[t][i];
+      }
+    lane_pair<16>(ps, a, c);
+    ps = a + c;
+    lane_pair<32>(ps, a, c);
+    ps = a + c;
+    l_run = l_run * alpha + ps;
+
+    // weights [row][head] and the heads' rescale factors to the wave's LDS
+    wave_sync();                                 // the previous batch's reads are done
+    if (col < G) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wscr[(16 * t + 4 * quad + i) * G + col] = z[t][i];
+      if (quad == 0) wscr[256 + col] = alpha;
+    }
+    wave_sync();
+    {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(wscr + 256), a1 = *reinterpret_cast<const f32x4*>(wscr + 260);
+      const float al[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] *= al[g];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(wscr + (8 * quad + u) * G);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(wscr + (8 * quad + u) * G + 4);
+      const float pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      const u32x4 w = vw[u];
+      float vv[8] = {bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]),
+                     bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vv[j] = okV[u] ? vv[j] : 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pw[g], vv[j], o[g][j]);
+    }
+  }
+  // every lane: the wave's (m, l) per head, l counted once (processor 0)
+  wave_sync();
+  if (col < G && quad == 0) {
+    wscr[272 + col] = m_run;
+    wscr[280 + col] = l_run;
+  }
+  wave_sync();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = wscr[272 + g];
+    l[g] = quad == 0 ? wscr[280 + g] : 0.f;
+  }
+}
+
 }  // namespace hws
 

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   __shared__ int ltok_s[LOCAL_CHUNK];               // local: row tokens
   __shared__ unsigned int tmp[8];
   __shared__ float wm[4][MAX_G], wl[4][MAX_G];
-  __shared__ float wo[4][MAX_G][D];
+  __shared__ __align__(16) float wo[4][MAX_G][D];   // (also the MFMA path's per-wave weights)
 
   int nrows = 0, lo = 0;
   if (is_ret) {
@@ -189,7 +189,17 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   // (G = 8 with K rows: 4 rows per processor per batch here, where the
   // kernel has the registers for them; the single launches keep 2)
   constexpr int RB = (G == 8 && MODE == 0) ? 4 : AttRB<G, MODE>::value;
-  if (FP8 && !is_ret && p.ring_rows > 0)         // the ring holds bf16 rows
+  // (G = 8, bf16 rows, queries not rotated, one set per KV head: the dot
+  // products on the matrix cores)
+  bool mfma_rows = false;
+  if constexpr (G == 8 && MODE == 0 && !FP8) {
+    if (p.qrot == nullptr && p.GS == 1) {
+      accumulate_rows_mfma8(p, b, h, hr, lo, nrows, rows_s, pages_s, ltok_s, pages_s, &wo[wave][0][0], m, l, o);
+      mfma_rows = true;
+    }
+  }
+  if (mfma_rows) {
+  } else if (FP8 && !is_ret && p.ring_rows > 0)  // the ring holds bf16 rows
     accumulate_rows<G, false, MODE, RB, false, true>(p, b, h, hr, lo, nrows, proc * RB, 16 * RB, sub, rows_s,
                                                      pages_s, ltok_s, pages_s, nullptr, m, l, o, nullptr);
   else
