@@ -476,14 +476,16 @@ __device__ __forceinline__ void combine_wave_procs(float (&m)[G], float (&l)[G],
 // add p v on the vector ALUs.  Every processor of a wave shares the wave's
 // running max, so the processors' partials differ only in o: on return m is
 // the wave's max, l the wave's sum in processor 0 and 0 in the others, which
-// combine_wave_procs adds up exactly.  wscr: 288 floats of LDS owned by the
-// wave.  Products of bf16 values are exact in fp32; only the order of the
-// fp32 sums differs from the vector path.
+// combine_wave_procs adds up exactly.  With one set per query head
+// (row_mask: each listed row's head bits), a row outside head g's set gets
+// the logit -inf for that head.  wscr: 288 floats of LDS owned by the wave.
+// Products of bf16 values are exact in fp32; only the order of the fp32 sums
+// differs from the vector path.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void accumulate_rows_mfma8(const DecodeParams& p, int b, int h, int hr, int lo, int nrows,
                                                       const unsigned short* rows, const int* pages, const int* ltok,
                                                       const int* lpg, float* wscr, float (&m)[8], float (&l)[8],
-                                                      float (&o)[8][8]) {
+                                                      float (&o)[8][8], const unsigned char* row_mask = nullptr) {
   constexpr int G = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int col = lane & 15, quad = lane >> 4;   // MFMA operand lane; also (sub, proc) of the row processors
@@ -571,7 +573,10 @@ __device__ __forceinline__ void accumulate_rows_mfma8(const DecodeParams& p, int
       const unsigned okb = t ? okb1 : okb0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        z[t][i] = ((okb >> (4 * quad + i)) & 1u) ? acc[i] * p.c2_attn : NEG_INF;
+        bool keep = (okb >> (4 * quad + i)) & 1u;
+        if (is_ret && row_mask != nullptr)         // one set per query head: the row's head bits
+          keep = keep && ((row_mask[min(r0 + 16 * t + 4 * quad + i, nrows - 1)] >> col) & 1u);
+        z[t][i] = keep ? acc[i] * p.c2_attn : NEG_INF;
         mx = fmaxf(mx, z[t][i]);
       }
     }

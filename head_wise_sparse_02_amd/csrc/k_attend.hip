@@ -189,12 +189,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   // (G = 8 with K rows: 4 rows per processor per batch here, where the
   // kernel has the registers for them; the single launches keep 2)
   constexpr int RB = (G == 8 && MODE == 0) ? 4 : AttRB<G, MODE>::value;
-  // (G = 8, bf16 rows, queries not rotated, one set per KV head: the dot
-  // products on the matrix cores)
+  // (G = 8, bf16 rows, queries not rotated: the dot products on the matrix
+  // cores; with one set per query head each row's head bits mask its logits)
   bool mfma_rows = false;
   if constexpr (G == 8 && MODE == 0 && !FP8) {
-    if (p.qrot == nullptr && p.GS == 1) {
-      accumulate_rows_mfma8(p, b, h, hr, lo, nrows, rows_s, pages_s, ltok_s, pages_s, &wo[wave][0][0], m, l, o);
+    if (p.qrot == nullptr) {
+      accumulate_rows_mfma8(p, b, h, hr, lo, nrows, rows_s, pages_s, ltok_s, pages_s, &wo[wave][0][0], m, l, o,
+                            p.GS > 1 ? rmask_s : nullptr);
       mfma_rows = true;
     }
   }

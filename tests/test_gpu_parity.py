@@ -211,14 +211,16 @@ def test_long_256k_all_heads():
     print("config 4 retrieval |S| =", res["sel_counts"][0, 0], flush=True)
 
 
-@pytest.mark.parametrize("n,launch", [(40, MULTI), (1000, MULTI), (5000, MULTI), (5000, AUTO)],
-                         ids=["40-multi", "1000-multi", "5000-multi", "5000-auto"])
-def test_g8_rows_on_matrix_cores(n, launch):
-    """G = 8 rows with K (bf16 pages, queries not rotated, one set per KV
-    head) take the matrix-core attention: two ragged sequences, so chunks
-    leave waves with no 32-row batch, a partial one or several; every head
-    of both sequences against the oracle, and the rows each read."""
-    wl = W.make_workload(4, n=n, batch=2)
+@pytest.mark.parametrize("n,launch,scope", [(40, MULTI, "kv"), (1000, MULTI, "kv"), (5000, MULTI, "kv"),
+                                           (5000, AUTO, "kv"), (40, AUTO, "query"), (5000, AUTO, "query")],
+                         ids=["40-multi", "1000-multi", "5000-multi", "5000-auto", "40-query", "5000-query"])
+def test_g8_rows_on_matrix_cores(n, launch, scope):
+    """G = 8 rows with K (bf16 pages, queries not rotated) take the
+    matrix-core attention: two ragged sequences, so chunks leave waves with
+    no 32-row batch, a partial one or several; with one set per query head
+    each row's head bits mask its logits.  Every head of both sequences
+    against the oracle, and the rows each read."""
+    wl = W.make_workload(4, n=n, batch=2, select_scope=scope)
     wl.seq_lens = [n, n // 3 + 1]
     _run(wl, launch=launch, pairs=[(b, h) for b in range(2) for h in range(wl.Hkv)])
 
